@@ -1,0 +1,191 @@
+"""Throughput of one MoE layer's expert stage (forward + backward) on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is the whole stage on one batch of synthetic input already resident
+in HBM: route -> expert indexing + gather -> gate/up GEMM (SwiGLU epilogue)
+-> down GEMM -> combine, then combine backward -> down dgrad (SwiGLU backward
+epilogue) -> down wgrad -> gate/up dgrad -> gate/up wgrad -> unpermute-sum ->
+router backward, every step a call of the C ABI (the six GEMMs through their
+one-kernel entry points, which is what moe_grouped_gemm_fwd/bwd chain).
+
+Prints one JSON line. `value` is tokens/s of the whole stage; TFLOP/s counts
+the expert GEMMs (18*T*k*H*I per step). `roofline` covers the dominant kernel:
+its algorithmic flops per launch over its average launch time, measured with
+HIP events around that kernel's call on the stream it runs on, against the
+bf16 dense MFMA peak. `cpu_baseline` times the CPU oracle on a bounded token
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE expert-stage tokens/s and TFLOP/s (fwd+bwd), Qwen3-30B-A3B shape, 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gemm_flops(c) -> dict:
+    """Algorithmic flops of each grouped GEMM per launch (M = T*k rows)."""
+    m, h, i = c.T * c.k, c.H, c.I
+    return {
+        "moe_gemm_gate_up": 4.0 * m * h * i,
+        "moe_gemm_down": 2.0 * m * h * i,
+        "moe_gemm_down_dgrad": 2.0 * m * h * i,
+        "moe_gemm_down_wgrad": 2.0 * m * h * i,
+        "moe_gemm_gate_up_dgrad": 4.0 * m * h * i,
+        "moe_gemm_gate_up_wgrad": 4.0 * m * h * i,
+    }
+
+
+def cpu_baseline(cfg, seed: int, tokens: int) -> dict:
+    """The oracle, as it stands, on the first `tokens` tokens of the workload."""
+    import numpy as np  # noqa: F401
+
+    from mixture_experts_expert_amd import synth
+    from oracle import oracle as O
+
+    threads = min(16, os.cpu_count() or 1)
+    O.set_threads(threads)
+    inp = synth.make_inputs(cfg, seed, T=tokens)
+    f = {n: inp.f32(n) for n in inp.names()}
+    t0 = time.perf_counter()
+    fwd = O.forward(f["x"], f["w_router"], f["w_gate"], f["w_up"], f["w_down"], cfg.k, logit_bias=inp.logit_bias)
+    O.backward(fwd, f["dy"], f["w_gate"], f["w_up"], f["w_down"])
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{tokens} of {cfg.T} tokens (same H, E, k, I), fwd+bwd, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_30b_a3b_train")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=512)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from mixture_experts_expert_amd import binding as B
+    from mixture_experts_expert_amd import synth
+
+    cfg = synth.CONFIGS[args.workload]
+    assert cfg.backward and cfg.dtype == "bf16", "the benchmark runs bf16 training-step workloads"
+    torch.cuda.set_device(0)
+    log(f"workload {cfg}")
+    t0 = time.perf_counter()
+    inp = synth.make_inputs(cfg, args.seed)
+    dev = {n: torch.from_numpy(inp.bits[n].view(np.int16)).to("cuda").view(torch.bfloat16) for n in inp.names()}
+    bias = None if inp.logit_bias is None else torch.from_numpy(inp.logit_bias).to("cuda")
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    st = B.MoEStage(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, torch.bfloat16)
+    st._alloc_bwd()
+    b, s = st.buf, st.s
+    lw = B.moe_workspace_bytes(s)
+    dgu = st.ws[lw - cfg.M * 2 * cfg.I * 2:].view(torch.bfloat16).view(cfg.M, 2 * cfg.I)
+    x, wr, wg, wu, wd, dy = (dev[n] for n in ["x", "w_router", "w_gate", "w_up", "w_down", "dy"])
+    stream = torch.cuda.current_stream()
+    names = ["moe_route", "moe_permute", "moe_gemm_gate_up", "moe_gemm_down", "moe_combine", "moe_combine_bwd",
+             "moe_gemm_down_dgrad", "moe_gemm_down_wgrad", "moe_gemm_gate_up_dgrad", "moe_gemm_gate_up_wgrad",
+             "moe_unpermute_sum", "moe_route_bwd"]
+    calls = [
+        lambda: B.moe_route(s, x, wr, bias, b["logits"], b["topk_idx"], b["topk_w"]),
+        lambda: B.moe_permute(s, b["topk_idx"], x, b["counts"], b["offsets"], b["sorted_to_flat"],
+                              b["flat_to_sorted"], b["x_perm"], st.ws),
+        lambda: B.moe_gemm_gate_up(s, b["x_perm"], b["offsets"], wg, wu, b["g"], b["u"], b["a"]),
+        lambda: B.moe_gemm_down(s, b["a"], b["offsets"], wd, b["o_perm"]),
+        lambda: B.moe_combine(s, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["y"]),
+        lambda: B.moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["do_perm"],
+                                  b["d_topk_w"]),
+        lambda: B.moe_gemm_down_dgrad(s, b["do_perm"], b["offsets"], wd, b["g"], b["u"], dgu),
+        lambda: B.moe_gemm_down_wgrad(s, b["do_perm"], b["a"], b["offsets"], b["dw_down"], 0),
+        lambda: B.moe_gemm_gate_up_dgrad(s, dgu, b["offsets"], wg, wu, b["dx_perm"]),
+        lambda: B.moe_gemm_gate_up_wgrad(s, dgu, b["x_perm"], b["offsets"], b["dw_gate"], b["dw_up"], 0),
+        lambda: B.moe_unpermute_sum(s, b["dx_perm"], b["flat_to_sorted"], b["dx"]),
+        lambda: B.moe_route_bwd(s, b["d_topk_w"], b["topk_w"], b["topk_idx"], b["d_logits"]),
+    ]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+
+    def step(events=None):
+        for i, c in enumerate(calls):
+            if events is not None:
+                events[i].record(stream)
+            c()
+        if events is not None:
+            events[-1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        step(ev[k])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / args.steps
+    per_call = {n: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)) / args.steps
+                for i, n in enumerate(names)}
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step; " + ", ".join(f"{n}={v:.3f}" for n, v in per_call.items()))
+
+    flops = gemm_flops(cfg)
+    step_flops = sum(flops.values())
+    tflops = step_flops / (ms * 1e-3) / 1e12
+    dominant = max(flops, key=lambda n: per_call[n])
+    ach = flops[dominant] / (per_call[dominant] * 1e-3) / 1e12
+    gemm_tflops = {n: round(flops[n] / (per_call[n] * 1e-3) / 1e12, 1) for n in flops}
+    out = {
+        "metric": METRIC,
+        "value": round(cfg.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal inputs, random-init weights of the Qwen3-30B-A3B MoE layer shape)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
+                   "seed": args.seed, "pass": "fwd+bwd"},
+        "tflops": round(tflops, 1),
+        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "gemm_tflops": gemm_tflops,
+        "call_ms": {n: round(v, 4) for n, v in per_call.items()},
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
+        out["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,193 @@
+/* moe.h — C ABI of the fused MoE expert stage for MI355X (gfx950).
+ *
+ * One MoE layer's expert stage on one GPU, forward and backward, as a chain of
+ * calls on one HIP stream:
+ *
+ *   forward : moe_route -> moe_permute -> moe_grouped_gemm_fwd -> moe_combine
+ *   backward: moe_combine_bwd -> moe_grouped_gemm_bwd -> moe_unpermute_sum -> moe_route_bwd
+ *
+ * It replaces the per-expert for-loop of the Hugging Face MoE block (axolotl
+ * issue #3155, "Feature description") with router softmax/top-k, a sort of the
+ * (token, expert) pairs by expert, grouped GEMMs over the stacked expert
+ * weights with a SwiGLU epilogue, and a weighted combine (sourcepulse summary
+ * of the Triton fused-MoE repository, "How It Works").
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer (hipMalloc'd or a torch CUDA
+ *     tensor's data_ptr), to a dense row-major array.
+ *   - Indices are int32. T*k must stay below 2^31.
+ *   - Activations and weights (x, w_*, g, u, a, o_perm, y, dy, do_perm,
+ *     dx_perm, dx) have element type shape.dtype: MOE_F32 (float) or MOE_BF16
+ *     (bfloat16 bit patterns). Router outputs (logits, topk_w, d_topk_w,
+ *     d_logits) and weight gradients (dw_*) are always float32.
+ *   - The caller owns every buffer, including the workspace; the library never
+ *     allocates device memory and keeps no pointer after a call returns.
+ *   - Each call only enqueues kernels on `stream` and returns; it never
+ *     synchronises. Outputs are fully overwritten (except dw_* with
+ *     accumulate_dw = 1). Results are deterministic: no floating-point
+ *     atomics, so reruns are bitwise identical.
+ *   - Errors: every argument is checked on the host before any HIP call; a
+ *     bad argument returns MOE_EINVAL (null pointer, non-positive size, k > E,
+ *     E > 1024, T*k >= 2^31), MOE_EUNSUPPORTED (H or I not a multiple of 64,
+ *     unknown dtype) or MOE_EWORKSPACE (workspace too small), with nothing
+ *     enqueued. A failed launch returns MOE_EHIP. Faults inside kernels
+ *     surface at the caller's next synchronisation. No C++ exception crosses
+ *     this interface.
+ *   - Calls on disjoint buffers may run concurrently on different streams.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,
+  MOE_EUNSUPPORTED = 2,
+  MOE_EWORKSPACE = 3,
+  MOE_EHIP = 4
+} moe_status;
+
+/* T tokens, hidden size H, E experts, k experts per token, expert
+ * intermediate size I; dtype is a moe_dtype. */
+typedef struct {
+  int32_t T, H, E, k, I;
+  int32_t dtype;
+} moe_shape;
+
+/* Bytes of device workspace for this shape. One buffer of this size serves
+ * every call that takes a workspace: moe_permute's per-block expert
+ * histograms, and moe_grouped_gemm_bwd's dG and dU for every row
+ * ([T*k, 2I] in dtype). */
+size_t moe_workspace_bytes(moe_shape s);
+
+/* Router (torchtune PR #2820 "[WIP] Qwen3 MoE support", comment on dividing
+ * the top scores by their sum plus 1e-20; axolotl issue #3155, comments on
+ * the router weight shape; sourcepulse summary, "Highlighted Details": fused
+ * softmax + top-k).
+ *   x [T,H], w_router [E,H] (nn.Linear(H, E) layout), logit_bias [E] float32
+ *   or NULL.
+ *   logits[t,e] = fp32 fma chain over h ascending from +0, then + bias[e];
+ *   topk_idx[t,:] = the k largest logits, largest first, ties to the lower
+ *   expert index; topk_w[t,j] = p[idx] / (sum_j p[idx] + 1e-20) with
+ *   p = softmax(logits[t,:]) in fp32.
+ * Outputs: logits [T,E] f32, topk_idx [T,k] int32, topk_w [T,k] f32. */
+moe_status moe_route(moe_shape s, const void* x, const void* w_router, const float* logit_bias,
+                     float* logits, int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+/* Expert indexing and gather (unsloth PR #3812 "[MoE] Improve moe kernels",
+ * review suggestion: counts by bincount, the order by a stable argsort of
+ * the flattened expert ids).
+ *   counts[e] = #{f : topk_idx[f] == e} (shape [E]), offsets [E+1] its
+ *   exclusive prefix sum; for flat index f = t*k + j,
+ *   flat_to_sorted[f] = offsets[e_f] + #{f' < f : e_f' == e_f},
+ *   sorted_to_flat is its inverse; x_perm[p,:] = x[sorted_to_flat[p] / k, :].
+ *   topk_idx values must lie in [0, E) (not checked on the device).
+ * Outputs: counts [E], offsets [E+1], sorted_to_flat [T*k],
+ * flat_to_sorted [T*k] (int32), x_perm [T*k,H]. Workspace: ws of ws_bytes >=
+ * moe_workspace_bytes(s). */
+moe_status moe_permute(moe_shape s, const int32_t* topk_idx, const void* x, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_perm,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Grouped GEMMs of the forward over the expert-sorted rows (sourcepulse
+ * summary, "How It Works": grouped GEMM on inputs sorted by expert; unsloth
+ * PR #3812, stacked gate/up [E,2I,H] and down [E,H,I] weights, held here as
+ * separate W_gate and W_up; axolotl issue #3155, numerical-check comment:
+ * silu gating, no bias). For each expert e and row p in
+ * [offsets[e], offsets[e+1]):
+ *   g = x_perm[p] W_gate[e]^T, u = x_perm[p] W_up[e]^T, a = silu(g) * u,
+ *   o_perm[p] = a W_down[e]^T      (fp32 accumulation; stored in dtype).
+ * Inputs: x_perm [T*k,H], offsets [E+1] (device, from moe_permute),
+ * w_gate, w_up [E,I,H], w_down [E,H,I]. Outputs: g, u, a [T*k,I] (kept for
+ * the backward), o_perm [T*k,H]. ws/ws_bytes are accepted for interface
+ * symmetry and may be NULL/0. */
+moe_status moe_grouped_gemm_fwd(moe_shape s, const void* x_perm, const int32_t* offsets, const void* w_gate,
+                                const void* w_up, const void* w_down, void* g, void* u, void* a, void* o_perm,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The six grouped GEMMs one at a time (moe_grouped_gemm_fwd and
+ * moe_grouped_gemm_bwd chain them). Same operands, layouts and arithmetic as
+ * described there; dgu is [T*k, 2I] in dtype holding dG in columns [0, I)
+ * and dU in columns [I, 2I). Callers that train adapters on frozen experts
+ * can run the data gradients without the weight gradients.
+ *   moe_gemm_gate_up       g, u, a  <- x_perm, W_gate, W_up
+ *   moe_gemm_down          o_perm   <- a, W_down
+ *   moe_gemm_down_dgrad    dgu      <- do_perm, W_down, g, u
+ *   moe_gemm_down_wgrad    dw_down  <- do_perm, a              (f32; += if accumulate_dw)
+ *   moe_gemm_gate_up_dgrad dx_perm  <- dgu, W_gate, W_up
+ *   moe_gemm_gate_up_wgrad dw_gate, dw_up <- dgu, x_perm       (f32; += if accumulate_dw) */
+moe_status moe_gemm_gate_up(moe_shape s, const void* x_perm, const int32_t* offsets, const void* w_gate,
+                            const void* w_up, void* g, void* u, void* a, hipStream_t stream);
+moe_status moe_gemm_down(moe_shape s, const void* a, const int32_t* offsets, const void* w_down, void* o_perm,
+                         hipStream_t stream);
+moe_status moe_gemm_down_dgrad(moe_shape s, const void* do_perm, const int32_t* offsets, const void* w_down,
+                               const void* g, const void* u, void* dgu, hipStream_t stream);
+moe_status moe_gemm_down_wgrad(moe_shape s, const void* do_perm, const void* a, const int32_t* offsets,
+                               float* dw_down, int accumulate_dw, hipStream_t stream);
+moe_status moe_gemm_gate_up_dgrad(moe_shape s, const void* dgu, const int32_t* offsets, const void* w_gate,
+                                  const void* w_up, void* dx_perm, hipStream_t stream);
+moe_status moe_gemm_gate_up_wgrad(moe_shape s, const void* dgu, const void* x_perm, const int32_t* offsets,
+                                  float* dw_gate, float* dw_up, int accumulate_dw, hipStream_t stream);
+
+/* Weighted combine (modelopt.torch.utils.moe, a2a_moe: each token's k expert
+ * results are weighted by its routing weights in their own precision and
+ * summed; the result returns in the hidden dtype).
+ *   y[t,:] = sum over j ascending of topk_w[t,j] * o_perm[flat_to_sorted[t*k+j],:]
+ *   in fp32, rounded once to dtype. Output: y [T,H]. */
+moe_status moe_combine(moe_shape s, const void* o_perm, const float* topk_w, const int32_t* flat_to_sorted,
+                       void* y, hipStream_t stream);
+
+/* Backward of moe_combine (chain rule of the combine above).
+ *   do_perm[p,:] = topk_w[t,j] * dy[t,:], d_topk_w[t,j] = <dy[t,:], o_perm[p,:]>
+ *   with p = flat_to_sorted[t*k+j]. Outputs: do_perm [T*k,H] (dtype),
+ *   d_topk_w [T,k] f32. */
+moe_status moe_combine_bwd(moe_shape s, const void* dy, const void* o_perm, const float* topk_w,
+                           const int32_t* flat_to_sorted, void* do_perm, float* d_topk_w, hipStream_t stream);
+
+/* Backward of moe_grouped_gemm_fwd (chain rule of the expert MLP above). For
+ * each expert e, over its rows:
+ *   dA = do_perm W_down[e];  dU = dA * silu(g);  dG = dA * u * s * (1 + g (1 - s)), s = sigmoid(g)
+ *   dx_perm = dG W_gate[e] + dU W_up[e]
+ *   dW_down[e] = do_perm^T a,  dW_gate[e] = dG^T x_perm,  dW_up[e] = dU^T x_perm
+ * Weight gradients are float32 with fp32 accumulation; an expert with no rows
+ * gets zeros. accumulate_dw = 0 overwrites dw_*, 1 adds to them.
+ * Inputs as produced by the forward. Outputs: dx_perm [T*k,H] (dtype),
+ * dw_gate, dw_up [E,I,H] f32, dw_down [E,H,I] f32. Workspace: ws of
+ * ws_bytes >= moe_workspace_bytes(s). */
+moe_status moe_grouped_gemm_bwd(moe_shape s, const void* do_perm, const void* x_perm, const void* g,
+                                const void* u, const void* a, const int32_t* offsets, const void* w_gate,
+                                const void* w_up, const void* w_down, void* dx_perm, float* dw_gate,
+                                float* dw_up, float* dw_down, int accumulate_dw, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* Backward of the gather in moe_permute: dx[t,:] = sum over j ascending of
+ * dx_perm[flat_to_sorted[t*k+j],:] in fp32, rounded once. Output: dx [T,H]. */
+moe_status moe_unpermute_sum(moe_shape s, const void* dx_perm, const int32_t* flat_to_sorted, void* dx,
+                             hipStream_t stream);
+
+/* Backward of the routing weights (chain rule of the renormalised top-k
+ * softmax in moe_route):
+ *   d_logits[t,e] = w_j (g_j - sum_i w_i g_i) if e = topk_idx[t,j], else 0,
+ *   with w = topk_w and g = d_topk_w. (The exact derivative also carries terms
+ *   of relative size 1e-20 from the renormalisation constant; they are
+ *   dropped.) Output: d_logits [T,E] f32. */
+moe_status moe_route_bwd(moe_shape s, const float* d_topk_w, const float* topk_w, const int32_t* topk_idx,
+                         float* d_logits, hipStream_t stream);
+
+/* A static, human-readable name for a status code. */
+const char* moe_status_string(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,248 @@
+"""Python binding of libmoe's C ABI (include/moe.h), by ctypes.
+
+Argument marshalling only: every function here has the name of a C entry
+point, checks nothing the library does not check itself, passes torch CUDA
+tensors as raw device pointers and the current HIP stream, and raises
+``MoEError`` on a non-zero status. Every step of the stage runs in the
+library's HIP kernels; there is no other code path. Importing this module on a
+machine without the built library raises ImportError.
+
+``MoEStage`` chains the calls of one forward and one backward pass, holding
+the buffers (torch is used for device memory only).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWORKSPACE", 4: "MOE_EHIP"}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("I", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run mixture_experts_expert_amd/build.py (or __graft_entry__.build())")
+lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "moe_workspace_bytes": ([moe_shape], ctypes.c_size_t),
+    "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "moe_route": ([moe_shape, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_permute": ([moe_shape, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_grouped_gemm_fwd": ([moe_shape, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_combine": ([moe_shape, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_combine_bwd": ([moe_shape, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_grouped_gemm_bwd": ([moe_shape, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P,
+                              ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_unpermute_sum": ([moe_shape, _P, _P, _P, _P], ctypes.c_int),
+    "moe_route_bwd": ([moe_shape, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_gemm_gate_up": ([moe_shape, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_gemm_down": ([moe_shape, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_gemm_down_dgrad": ([moe_shape, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_gemm_down_wgrad": ([moe_shape, _P, _P, _P, _P, ctypes.c_int, _P], ctypes.c_int),
+    "moe_gemm_gate_up_dgrad": ([moe_shape, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_gemm_gate_up_wgrad": ([moe_shape, _P, _P, _P, _P, _P, ctypes.c_int, _P], ctypes.c_int),
+}
+for _name, (_args, _ret) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _ret
+
+
+def shape(T: int, H: int, E: int, k: int, I: int, dtype) -> moe_shape:
+    if dtype in (torch.bfloat16, "bf16", MOE_BF16):
+        dt = MOE_BF16
+    elif dtype in (torch.float32, "f32", MOE_F32):
+        dt = MOE_F32
+    else:
+        dt = int(dtype)  # passed through; the library rejects unknown codes
+    return moe_shape(T, H, E, k, I, dt)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise MoEError(fn, rc, lib.moe_status_string(rc).decode())
+
+
+def moe_workspace_bytes(s: moe_shape) -> int:
+    return int(lib.moe_workspace_bytes(s))
+
+
+def moe_status_string(status: int) -> str:
+    return lib.moe_status_string(status).decode()
+
+
+def moe_route(s, x, w_router, logit_bias, logits, topk_idx, topk_w, stream=None):
+    _check("moe_route", lib.moe_route(s, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(logits), _ptr(topk_idx),
+                                      _ptr(topk_w), _stream(stream)))
+
+
+def moe_permute(s, topk_idx, x, counts, offsets, sorted_to_flat, flat_to_sorted, x_perm, ws, ws_bytes=None,
+                stream=None):
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_permute", lib.moe_permute(s, _ptr(topk_idx), _ptr(x), _ptr(counts), _ptr(offsets),
+                                          _ptr(sorted_to_flat), _ptr(flat_to_sorted), _ptr(x_perm), _ptr(ws), nb,
+                                          _stream(stream)))
+
+
+def moe_grouped_gemm_fwd(s, x_perm, offsets, w_gate, w_up, w_down, g, u, a, o_perm, ws=None, ws_bytes=0,
+                         stream=None):
+    _check("moe_grouped_gemm_fwd", lib.moe_grouped_gemm_fwd(
+        s, _ptr(x_perm), _ptr(offsets), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(g), _ptr(u), _ptr(a),
+        _ptr(o_perm), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_combine(s, o_perm, topk_w, flat_to_sorted, y, stream=None):
+    _check("moe_combine", lib.moe_combine(s, _ptr(o_perm), _ptr(topk_w), _ptr(flat_to_sorted), _ptr(y),
+                                          _stream(stream)))
+
+
+def moe_combine_bwd(s, dy, o_perm, topk_w, flat_to_sorted, do_perm, d_topk_w, stream=None):
+    _check("moe_combine_bwd", lib.moe_combine_bwd(s, _ptr(dy), _ptr(o_perm), _ptr(topk_w), _ptr(flat_to_sorted),
+                                                  _ptr(do_perm), _ptr(d_topk_w), _stream(stream)))
+
+
+def moe_grouped_gemm_bwd(s, do_perm, x_perm, g, u, a, offsets, w_gate, w_up, w_down, dx_perm, dw_gate, dw_up,
+                         dw_down, accumulate_dw, ws, ws_bytes=None, stream=None):
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_grouped_gemm_bwd", lib.moe_grouped_gemm_bwd(
+        s, _ptr(do_perm), _ptr(x_perm), _ptr(g), _ptr(u), _ptr(a), _ptr(offsets), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), _ptr(dx_perm), _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), int(accumulate_dw), _ptr(ws), nb,
+        _stream(stream)))
+
+
+def moe_unpermute_sum(s, dx_perm, flat_to_sorted, dx, stream=None):
+    _check("moe_unpermute_sum", lib.moe_unpermute_sum(s, _ptr(dx_perm), _ptr(flat_to_sorted), _ptr(dx),
+                                                      _stream(stream)))
+
+
+def moe_route_bwd(s, d_topk_w, topk_w, topk_idx, d_logits, stream=None):
+    _check("moe_route_bwd", lib.moe_route_bwd(s, _ptr(d_topk_w), _ptr(topk_w), _ptr(topk_idx), _ptr(d_logits),
+                                              _stream(stream)))
+
+
+def moe_gemm_gate_up(s, x_perm, offsets, w_gate, w_up, g, u, a, stream=None):
+    _check("moe_gemm_gate_up", lib.moe_gemm_gate_up(s, _ptr(x_perm), _ptr(offsets), _ptr(w_gate), _ptr(w_up),
+                                                    _ptr(g), _ptr(u), _ptr(a), _stream(stream)))
+
+
+def moe_gemm_down(s, a, offsets, w_down, o_perm, stream=None):
+    _check("moe_gemm_down", lib.moe_gemm_down(s, _ptr(a), _ptr(offsets), _ptr(w_down), _ptr(o_perm),
+                                              _stream(stream)))
+
+
+def moe_gemm_down_dgrad(s, do_perm, offsets, w_down, g, u, dgu, stream=None):
+    _check("moe_gemm_down_dgrad", lib.moe_gemm_down_dgrad(s, _ptr(do_perm), _ptr(offsets), _ptr(w_down), _ptr(g),
+                                                          _ptr(u), _ptr(dgu), _stream(stream)))
+
+
+def moe_gemm_down_wgrad(s, do_perm, a, offsets, dw_down, accumulate_dw=0, stream=None):
+    _check("moe_gemm_down_wgrad", lib.moe_gemm_down_wgrad(s, _ptr(do_perm), _ptr(a), _ptr(offsets), _ptr(dw_down),
+                                                          int(accumulate_dw), _stream(stream)))
+
+
+def moe_gemm_gate_up_dgrad(s, dgu, offsets, w_gate, w_up, dx_perm, stream=None):
+    _check("moe_gemm_gate_up_dgrad", lib.moe_gemm_gate_up_dgrad(s, _ptr(dgu), _ptr(offsets), _ptr(w_gate),
+                                                                _ptr(w_up), _ptr(dx_perm), _stream(stream)))
+
+
+def moe_gemm_gate_up_wgrad(s, dgu, x_perm, offsets, dw_gate, dw_up, accumulate_dw=0, stream=None):
+    _check("moe_gemm_gate_up_wgrad", lib.moe_gemm_gate_up_wgrad(s, _ptr(dgu), _ptr(x_perm), _ptr(offsets),
+                                                                _ptr(dw_gate), _ptr(dw_up), int(accumulate_dw),
+                                                                _stream(stream)))
+
+
+class MoEStage:
+    """Buffers and call order of one MoE layer's expert stage on one GPU.
+
+    ``weights``: x-independent tensors on the device: w_router [E,H],
+    w_gate/w_up [E,I,H], w_down [E,H,I] (dtype), optional logit_bias [E]
+    float32. ``forward(x)`` and ``backward(dy)`` enqueue the library calls on
+    the current stream and return views of the held buffers (overwritten by
+    the next call).
+    """
+
+    def __init__(self, T: int, H: int, E: int, k: int, I: int, dtype: torch.dtype, device="cuda"):
+        self.T, self.H, self.E, self.k, self.I, self.dtype = T, H, E, k, I, dtype
+        self.s = shape(T, H, E, k, I, dtype)
+        M = T * k
+        dev = torch.device(device)
+        f32, i32 = torch.float32, torch.int32
+        e = lambda *sz, dt=dtype: torch.empty(*sz, dtype=dt, device=dev)  # noqa: E731
+        self.buf: Dict[str, torch.Tensor] = {
+            "logits": e(T, E, dt=f32), "topk_idx": e(T, k, dt=i32), "topk_w": e(T, k, dt=f32),
+            "counts": e(E, dt=i32), "offsets": e(E + 1, dt=i32), "sorted_to_flat": e(M, dt=i32),
+            "flat_to_sorted": e(M, dt=i32), "x_perm": e(M, H), "g": e(M, I), "u": e(M, I), "a": e(M, I),
+            "o_perm": e(M, H), "y": e(T, H),
+        }
+        ws_bytes = moe_workspace_bytes(self.s)
+        if ws_bytes == 0:
+            raise MoEError("moe_workspace_bytes", 1, "shape rejected")
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        self._bwd_ready = False
+
+    def _alloc_bwd(self):
+        if self._bwd_ready:
+            return
+        T, H, E, k, I, dt = self.T, self.H, self.E, self.k, self.I, self.dtype
+        dev = self.ws.device
+        M = T * k
+        f32 = torch.float32
+        self.buf.update({
+            "do_perm": torch.empty(M, H, dtype=dt, device=dev), "d_topk_w": torch.empty(T, k, dtype=f32, device=dev),
+            "dx_perm": torch.empty(M, H, dtype=dt, device=dev), "dx": torch.empty(T, H, dtype=dt, device=dev),
+            "dw_gate": torch.empty(E, I, H, dtype=f32, device=dev), "dw_up": torch.empty(E, I, H, dtype=f32, device=dev),
+            "dw_down": torch.empty(E, H, I, dtype=f32, device=dev), "d_logits": torch.empty(T, E, dtype=f32, device=dev),
+        })
+        self._bwd_ready = True
+
+    def forward(self, x, w_router, w_gate, w_up, w_down, logit_bias=None, stream=None):
+        b, s = self.buf, self.s
+        self.w = (w_gate, w_up, w_down)
+        moe_route(s, x, w_router, logit_bias, b["logits"], b["topk_idx"], b["topk_w"], stream)
+        moe_permute(s, b["topk_idx"], x, b["counts"], b["offsets"], b["sorted_to_flat"], b["flat_to_sorted"],
+                    b["x_perm"], self.ws, stream=stream)
+        moe_grouped_gemm_fwd(s, b["x_perm"], b["offsets"], w_gate, w_up, w_down, b["g"], b["u"], b["a"],
+                             b["o_perm"], stream=stream)
+        moe_combine(s, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["y"], stream)
+        return b["y"]
+
+    def backward(self, dy, accumulate_dw: bool = False, stream=None):
+        self._alloc_bwd()
+        b, s = self.buf, self.s
+        w_gate, w_up, w_down = self.w
+        moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["do_perm"], b["d_topk_w"], stream)
+        moe_grouped_gemm_bwd(s, b["do_perm"], b["x_perm"], b["g"], b["u"], b["a"], b["offsets"], w_gate, w_up,
+                             w_down, b["dx_perm"], b["dw_gate"], b["dw_up"], b["dw_down"], int(accumulate_dw),
+                             self.ws, stream=stream)
+        moe_unpermute_sum(s, b["dx_perm"], b["flat_to_sorted"], b["dx"], stream)
+        moe_route_bwd(s, b["d_topk_w"], b["topk_w"], b["topk_idx"], b["d_logits"], stream)
+        return b["dx"]

@@ -1,0 +1,221 @@
+// C ABI of libmoe: argument checks on the host, then kernel launches.
+// Every check runs before any HIP call, so a rejected call enqueues nothing.
+#include <limits.h>
+
+#include "moe_internal.h"
+
+using moe::WsLayout;
+
+namespace {
+
+// Shape checks shared by every entry point.
+moe_status check_shape(const moe_shape& s) {
+  if (s.T <= 0 || s.H <= 0 || s.E <= 0 || s.k <= 0 || s.I <= 0) return MOE_EINVAL;
+  if (s.k > s.E || s.E > 1024) return MOE_EINVAL;
+  if (static_cast<int64_t>(s.T) * s.k >= (static_cast<int64_t>(1) << 31)) return MOE_EINVAL;
+  if (s.dtype != MOE_F32 && s.dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (s.H % 64 != 0 || s.I % 64 != 0) return MOE_EUNSUPPORTED;
+  // Element offsets inside one expert's weights and one row block stay int32.
+  if (static_cast<int64_t>(s.E) * s.I * s.H >= (static_cast<int64_t>(1) << 31)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+template <class... P>
+bool any_null(P... p) {
+  return ((p == nullptr) || ...);
+}
+
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(moe_shape s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return moe::ws_layout(s).total;
+}
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: shape or dtype not supported";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP launch failed";
+  }
+  return "unknown moe_status";
+}
+
+moe_status moe_route(moe_shape s, const void* x, const void* w_router, const float* logit_bias, float* logits,
+                     int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(x, w_router, logits, topk_idx, topk_w)) return MOE_EINVAL;
+  return from_hip(moe::launch_route(s, x, w_router, logit_bias, logits, topk_idx, topk_w, stream));
+}
+
+moe_status moe_permute(moe_shape s, const int32_t* topk_idx, const void* x, int32_t* counts, int32_t* offsets,
+                       int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_perm, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(topk_idx, x, counts, offsets, sorted_to_flat, flat_to_sorted, x_perm, ws)) return MOE_EINVAL;
+  if (ws_bytes < moe::ws_layout(s).total) return MOE_EWORKSPACE;
+  return from_hip(moe::launch_permute(s, topk_idx, x, counts, offsets, sorted_to_flat, flat_to_sorted, x_perm, ws,
+                                      stream));
+}
+
+moe_status moe_gemm_gate_up(moe_shape s, const void* x_perm, const int32_t* offsets, const void* w_gate,
+                            const void* w_up, void* g, void* u, void* a, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(x_perm, offsets, w_gate, w_up, g, u, a)) return MOE_EINVAL;
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = x_perm;
+  ga.b0 = w_gate;
+  ga.b1 = w_up;
+  ga.out0 = g;
+  ga.out1 = u;
+  ga.out2 = a;
+  return from_hip(moe::launch_gemm(moe::GEMM_GATEUP, s, ga, stream));
+}
+
+moe_status moe_gemm_down(moe_shape s, const void* a, const int32_t* offsets, const void* w_down, void* o_perm,
+                         hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(a, offsets, w_down, o_perm)) return MOE_EINVAL;
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = a;
+  ga.b0 = w_down;
+  ga.out0 = o_perm;
+  return from_hip(moe::launch_gemm(moe::GEMM_DOWN, s, ga, stream));
+}
+
+moe_status moe_gemm_down_dgrad(moe_shape s, const void* do_perm, const int32_t* offsets, const void* w_down,
+                               const void* g, const void* u, void* dgu, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(do_perm, offsets, w_down, g, u, dgu)) return MOE_EINVAL;
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = do_perm;
+  ga.b0 = w_down;
+  ga.g_in = g;
+  ga.u_in = u;
+  ga.out0 = dgu;
+  return from_hip(moe::launch_gemm(moe::GEMM_DGRAD_DOWN, s, ga, stream));
+}
+
+moe_status moe_gemm_down_wgrad(moe_shape s, const void* do_perm, const void* a, const int32_t* offsets,
+                               float* dw_down, int accumulate_dw, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(do_perm, a, offsets, dw_down)) return MOE_EINVAL;
+  if (accumulate_dw != 0 && accumulate_dw != 1) return MOE_EINVAL;
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = do_perm;
+  ga.b0 = a;
+  ga.dw0 = dw_down;
+  ga.accumulate = accumulate_dw;
+  return from_hip(moe::launch_gemm(moe::GEMM_WGRAD_DOWN, s, ga, stream));
+}
+
+moe_status moe_gemm_gate_up_dgrad(moe_shape s, const void* dgu, const int32_t* offsets, const void* w_gate,
+                                  const void* w_up, void* dx_perm, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(dgu, offsets, w_gate, w_up, dx_perm)) return MOE_EINVAL;
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = dgu;
+  ga.b0 = w_gate;
+  ga.b1 = w_up;
+  ga.out0 = dx_perm;
+  return from_hip(moe::launch_gemm(moe::GEMM_DGRAD_GATEUP, s, ga, stream));
+}
+
+moe_status moe_gemm_gate_up_wgrad(moe_shape s, const void* dgu, const void* x_perm, const int32_t* offsets,
+                                  float* dw_gate, float* dw_up, int accumulate_dw, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(dgu, x_perm, offsets, dw_gate, dw_up)) return MOE_EINVAL;
+  if (accumulate_dw != 0 && accumulate_dw != 1) return MOE_EINVAL;
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = dgu;
+  ga.b0 = x_perm;
+  ga.dw0 = dw_gate;
+  ga.dw1 = dw_up;
+  ga.accumulate = accumulate_dw;
+  return from_hip(moe::launch_gemm(moe::GEMM_WGRAD_GATEUP, s, ga, stream));
+}
+
+moe_status moe_grouped_gemm_fwd(moe_shape s, const void* x_perm, const int32_t* offsets, const void* w_gate,
+                                const void* w_up, const void* w_down, void* g, void* u, void* a, void* o_perm,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(x_perm, offsets, w_gate, w_up, w_down, g, u, a, o_perm)) return MOE_EINVAL;
+  st = moe_gemm_gate_up(s, x_perm, offsets, w_gate, w_up, g, u, a, stream);
+  if (st != MOE_OK) return st;
+  return moe_gemm_down(s, a, offsets, w_down, o_perm, stream);
+}
+
+moe_status moe_combine(moe_shape s, const void* o_perm, const float* topk_w, const int32_t* flat_to_sorted,
+                       void* y, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(o_perm, topk_w, flat_to_sorted, y)) return MOE_EINVAL;
+  return from_hip(moe::launch_combine(s, o_perm, topk_w, flat_to_sorted, y, stream));
+}
+
+moe_status moe_combine_bwd(moe_shape s, const void* dy, const void* o_perm, const float* topk_w,
+                           const int32_t* flat_to_sorted, void* do_perm, float* d_topk_w, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(dy, o_perm, topk_w, flat_to_sorted, do_perm, d_topk_w)) return MOE_EINVAL;
+  return from_hip(moe::launch_combine_bwd(s, dy, o_perm, topk_w, flat_to_sorted, do_perm, d_topk_w, stream));
+}
+
+moe_status moe_grouped_gemm_bwd(moe_shape s, const void* do_perm, const void* x_perm, const void* g, const void* u,
+                                const void* a, const int32_t* offsets, const void* w_gate, const void* w_up,
+                                const void* w_down, void* dx_perm, float* dw_gate, float* dw_up, float* dw_down,
+                                int accumulate_dw, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(do_perm, x_perm, g, u, a, offsets, w_gate, w_up, w_down, dx_perm, dw_gate, dw_up, dw_down, ws))
+    return MOE_EINVAL;
+  if (accumulate_dw != 0 && accumulate_dw != 1) return MOE_EINVAL;
+  const WsLayout l = moe::ws_layout(s);
+  if (ws_bytes < l.total) return MOE_EWORKSPACE;
+  void* dgu = static_cast<char*>(ws) + l.dgu_off;
+  if ((st = moe_gemm_down_dgrad(s, do_perm, offsets, w_down, g, u, dgu, stream)) != MOE_OK) return st;
+  if ((st = moe_gemm_down_wgrad(s, do_perm, a, offsets, dw_down, accumulate_dw, stream)) != MOE_OK) return st;
+  if ((st = moe_gemm_gate_up_dgrad(s, dgu, offsets, w_gate, w_up, dx_perm, stream)) != MOE_OK) return st;
+  return moe_gemm_gate_up_wgrad(s, dgu, x_perm, offsets, dw_gate, dw_up, accumulate_dw, stream);
+}
+
+moe_status moe_unpermute_sum(moe_shape s, const void* dx_perm, const int32_t* flat_to_sorted, void* dx,
+                             hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(dx_perm, flat_to_sorted, dx)) return MOE_EINVAL;
+  return from_hip(moe::launch_unpermute_sum(s, dx_perm, flat_to_sorted, dx, stream));
+}
+
+moe_status moe_route_bwd(moe_shape s, const float* d_topk_w, const float* topk_w, const int32_t* topk_idx,
+                         float* d_logits, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(d_topk_w, topk_w, topk_idx, d_logits)) return MOE_EINVAL;
+  return from_hip(moe::launch_route_bwd(s, d_topk_w, topk_w, topk_idx, d_logits, stream));
+}
+
+}  // extern "C"

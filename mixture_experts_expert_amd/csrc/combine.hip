@@ -1,0 +1,150 @@
+// Weighted combine (forward), its backward, and the unpermute-sum.
+//
+// The combine follows modelopt.torch.utils.moe, a2a_moe: a token's k expert
+// results are weighted by its routing weights in the weights' own precision
+// (fp32 here) and summed, then returned in the hidden dtype. One wavefront
+// handles one token; each lane owns 16-byte column chunks, so every row read
+// and the output row write are contiguous across the wavefront.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / kWave;
+
+template <class T> struct Vec;
+template <> struct Vec<float> {
+  static constexpr int N = 4;  // elements per 16-byte chunk
+  __device__ __forceinline__ static void unpack(const uint4& v, float* o) {
+    o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+  }
+  __device__ __forceinline__ static uint4 pack(const float* o) {
+    return make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3]));
+  }
+};
+template <> struct Vec<bf16_t> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void unpack(const uint4& v, float* o) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static uint4 pack(const float* o) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16(o[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(o[2 * i + 1])) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+// y[t] = sum_j w[t,j] * o_perm[f2s[t*k+j]]   (WEIGHTED)   or   sum_j src[f2s[t*k+j]]
+template <class T, bool WEIGHTED>
+__global__ __launch_bounds__(kThreads) void gather_sum_kernel(int Tn, int k, int chunks,
+                                                              const uint4* __restrict__ src,
+                                                              const float* __restrict__ w,
+                                                              const int32_t* __restrict__ f2s,
+                                                              uint4* __restrict__ out) {
+  constexpr int N = Vec<T>::N;
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (t >= Tn) return;
+  const int64_t tk = static_cast<int64_t>(t) * k;
+  for (int c = lane; c < chunks; c += kWave) {
+    float acc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int64_t p = f2s[tk + j];
+      float v[N];
+      Vec<T>::unpack(src[p * chunks + c], v);
+      if (WEIGHTED) {
+        const float wj = w[tk + j];
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc[i] += wj * v[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc[i] += v[i];
+      }
+    }
+    out[static_cast<int64_t>(t) * chunks + c] = Vec<T>::pack(acc);
+  }
+}
+
+// do_perm[p] = w[t,j] * dy[t];  gw[t,j] = <dy[t], o_perm[p]>,  p = f2s[t*k+j]
+template <class T>
+__global__ __launch_bounds__(kThreads) void combine_bwd_kernel(int Tn, int k, int chunks,
+                                                               const uint4* __restrict__ dy,
+                                                               const uint4* __restrict__ o_perm,
+                                                               const float* __restrict__ w,
+                                                               const int32_t* __restrict__ f2s,
+                                                               uint4* __restrict__ do_perm,
+                                                               float* __restrict__ gw) {
+  constexpr int N = Vec<T>::N;
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (t >= Tn) return;  // wave-uniform: no block barrier in this kernel
+  const int64_t tk = static_cast<int64_t>(t) * k;
+  for (int j = 0; j < k; ++j) {
+    const int64_t p = f2s[tk + j];
+    const float wj = w[tk + j];
+    float dot = 0.0f;
+    for (int c = lane; c < chunks; c += kWave) {
+      float d[N], o[N], g[N];
+      Vec<T>::unpack(dy[static_cast<int64_t>(t) * chunks + c], d);
+      Vec<T>::unpack(o_perm[p * chunks + c], o);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        g[i] = wj * d[i];
+        dot += d[i] * o[i];
+      }
+      do_perm[p * chunks + c] = Vec<T>::pack(g);
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) gw[tk + j] = dot;
+  }
+}
+
+template <class T, bool WEIGHTED>
+hipError_t gather_sum(const moe_shape& s, const void* src, const float* w, const int32_t* f2s, void* out,
+                      hipStream_t st) {
+  const int chunks = s.H / Vec<T>::N;
+  gather_sum_kernel<T, WEIGHTED><<<ceil_div(s.T, kWavesPerBlock), kThreads, 0, st>>>(
+      s.T, s.k, chunks, static_cast<const uint4*>(src), w, f2s, static_cast<uint4*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_shape& s, const void* o_perm, const float* w, const int32_t* f2s, void* y,
+                          hipStream_t st) {
+  return s.dtype == MOE_BF16 ? gather_sum<bf16_t, true>(s, o_perm, w, f2s, y, st)
+                             : gather_sum<float, true>(s, o_perm, w, f2s, y, st);
+}
+
+hipError_t launch_unpermute_sum(const moe_shape& s, const void* dx_perm, const int32_t* f2s, void* dx,
+                                hipStream_t st) {
+  return s.dtype == MOE_BF16 ? gather_sum<bf16_t, false>(s, dx_perm, nullptr, f2s, dx, st)
+                             : gather_sum<float, false>(s, dx_perm, nullptr, f2s, dx, st);
+}
+
+hipError_t launch_combine_bwd(const moe_shape& s, const void* dy, const void* o_perm, const float* w,
+                              const int32_t* f2s, void* do_perm, float* gw, hipStream_t st) {
+  const dim3 grid(ceil_div(s.T, kWavesPerBlock));
+  if (s.dtype == MOE_BF16)
+    combine_bwd_kernel<bf16_t><<<grid, kThreads, 0, st>>>(
+        s.T, s.k, s.H / Vec<bf16_t>::N, static_cast<const uint4*>(dy), static_cast<const uint4*>(o_perm), w, f2s,
+        static_cast<uint4*>(do_perm), gw);
+  else
+    combine_bwd_kernel<float><<<grid, kThreads, 0, st>>>(
+        s.T, s.k, s.H / Vec<float>::N, static_cast<const uint4*>(dy), static_cast<const uint4*>(o_perm), w, f2s,
+        static_cast<uint4*>(do_perm), gw);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,131 @@
+// Internal declarations shared by the HIP sources of libmoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// ---------------------------------------------------------------------------
+// Element types. bf16 travels as raw uint16 bit patterns.
+// ---------------------------------------------------------------------------
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+// Round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <class T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static float to_f32(float v) { return v; }
+  __device__ __forceinline__ static float from_f32(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  __device__ __forceinline__ static float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static float to_f32(bf16_t v) { return bf16_to_f32(v); }
+  __device__ __forceinline__ static bf16_t from_f32(float v) { return f32_to_bf16(v); }
+};
+
+__device__ __forceinline__ float sigmoidf_dev(float g) { return 1.0f / (1.0f + expf(-g)); }
+
+// Wave-wide sum (butterfly over the 64 lanes).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Permute workspace layout (bytes from the start of ws).
+// ---------------------------------------------------------------------------
+constexpr int kPermBlock = 1024;  // (token, slot) entries per indexing block
+
+struct WsLayout {
+  size_t hist_off;   // int32 [nblocks][E] per-block counts, then per-block bases
+  size_t hist_bytes;
+  size_t dgu_off;    // dtype [T*k][2I]: dG | dU for the backward
+  size_t dgu_bytes;
+  size_t total;
+};
+
+WsLayout ws_layout(const moe_shape& s);
+
+// ---------------------------------------------------------------------------
+// Launchers (each returns hipGetLastError() after enqueueing).
+// ---------------------------------------------------------------------------
+hipError_t launch_route(const moe_shape& s, const void* x, const void* wr, const float* bias, float* logits,
+                        int32_t* idx, float* w, hipStream_t st);
+hipError_t launch_route_bwd(const moe_shape& s, const float* gw, const float* w, const int32_t* idx,
+                            float* d_logits, hipStream_t st);
+hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const void* x, int32_t* counts,
+                          int32_t* offsets, int32_t* s2f, int32_t* f2s, void* x_perm, void* ws,
+                          hipStream_t st);
+hipError_t launch_combine(const moe_shape& s, const void* o_perm, const float* w, const int32_t* f2s, void* y,
+                          hipStream_t st);
+hipError_t launch_combine_bwd(const moe_shape& s, const void* dy, const void* o_perm, const float* w,
+                              const int32_t* f2s, void* do_perm, float* gw, hipStream_t st);
+hipError_t launch_unpermute_sum(const moe_shape& s, const void* dx_perm, const int32_t* f2s, void* dx,
+                                hipStream_t st);
+
+// The six grouped GEMMs of the stage. Operand roles per mode (all row-major,
+// rows sorted by expert; dgu is [T*k, 2I] with dG in columns [0, I) and dU in
+// [I, 2I)):
+//   GEMM_GATEUP        a = x_perm,  b0 = w_gate, b1 = w_up  -> out0 = g, out1 = u, out2 = a
+//   GEMM_DOWN          a = act,     b0 = w_down             -> out0 = o_perm
+//   GEMM_DGRAD_DOWN    a = do_perm, b0 = w_down, g_in, u_in -> out0 = dgu
+//   GEMM_DGRAD_GATEUP  a = dgu,     b0 = w_gate, b1 = w_up  -> out0 = dx_perm
+//   GEMM_WGRAD_DOWN    a = do_perm, b0 = act                -> dw0 = dw_down
+//   GEMM_WGRAD_GATEUP  a = dgu,     b0 = x_perm             -> dw0 = dw_gate, dw1 = dw_up
+enum GemmMode : int {
+  GEMM_GATEUP = 0,
+  GEMM_DOWN = 1,
+  GEMM_DGRAD_DOWN = 2,
+  GEMM_DGRAD_GATEUP = 3,
+  GEMM_WGRAD_DOWN = 4,
+  GEMM_WGRAD_GATEUP = 5
+};
+
+struct GemmArgs {
+  const int32_t* offsets;
+  const void* a;
+  const void* b0;
+  const void* b1;
+  const void* g_in;
+  const void* u_in;
+  void* out0;
+  void* out1;
+  void* out2;
+  float* dw0;
+  float* dw1;
+  int accumulate;
+};
+
+hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_f32(GemmMode mode, const moe_shape& s, const GemmArgs& a, hipStream_t st);
+
+inline hipError_t launch_gemm(GemmMode mode, const moe_shape& s, const GemmArgs& a, hipStream_t st) {
+  return s.dtype == MOE_BF16 ? launch_gemm_bf16(mode, s, a, st) : launch_gemm_f32(mode, s, a, st);
+}
+
+}  // namespace moe

@@ -1,0 +1,188 @@
+// Expert indexing and gather: counts, offsets, the stable permutation of the
+// T*k (token, slot) pairs by expert, and the gather of x into that order.
+//
+// The stable counting sort (unsloth PR #3812, review suggestion: a stable
+// argsort of the flattened expert ids plus a bincount) runs in three passes
+// over fixed blocks of kPermBlock pairs, with no atomics on positions:
+//   1. per-block expert histograms (LDS integer atomics; counts only),
+//   2. one block scans each expert's column of block counts (block bases and
+//      counts) and the counts themselves (offsets),
+//   3. each block ranks its pairs in flat order: inside a wavefront the pairs
+//      with the same expert are found by one ballot per bit of the expert id,
+//      and a pair's rank is the number of such lanes below it; wavefronts and
+//      chunks are ordered through per-expert counters in LDS.
+// The position of pair f is offsets[e] + (pairs of expert e in earlier
+// blocks) + (rank inside its block): the definition of the stable order.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kScanThreads = 1024;
+constexpr int kSlabInts = 8192;  // block counts staged in LDS per scan step
+
+__device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
+
+__global__ __launch_bounds__(kThreads) void block_hist_kernel(int n, int E, const int32_t* __restrict__ idx,
+                                                              int32_t* __restrict__ hist) {
+  __shared__ int32_t h[1024];
+  for (int e = threadIdx.x; e < E; e += kThreads) h[e] = 0;
+  __syncthreads();
+  const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kPermBlock;
+  for (int i = threadIdx.x; i < kPermBlock; i += kThreads) {
+    const int64_t f = f0 + i;
+    if (f < n) atomicAdd(&h[clamp_expert(idx[f], E)], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) hist[static_cast<int64_t>(blockIdx.x) * E + e] = h[e];
+}
+
+// One block. Column scan of hist[nb][E] in place (exclusive: pairs of expert
+// e in earlier blocks), counts[e] = column total, offsets = exclusive scan of
+// counts.
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(int nb, int E, int32_t* __restrict__ hist,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets) {
+  __shared__ int32_t slab[kSlabInts];
+  __shared__ int32_t part[kScanThreads];
+  const int tid = threadIdx.x;
+  const int rows_per_slab = kSlabInts / E;  // >= 8 since E <= 1024
+  int32_t running = 0;                      // thread e < E owns column e
+  for (int b0 = 0; b0 < nb; b0 += rows_per_slab) {
+    const int rows = min(rows_per_slab, nb - b0);
+    const int64_t base = static_cast<int64_t>(b0) * E;
+    for (int q = tid; q < rows * E; q += kScanThreads) slab[q] = hist[base + q];
+    __syncthreads();
+    if (tid < E) {
+      for (int r = 0; r < rows; ++r) {
+        const int32_t c = slab[r * E + tid];
+        slab[r * E + tid] = running;
+        running += c;
+      }
+    }
+    __syncthreads();
+    for (int q = tid; q < rows * E; q += kScanThreads) hist[base + q] = slab[q];
+    __syncthreads();
+  }
+  // Exclusive scan of the E column totals (Hillis-Steele over the block).
+  part[tid] = tid < E ? running : 0;
+  __syncthreads();
+  for (int o = 1; o < kScanThreads; o <<= 1) {
+    const int32_t v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) {
+    counts[tid] = running;
+    offsets[tid] = part[tid] - running;
+  }
+  if (tid == E - 1) offsets[E] = part[tid];
+}
+
+constexpr int kWavesPerBlock = kThreads / kWave;
+
+__global__ __launch_bounds__(kThreads) void rank_scatter_kernel(int n, int E, int nbits,
+                                                                const int32_t* __restrict__ idx,
+                                                                const int32_t* __restrict__ hist_base,
+                                                                const int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ s2f,
+                                                                int32_t* __restrict__ f2s) {
+  __shared__ int32_t running[1024];
+  __shared__ int32_t wcount[kWavesPerBlock][1024];
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wv = tid / kWave;
+  for (int e = tid; e < E; e += kThreads) {
+    running[e] = offsets[e] + hist_base[static_cast<int64_t>(blockIdx.x) * E + e];
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) wcount[w][e] = 0;
+  }
+  __syncthreads();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kPermBlock;
+  for (int c0 = 0; c0 < kPermBlock; c0 += kThreads) {
+    const int64_t f = f0 + c0 + tid;
+    const bool valid = f < n;
+    const int e = valid ? clamp_expert(idx[f], E) : 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t ones = __ballot(valid && bit);
+      peers &= bit ? ones : ~ones;
+    }
+    const int rank = __popcll(peers & below);
+    if (valid && rank == 0) wcount[wv][e] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      int32_t pos = running[e] + rank;
+      for (int w = 0; w < wv; ++w) pos += wcount[w][e];
+      s2f[pos] = static_cast<int32_t>(f);
+      f2s[f] = pos;
+    }
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += kThreads) {
+      int32_t add = 0;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) {
+        add += wcount[w][ee];
+        wcount[w][ee] = 0;
+      }
+      running[ee] += add;
+    }
+    __syncthreads();
+  }
+}
+
+// x_perm[p, :] = x[s2f[p] / k, :] with 16-byte copies; one wavefront per row.
+__global__ __launch_bounds__(kThreads) void gather_kernel(int64_t rows, int k, int chunks_per_row,
+                                                          const int32_t* __restrict__ s2f,
+                                                          const uint4* __restrict__ x, uint4* __restrict__ x_perm) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
+  if (p >= rows) return;
+  const int64_t src = static_cast<int64_t>(s2f[p] / k) * chunks_per_row;
+  const int64_t dst = p * chunks_per_row;
+  for (int c = lane; c < chunks_per_row; c += kWave) x_perm[dst + c] = x[src + c];
+}
+
+}  // namespace
+
+WsLayout ws_layout(const moe_shape& s) {
+  WsLayout l{};
+  const int64_t n = static_cast<int64_t>(s.T) * s.k;
+  const int64_t nb = ceil_div64(n, kPermBlock);
+  const size_t esz = s.dtype == MOE_BF16 ? 2 : 4;
+  l.hist_off = 0;
+  l.hist_bytes = static_cast<size_t>(nb) * s.E * sizeof(int32_t);
+  l.dgu_off = (l.hist_bytes + 255) & ~static_cast<size_t>(255);
+  l.dgu_bytes = static_cast<size_t>(n) * 2 * s.I * esz;
+  l.total = l.dgu_off + l.dgu_bytes;
+  return l;
+}
+
+hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const void* x, int32_t* counts,
+                          int32_t* offsets, int32_t* s2f, int32_t* f2s, void* x_perm, void* ws,
+                          hipStream_t st) {
+  const int n = s.T * s.k;
+  const int nb = ceil_div(n, kPermBlock);
+  int32_t* hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ws_layout(s).hist_off);
+  int nbits = 0;
+  while ((1 << nbits) < s.E) ++nbits;
+  block_hist_kernel<<<nb, kThreads, 0, st>>>(n, s.E, idx, hist);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  scan_kernel<<<1, kScanThreads, 0, st>>>(nb, s.E, hist, counts, offsets);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  rank_scatter_kernel<<<nb, kThreads, 0, st>>>(n, s.E, nbits, idx, hist, offsets, s2f, f2s);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int esz = s.dtype == MOE_BF16 ? 2 : 4;
+  const int chunks = s.H * esz / 16;
+  gather_kernel<<<ceil_div(n, kWavesPerBlock), kThreads, 0, st>>>(n, s.k, chunks, s2f,
+                                                                  static_cast<const uint4*>(x),
+                                                                  static_cast<uint4*>(x_perm));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,205 @@
+// Router kernels: logits, top-k + softmax + renormalisation, and the
+// backward of the routing weights.
+//
+// The logits feed an integer decision (which experts a token goes to), so
+// they are computed in a fixed order that a CPU can reproduce bit for bit: one
+// fp32 fma chain per (token, expert) over h ascending from +0, then + bias.
+// The chain runs on the vector ALUs; a matrix-core accumulation order is not
+// specified and could not be matched. The work is register-tiled so each
+// thread keeps 16 independent chains in flight.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRT = 4;           // tokens per thread
+constexpr int kRE = 4;           // experts per thread
+constexpr int kTy = 8, kTx = 16; // thread grid of a block
+constexpr int kTileT = kTy * kRT;  // 32 tokens per block
+constexpr int kTileE = kTx * kRE;  // 64 experts per block
+constexpr int kHC = 64;            // h values staged per step
+constexpr int kLogitThreads = kTy * kTx;  // 128
+
+template <class T>
+__global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(int Tn, int H, int E, const T* __restrict__ x,
+                                                                      const T* __restrict__ wr,
+                                                                      const float* __restrict__ bias,
+                                                                      float* __restrict__ logits) {
+  __shared__ float xs[kHC][kTileT];  // [h][token]
+  __shared__ float ws[kHC][kTileE];  // [h][expert]
+  const int tid = threadIdx.x;
+  const int ty = tid / kTx, tx = tid % kTx;
+  const int t0 = blockIdx.x * kTileT;
+  const int e0 = blockIdx.y * kTileE;
+
+  float acc[kRT][kRE];
+#pragma unroll
+  for (int i = 0; i < kRT; ++i)
+#pragma unroll
+    for (int j = 0; j < kRE; ++j) acc[i][j] = 0.0f;
+
+  for (int h0 = 0; h0 < H; h0 += kHC) {
+    // Stage x[t0:t0+32, h0:h0+64] and wr[e0:e0+64, h0:h0+64] as fp32,
+    // transposed to [h][row]. Rows past the end are zero (never stored).
+    for (int q = tid; q < kTileT * kHC; q += kLogitThreads) {
+      const int r = q / kHC, hh = q % kHC;
+      const int t = t0 + r;
+      xs[hh][r] = (t < Tn) ? Elem<T>::to_f32(x[static_cast<int64_t>(t) * H + h0 + hh]) : 0.0f;
+    }
+    for (int q = tid; q < kTileE * kHC; q += kLogitThreads) {
+      const int r = q / kHC, hh = q % kHC;
+      const int e = e0 + r;
+      ws[hh][r] = (e < E) ? Elem<T>::to_f32(wr[static_cast<int64_t>(e) * H + h0 + hh]) : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int hh = 0; hh < kHC; ++hh) {
+      const float4 xv = *reinterpret_cast<const float4*>(&xs[hh][ty * kRT]);
+      const float4 wv = *reinterpret_cast<const float4*>(&ws[hh][tx * kRE]);
+      const float xa[kRT] = {xv.x, xv.y, xv.z, xv.w};
+      const float wa[kRE] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int i = 0; i < kRT; ++i)
+#pragma unroll
+        for (int j = 0; j < kRE; ++j) acc[i][j] = __fmaf_rn(xa[i], wa[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < kRT; ++i) {
+    const int t = t0 + ty * kRT + i;
+    if (t >= Tn) continue;
+#pragma unroll
+    for (int j = 0; j < kRE; ++j) {
+      const int e = e0 + tx * kRE + j;
+      if (e >= E) continue;
+      float v = acc[i][j];
+      if (bias) v = v + bias[e];
+      logits[static_cast<int64_t>(t) * E + e] = v;
+    }
+  }
+}
+
+constexpr int kMaxPerLane = 1024 / kWave;  // E <= 1024
+constexpr int kTokPerBlock = 4;            // one wave per token
+
+// (value, index) order of the selection: larger value first, then lower index.
+__device__ __forceinline__ bool before(float v, int i, float ov, int oi) {
+  return v > ov || (v == ov && i < oi);
+}
+
+__global__ __launch_bounds__(kWave* kTokPerBlock) void router_topk_kernel(int Tn, int E, int k,
+                                                                          const float* __restrict__ logits,
+                                                                          int32_t* __restrict__ idx,
+                                                                          float* __restrict__ w) {
+  __shared__ float sval[kTokPerBlock][1024];
+  const int lane = threadIdx.x % kWave;
+  const int wv = threadIdx.x / kWave;
+  const int t = blockIdx.x * kTokPerBlock + wv;
+  // Every wave runs to the block barrier below; a wave past the last token
+  // works on -inf logits and stores nothing.
+  const bool active = t < Tn;
+  const float* l = logits + static_cast<int64_t>(active ? t : 0) * E;
+  const int nc = (E + kWave - 1) / kWave;
+
+  float v[kMaxPerLane];
+  uint32_t valid = 0;  // bit c: v[c] holds a logit of this token
+#pragma unroll
+  for (int c = 0; c < kMaxPerLane; ++c) {
+    const int e = lane + c * kWave;
+    const bool in = active && c < nc && e < E;
+    v[c] = in ? l[e] : -INFINITY;
+    if (in) valid |= 1u << c;
+  }
+  uint32_t taken = ~valid;  // bit c: v[c] already selected (or not a logit)
+
+  float vmax = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int c = 0; c < kMaxPerLane; ++c) {
+      if (taken & (1u << c)) continue;
+      const int e = lane + c * kWave;
+      if (before(v[c], e, bv, bi)) { bv = v[c]; bi = e; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      if (before(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    if (active && (bi % kWave) == lane) taken |= 1u << (bi / kWave);
+    if (active && lane == 0) {
+      idx[static_cast<int64_t>(t) * k + j] = bi;
+      sval[wv][j] = bv;
+    }
+    if (j == 0) vmax = bv;
+  }
+  // Softmax denominator over all E logits, shifted by the maximum.
+  float z = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kMaxPerLane; ++c)
+    if (valid & (1u << c)) z += expf(v[c] - vmax);
+  z = wave_sum(z);
+  __syncthreads();  // sval written by lane 0 becomes visible to its wave
+  if (!active) return;
+  float s = 0.0f;
+  for (int j = lane; j < k; j += kWave) s += expf(sval[wv][j] - vmax) / z;
+  s = wave_sum(s);
+  const float den = s + 1e-20f;
+  for (int j = lane; j < k; j += kWave)
+    w[static_cast<int64_t>(t) * k + j] = (expf(sval[wv][j] - vmax) / z) / den;
+}
+
+__global__ __launch_bounds__(kWave* kTokPerBlock) void router_bwd_kernel(int Tn, int E, int k,
+                                                                         const float* __restrict__ gw,
+                                                                         const float* __restrict__ w,
+                                                                         const int32_t* __restrict__ idx,
+                                                                         float* __restrict__ d_logits) {
+  __shared__ float row[kTokPerBlock][1024];
+  const int lane = threadIdx.x % kWave;
+  const int wv = threadIdx.x / kWave;
+  const int t = blockIdx.x * kTokPerBlock + wv;
+  const bool active = t < Tn;
+  const int64_t tk = static_cast<int64_t>(t) * k;
+  float gs = 0.0f;
+  if (active) {
+    for (int j = lane; j < k; j += kWave) gs += w[tk + j] * gw[tk + j];
+    for (int e = lane; e < E; e += kWave) row[wv][e] = 0.0f;
+  }
+  gs = wave_sum(gs);
+  __syncthreads();
+  if (active)
+    for (int j = lane; j < k; j += kWave) row[wv][idx[tk + j]] = w[tk + j] * (gw[tk + j] - gs);
+  __syncthreads();
+  if (active)
+    for (int e = lane; e < E; e += kWave) d_logits[static_cast<int64_t>(t) * E + e] = row[wv][e];
+}
+
+}  // namespace
+
+hipError_t launch_route(const moe_shape& s, const void* x, const void* wr, const float* bias, float* logits,
+                        int32_t* idx, float* w, hipStream_t st) {
+  dim3 grid(ceil_div(s.T, kTileT), ceil_div(s.E, kTileE));
+  if (s.dtype == MOE_BF16)
+    router_logits_kernel<bf16_t><<<grid, kLogitThreads, 0, st>>>(
+        s.T, s.H, s.E, static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(wr), bias, logits);
+  else
+    router_logits_kernel<float><<<grid, kLogitThreads, 0, st>>>(
+        s.T, s.H, s.E, static_cast<const float*>(x), static_cast<const float*>(wr), bias, logits);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  router_topk_kernel<<<ceil_div(s.T, kTokPerBlock), kWave * kTokPerBlock, 0, st>>>(s.T, s.E, s.k, logits, idx, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_bwd(const moe_shape& s, const float* gw, const float* w, const int32_t* idx,
+                            float* d_logits, hipStream_t st) {
+  router_bwd_kernel<<<ceil_div(s.T, kTokPerBlock), kWave * kTokPerBlock, 0, st>>>(s.T, s.E, s.k, gw, w, idx,
+                                                                                   d_logits);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -17,3 +17,17 @@ def pytest_configure(config):
 def oracle():
     from oracle import oracle as O
     return O
+
+
+def _ensure_built():
+    lib = os.path.join(ROOT, "mixture_experts_expert_amd", "libmoe.so")
+    if not os.path.exists(lib):
+        from mixture_experts_expert_amd import build
+        build.build()
+    olib = os.path.join(ROOT, "oracle", "liboracle.so")
+    if not os.path.exists(olib):
+        from oracle import build as obuild
+        obuild.build()
+
+
+_ensure_built()

@@ -1,0 +1,98 @@
+"""The C-ABI library loads, exports every entry point include/moe.h declares,
+and rejects bad arguments on the host before any HIP call (so these run on a
+machine without a GPU: no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from mixture_experts_expert_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(B):
+    names = declared_functions()
+    assert len(names) == 16, names
+    for n in names:
+        assert hasattr(B.lib, n), n
+
+
+def test_status_strings(B):
+    for code in range(5):
+        assert B.moe_status_string(code).startswith(B.STATUS[code])
+
+
+def test_workspace_bytes(B):
+    s = B.shape(8192, 2048, 128, 8, 768, "bf16")
+    ws = B.moe_workspace_bytes(s)
+    assert ws >= 8192 * 8 * 2 * 768 * 2  # dG | dU scratch
+    assert B.moe_workspace_bytes(B.shape(8, 64, 4, 5, 64, "bf16")) == 0  # k > E rejected
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def _route(B, s, **over):
+    args = dict(x=FAKE, wr=FAKE, bias=None, logits=FAKE, idx=FAKE, w=FAKE)
+    args.update(over)
+    return B.lib.moe_route(s, args["x"], args["wr"], args["bias"], args["logits"], args["idx"], args["w"], None)
+
+
+@pytest.mark.parametrize("T,H,E,k,I,dt,code", [
+    (0, 64, 4, 2, 64, 1, 1),       # T <= 0
+    (8, 64, 4, 5, 64, 1, 1),       # k > E
+    (8, 64, 2000, 2, 64, 1, 1),    # E > 1024
+    (8, 64, 4, 0, 64, 1, 1),       # k <= 0
+    (8, 96, 4, 2, 64, 1, 2),       # H % 64
+    (8, 64, 4, 2, 48, 1, 2),       # I % 64
+    (8, 64, 4, 2, 64, 7, 2),       # unknown dtype
+    (1 << 28, 64, 16, 8, 64, 1, 1),  # T*k >= 2^31
+])
+def test_shape_validation(B, T, H, E, k, I, dt, code):
+    assert _route(B, B.moe_shape(T, H, E, k, I, dt)) == code
+
+
+def test_null_pointers_rejected(B):
+    s = B.shape(8, 64, 4, 2, 64, "bf16")
+    for key in ["x", "wr", "logits", "idx", "w"]:
+        assert _route(B, s, **{key: None}) == 1
+    P = [FAKE] * 8
+    assert B.lib.moe_permute(s, None, *P[:6], FAKE, 1 << 30, None) == 1
+    assert B.lib.moe_combine(s, FAKE, FAKE, None, FAKE, None) == 1
+    assert B.lib.moe_combine_bwd(s, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == 1
+    assert B.lib.moe_unpermute_sum(s, FAKE, FAKE, None, None) == 1
+    assert B.lib.moe_route_bwd(s, FAKE, None, FAKE, FAKE, None) == 1
+    assert B.lib.moe_grouped_gemm_fwd(s, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 1
+
+
+def test_workspace_too_small(B):
+    s = B.shape(64, 128, 8, 2, 64, "bf16")
+    need = B.moe_workspace_bytes(s)
+    P = [FAKE] * 7
+    assert B.lib.moe_permute(s, *P, FAKE, need - 1, None) == 3
+    G = [FAKE] * 13
+    assert B.lib.moe_grouped_gemm_bwd(s, *G, 0, FAKE, need - 1, None) == 3
+    assert B.lib.moe_grouped_gemm_bwd(s, *G, 2, FAKE, need, None) == 1  # accumulate_dw not 0/1
+
+
+def test_binding_raises_on_error(B):
+    import torch
+    s = B.shape(8, 64, 4, 5, 64, "bf16")
+    t = torch.empty(1)
+    with pytest.raises(B.MoEError) as ei:
+        B.lib  # noqa: B018
+        B._check("moe_route", _route(B, s))
+    assert ei.value.status == 1
