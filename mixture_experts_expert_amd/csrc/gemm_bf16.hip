@@ -22,14 +22,20 @@
 //
 // Tile: 256 x 256 x 64 per workgroup of 4 wavefronts (2 x 2), 128 x 128 per
 // wavefront as 4 x 4 MFMA blocks of 32 x 32, accumulators in the register
-// file (256 fp32 per lane). Operands go global -> registers -> LDS (two
-// stages, 128 KiB) with the next k-step's global loads in flight while the
-// current one multiplies. Both operands sit in LDS as [row][k] with k
-// contiguous, in 16-byte chunks XOR-swizzled by row so the MFMA operand
-// reads (32 rows at one k-chunk) hit distinct banks. Operands whose k is the
-// strided index (data-gradient weights, both weight-gradient operands) are
-// transposed in registers on their way into LDS (4 k-rows x 8 columns per
-// thread).
+// file (256 fp32 per lane). Operands go straight from global memory into LDS
+// (global_load_lds_dwordx4: each wavefront instruction fills one contiguous
+// KiB, lane l at byte 16 l), two stages of 64 KiB, the next k-step's loads in
+// flight while the current one multiplies; no register staging and no LDS
+// store phase. An operand whose reduction index is contiguous in memory
+// ("k-major": the forward operands, the data-gradient activations) sits in
+// LDS as [row][k], 16-byte chunks XOR-swizzled by row, and is read with
+// ds_read_b128. An operand whose reduction index is the strided one
+// ("mn-major": the data-gradient weights, both weight-gradient operands) sits
+// as [k][column] as it is in memory, chunks swizzled by k, and is read with
+// ds_read_b64_tr_b16, which hands each lane four consecutive k of one column
+// (within each 16-lane group, lane i receives element i%4 of the pieces that
+// lanes 4j + i/4 address). Either way the swizzle is applied on the global
+// side: each lane fetches the chunk that belongs at its fixed LDS slot.
 //
 // Scheduling: one workgroup per CU, persistent. Tile i of the list belongs
 // to XCD-local workgroups: the list is cut into 8 contiguous ranges, one per
@@ -77,85 +83,39 @@ struct Params {
   int accumulate;
 };
 
-// Physical element offset of 16-byte chunk `c` of LDS row `r`.
-__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ ((r ^ (r >> 3)) & 7)) << 3); }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+// LDS layouts of one operand stage (bf16 elements):
+//   k-major  [256 rows][64 k]   chunk c of row r at r*64 + (c ^ swk(r))*8
+//   mn-major [64 k][256 cols]   chunk c of row k at k*256 + (c ^ swt(k))*8
+__device__ __forceinline__ int swk(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int swt(int k) { return (k & 3) << 2; }
 
-// Operand with k contiguous in memory: R rows x BK, one 16-byte chunk per
-// (row, chunk) pair; thread t owns chunks t + i*NT, i.e. row i*(NT/CH) + t/CH,
-// chunk t % CH.
-template <int R>
-struct KLoader {
-  static constexpr int N = R * CH / NT;
-  const bf16_t* base[N];
-  int off[N];
-  u32x4 v[N];
-  __device__ __forceinline__ void load(int k0) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = *reinterpret_cast<const u32x4*>(base[i] + off[i] + k0);
-  }
-  __device__ __forceinline__ void store(bf16_t* lds, int tid) const {
-    const int c = tid % CH;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int r = i * (NT / CH) + tid / CH;
-      *reinterpret_cast<u32x4*>(lds + swz(r, c)) = v[i];
-    }
-  }
-};
+// One 16-byte chunk per lane from global memory into LDS: lane l lands at
+// byte 16 l of the 1 KiB block `blk` (wavefront-uniform).
+__device__ __forceinline__ void g2lds(const bf16_t* src, bf16_t* blk) {
+  __builtin_amdgcn_global_load_lds(src, blk, 16, 0, 0);
+}
 
-// Operand with k strided in memory ([k][mn], mn contiguous): blocks of 4
-// k-rows x 8 columns; thread t owns blocks q = t + i*NT with kb = q % 16
-// (k-rows 4kb..4kb+3 of the step) and mb = q / 16 (columns 8mb..8mb+7).
-// Rows at or past `rows_left` read as zero (ragged reductions).
-template <int R>
-struct TLoader {
-  static constexpr int N = 2 * R / NT;
-  int off[N];  // (4*kb)*ld + first column of the block
-  u32x4 v[N][4];
-  __device__ __forceinline__ void load(const bf16_t* base, int ld, int rows_left, int tid) {
-    const int kb = tid % 16;
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-#pragma unroll
-      for (int kr = 0; kr < 4; ++kr) {
-        const int row = kb * 4 + kr;
-        u32x4 z = {0u, 0u, 0u, 0u};
-        if (row < rows_left) z = *reinterpret_cast<const u32x4*>(base + off[i] + kr * ld);
-        v[i][kr] = z;
-      }
-  }
-  __device__ __forceinline__ void store(bf16_t* lds, int tid) const {
-    const int kb = tid % 16;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int mb = (tid + i * NT) / 16;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int w = c >> 1;
-        u32x2 o;
-        if (c & 1) {
-          o.x = hi_pair(v[i][0][w], v[i][1][w]);
-          o.y = hi_pair(v[i][2][w], v[i][3][w]);
-        } else {
-          o.x = lo_pair(v[i][0][w], v[i][1][w]);
-          o.y = lo_pair(v[i][2][w], v[i][3][w]);
-        }
-        const int r = mb * 8 + c;
-        *reinterpret_cast<u32x2*>(lds + swz(r, kb >> 1) + ((kb & 1) << 2)) = o;
-      }
-    }
-  }
-};
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float bf(bf16_t v) { return bf16_to_f32(v); }
+// Four floats -> four bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+  const f32x2 lo = {a, b}, hi = {c, d};
+  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
+                    __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2)));
+}
 
 template <int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(
     Params P) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * STAGE];
+  // Two stages as two objects: with the stage of every access known at
+  // compile time, the compiler sees that loads landing in one stage do not
+  // alias reads of the other and does not wait for them before reading.
+  __shared__ __attribute__((aligned(16))) bf16_t lds0[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16_t lds1[STAGE];
   __shared__ int tstart[1025];  // grouped-M: first m-tile of each expert
   __shared__ int part[NT];
 
@@ -216,10 +176,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   const int lo = static_cast<int>((static_cast<int64_t>(total) * xcd) / 8);
   const int hi = static_cast<int>((static_cast<int64_t>(total) * (xcd + 1)) / 8);
 
-  KLoader<BM> ka;   // A, k contiguous (grouped-M)
-  TLoader<BM> ta;   // A, k strided (grouped-K)
-  KLoader<BN> kb;   // B, k contiguous (GATEUP, DOWN)
-  TLoader<BN> tb;   // B, k strided (data and weight gradients)
+  constexpr bool A_KMAJOR = !grouped_k(MODE);
+  constexpr bool B_KMAJOR = b_kcontig(MODE);
 
   for (int L = lo + slot; L < hi; L += nslots) {
     // ---- decode the tile ---------------------------------------------------
@@ -249,9 +207,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       kend = P.offsets[e + 1];
     }
 
-    // ---- per-tile operand addressing ----------------------------------------
-    int ksteps;
-    int lda = 0, ldb = 0;
+    int ksteps, lda = 0, ldb = 0;
     if constexpr (MODE == GATEUP) { lda = H; ksteps = H / BK; }
     if constexpr (MODE == DOWN) { lda = I; ksteps = I / BK; }
     if constexpr (MODE == DGRAD_DOWN) { lda = H; ldb = I; ksteps = H / BK; }
@@ -259,79 +215,144 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
     if constexpr (MODE == WGRAD_DOWN) { lda = H; ldb = I; ksteps = (kend - kbeg + BK - 1) / BK; }
     if constexpr (MODE == WGRAD_GATEUP) { lda = 2 * I; ldb = H; ksteps = (kend - kbeg + BK - 1) / BK; }
 
-    if constexpr (!grouped_k(MODE)) {
-      const bf16_t* abase = P.a + static_cast<int64_t>(row0) * lda;
+    // ---- per-lane source offsets of this wavefront's 8 + 8 load
+    // instructions; instruction t fills LDS block wave*8 + t (1 KiB) of each
+    // operand stage. Rows and columns past the operand's end are clamped to
+    // its last one (their products land in rows or columns that are never
+    // stored).
+    int aoff[8], boff[8];
+    const bf16_t* bbase[8];
 #pragma unroll
-      for (int i = 0; i < KLoader<BM>::N; ++i) {
-        const int r = i * (NT / CH) + tid / CH;
-        ka.off[i] = min(r, mvalid - 1) * lda + (tid % CH) * 8;
-        ka.base[i] = abase;
+    for (int t = 0; t < 8; ++t) {
+      const int blk = wave * 8 + t;
+      if constexpr (A_KMAJOR) {
+        const int r = blk * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swk(r);
+        aoff[t] = min(r, mvalid - 1) * lda + c * 8;
+      } else {
+        const int k = blk * 2 + (lane >> 5);
+        const int c = (lane & 31) ^ swt(k);
+        const int mrows = MODE == WGRAD_DOWN ? H : 2 * I;
+        aoff[t] = k * lda + min(m0 + c * 8, mrows - 8);
       }
-    } else {
-      const int mrows = MODE == WGRAD_DOWN ? H : 2 * I;
-#pragma unroll
-      for (int i = 0; i < TLoader<BM>::N; ++i) {
-        const int q = tid + i * NT;
-        const int col = min(m0 + (q / 16) * 8, mrows - 8);
-        ta.off[i] = (q % 16) * 4 * lda + col;
-      }
-    }
-    if constexpr (MODE == GATEUP) {
-      const int64_t ebase = static_cast<int64_t>(e) * I * H;
-#pragma unroll
-      for (int i = 0; i < KLoader<BN>::N; ++i) {
-        // LDS row r = 32 i + tid / 8; wavefront column half wn = i / 4 and
-        // 32-column block j = i % 4 (j < 2: gate, j >= 2: up) of that half.
-        const int j = i % 4, half = i / 4;
-        const int idx = min(n0 + half * 64 + (j & 1) * 32 + tid / CH, I - 1);
-        kb.off[i] = idx * H + (tid % CH) * 8;
-        kb.base[i] = (j < 2 ? P.b0 : P.b1) + ebase;
-      }
-    }
-    if constexpr (MODE == DOWN) {
-      const bf16_t* bbase = P.b0 + static_cast<int64_t>(e) * H * I;
-#pragma unroll
-      for (int i = 0; i < KLoader<BN>::N; ++i) {
-        const int r = i * (NT / CH) + tid / CH;
-        kb.off[i] = min(n0 + r, H - 1) * I + (tid % CH) * 8;
-        kb.base[i] = bbase;
-      }
-    }
-    if constexpr (!b_kcontig(MODE)) {
-      const int ncols = (MODE == DGRAD_DOWN || MODE == WGRAD_DOWN) ? I : H;
-#pragma unroll
-      for (int i = 0; i < TLoader<BN>::N; ++i) {
-        const int q = tid + i * NT;
-        const int col = min(n0 + (q / 16) * 8, ncols - 8);
-        tb.off[i] = (q % 16) * 4 * ldb + col;
+      if constexpr (MODE == GATEUP) {
+        const int r = blk * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swk(r);
+        // LDS row r: wavefront column half r / 128 and 32-column block
+        // j = (r % 128) / 32 of it (j < 2: gate, j >= 2: up, same indices).
+        const int j = (r & 127) >> 5;
+        const int idx = min(n0 + (r >> 7) * 64 + (j & 1) * 32 + (r & 31), I - 1);
+        boff[t] = idx * H + c * 8;
+        bbase[t] = (j < 2 ? P.b0 : P.b1) + static_cast<int64_t>(e) * I * H;
+      } else if constexpr (MODE == DOWN) {
+        const int r = blk * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swk(r);
+        boff[t] = min(n0 + r, H - 1) * I + c * 8;
+        bbase[t] = P.b0 + static_cast<int64_t>(e) * H * I;
+      } else {
+        const int k = blk * 2 + (lane >> 5);
+        const int c = (lane & 31) ^ swt(k);
+        const int ncols = (MODE == DGRAD_DOWN || MODE == WGRAD_DOWN) ? I : H;
+        boff[t] = k * ldb + min(n0 + c * 8, ncols - 8);
+        bbase[t] = nullptr;
       }
     }
+    const bf16_t* abase_m = P.a + static_cast<int64_t>(row0) * lda;  // grouped-M A
 
-    // k-step s: global loads of A and B into registers.
-    auto load_step = [&](int s) {
+    // Issue every load of k-step s into LDS stage `stage`. Weight-gradient
+    // k-rows past the expert's last row are written as zeros instead.
+    auto issue = [&](int s, bf16_t* As) {
+      bf16_t* Bs = As + STAGE_A;
       const int k0 = s * BK;
       if constexpr (!grouped_k(MODE)) {
-        ka.load(k0);
-      } else {
-        ta.load(P.a + static_cast<int64_t>(kbeg + k0) * lda, lda, kend - kbeg - k0, tid);
+        if (s >= ksteps) {  // the padding step of an odd step count: zeros
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            *reinterpret_cast<u32x4*>(As + (wave * 8 + t) * 512 + lane * 8) = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(Bs + (wave * 8 + t) * 512 + lane * 8) = u32x4{0u, 0u, 0u, 0u};
+          }
+          return;
+        }
       }
-      if constexpr (b_kcontig(MODE)) {
-        kb.load(k0);
-      } else if constexpr (MODE == DGRAD_DOWN) {
-        tb.load(P.b0 + static_cast<int64_t>(e) * H * I + static_cast<int64_t>(k0) * I, ldb, BK, tid);
-      } else if constexpr (MODE == DGRAD_GATEUP) {
-        const bf16_t* base = k0 < I ? P.b0 + static_cast<int64_t>(e) * I * H + static_cast<int64_t>(k0) * H
-                                    : P.b1 + static_cast<int64_t>(e) * I * H + static_cast<int64_t>(k0 - I) * H;
-        tb.load(base, ldb, BK, tid);
+      if constexpr (A_KMAJOR) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) g2lds(abase_m + aoff[t] + k0, As + (wave * 8 + t) * 512);
       } else {
-        tb.load(P.b0 + static_cast<int64_t>(kbeg + k0) * ldb, ldb, kend - kbeg - k0, tid);
+        const bf16_t* base = P.a + static_cast<int64_t>(kbeg + k0) * lda;
+        const int left = kend - kbeg - k0;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          bf16_t* blk = As + (wave * 8 + t) * 512;
+          if ((wave * 8 + t) * 2 + (lane >> 5) < left) g2lds(base + aoff[t], blk);
+          else *reinterpret_cast<u32x4*>(blk + lane * 8) = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      if constexpr (B_KMAJOR) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) g2lds(bbase[t] + boff[t] + k0, Bs + (wave * 8 + t) * 512);
+      } else {
+        const bf16_t* base;
+        int left = BK;
+        if constexpr (MODE == DGRAD_DOWN) {
+          base = P.b0 + static_cast<int64_t>(e) * H * I + static_cast<int64_t>(k0) * I;
+        } else if constexpr (MODE == DGRAD_GATEUP) {
+          base = k0 < I ? P.b0 + static_cast<int64_t>(e) * I * H + static_cast<int64_t>(k0) * H
+                        : P.b1 + static_cast<int64_t>(e) * I * H + static_cast<int64_t>(k0 - I) * H;
+        } else {
+          base = P.b0 + static_cast<int64_t>(kbeg + k0) * ldb;
+          left = kend - kbeg - k0;
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          bf16_t* blk = Bs + (wave * 8 + t) * 512;
+          if (grouped_k(MODE) && (wave * 8 + t) * 2 + (lane >> 5) >= left)
+            *reinterpret_cast<u32x4*>(blk + lane * 8) = u32x4{0u, 0u, 0u, 0u};
+          else
+            g2lds(base + boff[t], blk);
+        }
       }
     };
-    auto store_step = [&](int stage) {
-      bf16_t* As = lds + stage * STAGE;
-      bf16_t* Bs = As + STAGE_A;
-      if constexpr (!grouped_k(MODE)) ka.store(As, tid); else ta.store(As, tid);
-      if constexpr (b_kcontig(MODE)) kb.store(Bs, tid); else tb.store(Bs, tid);
+
+    // Operand fragments of k-slice kk (16 k) for 32-row block i, as byte
+    // offsets inside a stage. k-major (ds_read_b128, lane: row i*32 + lane%32,
+    // chunk 2 kk + lane/32): the chunk XOR makes slice kk the slice-0 offset
+    // XOR 32 kk. mn-major (two ds_read_b64_tr_b16, lane: k-row
+    // 8 (lane/32) + (lane%16)/4, columns 4 (lane%4) .. + 3 of the block's
+    // 16-column half (lane/16)%2): slice kk adds 16 rows = 8 KiB, the second
+    // read 4 rows = 2 KiB.
+    const int hi32 = lane >> 5;
+    const int g16 = lane >> 4, i16 = lane & 15;
+    int aof[FM], bof[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if constexpr (A_KMAJOR) {
+        const int r = wm * WTM + i * 32 + (lane & 31);
+        aof[i] = r * (BK * 2) + ((hi32 ^ swk(r)) << 4);
+      } else {
+        const int k = 8 * (g16 >> 1) + (i16 >> 2);
+        const int col = wm * WTM + i * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
+        aof[i] = k * 512 + (((col >> 3) ^ swt(k)) << 4) + ((col & 7) << 1);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (B_KMAJOR) {
+        const int r = wn * WTN + j * 32 + (lane & 31);
+        bof[j] = r * (BK * 2) + ((hi32 ^ swk(r)) << 4);
+      } else {
+        const int k = 8 * (g16 >> 1) + (i16 >> 2);
+        const int col = wn * WTN + j * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
+        bof[j] = k * 512 + (((col >> 3) ^ swt(k)) << 4) + ((col & 7) << 1);
+      }
+    }
+    auto frag = [&](const bf16_t* S, int off, int kk, bool kmajor) -> bf16x8 {
+      const char* base = reinterpret_cast<const char*>(S);
+      if (kmajor) return *reinterpret_cast<const bf16x8*>(base + (off ^ (kk * 32)));
+      const char* p = base + off + kk * 8192;
+      const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+      const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 2048));
+      const v4i16 both[2] = {lo4, hi4};
+      return __builtin_bit_cast(bf16x8, both);
     };
 
     f32x16 acc[FM][FN];
@@ -342,100 +363,131 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-    if (ksteps > 0) {
-      load_step(0);
-      store_step(0);
-      __syncthreads();
-      for (int s = 0; s < ksteps; ++s) {
-        if (s + 1 < ksteps) load_step(s + 1);
-        const bf16_t* As = lds + (s & 1) * STAGE;
-        const bf16_t* Bs = As + STAGE_A;
+    // One k-step on the stage at As: operand fragments of k-slice kk + 1
+    // are read while the 16 MFMAs of slice kk run; scheduling fences keep the
+    // slices apart so the reads' latency runs under the matrix work.
+    auto compute = [&](const bf16_t* As) {
+      const bf16_t* Bs = As + STAGE_A;
+      // Opaque to the optimiser: keeps the per-slice addresses below from
+      // being hoisted out of the k-loop (for both stages and all slices,
+      // which would not fit in registers).
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-          const int c = kk * 2 + (lane >> 5);
-          bf16x8 av[FM], bv[FN];
+      for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(aof[i]));
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
-            av[i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * WTM + i * 32 + (lane & 31), c));
+      for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(bof[j]));
+      bf16x8 av[2][FM], bv[2][FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) av[0][i] = frag(As, aof[i], 0, A_KMAJOR);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bv[0][j] = frag(Bs, bof[j], 0, B_KMAJOR);
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int cur = kk & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk + 1 < BK / 16) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i) av[cur ^ 1][i] = frag(As, aof[i], kk + 1, A_KMAJOR);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) bv[cur ^ 1][j] = frag(Bs, bof[j], kk + 1, B_KMAJOR);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            bv[j] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * WTN + j * 32 + (lane & 31), c));
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-        }
-        if (s + 1 < ksteps) store_step((s + 1) & 1);
-        __syncthreads();
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads of the next step have landed
+      __syncthreads();                // everyone's have, and this stage is free again
+    };
+
+    if (ksteps > 0) {
+      issue(0, lds0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      // Steps go in pairs (stage 0, stage 1); an odd count gets one more
+      // step of zeros (weight-gradient rows past the end already read as 0).
+      const int ksteps2 = (ksteps + 1) & ~1;
+      for (int s = 0; s < ksteps2; s += 2) {
+        issue(s + 1, lds1);
+        compute(lds0);
+        if (s + 2 < ksteps2) issue(s + 2, lds0);
+        compute(lds1);
       }
     }
 
     // ---- epilogue -------------------------------------------------------------
-    // acc[i][j][q] holds tile row wm*128 + i*32 + 8*(q/4) + 4*(lane/32) + q%4,
-    // tile column wn*128 + j*32 + lane%32.
-    const int rbase = wm * WTM + 4 * (lane >> 5);
-    const int cl = lane & 31;
-    if constexpr (MODE == GATEUP) {
+    // acc[i][j][q] holds wavefront-tile row i*32 + 8*(q/4) + 4*(lane/32) + q%4,
+    // column j*32 + lane%32. Each 32-row block goes through this wavefront's
+    // 16 KiB slice of LDS (fp32, [32][128]) and leaves as row-contiguous
+    // vectors: 4 columns per lane, 32 lanes per 128-column row.
+    float* stage = reinterpret_cast<float*>(lds0) + wave * (32 * WTN);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int idx = n0 + wn * 64 + jj * 32 + cl;
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int tr = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
-            if (tr < mvalid && idx < I) {
-              const int64_t o = static_cast<int64_t>(row0 + tr) * I + idx;
-              const float gv = acc[i][jj][q], uv = acc[i][jj + 2][q];
-              P.out0[o] = f32_to_bf16(gv);
-              P.out1[o] = f32_to_bf16(uv);
-              P.out2[o] = f32_to_bf16(gv * sigmoidf_dev(gv) * uv);
-            }
+        for (int q = 0; q < 16; ++q)
+          stage[(8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * WTN + j * 32 + (lane & 31)] = acc[i][j][q];
+      __syncthreads();
+      const int trow0 = wm * WTM + i * 32;  // tile row of stage row 0
+      if constexpr (MODE == GATEUP) {
+        // Columns 0..63 of the wavefront tile are gate, 64..127 up, for the
+        // same 64 intermediate indices.
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const int r = it * 4 + (lane >> 4);
+          const int c = (lane & 15) * 4;
+          const int tr = trow0 + r;
+          const int idx = n0 + wn * 64 + c;
+          if (tr < mvalid && idx < I) {
+            const float4 gv = *reinterpret_cast<const float4*>(stage + r * WTN + c);
+            const float4 uv = *reinterpret_cast<const float4*>(stage + r * WTN + 64 + c);
+            const float av[4] = {gv.x * sigmoidf_dev(gv.x) * uv.x, gv.y * sigmoidf_dev(gv.y) * uv.y,
+                                 gv.z * sigmoidf_dev(gv.z) * uv.z, gv.w * sigmoidf_dev(gv.w) * uv.w};
+            const int64_t o = static_cast<int64_t>(row0 + tr) * I + idx;
+            *reinterpret_cast<uint2*>(P.out0 + o) = pack_bf16x4(gv.x, gv.y, gv.z, gv.w);
+            *reinterpret_cast<uint2*>(P.out1 + o) = pack_bf16x4(uv.x, uv.y, uv.z, uv.w);
+            *reinterpret_cast<uint2*>(P.out2 + o) = pack_bf16x4(av[0], av[1], av[2], av[3]);
           }
         }
-    } else if constexpr (MODE == DOWN || MODE == DGRAD_GATEUP) {
+      } else {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int n = n0 + wn * WTN + j * 32 + cl;
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int tr = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
-            if (tr < mvalid && n < H) P.out0[static_cast<int64_t>(row0 + tr) * H + n] = f32_to_bf16(acc[i][j][q]);
-          }
-        }
-    } else if constexpr (MODE == DGRAD_DOWN) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int idx = n0 + wn * WTN + j * 32 + cl;
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int tr = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
-            if (tr < mvalid && idx < I) {
+        for (int it = 0; it < 16; ++it) {
+          const int r = it * 2 + (lane >> 5);
+          const int c = (lane & 31) * 4;
+          const int tr = trow0 + r;
+          const float4 v = *reinterpret_cast<const float4*>(stage + r * WTN + c);
+          const int n = n0 + wn * WTN + c;
+          if constexpr (MODE == DOWN || MODE == DGRAD_GATEUP) {
+            if (tr < mvalid && n < H)
+              *reinterpret_cast<uint2*>(P.out0 + static_cast<int64_t>(row0 + tr) * H + n) =
+                  pack_bf16x4(v.x, v.y, v.z, v.w);
+          } else if constexpr (MODE == DGRAD_DOWN) {
+            if (tr < mvalid && n < I) {
               const int64_t p = row0 + tr;
-              const float gv = bf(P.g_in[p * I + idx]), uv = bf(P.u_in[p * I + idx]);
-              const float sg = sigmoidf_dev(gv);
-              const float da = acc[i][j][q];
-              P.out0[p * 2 * I + idx] = f32_to_bf16(da * uv * sg * (1.0f + gv * (1.0f - sg)));
-              P.out0[p * 2 * I + I + idx] = f32_to_bf16(da * (gv * sg));
+              const uint2 gb = *reinterpret_cast<const uint2*>(P.g_in + p * I + n);
+              const uint2 ub = *reinterpret_cast<const uint2*>(P.u_in + p * I + n);
+              const float gv[4] = {__uint_as_float(gb.x << 16), __uint_as_float(gb.x & 0xffff0000u),
+                                   __uint_as_float(gb.y << 16), __uint_as_float(gb.y & 0xffff0000u)};
+              const float uv[4] = {__uint_as_float(ub.x << 16), __uint_as_float(ub.x & 0xffff0000u),
+                                   __uint_as_float(ub.y << 16), __uint_as_float(ub.y & 0xffff0000u)};
+              const float da[4] = {v.x, v.y, v.z, v.w};
+              float dg[4], du[4];
+#pragma unroll
+              for (int e2 = 0; e2 < 4; ++e2) {
+                const float sg = sigmoidf_dev(gv[e2]);
+                dg[e2] = da[e2] * uv[e2] * sg * (1.0f + gv[e2] * (1.0f - sg));
+                du[e2] = da[e2] * (gv[e2] * sg);
+              }
+              *reinterpret_cast<uint2*>(P.out0 + p * 2 * I + n) = pack_bf16x4(dg[0], dg[1], dg[2], dg[3]);
+              *reinterpret_cast<uint2*>(P.out0 + p * 2 * I + I + n) = pack_bf16x4(du[0], du[1], du[2], du[3]);
             }
-          }
-        }
-    } else {
-      const int mrows = MODE == WGRAD_DOWN ? H : 2 * I;
-      const int ncols = MODE == WGRAD_DOWN ? I : H;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int n = n0 + wn * WTN + j * 32 + cl;
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int m = m0 + rbase + i * 32 + 8 * (q >> 2) + (q & 3);
+          } else {
+            const int mrows = MODE == WGRAD_DOWN ? H : 2 * I;
+            const int ncols = MODE == WGRAD_DOWN ? I : H;
+            const int m = m0 + tr;
             if (m < mrows && n < ncols) {
               float* dst;
               if constexpr (MODE == WGRAD_DOWN) {
@@ -444,10 +496,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
                 dst = m < I ? P.dw0 + (static_cast<int64_t>(e) * I + m) * H + n
                             : P.dw1 + (static_cast<int64_t>(e) * I + (m - I)) * H + n;
               }
-              *dst = P.accumulate ? *dst + acc[i][j][q] : acc[i][j][q];
+              float4 o = v;
+              if (P.accumulate) {
+                const float4 old = *reinterpret_cast<const float4*>(dst);
+                o.x += old.x;
+                o.y += old.y;
+                o.z += old.z;
+                o.w += old.w;
+              }
+              *reinterpret_cast<float4*>(dst) = o;
             }
           }
         }
+      }
+      __syncthreads();  // the slice is rewritten by the next block (or the next tile's loads)
     }
   }
 }

@@ -12,21 +12,62 @@
 namespace moe {
 namespace {
 
-constexpr int kRT = 4;           // tokens per thread
-constexpr int kRE = 4;           // experts per thread
-constexpr int kTy = 8, kTx = 16; // thread grid of a block
-constexpr int kTileT = kTy * kRT;  // 32 tokens per block
-constexpr int kTileE = kTx * kRE;  // 64 experts per block
-constexpr int kHC = 64;            // h values staged per step
-constexpr int kLogitThreads = kTy * kTx;  // 128
+constexpr int kRT = 2;              // tokens per thread
+constexpr int kRE = 4;              // experts per thread
+constexpr int kTy = 16, kTx = 16;   // thread grid of a block
+constexpr int kTileT = kTy * kRT;   // 32 tokens per block
+constexpr int kTileE = kTx * kRE;   // 64 experts per block
+constexpr int kHC = 64;             // h values staged per step
+constexpr int kLogitThreads = kTy * kTx;  // 256
+constexpr int kXS = kTileT + 4;     // LDS row strides (floats), 16-byte aligned
+constexpr int kWS = kTileE + 4;
+
+// Staging of one kHC-wide h slice of `rows` rows into LDS as fp32 [h][row]:
+// 16-byte global loads along h (coalesced), one thread per chunk.
+template <class T, int ROWS>
+struct Stager {
+  static constexpr int VE = 16 / sizeof(T);            // elements per 16-byte chunk
+  static constexpr int CPR = kHC / VE;                 // chunks per row
+  static constexpr int PER = (ROWS * CPR + kLogitThreads - 1) / kLogitThreads;
+  uint4 v[PER];
+  __device__ __forceinline__ void load(const T* __restrict__ src, int row0, int nrows, int H, int h0, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = tid + i * kLogitThreads;
+      const int r = q / CPR, c = q % CPR;
+      v[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (q < ROWS * CPR && row0 + r < nrows)
+        v[i] = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(row0 + r) * H + h0 + c * VE);
+    }
+  }
+  __device__ __forceinline__ void store(float* lds, int stride, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = tid + i * kLogitThreads;
+      if (q >= ROWS * CPR) continue;
+      const int r = q / CPR, c = q % CPR;
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lds[(c * 8 + 2 * e) * stride + r] = __uint_as_float(w[e] << 16);
+          lds[(c * 8 + 2 * e + 1) * stride + r] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lds[(c * 4 + e) * stride + r] = __uint_as_float(w[e]);
+      }
+    }
+  }
+};
 
 template <class T>
 __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(int Tn, int H, int E, const T* __restrict__ x,
                                                                       const T* __restrict__ wr,
                                                                       const float* __restrict__ bias,
                                                                       float* __restrict__ logits) {
-  __shared__ float xs[kHC][kTileT];  // [h][token]
-  __shared__ float ws[kHC][kTileE];  // [h][expert]
+  __shared__ __attribute__((aligned(16))) float xs[2][kHC * kXS];  // [h][token]
+  __shared__ __attribute__((aligned(16))) float ws[2][kHC * kWS];  // [h][expert]
   const int tid = threadIdx.x;
   const int ty = tid / kTx, tx = tid % kTx;
   const int t0 = blockIdx.x * kTileT;
@@ -38,30 +79,36 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(int Tn, in
 #pragma unroll
     for (int j = 0; j < kRE; ++j) acc[i][j] = 0.0f;
 
-  for (int h0 = 0; h0 < H; h0 += kHC) {
-    // Stage x[t0:t0+32, h0:h0+64] and wr[e0:e0+64, h0:h0+64] as fp32,
-    // transposed to [h][row]. Rows past the end are zero (never stored).
-    for (int q = tid; q < kTileT * kHC; q += kLogitThreads) {
-      const int r = q / kHC, hh = q % kHC;
-      const int t = t0 + r;
-      xs[hh][r] = (t < Tn) ? Elem<T>::to_f32(x[static_cast<int64_t>(t) * H + h0 + hh]) : 0.0f;
+  Stager<T, kTileT> sx;
+  Stager<T, kTileE> sw;
+  sx.load(x, t0, Tn, H, 0, tid);
+  sw.load(wr, e0, E, H, 0, tid);
+  sx.store(xs[0], kXS, tid);
+  sw.store(ws[0], kWS, tid);
+  __syncthreads();
+  const int nsteps = H / kHC;
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nsteps) {  // next slice in flight while this one is multiplied
+      sx.load(x, t0, Tn, H, (s + 1) * kHC, tid);
+      sw.load(wr, e0, E, H, (s + 1) * kHC, tid);
     }
-    for (int q = tid; q < kTileE * kHC; q += kLogitThreads) {
-      const int r = q / kHC, hh = q % kHC;
-      const int e = e0 + r;
-      ws[hh][r] = (e < E) ? Elem<T>::to_f32(wr[static_cast<int64_t>(e) * H + h0 + hh]) : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll 8
+    const float* xb = xs[buf];
+    const float* wb = ws[buf];
+#pragma unroll 16
     for (int hh = 0; hh < kHC; ++hh) {
-      const float4 xv = *reinterpret_cast<const float4*>(&xs[hh][ty * kRT]);
-      const float4 wv = *reinterpret_cast<const float4*>(&ws[hh][tx * kRE]);
-      const float xa[kRT] = {xv.x, xv.y, xv.z, xv.w};
+      const float2 xv = *reinterpret_cast<const float2*>(xb + hh * kXS + ty * kRT);
+      const float4 wv = *reinterpret_cast<const float4*>(wb + hh * kWS + tx * kRE);
+      const float xa[kRT] = {xv.x, xv.y};
       const float wa[kRE] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
       for (int i = 0; i < kRT; ++i)
 #pragma unroll
         for (int j = 0; j < kRE; ++j) acc[i][j] = __fmaf_rn(xa[i], wa[j], acc[i][j]);
+    }
+    if (s + 1 < nsteps) {
+      sx.store(xs[buf ^ 1], kXS, tid);
+      sw.store(ws[buf ^ 1], kWS, tid);
     }
     __syncthreads();
   }
@@ -70,13 +117,17 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(int Tn, in
   for (int i = 0; i < kRT; ++i) {
     const int t = t0 + ty * kRT + i;
     if (t >= Tn) continue;
+    const int e = e0 + tx * kRE;
+    float v[kRE];
 #pragma unroll
-    for (int j = 0; j < kRE; ++j) {
-      const int e = e0 + tx * kRE + j;
-      if (e >= E) continue;
-      float v = acc[i][j];
-      if (bias) v = v + bias[e];
-      logits[static_cast<int64_t>(t) * E + e] = v;
+    for (int j = 0; j < kRE; ++j) v[j] = (bias && e + j < E) ? acc[i][j] + bias[e + j] : acc[i][j];
+    float* dst = logits + static_cast<int64_t>(t) * E + e;
+    if (e + kRE <= E && (E % 4) == 0) {
+      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kRE; ++j)
+        if (e + j < E) dst[j] = v[j];
     }
   }
 }
