@@ -92,11 +92,45 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 __device__ __forceinline__ int swk(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int swt(int k) { return (k & 3) << 2; }
 
-// One 16-byte chunk per lane from global memory into LDS: lane l lands at
-// byte 16 l of the 1 KiB block `blk` (wavefront-uniform).
-__device__ __forceinline__ void g2lds(const bf16_t* src, bf16_t* blk) {
-  __builtin_amdgcn_global_load_lds(src, blk, 16, 0, 0);
+// Operand loads go through buffer resources: a wavefront-uniform base and a
+// byte range (num_records); each lane supplies a 32-bit byte offset. A lane
+// whose dwords fall outside the range writes zeros, which is how reduction
+// rows past an expert's last row, the padding step of an odd step count and
+// prefetches past the last step are handled, without branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, kRsrcWord3);
 }
+// One 16-byte chunk per lane into LDS: lane l lands at byte 16 l of the
+// 1 KiB block `blk` (wavefront-uniform).
+__device__ __forceinline__ void buf_to_lds16(rsrc_t r, uint32_t voff, bf16_t* blk) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)blk, 16, voff, 0, 0, 0);
+}
+// L2 prefetch: one dword per lane (one per 128-byte line) dropped into a
+// scratch LDS slot that nothing reads; it has no register destination, so it
+// can stay in flight across k-steps.
+__device__ __forceinline__ void buf_prefetch(rsrc_t r, uint32_t voff, uint32_t* sink) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)sink, 4, voff, 0, 0, 0);
+}
+
+// Workgroup barrier between k-steps. The explicit s_waitcnt before it has
+// already made this wavefront's LDS traffic and needed loads complete; a
+// __syncthreads() would add a release fence that also waits for the L2
+// prefetches still in flight. The empty asm statements keep the compiler from
+// moving memory accesses across the barrier.
+__device__ __forceinline__ void step_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt in [3:0] and [15:14], expcnt in
+// [6:4], lgkmcnt in [11:8]. Both wait for LDS traffic and for all but the
+// newest `n` vector-memory instructions (expcnt left unconstrained).
+constexpr int kWaitVm0 = 0x0070;  // vmcnt(0) lgkmcnt(0)
+constexpr int kWaitVm2 = 0x0072;  // vmcnt(2) lgkmcnt(0)
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -117,11 +151,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   __shared__ __attribute__((aligned(16))) bf16_t lds0[STAGE];
   __shared__ __attribute__((aligned(16))) bf16_t lds1[STAGE];
   __shared__ int tstart[1025];  // grouped-M: first m-tile of each expert
+  __shared__ uint32_t pf_sink[4 * 64];  // L2-prefetch landing slots, never read
   __shared__ int part[NT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
   const int wm = wave >> 1, wn = wave & 1;
   const int H = P.H, E = P.E, I = P.I;
 
@@ -207,6 +242,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       kend = P.offsets[e + 1];
     }
 
+    // The decode is the same on every lane; say so, so that the operand
+    // bases live in scalar registers and the loads use the scalar-base form.
+    e = __builtin_amdgcn_readfirstlane(e);
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    mvalid = __builtin_amdgcn_readfirstlane(mvalid);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    n0 = __builtin_amdgcn_readfirstlane(n0);
+    kbeg = __builtin_amdgcn_readfirstlane(kbeg);
+    kend = __builtin_amdgcn_readfirstlane(kend);
+
     int ksteps, lda = 0, ldb = 0;
     if constexpr (MODE == GATEUP) { lda = H; ksteps = H / BK; }
     if constexpr (MODE == DOWN) { lda = I; ksteps = I / BK; }
@@ -215,102 +260,118 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
     if constexpr (MODE == WGRAD_DOWN) { lda = H; ldb = I; ksteps = (kend - kbeg + BK - 1) / BK; }
     if constexpr (MODE == WGRAD_GATEUP) { lda = 2 * I; ldb = H; ksteps = (kend - kbeg + BK - 1) / BK; }
 
-    // ---- per-lane source offsets of this wavefront's 8 + 8 load
-    // instructions; instruction t fills LDS block wave*8 + t (1 KiB) of each
-    // operand stage. Rows and columns past the operand's end are clamped to
-    // its last one (their products land in rows or columns that are never
-    // stored).
-    int aoff[8], boff[8];
-    const bf16_t* bbase[8];
+    // ---- per-lane byte offsets of this wavefront's 8 + 8 load instructions,
+    // relative to the operand's base at the current k-step; instruction t
+    // fills LDS block wave*8 + t (1 KiB) of each operand stage. Rows and
+    // columns past the operand's end are clamped to its last one (their
+    // products land in rows or columns that are never stored). k-major:
+    // LDS row r = 8 (wave*8 + t) + lane/8, chunk lane%8 (swizzled). mn-major:
+    // k-row 2 (wave*8 + t) + lane/32, chunk lane%32 (swizzled).
+    uint32_t aoff[8], boff[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int blk = wave * 8 + t;
       if constexpr (A_KMAJOR) {
         const int r = blk * 8 + (lane >> 3);
         const int c = (lane & 7) ^ swk(r);
-        aoff[t] = min(r, mvalid - 1) * lda + c * 8;
+        aoff[t] = 2u * (min(r, mvalid - 1) * lda + c * 8);
       } else {
         const int k = blk * 2 + (lane >> 5);
         const int c = (lane & 31) ^ swt(k);
         const int mrows = MODE == WGRAD_DOWN ? H : 2 * I;
-        aoff[t] = k * lda + min(m0 + c * 8, mrows - 8);
+        aoff[t] = 2u * (k * lda + min(m0 + c * 8, mrows - 8));
       }
       if constexpr (MODE == GATEUP) {
-        const int r = blk * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ swk(r);
         // LDS row r: wavefront column half r / 128 and 32-column block
         // j = (r % 128) / 32 of it (j < 2: gate, j >= 2: up, same indices).
+        // A wavefront's 64 rows are all gate (even waves) or all up (odd).
+        const int r = blk * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swk(r);
         const int j = (r & 127) >> 5;
         const int idx = min(n0 + (r >> 7) * 64 + (j & 1) * 32 + (r & 31), I - 1);
-        boff[t] = idx * H + c * 8;
-        bbase[t] = (j < 2 ? P.b0 : P.b1) + static_cast<int64_t>(e) * I * H;
+        boff[t] = 2u * (idx * H + c * 8);
       } else if constexpr (MODE == DOWN) {
         const int r = blk * 8 + (lane >> 3);
         const int c = (lane & 7) ^ swk(r);
-        boff[t] = min(n0 + r, H - 1) * I + c * 8;
-        bbase[t] = P.b0 + static_cast<int64_t>(e) * H * I;
+        boff[t] = 2u * (min(n0 + r, H - 1) * I + c * 8);
       } else {
         const int k = blk * 2 + (lane >> 5);
         const int c = (lane & 31) ^ swt(k);
         const int ncols = (MODE == DGRAD_DOWN || MODE == WGRAD_DOWN) ? I : H;
-        boff[t] = k * ldb + min(n0 + c * 8, ncols - 8);
-        bbase[t] = nullptr;
+        boff[t] = 2u * (k * ldb + min(n0 + c * 8, ncols - 8));
       }
     }
     const bf16_t* abase_m = P.a + static_cast<int64_t>(row0) * lda;  // grouped-M A
 
-    // Issue every load of k-step s into LDS stage `stage`. Weight-gradient
-    // k-rows past the expert's last row are written as zeros instead.
+    // L2 prefetch offsets, one 128-byte line per lane per operand and k-step:
+    // k-major operands, row wave*64 + lane (its 64 k of the step); mn-major
+    // operands, k-row wave*16 + lane/4, line lane%4 of the 256 columns.
+    uint32_t pfa, pfb;
+    {
+      const int r = wave * 64 + lane;
+      const int kr = wave * 16 + (lane >> 2);
+      if constexpr (A_KMAJOR) {
+        pfa = 2u * (min(r, mvalid - 1) * lda);
+      } else {
+        const int mrows = MODE == WGRAD_DOWN ? H : 2 * I;
+        pfa = 2u * (kr * lda + min(m0 + (lane & 3) * 64, mrows - 64));
+      }
+      if constexpr (MODE == GATEUP) {
+        const int j = (r & 127) >> 5;
+        pfb = 2u * (min(n0 + (r >> 7) * 64 + (j & 1) * 32 + (r & 31), I - 1) * H);
+      } else if constexpr (MODE == DOWN) {
+        pfb = 2u * (min(n0 + r, H - 1) * I);
+      } else {
+        const int ncols = (MODE == DGRAD_DOWN || MODE == WGRAD_DOWN) ? I : H;
+        pfb = 2u * (kr * ldb + min(n0 + (lane & 3) * 64, ncols - 64));
+      }
+    }
+    uint32_t* sink = pf_sink + wave * 64;
+
+    // Buffer resources of k-step s (num_records 0 past the last step).
+    auto rsrc_a = [&](int s) -> rsrc_t {
+      const int k0 = s * BK;
+      if constexpr (A_KMAJOR) {
+        return make_rsrc(abase_m + k0, s < ksteps ? 2 * (mvalid * lda - k0) : 0);
+      } else {
+        const int left = kend - kbeg - k0;
+        return make_rsrc(P.a + static_cast<int64_t>(kbeg + k0) * lda, left > 0 ? 2 * left * lda : 0);
+      }
+    };
+    auto rsrc_b = [&](int s) -> rsrc_t {
+      const int k0 = s * BK;
+      const bool live = s < ksteps;
+      if constexpr (MODE == GATEUP) {
+        const bf16_t* w = ((wave & 1) ? P.b1 : P.b0) + static_cast<int64_t>(e) * I * H + k0;
+        return make_rsrc(w, live ? 2 * (I * H - k0) : 0);
+      } else if constexpr (MODE == DOWN) {
+        return make_rsrc(P.b0 + static_cast<int64_t>(e) * H * I + k0, live ? 2 * (H * I - k0) : 0);
+      } else if constexpr (MODE == DGRAD_DOWN) {
+        return make_rsrc(P.b0 + static_cast<int64_t>(e) * H * I + static_cast<int64_t>(k0) * I,
+                         live ? 2 * (H - k0) * I : 0);
+      } else if constexpr (MODE == DGRAD_GATEUP) {
+        const bool up = k0 >= I;
+        const int kk0 = up ? k0 - I : k0;
+        return make_rsrc((up ? P.b1 : P.b0) + static_cast<int64_t>(e) * I * H + static_cast<int64_t>(kk0) * H,
+                         live ? 2 * (I - kk0) * H : 0);
+      } else {
+        const int left = kend - kbeg - k0;
+        return make_rsrc(P.b0 + static_cast<int64_t>(kbeg + k0) * ldb, left > 0 ? 2 * left * ldb : 0);
+      }
+    };
+
+    // Issue every load of k-step s into the stage at As, then the L2 prefetch
+    // of step s + 1 (always exactly two more vector-memory instructions).
     auto issue = [&](int s, bf16_t* As) {
       bf16_t* Bs = As + STAGE_A;
-      const int k0 = s * BK;
-      if constexpr (!grouped_k(MODE)) {
-        if (s >= ksteps) {  // the padding step of an odd step count: zeros
+      const rsrc_t ra = rsrc_a(s);
+      const rsrc_t rb = rsrc_b(s);
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            *reinterpret_cast<u32x4*>(As + (wave * 8 + t) * 512 + lane * 8) = u32x4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(Bs + (wave * 8 + t) * 512 + lane * 8) = u32x4{0u, 0u, 0u, 0u};
-          }
-          return;
-        }
-      }
-      if constexpr (A_KMAJOR) {
+      for (int t = 0; t < 8; ++t) buf_to_lds16(ra, aoff[t], As + (wave * 8 + t) * 512);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) g2lds(abase_m + aoff[t] + k0, As + (wave * 8 + t) * 512);
-      } else {
-        const bf16_t* base = P.a + static_cast<int64_t>(kbeg + k0) * lda;
-        const int left = kend - kbeg - k0;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          bf16_t* blk = As + (wave * 8 + t) * 512;
-          if ((wave * 8 + t) * 2 + (lane >> 5) < left) g2lds(base + aoff[t], blk);
-          else *reinterpret_cast<u32x4*>(blk + lane * 8) = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-      if constexpr (B_KMAJOR) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) g2lds(bbase[t] + boff[t] + k0, Bs + (wave * 8 + t) * 512);
-      } else {
-        const bf16_t* base;
-        int left = BK;
-        if constexpr (MODE == DGRAD_DOWN) {
-          base = P.b0 + static_cast<int64_t>(e) * H * I + static_cast<int64_t>(k0) * I;
-        } else if constexpr (MODE == DGRAD_GATEUP) {
-          base = k0 < I ? P.b0 + static_cast<int64_t>(e) * I * H + static_cast<int64_t>(k0) * H
-                        : P.b1 + static_cast<int64_t>(e) * I * H + static_cast<int64_t>(k0 - I) * H;
-        } else {
-          base = P.b0 + static_cast<int64_t>(kbeg + k0) * ldb;
-          left = kend - kbeg - k0;
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          bf16_t* blk = Bs + (wave * 8 + t) * 512;
-          if (grouped_k(MODE) && (wave * 8 + t) * 2 + (lane >> 5) >= left)
-            *reinterpret_cast<u32x4*>(blk + lane * 8) = u32x4{0u, 0u, 0u, 0u};
-          else
-            g2lds(base + boff[t], blk);
-        }
-      }
+      for (int t = 0; t < 8; ++t) buf_to_lds16(rb, boff[t], Bs + (wave * 8 + t) * 512);
+      buf_prefetch(rsrc_a(s + 1), pfa, sink);
+      buf_prefetch(rsrc_b(s + 1), pfb, sink);
     };
 
     // Operand fragments of k-slice kk (16 k) for 32-row block i, as byte
@@ -366,15 +427,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
     // One k-step on the stage at As: operand fragments of k-slice kk + 1
     // are read while the 16 MFMAs of slice kk run; scheduling fences keep the
     // slices apart so the reads' latency runs under the matrix work.
+    // Each k-step ends waiting for all but this wavefront's two newest
+    // vector-memory instructions: the L2 prefetches, which may stay in flight.
     auto compute = [&](const bf16_t* As) {
       const bf16_t* Bs = As + STAGE_A;
       // Opaque to the optimiser: keeps the per-slice addresses below from
       // being hoisted out of the k-loop (for both stages and all slices,
       // which would not fit in registers).
-#pragma unroll
-      for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(aof[i]));
-#pragma unroll
-      for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(bof[j]));
+
       bf16x8 av[2][FM], bv[2][FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) av[0][i] = frag(As, aof[i], 0, A_KMAJOR);
@@ -398,16 +458,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads of the next step have landed
-      __syncthreads();                // everyone's have, and this stage is free again
+      __builtin_amdgcn_s_waitcnt(kWaitVm2);  // this wavefront's loads of the next step have landed ...
+      step_barrier();                        // ... everyone's have, and this stage is free again
     };
 
     if (ksteps > 0) {
       issue(0, lds0);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(kWaitVm2);
+      step_barrier();
       // Steps go in pairs (stage 0, stage 1); an odd count gets one more
-      // step of zeros (weight-gradient rows past the end already read as 0).
+      // step, which reads as zeros (its buffer range is empty).
       const int ksteps2 = (ksteps + 1) & ~1;
       for (int s = 0; s < ksteps2; s += 2) {
         issue(s + 1, lds1);
