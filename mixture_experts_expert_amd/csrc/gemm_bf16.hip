@@ -23,9 +23,8 @@
 // Tile: 256 x 256 x 64 per workgroup of 4 wavefronts (2 x 2), 128 x 128 per
 // wavefront as 4 x 4 MFMA blocks of 32 x 32, accumulators in the register
 // file (256 fp32 per lane). Operands go straight from global memory into LDS
-// (global_load_lds_dwordx4: each wavefront instruction fills one contiguous
-// KiB, lane l at byte 16 l), two stages of 64 KiB, the next k-step's loads in
-// flight while the current one multiplies; no register staging and no LDS
+// (buffer_load ... lds: each wavefront instruction fills one contiguous KiB,
+// lane l at byte 16 l), two stages of 64 KiB; no register staging and no LDS
 // store phase. An operand whose reduction index is contiguous in memory
 // ("k-major": the forward operands, the data-gradient activations) sits in
 // LDS as [row][k], 16-byte chunks XOR-swizzled by row, and is read with
@@ -36,6 +35,16 @@
 // (within each 16-lane group, lane i receives element i%4 of the pieces that
 // lanes 4j + i/4 address). Either way the swizzle is applied on the global
 // side: each lane fetches the chunk that belongs at its fixed LDS slot.
+//
+// Pipeline: with one wavefront per SIMD nothing hides a stall, so every
+// k-step threads the next step's 16 load instructions between its MFMA
+// groups (the address unit takes about 64 bytes per clock per CU; issued in
+// one burst they would hold the wavefront for ~1000 clocks) and ends with one
+// wait and one barrier. A tile's last k-step loads the next tile's first, and
+// the epilogue works from registers (SwiGLU in place: gate and up of one
+// element share a lane; a DPP quad transpose and a half-wave swap turn the
+// MFMA layout into four-row x 128-byte store runs), so those loads land
+// while the results go out.
 //
 // Scheduling: one workgroup per CU, persistent. Tile i of the list belongs
 // to XCD-local workgroups: the list is cut into 8 contiguous ranges, one per
@@ -61,6 +70,12 @@ constexpr int STAGE_A = BM * BK;        // bf16 elements
 constexpr int STAGE_B = BN * BK;
 constexpr int STAGE = STAGE_A + STAGE_B;
 constexpr int GU_COLS = BN / 2;         // intermediate columns per GATEUP tile (gate + up)
+
+// Vector-memory instructions of a k-step issued before MFMA group g (of 16)
+// ends: kVmBefore[g + 1] - kVmBefore[g] of them follow group g. Front-loaded
+// (two per group over the first half) so the last load has half a step to
+// land; the two L2 prefetches follow group 8.
+constexpr int kVmBefore[17] = {0, 2, 4, 6, 8, 10, 12, 14, 16, 18, 18, 18, 18, 18, 18, 18, 18};
 
 enum Mode : int { GATEUP = 0, DOWN = 1, DGRAD_DOWN = 2, DGRAD_GATEUP = 3, WGRAD_DOWN = 4, WGRAD_GATEUP = 5 };
 
@@ -129,8 +144,8 @@ __device__ __forceinline__ void step_barrier() {
 // s_waitcnt immediates (gfx9 encoding): vmcnt in [3:0] and [15:14], expcnt in
 // [6:4], lgkmcnt in [11:8]. Both wait for LDS traffic and for all but the
 // newest `n` vector-memory instructions (expcnt left unconstrained).
-constexpr int kWaitVm0 = 0x0070;  // vmcnt(0) lgkmcnt(0)
 constexpr int kWaitVm2 = 0x0072;  // vmcnt(2) lgkmcnt(0)
+constexpr int kWaitAll = 0x0000;  // vmcnt(0) expcnt(0) lgkmcnt(0)
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -140,6 +155,106 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d)
   const f32x2 lo = {a, b}, hi = {c, d};
   return make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
                     __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2)));
+}
+
+// Epilogue helpers ------------------------------------------------------------
+
+// Raw-buffer loads and stores of 8 or 16 bytes per lane. A lane whose bytes
+// fall outside the resource's range reads zeros and writes nothing; kNoWrite
+// is an offset outside every range used here (all are below 2^31 bytes).
+constexpr uint32_t kNoWrite = 0x80000000u;
+__device__ __forceinline__ u32x2 load_b64(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x4 load_b128(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ void store_b64(u32x2 v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void store_b128(u32x4 v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ u32x2 pack_bf16x4v(const float (&v)[4]) {
+  return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Lane exchanges inside each quad of lanes (DPP quad_perm [1,0,3,2] and
+// [2,3,0,1]): the value of lane l ^ 1, of lane l ^ 2.
+__device__ __forceinline__ uint32_t quad_swap1(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t quad_swap2(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_swap1f(float v) { return __uint_as_float(quad_swap1(__float_as_uint(v))); }
+__device__ __forceinline__ float quad_swap2f(float v) { return __uint_as_float(quad_swap2(__float_as_uint(v))); }
+
+// 4 x 4 transpose across each quad of lanes. On entry lane c (= lane % 4)
+// holds column c of rows 0..3 in v[0..3]; on exit it holds row c, columns
+// 0..3. The first exchange pairs lanes across bit 1 (each keeps rows 0-1 or
+// rows 2-3, of columns c%2 and c%2 + 2), the second across bit 0.
+__device__ __forceinline__ void quad_transpose(float (&v)[4], int lane) {
+  const bool c1 = (lane & 2) != 0, c0 = (lane & 1) != 0;
+  const float x0 = quad_swap2f(c1 ? v[0] : v[2]);
+  const float x1 = quad_swap2f(c1 ? v[1] : v[3]);
+  const float a0 = c1 ? x0 : v[0], a1 = c1 ? x1 : v[1];  // rows 2 c1, 2 c1 + 1 of column c%2
+  const float a2 = c1 ? v[2] : x0, a3 = c1 ? v[3] : x1;  // the same rows of column c%2 + 2
+  const float y0 = quad_swap1f(c0 ? a0 : a1);
+  const float y1 = quad_swap1f(c0 ? a2 : a3);
+  v[0] = c0 ? y0 : a0;
+  v[1] = c0 ? a1 : y0;
+  v[2] = c0 ? y1 : a2;
+  v[3] = c0 ? a3 : y1;
+}
+
+// The same transpose for values bound for bf16: rounded (to nearest even)
+// and packed first, so the exchanges move half as many words; the second
+// exchange splices 16-bit halves with v_perm_b32 (selector bytes 0-3 pick
+// bytes of the second operand, 4-7 of the first). Returns row c, columns
+// 0..3, as four bf16.
+__device__ __forceinline__ u32x2 quad_transpose_bf16(const float (&v)[4], int lane) {
+  const bool c1 = (lane & 2) != 0, c0 = (lane & 1) != 0;
+  const uint32_t p0 = pack_bf16x2(v[0], v[1]);  // rows 0 (low half), 1 of column c
+  const uint32_t p1 = pack_bf16x2(v[2], v[3]);  // rows 2, 3
+  const uint32_t x = quad_swap2(c1 ? p0 : p1);
+  const uint32_t a0 = c1 ? x : p0;  // rows 2 c1, 2 c1 + 1 of column c%2
+  const uint32_t a1 = c1 ? p1 : x;  // the same rows of column c%2 + 2
+  const uint32_t y0 = quad_swap1(a0), y1 = quad_swap1(a1);
+  const uint32_t sel = c0 ? 0x03020706u : 0x05040100u;  // high halves / low halves, in column order
+  return u32x2{__builtin_amdgcn_perm(y0, a0, sel), __builtin_amdgcn_perm(y1, a1, sel)};
+}
+
+// Swap of wavefront halves between two registers: afterwards x holds the
+// low 32 lanes of both inputs (x's in lanes 0-31, y's in lanes 32-63), y the
+// high 32 lanes of both (v_permlane32_swap).
+__device__ __forceinline__ void swap_halves(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
+__device__ __forceinline__ void swap_halves(u32x2& x, u32x2& y) {
+  uint32_t x0 = x.x, x1 = x.y, y0 = y.x, y1 = y.y;
+  swap_halves(x0, y0);
+  swap_halves(x1, y1);
+  x = u32x2{x0, x1};
+  y = u32x2{y0, y1};
+}
+__device__ __forceinline__ void swap_halves(float (&x)[4], float (&y)[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t a = __float_as_uint(x[q]), b = __float_as_uint(y[q]);
+    swap_halves(a, b);
+    x[q] = __uint_as_float(a);
+    y[q] = __uint_as_float(b);
+  }
 }
 
 template <int MODE>
@@ -156,6 +271,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const int lane_id = lane;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
   const int wm = wave >> 1, wn = wave & 1;
   const int H = P.H, E = P.E, I = P.I;
@@ -214,60 +330,74 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   constexpr bool A_KMAJOR = !grouped_k(MODE);
   constexpr bool B_KMAJOR = b_kcontig(MODE);
 
-  for (int L = lo + slot; L < hi; L += nslots) {
-    // ---- decode the tile ---------------------------------------------------
-    int e, row0 = 0, mvalid = 0, m0 = 0, n0 = 0, nt = 0, kbeg = 0, kend = 0;
+  // ---- tile state ------------------------------------------------------------
+  // Everything the operand loads of a tile depend on. A tile's last k-step
+  // already loads the next tile's first one, so the state moves on to the
+  // next tile before the finished tile's epilogue, which keeps its own copy
+  // of the few scalars it needs.
+  int lda = 0, ldb = 0, kfixed = 0;
+  if constexpr (MODE == GATEUP) { lda = H; kfixed = H / BK; }
+  if constexpr (MODE == DOWN) { lda = I; kfixed = I / BK; }
+  if constexpr (MODE == DGRAD_DOWN) { lda = H; ldb = I; kfixed = H / BK; }
+  if constexpr (MODE == DGRAD_GATEUP) { lda = 2 * I; ldb = H; kfixed = 2 * I / BK; }
+  if constexpr (MODE == WGRAD_DOWN) { lda = H; ldb = I; }
+  if constexpr (MODE == WGRAD_GATEUP) { lda = 2 * I; ldb = H; }
+
+  int e = 0, row0 = 0, mvalid = 0, m0 = 0, n0 = 0, kbeg = 0, kend = 0, ksteps = 0;
+  uint32_t aoff[8], boff[8], pfa = 0, pfb = 0;
+  const bf16_t* abase_m = P.a;  // grouped-M: the tile's first row of A
+
+  auto set_tile = [&](int L) {
+    int te, trow0 = 0, tmvalid = 0, tm0 = 0, tn0 = 0, tkbeg = 0, tkend = 0;
     if constexpr (!grouped_k(MODE)) {
       int l2 = 0, h2 = E - 1;
       while (l2 < h2) {
         const int mid = (l2 + h2 + 1) >> 1;
         if (tstart[mid] * ntn <= L) l2 = mid; else h2 = mid - 1;
       }
-      e = l2;
-      const int rem = L - tstart[e] * ntn;
-      const int mte = tstart[e + 1] - tstart[e];
-      nt = rem / mte;
+      te = l2;
+      const int rem = L - tstart[te] * ntn;
+      const int mte = tstart[te + 1] - tstart[te];
+      const int nt = rem / mte;
       const int mt = rem - nt * mte;
-      row0 = P.offsets[e] + mt * BM;
-      mvalid = min(BM, P.offsets[e + 1] - row0);
-      n0 = nt * (MODE == GATEUP ? GU_COLS : BN);
+      trow0 = P.offsets[te] + mt * BM;
+      tmvalid = min(BM, P.offsets[te + 1] - trow0);
+      tn0 = nt * (MODE == GATEUP ? GU_COLS : BN);
     } else {
-      e = L / tpe;
-      const int rem = L - e * tpe;
+      te = L / tpe;
+      const int rem = L - te * tpe;
       const int mt = rem / ntn;
-      nt = rem - mt * ntn;
-      m0 = mt * BM;
-      n0 = nt * BN;
-      kbeg = P.offsets[e];
-      kend = P.offsets[e + 1];
+      const int nt = rem - mt * ntn;
+      tm0 = mt * BM;
+      tn0 = nt * BN;
+      tkbeg = P.offsets[te];
+      tkend = P.offsets[te + 1];
     }
-
     // The decode is the same on every lane; say so, so that the operand
     // bases live in scalar registers and the loads use the scalar-base form.
-    e = __builtin_amdgcn_readfirstlane(e);
-    row0 = __builtin_amdgcn_readfirstlane(row0);
-    mvalid = __builtin_amdgcn_readfirstlane(mvalid);
-    m0 = __builtin_amdgcn_readfirstlane(m0);
-    n0 = __builtin_amdgcn_readfirstlane(n0);
-    kbeg = __builtin_amdgcn_readfirstlane(kbeg);
-    kend = __builtin_amdgcn_readfirstlane(kend);
-
-    int ksteps, lda = 0, ldb = 0;
-    if constexpr (MODE == GATEUP) { lda = H; ksteps = H / BK; }
-    if constexpr (MODE == DOWN) { lda = I; ksteps = I / BK; }
-    if constexpr (MODE == DGRAD_DOWN) { lda = H; ldb = I; ksteps = H / BK; }
-    if constexpr (MODE == DGRAD_GATEUP) { lda = 2 * I; ldb = H; ksteps = 2 * I / BK; }
-    if constexpr (MODE == WGRAD_DOWN) { lda = H; ldb = I; ksteps = (kend - kbeg + BK - 1) / BK; }
-    if constexpr (MODE == WGRAD_GATEUP) { lda = 2 * I; ldb = H; ksteps = (kend - kbeg + BK - 1) / BK; }
-
-    // ---- per-lane byte offsets of this wavefront's 8 + 8 load instructions,
+    e = __builtin_amdgcn_readfirstlane(te);
+    row0 = __builtin_amdgcn_readfirstlane(trow0);
+    mvalid = __builtin_amdgcn_readfirstlane(tmvalid);
+    m0 = __builtin_amdgcn_readfirstlane(tm0);
+    n0 = __builtin_amdgcn_readfirstlane(tn0);
+    kbeg = __builtin_amdgcn_readfirstlane(tkbeg);
+    kend = __builtin_amdgcn_readfirstlane(tkend);
+    ksteps = grouped_k(MODE) ? (kend - kbeg + BK - 1) / BK : kfixed;
+  };
+  // Per-lane load offsets of the current tile (vector registers; recomputed
+  // rather than kept alive across an epilogue).
+  auto set_offsets = [&]() {
+    // An opaque copy of the lane index keeps the lane-only parts of these
+    // offsets from being hoisted out of the tile loop (and spilled).
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    // Per-lane byte offsets of this wavefront's 8 + 8 load instructions,
     // relative to the operand's base at the current k-step; instruction t
     // fills LDS block wave*8 + t (1 KiB) of each operand stage. Rows and
     // columns past the operand's end are clamped to its last one (their
     // products land in rows or columns that are never stored). k-major:
     // LDS row r = 8 (wave*8 + t) + lane/8, chunk lane%8 (swizzled). mn-major:
     // k-row 2 (wave*8 + t) + lane/32, chunk lane%32 (swizzled).
-    uint32_t aoff[8], boff[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int blk = wave * 8 + t;
@@ -301,276 +431,433 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
         boff[t] = 2u * (k * ldb + min(n0 + c * 8, ncols - 8));
       }
     }
-    const bf16_t* abase_m = P.a + static_cast<int64_t>(row0) * lda;  // grouped-M A
+    abase_m = P.a + static_cast<int64_t>(row0) * lda;
 
     // L2 prefetch offsets, one 128-byte line per lane per operand and k-step:
     // k-major operands, row wave*64 + lane (its 64 k of the step); mn-major
     // operands, k-row wave*16 + lane/4, line lane%4 of the 256 columns.
-    uint32_t pfa, pfb;
-    {
-      const int r = wave * 64 + lane;
-      const int kr = wave * 16 + (lane >> 2);
-      if constexpr (A_KMAJOR) {
-        pfa = 2u * (min(r, mvalid - 1) * lda);
-      } else {
-        const int mrows = MODE == WGRAD_DOWN ? H : 2 * I;
-        pfa = 2u * (kr * lda + min(m0 + (lane & 3) * 64, mrows - 64));
+    const int r = wave * 64 + lane;
+    const int kr = wave * 16 + (lane >> 2);
+    if constexpr (A_KMAJOR) {
+      pfa = 2u * (min(r, mvalid - 1) * lda);
+    } else {
+      const int mrows = MODE == WGRAD_DOWN ? H : 2 * I;
+      pfa = 2u * (kr * lda + min(m0 + (lane & 3) * 64, mrows - 64));
+    }
+    if constexpr (MODE == GATEUP) {
+      const int j = (r & 127) >> 5;
+      pfb = 2u * (min(n0 + (r >> 7) * 64 + (j & 1) * 32 + (r & 31), I - 1) * H);
+    } else if constexpr (MODE == DOWN) {
+      pfb = 2u * (min(n0 + r, H - 1) * I);
+    } else {
+      const int ncols = (MODE == DGRAD_DOWN || MODE == WGRAD_DOWN) ? I : H;
+      pfb = 2u * (kr * ldb + min(n0 + (lane & 3) * 64, ncols - 64));
+    }
+  };
+  // No next tile: every load of the chained step reads an empty range.
+  auto clear_tile = [&]() {
+    ksteps = 0;
+    kend = kbeg;
+  };
+  auto set_tile_and_offsets = [&](int L) {
+    set_tile(L);
+    set_offsets();
+  };
+
+  uint32_t* sink = pf_sink + wave * 64;
+
+  // Buffer resources of k-step s (num_records 0 past the last step).
+  auto rsrc_a = [&](int s) -> rsrc_t {
+    const int k0 = s * BK;
+    if constexpr (A_KMAJOR) {
+      return make_rsrc(abase_m + k0, s < ksteps ? 2 * (mvalid * lda - k0) : 0);
+    } else {
+      const int left = kend - kbeg - k0;
+      return make_rsrc(P.a + static_cast<int64_t>(kbeg + k0) * lda, left > 0 ? 2 * left * lda : 0);
+    }
+  };
+  auto rsrc_b = [&](int s) -> rsrc_t {
+    const int k0 = s * BK;
+    const bool live = s < ksteps;
+    if constexpr (MODE == GATEUP) {
+      const bf16_t* w = ((wave & 1) ? P.b1 : P.b0) + static_cast<int64_t>(e) * I * H + k0;
+      return make_rsrc(w, live ? 2 * (I * H - k0) : 0);
+    } else if constexpr (MODE == DOWN) {
+      return make_rsrc(P.b0 + static_cast<int64_t>(e) * H * I + k0, live ? 2 * (H * I - k0) : 0);
+    } else if constexpr (MODE == DGRAD_DOWN) {
+      return make_rsrc(P.b0 + static_cast<int64_t>(e) * H * I + static_cast<int64_t>(k0) * I,
+                       live ? 2 * (H - k0) * I : 0);
+    } else if constexpr (MODE == DGRAD_GATEUP) {
+      const bool up = k0 >= I;
+      const int kk0 = up ? k0 - I : k0;
+      return make_rsrc((up ? P.b1 : P.b0) + static_cast<int64_t>(e) * I * H + static_cast<int64_t>(kk0) * H,
+                       live ? 2 * (I - kk0) * H : 0);
+    } else {
+      const int left = kend - kbeg - k0;
+      return make_rsrc(P.b0 + static_cast<int64_t>(kbeg + k0) * ldb, left > 0 ? 2 * left * ldb : 0);
+    }
+  };
+
+  // Vector-memory instruction v of a k-step's 18, for step sn into the
+  // stage at L: v < 16 alternate A and B blocks (v/2 of each), 16 and 17
+  // are the L2 prefetches of step sn + 1.
+  auto vmem = [&](int v, const rsrc_t& ra, const rsrc_t& rb, bf16_t* L, int sn) {
+    if (v < 16) {
+      const int t = v >> 1;
+      if ((v & 1) == 0) buf_to_lds16(ra, aoff[t], L + (wave * 8 + t) * 512);
+      else buf_to_lds16(rb, boff[t], L + STAGE_A + (wave * 8 + t) * 512);
+    } else if (v == 16) {
+      buf_prefetch(rsrc_a(sn + 1), pfa, sink);
+    } else {
+      buf_prefetch(rsrc_b(sn + 1), pfb, sink);
+    }
+  };
+  // All 18 at once (the first step of a workgroup's first tile).
+  auto issue = [&](int s, bf16_t* L) {
+    const rsrc_t ra = rsrc_a(s);
+    const rsrc_t rb = rsrc_b(s);
+#pragma unroll
+    for (int v = 0; v < 18; ++v) vmem(v, ra, rb, L, s);
+  };
+
+  // Operand fragments of k-slice kk (16 k) for 32-row block i, as byte
+  // offsets inside a stage. k-major (ds_read_b128, lane: row i*32 + lane%32,
+  // chunk 2 kk + lane/32): the chunk XOR makes slice kk the slice-0 offset
+  // XOR 32 kk. mn-major (two ds_read_b64_tr_b16, lane: k-row
+  // 8 (lane/32) + (lane%16)/4, columns 4 (lane%4) .. + 3 of the block's
+  // 16-column half (lane/16)%2): slice kk adds 16 rows = 8 KiB, the second
+  // read 4 rows = 2 KiB.
+  int aof[FM], bof[FN];
+  // Computed at the start of every tile from an opaque copy of the lane
+  // index: alive through the k-loop only, not through the epilogue.
+  auto set_frag_offsets = [&]() {
+  int lane = lane_id;
+  asm volatile("" : "+v"(lane));
+  const int hi32 = lane >> 5;
+  const int g16 = lane >> 4, i16 = lane & 15;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    if constexpr (A_KMAJOR) {
+      const int r = wm * WTM + i * 32 + (lane & 31);
+      aof[i] = r * (BK * 2) + ((hi32 ^ swk(r)) << 4);
+    } else {
+      const int k = 8 * (g16 >> 1) + (i16 >> 2);
+      const int col = wm * WTM + i * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
+      aof[i] = k * 512 + (((col >> 3) ^ swt(k)) << 4) + ((col & 7) << 1);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    if constexpr (B_KMAJOR) {
+      const int r = wn * WTN + j * 32 + (lane & 31);
+      bof[j] = r * (BK * 2) + ((hi32 ^ swk(r)) << 4);
+    } else {
+      const int k = 8 * (g16 >> 1) + (i16 >> 2);
+      const int col = wn * WTN + j * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
+      bof[j] = k * 512 + (((col >> 3) ^ swt(k)) << 4) + ((col & 7) << 1);
+    }
+  }
+  };
+  auto frag = [&](const bf16_t* S, int off, int kk, bool kmajor) -> bf16x8 {
+    const char* base = reinterpret_cast<const char*>(S);
+    if (kmajor) return *reinterpret_cast<const bf16x8*>(base + (off ^ (kk * 32)));
+    const char* p = base + off + kk * 8192;
+    const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+    const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 2048));
+    const v4i16 both[2] = {lo4, hi4};
+    return __builtin_bit_cast(bf16x8, both);
+  };
+
+  f32x16 acc[FM][FN];
+
+  // One k-step: the 64 MFMAs on the stage at Ac, in 16 groups of four
+  // (k-slice kk, row block i), with the loads of step sn into the stage at
+  // Ln threaded between the groups (kVmBefore) so that the wavefront never
+  // stalls on a full address queue with matrix work waiting behind it.
+  // Fragments of slice kk + 1 are read while slice kk multiplies;
+  // scheduling fences keep every group where it is written. The step ends
+  // waiting for all but this wavefront's two newest vector-memory
+  // instructions (the L2 prefetches, which may stay in flight), then for
+  // the other wavefronts. A tile's last step (sync = false) skips both: the
+  // loads it issues are the next tile's first, and the wait for them comes
+  // after the epilogue.
+  auto kstep = [&](const bf16_t* Ac, int sn, bf16_t* Ln, bool sync) {
+    const bf16_t* Bc = Ac + STAGE_A;
+    const rsrc_t ra = rsrc_a(sn);
+    const rsrc_t rb = rsrc_b(sn);
+    bf16x8 av[2][FM], bv[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) av[0][i] = frag(Ac, aof[i], 0, A_KMAJOR);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bv[0][j] = frag(Bc, bof[j], 0, B_KMAJOR);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int cur = kk & 1;
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk + 1 < BK / 16) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) av[cur ^ 1][i] = frag(Ac, aof[i], kk + 1, A_KMAJOR);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bv[cur ^ 1][j] = frag(Bc, bof[j], kk + 1, B_KMAJOR);
       }
-      if constexpr (MODE == GATEUP) {
-        const int j = (r & 127) >> 5;
-        pfb = 2u * (min(n0 + (r >> 7) * 64 + (j & 1) * 32 + (r & 31), I - 1) * H);
-      } else if constexpr (MODE == DOWN) {
-        pfb = 2u * (min(n0 + r, H - 1) * I);
-      } else {
-        const int ncols = (MODE == DGRAD_DOWN || MODE == WGRAD_DOWN) ? I : H;
-        pfb = 2u * (kr * ldb + min(n0 + (lane & 3) * 64, ncols - 64));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        const int g = kk * FM + i;
+#pragma unroll
+        for (int v = kVmBefore[g]; v < kVmBefore[g + 1]; ++v) vmem(v, ra, rb, Ln, sn);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    uint32_t* sink = pf_sink + wave * 64;
+    if (sync) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm2);  // this wavefront's loads of step sn have landed ...
+      step_barrier();                        // ... everyone's have, and the stage at Ac is free again
+    }
+  };
 
-    // Buffer resources of k-step s (num_records 0 past the last step).
-    auto rsrc_a = [&](int s) -> rsrc_t {
-      const int k0 = s * BK;
-      if constexpr (A_KMAJOR) {
-        return make_rsrc(abase_m + k0, s < ksteps ? 2 * (mvalid * lda - k0) : 0);
-      } else {
-        const int left = kend - kbeg - k0;
-        return make_rsrc(P.a + static_cast<int64_t>(kbeg + k0) * lda, left > 0 ? 2 * left * lda : 0);
+  // ---- epilogue -------------------------------------------------------------
+  // acc[i][j][q] holds wavefront-tile row i*32 + 8*(q/4) + 4*(lane/32) + q%4,
+  // column j*32 + lane%32. A quad transpose of each group of four q leaves
+  // lane l with row i*32 + 8*(q/4) + erow, columns j*32 + ecol .. + 3, so
+  // every lane stores four consecutive columns of one row. Results go out
+  // straight from registers through buffer resources whose range ends at the
+  // tile's last valid row; columns past the output's end get an offset
+  // outside every range. No LDS and no barriers: the next tile's first
+  // loads, already in flight, land meanwhile.
+  auto epilogue = [&](int te, int trow0, int tmvalid, int tm0, int tn0) {
+    // Lane-only terms from an opaque copy of the lane index, so that they
+    // are not hoisted out of the tile loop (and spilled).
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    // After the quad transpose, a swap of the wavefront halves between the
+    // column blocks 2 jp and 2 jp + 1 leaves lane l with row 8*(q/4) + prow
+    // (first result) or that + 4 (second), columns 64 jp + pcol .. + 3: each
+    // store covers four rows, 64 contiguous columns of each.
+    const int prow = lane & 3;
+    const int pcol = lane & ~3;
+    if constexpr (MODE == GATEUP) {
+      // Wavefront-tile columns 0..63 are gate, 64..127 up, for the same 64
+      // intermediate indices: G, U and A = silu(G) U of one element sit in
+      // one lane.
+      const int64_t base = static_cast<int64_t>(trow0) * I;
+      const int bytes = 2 * tmvalid * I;
+      const rsrc_t rg = make_rsrc(P.out0 + base, bytes);
+      const rsrc_t ru = make_rsrc(P.out1 + base, bytes);
+      const rsrc_t rs = make_rsrc(P.out2 + base, bytes);
+      const int idx = tn0 + wn * 64 + pcol;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int r = wm * WTM + i * 32 + 8 * b + prow;
+          const uint32_t off = idx < I ? 2u * static_cast<uint32_t>(r * I + idx) : kNoWrite;
+          const uint32_t off4 = idx < I ? off + 8u * I : kNoWrite;
+          u32x2 gp[2], up[2], ap[2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            float g[4], u[4], a[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              g[q] = acc[i][j][4 * b + q];
+              u[q] = acc[i][j + 2][4 * b + q];
+              a[q] = g[q] * sigmoidf_dev(g[q]) * u[q];
+            }
+            gp[j] = quad_transpose_bf16(g, lane);
+            up[j] = quad_transpose_bf16(u, lane);
+            ap[j] = quad_transpose_bf16(a, lane);
+          }
+          swap_halves(gp[0], gp[1]);
+          swap_halves(up[0], up[1]);
+          swap_halves(ap[0], ap[1]);
+          store_b64(gp[0], rg, off);
+          store_b64(gp[1], rg, off4);
+          store_b64(up[0], ru, off);
+          store_b64(up[1], ru, off4);
+          store_b64(ap[0], rs, off);
+          store_b64(ap[1], rs, off4);
+        }
+    } else if constexpr (MODE == DOWN || MODE == DGRAD_GATEUP) {
+      const rsrc_t ro = make_rsrc(P.out0 + static_cast<int64_t>(trow0) * H, 2 * tmvalid * H);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jp = 0; jp < FN / 2; ++jp)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int r = wm * WTM + i * 32 + 8 * b + prow;
+            const int n = tn0 + wn * WTN + jp * 64 + pcol;
+            const uint32_t off = n < H ? 2u * static_cast<uint32_t>(r * H + n) : kNoWrite;
+            const uint32_t off4 = n < H ? off + 8u * H : kNoWrite;
+            u32x2 t[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              float v[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[q] = acc[i][2 * jp + j][4 * b + q];
+              t[j] = quad_transpose_bf16(v, lane);
+            }
+            swap_halves(t[0], t[1]);
+            store_b64(t[0], ro, off);
+            store_b64(t[1], ro, off4);
+          }
+    } else if constexpr (MODE == DGRAD_DOWN) {
+      // dA -> dG = dA U silu'(G), dU = dA silu(G), with the saved G and U of
+      // the same rows; written side by side as [dG | dU] (row length 2I).
+      const int64_t base = static_cast<int64_t>(trow0) * I;
+      const rsrc_t rg = make_rsrc(P.g_in + base, 2 * tmvalid * I);
+      const rsrc_t ru = make_rsrc(P.u_in + base, 2 * tmvalid * I);
+      const rsrc_t ro = make_rsrc(P.out0 + 2 * base, 4 * tmvalid * I);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        // All of a row block's saved G and U first, so that their latency
+        // overlaps.
+        u32x2 gb[FN / 2][4][2], ub[FN / 2][4][2];
+#pragma unroll
+        for (int jp = 0; jp < FN / 2; ++jp)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int r = wm * WTM + i * 32 + 8 * b + prow;
+            const int n = tn0 + wn * WTN + jp * 64 + pcol;
+            const uint32_t off = n < I ? 2u * static_cast<uint32_t>(r * I + n) : kNoWrite;
+            const uint32_t off4 = n < I ? off + 8u * I : kNoWrite;
+            gb[jp][b][0] = load_b64(rg, off);
+            gb[jp][b][1] = load_b64(rg, off4);
+            ub[jp][b][0] = load_b64(ru, off);
+            ub[jp][b][1] = load_b64(ru, off4);
+          }
+#pragma unroll
+        for (int jp = 0; jp < FN / 2; ++jp)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int r = wm * WTM + i * 32 + 8 * b + prow;
+            const int n = tn0 + wn * WTN + jp * 64 + pcol;
+            float da[2][4];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) da[j][q] = acc[i][2 * jp + j][4 * b + q];
+              quad_transpose(da[j], lane);
+            }
+            swap_halves(da[0], da[1]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const u32x2 gw = gb[jp][b][h], uw = ub[jp][b][h];
+              const float gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
+              const float uv[4] = {bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y)};
+              float dg[4], du[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float sg = sigmoidf_dev(gv[q]);
+                dg[q] = da[h][q] * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
+                du[q] = da[h][q] * (gv[q] * sg);
+              }
+              const uint32_t off = n < I ? 2u * static_cast<uint32_t>((r + 4 * h) * 2 * I + n) : kNoWrite;
+              store_b64(pack_bf16x4v(dg), ro, off);
+              store_b64(pack_bf16x4v(du), ro, off == kNoWrite ? kNoWrite : off + 2u * I);
+            }
+          }
       }
-    };
-    auto rsrc_b = [&](int s) -> rsrc_t {
-      const int k0 = s * BK;
-      const bool live = s < ksteps;
-      if constexpr (MODE == GATEUP) {
-        const bf16_t* w = ((wave & 1) ? P.b1 : P.b0) + static_cast<int64_t>(e) * I * H + k0;
-        return make_rsrc(w, live ? 2 * (I * H - k0) : 0);
-      } else if constexpr (MODE == DOWN) {
-        return make_rsrc(P.b0 + static_cast<int64_t>(e) * H * I + k0, live ? 2 * (H * I - k0) : 0);
-      } else if constexpr (MODE == DGRAD_DOWN) {
-        return make_rsrc(P.b0 + static_cast<int64_t>(e) * H * I + static_cast<int64_t>(k0) * I,
-                         live ? 2 * (H - k0) * I : 0);
-      } else if constexpr (MODE == DGRAD_GATEUP) {
-        const bool up = k0 >= I;
-        const int kk0 = up ? k0 - I : k0;
-        return make_rsrc((up ? P.b1 : P.b0) + static_cast<int64_t>(e) * I * H + static_cast<int64_t>(kk0) * H,
-                         live ? 2 * (I - kk0) * H : 0);
-      } else {
-        const int left = kend - kbeg - k0;
-        return make_rsrc(P.b0 + static_cast<int64_t>(kbeg + k0) * ldb, left > 0 ? 2 * left * ldb : 0);
-      }
-    };
-
-    // Issue every load of k-step s into the stage at As, then the L2 prefetch
-    // of step s + 1 (always exactly two more vector-memory instructions).
-    auto issue = [&](int s, bf16_t* As) {
-      bf16_t* Bs = As + STAGE_A;
-      const rsrc_t ra = rsrc_a(s);
-      const rsrc_t rb = rsrc_b(s);
+    } else {
+      // fp32 weight gradient of expert te, rows m0.., columns n0..; a 32-row
+      // block lies wholly in dW_gate or wholly in dW_up (I % 64 == 0).
+      const int mrows = MODE == WGRAD_DOWN ? H : 2 * I;
+      const int ncols = MODE == WGRAD_DOWN ? I : H;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) buf_to_lds16(ra, aoff[t], As + (wave * 8 + t) * 512);
+      for (int i = 0; i < FM; ++i) {
+        const int mblk = tm0 + wm * WTM + i * 32;
+        if (mblk >= mrows) continue;
+        float* dst;
+        if constexpr (MODE == WGRAD_DOWN) {
+          dst = P.dw0 + (static_cast<int64_t>(te) * H + mblk) * I;
+        } else {
+          dst = mblk < I ? P.dw0 + (static_cast<int64_t>(te) * I + mblk) * H
+                         : P.dw1 + (static_cast<int64_t>(te) * I + (mblk - I)) * H;
+        }
+        const rsrc_t ro = make_rsrc(dst, 32 * ncols * 4);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) buf_to_lds16(rb, boff[t], Bs + (wave * 8 + t) * 512);
-      buf_prefetch(rsrc_a(s + 1), pfa, sink);
-      buf_prefetch(rsrc_b(s + 1), pfb, sink);
-    };
-
-    // Operand fragments of k-slice kk (16 k) for 32-row block i, as byte
-    // offsets inside a stage. k-major (ds_read_b128, lane: row i*32 + lane%32,
-    // chunk 2 kk + lane/32): the chunk XOR makes slice kk the slice-0 offset
-    // XOR 32 kk. mn-major (two ds_read_b64_tr_b16, lane: k-row
-    // 8 (lane/32) + (lane%16)/4, columns 4 (lane%4) .. + 3 of the block's
-    // 16-column half (lane/16)%2): slice kk adds 16 rows = 8 KiB, the second
-    // read 4 rows = 2 KiB.
-    const int hi32 = lane >> 5;
-    const int g16 = lane >> 4, i16 = lane & 15;
-    int aof[FM], bof[FN];
+        for (int jp = 0; jp < FN / 2; ++jp) {
+          const int n = tn0 + wn * WTN + jp * 64 + pcol;
+          u32x4 old[4][2];
+          if (P.accumulate) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if constexpr (A_KMAJOR) {
-        const int r = wm * WTM + i * 32 + (lane & 31);
-        aof[i] = r * (BK * 2) + ((hi32 ^ swk(r)) << 4);
-      } else {
-        const int k = 8 * (g16 >> 1) + (i16 >> 2);
-        const int col = wm * WTM + i * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
-        aof[i] = k * 512 + (((col >> 3) ^ swt(k)) << 4) + ((col & 7) << 1);
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+                old[b][h] = load_b128(ro, n < ncols ? 4u * static_cast<uint32_t>((8 * b + 4 * h + prow) * ncols + n)
+                                                    : kNoWrite);
+          }
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            float v[2][4];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[j][q] = acc[i][2 * jp + j][4 * b + q];
+              quad_transpose(v[j], lane);
+            }
+            swap_halves(v[0], v[1]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              if (P.accumulate) {
+                v[h][0] += __uint_as_float(old[b][h].x);
+                v[h][1] += __uint_as_float(old[b][h].y);
+                v[h][2] += __uint_as_float(old[b][h].z);
+                v[h][3] += __uint_as_float(old[b][h].w);
+              }
+              const uint32_t off =
+                  n < ncols ? 4u * static_cast<uint32_t>((8 * b + 4 * h + prow) * ncols + n) : kNoWrite;
+              store_b128(u32x4{__float_as_uint(v[h][0]), __float_as_uint(v[h][1]), __float_as_uint(v[h][2]),
+                               __float_as_uint(v[h][3])},
+                         ro, off);
+            }
+          }
+        }
       }
     }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      if constexpr (B_KMAJOR) {
-        const int r = wn * WTN + j * 32 + (lane & 31);
-        bof[j] = r * (BK * 2) + ((hi32 ^ swk(r)) << 4);
-      } else {
-        const int k = 8 * (g16 >> 1) + (i16 >> 2);
-        const int col = wn * WTN + j * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
-        bof[j] = k * 512 + (((col >> 3) ^ swt(k)) << 4) + ((col & 7) << 1);
-      }
-    }
-    auto frag = [&](const bf16_t* S, int off, int kk, bool kmajor) -> bf16x8 {
-      const char* base = reinterpret_cast<const char*>(S);
-      if (kmajor) return *reinterpret_cast<const bf16x8*>(base + (off ^ (kk * 32)));
-      const char* p = base + off + kk * 8192;
-      const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
-      const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 2048));
-      const v4i16 both[2] = {lo4, hi4};
-      return __builtin_bit_cast(bf16x8, both);
-    };
+  };
 
-    f32x16 acc[FM][FN];
+  // ---- tile loop ---------------------------------------------------------------
+  int L = lo + slot;
+  if (L < hi) {
+    set_tile_and_offsets(L);
+    issue(0, lds0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm2);
+    step_barrier();
+  }
+  for (; L < hi; L += nslots) {
+    set_frag_offsets();
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-
-    // One k-step on the stage at As: operand fragments of k-slice kk + 1
-    // are read while the 16 MFMAs of slice kk run; scheduling fences keep the
-    // slices apart so the reads' latency runs under the matrix work.
-    // Each k-step ends waiting for all but this wavefront's two newest
-    // vector-memory instructions: the L2 prefetches, which may stay in flight.
-    auto compute = [&](const bf16_t* As) {
-      const bf16_t* Bs = As + STAGE_A;
-      // Opaque to the optimiser: keeps the per-slice addresses below from
-      // being hoisted out of the k-loop (for both stages and all slices,
-      // which would not fit in registers).
-
-      bf16x8 av[2][FM], bv[2][FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) av[0][i] = frag(As, aof[i], 0, A_KMAJOR);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bv[0][j] = frag(Bs, bof[j], 0, B_KMAJOR);
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int cur = kk & 1;
-        __builtin_amdgcn_sched_barrier(0);
-        if (kk + 1 < BK / 16) {
-#pragma unroll
-          for (int i = 0; i < FM; ++i) av[cur ^ 1][i] = frag(As, aof[i], kk + 1, A_KMAJOR);
-#pragma unroll
-          for (int j = 0; j < FN; ++j) bv[cur ^ 1][j] = frag(Bs, bof[j], kk + 1, B_KMAJOR);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(kWaitVm2);  // this wavefront's loads of the next step have landed ...
-      step_barrier();                        // ... everyone's have, and this stage is free again
-    };
-
-    if (ksteps > 0) {
-      issue(0, lds0);
-      __builtin_amdgcn_s_waitcnt(kWaitVm2);
-      step_barrier();
-      // Steps go in pairs (stage 0, stage 1); an odd count gets one more
-      // step, which reads as zeros (its buffer range is empty).
-      const int ksteps2 = (ksteps + 1) & ~1;
-      for (int s = 0; s < ksteps2; s += 2) {
-        issue(s + 1, lds1);
-        compute(lds0);
-        if (s + 2 < ksteps2) issue(s + 2, lds0);
-        compute(lds1);
-      }
+    // Steps go in pairs (stage 0, stage 1), at least one pair; a padding
+    // step (odd count, or an empty reduction) reads as zeros.
+    const int ksteps2 = max(2, (ksteps + 1) & ~1);
+    for (int s = 0; s + 2 < ksteps2; s += 2) {
+      kstep(lds0, s + 1, lds1, true);
+      kstep(lds1, s + 2, lds0, true);
     }
-
-    // ---- epilogue -------------------------------------------------------------
-    // acc[i][j][q] holds wavefront-tile row i*32 + 8*(q/4) + 4*(lane/32) + q%4,
-    // column j*32 + lane%32. Each 32-row block goes through this wavefront's
-    // 16 KiB slice of LDS (fp32, [32][128]) and leaves as row-contiguous
-    // vectors: 4 columns per lane, 32 lanes per 128-column row.
-    float* stage = reinterpret_cast<float*>(lds0) + wave * (32 * WTN);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-          stage[(8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * WTN + j * 32 + (lane & 31)] = acc[i][j][q];
-      __syncthreads();
-      const int trow0 = wm * WTM + i * 32;  // tile row of stage row 0
-      if constexpr (MODE == GATEUP) {
-        // Columns 0..63 of the wavefront tile are gate, 64..127 up, for the
-        // same 64 intermediate indices.
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-          const int r = it * 4 + (lane >> 4);
-          const int c = (lane & 15) * 4;
-          const int tr = trow0 + r;
-          const int idx = n0 + wn * 64 + c;
-          if (tr < mvalid && idx < I) {
-            const float4 gv = *reinterpret_cast<const float4*>(stage + r * WTN + c);
-            const float4 uv = *reinterpret_cast<const float4*>(stage + r * WTN + 64 + c);
-            const float av[4] = {gv.x * sigmoidf_dev(gv.x) * uv.x, gv.y * sigmoidf_dev(gv.y) * uv.y,
-                                 gv.z * sigmoidf_dev(gv.z) * uv.z, gv.w * sigmoidf_dev(gv.w) * uv.w};
-            const int64_t o = static_cast<int64_t>(row0 + tr) * I + idx;
-            *reinterpret_cast<uint2*>(P.out0 + o) = pack_bf16x4(gv.x, gv.y, gv.z, gv.w);
-            *reinterpret_cast<uint2*>(P.out1 + o) = pack_bf16x4(uv.x, uv.y, uv.z, uv.w);
-            *reinterpret_cast<uint2*>(P.out2 + o) = pack_bf16x4(av[0], av[1], av[2], av[3]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int it = 0; it < 16; ++it) {
-          const int r = it * 2 + (lane >> 5);
-          const int c = (lane & 31) * 4;
-          const int tr = trow0 + r;
-          const float4 v = *reinterpret_cast<const float4*>(stage + r * WTN + c);
-          const int n = n0 + wn * WTN + c;
-          if constexpr (MODE == DOWN || MODE == DGRAD_GATEUP) {
-            if (tr < mvalid && n < H)
-              *reinterpret_cast<uint2*>(P.out0 + static_cast<int64_t>(row0 + tr) * H + n) =
-                  pack_bf16x4(v.x, v.y, v.z, v.w);
-          } else if constexpr (MODE == DGRAD_DOWN) {
-            if (tr < mvalid && n < I) {
-              const int64_t p = row0 + tr;
-              const uint2 gb = *reinterpret_cast<const uint2*>(P.g_in + p * I + n);
-              const uint2 ub = *reinterpret_cast<const uint2*>(P.u_in + p * I + n);
-              const float gv[4] = {__uint_as_float(gb.x << 16), __uint_as_float(gb.x & 0xffff0000u),
-                                   __uint_as_float(gb.y << 16), __uint_as_float(gb.y & 0xffff0000u)};
-              const float uv[4] = {__uint_as_float(ub.x << 16), __uint_as_float(ub.x & 0xffff0000u),
-                                   __uint_as_float(ub.y << 16), __uint_as_float(ub.y & 0xffff0000u)};
-              const float da[4] = {v.x, v.y, v.z, v.w};
-              float dg[4], du[4];
-#pragma unroll
-              for (int e2 = 0; e2 < 4; ++e2) {
-                const float sg = sigmoidf_dev(gv[e2]);
-                dg[e2] = da[e2] * uv[e2] * sg * (1.0f + gv[e2] * (1.0f - sg));
-                du[e2] = da[e2] * (gv[e2] * sg);
-              }
-              *reinterpret_cast<uint2*>(P.out0 + p * 2 * I + n) = pack_bf16x4(dg[0], dg[1], dg[2], dg[3]);
-              *reinterpret_cast<uint2*>(P.out0 + p * 2 * I + I + n) = pack_bf16x4(du[0], du[1], du[2], du[3]);
-            }
-          } else {
-            const int mrows = MODE == WGRAD_DOWN ? H : 2 * I;
-            const int ncols = MODE == WGRAD_DOWN ? I : H;
-            const int m = m0 + tr;
-            if (m < mrows && n < ncols) {
-              float* dst;
-              if constexpr (MODE == WGRAD_DOWN) {
-                dst = P.dw0 + (static_cast<int64_t>(e) * H + m) * I + n;
-              } else {
-                dst = m < I ? P.dw0 + (static_cast<int64_t>(e) * I + m) * H + n
-                            : P.dw1 + (static_cast<int64_t>(e) * I + (m - I)) * H + n;
-              }
-              float4 o = v;
-              if (P.accumulate) {
-                const float4 old = *reinterpret_cast<const float4*>(dst);
-                o.x += old.x;
-                o.y += old.y;
-                o.z += old.z;
-                o.w += old.w;
-              }
-              *reinterpret_cast<float4*>(dst) = o;
-            }
-          }
-        }
-      }
-      __syncthreads();  // the slice is rewritten by the next block (or the next tile's loads)
-    }
+    kstep(lds0, ksteps2 - 1, lds1, true);
+    const int fe = e, frow0 = row0, fmvalid = mvalid, fm0 = m0, fn0 = n0;
+    if (L + nslots < hi) set_tile_and_offsets(L + nslots);
+    else clear_tile();
+    kstep(lds1, 0, lds0, false);  // the last step; its loads are the next tile's first
+    epilogue(fe, frow0, fmvalid, fm0, fn0);
+    // The next tile's first step has landed (everything this wavefront
+    // issued has: loads and the epilogue's stores, which the counter does
+    // not order against each other) in every wavefront, and all are done
+    // with the last stage.
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    step_barrier();
+    // The offsets again rather than kept alive through the epilogue (the
+    // opaque lane index in set_offsets makes this a real recomputation).
+    set_offsets();
   }
 }
 
