@@ -10,15 +10,21 @@ router backward, every step a call of the C ABI (the six GEMMs through their
 one-kernel entry points, which is what moe_grouped_gemm_fwd/bwd chain).
 
 Prints one JSON line. `value` is tokens/s of the whole stage; TFLOP/s counts
-the expert GEMMs (18*T*k*H*I per step). `roofline` covers the dominant kernel:
-its algorithmic flops per launch over its average launch time, measured with
-HIP events around that kernel's call on the stream it runs on, against the
-bf16 dense MFMA peak. `cpu_baseline` times the CPU oracle on a bounded token
-sample of the same workload.
+the expert GEMMs (18*T*k*H*I per step). `roofline` covers the dominant kernel
+(the call with the largest average time): its algorithmic flops or bytes per
+launch (whichever of the MFMA and HBM minimum times is larger decides the
+bound) over its average launch time, measured with HIP events around that
+call on the stream it runs on. `traffic` is the HBM bytes per launch that
+rocprofv3's FETCH_SIZE and WRITE_SIZE counters gave for that kernel, scaled by
+what they read for a plain device copy of known size (--calibrate-copy); it is
+taken from the committed summary under profiles/ and reported only while the
+GEMM source still hashes to the value recorded there. `cpu_baseline` times
+the CPU oracle on a bounded token sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +40,72 @@ PEAK_HBM_GBS = 8000.0
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_expert_amd", "csrc", "gemm_bf16.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def alg_bytes(c) -> dict:
+    """Algorithmic HBM bytes of every call per launch: each tensor read or
+    written once (weights once per kernel), indices included."""
+    T, H, E, k, I = c.T, c.H, c.E, c.k, c.I
+    M = T * k
+    b16, f32, i32 = 2, 4, 4
+    return {
+        "moe_route": T * H * b16 + E * H * b16 + T * E * f32 + 2 * M * i32,
+        "moe_permute": M * i32 + T * H * b16 + 2 * M * i32 + M * H * b16,
+        "moe_gemm_gate_up": M * H * b16 + 2 * E * I * H * b16 + 3 * M * I * b16,
+        "moe_gemm_down": M * I * b16 + E * H * I * b16 + M * H * b16,
+        "moe_combine": M * H * b16 + 2 * M * i32 + T * H * b16,
+        "moe_combine_bwd": T * H * b16 + M * H * b16 + 2 * M * i32 + M * H * b16 + M * f32,
+        "moe_gemm_down_dgrad": M * H * b16 + E * H * I * b16 + 2 * M * I * b16 + 2 * M * I * b16,
+        "moe_gemm_down_wgrad": M * H * b16 + M * I * b16 + E * H * I * f32,
+        "moe_gemm_gate_up_dgrad": 2 * M * I * b16 + 2 * E * I * H * b16 + M * H * b16,
+        "moe_gemm_gate_up_wgrad": 2 * M * I * b16 + M * H * b16 + 2 * E * I * H * f32,
+        "moe_unpermute_sum": M * H * b16 + M * i32 + T * H * b16,
+        "moe_route_bwd": 3 * M * i32 + T * E * f32,
+    }
+
+
+def source_hash() -> str:
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def profiled_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from profiles/<kernel>.<workload>.traffic.txt,
+    or None when there is no such summary or the GEMM source changed since."""
+    path = os.path.join(PROFILES, f"{kernel}.{workload}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                rec[key.strip()] = val.strip()
+    if rec.get("gemm_source_sha256_16") != source_hash():
+        return None
+    try:
+        return int(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(nbytes: int, reps: int) -> int:
+    """A plain device-to-device copy of known size, for scaling the PMC byte
+    counters (run under rocprofv3 --pmc)."""
+    import torch
+
+    torch.cuda.set_device(0)
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "reps": reps}), flush=True)
+    return 0
 
 
 def gemm_flops(c) -> dict:
@@ -76,8 +148,12 @@ def main() -> int:
     ap.add_argument("--workload", default="qwen3_30b_a3b_train")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (PMC counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        return calibrate_copy(args.calibrate_copy, 3)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -153,11 +229,28 @@ def main() -> int:
     log(f"timed {args.steps} steps: {ms:.3f} ms/step; " + ", ".join(f"{n}={v:.3f}" for n, v in per_call.items()))
 
     flops = gemm_flops(cfg)
+    nbytes = alg_bytes(cfg)
     step_flops = sum(flops.values())
     tflops = step_flops / (ms * 1e-3) / 1e12
-    dominant = max(flops, key=lambda n: per_call[n])
-    ach = flops[dominant] / (per_call[dominant] * 1e-3) / 1e12
     gemm_tflops = {n: round(flops[n] / (per_call[n] * 1e-3) / 1e12, 1) for n in flops}
+    # HBM fraction of the calls without matrix work (algorithmic bytes).
+    hbm_frac = {n: round(nbytes[n] / (per_call[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)
+                for n in names if n not in flops}
+    dominant = max(names, key=lambda n: per_call[n])
+    t_mfma = flops.get(dominant, 0.0) / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes[dominant] / (PEAK_HBM_GBS * 1e9)
+    secs = per_call[dominant] * 1e-3
+    if t_mfma >= t_hbm:
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(flops[dominant] / secs / 1e12, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": round(nbytes[dominant] / secs / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = profiled_traffic(dominant, cfg.name)
+    roof["alg_bytes"] = nbytes[dominant]
+    if dominant in flops:
+        roof["mfma_frac"] = round(flops[dominant] / secs / 1e12 / PEAK_BF16_TFLOPS, 4)
     out = {
         "metric": METRIC,
         "value": round(cfg.T / (ms * 1e-3), 1),
@@ -177,8 +270,8 @@ def main() -> int:
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "gemm_tflops": gemm_tflops,
         "call_ms": {n: round(v, 4) for n, v in per_call.items()},
-        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "hbm_frac": hbm_frac,
+        "roofline": roof,
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
