@@ -20,37 +20,42 @@
 //   WGRAD_DOWN   dW_down[e] = dO_e^T A_e                          (fp32 out)
 //   WGRAD_GATEUP [dW_gate ; dW_up][e] = [dG | dU]_e^T X_e          (fp32 out)
 //
-// Tile: 256 x 256 x 64 per workgroup of 4 wavefronts (2 x 2), 128 x 128 per
+// Tile: 256 x 256 per workgroup of 4 wavefronts (2 x 2), 128 x 128 per
 // wavefront as 4 x 4 MFMA blocks of 32 x 32, accumulators in the register
-// file (256 fp32 per lane). Operands go straight from global memory into LDS
-// (buffer_load ... lds: each wavefront instruction fills one contiguous KiB,
-// lane l at byte 16 l), two stages of 64 KiB; no register staging and no LDS
-// store phase. An operand whose reduction index is contiguous in memory
-// ("k-major": the forward operands, the data-gradient activations) sits in
-// LDS as [row][k], 16-byte chunks XOR-swizzled by row, and is read with
-// ds_read_b128. An operand whose reduction index is the strided one
-// ("mn-major": the data-gradient weights, both weight-gradient operands) sits
-// as [k][column] as it is in memory, chunks swizzled by k, and is read with
-// ds_read_b64_tr_b16, which hands each lane four consecutive k of one column
-// (within each 16-lane group, lane i receives element i%4 of the pieces that
-// lanes 4j + i/4 address). Either way the swizzle is applied on the global
-// side: each lane fetches the chunk that belongs at its fixed LDS slot.
+// file (256 fp32 per lane); k-steps of 32. Operands go straight from global
+// memory into LDS (buffer_load ... lds: each wavefront instruction fills one
+// contiguous KiB, lane l at byte 16 l) through a ring of four 32 KiB stages;
+// no register staging and no LDS store phase. An operand whose reduction
+// index is contiguous in memory ("k-major": the forward operands, the
+// data-gradient activations) sits in LDS as [row][k], 16-byte chunks
+// XOR-swizzled by row, and is read with ds_read_b128. An operand whose
+// reduction index is the strided one ("mn-major": the data-gradient weights,
+// both weight-gradient operands) sits as [k][column] as it is in memory,
+// chunks swizzled by k, and is read with ds_read_b64_tr_b16, which hands each
+// lane four consecutive k of one column (within each 16-lane group, lane i
+// receives element i%4 of the pieces that lanes 4j + i/4 address). Either way
+// the swizzle is applied on the global side: each lane fetches the chunk
+// that belongs at its fixed LDS slot.
 //
-// Pipeline: with one wavefront per SIMD nothing hides a stall, so every
-// k-step threads the next step's 16 load instructions between its MFMA
-// groups (the address unit takes about 64 bytes per clock per CU; issued in
-// one burst they would hold the wavefront for ~1000 clocks) and ends with one
-// wait and one barrier. A tile's last k-step loads the next tile's first, and
-// the epilogue works from registers (SwiGLU in place: gate and up of one
-// element share a lane; a DPP quad transpose and a half-wave swap turn the
-// MFMA layout into four-row x 128-byte store runs), so those loads land
-// while the results go out.
+// Pipeline: with one wavefront per SIMD nothing hides a stall. Loads run
+// three steps ahead of the MFMAs, one load instruction after every group of
+// four MFMAs (the address unit takes about 64 bytes per clock per CU; issued
+// in a burst they would hold the wavefront), and each step has a single
+// barrier in its middle, after which the next step's first fragments are
+// read under the current step's second half. A tile's last steps load the
+// next tile's first three, and the epilogue works from registers (SwiGLU in
+// place: gate and up of one element share a lane; a DPP quad transpose and a
+// half-wave swap turn the MFMA layout into four-row x 128-byte store runs,
+// written non-temporally), so those loads land while the results go out.
+// Row blocks of a ragged last tile that hold no rows skip their MFMAs.
 //
 // Scheduling: one workgroup per CU, persistent. Tile i of the list belongs
 // to XCD-local workgroups: the list is cut into 8 contiguous ranges, one per
 // XCD (workgroup b runs on XCD b % 8), and the tiles of one expert and one
 // column block sit next to each other, so the weight slice they share is
 // fetched into one XCD's L2 once.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -61,7 +66,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int NT = 256;                 // threads per workgroup
 constexpr int WTM = 128, WTN = 128;     // wavefront tile
 constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -71,11 +76,8 @@ constexpr int STAGE_B = BN * BK;
 constexpr int STAGE = STAGE_A + STAGE_B;
 constexpr int GU_COLS = BN / 2;         // intermediate columns per GATEUP tile (gate + up)
 
-// Vector-memory instructions of a k-step issued before MFMA group g (of 16)
-// ends: kVmBefore[g + 1] - kVmBefore[g] of them follow group g. Front-loaded
-// (two per group over the first half) so the last load has half a step to
-// land; the two L2 prefetches follow group 8.
-constexpr int kVmBefore[17] = {0, 2, 4, 6, 8, 10, 12, 14, 16, 18, 18, 18, 18, 18, 18, 18, 18};
+constexpr int NSTAGE = 4;               // LDS ring of k-steps; loads run NSTAGE - 1 steps ahead
+constexpr int LOADS = 8;                // load instructions per wavefront and k-step (4 A + 4 B)
 
 enum Mode : int { GATEUP = 0, DOWN = 1, DGRAD_DOWN = 2, DGRAD_GATEUP = 3, WGRAD_DOWN = 4, WGRAD_GATEUP = 5 };
 
@@ -102,9 +104,11 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // LDS layouts of one operand stage (bf16 elements):
-//   k-major  [256 rows][64 k]   chunk c of row r at r*64 + (c ^ swk(r))*8
-//   mn-major [64 k][256 cols]   chunk c of row k at k*256 + (c ^ swt(k))*8
-__device__ __forceinline__ int swk(int r) { return (r ^ (r >> 3)) & 7; }
+//   k-major  [256 rows][32 k]   chunk c of row r at r*32 + (c ^ swk(r))*8
+//   mn-major [32 k][256 cols]   chunk c of row k at k*256 + (c ^ swt(k))*8
+// A k-major row is 64 bytes (four chunks); the XOR with bits 2-3 of the row
+// spreads the 16 rows that one ds_read_b128 pass touches over all banks.
+__device__ __forceinline__ int swk(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int swt(int k) { return (k & 3) << 2; }
 
 // Operand loads go through buffer resources: a wavefront-uniform base and a
@@ -123,12 +127,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
 __device__ __forceinline__ void buf_to_lds16(rsrc_t r, uint32_t voff, bf16_t* blk) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)blk, 16, voff, 0, 0, 0);
 }
-// L2 prefetch: one dword per lane (one per 128-byte line) dropped into a
-// scratch LDS slot that nothing reads; it has no register destination, so it
-// can stay in flight across k-steps.
-__device__ __forceinline__ void buf_prefetch(rsrc_t r, uint32_t voff, uint32_t* sink) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)sink, 4, voff, 0, 0, 0);
-}
 
 // Workgroup barrier between k-steps. The explicit s_waitcnt before it has
 // already made this wavefront's LDS traffic and needed loads complete; a
@@ -142,10 +140,11 @@ __device__ __forceinline__ void step_barrier() {
 }
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt in [3:0] and [15:14], expcnt in
-// [6:4], lgkmcnt in [11:8]. Both wait for LDS traffic and for all but the
+// [6:4], lgkmcnt in [11:8]. They wait for LDS traffic and for all but the
 // newest `n` vector-memory instructions (expcnt left unconstrained).
-constexpr int kWaitVm2 = 0x0072;  // vmcnt(2) lgkmcnt(0)
-constexpr int kWaitAll = 0x0000;  // vmcnt(0) expcnt(0) lgkmcnt(0)
+constexpr int kWaitVm12 = 0x007C;  // vmcnt(12) lgkmcnt(0)
+constexpr int kWaitVm16 = 0x4070;  // vmcnt(16) lgkmcnt(0)
+constexpr int kWaitAll = 0x0000;   // vmcnt(0) expcnt(0) lgkmcnt(0)
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -159,10 +158,21 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d)
 
 // Epilogue helpers ------------------------------------------------------------
 
+// Logistic sigmoid from the hardware base-2 exponential and reciprocal
+// (v_exp_f32, v_rcp_f32; about 1 ulp each): 1 / (1 + 2^(-g log2 e)). Large
+// |g| saturates cleanly to 0 or 1. The results are rounded to bf16 anyway, so
+// the few ulps against an IEEE exp and divide never show.
+__device__ __forceinline__ float sigmoid_fast(float g) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
+
 // Raw-buffer loads and stores of 8 or 16 bytes per lane. A lane whose bytes
 // fall outside the resource's range reads zeros and writes nothing; kNoWrite
 // is an offset outside every range used here (all are below 2^31 bytes).
 constexpr uint32_t kNoWrite = 0x80000000u;
+// Results are streamed out (non-temporal): the next kernel reads them from
+// memory anyway, and lines left dirty in the L2 slow that read down.
+constexpr int kStoreNT = 2;
 __device__ __forceinline__ u32x2 load_b64(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
 }
@@ -170,10 +180,10 @@ __device__ __forceinline__ u32x4 load_b128(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 __device__ __forceinline__ void store_b64(u32x2 v, rsrc_t r, uint32_t off) {
-  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kStoreNT);
 }
 __device__ __forceinline__ void store_b128(u32x4 v, rsrc_t r, uint32_t off) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStoreNT);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -260,13 +270,14 @@ __device__ __forceinline__ void swap_halves(float (&x)[4], float (&y)[4]) {
 template <int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(
     Params P) {
-  // Two stages as two objects: with the stage of every access known at
+  // The stages as separate objects: with the stage of every access known at
   // compile time, the compiler sees that loads landing in one stage do not
-  // alias reads of the other and does not wait for them before reading.
+  // alias reads of another and does not wait for them before reading.
   __shared__ __attribute__((aligned(16))) bf16_t lds0[STAGE];
   __shared__ __attribute__((aligned(16))) bf16_t lds1[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16_t lds2[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16_t lds3[STAGE];
   __shared__ int tstart[1025];  // grouped-M: first m-tile of each expert
-  __shared__ uint32_t pf_sink[4 * 64];  // L2-prefetch landing slots, never read
   __shared__ int part[NT];
 
   const int tid = threadIdx.x;
@@ -344,10 +355,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   if constexpr (MODE == WGRAD_GATEUP) { lda = 2 * I; ldb = H; }
 
   int e = 0, row0 = 0, mvalid = 0, m0 = 0, n0 = 0, kbeg = 0, kend = 0, ksteps = 0;
-  uint32_t aoff[8], boff[8], pfa = 0, pfb = 0;
+  uint32_t aoff[LOADS / 2], boff[LOADS / 2];
   const bf16_t* abase_m = P.a;  // grouped-M: the tile's first row of A
 
-  auto set_tile = [&](int L) {
+  auto set_tile = [&](int L) __attribute__((always_inline)) {
     int te, trow0 = 0, tmvalid = 0, tm0 = 0, tn0 = 0, tkbeg = 0, tkend = 0;
     if constexpr (!grouped_k(MODE)) {
       int l2 = 0, h2 = E - 1;
@@ -386,25 +397,27 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   };
   // Per-lane load offsets of the current tile (vector registers; recomputed
   // rather than kept alive across an epilogue).
-  auto set_offsets = [&]() {
+  auto set_offsets = [&]() __attribute__((always_inline)) {
     // An opaque copy of the lane index keeps the lane-only parts of these
     // offsets from being hoisted out of the tile loop (and spilled).
     int lane = lane_id;
     asm volatile("" : "+v"(lane));
-    // Per-lane byte offsets of this wavefront's 8 + 8 load instructions,
+    // Per-lane byte offsets of this wavefront's 4 + 4 load instructions,
     // relative to the operand's base at the current k-step; instruction t
-    // fills LDS block wave*8 + t (1 KiB) of each operand stage. Rows and
-    // columns past the operand's end are clamped to its last one (their
-    // products land in rows or columns that are never stored). k-major:
-    // LDS row r = 8 (wave*8 + t) + lane/8, chunk lane%8 (swizzled). mn-major:
-    // k-row 2 (wave*8 + t) + lane/32, chunk lane%32 (swizzled).
+    // fills LDS block wave*4 + t (1 KiB) of each operand stage. Rows and
+    // columns past the operand's end are clamped to its last one, or (A rows
+    // of a grouped-M tile) fall outside the buffer range and read as zeros;
+    // either way their products land in rows or columns that are never
+    // stored. k-major: LDS row r = 16 (wave*4 + t) + lane/4, chunk lane%4
+    // (swizzled). mn-major: k-row 2 (wave*4 + t) + lane/32, chunk lane%32
+    // (swizzled).
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int blk = wave * 8 + t;
+    for (int t = 0; t < LOADS / 2; ++t) {
+      const int blk = wave * (LOADS / 2) + t;
       if constexpr (A_KMAJOR) {
-        const int r = blk * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ swk(r);
-        aoff[t] = 2u * (min(r, mvalid - 1) * lda + c * 8);
+        const int r = blk * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swk(r);
+        aoff[t] = 2u * (r * lda + c * 8);  // rows >= mvalid: outside the range, read as zeros
       } else {
         const int k = blk * 2 + (lane >> 5);
         const int c = (lane & 31) ^ swt(k);
@@ -415,14 +428,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
         // LDS row r: wavefront column half r / 128 and 32-column block
         // j = (r % 128) / 32 of it (j < 2: gate, j >= 2: up, same indices).
         // A wavefront's 64 rows are all gate (even waves) or all up (odd).
-        const int r = blk * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ swk(r);
+        const int r = blk * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swk(r);
         const int j = (r & 127) >> 5;
         const int idx = min(n0 + (r >> 7) * 64 + (j & 1) * 32 + (r & 31), I - 1);
         boff[t] = 2u * (idx * H + c * 8);
       } else if constexpr (MODE == DOWN) {
-        const int r = blk * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ swk(r);
+        const int r = blk * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swk(r);
         boff[t] = 2u * (min(n0 + r, H - 1) * I + c * 8);
       } else {
         const int k = blk * 2 + (lane >> 5);
@@ -432,39 +445,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       }
     }
     abase_m = P.a + static_cast<int64_t>(row0) * lda;
-
-    // L2 prefetch offsets, one 128-byte line per lane per operand and k-step:
-    // k-major operands, row wave*64 + lane (its 64 k of the step); mn-major
-    // operands, k-row wave*16 + lane/4, line lane%4 of the 256 columns.
-    const int r = wave * 64 + lane;
-    const int kr = wave * 16 + (lane >> 2);
-    if constexpr (A_KMAJOR) {
-      pfa = 2u * (min(r, mvalid - 1) * lda);
-    } else {
-      const int mrows = MODE == WGRAD_DOWN ? H : 2 * I;
-      pfa = 2u * (kr * lda + min(m0 + (lane & 3) * 64, mrows - 64));
-    }
-    if constexpr (MODE == GATEUP) {
-      const int j = (r & 127) >> 5;
-      pfb = 2u * (min(n0 + (r >> 7) * 64 + (j & 1) * 32 + (r & 31), I - 1) * H);
-    } else if constexpr (MODE == DOWN) {
-      pfb = 2u * (min(n0 + r, H - 1) * I);
-    } else {
-      const int ncols = (MODE == DGRAD_DOWN || MODE == WGRAD_DOWN) ? I : H;
-      pfb = 2u * (kr * ldb + min(n0 + (lane & 3) * 64, ncols - 64));
-    }
   };
   // No next tile: every load of the chained step reads an empty range.
   auto clear_tile = [&]() {
     ksteps = 0;
     kend = kbeg;
   };
-  auto set_tile_and_offsets = [&](int L) {
+  auto set_tile_and_offsets = [&](int L) __attribute__((always_inline)) {
     set_tile(L);
     set_offsets();
   };
 
-  uint32_t* sink = pf_sink + wave * 64;
 
   // Buffer resources of k-step s (num_records 0 past the last step).
   auto rsrc_a = [&](int s) -> rsrc_t {
@@ -498,39 +489,32 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
     }
   };
 
-  // Vector-memory instruction v of a k-step's 18, for step sn into the
-  // stage at L: v < 16 alternate A and B blocks (v/2 of each), 16 and 17
-  // are the L2 prefetches of step sn + 1.
-  auto vmem = [&](int v, const rsrc_t& ra, const rsrc_t& rb, bf16_t* L, int sn) {
-    if (v < 16) {
-      const int t = v >> 1;
-      if ((v & 1) == 0) buf_to_lds16(ra, aoff[t], L + (wave * 8 + t) * 512);
-      else buf_to_lds16(rb, boff[t], L + STAGE_A + (wave * 8 + t) * 512);
-    } else if (v == 16) {
-      buf_prefetch(rsrc_a(sn + 1), pfa, sink);
-    } else {
-      buf_prefetch(rsrc_b(sn + 1), pfb, sink);
-    }
+  // Load instruction v of a k-step's 8, for step sn into the stage at L:
+  // even v an A block, odd v a B block (block v/2 of this wavefront's 4).
+  auto vmem = [&](int v, const rsrc_t& ra, const rsrc_t& rb, bf16_t* L) __attribute__((always_inline)) {
+    const int t = v >> 1;
+    if ((v & 1) == 0) buf_to_lds16(ra, aoff[t], L + (wave * (LOADS / 2) + t) * 512);
+    else buf_to_lds16(rb, boff[t], L + STAGE_A + (wave * (LOADS / 2) + t) * 512);
   };
-  // All 18 at once (the first step of a workgroup's first tile).
-  auto issue = [&](int s, bf16_t* L) {
+  // All 8 at once (the first steps of a workgroup's first tile).
+  auto issue = [&](int s, bf16_t* L) __attribute__((always_inline)) {
     const rsrc_t ra = rsrc_a(s);
     const rsrc_t rb = rsrc_b(s);
 #pragma unroll
-    for (int v = 0; v < 18; ++v) vmem(v, ra, rb, L, s);
+    for (int v = 0; v < LOADS; ++v) vmem(v, ra, rb, L);
   };
 
-  // Operand fragments of k-slice kk (16 k) for 32-row block i, as byte
-  // offsets inside a stage. k-major (ds_read_b128, lane: row i*32 + lane%32,
-  // chunk 2 kk + lane/32): the chunk XOR makes slice kk the slice-0 offset
-  // XOR 32 kk. mn-major (two ds_read_b64_tr_b16, lane: k-row
+  // Operand fragments of k-slice kk (16 k; two per step) for 32-row block
+  // i, as byte offsets inside a stage. k-major (ds_read_b128, lane: row
+  // i*32 + lane%32, chunk 2 kk + lane/32): the chunk XOR makes slice kk the
+  // slice-0 offset XOR 32 kk. mn-major (two ds_read_b64_tr_b16, lane: k-row
   // 8 (lane/32) + (lane%16)/4, columns 4 (lane%4) .. + 3 of the block's
   // 16-column half (lane/16)%2): slice kk adds 16 rows = 8 KiB, the second
   // read 4 rows = 2 KiB.
   int aof[FM], bof[FN];
   // Computed at the start of every tile from an opaque copy of the lane
   // index: alive through the k-loop only, not through the epilogue.
-  auto set_frag_offsets = [&]() {
+  auto set_frag_offsets = [&]() __attribute__((always_inline)) {
   int lane = lane_id;
   asm volatile("" : "+v"(lane));
   const int hi32 = lane >> 5;
@@ -569,54 +553,67 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   };
 
   f32x16 acc[FM][FN];
+  bf16x8 fa0[FM], fb0[FN];  // slice 0 of the step about to run, read during the step before
 
-  // One k-step: the 64 MFMAs on the stage at Ac, in 16 groups of four
-  // (k-slice kk, row block i), with the loads of step sn into the stage at
-  // Ln threaded between the groups (kVmBefore) so that the wavefront never
-  // stalls on a full address queue with matrix work waiting behind it.
-  // Fragments of slice kk + 1 are read while slice kk multiplies;
-  // scheduling fences keep every group where it is written. The step ends
-  // waiting for all but this wavefront's two newest vector-memory
-  // instructions (the L2 prefetches, which may stay in flight), then for
-  // the other wavefronts. A tile's last step (sync = false) skips both: the
-  // loads it issues are the next tile's first, and the wait for them comes
-  // after the epilogue.
-  auto kstep = [&](const bf16_t* Ac, int sn, bf16_t* Ln, bool sync) {
-    const bf16_t* Bc = Ac + STAGE_A;
-    const rsrc_t ra = rsrc_a(sn);
-    const rsrc_t rb = rsrc_b(sn);
-    bf16x8 av[2][FM], bv[2][FN];
+  // Fragments of k-slice kk of the stage at S (A blocks with valid rows only).
+  auto read_slice = [&](auto nbc, const bf16_t* S, int kk, bf16x8 (&fa)[FM], bf16x8 (&fb)[FN])
+                        __attribute__((always_inline)) {
+    constexpr int nbm = decltype(nbc)::value;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) av[0][i] = frag(Ac, aof[i], 0, A_KMAJOR);
+    for (int i = 0; i < FM; ++i)
+      if (i < nbm) fa[i] = frag(S, aof[i], kk, A_KMAJOR);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bv[0][j] = frag(Bc, bof[j], 0, B_KMAJOR);
+    for (int j = 0; j < FN; ++j)
+      if (nbm > 0) fb[j] = frag(S + STAGE_A, bof[j], kk, B_KMAJOR);
+  };
+  // The 16 MFMAs of one slice in four groups (row block i); load v0 + i of
+  // step sn follows group i, so that the wavefront never stalls on a full
+  // address queue with matrix work waiting behind it.
+  auto mfma_slice = [&](auto nbc, const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN], int v0, const rsrc_t& ra,
+                        const rsrc_t& rb, bf16_t* Ln) __attribute__((always_inline)) {
+    constexpr int nbm = decltype(nbc)::value;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int cur = kk & 1;
-      __builtin_amdgcn_sched_barrier(0);
-      if (kk + 1 < BK / 16) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) av[cur ^ 1][i] = frag(Ac, aof[i], kk + 1, A_KMAJOR);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) bv[cur ^ 1][j] = frag(Bc, bof[j], kk + 1, B_KMAJOR);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FM; ++i) {
+      if (i < nbm) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        const int g = kk * FM + i;
-#pragma unroll
-        for (int v = kVmBefore[g]; v < kVmBefore[g + 1]; ++v) vmem(v, ra, rb, Ln, sn);
-        __builtin_amdgcn_sched_barrier(0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      vmem(v0 + i, ra, rb, Ln);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (sync) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm2);  // this wavefront's loads of step sn have landed ...
-      step_barrier();                        // ... everyone's have, and the stage at Ac is free again
+  };
+
+  // One k-step (32 k) on the stage at Ac, with loads of step sn (three
+  // ahead) going into the stage at Ln:
+  //   slice 0: MFMAs (fragments already in registers), slice 1's fragment
+  //            reads, loads 0-3;
+  //   middle:  this wavefront's loads of the next step have landed (all but
+  //            the 12 newest: the step after that and this step's first
+  //            half) and its fragment reads are done; then the barrier
+  //            makes both true for every wavefront, which also frees the
+  //            stage read two steps ago for the loads issued from here on;
+  //   slice 1: MFMAs, the next step's slice-0 fragments from An, loads 4-7.
+  // Scheduling fences keep every group where it is written. A tile's last
+  // step (last = true) has no middle and reads nothing ahead: the wait for
+  // the next tile's first steps comes after the epilogue.
+  auto kstep = [&](auto nbc, const bf16_t* Ac, const bf16_t* An, int sn, bf16_t* Ln, bool last)
+                   __attribute__((always_inline)) {
+    const rsrc_t ra = rsrc_a(sn);
+    const rsrc_t rb = rsrc_b(sn);
+    bf16x8 fa1[FM], fb1[FN];
+    __builtin_amdgcn_sched_barrier(0);
+    read_slice(nbc, Ac, 1, fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_slice(nbc, fa0, fb0, 0, ra, rb, Ln);
+    if (!last) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm12);
+      step_barrier();
+      read_slice(nbc, An, 0, fa0, fb0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_slice(nbc, fa1, fb1, LOADS / 2, ra, rb, Ln);
   };
 
   // ---- epilogue -------------------------------------------------------------
@@ -628,7 +625,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   // tile's last valid row; columns past the output's end get an offset
   // outside every range. No LDS and no barriers: the next tile's first
   // loads, already in flight, land meanwhile.
-  auto epilogue = [&](int te, int trow0, int tmvalid, int tm0, int tn0) {
+  auto epilogue = [&](int te, int trow0, int tmvalid, int tm0, int tn0, int nbm) __attribute__((always_inline)) {
     // Lane-only terms from an opaque copy of the lane index, so that they
     // are not hoisted out of the tile loop (and spilled).
     int lane = lane_id;
@@ -653,6 +650,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
+          if (i >= nbm) continue;  // no valid rows in this block
           const int r = wm * WTM + i * 32 + 8 * b + prow;
           const uint32_t off = idx < I ? 2u * static_cast<uint32_t>(r * I + idx) : kNoWrite;
           const uint32_t off4 = idx < I ? off + 8u * I : kNoWrite;
@@ -664,7 +662,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
             for (int q = 0; q < 4; ++q) {
               g[q] = acc[i][j][4 * b + q];
               u[q] = acc[i][j + 2][4 * b + q];
-              a[q] = g[q] * sigmoidf_dev(g[q]) * u[q];
+              a[q] = g[q] * sigmoid_fast(g[q]) * u[q];
             }
             gp[j] = quad_transpose_bf16(g, lane);
             up[j] = quad_transpose_bf16(u, lane);
@@ -688,6 +686,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
         for (int jp = 0; jp < FN / 2; ++jp)
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
+            if (i >= nbm) continue;  // no valid rows in this block
             const int r = wm * WTM + i * 32 + 8 * b + prow;
             const int n = tn0 + wn * WTN + jp * 64 + pcol;
             const uint32_t off = n < H ? 2u * static_cast<uint32_t>(r * H + n) : kNoWrite;
@@ -713,6 +712,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       const rsrc_t ro = make_rsrc(P.out0 + 2 * base, 4 * tmvalid * I);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
+        if (i >= nbm) continue;  // no valid rows in this block
         // All of a row block's saved G and U first, so that their latency
         // overlaps.
         u32x2 gb[FN / 2][4][2], ub[FN / 2][4][2];
@@ -751,7 +751,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
               float dg[4], du[4];
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                const float sg = sigmoidf_dev(gv[q]);
+                const float sg = sigmoid_fast(gv[q]);
                 dg[q] = da[h][q] * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
                 du[q] = da[h][q] * (gv[q] * sg);
               }
@@ -821,38 +821,63 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   };
 
   // ---- tile loop ---------------------------------------------------------------
+  // Steps of a tile come in groups of NSTAGE (a padded step reads zeros), so
+  // step u of a group always uses stage u and every stage is a distinct
+  // object at compile time. In step s the loads of step s + 3 go out; in a
+  // tile's last group they turn into the next tile's steps 0-2.
   int L = lo + slot;
   if (L < hi) {
     set_tile_and_offsets(L);
     issue(0, lds0);
-    __builtin_amdgcn_s_waitcnt(kWaitVm2);
+    issue(1, lds1);
+    issue(2, lds2);
+    __builtin_amdgcn_s_waitcnt(kWaitVm16);  // step 0 has landed (steps 1 and 2 may not have)
     step_barrier();
   }
   for (; L < hi; L += nslots) {
     set_frag_offsets();
+    read_slice(std::integral_constant<int, FM>{}, lds0, 0, fa0, fb0);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-    // Steps go in pairs (stage 0, stage 1), at least one pair; a padding
-    // step (odd count, or an empty reduction) reads as zeros.
-    const int ksteps2 = max(2, (ksteps + 1) & ~1);
-    for (int s = 0; s + 2 < ksteps2; s += 2) {
-      kstep(lds0, s + 1, lds1, true);
-      kstep(lds1, s + 2, lds0, true);
-    }
-    kstep(lds0, ksteps2 - 1, lds1, true);
+    // This wavefront's 32-row blocks that hold valid rows of the tile (a
+    // ragged last tile of an expert skips the MFMAs, fragment reads and
+    // stores of the others). The k-loop is compiled once per count, so no
+    // branch sits between the MFMAs.
+    const int mrows_valid = grouped_k(MODE) ? (MODE == WGRAD_DOWN ? H : 2 * I) - m0 : mvalid;
+    const int nbm = __builtin_amdgcn_readfirstlane(max(0, min(FM, (mrows_valid - wm * WTM + 31) / 32)));
+    const int nsteps = max(NSTAGE, (ksteps + NSTAGE - 1) / NSTAGE * NSTAGE);
     const int fe = e, frow0 = row0, fmvalid = mvalid, fm0 = m0, fn0 = n0;
-    if (L + nslots < hi) set_tile_and_offsets(L + nslots);
-    else clear_tile();
-    kstep(lds1, 0, lds0, false);  // the last step; its loads are the next tile's first
-    epilogue(fe, frow0, fmvalid, fm0, fn0);
-    // The next tile's first step has landed (everything this wavefront
+    const int Lnext = L + nslots;
+    auto kloop = [&](auto nbc) __attribute__((always_inline)) {
+      for (int s = 0; s + NSTAGE < nsteps; s += NSTAGE) {
+        kstep(nbc, lds0, lds1, s + 3, lds3, false);
+        kstep(nbc, lds1, lds2, s + 4, lds0, false);
+        kstep(nbc, lds2, lds3, s + 5, lds1, false);
+        kstep(nbc, lds3, lds0, s + 6, lds2, false);
+      }
+      kstep(nbc, lds0, lds1, nsteps - 1, lds3, false);
+      if (Lnext < hi) set_tile_and_offsets(Lnext);
+      else clear_tile();
+      kstep(nbc, lds1, lds2, 0, lds0, false);
+      kstep(nbc, lds2, lds3, 1, lds1, false);
+      kstep(nbc, lds3, lds0, 2, lds2, true);
+    };
+    switch (nbm) {
+      case 4: kloop(std::integral_constant<int, 4>{}); break;
+      case 3: kloop(std::integral_constant<int, 3>{}); break;
+      case 2: kloop(std::integral_constant<int, 2>{}); break;
+      case 1: kloop(std::integral_constant<int, 1>{}); break;
+      default: kloop(std::integral_constant<int, 0>{}); break;
+    }
+    epilogue(fe, frow0, fmvalid, fm0, fn0, nbm);
+    // The next tile's first steps have landed (everything this wavefront
     // issued has: loads and the epilogue's stores, which the counter does
     // not order against each other) in every wavefront, and all are done
-    // with the last stage.
+    // with the last stages.
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     step_barrier();
     // The offsets again rather than kept alive through the epilogue (the
