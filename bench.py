@@ -195,9 +195,9 @@ def main() -> int:
         lambda: B.moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["do_perm"],
                                   b["d_topk_w"]),
         lambda: B.moe_gemm_down_dgrad(s, b["do_perm"], b["offsets"], wd, b["g"], b["u"], dgu),
-        lambda: B.moe_gemm_down_wgrad(s, b["do_perm"], b["a"], b["offsets"], b["dw_down"], 0),
+        lambda: B.moe_gemm_down_wgrad(s, b["do_perm"], b["a"], b["offsets"], b["dw_down"], 0, st.ws),
         lambda: B.moe_gemm_gate_up_dgrad(s, dgu, b["offsets"], wg, wu, b["dx_perm"]),
-        lambda: B.moe_gemm_gate_up_wgrad(s, dgu, b["x_perm"], b["offsets"], b["dw_gate"], b["dw_up"], 0),
+        lambda: B.moe_gemm_gate_up_wgrad(s, dgu, b["x_perm"], b["offsets"], b["dw_gate"], b["dw_up"], 0, st.ws),
         lambda: B.moe_unpermute_sum(s, b["dx_perm"], b["flat_to_sorted"], b["dx"]),
         lambda: B.moe_route_bwd(s, b["d_topk_w"], b["topk_w"], b["topk_idx"], b["d_logits"]),
     ]

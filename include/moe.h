@@ -63,10 +63,14 @@ typedef struct {
   int32_t dtype;
 } moe_shape;
 
-/* Bytes of device workspace for this shape. One buffer of this size serves
- * every call that takes a workspace: moe_permute's per-block expert
- * histograms, and moe_grouped_gemm_bwd's dG and dU for every row
- * ([T*k, 2I] in dtype). */
+/* Bytes of device workspace for this shape on the current device. One
+ * buffer of this size serves every call that takes a workspace:
+ * moe_permute's per-block expert histograms, moe_grouped_gemm_bwd's dG and
+ * dU for every row ([T*k, 2I] in dtype), and (bf16) the weight gradients'
+ * split-K partial tiles: an expert whose row count is far above a CU's share
+ * of the launch is reduced in chunks whose fp32 partial 256 x 256 tiles are
+ * added in chunk order afterwards (deterministic; at most two tiles per
+ * compute unit, 128 MiB on a 256-CU device, fewer for small shapes). */
 size_t moe_workspace_bytes(moe_shape s);
 
 /* Router (torchtune PR #2820 "[WIP] Qwen3 MoE support", comment on dividing
@@ -124,7 +128,10 @@ moe_status moe_grouped_gemm_fwd(moe_shape s, const void* x_perm, const int32_t* 
  *   moe_gemm_down_dgrad    dgu      <- do_perm, W_down, g, u
  *   moe_gemm_down_wgrad    dw_down  <- do_perm, a              (f32; += if accumulate_dw)
  *   moe_gemm_gate_up_dgrad dx_perm  <- dgu, W_gate, W_up
- *   moe_gemm_gate_up_wgrad dw_gate, dw_up <- dgu, x_perm       (f32; += if accumulate_dw) */
+ *   moe_gemm_gate_up_wgrad dw_gate, dw_up <- dgu, x_perm       (f32; += if accumulate_dw)
+ * The two weight-gradient calls take the workspace (ws_bytes >=
+ * moe_workspace_bytes(s), else MOE_EWORKSPACE) for their split-K partial
+ * tiles; calls that share one workspace must not overlap in time. */
 moe_status moe_gemm_gate_up(moe_shape s, const void* x_perm, const int32_t* offsets, const void* w_gate,
                             const void* w_up, void* g, void* u, void* a, hipStream_t stream);
 moe_status moe_gemm_down(moe_shape s, const void* a, const int32_t* offsets, const void* w_down, void* o_perm,
@@ -132,11 +139,12 @@ moe_status moe_gemm_down(moe_shape s, const void* a, const int32_t* offsets, con
 moe_status moe_gemm_down_dgrad(moe_shape s, const void* do_perm, const int32_t* offsets, const void* w_down,
                                const void* g, const void* u, void* dgu, hipStream_t stream);
 moe_status moe_gemm_down_wgrad(moe_shape s, const void* do_perm, const void* a, const int32_t* offsets,
-                               float* dw_down, int accumulate_dw, hipStream_t stream);
+                               float* dw_down, int accumulate_dw, void* ws, size_t ws_bytes, hipStream_t stream);
 moe_status moe_gemm_gate_up_dgrad(moe_shape s, const void* dgu, const int32_t* offsets, const void* w_gate,
                                   const void* w_up, void* dx_perm, hipStream_t stream);
 moe_status moe_gemm_gate_up_wgrad(moe_shape s, const void* dgu, const void* x_perm, const int32_t* offsets,
-                                  float* dw_gate, float* dw_up, int accumulate_dw, hipStream_t stream);
+                                  float* dw_gate, float* dw_up, int accumulate_dw, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
 
 /* Weighted combine (modelopt.torch.utils.moe, a2a_moe: each token's k expert
  * results are weighted by its routing weights in their own precision and

@@ -56,9 +56,10 @@ _SIGS = {
     "moe_gemm_gate_up": ([moe_shape, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_gemm_down": ([moe_shape, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_gemm_down_dgrad": ([moe_shape, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
-    "moe_gemm_down_wgrad": ([moe_shape, _P, _P, _P, _P, ctypes.c_int, _P], ctypes.c_int),
+    "moe_gemm_down_wgrad": ([moe_shape, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "moe_gemm_gate_up_dgrad": ([moe_shape, _P, _P, _P, _P, _P, _P], ctypes.c_int),
-    "moe_gemm_gate_up_wgrad": ([moe_shape, _P, _P, _P, _P, _P, ctypes.c_int, _P], ctypes.c_int),
+    "moe_gemm_gate_up_wgrad": ([moe_shape, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_size_t, _P],
+                               ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -164,9 +165,10 @@ def moe_gemm_down_dgrad(s, do_perm, offsets, w_down, g, u, dgu, stream=None):
                                                           _ptr(u), _ptr(dgu), _stream(stream)))
 
 
-def moe_gemm_down_wgrad(s, do_perm, a, offsets, dw_down, accumulate_dw=0, stream=None):
+def moe_gemm_down_wgrad(s, do_perm, a, offsets, dw_down, accumulate_dw, ws, ws_bytes=None, stream=None):
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     _check("moe_gemm_down_wgrad", lib.moe_gemm_down_wgrad(s, _ptr(do_perm), _ptr(a), _ptr(offsets), _ptr(dw_down),
-                                                          int(accumulate_dw), _stream(stream)))
+                                                          int(accumulate_dw), _ptr(ws), nb, _stream(stream)))
 
 
 def moe_gemm_gate_up_dgrad(s, dgu, offsets, w_gate, w_up, dx_perm, stream=None):
@@ -174,10 +176,11 @@ def moe_gemm_gate_up_dgrad(s, dgu, offsets, w_gate, w_up, dx_perm, stream=None):
                                                                 _ptr(w_up), _ptr(dx_perm), _stream(stream)))
 
 
-def moe_gemm_gate_up_wgrad(s, dgu, x_perm, offsets, dw_gate, dw_up, accumulate_dw=0, stream=None):
+def moe_gemm_gate_up_wgrad(s, dgu, x_perm, offsets, dw_gate, dw_up, accumulate_dw, ws, ws_bytes=None, stream=None):
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     _check("moe_gemm_gate_up_wgrad", lib.moe_gemm_gate_up_wgrad(s, _ptr(dgu), _ptr(x_perm), _ptr(offsets),
                                                                 _ptr(dw_gate), _ptr(dw_up), int(accumulate_dw),
-                                                                _stream(stream)))
+                                                                _ptr(ws), nb, _stream(stream)))
 
 
 class MoEStage:

@@ -17,6 +17,9 @@ moe_status check_shape(const moe_shape& s) {
   if (s.H % 64 != 0 || s.I % 64 != 0) return MOE_EUNSUPPORTED;
   // Element offsets inside one expert's weights and one row block stay int32.
   if (static_cast<int64_t>(s.E) * s.I * s.H >= (static_cast<int64_t>(1) << 31)) return MOE_EUNSUPPORTED;
+  // The weight-gradient tile plan counts work (tiles x 32-row k-steps) in int32.
+  const int64_t tiles = static_cast<int64_t>((2 * s.I + 255) / 256) * ((s.H + 255) / 256);
+  if (tiles * (static_cast<int64_t>(s.T) * s.k / 32 + s.E) >= (static_cast<int64_t>(1) << 30)) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -111,12 +114,15 @@ moe_status moe_gemm_down_dgrad(moe_shape s, const void* do_perm, const int32_t* 
 }
 
 moe_status moe_gemm_down_wgrad(moe_shape s, const void* do_perm, const void* a, const int32_t* offsets,
-                               float* dw_down, int accumulate_dw, hipStream_t stream) {
+                               float* dw_down, int accumulate_dw, void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
-  if (any_null(do_perm, a, offsets, dw_down)) return MOE_EINVAL;
+  if (any_null(do_perm, a, offsets, dw_down, ws)) return MOE_EINVAL;
   if (accumulate_dw != 0 && accumulate_dw != 1) return MOE_EINVAL;
+  const WsLayout l = moe::ws_layout(s);
+  if (ws_bytes < l.total) return MOE_EWORKSPACE;
   moe::GemmArgs ga{};
+  ga.part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.part_off);
   ga.offsets = offsets;
   ga.a = do_perm;
   ga.b0 = a;
@@ -140,12 +146,16 @@ moe_status moe_gemm_gate_up_dgrad(moe_shape s, const void* dgu, const int32_t* o
 }
 
 moe_status moe_gemm_gate_up_wgrad(moe_shape s, const void* dgu, const void* x_perm, const int32_t* offsets,
-                                  float* dw_gate, float* dw_up, int accumulate_dw, hipStream_t stream) {
+                                  float* dw_gate, float* dw_up, int accumulate_dw, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
-  if (any_null(dgu, x_perm, offsets, dw_gate, dw_up)) return MOE_EINVAL;
+  if (any_null(dgu, x_perm, offsets, dw_gate, dw_up, ws)) return MOE_EINVAL;
   if (accumulate_dw != 0 && accumulate_dw != 1) return MOE_EINVAL;
+  const WsLayout l = moe::ws_layout(s);
+  if (ws_bytes < l.total) return MOE_EWORKSPACE;
   moe::GemmArgs ga{};
+  ga.part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.part_off);
   ga.offsets = offsets;
   ga.a = dgu;
   ga.b0 = x_perm;
@@ -197,9 +207,10 @@ moe_status moe_grouped_gemm_bwd(moe_shape s, const void* do_perm, const void* x_
   if (ws_bytes < l.total) return MOE_EWORKSPACE;
   void* dgu = static_cast<char*>(ws) + l.dgu_off;
   if ((st = moe_gemm_down_dgrad(s, do_perm, offsets, w_down, g, u, dgu, stream)) != MOE_OK) return st;
-  if ((st = moe_gemm_down_wgrad(s, do_perm, a, offsets, dw_down, accumulate_dw, stream)) != MOE_OK) return st;
+  if ((st = moe_gemm_down_wgrad(s, do_perm, a, offsets, dw_down, accumulate_dw, ws, ws_bytes, stream)) != MOE_OK)
+    return st;
   if ((st = moe_gemm_gate_up_dgrad(s, dgu, offsets, w_gate, w_up, dx_perm, stream)) != MOE_OK) return st;
-  return moe_gemm_gate_up_wgrad(s, dgu, x_perm, offsets, dw_gate, dw_up, accumulate_dw, stream);
+  return moe_gemm_gate_up_wgrad(s, dgu, x_perm, offsets, dw_gate, dw_up, accumulate_dw, ws, ws_bytes, stream);
 }
 
 moe_status moe_unpermute_sum(moe_shape s, const void* dx_perm, const int32_t* flat_to_sorted, void* dx,

@@ -54,6 +54,7 @@
 // XCD (workgroup b runs on XCD b % 8), and the tiles of one expert and one
 // column block sit next to each other, so the weight slice they share is
 // fetched into one XCD's L2 once.
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -98,6 +99,7 @@ struct Params {
   float* dw0;          // dw_down | dw_gate
   float* dw1;          // dw_up
   int accumulate;
+  float* part;         // weight gradients: split-K partial tiles [tile][256][256]
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -267,6 +269,46 @@ __device__ __forceinline__ void swap_halves(float (&x)[4], float (&y)[4]) {
   }
 }
 
+// Exclusive prefix over experts of v (expert tid*4 + j in v[j]) into
+// out[0..E], out[E] the total; a block of NT threads, `part` NT ints of LDS.
+__device__ __forceinline__ void expert_scan(const int (&v)[4], int* out, int* part, int E, int tid) {
+  const int sum = v[0] + v[1] + v[2] + v[3];
+  part[tid] = sum;
+  __syncthreads();
+  for (int o = 1; o < NT; o <<= 1) {
+    const int x = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += x;
+    __syncthreads();
+  }
+  int run = part[tid] - sum;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid * 4 + j;
+    if (e < E) out[e] = run;
+    run += v[j];
+  }
+  if (tid == NT - 1) out[E] = part[NT - 1];
+  __syncthreads();
+}
+
+// Split-K plan of the weight gradients. Their reduction runs over an
+// expert's rows, a ragged count; an expert far longer than a workgroup's
+// share of the launch would keep one CU busy long after the others, so it is
+// cut into chunks of about equal length, each a tile of its own:
+//   cap       = max(kMinChunkSteps, ceil(W / (2 * grid)))   W = tiles per expert * sum of k-steps
+//   chunks(e) = ceil(steps(e) / cap)                         (1 while steps(e) <= cap)
+// Chunk 0 writes the gradient; later chunks write fp32 partial tiles to the
+// workspace, which a second kernel adds in chunk order (no atomics: the
+// result does not depend on timing). Fewer than W / cap <= 2 * grid partial
+// tiles exist at any shape.
+constexpr int kMinChunkSteps = 64;
+__device__ __forceinline__ int split_cap(int work, int grid) {
+  return max(kMinChunkSteps, (work + 2 * grid - 1) / (2 * grid));
+}
+__device__ __forceinline__ int split_chunks(int steps, int cap) { return steps > cap ? (steps + cap - 1) / cap : 1; }
+__device__ __forceinline__ int split_len(int steps, int chunks) { return (steps + chunks - 1) / chunks; }
+
 template <int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(
     Params P) {
@@ -277,7 +319,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   __shared__ __attribute__((aligned(16))) bf16_t lds1[STAGE];
   __shared__ __attribute__((aligned(16))) bf16_t lds2[STAGE];
   __shared__ __attribute__((aligned(16))) bf16_t lds3[STAGE];
-  __shared__ int tstart[1025];  // grouped-M: first m-tile of each expert
+  __shared__ int tstart[1025];  // grouped-M: first m-tile of each expert; grouped-K: first tile
+  __shared__ int pstart[1025];  // grouped-K: first partial tile of each expert
+  __shared__ int wstart[1025];  // grouped-K: work (k-steps) before each expert's tiles
   __shared__ int part[NT];
 
   const int tid = threadIdx.x;
@@ -289,7 +333,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
 
   // ---- tile list -----------------------------------------------------------
   int ntn, total;
-  int tpe = 0;
+  int tpe = 0, kcap = 0;
   if constexpr (!grouped_k(MODE)) {
     // tstart[e] = sum over e' < e of ceil(count[e'] / BM): 4 experts per thread.
     int loc[4];
@@ -325,18 +369,58 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
     ntn = (ncols + (MODE == GATEUP ? GU_COLS : BN) - 1) / (MODE == GATEUP ? GU_COLS : BN);
     total = tstart[E] * ntn;
   } else {
+    // Tiles of expert e: chunks(e) x tpe, chunk-major; the split plan above.
     const int mrows = MODE == WGRAD_DOWN ? H : 2 * I;
     const int ncols = MODE == WGRAD_DOWN ? I : H;
     ntn = (ncols + BN - 1) / BN;
     tpe = ((mrows + BM - 1) / BM) * ntn;
-    total = E * tpe;
+    int st[4], c[4], v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = tid * 4 + j;
+      st[j] = e < E ? (P.offsets[e + 1] - P.offsets[e] + BK - 1) / BK : 0;
+    }
+    expert_scan(st, wstart, part, E, tid);
+    kcap = split_cap(tpe * wstart[E], gridDim.x);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = tid * 4 + j < E ? split_chunks(st[j], kcap) : 0;
+      v[j] = c[j] * tpe;
+    }
+    expert_scan(v, tstart, part, E, tid);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = c[j] > 0 ? (c[j] - 1) * tpe : 0;
+    expert_scan(v, pstart, part, E, tid);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = c[j] * tpe * (c[j] > 0 ? max(1, split_len(st[j], c[j])) : 0);
+    expert_scan(v, wstart, part, E, tid);
+    total = tstart[E];
   }
 
+  // Tile range of this workgroup's XCD: an eighth of the tiles (grouped-M:
+  // all tiles cost the same) or of the work (grouped-K: tiles of one expert
+  // cost the same, those of different experts do not).
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int nslots = gridDim.x >> 3;
-  const int lo = static_cast<int>((static_cast<int64_t>(total) * xcd) / 8);
-  const int hi = static_cast<int>((static_cast<int64_t>(total) * (xcd + 1)) / 8);
+  auto tile_at = [&](int x8) -> int {
+    if constexpr (!grouped_k(MODE)) {
+      return static_cast<int>((static_cast<int64_t>(total) * x8) / 8);
+    } else {
+      const int w = static_cast<int>((static_cast<int64_t>(wstart[E]) * x8) / 8);
+      if (x8 >= 8) return total;
+      int l2 = 0, h2 = E - 1;
+      while (l2 < h2) {
+        const int mid = (l2 + h2 + 1) >> 1;
+        if (wstart[mid] <= w) l2 = mid; else h2 = mid - 1;
+      }
+      const int tiles = tstart[l2 + 1] - tstart[l2];
+      const int wt = (wstart[l2 + 1] - wstart[l2]) / tiles;
+      return tstart[l2] + min(tiles, (w - wstart[l2] + wt - 1) / wt);
+    }
+  };
+  const int lo = tile_at(xcd);
+  const int hi = tile_at(xcd + 1);
 
   constexpr bool A_KMAJOR = !grouped_k(MODE);
   constexpr bool B_KMAJOR = b_kcontig(MODE);
@@ -355,11 +439,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   if constexpr (MODE == WGRAD_GATEUP) { lda = 2 * I; ldb = H; }
 
   int e = 0, row0 = 0, mvalid = 0, m0 = 0, n0 = 0, kbeg = 0, kend = 0, ksteps = 0;
+  int pidx = -1;  // grouped-K: partial tile of a later chunk, -1 for chunk 0
   uint32_t aoff[LOADS / 2], boff[LOADS / 2];
   const bf16_t* abase_m = P.a;  // grouped-M: the tile's first row of A
 
   auto set_tile = [&](int L) __attribute__((always_inline)) {
-    int te, trow0 = 0, tmvalid = 0, tm0 = 0, tn0 = 0, tkbeg = 0, tkend = 0;
+    int te, trow0 = 0, tmvalid = 0, tm0 = 0, tn0 = 0, tkbeg = 0, tkend = 0, tpidx = -1;
     if constexpr (!grouped_k(MODE)) {
       int l2 = 0, h2 = E - 1;
       while (l2 < h2) {
@@ -375,14 +460,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       tmvalid = min(BM, P.offsets[te + 1] - trow0);
       tn0 = nt * (MODE == GATEUP ? GU_COLS : BN);
     } else {
-      te = L / tpe;
-      const int rem = L - te * tpe;
-      const int mt = rem / ntn;
-      const int nt = rem - mt * ntn;
+      int l2 = 0, h2 = E - 1;
+      while (l2 < h2) {
+        const int mid = (l2 + h2 + 1) >> 1;
+        if (tstart[mid] <= L) l2 = mid; else h2 = mid - 1;
+      }
+      te = l2;
+      const int rem = L - tstart[te];
+      const int chunk = rem / tpe;
+      const int t = rem - chunk * tpe;
+      const int mt = t / ntn;
+      const int nt = t - mt * ntn;
       tm0 = mt * BM;
       tn0 = nt * BN;
-      tkbeg = P.offsets[te];
-      tkend = P.offsets[te + 1];
+      const int ob = P.offsets[te], oe = P.offsets[te + 1];
+      const int steps = (oe - ob + BK - 1) / BK;
+      const int len = split_len(steps, split_chunks(steps, kcap)) * BK;
+      tkbeg = ob + chunk * len;
+      tkend = min(oe, tkbeg + len);
+      tpidx = chunk > 0 ? pstart[te] + (chunk - 1) * tpe + t : -1;
     }
     // The decode is the same on every lane; say so, so that the operand
     // bases live in scalar registers and the loads use the scalar-base form.
@@ -393,6 +489,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
     n0 = __builtin_amdgcn_readfirstlane(tn0);
     kbeg = __builtin_amdgcn_readfirstlane(tkbeg);
     kend = __builtin_amdgcn_readfirstlane(tkend);
+    pidx = __builtin_amdgcn_readfirstlane(tpidx);
     ksteps = grouped_k(MODE) ? (kend - kbeg + BK - 1) / BK : kfixed;
   };
   // Per-lane load offsets of the current tile (vector registers; recomputed
@@ -625,7 +722,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   // tile's last valid row; columns past the output's end get an offset
   // outside every range. No LDS and no barriers: the next tile's first
   // loads, already in flight, land meanwhile.
-  auto epilogue = [&](int te, int trow0, int tmvalid, int tm0, int tn0, int nbm) __attribute__((always_inline)) {
+  auto epilogue = [&](int te, int trow0, int tmvalid, int tm0, int tn0, int nbm, int tp)
+                      __attribute__((always_inline)) {
     // Lane-only terms from an opaque copy of the lane index, so that they
     // are not hoisted out of the tile loop (and spilled).
     int lane = lane_id;
@@ -763,31 +861,39 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       }
     } else {
       // fp32 weight gradient of expert te, rows m0.., columns n0..; a 32-row
-      // block lies wholly in dW_gate or wholly in dW_up (I % 64 == 0).
+      // block lies wholly in dW_gate or wholly in dW_up (I % 64 == 0). A
+      // later split-K chunk (tp >= 0) writes its tile to the workspace
+      // instead ([256][256], never accumulated).
       const int mrows = MODE == WGRAD_DOWN ? H : 2 * I;
       const int ncols = MODE == WGRAD_DOWN ? I : H;
+      const bool to_part = tp >= 0;
+      const bool accum = !to_part && P.accumulate != 0;
+      const int ld = to_part ? BN : ncols;  // row length of the destination, floats
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int mblk = tm0 + wm * WTM + i * 32;
         if (mblk >= mrows) continue;
         float* dst;
-        if constexpr (MODE == WGRAD_DOWN) {
+        if (to_part) {
+          dst = P.part + static_cast<int64_t>(tp) * (BM * BN) + (wm * WTM + i * 32) * BN;
+        } else if constexpr (MODE == WGRAD_DOWN) {
           dst = P.dw0 + (static_cast<int64_t>(te) * H + mblk) * I;
         } else {
           dst = mblk < I ? P.dw0 + (static_cast<int64_t>(te) * I + mblk) * H
                          : P.dw1 + (static_cast<int64_t>(te) * I + (mblk - I)) * H;
         }
-        const rsrc_t ro = make_rsrc(dst, 32 * ncols * 4);
+        const rsrc_t ro = make_rsrc(dst, 32 * ld * 4);
 #pragma unroll
         for (int jp = 0; jp < FN / 2; ++jp) {
-          const int n = tn0 + wn * WTN + jp * 64 + pcol;
+          const int n = tn0 + wn * WTN + jp * 64 + pcol;  // column of the gradient
+          const int nd = to_part ? n - tn0 : n;           // column in the destination
           u32x4 old[4][2];
-          if (P.accumulate) {
+          if (accum) {
 #pragma unroll
             for (int b = 0; b < 4; ++b)
 #pragma unroll
               for (int h = 0; h < 2; ++h)
-                old[b][h] = load_b128(ro, n < ncols ? 4u * static_cast<uint32_t>((8 * b + 4 * h + prow) * ncols + n)
+                old[b][h] = load_b128(ro, n < ncols ? 4u * static_cast<uint32_t>((8 * b + 4 * h + prow) * ld + nd)
                                                     : kNoWrite);
           }
 #pragma unroll
@@ -802,14 +908,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
             swap_halves(v[0], v[1]);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-              if (P.accumulate) {
+              if (accum) {
                 v[h][0] += __uint_as_float(old[b][h].x);
                 v[h][1] += __uint_as_float(old[b][h].y);
                 v[h][2] += __uint_as_float(old[b][h].z);
                 v[h][3] += __uint_as_float(old[b][h].w);
               }
-              const uint32_t off =
-                  n < ncols ? 4u * static_cast<uint32_t>((8 * b + 4 * h + prow) * ncols + n) : kNoWrite;
+              const uint32_t off = n < ncols ? 4u * static_cast<uint32_t>((8 * b + 4 * h + prow) * ld + nd) : kNoWrite;
               store_b128(u32x4{__float_as_uint(v[h][0]), __float_as_uint(v[h][1]), __float_as_uint(v[h][2]),
                                __float_as_uint(v[h][3])},
                          ro, off);
@@ -850,7 +955,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
     const int mrows_valid = grouped_k(MODE) ? (MODE == WGRAD_DOWN ? H : 2 * I) - m0 : mvalid;
     const int nbm = __builtin_amdgcn_readfirstlane(max(0, min(FM, (mrows_valid - wm * WTM + 31) / 32)));
     const int nsteps = max(NSTAGE, (ksteps + NSTAGE - 1) / NSTAGE * NSTAGE);
-    const int fe = e, frow0 = row0, fmvalid = mvalid, fm0 = m0, fn0 = n0;
+    const int fe = e, frow0 = row0, fmvalid = mvalid, fm0 = m0, fn0 = n0, fp = pidx;
     const int Lnext = L + nslots;
     auto kloop = [&](auto nbc) __attribute__((always_inline)) {
       for (int s = 0; s + NSTAGE < nsteps; s += NSTAGE) {
@@ -873,7 +978,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       case 1: kloop(std::integral_constant<int, 1>{}); break;
       default: kloop(std::integral_constant<int, 0>{}); break;
     }
-    epilogue(fe, frow0, fmvalid, fm0, fn0, nbm);
+    epilogue(fe, frow0, fmvalid, fm0, fn0, nbm, fp);
     // The next tile's first steps have landed (everything this wavefront
     // issued has: loads and the epilogue's stores, which the counter does
     // not order against each other) in every wavefront, and all are done
@@ -883,6 +988,75 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
     // The offsets again rather than kept alive through the epilogue (the
     // opaque lane index in set_offsets makes this a real recomputation).
     set_offsets();
+  }
+}
+
+// Adds the partial tiles of every split expert into its weight gradient, in
+// chunk order (chunk 0 is already there). Block b takes the split tiles b,
+// b + grid, ...; the split plan is recomputed from the offsets exactly as the
+// GEMM made it (same formulas, same GEMM grid).
+template <int MODE>
+__global__ __launch_bounds__(NT) void wgrad_reduce_kernel(Params P, int gemm_grid) {
+  __shared__ int rstart[1025];  // first split tile of each expert (only split experts have any)
+  __shared__ int pstart[1025];  // first partial tile of each expert
+  __shared__ int part[NT];
+  const int tid = threadIdx.x;
+  const int H = P.H, E = P.E, I = P.I;
+  const int mrows = MODE == WGRAD_DOWN ? H : 2 * I;
+  const int ncols = MODE == WGRAD_DOWN ? I : H;
+  const int ntn = (ncols + BN - 1) / BN;
+  const int tpe = ((mrows + BM - 1) / BM) * ntn;
+  int st[4], c[4], v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid * 4 + j;
+    st[j] = e < E ? (P.offsets[e + 1] - P.offsets[e] + BK - 1) / BK : 0;
+  }
+  expert_scan(st, rstart, part, E, tid);
+  const int cap = split_cap(tpe * rstart[E], gemm_grid);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c[j] = tid * 4 + j < E ? split_chunks(st[j], cap) : 0;
+    v[j] = c[j] > 1 ? tpe : 0;
+  }
+  expert_scan(v, rstart, part, E, tid);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = c[j] > 0 ? (c[j] - 1) * tpe : 0;
+  expert_scan(v, pstart, part, E, tid);
+  const int R = rstart[E];
+  for (int rt = blockIdx.x; rt < R; rt += gridDim.x) {
+    int l2 = 0, h2 = E - 1;  // the split expert whose tiles hold rt
+    while (l2 < h2) {
+      const int mid = (l2 + h2 + 1) >> 1;
+      if (rstart[mid] <= rt) l2 = mid; else h2 = mid - 1;
+    }
+    const int e = l2;
+    const int t = rt - rstart[e];
+    const int mt = t / ntn, nt = t - (t / ntn) * ntn;
+    const int steps = (P.offsets[e + 1] - P.offsets[e] + BK - 1) / BK;
+    const int chunks = split_chunks(steps, cap);
+    for (int q = tid; q < BM * BN / 4; q += NT) {
+      const int row = q / (BN / 4), c4 = (q - row * (BN / 4)) * 4;
+      const int m = mt * BM + row, n = nt * BN + c4;
+      if (m >= mrows || n >= ncols) continue;
+      float* dst;
+      if constexpr (MODE == WGRAD_DOWN) {
+        dst = P.dw0 + (static_cast<int64_t>(e) * H + m) * I + n;
+      } else {
+        dst = m < I ? P.dw0 + (static_cast<int64_t>(e) * I + m) * H + n
+                    : P.dw1 + (static_cast<int64_t>(e) * I + (m - I)) * H + n;
+      }
+      float4 sum = *reinterpret_cast<const float4*>(dst);
+      for (int ch = 1; ch < chunks; ++ch) {
+        const float4 pv = *reinterpret_cast<const float4*>(
+            P.part + static_cast<int64_t>(pstart[e] + (ch - 1) * tpe + t) * (BM * BN) + row * BN + c4);
+        sum.x += pv.x;
+        sum.y += pv.y;
+        sum.z += pv.z;
+        sum.w += pv.w;
+      }
+      *reinterpret_cast<float4*>(dst) = sum;
+    }
   }
 }
 
@@ -900,11 +1074,28 @@ int persistent_grid() {
 
 template <int MODE>
 hipError_t run(const Params& p, hipStream_t st) {
-  grouped_gemm_kernel<MODE><<<persistent_grid(), NT, 0, st>>>(p);
-  return hipGetLastError();
+  const int grid = persistent_grid();
+  grouped_gemm_kernel<MODE><<<grid, NT, 0, st>>>(p);
+  hipError_t err = hipGetLastError();
+  if constexpr (grouped_k(MODE)) {
+    if (err != hipSuccess) return err;
+    // At most 2 * grid split tiles, two per reduction block at most.
+    wgrad_reduce_kernel<MODE><<<grid, NT, 0, st>>>(p, grid);
+    err = hipGetLastError();
+  }
+  return err;
 }
 
 }  // namespace
+
+int gemm_grid() { return persistent_grid(); }
+
+int64_t wgrad_part_tiles(const moe_shape& s) {
+  if (s.dtype != MOE_BF16) return 0;
+  const int64_t tpe_max = static_cast<int64_t>(ceil_div(2 * s.I, BM)) * ceil_div(s.H, BN);
+  const int64_t steps = static_cast<int64_t>(s.T) * s.k / BK + s.E;  // >= the sum over experts of ceil(n_e / BK)
+  return std::min<int64_t>(2 * static_cast<int64_t>(persistent_grid()), tpe_max * (steps / kMinChunkSteps));
+}
 
 hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g, hipStream_t st) {
   Params p{};
@@ -923,6 +1114,7 @@ hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g
   p.dw0 = g.dw0;
   p.dw1 = g.dw1;
   p.accumulate = g.accumulate;
+  p.part = g.part;
   switch (mode) {
     case GEMM_GATEUP: return run<GATEUP>(p, st);
     case GEMM_DOWN: return run<DOWN>(p, st);

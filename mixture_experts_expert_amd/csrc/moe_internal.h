@@ -66,8 +66,16 @@ struct WsLayout {
   size_t hist_bytes;
   size_t dgu_off;    // dtype [T*k][2I]: dG | dU for the backward
   size_t dgu_bytes;
+  size_t part_off;   // fp32 [part_tiles][256][256]: split-K partial weight-gradient tiles
+  size_t part_bytes;
   size_t total;
 };
+
+// Workgroups of a grouped-GEMM launch (one per CU, a multiple of 8) on the
+// current device, and the most partial tiles a weight-gradient launch of
+// shape s can leave for its reduction (bf16 only; 0 for fp32).
+int gemm_grid();
+int64_t wgrad_part_tiles(const moe_shape& s);
 
 WsLayout ws_layout(const moe_shape& s);
 
@@ -108,6 +116,7 @@ enum GemmMode : int {
 
 struct GemmArgs {
   const int32_t* offsets;
+  float* part;  // weight gradients: split-K partial tiles (workspace)
   const void* a;
   const void* b0;
   const void* b1;

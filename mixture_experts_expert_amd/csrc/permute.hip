@@ -158,7 +158,9 @@ WsLayout ws_layout(const moe_shape& s) {
   l.hist_bytes = static_cast<size_t>(nb) * s.E * sizeof(int32_t);
   l.dgu_off = (l.hist_bytes + 255) & ~static_cast<size_t>(255);
   l.dgu_bytes = static_cast<size_t>(n) * 2 * s.I * esz;
-  l.total = l.dgu_off + l.dgu_bytes;
+  l.part_off = (l.dgu_off + l.dgu_bytes + 255) & ~static_cast<size_t>(255);
+  l.part_bytes = static_cast<size_t>(wgrad_part_tiles(s)) * 256 * 256 * sizeof(float);
+  l.total = l.part_off + l.part_bytes;
   return l;
 }
 

@@ -15,6 +15,8 @@ import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
+SPLIT_K = synth.MoEConfig("bf16_split_k", T=4096, H=256, E=8, k=2, I=128, dtype="bf16", backward=True, zipf_s=4.0)
+
 SMALL = [
     synth.CONFIGS["tiny_f32"],
     synth.MoEConfig("tiny_f32_train", T=64, H=128, E=8, k=2, I=64, dtype="f32", backward=True),
@@ -25,6 +27,10 @@ SMALL = [
     synth.MoEConfig("bf16_one_token", T=1, H=64, E=16, k=8, I=64, dtype="bf16", backward=True),
     synth.MoEConfig("bf16_wide_E", T=200, H=128, E=1024, k=4, I=64, dtype="bf16", backward=True),
     synth.MoEConfig("bf16_skew", T=900, H=256, E=32, k=4, I=128, dtype="bf16", backward=True, zipf_s=2.5),
+    # Two experts take nearly every row (about T each): their weight gradients
+    # are reduced in two chunks with a partial-tile reduction (split-K); the
+    # down gradient's 128 columns make a ragged partial tile.
+    SPLIT_K,
 ]
 
 
@@ -79,3 +85,22 @@ def test_training_workloads_sampled(name):
         # The skewed workload leaves experts empty and gives one above 10%.
         assert (counts == 0).sum() >= 1 and counts.max() > 0.10 * cfg.M, counts
     U.check_sampled(d, st, experts)
+
+
+def test_split_k_is_deterministic_and_accumulates():
+    """Bitwise-identical reruns (no float atomics anywhere, split-K included),
+    and accumulate_dw adds a second pass onto the first."""
+    cfg = SPLIT_K
+    U.say(f"[determinism] {cfg}")
+    inp = synth.make_inputs(cfg, seed=3, with_dy=True)
+    d = U.DevInputs(inp)
+    st = U.run_stage(d, True)
+    counts = U.to_np(st.buf["counts"])
+    assert counts.max() > 2048, counts  # the plan splits experts above 64 k-steps of 32 rows here
+    first = {n: st.buf[n].clone() for n in ["y", "dx", "dw_gate", "dw_up", "dw_down", "d_logits", "dx_perm"]}
+    U.run_stage(d, True, stage=st)
+    for n, v in first.items():
+        assert torch.equal(st.buf[n], v), n
+    U.run_stage(d, True, accumulate=True, stage=st)
+    for n in ["dw_gate", "dw_up", "dw_down"]:
+        U.check_close(n + " x2", U.to_np(st.buf[n]), 2.0 * U.to_np(first[n]), 1e-6)
