@@ -5,17 +5,20 @@
 // they are computed in a fixed order that a CPU can reproduce bit for bit: one
 // fp32 fma chain per (token, expert) over h ascending from +0, then + bias.
 // The chain runs on the vector ALUs; a matrix-core accumulation order is not
-// specified and could not be matched. The work is register-tiled so each
-// thread keeps 16 independent chains in flight.
+// specified and could not be matched. Each thread keeps 4 tokens x 4 experts
+// = 16 independent chains in flight: per h it reads one float4 of tokens and
+// one of experts from LDS for 16 FMAs (2 bytes per FMA, what LDS returns at
+// the full fp32 FMA rate), and 16 chains per lane is also the most that still
+// gives every SIMD a wavefront at T = 8192, E = 128.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kRT = 2;              // tokens per thread
+constexpr int kRT = 4;              // tokens per thread
 constexpr int kRE = 4;              // experts per thread
 constexpr int kTy = 16, kTx = 16;   // thread grid of a block
-constexpr int kTileT = kTy * kRT;   // 32 tokens per block
+constexpr int kTileT = kTy * kRT;   // 64 tokens per block
 constexpr int kTileE = kTx * kRE;   // 64 experts per block
 constexpr int kHC = 64;             // h values staged per step
 constexpr int kLogitThreads = kTy * kTx;  // 256
@@ -97,9 +100,9 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(int Tn, in
     const float* wb = ws[buf];
 #pragma unroll 16
     for (int hh = 0; hh < kHC; ++hh) {
-      const float2 xv = *reinterpret_cast<const float2*>(xb + hh * kXS + ty * kRT);
+      const float4 xv = *reinterpret_cast<const float4*>(xb + hh * kXS + ty * kRT);
       const float4 wv = *reinterpret_cast<const float4*>(wb + hh * kWS + tx * kRE);
-      const float xa[kRT] = {xv.x, xv.y};
+      const float xa[kRT] = {xv.x, xv.y, xv.z, xv.w};
       const float wa[kRE] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
       for (int i = 0; i < kRT; ++i)
