@@ -4,7 +4,8 @@
 // results are weighted by its routing weights in the weights' own precision
 // (fp32 here) and summed, then returned in the hidden dtype. One wavefront
 // handles one token; each lane owns 16-byte column chunks, so every row read
-// and the output row write are contiguous across the wavefront.
+// and the output row write are contiguous across the wavefront, and a
+// token's rows are read in batches so that several are in flight at once.
 #include "moe_internal.h"
 
 namespace moe {
@@ -43,7 +44,28 @@ template <> struct Vec<bf16_t> {
   }
 };
 
+// Rows of one token in flight together: a batch's row indices (and weights)
+// come in with one vector load (lane j holds slot j) and are broadcast with
+// readlane, then every row's chunk is loaded, then the sums run in slot
+// order. Slots past k reload the last row and are masked out of the sum
+// (a select, not a branch, so that no load sinks into a conditional).
+constexpr int kBatch = 8;
+
+// Slot j0 + lane's row index and weight (lanes >= kBatch and slots past k
+// repeat the last slot); broadcast one of them with slot_bcast.
+__device__ __forceinline__ void load_slots(const int32_t* __restrict__ f2s, const float* __restrict__ w,
+                                           int64_t tk, int j0, int k, int lane, int& idx, float& wt) {
+  const int j = min(j0 + min(lane, kBatch - 1), k - 1);
+  idx = f2s[tk + j];
+  wt = w ? w[tk + j] : 1.0f;
+}
+__device__ __forceinline__ int slot_bcast(int v, int jj) { return __builtin_amdgcn_readlane(v, jj); }
+__device__ __forceinline__ float slot_bcast(float v, int jj) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), jj));
+}
+
 // y[t] = sum_j w[t,j] * o_perm[f2s[t*k+j]]   (WEIGHTED)   or   sum_j src[f2s[t*k+j]]
+// fp32 sums in ascending j, one rounding to T at the end.
 template <class T, bool WEIGHTED>
 __global__ __launch_bounds__(kThreads) void gather_sum_kernel(int Tn, int k, int chunks,
                                                               const uint4* __restrict__ src,
@@ -52,24 +74,31 @@ __global__ __launch_bounds__(kThreads) void gather_sum_kernel(int Tn, int k, int
                                                               uint4* __restrict__ out) {
   constexpr int N = Vec<T>::N;
   const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + static_cast<int>(threadIdx.x) / kWave);
   if (t >= Tn) return;
   const int64_t tk = static_cast<int64_t>(t) * k;
   for (int c = lane; c < chunks; c += kWave) {
     float acc[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int64_t p = f2s[tk + j];
-      float v[N];
-      Vec<T>::unpack(src[p * chunks + c], v);
-      if (WEIGHTED) {
-        const float wj = w[tk + j];
+    for (int j0 = 0; j0 < k; j0 += kBatch) {
+      int idx;
+      float wt;
+      load_slots(f2s, WEIGHTED ? w : nullptr, tk, j0, k, lane, idx, wt);
+      uint4 v[kBatch];
 #pragma unroll
-        for (int i = 0; i < N; ++i) acc[i] += wj * v[i];
-      } else {
+      for (int jj = 0; jj < kBatch; ++jj) v[jj] = src[static_cast<int64_t>(slot_bcast(idx, jj)) * chunks + c];
 #pragma unroll
-        for (int i = 0; i < N; ++i) acc[i] += v[i];
+      for (int jj = 0; jj < kBatch; ++jj) {
+        const bool live = j0 + jj < k;
+        const float wj = slot_bcast(wt, jj);
+        float x[N];
+        Vec<T>::unpack(v[jj], x);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const float sum = WEIGHTED ? acc[i] + wj * x[i] : acc[i] + x[i];
+          acc[i] = live ? sum : acc[i];
+        }
       }
     }
     out[static_cast<int64_t>(t) * chunks + c] = Vec<T>::pack(acc);
@@ -77,6 +106,9 @@ __global__ __launch_bounds__(kThreads) void gather_sum_kernel(int Tn, int k, int
 }
 
 // do_perm[p] = w[t,j] * dy[t];  gw[t,j] = <dy[t], o_perm[p]>,  p = f2s[t*k+j]
+// Slots go in batches of kBwdBatch; for each batch the row is walked in
+// bands of kWave chunks with the batch's o_perm chunks in flight together.
+constexpr int kBwdBatch = 4;
 template <class T>
 __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(int Tn, int k, int chunks,
                                                                const uint4* __restrict__ dy,
@@ -87,26 +119,47 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(int Tn, int k, in
                                                                float* __restrict__ gw) {
   constexpr int N = Vec<T>::N;
   const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + static_cast<int>(threadIdx.x) / kWave);
   if (t >= Tn) return;  // wave-uniform: no block barrier in this kernel
   const int64_t tk = static_cast<int64_t>(t) * k;
-  for (int j = 0; j < k; ++j) {
-    const int64_t p = f2s[tk + j];
-    const float wj = w[tk + j];
-    float dot = 0.0f;
-    for (int c = lane; c < chunks; c += kWave) {
-      float d[N], o[N], g[N];
-      Vec<T>::unpack(dy[static_cast<int64_t>(t) * chunks + c], d);
-      Vec<T>::unpack(o_perm[p * chunks + c], o);
+  for (int j0 = 0; j0 < k; j0 += kBwdBatch) {
+    int idx;
+    float wt;
+    load_slots(f2s, w, tk, j0, k, lane, idx, wt);
+    int64_t p[kBwdBatch];
+    float wj[kBwdBatch], dot[kBwdBatch];
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        g[i] = wj * d[i];
-        dot += d[i] * o[i];
-      }
-      do_perm[p * chunks + c] = Vec<T>::pack(g);
+    for (int jj = 0; jj < kBwdBatch; ++jj) {
+      p[jj] = slot_bcast(idx, jj);
+      wj[jj] = slot_bcast(wt, jj);
+      dot[jj] = 0.0f;
     }
-    dot = wave_sum(dot);
-    if (lane == 0) gw[tk + j] = dot;
+    for (int c = lane; c < chunks; c += kWave) {
+      const uint4 dv = dy[static_cast<int64_t>(t) * chunks + c];
+      uint4 ov[kBwdBatch];
+#pragma unroll
+      for (int jj = 0; jj < kBwdBatch; ++jj) ov[jj] = o_perm[p[jj] * chunks + c];
+      float d[N];
+      Vec<T>::unpack(dv, d);
+#pragma unroll
+      for (int jj = 0; jj < kBwdBatch; ++jj) {
+        float o[N], g[N];
+        Vec<T>::unpack(ov[jj], o);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          g[i] = wj[jj] * d[i];
+          dot[jj] += d[i] * o[i];
+        }
+        // Slots past k repeat the last row: the same values again, harmless.
+        do_perm[p[jj] * chunks + c] = Vec<T>::pack(g);
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < kBwdBatch; ++jj) {
+      if (j0 + jj >= k) break;
+      const float sdot = wave_sum(dot[jj]);
+      if (lane == 0) gw[tk + j0 + jj] = sdot;
+    }
   }
 }
 
