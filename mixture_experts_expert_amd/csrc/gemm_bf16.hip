@@ -665,16 +665,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   };
   // The 16 MFMAs of one slice in four groups (row block i); load v0 + i of
   // step sn follows group i, so that the wavefront never stalls on a full
-  // address queue with matrix work waiting behind it.
-  auto mfma_slice = [&](auto nbc, const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN], int v0, const rsrc_t& ra,
-                        const rsrc_t& rb, bf16_t* Ln) __attribute__((always_inline)) {
+  // address queue with matrix work waiting behind it. The first slice of a
+  // tile (zc) starts from a zero accumulator instead of clearing it first.
+  auto mfma_slice = [&](auto nbc, auto zc, const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN], int v0,
+                        const rsrc_t& ra, const rsrc_t& rb, bf16_t* Ln) __attribute__((always_inline)) {
     constexpr int nbm = decltype(nbc)::value;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       if (i < nbm) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j) {
+          if constexpr (decltype(zc)::value)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], f32x16{}, 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+      } else if constexpr (decltype(zc)::value) {
+        // Blocks without valid rows are never stored; defined all the same,
+        // so that no value of the previous tile stays alive through this one.
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
       }
       __builtin_amdgcn_sched_barrier(0);
       vmem(v0 + i, ra, rb, Ln);
@@ -695,7 +705,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   // Scheduling fences keep every group where it is written. A tile's last
   // step (last = true) has no middle and reads nothing ahead: the wait for
   // the next tile's first steps comes after the epilogue.
-  auto kstep = [&](auto nbc, const bf16_t* Ac, const bf16_t* An, int sn, bf16_t* Ln, bool last)
+  auto kstep = [&](auto nbc, auto first, const bf16_t* Ac, const bf16_t* An, int sn, bf16_t* Ln, bool last)
                    __attribute__((always_inline)) {
     const rsrc_t ra = rsrc_a(sn);
     const rsrc_t rb = rsrc_b(sn);
@@ -703,14 +713,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
     __builtin_amdgcn_sched_barrier(0);
     read_slice(nbc, Ac, 1, fa1, fb1);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_slice(nbc, fa0, fb0, 0, ra, rb, Ln);
+    mfma_slice(nbc, first, fa0, fb0, 0, ra, rb, Ln);
     if (!last) {
       __builtin_amdgcn_s_waitcnt(kWaitVm12);
       step_barrier();
       read_slice(nbc, An, 0, fa0, fb0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    mfma_slice(nbc, fa1, fb1, LOADS / 2, ra, rb, Ln);
+    mfma_slice(nbc, std::false_type{}, fa1, fb1, LOADS / 2, ra, rb, Ln);
   };
 
   // ---- epilogue -------------------------------------------------------------
@@ -942,12 +952,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   for (; L < hi; L += nslots) {
     set_frag_offsets();
     read_slice(std::integral_constant<int, FM>{}, lds0, 0, fa0, fb0);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
     // This wavefront's 32-row blocks that hold valid rows of the tile (a
     // ragged last tile of an expert skips the MFMAs, fragment reads and
     // stores of the others). The k-loop is compiled once per count, so no
@@ -957,19 +961,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
     const int nsteps = max(NSTAGE, (ksteps + NSTAGE - 1) / NSTAGE * NSTAGE);
     const int fe = e, frow0 = row0, fmvalid = mvalid, fm0 = m0, fn0 = n0, fp = pidx;
     const int Lnext = L + nslots;
+    constexpr std::false_type no{};
     auto kloop = [&](auto nbc) __attribute__((always_inline)) {
-      for (int s = 0; s + NSTAGE < nsteps; s += NSTAGE) {
-        kstep(nbc, lds0, lds1, s + 3, lds3, false);
-        kstep(nbc, lds1, lds2, s + 4, lds0, false);
-        kstep(nbc, lds2, lds3, s + 5, lds1, false);
-        kstep(nbc, lds3, lds0, s + 6, lds2, false);
+      kstep(nbc, std::true_type{}, lds0, lds1, 3, lds3, false);  // step 0: accumulators start at zero
+      for (int s = NSTAGE; s < nsteps; s += NSTAGE) {           // steps s - 3 .. s
+        kstep(nbc, no, lds1, lds2, s, lds0, false);
+        kstep(nbc, no, lds2, lds3, s + 1, lds1, false);
+        kstep(nbc, no, lds3, lds0, s + 2, lds2, false);
+        kstep(nbc, no, lds0, lds1, s + 3, lds3, false);
       }
-      kstep(nbc, lds0, lds1, nsteps - 1, lds3, false);
       if (Lnext < hi) set_tile_and_offsets(Lnext);
       else clear_tile();
-      kstep(nbc, lds1, lds2, 0, lds0, false);
-      kstep(nbc, lds2, lds3, 1, lds1, false);
-      kstep(nbc, lds3, lds0, 2, lds2, true);
+      kstep(nbc, no, lds1, lds2, 0, lds0, false);
+      kstep(nbc, no, lds2, lds3, 1, lds1, false);
+      kstep(nbc, no, lds3, lds0, 2, lds2, true);
     };
     switch (nbm) {
       case 4: kloop(std::integral_constant<int, 4>{}); break;
