@@ -200,11 +200,12 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // Lane exchanges inside each quad of lanes (DPP quad_perm [1,0,3,2] and
 // [2,3,0,1]): the value of lane l ^ 1, of lane l ^ 2.
+// Every lane of a quad has a valid source, so no "old" value is needed.
 __device__ __forceinline__ uint32_t quad_swap1(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, true));
 }
 __device__ __forceinline__ uint32_t quad_swap2(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false));
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float quad_swap1f(float v) { return __uint_as_float(quad_swap1(__float_as_uint(v))); }
 __device__ __forceinline__ float quad_swap2f(float v) { return __uint_as_float(quad_swap2(__float_as_uint(v))); }
@@ -877,61 +878,59 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       const int mrows = MODE == WGRAD_DOWN ? H : 2 * I;
       const int ncols = MODE == WGRAD_DOWN ? I : H;
       const bool to_part = tp >= 0;
-      const bool accum = !to_part && P.accumulate != 0;
       const int ld = to_part ? BN : ncols;  // row length of the destination, floats
+      // After the quad transpose lane l holds row 8b + 4(l/32) + l%4 of the
+      // 32-row block, columns (l%32)/4*4 .. + 3 of the 32-column block: each
+      // store covers 8 rows x 128 bytes. The += form (compiled separately,
+      // so the plain form carries none of it) reads the old values first.
+      const int hrow = (lane >> 5) * 4 + prow;
+      const int lcol = (lane & 31) & ~3;
+      auto store_blocks = [&](auto accum) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int mblk = tm0 + wm * WTM + i * 32;
-        if (mblk >= mrows) continue;
-        float* dst;
-        if (to_part) {
-          dst = P.part + static_cast<int64_t>(tp) * (BM * BN) + (wm * WTM + i * 32) * BN;
-        } else if constexpr (MODE == WGRAD_DOWN) {
-          dst = P.dw0 + (static_cast<int64_t>(te) * H + mblk) * I;
-        } else {
-          dst = mblk < I ? P.dw0 + (static_cast<int64_t>(te) * I + mblk) * H
-                         : P.dw1 + (static_cast<int64_t>(te) * I + (mblk - I)) * H;
-        }
-        const rsrc_t ro = make_rsrc(dst, 32 * ld * 4);
-#pragma unroll
-        for (int jp = 0; jp < FN / 2; ++jp) {
-          const int n = tn0 + wn * WTN + jp * 64 + pcol;  // column of the gradient
-          const int nd = to_part ? n - tn0 : n;           // column in the destination
-          u32x4 old[4][2];
-          if (accum) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-              for (int h = 0; h < 2; ++h)
-                old[b][h] = load_b128(ro, n < ncols ? 4u * static_cast<uint32_t>((8 * b + 4 * h + prow) * ld + nd)
-                                                    : kNoWrite);
+        for (int i = 0; i < FM; ++i) {
+          const int mblk = tm0 + wm * WTM + i * 32;
+          if (mblk >= mrows) continue;
+          float* dst;
+          if (to_part) {
+            dst = P.part + static_cast<int64_t>(tp) * (BM * BN) + (wm * WTM + i * 32) * BN;
+          } else if constexpr (MODE == WGRAD_DOWN) {
+            dst = P.dw0 + (static_cast<int64_t>(te) * H + mblk) * I;
+          } else {
+            dst = mblk < I ? P.dw0 + (static_cast<int64_t>(te) * I + mblk) * H
+                           : P.dw1 + (static_cast<int64_t>(te) * I + (mblk - I)) * H;
           }
+          const rsrc_t ro = make_rsrc(dst, 32 * ld * 4);
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            float v[2][4];
+          for (int j = 0; j < FN; ++j) {
+            const int n = tn0 + wn * WTN + j * 32 + lcol;  // column of the gradient
+            const int nd = to_part ? n - tn0 : n;          // column in the destination
+            u32x4 old[4];
+            if constexpr (decltype(accum)::value) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-#pragma unroll
-              for (int q = 0; q < 4; ++q) v[j][q] = acc[i][2 * jp + j][4 * b + q];
-              quad_transpose(v[j], lane);
+              for (int b = 0; b < 4; ++b)
+                old[b] = load_b128(ro, n < ncols ? 4u * static_cast<uint32_t>((8 * b + hrow) * ld + nd) : kNoWrite);
             }
-            swap_halves(v[0], v[1]);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              if (accum) {
-                v[h][0] += __uint_as_float(old[b][h].x);
-                v[h][1] += __uint_as_float(old[b][h].y);
-                v[h][2] += __uint_as_float(old[b][h].z);
-                v[h][3] += __uint_as_float(old[b][h].w);
+            for (int b = 0; b < 4; ++b) {
+              float v[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * b + q];
+              quad_transpose(v, lane);
+              if constexpr (decltype(accum)::value) {
+                v[0] += __uint_as_float(old[b].x);
+                v[1] += __uint_as_float(old[b].y);
+                v[2] += __uint_as_float(old[b].z);
+                v[3] += __uint_as_float(old[b].w);
               }
-              const uint32_t off = n < ncols ? 4u * static_cast<uint32_t>((8 * b + 4 * h + prow) * ld + nd) : kNoWrite;
-              store_b128(u32x4{__float_as_uint(v[h][0]), __float_as_uint(v[h][1]), __float_as_uint(v[h][2]),
-                               __float_as_uint(v[h][3])},
+              const uint32_t off = n < ncols ? 4u * static_cast<uint32_t>((8 * b + hrow) * ld + nd) : kNoWrite;
+              store_b128(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])},
                          ro, off);
             }
           }
         }
-      }
+      };
+      if (!to_part && P.accumulate != 0) store_blocks(std::true_type{});
+      else store_blocks(std::false_type{});
     }
   };
 
