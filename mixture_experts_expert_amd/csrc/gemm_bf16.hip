@@ -270,6 +270,25 @@ __device__ __forceinline__ void swap_halves(float (&x)[4], float (&y)[4]) {
   }
 }
 
+// Exchange with lane l ^ 4: a DPP row shift left by 4 writes the lanes with
+// bit 2 clear (banks 0 and 2 of each 16-lane row), a shift right by 4 the
+// others (banks 1 and 3).
+__device__ __forceinline__ uint32_t swap4(uint32_t v) {
+  const int a = __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x104, 0xF, 0x5, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(a, static_cast<int>(v), 0x114, 0xF, 0xA, false));
+}
+// Two quad-transposed bf16 results of column blocks 2jp (t0) and 2jp + 1
+// (t1), same row, into eight consecutive columns per lane: lanes with bit 2
+// clear take columns 8m .. 8m + 7 (m = lane%32 / 8) of block 2jp, the others
+// the same columns of block 2jp + 1. A store of the result covers eight rows
+// (four per wavefront half) x 64 columns.
+__device__ __forceinline__ u32x4 pair_cols8(u32x2 t0, u32x2 t1, int lane) {
+  const bool hi = (lane & 4) != 0;
+  const u32x2 send = hi ? t0 : t1;
+  const uint32_t r0 = swap4(send.x), r1 = swap4(send.y);
+  return hi ? u32x4{r0, r1, t1.x, t1.y} : u32x4{t0.x, t0.y, r0, r1};
+}
+
 // Exclusive prefix over experts of v (expert tid*4 + j in v[j]) into
 // out[0..E], out[E] the total; a block of NT threads, `part` NT ints of LDS.
 __device__ __forceinline__ void expert_scan(const int (&v)[4], int* out, int* part, int E, int tid) {
@@ -788,7 +807,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
           store_b64(ap[1], rs, off4);
         }
     } else if constexpr (MODE == DOWN || MODE == DGRAD_GATEUP) {
+      // 16-byte stores: lane l writes row 8b + 4(l/32) + l%4, columns
+      // jp*64 + 32*((l/4)%2) + 8*((l%32)/8) .. + 7 (pair_cols8).
       const rsrc_t ro = make_rsrc(P.out0 + static_cast<int64_t>(trow0) * H, 2 * tmvalid * H);
+      const int hrow = 4 * (lane >> 5) + prow;
+      const int ncol8 = ((lane >> 2) & 1) * 32 + ((lane & 31) >> 3) * 8;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -796,10 +819,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             if (i >= nbm) continue;  // no valid rows in this block
-            const int r = wm * WTM + i * 32 + 8 * b + prow;
-            const int n = tn0 + wn * WTN + jp * 64 + pcol;
+            const int r = wm * WTM + i * 32 + 8 * b + hrow;
+            const int n = tn0 + wn * WTN + jp * 64 + ncol8;
             const uint32_t off = n < H ? 2u * static_cast<uint32_t>(r * H + n) : kNoWrite;
-            const uint32_t off4 = n < H ? off + 8u * H : kNoWrite;
             u32x2 t[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -808,9 +830,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
               for (int q = 0; q < 4; ++q) v[q] = acc[i][2 * jp + j][4 * b + q];
               t[j] = quad_transpose_bf16(v, lane);
             }
-            swap_halves(t[0], t[1]);
-            store_b64(t[0], ro, off);
-            store_b64(t[1], ro, off4);
+            store_b128(pair_cols8(t[0], t[1], lane), ro, off);
           }
     } else if constexpr (MODE == DGRAD_DOWN) {
       // dA -> dG = dA U silu'(G), dU = dA silu(G), with the saved G and U of
@@ -819,12 +839,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       const rsrc_t rg = make_rsrc(P.g_in + base, 2 * tmvalid * I);
       const rsrc_t ru = make_rsrc(P.u_in + base, 2 * tmvalid * I);
       const rsrc_t ro = make_rsrc(P.out0 + 2 * base, 4 * tmvalid * I);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        if (i >= nbm) continue;  // no valid rows in this block
-        // All of a row block's saved G and U first, so that their latency
-        // overlaps.
-        u32x2 gb[FN / 2][4][2], ub[FN / 2][4][2];
+      // The saved G and U of a row block (32 loads per lane) are read one
+      // row block ahead, so that their latency overlaps the previous block's
+      // arithmetic and stores.
+      typedef u32x2 GU[FN / 2][4][2];
+      auto load_gu = [&](int i, GU& gb, GU& ub) __attribute__((always_inline)) {
 #pragma unroll
         for (int jp = 0; jp < FN / 2; ++jp)
 #pragma unroll
@@ -838,6 +857,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
             ub[jp][b][0] = load_b64(ru, off);
             ub[jp][b][1] = load_b64(ru, off4);
           }
+      };
+      GU gb[2], ub[2];
+      if (nbm > 0) load_gu(0, gb[0], ub[0]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if (i >= nbm) continue;  // no valid rows in this block
+        if (i + 1 < FM && i + 1 < nbm) load_gu(i + 1, gb[(i + 1) & 1], ub[(i + 1) & 1]);
+        const GU& gc = gb[i & 1];
+        const GU& uc = ub[i & 1];
 #pragma unroll
         for (int jp = 0; jp < FN / 2; ++jp)
 #pragma unroll
@@ -854,7 +882,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
             swap_halves(da[0], da[1]);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-              const u32x2 gw = gb[jp][b][h], uw = ub[jp][b][h];
+              const u32x2 gw = gc[jp][b][h], uw = uc[jp][b][h];
               const float gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
               const float uv[4] = {bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y)};
               float dg[4], du[4];
