@@ -245,31 +245,6 @@ __device__ __forceinline__ u32x2 quad_transpose_bf16(const float (&v)[4], int la
   return u32x2{__builtin_amdgcn_perm(y0, a0, sel), __builtin_amdgcn_perm(y1, a1, sel)};
 }
 
-// Swap of wavefront halves between two registers: afterwards x holds the
-// low 32 lanes of both inputs (x's in lanes 0-31, y's in lanes 32-63), y the
-// high 32 lanes of both (v_permlane32_swap).
-__device__ __forceinline__ void swap_halves(uint32_t& x, uint32_t& y) {
-  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
-  x = r[0];
-  y = r[1];
-}
-__device__ __forceinline__ void swap_halves(u32x2& x, u32x2& y) {
-  uint32_t x0 = x.x, x1 = x.y, y0 = y.x, y1 = y.y;
-  swap_halves(x0, y0);
-  swap_halves(x1, y1);
-  x = u32x2{x0, x1};
-  y = u32x2{y0, y1};
-}
-__device__ __forceinline__ void swap_halves(float (&x)[4], float (&y)[4]) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t a = __float_as_uint(x[q]), b = __float_as_uint(y[q]);
-    swap_halves(a, b);
-    x[q] = __uint_as_float(a);
-    y[q] = __uint_as_float(b);
-  }
-}
-
 // Exchange with lane l ^ 4: a DPP row shift left by 4 writes the lanes with
 // bit 2 clear (banks 0 and 2 of each 16-lane row), a shift right by 4 the
 // others (banks 1 and 3).
@@ -287,6 +262,17 @@ __device__ __forceinline__ u32x4 pair_cols8(u32x2 t0, u32x2 t1, int lane) {
   const u32x2 send = hi ? t0 : t1;
   const uint32_t r0 = swap4(send.x), r1 = swap4(send.y);
   return hi ? u32x4{r0, r1, t1.x, t1.y} : u32x4{t0.x, t0.y, r0, r1};
+}
+
+// The same for fp32 values: eight consecutive columns of one row in o.
+__device__ __forceinline__ void pair_cols8(const float (&t0)[4], const float (&t1)[4], int lane, float (&o)[8]) {
+  const bool hi = (lane & 4) != 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float r = __uint_as_float(swap4(__float_as_uint(hi ? t0[q] : t1[q])));
+    o[q] = hi ? r : t0[q];
+    o[q + 4] = hi ? t1[q] : r;
+  }
 }
 
 // Exclusive prefix over experts of v (expert tid*4 + j in v[j]) into
@@ -746,24 +732,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   // ---- epilogue -------------------------------------------------------------
   // acc[i][j][q] holds wavefront-tile row i*32 + 8*(q/4) + 4*(lane/32) + q%4,
   // column j*32 + lane%32. A quad transpose of each group of four q leaves
-  // lane l with row i*32 + 8*(q/4) + erow, columns j*32 + ecol .. + 3, so
-  // every lane stores four consecutive columns of one row. Results go out
-  // straight from registers through buffer resources whose range ends at the
-  // tile's last valid row; columns past the output's end get an offset
-  // outside every range. No LDS and no barriers: the next tile's first
-  // loads, already in flight, land meanwhile.
+  // lane l with row i*32 + 8*(q/4) + 4*(lane/32) + lane%4, columns
+  // j*32 + (lane%32)/4*4 .. + 3: four consecutive columns of one row (fp32
+  // outputs store these, 8 rows x 128 bytes per store). For bf16 outputs an
+  // exchange with lane l ^ 4 (pair_cols8) joins column blocks 2jp and
+  // 2jp + 1 into eight columns per lane, so that each 16-byte store covers
+  // 8 rows x 128 bytes. Results go out straight from registers through
+  // buffer resources whose range ends at the tile's last valid row; columns
+  // past the output's end get an offset outside every range. No LDS and no
+  // barriers: the next tile's first loads, already in flight, land meanwhile.
   auto epilogue = [&](int te, int trow0, int tmvalid, int tm0, int tn0, int nbm, int tp)
                       __attribute__((always_inline)) {
     // Lane-only terms from an opaque copy of the lane index, so that they
     // are not hoisted out of the tile loop (and spilled).
     int lane = lane_id;
     asm volatile("" : "+v"(lane));
-    // After the quad transpose, a swap of the wavefront halves between the
-    // column blocks 2 jp and 2 jp + 1 leaves lane l with row 8*(q/4) + prow
-    // (first result) or that + 4 (second), columns 64 jp + pcol .. + 3: each
-    // store covers four rows, 64 contiguous columns of each.
     const int prow = lane & 3;
-    const int pcol = lane & ~3;
     if constexpr (MODE == GATEUP) {
       // Wavefront-tile columns 0..63 are gate, 64..127 up, for the same 64
       // intermediate indices: G, U and A = silu(G) U of one element sit in
@@ -773,15 +757,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       const rsrc_t rg = make_rsrc(P.out0 + base, bytes);
       const rsrc_t ru = make_rsrc(P.out1 + base, bytes);
       const rsrc_t rs = make_rsrc(P.out2 + base, bytes);
-      const int idx = tn0 + wn * 64 + pcol;
+      // 16-byte stores (pair_cols8): lane l writes row 8b + 4(l/32) + l%4 of
+      // the row block, intermediate indices 32*((l/4)%2) + 8*((l%32)/8) .. + 7
+      // of the wavefront's 64.
+      const int hrow = 4 * (lane >> 5) + prow;
+      const int idx = tn0 + wn * 64 + ((lane >> 2) & 1) * 32 + ((lane & 31) >> 3) * 8;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           if (i >= nbm) continue;  // no valid rows in this block
-          const int r = wm * WTM + i * 32 + 8 * b + prow;
+          const int r = wm * WTM + i * 32 + 8 * b + hrow;
           const uint32_t off = idx < I ? 2u * static_cast<uint32_t>(r * I + idx) : kNoWrite;
-          const uint32_t off4 = idx < I ? off + 8u * I : kNoWrite;
           u32x2 gp[2], up[2], ap[2];
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
@@ -796,15 +783,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
             up[j] = quad_transpose_bf16(u, lane);
             ap[j] = quad_transpose_bf16(a, lane);
           }
-          swap_halves(gp[0], gp[1]);
-          swap_halves(up[0], up[1]);
-          swap_halves(ap[0], ap[1]);
-          store_b64(gp[0], rg, off);
-          store_b64(gp[1], rg, off4);
-          store_b64(up[0], ru, off);
-          store_b64(up[1], ru, off4);
-          store_b64(ap[0], rs, off);
-          store_b64(ap[1], rs, off4);
+          store_b128(pair_cols8(gp[0], gp[1], lane), rg, off);
+          store_b128(pair_cols8(up[0], up[1], lane), ru, off);
+          store_b128(pair_cols8(ap[0], ap[1], lane), rs, off);
         }
     } else if constexpr (MODE == DOWN || MODE == DGRAD_GATEUP) {
       // 16-byte stores: lane l writes row 8b + 4(l/32) + l%4, columns
@@ -839,23 +820,24 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       const rsrc_t rg = make_rsrc(P.g_in + base, 2 * tmvalid * I);
       const rsrc_t ru = make_rsrc(P.u_in + base, 2 * tmvalid * I);
       const rsrc_t ro = make_rsrc(P.out0 + 2 * base, 4 * tmvalid * I);
-      // The saved G and U of a row block (32 loads per lane) are read one
-      // row block ahead, so that their latency overlaps the previous block's
-      // arithmetic and stores.
-      typedef u32x2 GU[FN / 2][4][2];
+      // 16-byte lanes (pair_cols8): lane l handles row 8b + 4(l/32) + l%4 of
+      // the row block, columns 32*((l/4)%2) + 8*((l%32)/8) .. + 7 of the
+      // 64-column pair jp. The saved G and U of a row block (16 loads per
+      // lane) are read one row block ahead, so that their latency overlaps
+      // the previous block's arithmetic and stores.
+      const int hrow = 4 * (lane >> 5) + prow;
+      const int ncol8 = ((lane >> 2) & 1) * 32 + ((lane & 31) >> 3) * 8;
+      typedef u32x4 GU[FN / 2][4];
       auto load_gu = [&](int i, GU& gb, GU& ub) __attribute__((always_inline)) {
 #pragma unroll
         for (int jp = 0; jp < FN / 2; ++jp)
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
-            const int r = wm * WTM + i * 32 + 8 * b + prow;
-            const int n = tn0 + wn * WTN + jp * 64 + pcol;
+            const int r = wm * WTM + i * 32 + 8 * b + hrow;
+            const int n = tn0 + wn * WTN + jp * 64 + ncol8;
             const uint32_t off = n < I ? 2u * static_cast<uint32_t>(r * I + n) : kNoWrite;
-            const uint32_t off4 = n < I ? off + 8u * I : kNoWrite;
-            gb[jp][b][0] = load_b64(rg, off);
-            gb[jp][b][1] = load_b64(rg, off4);
-            ub[jp][b][0] = load_b64(ru, off);
-            ub[jp][b][1] = load_b64(ru, off4);
+            gb[jp][b] = load_b128(rg, off);
+            ub[jp][b] = load_b128(ru, off);
           }
       };
       GU gb[2], ub[2];
@@ -870,32 +852,36 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
         for (int jp = 0; jp < FN / 2; ++jp)
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
-            const int r = wm * WTM + i * 32 + 8 * b + prow;
-            const int n = tn0 + wn * WTN + jp * 64 + pcol;
-            float da[2][4];
+            const int r = wm * WTM + i * 32 + 8 * b + hrow;
+            const int n = tn0 + wn * WTN + jp * 64 + ncol8;
+            float da[2][4], d8[8];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
 #pragma unroll
               for (int q = 0; q < 4; ++q) da[j][q] = acc[i][2 * jp + j][4 * b + q];
               quad_transpose(da[j], lane);
             }
-            swap_halves(da[0], da[1]);
+            pair_cols8(da[0], da[1], lane, d8);
+            const u32x4 gw = gc[jp][b], uw = uc[jp][b];
+            const uint32_t gwv[4] = {gw.x, gw.y, gw.z, gw.w}, uwv[4] = {uw.x, uw.y, uw.z, uw.w};
+            uint32_t dgp[4], dup[4];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const u32x2 gw = gc[jp][b][h], uw = uc[jp][b][h];
-              const float gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
-              const float uv[4] = {bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y)};
-              float dg[4], du[4];
+            for (int w = 0; w < 4; ++w) {
+              float dg[2], du[2];
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const float sg = sigmoid_fast(gv[q]);
-                dg[q] = da[h][q] * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
-                du[q] = da[h][q] * (gv[q] * sg);
+              for (int h = 0; h < 2; ++h) {
+                const float gv = h ? bf16_hi(gwv[w]) : bf16_lo(gwv[w]);
+                const float uv = h ? bf16_hi(uwv[w]) : bf16_lo(uwv[w]);
+                const float sg = sigmoid_fast(gv);
+                dg[h] = d8[2 * w + h] * uv * sg * (1.0f + gv * (1.0f - sg));
+                du[h] = d8[2 * w + h] * (gv * sg);
               }
-              const uint32_t off = n < I ? 2u * static_cast<uint32_t>((r + 4 * h) * 2 * I + n) : kNoWrite;
-              store_b64(pack_bf16x4v(dg), ro, off);
-              store_b64(pack_bf16x4v(du), ro, off == kNoWrite ? kNoWrite : off + 2u * I);
+              dgp[w] = pack_bf16x2(dg[0], dg[1]);
+              dup[w] = pack_bf16x2(du[0], du[1]);
             }
+            const uint32_t off = n < I ? 2u * static_cast<uint32_t>(r * 2 * I + n) : kNoWrite;
+            store_b128(u32x4{dgp[0], dgp[1], dgp[2], dgp[3]}, ro, off);
+            store_b128(u32x4{dup[0], dup[1], dup[2], dup[3]}, ro, off == kNoWrite ? kNoWrite : off + 2u * I);
           }
       }
     } else {
