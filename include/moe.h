@@ -5,6 +5,9 @@
  *
  *   forward : moe_route -> moe_permute -> moe_grouped_gemm_fwd -> moe_combine
  *   backward: moe_combine_bwd -> moe_grouped_gemm_bwd -> moe_unpermute_sum -> moe_route_bwd
+ *   inference (gather and routing weights fused into the GEMMs):
+ *             moe_forward_fused = moe_route -> moe_permute_fused ->
+ *             moe_gemm_gate_up_gathered -> moe_gemm_down_weighted -> moe_unpermute_sum
  *
  * It replaces the per-expert for-loop of the Hugging Face MoE block (axolotl
  * issue #3155, "Feature description") with router softmax/top-k, a sort of the
@@ -190,6 +193,54 @@ moe_status moe_unpermute_sum(moe_shape s, const void* dx_perm, const int32_t* fl
  *   dropped.) Output: d_logits [T,E] f32. */
 moe_status moe_route_bwd(moe_shape s, const float* d_topk_w, const float* topk_w, const int32_t* topk_idx,
                          float* d_logits, hipStream_t stream);
+
+/* ---- Inference forward with the gather and the routing weights fused into
+ * the GEMMs (the fused-mul-post path of unsloth PR #3812, "[MoE] Improve moe
+ * kernels for unsloth fine tuning", Codex review of the grouped GEMM
+ * interface; the unsorted-token gather of the sourcepulse summary, "How It
+ * Works"). No x_perm is built and no weighted combine runs: the gate/up GEMM
+ * reads each sorted row straight from x, the down GEMM multiplies each output
+ * row by its routing weight before rounding, and y is the plain per-token sum
+ * of moe_unpermute_sum. The result equals moe_route -> moe_permute ->
+ * moe_grouped_gemm_fwd -> moe_combine up to where the rounding to the
+ * activation dtype happens (here after the weight is applied). */
+
+/* moe_permute without the gather: counts, offsets, sorted_to_flat and
+ * flat_to_sorted exactly as moe_permute, plus for each sorted row p
+ *   row_token[p]  = sorted_to_flat[p] / k          (int32 [T*k])
+ *   row_weight[p] = topk_w[sorted_to_flat[p]]      (f32   [T*k])
+ * Inputs: topk_idx [T,k] int32, topk_w [T,k] f32 (from moe_route).
+ * Workspace: ws of ws_bytes >= moe_workspace_bytes(s). */
+moe_status moe_permute_fused(moe_shape s, const int32_t* topk_idx, const float* topk_w, int32_t* counts,
+                             int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted, int32_t* row_token,
+                             float* row_weight, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_gemm_gate_up with row p of its input read as row row_token[p] of x
+ * [T,H] (dtype) instead of x_perm. g and u [T*k,I] are stored when both are
+ * non-null, skipped when both are null (inference needs a only); one null and
+ * one not is MOE_EINVAL. T*H*sizeof(dtype) must stay below 2^31
+ * (MOE_EUNSUPPORTED otherwise). */
+moe_status moe_gemm_gate_up_gathered(moe_shape s, const void* x, const int32_t* row_token, const int32_t* offsets,
+                                     const void* w_gate, const void* w_up, void* g, void* u, void* a,
+                                     hipStream_t stream);
+
+/* moe_gemm_down with output row p multiplied by row_weight[p] (f32, from
+ * moe_permute_fused) in fp32 before the rounding to dtype:
+ *   o_perm[p,:] = row_weight[p] * (a[p,:] W_down[e]^T). */
+moe_status moe_gemm_down_weighted(moe_shape s, const void* a, const int32_t* offsets, const void* w_down,
+                                  const float* row_weight, void* o_perm, hipStream_t stream);
+
+/* The fused inference forward in one call: moe_route (logits, topk_idx,
+ * topk_w), moe_permute_fused (counts, offsets, sorted_to_flat,
+ * flat_to_sorted, row_token, row_weight), moe_gemm_gate_up_gathered (a only),
+ * moe_gemm_down_weighted (o_perm) and moe_unpermute_sum (y [T,H]). Every
+ * buffer is caller-owned and overwritten; logit_bias may be NULL. Workspace:
+ * ws of ws_bytes >= moe_workspace_bytes(s). */
+moe_status moe_forward_fused(moe_shape s, const void* x, const void* w_router, const float* logit_bias,
+                             const void* w_gate, const void* w_up, const void* w_down, float* logits,
+                             int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted_to_flat, int32_t* flat_to_sorted, int32_t* row_token, float* row_weight,
+                             void* a, void* o_perm, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* A static, human-readable name for a status code. */
 const char* moe_status_string(moe_status status);

@@ -60,6 +60,10 @@ _SIGS = {
     "moe_gemm_gate_up_dgrad": ([moe_shape, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_gemm_gate_up_wgrad": ([moe_shape, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_size_t, _P],
                                ctypes.c_int),
+    "moe_permute_fused": ([moe_shape, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_gemm_gate_up_gathered": ([moe_shape, _P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_gemm_down_weighted": ([moe_shape, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_forward_fused": ([moe_shape] + [_P] * 19 + [ctypes.c_size_t, _P], ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -181,6 +185,35 @@ def moe_gemm_gate_up_wgrad(s, dgu, x_perm, offsets, dw_gate, dw_up, accumulate_d
     _check("moe_gemm_gate_up_wgrad", lib.moe_gemm_gate_up_wgrad(s, _ptr(dgu), _ptr(x_perm), _ptr(offsets),
                                                                 _ptr(dw_gate), _ptr(dw_up), int(accumulate_dw),
                                                                 _ptr(ws), nb, _stream(stream)))
+
+
+def moe_permute_fused(s, topk_idx, topk_w, counts, offsets, sorted_to_flat, flat_to_sorted, row_token, row_weight,
+                      ws, ws_bytes=None, stream=None):
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_permute_fused", lib.moe_permute_fused(s, _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets),
+                                                      _ptr(sorted_to_flat), _ptr(flat_to_sorted), _ptr(row_token),
+                                                      _ptr(row_weight), _ptr(ws), nb, _stream(stream)))
+
+
+def moe_gemm_gate_up_gathered(s, x, row_token, offsets, w_gate, w_up, g, u, a, stream=None):
+    _check("moe_gemm_gate_up_gathered", lib.moe_gemm_gate_up_gathered(
+        s, _ptr(x), _ptr(row_token), _ptr(offsets), _ptr(w_gate), _ptr(w_up), _ptr(g), _ptr(u), _ptr(a),
+        _stream(stream)))
+
+
+def moe_gemm_down_weighted(s, a, offsets, w_down, row_weight, o_perm, stream=None):
+    _check("moe_gemm_down_weighted", lib.moe_gemm_down_weighted(s, _ptr(a), _ptr(offsets), _ptr(w_down),
+                                                                _ptr(row_weight), _ptr(o_perm), _stream(stream)))
+
+
+def moe_forward_fused(s, x, w_router, logit_bias, w_gate, w_up, w_down, logits, topk_idx, topk_w, counts, offsets,
+                      sorted_to_flat, flat_to_sorted, row_token, row_weight, a, o_perm, y, ws, ws_bytes=None,
+                      stream=None):
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_forward_fused", lib.moe_forward_fused(
+        s, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(logits),
+        _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(sorted_to_flat), _ptr(flat_to_sorted),
+        _ptr(row_token), _ptr(row_weight), _ptr(a), _ptr(o_perm), _ptr(y), _ptr(ws), nb, _stream(stream)))
 
 
 class MoEStage:

@@ -178,6 +178,75 @@ moe_status moe_grouped_gemm_fwd(moe_shape s, const void* x_perm, const int32_t* 
   return moe_gemm_down(s, a, offsets, w_down, o_perm, stream);
 }
 
+moe_status moe_permute_fused(moe_shape s, const int32_t* topk_idx, const float* topk_w, int32_t* counts,
+                             int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted, int32_t* row_token,
+                             float* row_weight, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(topk_idx, topk_w, counts, offsets, sorted_to_flat, flat_to_sorted, row_token, row_weight, ws))
+    return MOE_EINVAL;
+  if (ws_bytes < moe::ws_layout(s).total) return MOE_EWORKSPACE;
+  return from_hip(moe::launch_permute_fused(s, topk_idx, topk_w, counts, offsets, sorted_to_flat, flat_to_sorted,
+                                            row_token, row_weight, ws, stream));
+}
+
+moe_status moe_gemm_gate_up_gathered(moe_shape s, const void* x, const int32_t* row_token, const int32_t* offsets,
+                                     const void* w_gate, const void* w_up, void* g, void* u, void* a,
+                                     hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(x, row_token, offsets, w_gate, w_up, a)) return MOE_EINVAL;
+  if ((g == nullptr) != (u == nullptr)) return MOE_EINVAL;
+  // x is addressed with 32-bit byte offsets.
+  if (static_cast<int64_t>(s.T) * s.H * (s.dtype == MOE_BF16 ? 2 : 4) >= (static_cast<int64_t>(1) << 31))
+    return MOE_EUNSUPPORTED;
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = x;
+  ga.row_token = row_token;
+  ga.b0 = w_gate;
+  ga.b1 = w_up;
+  ga.out0 = g;
+  ga.out1 = u;
+  ga.out2 = a;
+  return from_hip(moe::launch_gemm(moe::GEMM_GATEUP, s, ga, stream));
+}
+
+moe_status moe_gemm_down_weighted(moe_shape s, const void* a, const int32_t* offsets, const void* w_down,
+                                  const float* row_weight, void* o_perm, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(a, offsets, w_down, row_weight, o_perm)) return MOE_EINVAL;
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = a;
+  ga.b0 = w_down;
+  ga.row_weight = row_weight;
+  ga.out0 = o_perm;
+  return from_hip(moe::launch_gemm(moe::GEMM_DOWN, s, ga, stream));
+}
+
+moe_status moe_forward_fused(moe_shape s, const void* x, const void* w_router, const float* logit_bias,
+                             const void* w_gate, const void* w_up, const void* w_down, float* logits,
+                             int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted_to_flat, int32_t* flat_to_sorted, int32_t* row_token, float* row_weight,
+                             void* a, void* o_perm, void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(x, w_router, w_gate, w_up, w_down, logits, topk_idx, topk_w, counts, offsets, sorted_to_flat,
+               flat_to_sorted, row_token, row_weight, a, o_perm, y, ws))
+    return MOE_EINVAL;
+  if (ws_bytes < moe::ws_layout(s).total) return MOE_EWORKSPACE;
+  if ((st = moe_route(s, x, w_router, logit_bias, logits, topk_idx, topk_w, stream)) != MOE_OK) return st;
+  if ((st = moe_permute_fused(s, topk_idx, topk_w, counts, offsets, sorted_to_flat, flat_to_sorted, row_token,
+                              row_weight, ws, ws_bytes, stream)) != MOE_OK)
+    return st;
+  if ((st = moe_gemm_gate_up_gathered(s, x, row_token, offsets, w_gate, w_up, nullptr, nullptr, a, stream)) != MOE_OK)
+    return st;
+  if ((st = moe_gemm_down_weighted(s, a, offsets, w_down, row_weight, o_perm, stream)) != MOE_OK) return st;
+  return moe_unpermute_sum(s, o_perm, flat_to_sorted, y, stream);
+}
+
 moe_status moe_combine(moe_shape s, const void* o_perm, const float* topk_w, const int32_t* flat_to_sorted,
                        void* y, hipStream_t stream) {
   moe_status st = check_shape(s);

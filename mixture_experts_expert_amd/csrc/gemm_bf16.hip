@@ -86,7 +86,7 @@ constexpr bool grouped_k(int m) { return m >= WGRAD_DOWN; }
 constexpr bool b_kcontig(int m) { return m == GATEUP || m == DOWN; }
 
 struct Params {
-  int H, E, I;
+  int T, H, E, I;
   const int32_t* offsets;
   const bf16_t* a;     // x_perm | act | do_perm | dgu | do_perm | dgu
   const bf16_t* b0;    // w_gate | w_down | w_down | w_gate | act | x_perm
@@ -100,6 +100,11 @@ struct Params {
   float* dw1;          // dw_up
   int accumulate;
   float* part;         // weight gradients: split-K partial tiles [tile][256][256]
+  // Fused inference forward (both optional): GATEUP reads row p of A as row
+  // row_token[p] of x [T][H] (no x_perm); DOWN scales output row p by
+  // row_weight[p] before rounding. GATEUP with out0 == nullptr stores A only.
+  const int32_t* row_token;
+  const float* row_weight;
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -520,7 +525,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       if constexpr (A_KMAJOR) {
         const int r = blk * 16 + (lane >> 2);
         const int c = (lane & 3) ^ swk(r);
-        aoff[t] = 2u * (r * lda + c * 8);  // rows >= mvalid: outside the range, read as zeros
+        if (MODE == GATEUP && P.row_token != nullptr)  // row of x; rows >= mvalid read zeros
+          aoff[t] = r < mvalid ? 2u * (static_cast<uint32_t>(P.row_token[row0 + r]) * H + c * 8) : kNoWrite;
+        else
+          aoff[t] = 2u * (r * lda + c * 8);  // rows >= mvalid: outside the range, read as zeros
       } else {
         const int k = blk * 2 + (lane >> 5);
         const int c = (lane & 31) ^ swt(k);
@@ -564,6 +572,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   auto rsrc_a = [&](int s) -> rsrc_t {
     const int k0 = s * BK;
     if constexpr (A_KMAJOR) {
+      if (MODE == GATEUP && P.row_token != nullptr) return make_rsrc(P.a + k0, s < ksteps ? 2 * (P.T * H - k0) : 0);
       return make_rsrc(abase_m + k0, s < ksteps ? 2 * (mvalid * lda - k0) : 0);
     } else {
       const int left = kend - kbeg - k0;
@@ -754,8 +763,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       // one lane.
       const int64_t base = static_cast<int64_t>(trow0) * I;
       const int bytes = 2 * tmvalid * I;
-      const rsrc_t rg = make_rsrc(P.out0 + base, bytes);
-      const rsrc_t ru = make_rsrc(P.out1 + base, bytes);
+      const bool store_gu = P.out0 != nullptr;  // the fused forward keeps A only
+      const rsrc_t rg = make_rsrc(store_gu ? P.out0 + base : P.out2, store_gu ? bytes : 0);
+      const rsrc_t ru = make_rsrc(store_gu ? P.out1 + base : P.out2, store_gu ? bytes : 0);
       const rsrc_t rs = make_rsrc(P.out2 + base, bytes);
       // 16-byte stores (pair_cols8): lane l writes row 8b + 4(l/32) + l%4 of
       // the row block, intermediate indices 32*((l/4)%2) + 8*((l%32)/8) .. + 7
@@ -783,8 +793,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
             up[j] = quad_transpose_bf16(u, lane);
             ap[j] = quad_transpose_bf16(a, lane);
           }
-          store_b128(pair_cols8(gp[0], gp[1], lane), rg, off);
-          store_b128(pair_cols8(up[0], up[1], lane), ru, off);
+          if (store_gu) {
+            store_b128(pair_cols8(gp[0], gp[1], lane), rg, off);
+            store_b128(pair_cols8(up[0], up[1], lane), ru, off);
+          }
           store_b128(pair_cols8(ap[0], ap[1], lane), rs, off);
         }
     } else if constexpr (MODE == DOWN || MODE == DGRAD_GATEUP) {
@@ -793,6 +805,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       const rsrc_t ro = make_rsrc(P.out0 + static_cast<int64_t>(trow0) * H, 2 * tmvalid * H);
       const int hrow = 4 * (lane >> 5) + prow;
       const int ncol8 = ((lane >> 2) & 1) * 32 + ((lane & 31) >> 3) * 8;
+      // Fused forward (DOWN with row_weight): the weights of this lane's 16
+      // rows, read once before the stores.
+      const bool weighted = MODE == DOWN && P.row_weight != nullptr;
+      float rw[FM][4];
+      if (weighted) {
+        const rsrc_t rr = make_rsrc(P.row_weight + trow0, 4 * tmvalid);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            rw[i][b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rr, 4u * static_cast<uint32_t>(wm * WTM + i * 32 + 8 * b + hrow), 0, 0));
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -809,7 +834,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
               float v[4];
 #pragma unroll
               for (int q = 0; q < 4; ++q) v[q] = acc[i][2 * jp + j][4 * b + q];
-              t[j] = quad_transpose_bf16(v, lane);
+              if (weighted) {  // routing weight of this lane's row, applied in fp32 before rounding
+                quad_transpose(v, lane);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] *= rw[i][b];
+                t[j] = pack_bf16x4v(v);
+              } else {
+                t[j] = quad_transpose_bf16(v, lane);
+              }
             }
             store_b128(pair_cols8(t[0], t[1], lane), ro, off);
           }
@@ -1117,6 +1149,7 @@ int64_t wgrad_part_tiles(const moe_shape& s) {
 
 hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g, hipStream_t st) {
   Params p{};
+  p.T = s.T;
   p.H = s.H;
   p.E = s.E;
   p.I = s.I;
@@ -1133,6 +1166,8 @@ hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g
   p.dw1 = g.dw1;
   p.accumulate = g.accumulate;
   p.part = g.part;
+  p.row_token = g.row_token;
+  p.row_weight = g.row_weight;
   switch (mode) {
     case GEMM_GATEUP: return run<GATEUP>(p, st);
     case GEMM_DOWN: return run<DOWN>(p, st);

@@ -21,15 +21,19 @@ __device__ __forceinline__ int expert_of_row(int p, const int32_t* __restrict__ 
   return lo;
 }
 
+// row_token (fused forward): row p of the input is row row_token[p] of x;
+// g and u may then be null (A only).
 __global__ __launch_bounds__(kThreads) void gateup_f32(int rows, int H, int E, int I, const int32_t* offsets,
-                                                       const float* __restrict__ xp, const float* __restrict__ wg,
-                                                       const float* __restrict__ wu, float* __restrict__ g,
-                                                       float* __restrict__ u, float* __restrict__ a) {
+                                                       const float* __restrict__ xp,
+                                                       const int32_t* __restrict__ row_token,
+                                                       const float* __restrict__ wg, const float* __restrict__ wu,
+                                                       float* __restrict__ g, float* __restrict__ u,
+                                                       float* __restrict__ a) {
   const int64_t q = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (q >= static_cast<int64_t>(rows) * I) return;
   const int p = static_cast<int>(q / I), i = static_cast<int>(q % I);
   const int e = expert_of_row(p, offsets, E);
-  const float* x = xp + static_cast<int64_t>(p) * H;
+  const float* x = xp + static_cast<int64_t>(row_token ? row_token[p] : p) * H;
   const float* rg = wg + (static_cast<int64_t>(e) * I + i) * H;
   const float* ru = wu + (static_cast<int64_t>(e) * I + i) * H;
   float sg = 0.0f, su = 0.0f;
@@ -37,14 +41,15 @@ __global__ __launch_bounds__(kThreads) void gateup_f32(int rows, int H, int E, i
     sg += x[h] * rg[h];
     su += x[h] * ru[h];
   }
-  g[q] = sg;
-  u[q] = su;
+  if (g) g[q] = sg;
+  if (u) u[q] = su;
   a[q] = sg * sigmoidf_dev(sg) * su;
 }
 
+// row_weight (fused forward): output row p scaled by row_weight[p].
 __global__ __launch_bounds__(kThreads) void down_f32(int rows, int H, int E, int I, const int32_t* offsets,
                                                      const float* __restrict__ act, const float* __restrict__ wd,
-                                                     float* __restrict__ o) {
+                                                     const float* __restrict__ row_weight, float* __restrict__ o) {
   const int64_t q = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (q >= static_cast<int64_t>(rows) * H) return;
   const int p = static_cast<int>(q / H), h = static_cast<int>(q % H);
@@ -53,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void down_f32(int rows, int H, int E, int
   const float* r = wd + (static_cast<int64_t>(e) * H + h) * I;
   float s = 0.0f;
   for (int i = 0; i < I; ++i) s += av[i] * r[i];
-  o[q] = s;
+  o[q] = row_weight ? s * row_weight[p] : s;
 }
 
 // dA = dO W_down[e]; dU = dA silu(g); dG = dA u s (1 + g (1 - s)) -> dgu = [dG | dU]
@@ -141,12 +146,12 @@ hipError_t launch_gemm_f32(GemmMode mode, const moe_shape& s, const GemmArgs& g,
   switch (mode) {
     case GEMM_GATEUP:
       gateup_f32<<<blocks_for(static_cast<int64_t>(rows) * s.I), kThreads, 0, st>>>(
-          rows, s.H, s.E, s.I, g.offsets, A, B0, B1, static_cast<float*>(g.out0), static_cast<float*>(g.out1),
-          static_cast<float*>(g.out2));
+          rows, s.H, s.E, s.I, g.offsets, A, g.row_token, B0, B1, static_cast<float*>(g.out0),
+          static_cast<float*>(g.out1), static_cast<float*>(g.out2));
       break;
     case GEMM_DOWN:
       down_f32<<<blocks_for(static_cast<int64_t>(rows) * s.H), kThreads, 0, st>>>(
-          rows, s.H, s.E, s.I, g.offsets, A, B0, static_cast<float*>(g.out0));
+          rows, s.H, s.E, s.I, g.offsets, A, B0, g.row_weight, static_cast<float*>(g.out0));
       break;
     case GEMM_DGRAD_DOWN:
       dgrad_down_f32<<<blocks_for(static_cast<int64_t>(rows) * s.I), kThreads, 0, st>>>(

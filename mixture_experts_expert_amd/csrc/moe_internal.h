@@ -93,6 +93,9 @@ hipError_t launch_combine(const moe_shape& s, const void* o_perm, const float* w
                           hipStream_t st);
 hipError_t launch_combine_bwd(const moe_shape& s, const void* dy, const void* o_perm, const float* w,
                               const int32_t* f2s, void* do_perm, float* gw, hipStream_t st);
+hipError_t launch_permute_fused(const moe_shape& s, const int32_t* idx, const float* w, int32_t* counts,
+                                int32_t* offsets, int32_t* s2f, int32_t* f2s, int32_t* row_token, float* row_weight,
+                                void* ws, hipStream_t st);
 hipError_t launch_unpermute_sum(const moe_shape& s, const void* dx_perm, const int32_t* f2s, void* dx,
                                 hipStream_t st);
 
@@ -128,6 +131,8 @@ struct GemmArgs {
   float* dw0;
   float* dw1;
   int accumulate;
+  const int32_t* row_token;  // fused forward, GATEUP: row p of A is row row_token[p] of x [T][H]
+  const float* row_weight;   // fused forward, DOWN: output row p scaled by row_weight[p]
 };
 
 hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& a, hipStream_t st);

@@ -83,12 +83,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int nb, int E, int32
 
 constexpr int kWavesPerBlock = kThreads / kWave;
 
+// The fused inference forward also takes, per sorted row p, its token
+// row_token[p] = s2f[p] / k and its routing weight row_weight[p] = w[s2f[p]]
+// (both null otherwise).
 __global__ __launch_bounds__(kThreads) void rank_scatter_kernel(int n, int E, int nbits,
                                                                 const int32_t* __restrict__ idx,
                                                                 const int32_t* __restrict__ hist_base,
                                                                 const int32_t* __restrict__ offsets,
                                                                 int32_t* __restrict__ s2f,
-                                                                int32_t* __restrict__ f2s) {
+                                                                int32_t* __restrict__ f2s, int k,
+                                                                const float* __restrict__ w,
+                                                                int32_t* __restrict__ row_token,
+                                                                float* __restrict__ row_weight) {
   __shared__ int32_t running[1024];
   __shared__ int32_t wcount[kWavesPerBlock][1024];
   const int tid = threadIdx.x;
@@ -120,6 +126,10 @@ __global__ __launch_bounds__(kThreads) void rank_scatter_kernel(int n, int E, in
       for (int w = 0; w < wv; ++w) pos += wcount[w][e];
       s2f[pos] = static_cast<int32_t>(f);
       f2s[f] = pos;
+      if (row_token) {
+        row_token[pos] = static_cast<int32_t>(f / k);
+        row_weight[pos] = w[f];
+      }
     }
     __syncthreads();
     for (int ee = tid; ee < E; ee += kThreads) {
@@ -164,9 +174,12 @@ WsLayout ws_layout(const moe_shape& s) {
   return l;
 }
 
-hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const void* x, int32_t* counts,
-                          int32_t* offsets, int32_t* s2f, int32_t* f2s, void* x_perm, void* ws,
-                          hipStream_t st) {
+namespace {
+
+// The stable counting sort shared by both permute entry points.
+hipError_t launch_sort(const moe_shape& s, const int32_t* idx, int32_t* counts, int32_t* offsets, int32_t* s2f,
+                       int32_t* f2s, const float* w, int32_t* row_token, float* row_weight, void* ws,
+                       hipStream_t st) {
   const int n = s.T * s.k;
   const int nb = ceil_div(n, kPermBlock);
   int32_t* hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ws_layout(s).hist_off);
@@ -177,14 +190,31 @@ hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const void* x,
   if (err != hipSuccess) return err;
   scan_kernel<<<1, kScanThreads, 0, st>>>(nb, s.E, hist, counts, offsets);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  rank_scatter_kernel<<<nb, kThreads, 0, st>>>(n, s.E, nbits, idx, hist, offsets, s2f, f2s);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  rank_scatter_kernel<<<nb, kThreads, 0, st>>>(n, s.E, nbits, idx, hist, offsets, s2f, f2s, s.k, w, row_token,
+                                                row_weight);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const void* x, int32_t* counts,
+                          int32_t* offsets, int32_t* s2f, int32_t* f2s, void* x_perm, void* ws,
+                          hipStream_t st) {
+  hipError_t err = launch_sort(s, idx, counts, offsets, s2f, f2s, nullptr, nullptr, nullptr, ws, st);
+  if (err != hipSuccess) return err;
+  const int n = s.T * s.k;
   const int esz = s.dtype == MOE_BF16 ? 2 : 4;
   const int chunks = s.H * esz / 16;
   gather_kernel<<<ceil_div(n, kWavesPerBlock), kThreads, 0, st>>>(n, s.k, chunks, s2f,
                                                                   static_cast<const uint4*>(x),
                                                                   static_cast<uint4*>(x_perm));
   return hipGetLastError();
+}
+
+hipError_t launch_permute_fused(const moe_shape& s, const int32_t* idx, const float* w, int32_t* counts,
+                                int32_t* offsets, int32_t* s2f, int32_t* f2s, int32_t* row_token, float* row_weight,
+                                void* ws, hipStream_t st) {
+  return launch_sort(s, idx, counts, offsets, s2f, f2s, w, row_token, row_weight, ws, st);
 }
 
 }  // namespace moe

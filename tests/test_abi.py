@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(B):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(B.lib, n), n
 
@@ -86,6 +86,25 @@ def test_workspace_too_small(B):
     G = [FAKE] * 13
     assert B.lib.moe_grouped_gemm_bwd(s, *G, 0, FAKE, need - 1, None) == 3
     assert B.lib.moe_grouped_gemm_bwd(s, *G, 2, FAKE, need, None) == 1  # accumulate_dw not 0/1
+
+
+def test_fused_forward_validation(B):
+    s = B.shape(64, 128, 8, 2, 64, "bf16")
+    need = B.moe_workspace_bytes(s)
+    F = FAKE
+    # gathered gate/up: g and u both set or both null; row_token required
+    assert B.lib.moe_gemm_gate_up_gathered(s, F, F, F, F, F, F, None, F, None) == 1
+    assert B.lib.moe_gemm_gate_up_gathered(s, F, None, F, F, F, None, None, F, None) == 1
+    # x addressed with 32-bit byte offsets: T*H*2 >= 2^31 is not supported
+    big = B.shape(1 << 20, 1024, 8, 2, 64, "bf16")
+    assert B.lib.moe_gemm_gate_up_gathered(big, F, F, F, F, F, None, None, F, None) == 2
+    assert B.lib.moe_gemm_down_weighted(s, F, F, F, None, F, None) == 1
+    P = [F] * 8
+    assert B.lib.moe_permute_fused(s, *P, F, need - 1, None) == 3
+    assert B.lib.moe_permute_fused(s, F, None, *P[:6], F, need, None) == 1
+    A = [F] * 19
+    assert B.lib.moe_forward_fused(s, *A, need - 1, None) == 3
+    assert B.lib.moe_forward_fused(s, F, F, None, F, F, F, F, F, F, F, F, F, F, F, None, F, F, F, F, need, None) == 1
 
 
 def test_binding_raises_on_error(B):
