@@ -228,6 +228,37 @@ def main() -> int:
                 for i, n in enumerate(names)}
     log(f"timed {args.steps} steps: {ms:.3f} ms/step; " + ", ".join(f"{n}={v:.3f}" for n, v in per_call.items()))
 
+    # Inference forward at the same shape (outside the timed training steps):
+    # the unfused chain (route, permute with the gather, the two GEMMs, the
+    # weighted combine) against the fused path (no x_perm, routing weights in
+    # the down GEMM's epilogue, plain per-token sum).
+    fb = dict(row_token=torch.empty(cfg.M, dtype=torch.int32, device="cuda"),
+              row_weight=torch.empty(cfg.M, device="cuda"))
+
+    def infer_unfused():
+        for c in calls[:5]:
+            c()
+
+    def infer_fused():
+        B.moe_forward_fused(s, x, wr, bias, wg, wu, wd, b["logits"], b["topk_idx"], b["topk_w"], b["counts"],
+                            b["offsets"], b["sorted_to_flat"], b["flat_to_sorted"], fb["row_token"],
+                            fb["row_weight"], b["a"], b["o_perm"], b["y"], st.ws)
+
+    def time_fn(fn, reps=10):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    infer = {"unfused": round(time_fn(infer_unfused), 4), "fused": round(time_fn(infer_fused), 4)}
+    log(f"inference forward: unfused {infer['unfused']:.3f} ms, fused {infer['fused']:.3f} ms")
+
     flops = gemm_flops(cfg)
     nbytes = alg_bytes(cfg)
     step_flops = sum(flops.values())
@@ -272,6 +303,7 @@ def main() -> int:
         "call_ms": {n: round(v, 4) for n, v in per_call.items()},
         "hbm_frac": hbm_frac,
         "roofline": roof,
+        "inference_forward_ms": infer,
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")

@@ -320,7 +320,10 @@ __device__ __forceinline__ int split_cap(int work, int grid) {
 __device__ __forceinline__ int split_chunks(int steps, int cap) { return steps > cap ? (steps + cap - 1) / cap : 1; }
 __device__ __forceinline__ int split_len(int steps, int chunks) { return (steps + chunks - 1) / chunks; }
 
-template <int MODE>
+// FUSED (the inference forward, compiled separately so that the training
+// kernels carry none of it): GATEUP reads its A rows through P.row_token and
+// may skip storing G and U; DOWN scales its output rows by P.row_weight.
+template <int MODE, bool FUSED>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(
     Params P) {
   // The stages as separate objects: with the stage of every access known at
@@ -525,7 +528,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       if constexpr (A_KMAJOR) {
         const int r = blk * 16 + (lane >> 2);
         const int c = (lane & 3) ^ swk(r);
-        if (MODE == GATEUP && P.row_token != nullptr)  // row of x; rows >= mvalid read zeros
+        if (MODE == GATEUP && FUSED)  // row of x; rows >= mvalid read zeros
           aoff[t] = r < mvalid ? 2u * (static_cast<uint32_t>(P.row_token[row0 + r]) * H + c * 8) : kNoWrite;
         else
           aoff[t] = 2u * (r * lda + c * 8);  // rows >= mvalid: outside the range, read as zeros
@@ -572,7 +575,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   auto rsrc_a = [&](int s) -> rsrc_t {
     const int k0 = s * BK;
     if constexpr (A_KMAJOR) {
-      if (MODE == GATEUP && P.row_token != nullptr) return make_rsrc(P.a + k0, s < ksteps ? 2 * (P.T * H - k0) : 0);
+      if (MODE == GATEUP && FUSED) return make_rsrc(P.a + k0, s < ksteps ? 2 * (P.T * H - k0) : 0);
       return make_rsrc(abase_m + k0, s < ksteps ? 2 * (mvalid * lda - k0) : 0);
     } else {
       const int left = kend - kbeg - k0;
@@ -763,7 +766,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       // one lane.
       const int64_t base = static_cast<int64_t>(trow0) * I;
       const int bytes = 2 * tmvalid * I;
-      const bool store_gu = P.out0 != nullptr;  // the fused forward keeps A only
+      const bool store_gu = !FUSED || P.out0 != nullptr;  // the fused forward may keep A only
       const rsrc_t rg = make_rsrc(store_gu ? P.out0 + base : P.out2, store_gu ? bytes : 0);
       const rsrc_t ru = make_rsrc(store_gu ? P.out1 + base : P.out2, store_gu ? bytes : 0);
       const rsrc_t rs = make_rsrc(P.out2 + base, bytes);
@@ -807,9 +810,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       const int ncol8 = ((lane >> 2) & 1) * 32 + ((lane & 31) >> 3) * 8;
       // Fused forward (DOWN with row_weight): the weights of this lane's 16
       // rows, read once before the stores.
-      const bool weighted = MODE == DOWN && P.row_weight != nullptr;
+      constexpr bool weighted = MODE == DOWN && FUSED;
       float rw[FM][4];
-      if (weighted) {
+      if constexpr (weighted) {
         const rsrc_t rr = make_rsrc(P.row_weight + trow0, 4 * tmvalid);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -834,7 +837,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
               float v[4];
 #pragma unroll
               for (int q = 0; q < 4; ++q) v[q] = acc[i][2 * jp + j][4 * b + q];
-              if (weighted) {  // routing weight of this lane's row, applied in fp32 before rounding
+              if constexpr (weighted) {  // routing weight of this lane's row, applied in fp32 before rounding
                 quad_transpose(v, lane);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) v[q] *= rw[i][b];
@@ -1122,10 +1125,10 @@ int persistent_grid() {
   return cached;
 }
 
-template <int MODE>
+template <int MODE, bool FUSED = false>
 hipError_t run(const Params& p, hipStream_t st) {
   const int grid = persistent_grid();
-  grouped_gemm_kernel<MODE><<<grid, NT, 0, st>>>(p);
+  grouped_gemm_kernel<MODE, FUSED><<<grid, NT, 0, st>>>(p);
   hipError_t err = hipGetLastError();
   if constexpr (grouped_k(MODE)) {
     if (err != hipSuccess) return err;
@@ -1169,8 +1172,8 @@ hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g
   p.row_token = g.row_token;
   p.row_weight = g.row_weight;
   switch (mode) {
-    case GEMM_GATEUP: return run<GATEUP>(p, st);
-    case GEMM_DOWN: return run<DOWN>(p, st);
+    case GEMM_GATEUP: return g.row_token ? run<GATEUP, true>(p, st) : run<GATEUP>(p, st);
+    case GEMM_DOWN: return g.row_weight ? run<DOWN, true>(p, st) : run<DOWN>(p, st);
     case GEMM_DGRAD_DOWN: return run<DGRAD_DOWN>(p, st);
     case GEMM_DGRAD_GATEUP: return run<DGRAD_GATEUP>(p, st);
     case GEMM_WGRAD_DOWN: return run<WGRAD_DOWN>(p, st);
