@@ -14,7 +14,12 @@ the expert GEMMs (18*T*k*H*I per step). `roofline` covers the dominant kernel
 (the call with the largest average time): its algorithmic flops or bytes per
 launch (whichever of the MFMA and HBM minimum times is larger decides the
 bound) over its average launch time, measured with HIP events around that
-call on the stream it runs on. `traffic` is the HBM bytes per launch that
+call on the stream it runs on. The backward runs its weight-gradient GEMMs on
+a second stream, concurrently with the data-gradient GEMMs, so a call's time
+in the timed region includes waiting for CUs the other stream holds;
+`roofline_sequential`, `call_ms_sequential`, `gemm_tflops` and `hbm_frac`
+come from a pass after the timed region that runs the same calls one at a
+time on one stream (each kernel's own duration). `traffic` is the HBM bytes per launch that
 rocprofv3's FETCH_SIZE and WRITE_SIZE counters gave for that kernel, scaled by
 what they read for a plain device copy of known size (--calibrate-copy); it is
 taken from the committed summary under profiles/ and reported only while the
@@ -178,10 +183,15 @@ def main() -> int:
     st = B.MoEStage(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, torch.bfloat16)
     st._alloc_bwd()
     b, s = st.buf, st.s
-    lw = B.moe_workspace_bytes(s)
-    dgu = st.ws[lw - cfg.M * 2 * cfg.I * 2:].view(torch.bfloat16).view(cfg.M, 2 * cfg.I)
+    dgu = torch.empty(cfg.M, 2 * cfg.I, dtype=torch.bfloat16, device="cuda")  # [dG | dU]
     x, wr, wg, wu, wd, dy = (dev[n] for n in ["x", "w_router", "w_gate", "w_up", "w_down", "dy"])
     stream = torch.cuda.current_stream()
+    # The backward's weight-gradient GEMMs run on a second stream (default
+    # priority) while the data-gradient GEMMs run on the main one; each fills
+    # the other's tail. Dependencies: both down GEMMs need do_perm (combine
+    # backward), the gate/up ones need dG|dU (down dgrad); the step ends when
+    # both streams are done.
+    aux = torch.cuda.Stream()
     names = ["moe_route", "moe_permute", "moe_gemm_gate_up", "moe_gemm_down", "moe_combine", "moe_combine_bwd",
              "moe_gemm_down_dgrad", "moe_gemm_down_wgrad", "moe_gemm_gate_up_dgrad", "moe_gemm_gate_up_wgrad",
              "moe_unpermute_sum", "moe_route_bwd"]
@@ -201,15 +211,36 @@ def main() -> int:
         lambda: B.moe_unpermute_sum(s, b["dx_perm"], b["flat_to_sorted"], b["dx"]),
         lambda: B.moe_route_bwd(s, b["d_topk_w"], b["topk_w"], b["topk_idx"], b["d_logits"]),
     ]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    on_aux = {"moe_gemm_down_wgrad", "moe_gemm_gate_up_wgrad"}
+    # Program order of the step: down wgrad is enqueued before down dgrad so
+    # that it starts first on its stream; gate/up wgrad waits for dG|dU.
+    order = ["moe_route", "moe_permute", "moe_gemm_gate_up", "moe_gemm_down", "moe_combine", "moe_combine_bwd",
+             "moe_gemm_down_wgrad", "moe_gemm_down_dgrad", "moe_gemm_gate_up_wgrad", "moe_gemm_gate_up_dgrad",
+             "moe_unpermute_sum", "moe_route_bwd"]
+    by_name = dict(zip(names, calls))
+    ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+          for _ in range(args.steps)]
 
     def step(events=None):
-        for i, c in enumerate(calls):
+        for n in order:
+            if n == "moe_gemm_down_wgrad":  # fork after the combine backward
+                e = torch.cuda.Event()
+                e.record(stream)
+                aux.wait_event(e)
+            if n == "moe_gemm_gate_up_wgrad":  # dG | dU written by the down dgrad
+                e = torch.cuda.Event()
+                e.record(stream)
+                aux.wait_event(e)
+            strm = aux if n in on_aux else stream
             if events is not None:
-                events[i].record(stream)
-            c()
-        if events is not None:
-            events[-1].record(stream)
+                events[n][0].record(strm)
+            with torch.cuda.stream(strm):
+                by_name[n]()
+            if events is not None:
+                events[n][1].record(strm)
+        e = torch.cuda.Event()  # join
+        e.record(aux)
+        stream.wait_event(e)
 
     for _ in range(args.warmup):
         step()
@@ -224,8 +255,8 @@ def main() -> int:
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps
-    per_call = {n: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)) / args.steps
-                for i, n in enumerate(names)}
+    per_call = {n: sum(ev[k][n][0].elapsed_time(ev[k][n][1]) for k in range(args.steps)) / args.steps
+                for n in names}
     log(f"timed {args.steps} steps: {ms:.3f} ms/step; " + ", ".join(f"{n}={v:.3f}" for n, v in per_call.items()))
 
     # Inference forward at the same shape (outside the timed training steps):
@@ -263,25 +294,47 @@ def main() -> int:
     nbytes = alg_bytes(cfg)
     step_flops = sum(flops.values())
     tflops = step_flops / (ms * 1e-3) / 1e12
-    gemm_tflops = {n: round(flops[n] / (per_call[n] * 1e-3) / 1e12, 1) for n in flops}
+
+    def roofline(times):
+        dominant = max(names, key=lambda n: times[n])
+        t_mfma = flops.get(dominant, 0.0) / (PEAK_BF16_TFLOPS * 1e12)
+        t_hbm = nbytes[dominant] / (PEAK_HBM_GBS * 1e9)
+        secs = times[dominant] * 1e-3
+        if t_mfma >= t_hbm:
+            roof = {"kernel": dominant, "bound": "mfma", "achieved": round(flops[dominant] / secs / 1e12, 1),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+        else:
+            roof = {"kernel": dominant, "bound": "hbm", "achieved": round(nbytes[dominant] / secs / 1e9, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+        roof["traffic"] = profiled_traffic(dominant, cfg.name)
+        roof["alg_bytes"] = nbytes[dominant]
+        if dominant in flops:
+            roof["mfma_frac"] = round(flops[dominant] / secs / 1e12 / PEAK_BF16_TFLOPS, 4)
+        return roof
+
+    # Over the timed (two-stream) region: a call's time there includes any
+    # wait for CUs held by the concurrent stream.
+    roof = roofline(per_call)
+    roof["timing"] = "timed region, HIP events on the call's stream"
+    # The same calls one at a time on one stream: each kernel's own duration.
+    seq_ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+              for _ in range(5)]
+    torch.cuda.synchronize()
+    for k in range(len(seq_ev)):
+        for n in order:
+            seq_ev[k][n][0].record(stream)
+            by_name[n]()
+            seq_ev[k][n][1].record(stream)
+    torch.cuda.synchronize()
+    per_call_seq = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in seq_ev) / len(seq_ev) for n in names}
+    roof_seq = roofline(per_call_seq)
+    roof_seq["timing"] = "one call at a time on one stream, after the timed region"
+    # Per-kernel rates from the one-call-at-a-time pass (their own durations).
+    gemm_tflops = {n: round(flops[n] / (per_call_seq[n] * 1e-3) / 1e12, 1) for n in flops}
     # HBM fraction of the calls without matrix work (algorithmic bytes).
-    hbm_frac = {n: round(nbytes[n] / (per_call[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)
+    hbm_frac = {n: round(nbytes[n] / (per_call_seq[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)
                 for n in names if n not in flops}
-    dominant = max(names, key=lambda n: per_call[n])
-    t_mfma = flops.get(dominant, 0.0) / (PEAK_BF16_TFLOPS * 1e12)
-    t_hbm = nbytes[dominant] / (PEAK_HBM_GBS * 1e9)
-    secs = per_call[dominant] * 1e-3
-    if t_mfma >= t_hbm:
-        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(flops[dominant] / secs / 1e12, 1),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"kernel": dominant, "bound": "hbm", "achieved": round(nbytes[dominant] / secs / 1e9, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = profiled_traffic(dominant, cfg.name)
-    roof["alg_bytes"] = nbytes[dominant]
-    if dominant in flops:
-        roof["mfma_frac"] = round(flops[dominant] / secs / 1e12 / PEAK_BF16_TFLOPS, 4)
     out = {
         "metric": METRIC,
         "value": round(cfg.T / (ms * 1e-3), 1),
@@ -301,8 +354,10 @@ def main() -> int:
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "gemm_tflops": gemm_tflops,
         "call_ms": {n: round(v, 4) for n, v in per_call.items()},
+        "call_ms_sequential": {n: round(v, 4) for n, v in per_call_seq.items()},
         "hbm_frac": hbm_frac,
         "roofline": roof,
+        "roofline_sequential": roof_seq,
         "inference_forward_ms": infer,
     }
     if not args.no_cpu_baseline:

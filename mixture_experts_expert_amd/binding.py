@@ -271,14 +271,38 @@ class MoEStage:
         moe_combine(s, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["y"], stream)
         return b["y"]
 
-    def backward(self, dy, accumulate_dw: bool = False, stream=None):
+    def backward(self, dy, accumulate_dw: bool = False, stream=None, aux_stream=None):
+        """Backward of the last forward. With ``aux_stream`` (a second stream,
+        default priority) the weight-gradient GEMMs run there while the
+        data-gradient GEMMs run on ``stream``: each fills the other's tail.
+        The results are the same bits either way."""
         self._alloc_bwd()
         b, s = self.buf, self.s
         w_gate, w_up, w_down = self.w
         moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["do_perm"], b["d_topk_w"], stream)
-        moe_grouped_gemm_bwd(s, b["do_perm"], b["x_perm"], b["g"], b["u"], b["a"], b["offsets"], w_gate, w_up,
-                             w_down, b["dx_perm"], b["dw_gate"], b["dw_up"], b["dw_down"], int(accumulate_dw),
-                             self.ws, stream=stream)
+        if aux_stream is None:
+            moe_grouped_gemm_bwd(s, b["do_perm"], b["x_perm"], b["g"], b["u"], b["a"], b["offsets"], w_gate, w_up,
+                                 w_down, b["dx_perm"], b["dw_gate"], b["dw_up"], b["dw_down"], int(accumulate_dw),
+                                 self.ws, stream=stream)
+        else:
+            main = torch.cuda.current_stream() if stream is None else stream
+            if "dgu" not in b:
+                b["dgu"] = torch.empty(self.T * self.k, 2 * self.I, dtype=self.dtype, device=self.ws.device)
+            acc = int(accumulate_dw)
+            forked = torch.cuda.Event()
+            forked.record(main)
+            aux_stream.wait_event(forked)
+            moe_gemm_down_wgrad(s, b["do_perm"], b["a"], b["offsets"], b["dw_down"], acc, self.ws, stream=aux_stream)
+            moe_gemm_down_dgrad(s, b["do_perm"], b["offsets"], w_down, b["g"], b["u"], b["dgu"], main)
+            dgu_ready = torch.cuda.Event()
+            dgu_ready.record(main)
+            aux_stream.wait_event(dgu_ready)
+            moe_gemm_gate_up_wgrad(s, b["dgu"], b["x_perm"], b["offsets"], b["dw_gate"], b["dw_up"], acc, self.ws,
+                                   stream=aux_stream)
+            moe_gemm_gate_up_dgrad(s, b["dgu"], b["offsets"], w_gate, w_up, b["dx_perm"], main)
+            joined = torch.cuda.Event()
+            joined.record(aux_stream)
+            main.wait_event(joined)
         moe_unpermute_sum(s, b["dx_perm"], b["flat_to_sorted"], b["dx"], stream)
         moe_route_bwd(s, b["d_topk_w"], b["topk_w"], b["topk_idx"], b["d_logits"], stream)
         return b["dx"]
