@@ -1,30 +1,34 @@
 """Throughput of one MoE layer's expert stage (forward + backward) on one GPU.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--timed-only]
 
 One step is the whole stage on one batch of synthetic input already resident
-in HBM: route -> expert indexing + gather -> gate/up GEMM (SwiGLU epilogue)
--> down GEMM -> combine, then combine backward -> down dgrad (SwiGLU backward
-epilogue) -> down wgrad -> gate/up dgrad -> gate/up wgrad -> unpermute-sum ->
-router backward, every step a call of the C ABI (the six GEMMs through their
-one-kernel entry points, which is what moe_grouped_gemm_fwd/bwd chain).
+in HBM, on one stream: route -> expert indexing + gather -> gate/up GEMM
+(SwiGLU epilogue) -> down GEMM -> combine, then combine backward -> down
+dgrad (SwiGLU backward epilogue) -> down wgrad -> gate/up dgrad -> gate/up
+wgrad -> unpermute-sum -> router backward, every step a call of the C ABI
+(the six GEMMs through their one-kernel entry points, which is what
+moe_grouped_gemm_fwd/bwd chain).
 
 Prints one JSON line. `value` is tokens/s of the whole stage; TFLOP/s counts
-the expert GEMMs (18*T*k*H*I per step). `roofline` covers the dominant kernel
-(the call with the largest average time): its algorithmic flops or bytes per
-launch (whichever of the MFMA and HBM minimum times is larger decides the
-bound) over its average launch time, measured with HIP events around that
-call on the stream it runs on. The backward runs its weight-gradient GEMMs on
-a second stream, concurrently with the data-gradient GEMMs, so a call's time
-in the timed region includes waiting for CUs the other stream holds;
-`roofline_sequential`, `call_ms_sequential`, `gemm_tflops` and `hbm_frac`
-come from a pass after the timed region that runs the same calls one at a
-time on one stream (each kernel's own duration). `traffic` is the HBM bytes per launch that
+the expert GEMMs (18*T*k*H*I per step). Around every call the timed steps
+also record HIP events on the stream, which give `call_ms`, `gemm_tflops`,
+`hbm_frac` and `roofline`. `roofline` covers the dominant kernel (the call
+with the largest average time): its algorithmic flops or bytes per launch
+(whichever of the MFMA and HBM minimum times is larger decides the bound)
+over its average launch time. `traffic` is the HBM bytes per launch that
 rocprofv3's FETCH_SIZE and WRITE_SIZE counters gave for that kernel, scaled by
 what they read for a plain device copy of known size (--calibrate-copy); it is
 taken from the committed summary under profiles/ and reported only while the
 GEMM source still hashes to the value recorded there. `cpu_baseline` times
 the CPU oracle on a bounded token sample of the same workload.
+
+After the timed steps (and outside them): `two_stream_ms_per_step` times the
+same step with the backward's weight-gradient GEMMs on a second stream,
+concurrently with the data-gradient GEMMs, and `inference_forward_ms` the
+forward alone, unfused and fused (no x_perm, routing weights in the down
+GEMM's epilogue). `--timed-only` skips these and the CPU baseline, so that
+under a profiler the last K launches of every kernel are the timed steps.
 """
 from __future__ import annotations
 
@@ -154,6 +158,8 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--timed-only", action="store_true",
+                    help="launch nothing after the timed steps (for profiling): no sequential, inference or CPU pass")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (PMC counter calibration)")
     args = ap.parse_args()
@@ -186,12 +192,6 @@ def main() -> int:
     dgu = torch.empty(cfg.M, 2 * cfg.I, dtype=torch.bfloat16, device="cuda")  # [dG | dU]
     x, wr, wg, wu, wd, dy = (dev[n] for n in ["x", "w_router", "w_gate", "w_up", "w_down", "dy"])
     stream = torch.cuda.current_stream()
-    # The backward's weight-gradient GEMMs run on a second stream (default
-    # priority) while the data-gradient GEMMs run on the main one; each fills
-    # the other's tail. Dependencies: both down GEMMs need do_perm (combine
-    # backward), the gate/up ones need dG|dU (down dgrad); the step ends when
-    # both streams are done.
-    aux = torch.cuda.Stream()
     names = ["moe_route", "moe_permute", "moe_gemm_gate_up", "moe_gemm_down", "moe_combine", "moe_combine_bwd",
              "moe_gemm_down_dgrad", "moe_gemm_down_wgrad", "moe_gemm_gate_up_dgrad", "moe_gemm_gate_up_wgrad",
              "moe_unpermute_sum", "moe_route_bwd"]
@@ -211,33 +211,38 @@ def main() -> int:
         lambda: B.moe_unpermute_sum(s, b["dx_perm"], b["flat_to_sorted"], b["dx"]),
         lambda: B.moe_route_bwd(s, b["d_topk_w"], b["topk_w"], b["topk_idx"], b["d_logits"]),
     ]
-    on_aux = {"moe_gemm_down_wgrad", "moe_gemm_gate_up_wgrad"}
-    # Program order of the step: down wgrad is enqueued before down dgrad so
-    # that it starts first on its stream; gate/up wgrad waits for dG|dU.
-    order = ["moe_route", "moe_permute", "moe_gemm_gate_up", "moe_gemm_down", "moe_combine", "moe_combine_bwd",
-             "moe_gemm_down_wgrad", "moe_gemm_down_dgrad", "moe_gemm_gate_up_wgrad", "moe_gemm_gate_up_dgrad",
-             "moe_unpermute_sum", "moe_route_bwd"]
     by_name = dict(zip(names, calls))
     ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
           for _ in range(args.steps)]
 
     def step(events=None):
-        for n in order:
-            if n == "moe_gemm_down_wgrad":  # fork after the combine backward
-                e = torch.cuda.Event()
-                e.record(stream)
-                aux.wait_event(e)
-            if n == "moe_gemm_gate_up_wgrad":  # dG | dU written by the down dgrad
-                e = torch.cuda.Event()
-                e.record(stream)
-                aux.wait_event(e)
-            strm = aux if n in on_aux else stream
+        for n in names:
             if events is not None:
-                events[n][0].record(strm)
-            with torch.cuda.stream(strm):
+                events[n][0].record(stream)
+            by_name[n]()
+            if events is not None:
+                events[n][1].record(stream)
+
+    # The same step with the weight-gradient GEMMs on a second stream
+    # (default priority), each overlapping a data-gradient GEMM; they run one
+    # after the other there, so they can share the workspace.
+    aux = torch.cuda.Stream()
+    on_aux = {"moe_gemm_down_wgrad", "moe_gemm_gate_up_wgrad"}
+    order2 = ["moe_route", "moe_permute", "moe_gemm_gate_up", "moe_gemm_down", "moe_combine", "moe_combine_bwd",
+              "moe_gemm_down_wgrad", "moe_gemm_down_dgrad", "moe_gemm_gate_up_wgrad", "moe_gemm_gate_up_dgrad",
+              "moe_unpermute_sum", "moe_route_bwd"]
+
+    def step_two_streams():
+        for n in order2:
+            if n in ("moe_gemm_down_wgrad", "moe_gemm_gate_up_wgrad"):  # after combine bwd / down dgrad
+                e = torch.cuda.Event()
+                e.record(stream)
+                aux.wait_event(e)
+            if n in on_aux:
+                with torch.cuda.stream(aux):
+                    by_name[n]()
+            else:
                 by_name[n]()
-            if events is not None:
-                events[n][1].record(strm)
         e = torch.cuda.Event()  # join
         e.record(aux)
         stream.wait_event(e)
@@ -259,6 +264,22 @@ def main() -> int:
                 for n in names}
     log(f"timed {args.steps} steps: {ms:.3f} ms/step; " + ", ".join(f"{n}={v:.3f}" for n, v in per_call.items()))
 
+    def time_fn(fn, reps=10):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    two_stream_ms = None if args.timed_only else round(time_fn(step_two_streams), 4)
+    if two_stream_ms is not None:
+        log(f"two-stream backward: {two_stream_ms:.3f} ms/step")
+
     # Inference forward at the same shape (outside the timed training steps):
     # the unfused chain (route, permute with the gather, the two GEMMs, the
     # weighted combine) against the fused path (no x_perm, routing weights in
@@ -275,20 +296,10 @@ def main() -> int:
                             b["offsets"], b["sorted_to_flat"], b["flat_to_sorted"], fb["row_token"],
                             fb["row_weight"], b["a"], b["o_perm"], b["y"], st.ws)
 
-    def time_fn(fn, reps=10):
-        for _ in range(2):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
-
-    infer = {"unfused": round(time_fn(infer_unfused), 4), "fused": round(time_fn(infer_fused), 4)}
-    log(f"inference forward: unfused {infer['unfused']:.3f} ms, fused {infer['fused']:.3f} ms")
+    infer = None
+    if not args.timed_only:
+        infer = {"unfused": round(time_fn(infer_unfused), 4), "fused": round(time_fn(infer_fused), 4)}
+        log(f"inference forward: unfused {infer['unfused']:.3f} ms, fused {infer['fused']:.3f} ms")
 
     flops = gemm_flops(cfg)
     nbytes = alg_bytes(cfg)
@@ -313,27 +324,10 @@ def main() -> int:
             roof["mfma_frac"] = round(flops[dominant] / secs / 1e12 / PEAK_BF16_TFLOPS, 4)
         return roof
 
-    # Over the timed (two-stream) region: a call's time there includes any
-    # wait for CUs held by the concurrent stream.
     roof = roofline(per_call)
-    roof["timing"] = "timed region, HIP events on the call's stream"
-    # The same calls one at a time on one stream: each kernel's own duration.
-    seq_ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
-              for _ in range(5)]
-    torch.cuda.synchronize()
-    for k in range(len(seq_ev)):
-        for n in order:
-            seq_ev[k][n][0].record(stream)
-            by_name[n]()
-            seq_ev[k][n][1].record(stream)
-    torch.cuda.synchronize()
-    per_call_seq = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in seq_ev) / len(seq_ev) for n in names}
-    roof_seq = roofline(per_call_seq)
-    roof_seq["timing"] = "one call at a time on one stream, after the timed region"
-    # Per-kernel rates from the one-call-at-a-time pass (their own durations).
-    gemm_tflops = {n: round(flops[n] / (per_call_seq[n] * 1e-3) / 1e12, 1) for n in flops}
+    gemm_tflops = {n: round(flops[n] / (per_call[n] * 1e-3) / 1e12, 1) for n in flops}
     # HBM fraction of the calls without matrix work (algorithmic bytes).
-    hbm_frac = {n: round(nbytes[n] / (per_call_seq[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)
+    hbm_frac = {n: round(nbytes[n] / (per_call[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)
                 for n in names if n not in flops}
     out = {
         "metric": METRIC,
@@ -354,13 +348,12 @@ def main() -> int:
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "gemm_tflops": gemm_tflops,
         "call_ms": {n: round(v, 4) for n, v in per_call.items()},
-        "call_ms_sequential": {n: round(v, 4) for n, v in per_call_seq.items()},
         "hbm_frac": hbm_frac,
         "roofline": roof,
-        "roofline_sequential": roof_seq,
+        "two_stream_ms_per_step": two_stream_ms,
         "inference_forward_ms": infer,
     }
-    if not args.no_cpu_baseline:
+    if not (args.no_cpu_baseline or args.timed_only):
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
         out["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_tokens)
     print(json.dumps(out), flush=True)
