@@ -25,7 +25,9 @@ the CPU oracle on a bounded token sample of the same workload.
 
 After the timed steps (and outside them): `two_stream_ms_per_step` times the
 same step with the backward's weight-gradient GEMMs on a second stream,
-concurrently with the data-gradient GEMMs, and `inference_forward_ms` the
+concurrently with the data-gradient GEMMs; `gather_fused_ms` the step
+without x_perm (gate/up and its weight gradient read x through the sorted
+rows' tokens) and its three changed calls; and `inference_forward_ms` the
 forward alone, unfused and fused (no x_perm, routing weights in the down
 GEMM's epilogue). `--timed-only` skips these and the CPU baseline, so that
 under a profiler the last K launches of every kernel are the timed steps.
@@ -280,6 +282,30 @@ def main() -> int:
     if two_stream_ms is not None:
         log(f"two-stream backward: {two_stream_ms:.3f} ms/step")
 
+    # The same step without x_perm: the sort also writes each sorted row's
+    # token, and gate/up and its weight gradient read x rows through it.
+    rt = dict(row_token=torch.empty(cfg.M, dtype=torch.int32, device="cuda"),
+              row_weight=torch.empty(cfg.M, device="cuda"))
+    gf_calls = dict(by_name)
+    gf_calls["moe_permute"] = lambda: B.moe_permute_fused(
+        s, b["topk_idx"], b["topk_w"], b["counts"], b["offsets"], b["sorted_to_flat"], b["flat_to_sorted"],
+        rt["row_token"], rt["row_weight"], st.ws)
+    gf_calls["moe_gemm_gate_up"] = lambda: B.moe_gemm_gate_up_gathered(
+        s, x, rt["row_token"], b["offsets"], wg, wu, b["g"], b["u"], b["a"])
+    gf_calls["moe_gemm_gate_up_wgrad"] = lambda: B.moe_gemm_gate_up_wgrad_gathered(
+        s, dgu, x, rt["row_token"], b["offsets"], b["dw_gate"], b["dw_up"], 0, st.ws)
+
+    def step_gather_fused():
+        for n in names:
+            gf_calls[n]()
+
+    gather_fused_ms = None
+    if not args.timed_only:
+        gather_fused_ms = {"step": round(time_fn(step_gather_fused), 4)}
+        for n in ["moe_permute", "moe_gemm_gate_up", "moe_gemm_gate_up_wgrad"]:
+            gather_fused_ms[n] = round(time_fn(gf_calls[n], reps=5), 4)
+        log(f"step without x_perm: {gather_fused_ms}")
+
     # Inference forward at the same shape (outside the timed training steps):
     # the unfused chain (route, permute with the gather, the two GEMMs, the
     # weighted combine) against the fused path (no x_perm, routing weights in
@@ -351,6 +377,7 @@ def main() -> int:
         "hbm_frac": hbm_frac,
         "roofline": roof,
         "two_stream_ms_per_step": two_stream_ms,
+        "gather_fused_ms": gather_fused_ms,
         "inference_forward_ms": infer,
     }
     if not (args.no_cpu_baseline or args.timed_only):

@@ -8,6 +8,11 @@
  *   inference (gather and routing weights fused into the GEMMs):
  *             moe_forward_fused = moe_route -> moe_permute_fused ->
  *             moe_gemm_gate_up_gathered -> moe_gemm_down_weighted -> moe_unpermute_sum
+ *   training without x_perm (the gather fused into both GEMMs that read x):
+ *             moe_route -> moe_permute_fused -> moe_gemm_gate_up_gathered ->
+ *             moe_gemm_down -> moe_combine; moe_combine_bwd -> moe_gemm_down_dgrad,
+ *             moe_gemm_down_wgrad, moe_gemm_gate_up_dgrad,
+ *             moe_gemm_gate_up_wgrad_gathered -> moe_unpermute_sum -> moe_route_bwd
  *
  * It replaces the per-expert for-loop of the Hugging Face MoE block (axolotl
  * issue #3155, "Feature description") with router softmax/top-k, a sort of the
@@ -229,6 +234,17 @@ moe_status moe_gemm_gate_up_gathered(moe_shape s, const void* x, const int32_t* 
  *   o_perm[p,:] = row_weight[p] * (a[p,:] W_down[e]^T). */
 moe_status moe_gemm_down_weighted(moe_shape s, const void* a, const int32_t* offsets, const void* w_down,
                                   const float* row_weight, void* o_perm, hipStream_t stream);
+
+/* moe_gemm_gate_up_wgrad with k-row p of its x operand read as row
+ * row_token[p] of x [T,H] (dtype) instead of x_perm, so that training needs
+ * no x_perm either (row_token from moe_permute_fused):
+ *   dw_gate[e] = dG_e^T X_e,  dw_up[e] = dU_e^T X_e,  X_e[p,:] = x[row_token[p],:]
+ * over the rows p of expert e. Same outputs, workspace and accumulate_dw
+ * rules as moe_gemm_gate_up_wgrad. T*H*sizeof(dtype) and 4*(T*k + 256) must
+ * stay below 2^31 (MOE_EUNSUPPORTED otherwise). */
+moe_status moe_gemm_gate_up_wgrad_gathered(moe_shape s, const void* dgu, const void* x, const int32_t* row_token,
+                                           const int32_t* offsets, float* dw_gate, float* dw_up, int accumulate_dw,
+                                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* The fused inference forward in one call: moe_route (logits, topk_idx,
  * topk_w), moe_permute_fused (counts, offsets, sorted_to_flat,

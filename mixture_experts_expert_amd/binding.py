@@ -63,6 +63,8 @@ _SIGS = {
     "moe_permute_fused": ([moe_shape, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "moe_gemm_gate_up_gathered": ([moe_shape, _P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_gemm_down_weighted": ([moe_shape, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_gemm_gate_up_wgrad_gathered": ([moe_shape, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_size_t, _P],
+                                        ctypes.c_int),
     "moe_forward_fused": ([moe_shape] + [_P] * 19 + [ctypes.c_size_t, _P], ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
@@ -201,6 +203,14 @@ def moe_gemm_gate_up_gathered(s, x, row_token, offsets, w_gate, w_up, g, u, a, s
         _stream(stream)))
 
 
+def moe_gemm_gate_up_wgrad_gathered(s, dgu, x, row_token, offsets, dw_gate, dw_up, accumulate_dw, ws, ws_bytes=None,
+                                    stream=None):
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_gemm_gate_up_wgrad_gathered",
+           lib.moe_gemm_gate_up_wgrad_gathered(s, _ptr(dgu), _ptr(x), _ptr(row_token), _ptr(offsets), _ptr(dw_gate),
+                                               _ptr(dw_up), int(accumulate_dw), _ptr(ws), nb, _stream(stream)))
+
+
 def moe_gemm_down_weighted(s, a, offsets, w_down, row_weight, o_perm, stream=None):
     _check("moe_gemm_down_weighted", lib.moe_gemm_down_weighted(s, _ptr(a), _ptr(offsets), _ptr(w_down),
                                                                 _ptr(row_weight), _ptr(o_perm), _stream(stream)))
@@ -224,10 +234,16 @@ class MoEStage:
     float32. ``forward(x)`` and ``backward(dy)`` enqueue the library calls on
     the current stream and return views of the held buffers (overwritten by
     the next call).
+
+    ``gather_fused``: no x_perm. The sort also gives each sorted row's token
+    (moe_permute_fused), and the two GEMMs that read x rows (gate/up and its
+    weight gradient) read them from x through it. Same results, bit for bit.
     """
 
-    def __init__(self, T: int, H: int, E: int, k: int, I: int, dtype: torch.dtype, device="cuda"):
+    def __init__(self, T: int, H: int, E: int, k: int, I: int, dtype: torch.dtype, device="cuda",
+                 gather_fused: bool = False):
         self.T, self.H, self.E, self.k, self.I, self.dtype = T, H, E, k, I, dtype
+        self.gather_fused = gather_fused
         self.s = shape(T, H, E, k, I, dtype)
         M = T * k
         dev = torch.device(device)
@@ -236,9 +252,13 @@ class MoEStage:
         self.buf: Dict[str, torch.Tensor] = {
             "logits": e(T, E, dt=f32), "topk_idx": e(T, k, dt=i32), "topk_w": e(T, k, dt=f32),
             "counts": e(E, dt=i32), "offsets": e(E + 1, dt=i32), "sorted_to_flat": e(M, dt=i32),
-            "flat_to_sorted": e(M, dt=i32), "x_perm": e(M, H), "g": e(M, I), "u": e(M, I), "a": e(M, I),
+            "flat_to_sorted": e(M, dt=i32), "g": e(M, I), "u": e(M, I), "a": e(M, I),
             "o_perm": e(M, H), "y": e(T, H),
         }
+        if gather_fused:
+            self.buf.update({"row_token": e(M, dt=i32), "row_weight": e(M, dt=f32)})
+        else:
+            self.buf["x_perm"] = e(M, H)
         ws_bytes = moe_workspace_bytes(self.s)
         if ws_bytes == 0:
             raise MoEError("moe_workspace_bytes", 1, "shape rejected")
@@ -263,11 +283,19 @@ class MoEStage:
     def forward(self, x, w_router, w_gate, w_up, w_down, logit_bias=None, stream=None):
         b, s = self.buf, self.s
         self.w = (w_gate, w_up, w_down)
+        self.x = x
         moe_route(s, x, w_router, logit_bias, b["logits"], b["topk_idx"], b["topk_w"], stream)
-        moe_permute(s, b["topk_idx"], x, b["counts"], b["offsets"], b["sorted_to_flat"], b["flat_to_sorted"],
-                    b["x_perm"], self.ws, stream=stream)
-        moe_grouped_gemm_fwd(s, b["x_perm"], b["offsets"], w_gate, w_up, w_down, b["g"], b["u"], b["a"],
-                             b["o_perm"], stream=stream)
+        if self.gather_fused:
+            moe_permute_fused(s, b["topk_idx"], b["topk_w"], b["counts"], b["offsets"], b["sorted_to_flat"],
+                              b["flat_to_sorted"], b["row_token"], b["row_weight"], self.ws, stream=stream)
+            moe_gemm_gate_up_gathered(s, x, b["row_token"], b["offsets"], w_gate, w_up, b["g"], b["u"], b["a"],
+                                      stream)
+            moe_gemm_down(s, b["a"], b["offsets"], w_down, b["o_perm"], stream)
+        else:
+            moe_permute(s, b["topk_idx"], x, b["counts"], b["offsets"], b["sorted_to_flat"], b["flat_to_sorted"],
+                        b["x_perm"], self.ws, stream=stream)
+            moe_grouped_gemm_fwd(s, b["x_perm"], b["offsets"], w_gate, w_up, w_down, b["g"], b["u"], b["a"],
+                                 b["o_perm"], stream=stream)
         moe_combine(s, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["y"], stream)
         return b["y"]
 
@@ -280,29 +308,37 @@ class MoEStage:
         b, s = self.buf, self.s
         w_gate, w_up, w_down = self.w
         moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["do_perm"], b["d_topk_w"], stream)
-        if aux_stream is None:
+        acc = int(accumulate_dw)
+        if aux_stream is None and not self.gather_fused:
             moe_grouped_gemm_bwd(s, b["do_perm"], b["x_perm"], b["g"], b["u"], b["a"], b["offsets"], w_gate, w_up,
-                                 w_down, b["dx_perm"], b["dw_gate"], b["dw_up"], b["dw_down"], int(accumulate_dw),
-                                 self.ws, stream=stream)
+                                 w_down, b["dx_perm"], b["dw_gate"], b["dw_up"], b["dw_down"], acc, self.ws,
+                                 stream=stream)
         else:
             main = torch.cuda.current_stream() if stream is None else stream
+            wg = main if aux_stream is None else aux_stream  # the weight-gradient GEMMs' stream
             if "dgu" not in b:
                 b["dgu"] = torch.empty(self.T * self.k, 2 * self.I, dtype=self.dtype, device=self.ws.device)
-            acc = int(accumulate_dw)
-            forked = torch.cuda.Event()
-            forked.record(main)
-            aux_stream.wait_event(forked)
-            moe_gemm_down_wgrad(s, b["do_perm"], b["a"], b["offsets"], b["dw_down"], acc, self.ws, stream=aux_stream)
+            if aux_stream is not None:
+                forked = torch.cuda.Event()
+                forked.record(main)
+                aux_stream.wait_event(forked)
+            moe_gemm_down_wgrad(s, b["do_perm"], b["a"], b["offsets"], b["dw_down"], acc, self.ws, stream=wg)
             moe_gemm_down_dgrad(s, b["do_perm"], b["offsets"], w_down, b["g"], b["u"], b["dgu"], main)
-            dgu_ready = torch.cuda.Event()
-            dgu_ready.record(main)
-            aux_stream.wait_event(dgu_ready)
-            moe_gemm_gate_up_wgrad(s, b["dgu"], b["x_perm"], b["offsets"], b["dw_gate"], b["dw_up"], acc, self.ws,
-                                   stream=aux_stream)
+            if aux_stream is not None:
+                dgu_ready = torch.cuda.Event()
+                dgu_ready.record(main)
+                aux_stream.wait_event(dgu_ready)
+            if self.gather_fused:
+                moe_gemm_gate_up_wgrad_gathered(s, b["dgu"], self.x, b["row_token"], b["offsets"], b["dw_gate"],
+                                                b["dw_up"], acc, self.ws, stream=wg)
+            else:
+                moe_gemm_gate_up_wgrad(s, b["dgu"], b["x_perm"], b["offsets"], b["dw_gate"], b["dw_up"], acc,
+                                       self.ws, stream=wg)
             moe_gemm_gate_up_dgrad(s, b["dgu"], b["offsets"], w_gate, w_up, b["dx_perm"], main)
-            joined = torch.cuda.Event()
-            joined.record(aux_stream)
-            main.wait_event(joined)
+            if aux_stream is not None:
+                joined = torch.cuda.Event()
+                joined.record(aux_stream)
+                main.wait_event(joined)
         moe_unpermute_sum(s, b["dx_perm"], b["flat_to_sorted"], b["dx"], stream)
         moe_route_bwd(s, b["d_topk_w"], b["topk_w"], b["topk_idx"], b["d_logits"], stream)
         return b["dx"]

@@ -212,6 +212,31 @@ moe_status moe_gemm_gate_up_gathered(moe_shape s, const void* x, const int32_t* 
   return from_hip(moe::launch_gemm(moe::GEMM_GATEUP, s, ga, stream));
 }
 
+moe_status moe_gemm_gate_up_wgrad_gathered(moe_shape s, const void* dgu, const void* x, const int32_t* row_token,
+                                           const int32_t* offsets, float* dw_gate, float* dw_up, int accumulate_dw,
+                                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(dgu, x, row_token, offsets, dw_gate, dw_up, ws)) return MOE_EINVAL;
+  if (accumulate_dw != 0 && accumulate_dw != 1) return MOE_EINVAL;
+  const WsLayout l = moe::ws_layout(s);
+  if (ws_bytes < l.total) return MOE_EWORKSPACE;
+  // x and row_token are addressed with 32-bit byte offsets.
+  if (static_cast<int64_t>(s.T) * s.H * (s.dtype == MOE_BF16 ? 2 : 4) >= (static_cast<int64_t>(1) << 31) ||
+      4 * (static_cast<int64_t>(s.T) * s.k + 256) >= (static_cast<int64_t>(1) << 31))
+    return MOE_EUNSUPPORTED;
+  moe::GemmArgs ga{};
+  ga.part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.part_off);
+  ga.offsets = offsets;
+  ga.a = dgu;
+  ga.b0 = x;
+  ga.row_token = row_token;
+  ga.dw0 = dw_gate;
+  ga.dw1 = dw_up;
+  ga.accumulate = accumulate_dw;
+  return from_hip(moe::launch_gemm(moe::GEMM_WGRAD_GATEUP, s, ga, stream));
+}
+
 moe_status moe_gemm_down_weighted(moe_shape s, const void* a, const int32_t* offsets, const void* w_down,
                                   const float* row_weight, void* o_perm, hipStream_t stream) {
   moe_status st = check_shape(s);

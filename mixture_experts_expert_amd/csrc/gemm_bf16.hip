@@ -87,6 +87,7 @@ constexpr bool b_kcontig(int m) { return m == GATEUP || m == DOWN; }
 
 struct Params {
   int T, H, E, I;
+  int M;               // T * k rows of the sorted operands
   const int32_t* offsets;
   const bf16_t* a;     // x_perm | act | do_perm | dgu | do_perm | dgu
   const bf16_t* b0;    // w_gate | w_down | w_down | w_gate | act | x_perm
@@ -100,9 +101,10 @@ struct Params {
   float* dw1;          // dw_up
   int accumulate;
   float* part;         // weight gradients: split-K partial tiles [tile][256][256]
-  // Fused inference forward (both optional): GATEUP reads row p of A as row
-  // row_token[p] of x [T][H] (no x_perm); DOWN scales output row p by
-  // row_weight[p] before rounding. GATEUP with out0 == nullptr stores A only.
+  // Fused gather and routing weights (both optional): GATEUP reads row p of A
+  // as row row_token[p] of x [T][H] (no x_perm), WGRAD_GATEUP reads k-row p of
+  // B likewise; DOWN scales output row p by row_weight[p] before rounding.
+  // GATEUP with out0 == nullptr stores A only.
   const int32_t* row_token;
   const float* row_weight;
 };
@@ -150,6 +152,7 @@ __device__ __forceinline__ void step_barrier() {
 // [6:4], lgkmcnt in [11:8]. They wait for LDS traffic and for all but the
 // newest `n` vector-memory instructions (expcnt left unconstrained).
 constexpr int kWaitVm12 = 0x007C;  // vmcnt(12) lgkmcnt(0)
+constexpr int kWaitVm14 = 0x007E;  // vmcnt(14) lgkmcnt(0)
 constexpr int kWaitVm16 = 0x4070;  // vmcnt(16) lgkmcnt(0)
 constexpr int kWaitAll = 0x0000;   // vmcnt(0) expcnt(0) lgkmcnt(0)
 
@@ -320,9 +323,11 @@ __device__ __forceinline__ int split_cap(int work, int grid) {
 __device__ __forceinline__ int split_chunks(int steps, int cap) { return steps > cap ? (steps + cap - 1) / cap : 1; }
 __device__ __forceinline__ int split_len(int steps, int chunks) { return (steps + chunks - 1) / chunks; }
 
-// FUSED (the inference forward, compiled separately so that the training
-// kernels carry none of it): GATEUP reads its A rows through P.row_token and
-// may skip storing G and U; DOWN scales its output rows by P.row_weight.
+// FUSED (the gather and the routing weights fused into the GEMMs, compiled
+// separately so that the plain kernels carry none of it): GATEUP reads its A
+// rows through P.row_token and may skip storing G and U; WGRAD_GATEUP reads
+// its B k-rows (x) through P.row_token; DOWN scales its output rows by
+// P.row_weight.
 template <int MODE, bool FUSED>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(
     Params P) {
@@ -337,6 +342,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   __shared__ int pstart[1025];  // grouped-K: first partial tile of each expert
   __shared__ int wstart[1025];  // grouped-K: work (k-steps) before each expert's tiles
   __shared__ int part[NT];
+  __shared__ int eoff[1025];    // offsets[0..E]: read at every tile start, from LDS rather than
+                                // through a vector load whose wait would drain the prefetches
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -344,6 +351,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
   const int wm = wave >> 1, wn = wave & 1;
   const int H = P.H, E = P.E, I = P.I;
+
+  for (int x = tid; x <= E; x += NT) eoff[x] = P.offsets[x];  // visible after the scans' barriers
 
   // ---- tile list -----------------------------------------------------------
   int ntn, total;
@@ -438,6 +447,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
 
   constexpr bool A_KMAJOR = !grouped_k(MODE);
   constexpr bool B_KMAJOR = b_kcontig(MODE);
+  // Gate/up weight gradient with x read through row_token: the k-rows of B
+  // are gathered, so B's load offsets change with every k-step.
+  constexpr bool GATHER_B = MODE == WGRAD_GATEUP && FUSED;
 
   // ---- tile state ------------------------------------------------------------
   // Everything the operand loads of a tile depend on. A tile's last k-step
@@ -454,9 +466,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
 
   int e = 0, row0 = 0, mvalid = 0, m0 = 0, n0 = 0, kbeg = 0, kend = 0, ksteps = 0;
   int pidx = -1;  // grouped-K: partial tile of a later chunk, -1 for chunk 0
+  int nkbeg = 0;  // GATHER_B: first k-row of this workgroup's next tile
   uint32_t aoff[LOADS / 2], boff[LOADS / 2];
+  uint32_t bcol[LOADS / 2];  // GATHER_B: column byte offsets of the B loads
   const bf16_t* abase_m = P.a;  // grouped-M: the tile's first row of A
 
+  // Grouped-K: the first k-row of tile Lx's chunk.
+  auto kbeg_of = [&](int Lx) -> int {
+    int l2 = 0, h2 = E - 1;
+    while (l2 < h2) {
+      const int mid = (l2 + h2 + 1) >> 1;
+      if (tstart[mid] <= Lx) l2 = mid; else h2 = mid - 1;
+    }
+    const int ob = eoff[l2], oe = eoff[l2 + 1];
+    const int steps = (oe - ob + BK - 1) / BK;
+    return ob + (Lx - tstart[l2]) / tpe * split_len(steps, split_chunks(steps, kcap)) * BK;
+  };
   auto set_tile = [&](int L) __attribute__((always_inline)) {
     int te, trow0 = 0, tmvalid = 0, tm0 = 0, tn0 = 0, tkbeg = 0, tkend = 0, tpidx = -1;
     if constexpr (!grouped_k(MODE)) {
@@ -470,8 +495,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       const int mte = tstart[te + 1] - tstart[te];
       const int nt = rem / mte;
       const int mt = rem - nt * mte;
-      trow0 = P.offsets[te] + mt * BM;
-      tmvalid = min(BM, P.offsets[te + 1] - trow0);
+      trow0 = eoff[te] + mt * BM;
+      tmvalid = min(BM, eoff[te + 1] - trow0);
       tn0 = nt * (MODE == GATEUP ? GU_COLS : BN);
     } else {
       int l2 = 0, h2 = E - 1;
@@ -487,7 +512,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       const int nt = t - mt * ntn;
       tm0 = mt * BM;
       tn0 = nt * BN;
-      const int ob = P.offsets[te], oe = P.offsets[te + 1];
+      const int ob = eoff[te], oe = eoff[te + 1];
       const int steps = (oe - ob + BK - 1) / BK;
       const int len = split_len(steps, split_chunks(steps, kcap)) * BK;
       tkbeg = ob + chunk * len;
@@ -505,6 +530,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
     kend = __builtin_amdgcn_readfirstlane(tkend);
     pidx = __builtin_amdgcn_readfirstlane(tpidx);
     ksteps = grouped_k(MODE) ? (kend - kbeg + BK - 1) / BK : kfixed;
+    if constexpr (GATHER_B)  // the row tokens run two steps ahead, into the next tile
+      nkbeg = __builtin_amdgcn_readfirstlane(L + nslots < hi ? kbeg_of(L + nslots) : 0);
   };
   // Per-lane load offsets of the current tile (vector registers; recomputed
   // rather than kept alive across an epilogue).
@@ -555,7 +582,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
         const int k = blk * 2 + (lane >> 5);
         const int c = (lane & 31) ^ swt(k);
         const int ncols = (MODE == DGRAD_DOWN || MODE == WGRAD_DOWN) ? I : H;
-        boff[t] = 2u * (k * ldb + min(n0 + c * 8, ncols - 8));
+        if constexpr (GATHER_B) bcol[t] = 2u * min(n0 + c * 8, ncols - 8);  // row part: gather_boff
+        else boff[t] = 2u * (k * ldb + min(n0 + c * 8, ncols - 8));
       }
     }
     abase_m = P.a + static_cast<int64_t>(row0) * lda;
@@ -600,9 +628,44 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
                        live ? 2 * (I - kk0) * H : 0);
     } else {
       const int left = kend - kbeg - k0;
+      if constexpr (GATHER_B) return make_rsrc(P.b0, left > 0 ? 2 * P.T * H : 0);
       return make_rsrc(P.b0 + static_cast<int64_t>(kbeg + k0) * ldb, left > 0 ? 2 * left * ldb : 0);
     }
   };
+
+  // GATHER_B: the row tokens of B's k-rows. Instruction t of a wavefront's B
+  // loads covers k-rows 8 wave + 2t (lanes 0-31) and 8 wave + 2t + 1 (lanes
+  // 32-63) of its step; lane l fetches the token of k-row
+  // 8 wave + 2 (l % 4) + l / 32, so that lanes t and 32 + t hold the two rows
+  // of instruction t. Step q of the current tile, or (q past the tile's
+  // padded step count) step q - that count of the next one. Reads past the
+  // end of row_token return 0; such rows are never used.
+  const rsrc_t rtok = make_rsrc(P.row_token, GATHER_B ? 4 * P.M : 0);
+  auto load_tok = [&](int q) -> uint32_t {
+    const int nst = max(NSTAGE, (ksteps + NSTAGE - 1) / NSTAGE * NSTAGE);
+    const bool nxt = q >= nst;
+    int lane = lane_id;  // opaque copy: the lane term is recomputed here, not kept alive (and spilled)
+    asm volatile("" : "+v"(lane));
+    const int row = (nxt ? nkbeg : kbeg) + (nxt ? q - nst : q) * BK + wave * 8 + 2 * (lane & 3) + (lane >> 5);
+    return __builtin_amdgcn_raw_buffer_load_b32(rtok, 4u * static_cast<uint32_t>(row), 0, 0);
+  };
+  // B's byte offsets for step sn of the current tile from its tokens: row
+  // token * 2H plus the column part; k-rows past the chunk's end get an
+  // offset outside the range (zeros).
+  auto gather_boff = [&](uint32_t tok, int sn) __attribute__((always_inline)) {
+    const int left = kend - kbeg - sn * BK - wave * 8;
+    const bool hi32 = lane_id >= 32;
+#pragma unroll
+    for (int t = 0; t < LOADS / 2; ++t) {
+      const uint32_t t0 = __builtin_amdgcn_readlane(tok, t);
+      const uint32_t t1 = __builtin_amdgcn_readlane(tok, 32 + t);
+      const uint32_t o0 = 2 * t < left ? t0 * (2u * H) : kNoWrite;
+      const uint32_t o1 = 2 * t + 1 < left ? t1 * (2u * H) : kNoWrite;
+      boff[t] = (hi32 ? o1 : o0) + bcol[t];
+    }
+  };
+  // Tokens of steps sn and sn + 1 at the start of the k-step that loads sn.
+  uint32_t tkA = 0, tkB = 0;
 
   // Load instruction v of a k-step's 8, for step sn into the stage at L:
   // even v an A block, odd v a B block (block v/2 of this wavefront's 4).
@@ -725,6 +788,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   // the next tile's first steps comes after the epilogue.
   auto kstep = [&](auto nbc, auto first, const bf16_t* Ac, const bf16_t* An, int sn, bf16_t* Ln, bool last)
                    __attribute__((always_inline)) {
+    if constexpr (GATHER_B) {
+      // Step sn's B offsets from tokens loaded two k-steps ago (their wait
+      // covers only loads the pipeline has already waited for), then the
+      // tokens of step sn + 2, ahead of this step's operand loads.
+      gather_boff(tkA, sn);
+      const uint32_t tn = load_tok(sn + 2);
+      tkA = tkB;
+      tkB = tn;
+      __builtin_amdgcn_sched_barrier(0);
+    }
     const rsrc_t ra = rsrc_a(sn);
     const rsrc_t rb = rsrc_b(sn);
     bf16x8 fa1[FM], fb1[FN];
@@ -733,7 +806,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
     __builtin_amdgcn_sched_barrier(0);
     mfma_slice(nbc, first, fa0, fb0, 0, ra, rb, Ln);
     if (!last) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm12);
+      // GATHER_B: two token loads more among the newest.
+      __builtin_amdgcn_s_waitcnt(GATHER_B ? kWaitVm14 : kWaitVm12);
       step_barrier();
       read_slice(nbc, An, 0, fa0, fb0);
     }
@@ -991,9 +1065,21 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   int L = lo + slot;
   if (L < hi) {
     set_tile_and_offsets(L);
-    issue(0, lds0);
-    issue(1, lds1);
-    issue(2, lds2);
+    if constexpr (GATHER_B) {
+      const uint32_t tk0 = load_tok(0), tk1 = load_tok(1), tk2 = load_tok(2);
+      tkA = load_tok(3);
+      tkB = load_tok(4);
+      gather_boff(tk0, 0);
+      issue(0, lds0);
+      gather_boff(tk1, 1);
+      issue(1, lds1);
+      gather_boff(tk2, 2);
+      issue(2, lds2);
+    } else {
+      issue(0, lds0);
+      issue(1, lds1);
+      issue(2, lds2);
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVm16);  // step 0 has landed (steps 1 and 2 may not have)
     step_barrier();
   }
@@ -1153,6 +1239,7 @@ int64_t wgrad_part_tiles(const moe_shape& s) {
 hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g, hipStream_t st) {
   Params p{};
   p.T = s.T;
+  p.M = s.T * s.k;
   p.H = s.H;
   p.E = s.E;
   p.I = s.I;
@@ -1177,7 +1264,7 @@ hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g
     case GEMM_DGRAD_DOWN: return run<DGRAD_DOWN>(p, st);
     case GEMM_DGRAD_GATEUP: return run<DGRAD_GATEUP>(p, st);
     case GEMM_WGRAD_DOWN: return run<WGRAD_DOWN>(p, st);
-    case GEMM_WGRAD_GATEUP: return run<WGRAD_GATEUP>(p, st);
+    case GEMM_WGRAD_GATEUP: return g.row_token ? run<WGRAD_GATEUP, true>(p, st) : run<WGRAD_GATEUP>(p, st);
   }
   return hipErrorInvalidValue;
 }

@@ -116,11 +116,14 @@ __global__ __launch_bounds__(kThreads) void wgrad_down_f32(int H, int E, int I, 
   dw[q] = accumulate ? dw[q] + s : s;
 }
 
-// dW_gate[e][i][h] = sum_p dG[p][i] x[p][h]; dW_up likewise with dU.
+// dW_gate[e][i][h] = sum_p dG[p][i] x[p][h]; dW_up likewise with dU. With
+// row_token, row p of x is row row_token[p] of the unsorted x.
 __global__ __launch_bounds__(kThreads) void wgrad_gateup_f32(int H, int E, int I, const int32_t* offsets,
                                                              const float* __restrict__ dgu,
-                                                             const float* __restrict__ xp, float* __restrict__ dwg,
-                                                             float* __restrict__ dwu, int accumulate) {
+                                                             const float* __restrict__ xp,
+                                                             const int32_t* __restrict__ row_token,
+                                                             float* __restrict__ dwg, float* __restrict__ dwu,
+                                                             int accumulate) {
   const int64_t q = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t per = 2ll * I * H;
   if (q >= per * E) return;
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void wgrad_gateup_f32(int H, int E, int I
   const int m = static_cast<int>((q % per) / H), h = static_cast<int>(q % H);
   float s = 0.0f;
   for (int p = offsets[e]; p < offsets[e + 1]; ++p)
-    s += dgu[static_cast<int64_t>(p) * 2 * I + m] * xp[static_cast<int64_t>(p) * H + h];
+    s += dgu[static_cast<int64_t>(p) * 2 * I + m] * xp[static_cast<int64_t>(row_token ? row_token[p] : p) * H + h];
   float* out = (m < I) ? dwg + (static_cast<int64_t>(e) * I + m) * H + h
                        : dwu + (static_cast<int64_t>(e) * I + (m - I)) * H + h;
   *out = accumulate ? *out + s : s;
@@ -167,8 +170,8 @@ hipError_t launch_gemm_f32(GemmMode mode, const moe_shape& s, const GemmArgs& g,
           s.H, s.E, s.I, g.offsets, A, B0, g.dw0, g.accumulate);
       break;
     case GEMM_WGRAD_GATEUP:
-      wgrad_gateup_f32<<<blocks_for(2ll * s.E * s.I * s.H), kThreads, 0, st>>>(s.H, s.E, s.I, g.offsets, A, B0,
-                                                                                 g.dw0, g.dw1, g.accumulate);
+      wgrad_gateup_f32<<<blocks_for(2ll * s.E * s.I * s.H), kThreads, 0, st>>>(
+          s.H, s.E, s.I, g.offsets, A, B0, g.row_token, g.dw0, g.dw1, g.accumulate);
       break;
     default:
       return hipErrorInvalidValue;

@@ -131,7 +131,7 @@ struct GemmArgs {
   float* dw0;
   float* dw1;
   int accumulate;
-  const int32_t* row_token;  // fused forward, GATEUP: row p of A is row row_token[p] of x [T][H]
+  const int32_t* row_token;  // GATEUP: row p of A, WGRAD_GATEUP: k-row p of B is row row_token[p] of x [T][H]
   const float* row_weight;   // fused forward, DOWN: output row p scaled by row_weight[p]
 };
 
