@@ -306,6 +306,39 @@ def main() -> int:
             gather_fused_ms[n] = round(time_fn(gf_calls[n], reps=5), 4)
         log(f"step without x_perm: {gather_fused_ms}")
 
+    # The backward's GEMMs in two launches, each a data gradient and a weight
+    # gradient side by side (moe_gemm_down_bwd, moe_gemm_gate_up_bwd).
+    pair_calls = {
+        "moe_gemm_down_bwd": lambda: B.moe_gemm_down_bwd(s, b["do_perm"], b["a"], b["offsets"], wd, b["g"], b["u"],
+                                                         dgu, b["dw_down"], 0, st.ws),
+        "moe_gemm_gate_up_bwd": lambda: B.moe_gemm_gate_up_bwd(s, dgu, b["x_perm"], None, b["offsets"], wg, wu,
+                                                               b["dx_perm"], b["dw_gate"], b["dw_up"], 0, st.ws),
+    }
+    paired = ["moe_gemm_down_dgrad", "moe_gemm_down_wgrad", "moe_gemm_gate_up_dgrad", "moe_gemm_gate_up_wgrad"]
+
+    def step_paired(calls):
+        for n in names:
+            if n == "moe_gemm_down_dgrad":
+                pair_calls["moe_gemm_down_bwd"]()
+            elif n == "moe_gemm_gate_up_dgrad":
+                calls["moe_gemm_gate_up_bwd"]()
+            elif n not in paired:
+                calls[n]()
+
+    paired_ms = None
+    if not args.timed_only:
+        gf_pair = dict(gf_calls)
+        gf_pair["moe_gemm_gate_up_bwd"] = lambda: B.moe_gemm_gate_up_bwd(
+            s, dgu, x, rt["row_token"], b["offsets"], wg, wu, b["dx_perm"], b["dw_gate"], b["dw_up"], 0, st.ws)
+        xp_pair = dict(by_name)
+        xp_pair["moe_gemm_gate_up_bwd"] = pair_calls["moe_gemm_gate_up_bwd"]
+        paired_ms = {"step": round(time_fn(lambda: step_paired(xp_pair)), 4),
+                     "step_without_x_perm": round(time_fn(lambda: step_paired(gf_pair)), 4)}
+        for n, c in pair_calls.items():
+            paired_ms[n] = round(time_fn(c, reps=5), 4)
+        paired_ms["moe_gemm_gate_up_bwd_gathered"] = round(time_fn(gf_pair["moe_gemm_gate_up_bwd"], reps=5), 4)
+        log(f"paired backward GEMMs: {paired_ms}")
+
     # Inference forward at the same shape (outside the timed training steps):
     # the unfused chain (route, permute with the gather, the two GEMMs, the
     # weighted combine) against the fused path (no x_perm, routing weights in
@@ -378,6 +411,7 @@ def main() -> int:
         "roofline": roof,
         "two_stream_ms_per_step": two_stream_ms,
         "gather_fused_ms": gather_fused_ms,
+        "paired_ms": paired_ms,
         "inference_forward_ms": infer,
     }
     if not (args.no_cpu_baseline or args.timed_only):

@@ -185,6 +185,26 @@ moe_status moe_grouped_gemm_bwd(moe_shape s, const void* do_perm, const void* x_
                                 float* dw_up, float* dw_down, int accumulate_dw, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* The backward's GEMMs in two launches (moe_grouped_gemm_bwd chains these):
+ * each runs a data gradient and then the weight gradient that reads the
+ * same inputs in one persistent launch, so that a workgroup done with the
+ * first starts on the second without waiting for the first's slowest one.
+ * Results are the same bits as the single-GEMM calls above.
+ *   moe_gemm_down_bwd     dgu <- do_perm, W_down, g, u  and  dw_down <- do_perm, a
+ *   moe_gemm_gate_up_bwd  dx_perm <- dgu, W_gate, W_up  and  dw_gate, dw_up <- dgu, x rows
+ * x rows: x_perm when row_token is NULL; otherwise x [T,H] with sorted row p
+ * read as row row_token[p] (from moe_permute_fused; the limits of
+ * moe_gemm_gate_up_wgrad_gathered apply). dw_* f32 (+= if accumulate_dw).
+ * Workspace: ws of ws_bytes >= moe_workspace_bytes(s) (split-K partials of
+ * the weight gradient). */
+moe_status moe_gemm_down_bwd(moe_shape s, const void* do_perm, const void* a, const int32_t* offsets,
+                             const void* w_down, const void* g, const void* u, void* dgu, float* dw_down,
+                             int accumulate_dw, void* ws, size_t ws_bytes, hipStream_t stream);
+moe_status moe_gemm_gate_up_bwd(moe_shape s, const void* dgu, const void* x_rows, const int32_t* row_token,
+                                const int32_t* offsets, const void* w_gate, const void* w_up, void* dx_perm,
+                                float* dw_gate, float* dw_up, int accumulate_dw, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
 /* Backward of the gather in moe_permute: dx[t,:] = sum over j ascending of
  * dx_perm[flat_to_sorted[t*k+j],:] in fp32, rounded once. Output: dx [T,H]. */
 moe_status moe_unpermute_sum(moe_shape s, const void* dx_perm, const int32_t* flat_to_sorted, void* dx,

@@ -63,6 +63,8 @@ _SIGS = {
     "moe_permute_fused": ([moe_shape, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "moe_gemm_gate_up_gathered": ([moe_shape, _P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_gemm_down_weighted": ([moe_shape, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_gemm_down_bwd": ([moe_shape] + [_P] * 8 + [ctypes.c_int, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_gemm_gate_up_bwd": ([moe_shape] + [_P] * 9 + [ctypes.c_int, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "moe_gemm_gate_up_wgrad_gathered": ([moe_shape, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_size_t, _P],
                                         ctypes.c_int),
     "moe_forward_fused": ([moe_shape] + [_P] * 19 + [ctypes.c_size_t, _P], ctypes.c_int),
@@ -203,6 +205,24 @@ def moe_gemm_gate_up_gathered(s, x, row_token, offsets, w_gate, w_up, g, u, a, s
         _stream(stream)))
 
 
+def moe_gemm_down_bwd(s, do_perm, a, offsets, w_down, g, u, dgu, dw_down, accumulate_dw, ws, ws_bytes=None,
+                      stream=None):
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_gemm_down_bwd", lib.moe_gemm_down_bwd(s, _ptr(do_perm), _ptr(a), _ptr(offsets), _ptr(w_down), _ptr(g),
+                                                      _ptr(u), _ptr(dgu), _ptr(dw_down), int(accumulate_dw), _ptr(ws),
+                                                      nb, _stream(stream)))
+
+
+def moe_gemm_gate_up_bwd(s, dgu, x_rows, row_token, offsets, w_gate, w_up, dx_perm, dw_gate, dw_up, accumulate_dw, ws,
+                         ws_bytes=None, stream=None):
+    """row_token None: x_rows is x_perm; else x [T,H] read through row_token."""
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_gemm_gate_up_bwd",
+           lib.moe_gemm_gate_up_bwd(s, _ptr(dgu), _ptr(x_rows), _ptr(row_token), _ptr(offsets), _ptr(w_gate),
+                                    _ptr(w_up), _ptr(dx_perm), _ptr(dw_gate), _ptr(dw_up), int(accumulate_dw),
+                                    _ptr(ws), nb, _stream(stream)))
+
+
 def moe_gemm_gate_up_wgrad_gathered(s, dgu, x, row_token, offsets, dw_gate, dw_up, accumulate_dw, ws, ws_bytes=None,
                                     stream=None):
     nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
@@ -300,10 +320,12 @@ class MoEStage:
         return b["y"]
 
     def backward(self, dy, accumulate_dw: bool = False, stream=None, aux_stream=None):
-        """Backward of the last forward. With ``aux_stream`` (a second stream,
-        default priority) the weight-gradient GEMMs run there while the
-        data-gradient GEMMs run on ``stream``: each fills the other's tail.
-        The results are the same bits either way."""
+        """Backward of the last forward. By default each data-gradient GEMM
+        and the weight gradient that reads the same inputs run in one launch
+        (moe_gemm_down_bwd, moe_gemm_gate_up_bwd). With ``aux_stream`` (a
+        second stream, default priority) the six GEMMs run one per launch,
+        the weight gradients there and the data gradients on ``stream``. The
+        results are the same bits either way."""
         self._alloc_bwd()
         b, s = self.buf, self.s
         w_gate, w_up, w_down = self.w
@@ -313,32 +335,35 @@ class MoEStage:
             moe_grouped_gemm_bwd(s, b["do_perm"], b["x_perm"], b["g"], b["u"], b["a"], b["offsets"], w_gate, w_up,
                                  w_down, b["dx_perm"], b["dw_gate"], b["dw_up"], b["dw_down"], acc, self.ws,
                                  stream=stream)
-        else:
-            main = torch.cuda.current_stream() if stream is None else stream
-            wg = main if aux_stream is None else aux_stream  # the weight-gradient GEMMs' stream
+        elif aux_stream is None:
             if "dgu" not in b:
                 b["dgu"] = torch.empty(self.T * self.k, 2 * self.I, dtype=self.dtype, device=self.ws.device)
-            if aux_stream is not None:
-                forked = torch.cuda.Event()
-                forked.record(main)
-                aux_stream.wait_event(forked)
-            moe_gemm_down_wgrad(s, b["do_perm"], b["a"], b["offsets"], b["dw_down"], acc, self.ws, stream=wg)
+            moe_gemm_down_bwd(s, b["do_perm"], b["a"], b["offsets"], w_down, b["g"], b["u"], b["dgu"], b["dw_down"],
+                              acc, self.ws, stream=stream)
+            moe_gemm_gate_up_bwd(s, b["dgu"], self.x, b["row_token"], b["offsets"], w_gate, w_up, b["dx_perm"],
+                                 b["dw_gate"], b["dw_up"], acc, self.ws, stream=stream)
+        else:
+            main = torch.cuda.current_stream() if stream is None else stream
+            if "dgu" not in b:
+                b["dgu"] = torch.empty(self.T * self.k, 2 * self.I, dtype=self.dtype, device=self.ws.device)
+            forked = torch.cuda.Event()
+            forked.record(main)
+            aux_stream.wait_event(forked)
+            moe_gemm_down_wgrad(s, b["do_perm"], b["a"], b["offsets"], b["dw_down"], acc, self.ws, stream=aux_stream)
             moe_gemm_down_dgrad(s, b["do_perm"], b["offsets"], w_down, b["g"], b["u"], b["dgu"], main)
-            if aux_stream is not None:
-                dgu_ready = torch.cuda.Event()
-                dgu_ready.record(main)
-                aux_stream.wait_event(dgu_ready)
+            dgu_ready = torch.cuda.Event()
+            dgu_ready.record(main)
+            aux_stream.wait_event(dgu_ready)
             if self.gather_fused:
                 moe_gemm_gate_up_wgrad_gathered(s, b["dgu"], self.x, b["row_token"], b["offsets"], b["dw_gate"],
-                                                b["dw_up"], acc, self.ws, stream=wg)
+                                                b["dw_up"], acc, self.ws, stream=aux_stream)
             else:
                 moe_gemm_gate_up_wgrad(s, b["dgu"], b["x_perm"], b["offsets"], b["dw_gate"], b["dw_up"], acc,
-                                       self.ws, stream=wg)
+                                       self.ws, stream=aux_stream)
             moe_gemm_gate_up_dgrad(s, b["dgu"], b["offsets"], w_gate, w_up, b["dx_perm"], main)
-            if aux_stream is not None:
-                joined = torch.cuda.Event()
-                joined.record(aux_stream)
-                main.wait_event(joined)
+            joined = torch.cuda.Event()
+            joined.record(aux_stream)
+            main.wait_event(joined)
         moe_unpermute_sum(s, b["dx_perm"], b["flat_to_sorted"], b["dx"], stream)
         moe_route_bwd(s, b["d_topk_w"], b["topk_w"], b["topk_idx"], b["d_logits"], stream)
         return b["dx"]

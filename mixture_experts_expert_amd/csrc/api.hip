@@ -300,11 +300,70 @@ moe_status moe_grouped_gemm_bwd(moe_shape s, const void* do_perm, const void* x_
   const WsLayout l = moe::ws_layout(s);
   if (ws_bytes < l.total) return MOE_EWORKSPACE;
   void* dgu = static_cast<char*>(ws) + l.dgu_off;
-  if ((st = moe_gemm_down_dgrad(s, do_perm, offsets, w_down, g, u, dgu, stream)) != MOE_OK) return st;
-  if ((st = moe_gemm_down_wgrad(s, do_perm, a, offsets, dw_down, accumulate_dw, ws, ws_bytes, stream)) != MOE_OK)
+  if ((st = moe_gemm_down_bwd(s, do_perm, a, offsets, w_down, g, u, dgu, dw_down, accumulate_dw, ws, ws_bytes,
+                              stream)) != MOE_OK)
     return st;
-  if ((st = moe_gemm_gate_up_dgrad(s, dgu, offsets, w_gate, w_up, dx_perm, stream)) != MOE_OK) return st;
-  return moe_gemm_gate_up_wgrad(s, dgu, x_perm, offsets, dw_gate, dw_up, accumulate_dw, ws, ws_bytes, stream);
+  return moe_gemm_gate_up_bwd(s, dgu, x_perm, nullptr, offsets, w_gate, w_up, dx_perm, dw_gate, dw_up, accumulate_dw,
+                              ws, ws_bytes, stream);
+}
+
+moe_status moe_gemm_down_bwd(moe_shape s, const void* do_perm, const void* a, const int32_t* offsets,
+                             const void* w_down, const void* g, const void* u, void* dgu, float* dw_down,
+                             int accumulate_dw, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(do_perm, a, offsets, w_down, g, u, dgu, dw_down, ws)) return MOE_EINVAL;
+  if (accumulate_dw != 0 && accumulate_dw != 1) return MOE_EINVAL;
+  const WsLayout l = moe::ws_layout(s);
+  if (ws_bytes < l.total) return MOE_EWORKSPACE;
+  moe::GemmArgs gd{};
+  gd.offsets = offsets;
+  gd.a = do_perm;
+  gd.b0 = w_down;
+  gd.g_in = g;
+  gd.u_in = u;
+  gd.out0 = dgu;
+  moe::GemmArgs gw{};
+  gw.part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.part_off);
+  gw.offsets = offsets;
+  gw.a = do_perm;
+  gw.b0 = a;
+  gw.dw0 = dw_down;
+  gw.accumulate = accumulate_dw;
+  return from_hip(moe::launch_gemm_pair(moe::GEMM_DGRAD_DOWN, moe::GEMM_WGRAD_DOWN, s, gd, gw, stream));
+}
+
+moe_status moe_gemm_gate_up_bwd(moe_shape s, const void* dgu, const void* x_rows, const int32_t* row_token,
+                                const int32_t* offsets, const void* w_gate, const void* w_up, void* dx_perm,
+                                float* dw_gate, float* dw_up, int accumulate_dw, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(dgu, x_rows, offsets, w_gate, w_up, dx_perm, dw_gate, dw_up, ws)) return MOE_EINVAL;
+  if (accumulate_dw != 0 && accumulate_dw != 1) return MOE_EINVAL;
+  const WsLayout l = moe::ws_layout(s);
+  if (ws_bytes < l.total) return MOE_EWORKSPACE;
+  // Gathered x and row_token are addressed with 32-bit byte offsets.
+  if (row_token != nullptr &&
+      (static_cast<int64_t>(s.T) * s.H * (s.dtype == MOE_BF16 ? 2 : 4) >= (static_cast<int64_t>(1) << 31) ||
+       4 * (static_cast<int64_t>(s.T) * s.k + 256) >= (static_cast<int64_t>(1) << 31)))
+    return MOE_EUNSUPPORTED;
+  moe::GemmArgs gd{};
+  gd.offsets = offsets;
+  gd.a = dgu;
+  gd.b0 = w_gate;
+  gd.b1 = w_up;
+  gd.out0 = dx_perm;
+  moe::GemmArgs gw{};
+  gw.part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.part_off);
+  gw.offsets = offsets;
+  gw.a = dgu;
+  gw.b0 = x_rows;
+  gw.row_token = row_token;
+  gw.dw0 = dw_gate;
+  gw.dw1 = dw_up;
+  gw.accumulate = accumulate_dw;
+  return from_hip(moe::launch_gemm_pair(moe::GEMM_DGRAD_GATEUP, moe::GEMM_WGRAD_GATEUP, s, gd, gw, stream));
 }
 
 moe_status moe_unpermute_sum(moe_shape s, const void* dx_perm, const int32_t* flat_to_sorted, void* dx,

@@ -328,22 +328,48 @@ __device__ __forceinline__ int split_len(int steps, int chunks) { return (steps 
 // rows through P.row_token and may skip storing G and U; WGRAD_GATEUP reads
 // its B k-rows (x) through P.row_token; DOWN scales its output rows by
 // P.row_weight.
+// The workgroup's LDS. The stages are separate objects: with the stage of
+// every access known at compile time, the compiler sees that loads landing in
+// one stage do not alias reads of another and does not wait for them before
+// reading.
+struct Smem {
+  bf16_t (&lds0)[STAGE];
+  bf16_t (&lds1)[STAGE];
+  bf16_t (&lds2)[STAGE];
+  bf16_t (&lds3)[STAGE];
+  int (&tstart)[1025];  // grouped-M: first m-tile of each expert; grouped-K: first tile
+  int (&pstart)[1025];  // grouped-K: first partial tile of each expert
+  int (&wstart)[1025];  // grouped-K: work (k-steps) before each expert's tiles
+  int (&part)[NT];
+  int (&eoff)[1025];    // offsets[0..E]: read at every tile start, from LDS rather than
+                        // through a vector load whose wait would drain the prefetches
+};
+#define MOE_GEMM_SMEM                                          \
+  __shared__ __attribute__((aligned(16))) bf16_t lds0[STAGE]; \
+  __shared__ __attribute__((aligned(16))) bf16_t lds1[STAGE]; \
+  __shared__ __attribute__((aligned(16))) bf16_t lds2[STAGE]; \
+  __shared__ __attribute__((aligned(16))) bf16_t lds3[STAGE]; \
+  __shared__ int tstart[1025];                                 \
+  __shared__ int pstart[1025];                                 \
+  __shared__ int wstart[1025];                                 \
+  __shared__ int part[NT];                                     \
+  __shared__ int eoff[1025];                                   \
+  const Smem sm{lds0, lds1, lds2, lds3, tstart, pstart, wstart, part, eoff};
+
+// Every tile of one GEMM that workgroup `bid` of `nblk` (a multiple of 8)
+// owns, start to finish: on return every load and store this workgroup
+// issued has completed and its waves are past a barrier.
 template <int MODE, bool FUSED>
-__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(
-    Params P) {
-  // The stages as separate objects: with the stage of every access known at
-  // compile time, the compiler sees that loads landing in one stage do not
-  // alias reads of another and does not wait for them before reading.
-  __shared__ __attribute__((aligned(16))) bf16_t lds0[STAGE];
-  __shared__ __attribute__((aligned(16))) bf16_t lds1[STAGE];
-  __shared__ __attribute__((aligned(16))) bf16_t lds2[STAGE];
-  __shared__ __attribute__((aligned(16))) bf16_t lds3[STAGE];
-  __shared__ int tstart[1025];  // grouped-M: first m-tile of each expert; grouped-K: first tile
-  __shared__ int pstart[1025];  // grouped-K: first partial tile of each expert
-  __shared__ int wstart[1025];  // grouped-K: work (k-steps) before each expert's tiles
-  __shared__ int part[NT];
-  __shared__ int eoff[1025];    // offsets[0..E]: read at every tile start, from LDS rather than
-                                // through a vector load whose wait would drain the prefetches
+__device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const int nblk, const Smem& sm) {
+  bf16_t (&lds0)[STAGE] = sm.lds0;
+  bf16_t (&lds1)[STAGE] = sm.lds1;
+  bf16_t (&lds2)[STAGE] = sm.lds2;
+  bf16_t (&lds3)[STAGE] = sm.lds3;
+  int (&tstart)[1025] = sm.tstart;
+  int (&pstart)[1025] = sm.pstart;
+  int (&wstart)[1025] = sm.wstart;
+  int (&part)[NT] = sm.part;
+  int (&eoff)[1025] = sm.eoff;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -404,7 +430,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
       st[j] = e < E ? (P.offsets[e + 1] - P.offsets[e] + BK - 1) / BK : 0;
     }
     expert_scan(st, wstart, part, E, tid);
-    kcap = split_cap(tpe * wstart[E], gridDim.x);
+    kcap = split_cap(tpe * wstart[E], nblk);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       c[j] = tid * 4 + j < E ? split_chunks(st[j], kcap) : 0;
@@ -423,9 +449,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   // Tile range of this workgroup's XCD: an eighth of the tiles (grouped-M:
   // all tiles cost the same) or of the work (grouped-K: tiles of one expert
   // cost the same, those of different experts do not).
-  const int xcd = blockIdx.x & 7;
-  const int slot = blockIdx.x >> 3;
-  const int nslots = gridDim.x >> 3;
+  const int xcd = bid & 7;
+  const int slot = bid >> 3;
+  const int nslots = nblk >> 3;
   auto tile_at = [&](int x8) -> int {
     if constexpr (!grouped_k(MODE)) {
       return static_cast<int>((static_cast<int64_t>(total) * x8) / 8);
@@ -1130,6 +1156,29 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
   }
 }
 
+template <int MODE, bool FUSED>
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(
+    Params P) {
+  MOE_GEMM_SMEM
+  gemm_tiles<MODE, FUSED>(P, blockIdx.x, gridDim.x, sm);
+}
+
+// Two independent GEMMs of the backward in one persistent launch: a data
+// gradient (A) and the weight gradient that reads the same inputs (B). Every
+// workgroup runs its share of A, then its share of B: a workgroup that is
+// done with A starts on B at once instead of waiting for A's slowest one,
+// so only the launch's end has a tail. (Half the workgroups starting on B
+// was measured too and was slower: each XCD then works on tiles twice as
+// far apart, whose operands share its L2 less.)
+template <int MA, int MB, bool FB>
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void
+grouped_gemm_pair_kernel(Params PA, Params PB) {
+  MOE_GEMM_SMEM
+  gemm_tiles<MA, false>(PA, blockIdx.x, gridDim.x, sm);
+  __syncthreads();  // the tables and stages are B's now
+  gemm_tiles<MB, FB>(PB, blockIdx.x, gridDim.x, sm);
+}
+
 // Adds the partial tiles of every split expert into its weight gradient, in
 // chunk order (chunk 0 is already there). Block b takes the split tiles b,
 // b + grid, ...; the split plan is recomputed from the offsets exactly as the
@@ -1199,6 +1248,13 @@ __global__ __launch_bounds__(NT) void wgrad_reduce_kernel(Params P, int gemm_gri
   }
 }
 
+template <int MODE>
+hipError_t launch_wgrad_reduce(const Params& p, int grid, hipStream_t st) {
+  // At most 2 * grid split tiles, two per reduction block at most.
+  wgrad_reduce_kernel<MODE><<<grid, NT, 0, st>>>(p, grid);
+  return hipGetLastError();
+}
+
 int persistent_grid() {
   static int cached = 0;
   if (cached == 0) {
@@ -1218,25 +1274,21 @@ hipError_t run(const Params& p, hipStream_t st) {
   hipError_t err = hipGetLastError();
   if constexpr (grouped_k(MODE)) {
     if (err != hipSuccess) return err;
-    // At most 2 * grid split tiles, two per reduction block at most.
-    wgrad_reduce_kernel<MODE><<<grid, NT, 0, st>>>(p, grid);
-    err = hipGetLastError();
+    err = launch_wgrad_reduce<MODE>(p, grid, st);
   }
   return err;
 }
 
-}  // namespace
-
-int gemm_grid() { return persistent_grid(); }
-
-int64_t wgrad_part_tiles(const moe_shape& s) {
-  if (s.dtype != MOE_BF16) return 0;
-  const int64_t tpe_max = static_cast<int64_t>(ceil_div(2 * s.I, BM)) * ceil_div(s.H, BN);
-  const int64_t steps = static_cast<int64_t>(s.T) * s.k / BK + s.E;  // >= the sum over experts of ceil(n_e / BK)
-  return std::min<int64_t>(2 * static_cast<int64_t>(persistent_grid()), tpe_max * (steps / kMinChunkSteps));
+template <int MA, int MB, bool FB = false>
+hipError_t run_pair(const Params& pa, const Params& pb, hipStream_t st) {
+  const int grid = persistent_grid();
+  grouped_gemm_pair_kernel<MA, MB, FB><<<grid, NT, 0, st>>>(pa, pb);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_wgrad_reduce<MB>(pb, grid, st);
 }
 
-hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g, hipStream_t st) {
+Params make_params(const moe_shape& s, const GemmArgs& g) {
   Params p{};
   p.T = s.T;
   p.M = s.T * s.k;
@@ -1258,6 +1310,22 @@ hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g
   p.part = g.part;
   p.row_token = g.row_token;
   p.row_weight = g.row_weight;
+  return p;
+}
+
+}  // namespace
+
+int gemm_grid() { return persistent_grid(); }
+
+int64_t wgrad_part_tiles(const moe_shape& s) {
+  if (s.dtype != MOE_BF16) return 0;
+  const int64_t tpe_max = static_cast<int64_t>(ceil_div(2 * s.I, BM)) * ceil_div(s.H, BN);
+  const int64_t steps = static_cast<int64_t>(s.T) * s.k / BK + s.E;  // >= the sum over experts of ceil(n_e / BK)
+  return std::min<int64_t>(2 * static_cast<int64_t>(persistent_grid()), tpe_max * (steps / kMinChunkSteps));
+}
+
+hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g, hipStream_t st) {
+  const Params p = make_params(s, g);
   switch (mode) {
     case GEMM_GATEUP: return g.row_token ? run<GATEUP, true>(p, st) : run<GATEUP>(p, st);
     case GEMM_DOWN: return g.row_weight ? run<DOWN, true>(p, st) : run<DOWN>(p, st);
@@ -1266,6 +1334,16 @@ hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g
     case GEMM_WGRAD_DOWN: return run<WGRAD_DOWN>(p, st);
     case GEMM_WGRAD_GATEUP: return g.row_token ? run<WGRAD_GATEUP, true>(p, st) : run<WGRAD_GATEUP>(p, st);
   }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_pair_bf16(GemmMode ma, GemmMode mb, const moe_shape& s, const GemmArgs& ga, const GemmArgs& gb,
+                                 hipStream_t st) {
+  const Params pa = make_params(s, ga), pb = make_params(s, gb);
+  if (ma == GEMM_DGRAD_DOWN && mb == GEMM_WGRAD_DOWN) return run_pair<DGRAD_DOWN, WGRAD_DOWN>(pa, pb, st);
+  if (ma == GEMM_DGRAD_GATEUP && mb == GEMM_WGRAD_GATEUP)
+    return gb.row_token ? run_pair<DGRAD_GATEUP, WGRAD_GATEUP, true>(pa, pb, st)
+                        : run_pair<DGRAD_GATEUP, WGRAD_GATEUP>(pa, pb, st);
   return hipErrorInvalidValue;
 }
 

@@ -141,5 +141,16 @@ hipError_t launch_gemm_f32(GemmMode mode, const moe_shape& s, const GemmArgs& a,
 inline hipError_t launch_gemm(GemmMode mode, const moe_shape& s, const GemmArgs& a, hipStream_t st) {
   return s.dtype == MOE_BF16 ? launch_gemm_bf16(mode, s, a, st) : launch_gemm_f32(mode, s, a, st);
 }
+// A data gradient and a weight gradient that read the same inputs, in one
+// launch for bf16 (DGRAD_DOWN with WGRAD_DOWN, DGRAD_GATEUP with
+// WGRAD_GATEUP); f32 runs them one after the other.
+hipError_t launch_gemm_pair_bf16(GemmMode ma, GemmMode mb, const moe_shape& s, const GemmArgs& ga, const GemmArgs& gb,
+                                 hipStream_t st);
+inline hipError_t launch_gemm_pair(GemmMode ma, GemmMode mb, const moe_shape& s, const GemmArgs& ga,
+                                   const GemmArgs& gb, hipStream_t st) {
+  if (s.dtype == MOE_BF16) return launch_gemm_pair_bf16(ma, mb, s, ga, gb, st);
+  const hipError_t err = launch_gemm_f32(ma, s, ga, st);
+  return err != hipSuccess ? err : launch_gemm_f32(mb, s, gb, st);
+}
 
 }  // namespace moe

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(B):
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(B.lib, n), n
 
@@ -106,6 +106,13 @@ def test_fused_forward_validation(B):
     assert B.lib.moe_forward_fused(s, *A, need - 1, None) == 3
     assert B.lib.moe_forward_fused(s, F, F, None, F, F, F, F, F, F, F, F, F, F, F, None, F, F, F, F, need, None) == 1
     # gathered gate/up wgrad: row_token required, accumulate 0/1, workspace, 32-bit offsets
+    # paired backward GEMMs: required pointers (row_token optional), accumulate, workspace
+    assert B.lib.moe_gemm_down_bwd(s, F, F, F, F, F, F, F, None, 0, F, need, None) == 1
+    assert B.lib.moe_gemm_down_bwd(s, F, F, F, F, F, F, F, F, 3, F, need, None) == 1
+    assert B.lib.moe_gemm_down_bwd(s, F, F, F, F, F, F, F, F, 0, F, need - 1, None) == 3
+    assert B.lib.moe_gemm_gate_up_bwd(s, F, None, None, F, F, F, F, F, F, 0, F, need, None) == 1
+    assert B.lib.moe_gemm_gate_up_bwd(s, F, F, None, F, F, F, F, F, F, 0, F, need - 1, None) == 3
+    assert B.lib.moe_gemm_gate_up_bwd(big, F, F, F, F, F, F, F, F, F, 0, F, B.moe_workspace_bytes(big), None) == 2
     W = B.lib.moe_gemm_gate_up_wgrad_gathered
     assert W(s, F, F, None, F, F, F, 0, F, need, None) == 1
     assert W(s, F, F, F, F, F, F, 2, F, need, None) == 1

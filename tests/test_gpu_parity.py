@@ -126,3 +126,47 @@ def test_two_stream_backward_same_bits(cfg):
                 assert torch.allclose(st.buf[n], ref[n] * 2, rtol=1e-6, atol=1e-6), (n, accumulate)
             else:
                 assert torch.equal(st.buf[n], ref[n]), (n, accumulate)
+
+
+@pytest.mark.parametrize("cfg", [SMALL[1], SMALL[2], SMALL[3], SPLIT_K, synth.CONFIGS["qwen3_30b_a3b_train"]],
+                         ids=lambda c: c.name)
+def test_paired_backward_gemms_same_bits(cfg):
+    """moe_gemm_down_bwd and moe_gemm_gate_up_bwd (a data gradient and a
+    weight gradient per launch) against the four single-GEMM calls on the
+    same inputs: the same bits, overwriting and accumulating."""
+    from mixture_experts_expert_amd import binding as B
+    U.say(f"[paired backward GEMMs] {cfg}")
+    inp = synth.make_inputs(cfg, seed=4, with_dy=True)
+    d = U.DevInputs(inp)
+    st = U.run_stage(d, True)
+    b, s = st.buf, st.s
+    wg, wu, wd = d.t["w_gate"], d.t["w_up"], d.t["w_down"]
+    M = b["a"].shape[0]
+    out = {}
+    for mode in ("single", "paired"):
+        o = dict(dgu=torch.empty(M, 2 * cfg.I, dtype=b["a"].dtype, device="cuda"),
+                 dx_perm=torch.empty_like(b["dx_perm"]),
+                 dw_gate=torch.full_like(b["dw_gate"], 0.5), dw_up=torch.full_like(b["dw_up"], -0.25),
+                 dw_down=torch.full_like(b["dw_down"], 0.125))
+        for acc in (0, 1):
+            if mode == "single":
+                B.moe_gemm_down_dgrad(s, b["do_perm"], b["offsets"], wd, b["g"], b["u"], o["dgu"])
+                B.moe_gemm_down_wgrad(s, b["do_perm"], b["a"], b["offsets"], o["dw_down"], acc, st.ws)
+                B.moe_gemm_gate_up_dgrad(s, o["dgu"], b["offsets"], wg, wu, o["dx_perm"])
+                B.moe_gemm_gate_up_wgrad(s, o["dgu"], b["x_perm"], b["offsets"], o["dw_gate"], o["dw_up"], acc, st.ws)
+            else:
+                B.moe_gemm_down_bwd(s, b["do_perm"], b["a"], b["offsets"], wd, b["g"], b["u"], o["dgu"],
+                                    o["dw_down"], acc, st.ws)
+                B.moe_gemm_gate_up_bwd(s, o["dgu"], b["x_perm"], None, b["offsets"], wg, wu, o["dx_perm"],
+                                       o["dw_gate"], o["dw_up"], acc, st.ws)
+            torch.cuda.synchronize()
+            out[(mode, acc)] = {n: t.clone() for n, t in o.items()}
+    for acc in (0, 1):
+        for n in out[("single", acc)]:
+            x, y = out[("single", acc)][n], out[("paired", acc)][n]
+            if x.dtype == torch.bfloat16:
+                x, y = x.view(torch.int16), y.view(torch.int16)
+            assert torch.equal(x, y), (n, acc)
+    # and the stage's own backward (moe_grouped_gemm_bwd chains the paired calls)
+    for n in ["dx_perm", "dw_gate", "dw_up", "dw_down"]:
+        assert torch.equal(b[n], out[("single", 0)][n]), n
