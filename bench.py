@@ -358,7 +358,27 @@ def main() -> int:
     infer = None
     if not args.timed_only:
         infer = {"unfused": round(time_fn(infer_unfused), 4), "fused": round(time_fn(infer_fused), 4)}
-        log(f"inference forward: unfused {infer['unfused']:.3f} ms, fused {infer['fused']:.3f} ms")
+        # The same forward with E4M3 weights and activations (weights quantised
+        # once, outside the timing; x and the expert activations every call).
+        w8 = B.FP8Weights(wg, wu, wd)
+        u8 = torch.uint8
+        f8 = dict(xq=torch.empty(cfg.T, cfg.H, dtype=u8, device="cuda"), x_e8=torch.empty(cfg.M, dtype=u8, device="cuda"),
+                  aq=torch.empty(cfg.M, cfg.I, dtype=u8, device="cuda"), a_e8=torch.empty(cfg.M, dtype=u8, device="cuda"))
+
+        def infer_fp8():
+            B.moe_forward_fused_fp8(s, x, wr, bias, w8.gate[0], w8.gate[1], w8.up[0], w8.up[1], w8.down[0],
+                                    w8.down[1], b["logits"], b["topk_idx"], b["topk_w"], b["counts"], b["offsets"],
+                                    b["sorted_to_flat"], b["flat_to_sorted"], fb["row_token"], fb["row_weight"],
+                                    f8["xq"], f8["x_e8"], b["a"], f8["aq"], f8["a_e8"], b["o_perm"], b["y"], st.ws)
+
+        infer["fp8"] = round(time_fn(infer_fp8), 4)
+        gate_up8 = lambda: B.moe_gemm_gate_up_fp8(s, f8["xq"], f8["x_e8"], fb["row_token"], b["offsets"], w8.gate[0],  # noqa: E731
+                                                  w8.gate[1], w8.up[0], w8.up[1], b["a"])
+        down8 = lambda: B.moe_gemm_down_fp8(s, f8["aq"], f8["a_e8"], b["offsets"], w8.down[0], w8.down[1],  # noqa: E731
+                                            fb["row_weight"], b["o_perm"])
+        infer["fp8_gate_up"] = round(time_fn(gate_up8, reps=5), 4)
+        infer["fp8_down"] = round(time_fn(down8, reps=5), 4)
+        log(f"inference forward: {infer}")
 
     flops = gemm_flops(cfg)
     nbytes = alg_bytes(cfg)

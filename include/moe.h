@@ -8,6 +8,9 @@
  *   inference (gather and routing weights fused into the GEMMs):
  *             moe_forward_fused = moe_route -> moe_permute_fused ->
  *             moe_gemm_gate_up_gathered -> moe_gemm_down_weighted -> moe_unpermute_sum
+ *   fp8 inference: moe_forward_fused_fp8 = moe_route -> moe_permute_fused ->
+ *             moe_quantize_fp8_rows (x) -> moe_gemm_gate_up_fp8 ->
+ *             moe_quantize_fp8_rows (a) -> moe_gemm_down_fp8 -> moe_unpermute_sum
  *   training without x_perm (the gather fused into both GEMMs that read x):
  *             moe_route -> moe_permute_fused -> moe_gemm_gate_up_gathered ->
  *             moe_gemm_down -> moe_combine; moe_combine_bwd -> moe_gemm_down_dgrad,
@@ -277,6 +280,59 @@ moe_status moe_forward_fused(moe_shape s, const void* x, const void* w_router, c
                              int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
                              int32_t* sorted_to_flat, int32_t* flat_to_sorted, int32_t* row_token, float* row_weight,
                              void* a, void* o_perm, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- fp8 inference forward (the quantised-weight path of unsloth PR #3812,
+ * "[MoE] Improve moe kernels for unsloth fine tuning", and the 4-bit loading
+ * of the sourcepulse summary, "Highlighted Details", taken to the 8-bit
+ * floats gfx950's matrix cores multiply natively). Both GEMM operands are
+ * OCP E4M3 codes (bias 7, largest finite 448, 0x7F/0xFF NaN); every row of
+ * an operand carries one power-of-two scale as an E8M0 byte c (2^(c-127)).
+ * The GEMMs multiply codes and apply both scales inside the matrix core, so
+ * a product is exactly dequant(a) * dequant(w), summed in fp32. */
+
+/* Rows [rows, K] of bf16 -> E4M3 codes q [rows, K] and one scale per row.
+ * Scale 2^X with X = floor(log2(max |row|)) - 8, clamped to [-127, 127]
+ * (-127 for an all-zero row); q = E4M3(clamp(x / 2^X, -448, 448)), rounded
+ * to nearest, ties to even. e8 layout: [rows] when flat_to_sorted is NULL;
+ * otherwise [rows * k] in sorted order, row r's scale written at
+ * flat_to_sorted[r * k + j] for every j < k (x's scales for the gathered
+ * gate/up GEMM). K % 8 == 0 (MOE_EINVAL otherwise). Weights are quantised
+ * once with the same call: w_gate, w_up [E,I,H] as E*I rows, w_down [E,H,I]
+ * as E*H rows (one scale per output channel). */
+moe_status moe_quantize_fp8_rows(int32_t rows, int32_t K, const void* in, uint8_t* q, uint8_t* e8,
+                                 const int32_t* flat_to_sorted, int32_t k, hipStream_t stream);
+
+/* Gathered gate/up GEMM in fp8 with the SwiGLU epilogue, storing a only:
+ *   a[p,:] = bf16(silu(g) * u),  g = deq(xq[row_token[p]]) deq(Wg[e])^T,  u likewise
+ * xq [T,H] codes with x_e8 [T*k] (sorted order, from moe_quantize_fp8_rows
+ * with flat_to_sorted); wq_gate, wq_up [E,I,H] with w_gate_e8, w_up_e8
+ * [E,I]; a [T*k,I] bf16. Requires shape.dtype MOE_BF16, H and I multiples of
+ * 64 and T*H < 2^31 (MOE_EUNSUPPORTED otherwise). */
+moe_status moe_gemm_gate_up_fp8(moe_shape s, const uint8_t* xq, const uint8_t* x_e8, const int32_t* row_token,
+                                const int32_t* offsets, const uint8_t* wq_gate, const uint8_t* w_gate_e8,
+                                const uint8_t* wq_up, const uint8_t* w_up_e8, void* a, hipStream_t stream);
+
+/* Weighted down GEMM in fp8:
+ *   o_perm[p,:] = bf16(row_weight[p] * deq(aq[p]) deq(Wd[e])^T)
+ * aq [T*k,I] codes with a_e8 [T*k]; wq_down [E,H,I] with w_down_e8 [E,H];
+ * o_perm [T*k,H] bf16. Same shape limits as moe_gemm_gate_up_fp8. */
+moe_status moe_gemm_down_fp8(moe_shape s, const uint8_t* aq, const uint8_t* a_e8, const int32_t* offsets,
+                             const uint8_t* wq_down, const uint8_t* w_down_e8, const float* row_weight, void* o_perm,
+                             hipStream_t stream);
+
+/* The fp8 inference forward in one call: moe_route, moe_permute_fused,
+ * moe_quantize_fp8_rows (x -> xq [T,H], x_e8 [T*k] sorted),
+ * moe_gemm_gate_up_fp8 (a [T*k,I] bf16), moe_quantize_fp8_rows (a -> aq
+ * [T*k,I], a_e8 [T*k]), moe_gemm_down_fp8 (o_perm) and moe_unpermute_sum
+ * (y [T,H]). Weights come quantised. Every buffer is caller-owned;
+ * logit_bias may be NULL; ws of ws_bytes >= moe_workspace_bytes(s). */
+moe_status moe_forward_fused_fp8(moe_shape s, const void* x, const void* w_router, const float* logit_bias,
+                                 const uint8_t* wq_gate, const uint8_t* w_gate_e8, const uint8_t* wq_up,
+                                 const uint8_t* w_up_e8, const uint8_t* wq_down, const uint8_t* w_down_e8,
+                                 float* logits, int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                                 int32_t* sorted_to_flat, int32_t* flat_to_sorted, int32_t* row_token,
+                                 float* row_weight, uint8_t* xq, uint8_t* x_e8, void* a, uint8_t* aq, uint8_t* a_e8,
+                                 void* o_perm, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* A static, human-readable name for a status code. */
 const char* moe_status_string(moe_status status);

@@ -63,6 +63,10 @@ _SIGS = {
     "moe_permute_fused": ([moe_shape, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "moe_gemm_gate_up_gathered": ([moe_shape, _P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_gemm_down_weighted": ([moe_shape, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "moe_quantize_fp8_rows": ([ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, _P], ctypes.c_int),
+    "moe_gemm_gate_up_fp8": ([moe_shape] + [_P] * 9 + [_P], ctypes.c_int),
+    "moe_gemm_down_fp8": ([moe_shape] + [_P] * 7 + [_P], ctypes.c_int),
+    "moe_forward_fused_fp8": ([moe_shape] + [_P] * 26 + [ctypes.c_size_t, _P], ctypes.c_int),
     "moe_gemm_down_bwd": ([moe_shape] + [_P] * 8 + [ctypes.c_int, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "moe_gemm_gate_up_bwd": ([moe_shape] + [_P] * 9 + [ctypes.c_int, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "moe_gemm_gate_up_wgrad_gathered": ([moe_shape, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_size_t, _P],
@@ -203,6 +207,50 @@ def moe_gemm_gate_up_gathered(s, x, row_token, offsets, w_gate, w_up, g, u, a, s
     _check("moe_gemm_gate_up_gathered", lib.moe_gemm_gate_up_gathered(
         s, _ptr(x), _ptr(row_token), _ptr(offsets), _ptr(w_gate), _ptr(w_up), _ptr(g), _ptr(u), _ptr(a),
         _stream(stream)))
+
+
+def moe_quantize_fp8_rows(rows, K, x, q, e8, flat_to_sorted=None, k=0, stream=None):
+    _check("moe_quantize_fp8_rows", lib.moe_quantize_fp8_rows(int(rows), int(K), _ptr(x), _ptr(q), _ptr(e8),
+                                                              _ptr(flat_to_sorted), int(k), _stream(stream)))
+
+
+def moe_gemm_gate_up_fp8(s, xq, x_e8, row_token, offsets, wq_gate, w_gate_e8, wq_up, w_up_e8, a, stream=None):
+    _check("moe_gemm_gate_up_fp8", lib.moe_gemm_gate_up_fp8(s, _ptr(xq), _ptr(x_e8), _ptr(row_token), _ptr(offsets),
+                                                            _ptr(wq_gate), _ptr(w_gate_e8), _ptr(wq_up),
+                                                            _ptr(w_up_e8), _ptr(a), _stream(stream)))
+
+
+def moe_gemm_down_fp8(s, aq, a_e8, offsets, wq_down, w_down_e8, row_weight, o_perm, stream=None):
+    _check("moe_gemm_down_fp8", lib.moe_gemm_down_fp8(s, _ptr(aq), _ptr(a_e8), _ptr(offsets), _ptr(wq_down),
+                                                      _ptr(w_down_e8), _ptr(row_weight), _ptr(o_perm),
+                                                      _stream(stream)))
+
+
+def moe_forward_fused_fp8(s, x, w_router, logit_bias, wq_gate, w_gate_e8, wq_up, w_up_e8, wq_down, w_down_e8, logits,
+                          topk_idx, topk_w, counts, offsets, sorted_to_flat, flat_to_sorted, row_token, row_weight, xq,
+                          x_e8, a, aq, a_e8, o_perm, y, ws, ws_bytes=None, stream=None):
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    args = [x, w_router, logit_bias, wq_gate, w_gate_e8, wq_up, w_up_e8, wq_down, w_down_e8, logits, topk_idx,
+            topk_w, counts, offsets, sorted_to_flat, flat_to_sorted, row_token, row_weight, xq, x_e8, a, aq, a_e8,
+            o_perm, y, ws]
+    _check("moe_forward_fused_fp8", lib.moe_forward_fused_fp8(s, *[_ptr(t) for t in args], nb, _stream(stream)))
+
+
+class FP8Weights:
+    """Expert weights quantised once to E4M3 with a scale per output channel
+    (moe_quantize_fp8_rows): codes gate/up [E,I,H], down [E,H,I] (uint8)
+    and their E8M0 scales [E,I], [E,H]."""
+
+    def __init__(self, w_gate, w_up, w_down, stream=None):
+        E, I, H = w_gate.shape
+        dev = w_gate.device
+        u8 = torch.uint8
+        self.gate = (torch.empty(E, I, H, dtype=u8, device=dev), torch.empty(E, I, dtype=u8, device=dev))
+        self.up = (torch.empty(E, I, H, dtype=u8, device=dev), torch.empty(E, I, dtype=u8, device=dev))
+        self.down = (torch.empty(E, H, I, dtype=u8, device=dev), torch.empty(E, H, dtype=u8, device=dev))
+        for w, (q, e8) in ((w_gate, self.gate), (w_up, self.up)):
+            moe_quantize_fp8_rows(E * I, H, w, q, e8, stream=stream)
+        moe_quantize_fp8_rows(E * H, I, w_down, self.down[0], self.down[1], stream=stream)
 
 
 def moe_gemm_down_bwd(s, do_perm, a, offsets, w_down, g, u, dgu, dw_down, accumulate_dw, ws, ws_bytes=None,

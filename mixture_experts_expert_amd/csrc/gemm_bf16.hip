@@ -66,6 +66,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int NT = 256;                 // threads per workgroup
@@ -107,6 +108,12 @@ struct Params {
   // GATEUP with out0 == nullptr stores A only.
   const int32_t* row_token;
   const float* row_weight;
+  // fp8 (E4M3) GATEUP/DOWN of the inference forward: a, b0, b1 hold 8-bit
+  // codes; sa (one per sorted row of A) and sb0, sb1 (one per row of each
+  // expert's weight matrix) their power-of-two scales as E8M0 bytes.
+  const uint8_t* sa;
+  const uint8_t* sb0;
+  const uint8_t* sb1;
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -151,6 +158,7 @@ __device__ __forceinline__ void step_barrier() {
 // s_waitcnt immediates (gfx9 encoding): vmcnt in [3:0] and [15:14], expcnt in
 // [6:4], lgkmcnt in [11:8]. They wait for LDS traffic and for all but the
 // newest `n` vector-memory instructions (expcnt left unconstrained).
+constexpr int kWaitVm8 = 0x0078;   // vmcnt(8) lgkmcnt(0)
 constexpr int kWaitVm12 = 0x007C;  // vmcnt(12) lgkmcnt(0)
 constexpr int kWaitVm14 = 0x007E;  // vmcnt(14) lgkmcnt(0)
 constexpr int kWaitVm16 = 0x4070;  // vmcnt(16) lgkmcnt(0)
@@ -359,8 +367,14 @@ struct Smem {
 // Every tile of one GEMM that workgroup `bid` of `nblk` (a multiple of 8)
 // owns, start to finish: on return every load and store this workgroup
 // issued has completed and its waves are past a barrier.
-template <int MODE, bool FUSED>
+template <int MODE, bool FUSED, bool F8 = false>
 __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const int nblk, const Smem& sm) {
+  static_assert(!F8 || (FUSED && (MODE == GATEUP || MODE == DOWN)), "fp8: the inference forward's two GEMMs");
+  // Element size in bytes, elements per k-step (64 bytes of a k-major row
+  // either way) and per 16-byte chunk.
+  constexpr int ESZ = F8 ? 1 : 2;
+  constexpr int KS = F8 ? 64 : BK;
+  constexpr int CK = 16 / ESZ;
   bf16_t (&lds0)[STAGE] = sm.lds0;
   bf16_t (&lds1)[STAGE] = sm.lds1;
   bf16_t (&lds2)[STAGE] = sm.lds2;
@@ -483,8 +497,8 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   // next tile before the finished tile's epilogue, which keeps its own copy
   // of the few scalars it needs.
   int lda = 0, ldb = 0, kfixed = 0;
-  if constexpr (MODE == GATEUP) { lda = H; kfixed = H / BK; }
-  if constexpr (MODE == DOWN) { lda = I; kfixed = I / BK; }
+  if constexpr (MODE == GATEUP) { lda = H; kfixed = H / KS; }
+  if constexpr (MODE == DOWN) { lda = I; kfixed = I / KS; }
   if constexpr (MODE == DGRAD_DOWN) { lda = H; ldb = I; kfixed = H / BK; }
   if constexpr (MODE == DGRAD_GATEUP) { lda = 2 * I; ldb = H; kfixed = 2 * I / BK; }
   if constexpr (MODE == WGRAD_DOWN) { lda = H; ldb = I; }
@@ -495,7 +509,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   int nkbeg = 0;  // GATHER_B: first k-row of this workgroup's next tile
   uint32_t aoff[LOADS / 2], boff[LOADS / 2];
   uint32_t bcol[LOADS / 2];  // GATHER_B: column byte offsets of the B loads
-  const bf16_t* abase_m = P.a;  // grouped-M: the tile's first row of A
+  const char* abase_m = reinterpret_cast<const char*>(P.a);  // grouped-M: the tile's first row of A
 
   // Grouped-K: the first k-row of tile Lx's chunk.
   auto kbeg_of = [&](int Lx) -> int {
@@ -582,9 +596,9 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
         const int r = blk * 16 + (lane >> 2);
         const int c = (lane & 3) ^ swk(r);
         if (MODE == GATEUP && FUSED)  // row of x; rows >= mvalid read zeros
-          aoff[t] = r < mvalid ? 2u * (static_cast<uint32_t>(P.row_token[row0 + r]) * H + c * 8) : kNoWrite;
+          aoff[t] = r < mvalid ? ESZ * (static_cast<uint32_t>(P.row_token[row0 + r]) * H + c * CK) : kNoWrite;
         else
-          aoff[t] = 2u * (r * lda + c * 8);  // rows >= mvalid: outside the range, read as zeros
+          aoff[t] = ESZ * (r * lda + c * CK);  // rows >= mvalid: outside the range, read as zeros
       } else {
         const int k = blk * 2 + (lane >> 5);
         const int c = (lane & 31) ^ swt(k);
@@ -599,11 +613,11 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
         const int c = (lane & 3) ^ swk(r);
         const int j = (r & 127) >> 5;
         const int idx = min(n0 + (r >> 7) * 64 + (j & 1) * 32 + (r & 31), I - 1);
-        boff[t] = 2u * (idx * H + c * 8);
+        boff[t] = ESZ * (idx * H + c * CK);
       } else if constexpr (MODE == DOWN) {
         const int r = blk * 16 + (lane >> 2);
         const int c = (lane & 3) ^ swk(r);
-        boff[t] = 2u * (min(n0 + r, H - 1) * I + c * 8);
+        boff[t] = ESZ * (min(n0 + r, H - 1) * I + c * CK);
       } else {
         const int k = blk * 2 + (lane >> 5);
         const int c = (lane & 31) ^ swt(k);
@@ -612,7 +626,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
         else boff[t] = 2u * (k * ldb + min(n0 + c * 8, ncols - 8));
       }
     }
-    abase_m = P.a + static_cast<int64_t>(row0) * lda;
+    abase_m = reinterpret_cast<const char*>(P.a) + static_cast<int64_t>(row0) * lda * ESZ;
   };
   // No next tile: every load of the chained step reads an empty range.
   auto clear_tile = [&]() {
@@ -627,23 +641,25 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
 
   // Buffer resources of k-step s (num_records 0 past the last step).
   auto rsrc_a = [&](int s) -> rsrc_t {
-    const int k0 = s * BK;
+    const int k0 = s * KS;
     if constexpr (A_KMAJOR) {
-      if (MODE == GATEUP && FUSED) return make_rsrc(P.a + k0, s < ksteps ? 2 * (P.T * H - k0) : 0);
-      return make_rsrc(abase_m + k0, s < ksteps ? 2 * (mvalid * lda - k0) : 0);
+      if (MODE == GATEUP && FUSED)
+        return make_rsrc(reinterpret_cast<const char*>(P.a) + k0 * ESZ, s < ksteps ? ESZ * (P.T * H - k0) : 0);
+      return make_rsrc(abase_m + k0 * ESZ, s < ksteps ? ESZ * (mvalid * lda - k0) : 0);
     } else {
       const int left = kend - kbeg - k0;
       return make_rsrc(P.a + static_cast<int64_t>(kbeg + k0) * lda, left > 0 ? 2 * left * lda : 0);
     }
   };
   auto rsrc_b = [&](int s) -> rsrc_t {
-    const int k0 = s * BK;
+    const int k0 = s * KS;
     const bool live = s < ksteps;
     if constexpr (MODE == GATEUP) {
-      const bf16_t* w = ((wave & 1) ? P.b1 : P.b0) + static_cast<int64_t>(e) * I * H + k0;
-      return make_rsrc(w, live ? 2 * (I * H - k0) : 0);
+      const char* w = reinterpret_cast<const char*>((wave & 1) ? P.b1 : P.b0) + (static_cast<int64_t>(e) * I * H + k0) * ESZ;
+      return make_rsrc(w, live ? ESZ * (I * H - k0) : 0);
     } else if constexpr (MODE == DOWN) {
-      return make_rsrc(P.b0 + static_cast<int64_t>(e) * H * I + k0, live ? 2 * (H * I - k0) : 0);
+      return make_rsrc(reinterpret_cast<const char*>(P.b0) + (static_cast<int64_t>(e) * H * I + k0) * ESZ,
+                       live ? ESZ * (H * I - k0) : 0);
     } else if constexpr (MODE == DGRAD_DOWN) {
       return make_rsrc(P.b0 + static_cast<int64_t>(e) * H * I + static_cast<int64_t>(k0) * I,
                        live ? 2 * (H - k0) * I : 0);
@@ -839,6 +855,120 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
     }
     __builtin_amdgcn_sched_barrier(0);
     mfma_slice(nbc, std::false_type{}, fa1, fb1, LOADS / 2, ra, rb, Ln);
+  };
+
+  // ---- fp8 k-step -------------------------------------------------------------
+  // v_mfma_scale_f32_32x32x64_f8f6f4: one instruction covers a whole 64-byte
+  // stage row (64 k). Lane l of an operand holds 32 bytes of row l % 32:
+  // stage chunks 2 (l / 32) and 2 (l / 32) + 1 for both A and B, so lanes
+  // of the same half multiply the same k (the hardware pairs an A lane's byte
+  // j with the B lane's byte j of the same half). The scale operands are the
+  // rows' and columns' E8M0 bytes, replicated in every byte and in both
+  // halves, so that the instruction applies 2^(Xa + Xb) to every product
+  // whichever byte and lane it reads them from.
+  i32x8 fa8[FM], fb8[FN];
+  int sca[FM], scb[FN];
+  int aof8[FM], bof8[FN];
+  auto set_frag_offsets8 = [&]() __attribute__((always_inline)) {
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    const int h2 = 2 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WTM + i * 32 + (lane & 31);
+      aof8[i] = r * 64 + ((swk(r) ^ h2) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * WTN + j * 32 + (lane & 31);
+      bof8[j] = r * 64 + ((swk(r) ^ h2) << 4);
+    }
+  };
+  // This tile's scales: rows of A (sorted rows, valid or not: the codes of
+  // invalid rows read as zero) and columns of the output (weight rows).
+  auto load_scales8 = [&]() __attribute__((always_inline)) {
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    const int l32 = lane & 31;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = min(wm * WTM + i * 32 + l32, max(mvalid - 1, 0));
+      sca[i] = static_cast<int>(P.sa[row0 + r]) * 0x01010101;
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      int v;
+      if constexpr (MODE == GATEUP) {  // wavefront columns: 64 gate (j < 2), then 64 up, same indices
+        const int idx = min(n0 + wn * 64 + (j & 1) * 32 + l32, I - 1);
+        v = (j < 2 ? P.sb0 : P.sb1)[static_cast<int64_t>(e) * I + idx];
+      } else {
+        const int n = min(n0 + wn * WTN + j * 32 + l32, H - 1);
+        v = P.sb0[static_cast<int64_t>(e) * H + n];
+      }
+      scb[j] = v * 0x01010101;
+    }
+  };
+  auto frag8 = [&](const bf16_t* S, int off) -> i32x8 {
+    const char* base = reinterpret_cast<const char*>(S);
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + off);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + (off ^ 16));
+    return i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                 static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+  };
+  // A tile's first step: row block 0 and every B fragment (the others are
+  // read at the start of each step).
+  auto read_first8 = [&](auto nbc, const bf16_t* S) __attribute__((always_inline)) {
+    constexpr int nbm = decltype(nbc)::value;
+    if (nbm > 0) fa8[0] = frag8(S, aof8[0]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      if (nbm > 0) fb8[j] = frag8(S + STAGE_A, bof8[j]);
+  };
+  auto mfma8 = [&](auto zc, int i, int j) __attribute__((always_inline)) {
+    if constexpr (decltype(zc)::value)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa8[i], fb8[j], f32x16{}, 0, 0, 0, sca[i], 0, scb[j]);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa8[i], fb8[j], acc[i][j], 0, 0, 0, sca[i], 0, scb[j]);
+  };
+  // One k-step (64 k) on the stage at Ac, loads of step sn into Ln. At entry
+  // fa8[0] and fb8[] hold this step's fragments. First the wait for the next
+  // step's stage (all but the 8 newest loads, the step after it) and the
+  // barrier, which also frees the stage read during the step before for the
+  // loads issued from here on; then the other row blocks' fragments of this
+  // step. Row blocks run in order, two loads after each block's four MFMAs;
+  // block 0's fragment of the next step is read after block 0, and each
+  // column's after that column's MFMA of the last valid block.
+  auto kstep8 = [&](auto nbc, auto first, const bf16_t* Ac, const bf16_t* An, int sn, bf16_t* Ln, bool last)
+                    __attribute__((always_inline)) {
+    constexpr int nbm = decltype(nbc)::value;
+    const rsrc_t ra = rsrc_a(sn);
+    const rsrc_t rb = rsrc_b(sn);
+    if (!last) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm8);
+      step_barrier();
+    }
+#pragma unroll
+    for (int i = 1; i < FM; ++i)
+      if (i < nbm) fa8[i] = frag8(Ac, aof8[i]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (i < nbm) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          mfma8(first, i, j);
+          if (i == nbm - 1 && !last) fb8[j] = frag8(An + STAGE_A, bof8[j]);
+        }
+      } else if constexpr (decltype(first)::value) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      vmem(2 * i, ra, rb, Ln);
+      vmem(2 * i + 1, ra, rb, Ln);
+      if (i == 0 && nbm > 0 && !last) fa8[0] = frag8(An, aof8[0]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // ---- epilogue -------------------------------------------------------------
@@ -1110,8 +1240,14 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
     step_barrier();
   }
   for (; L < hi; L += nslots) {
-    set_frag_offsets();
-    read_slice(std::integral_constant<int, FM>{}, lds0, 0, fa0, fb0);
+    if constexpr (F8) {
+      set_frag_offsets8();
+      load_scales8();
+      read_first8(std::integral_constant<int, FM>{}, lds0);
+    } else {
+      set_frag_offsets();
+      read_slice(std::integral_constant<int, FM>{}, lds0, 0, fa0, fb0);
+    }
     // This wavefront's 32-row blocks that hold valid rows of the tile (a
     // ragged last tile of an expert skips the MFMAs, fragment reads and
     // stores of the others). The k-loop is compiled once per count, so no
@@ -1122,19 +1258,24 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
     const int fe = e, frow0 = row0, fmvalid = mvalid, fm0 = m0, fn0 = n0, fp = pidx;
     const int Lnext = L + nslots;
     constexpr std::false_type no{};
+    auto kst = [&](auto nbc, auto first, const bf16_t* Ac, const bf16_t* An, int sn, bf16_t* Ln, bool last)
+                   __attribute__((always_inline)) {
+      if constexpr (F8) kstep8(nbc, first, Ac, An, sn, Ln, last);
+      else kstep(nbc, first, Ac, An, sn, Ln, last);
+    };
     auto kloop = [&](auto nbc) __attribute__((always_inline)) {
-      kstep(nbc, std::true_type{}, lds0, lds1, 3, lds3, false);  // step 0: accumulators start at zero
-      for (int s = NSTAGE; s < nsteps; s += NSTAGE) {           // steps s - 3 .. s
-        kstep(nbc, no, lds1, lds2, s, lds0, false);
-        kstep(nbc, no, lds2, lds3, s + 1, lds1, false);
-        kstep(nbc, no, lds3, lds0, s + 2, lds2, false);
-        kstep(nbc, no, lds0, lds1, s + 3, lds3, false);
+      kst(nbc, std::true_type{}, lds0, lds1, 3, lds3, false);  // step 0: accumulators start at zero
+      for (int s = NSTAGE; s < nsteps; s += NSTAGE) {         // steps s - 3 .. s
+        kst(nbc, no, lds1, lds2, s, lds0, false);
+        kst(nbc, no, lds2, lds3, s + 1, lds1, false);
+        kst(nbc, no, lds3, lds0, s + 2, lds2, false);
+        kst(nbc, no, lds0, lds1, s + 3, lds3, false);
       }
       if (Lnext < hi) set_tile_and_offsets(Lnext);
       else clear_tile();
-      kstep(nbc, no, lds1, lds2, 0, lds0, false);
-      kstep(nbc, no, lds2, lds3, 1, lds1, false);
-      kstep(nbc, no, lds3, lds0, 2, lds2, true);
+      kst(nbc, no, lds1, lds2, 0, lds0, false);
+      kst(nbc, no, lds2, lds3, 1, lds1, false);
+      kst(nbc, no, lds3, lds0, 2, lds2, true);
     };
     switch (nbm) {
       case 4: kloop(std::integral_constant<int, 4>{}); break;
@@ -1156,11 +1297,11 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   }
 }
 
-template <int MODE, bool FUSED>
+template <int MODE, bool FUSED, bool F8>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(
     Params P) {
   MOE_GEMM_SMEM
-  gemm_tiles<MODE, FUSED>(P, blockIdx.x, gridDim.x, sm);
+  gemm_tiles<MODE, FUSED, F8>(P, blockIdx.x, gridDim.x, sm);
 }
 
 // Two independent GEMMs of the backward in one persistent launch: a data
@@ -1267,10 +1408,10 @@ int persistent_grid() {
   return cached;
 }
 
-template <int MODE, bool FUSED = false>
+template <int MODE, bool FUSED = false, bool F8 = false>
 hipError_t run(const Params& p, hipStream_t st) {
   const int grid = persistent_grid();
-  grouped_gemm_kernel<MODE, FUSED><<<grid, NT, 0, st>>>(p);
+  grouped_gemm_kernel<MODE, FUSED, F8><<<grid, NT, 0, st>>>(p);
   hipError_t err = hipGetLastError();
   if constexpr (grouped_k(MODE)) {
     if (err != hipSuccess) return err;
@@ -1310,6 +1451,9 @@ Params make_params(const moe_shape& s, const GemmArgs& g) {
   p.part = g.part;
   p.row_token = g.row_token;
   p.row_weight = g.row_weight;
+  p.sa = g.a_scale;
+  p.sb0 = g.b0_scale;
+  p.sb1 = g.b1_scale;
   return p;
 }
 
@@ -1327,8 +1471,12 @@ int64_t wgrad_part_tiles(const moe_shape& s) {
 hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g, hipStream_t st) {
   const Params p = make_params(s, g);
   switch (mode) {
-    case GEMM_GATEUP: return g.row_token ? run<GATEUP, true>(p, st) : run<GATEUP>(p, st);
-    case GEMM_DOWN: return g.row_weight ? run<DOWN, true>(p, st) : run<DOWN>(p, st);
+    case GEMM_GATEUP:
+      if (g.a_scale) return g.row_token ? run<GATEUP, true, true>(p, st) : hipErrorInvalidValue;
+      return g.row_token ? run<GATEUP, true>(p, st) : run<GATEUP>(p, st);
+    case GEMM_DOWN:
+      if (g.a_scale) return g.row_weight ? run<DOWN, true, true>(p, st) : hipErrorInvalidValue;
+      return g.row_weight ? run<DOWN, true>(p, st) : run<DOWN>(p, st);
     case GEMM_DGRAD_DOWN: return run<DGRAD_DOWN>(p, st);
     case GEMM_DGRAD_GATEUP: return run<DGRAD_GATEUP>(p, st);
     case GEMM_WGRAD_DOWN: return run<WGRAD_DOWN>(p, st);

@@ -133,6 +133,11 @@ struct GemmArgs {
   int accumulate;
   const int32_t* row_token;  // GATEUP: row p of A, WGRAD_GATEUP: k-row p of B is row row_token[p] of x [T][H]
   const float* row_weight;   // fused forward, DOWN: output row p scaled by row_weight[p]
+  // fp8 GATEUP (with row_token) and DOWN (with row_weight): a and b* hold
+  // E4M3 codes; E8M0 scales per sorted row of a and per weight row.
+  const uint8_t* a_scale;
+  const uint8_t* b0_scale;
+  const uint8_t* b1_scale;
 };
 
 hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& a, hipStream_t st);
@@ -141,6 +146,13 @@ hipError_t launch_gemm_f32(GemmMode mode, const moe_shape& s, const GemmArgs& a,
 inline hipError_t launch_gemm(GemmMode mode, const moe_shape& s, const GemmArgs& a, hipStream_t st) {
   return s.dtype == MOE_BF16 ? launch_gemm_bf16(mode, s, a, st) : launch_gemm_f32(mode, s, a, st);
 }
+// Rows [rows, K] of bf16 -> OCP E4M3 codes with a power-of-two scale per row
+// (E8M0 byte). K % 8 == 0. e8 has one byte per row, or, with flat_to_sorted
+// (a [rows * k] map), one per sorted row: the scale of row r lands at
+// flat_to_sorted[r k + j] for every j < k.
+hipError_t launch_quantize_fp8_rows(int rows, int K, const void* in, uint8_t* q, uint8_t* e8,
+                                    const int32_t* flat_to_sorted, int k, hipStream_t st);
+
 // A data gradient and a weight gradient that read the same inputs, in one
 // launch for bf16 (DGRAD_DOWN with WGRAD_DOWN, DGRAD_GATEUP with
 // WGRAD_GATEUP); f32 runs them one after the other.

@@ -1,0 +1,154 @@
+"""GPU parity of the fp8 (E4M3) inference forward against the fp8 oracle,
+through the C ABI.
+
+- The row quantiser is bit-exact: codes and E8M0 scales of x, of the expert
+  weights and of hand-made rows (zeros, a lone element, tiny and large
+  magnitudes, values past 448 after scaling), including the sorted-order
+  scatter of x's scales.
+- Routing and permutations are bit-exact as in the bf16 path.
+- The GEMMs multiply exactly the dequantised operands (the matrix core
+  applies both power-of-two scales) with fp32 sums: a is within the bf16
+  tolerance of the oracle, which runs the same definition in float64. a's
+  E4M3 codes and scales equal the oracle's except on rare elements and rows
+  where a sits on a rounding boundary; o_perm and y, downstream of those,
+  are within one E4M3 rounding step (2^-4) normwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_expert_amd import synth
+from oracle import fp8 as F8
+
+import gpu_util as U
+from test_gpu_parity import SMALL
+
+pytestmark = pytest.mark.gpu
+
+FP8_SMALL = [c for c in SMALL if c.dtype == "bf16" and c.H % 64 == 0 and c.I % 64 == 0]
+# One E4M3 rounding step (3 mantissa bits): the normwise bound for outputs
+# downstream of the quantisation of a, whose codes can flip where a itself
+# differs from the oracle's by a bf16 rounding step.
+FP8_TOL = 2.0 ** -4
+
+
+def bf16_dev(a: np.ndarray) -> torch.Tensor:
+    """float values that are bf16 -> device bf16 tensor (exact)."""
+    bits = (np.ascontiguousarray(a, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return torch.from_numpy(bits.view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def test_quantize_rows_bit_exact():
+    from mixture_experts_expert_amd import binding as B
+    rng = np.random.default_rng(0)
+    K = 768
+    rows = [rng.standard_normal(K) * 2.0 ** s for s in (-30, -8, 0, 6, 40)]
+    rows.append(np.zeros(K))
+    z = np.zeros(K)
+    z[5] = -3.0e-3
+    rows.append(z)
+    rows.append(np.r_[rng.uniform(-1, 1, K - 1), 7.99])  # largest element just under 8: scaled to 511.4 -> 448
+    rows.append(np.r_[rng.uniform(-1e-6, 1e-6, K - 1), 1.0])  # most elements subnormal or zero in E4M3
+    neg0 = np.zeros(K)
+    neg0[::2] = -0.0
+    neg0[1] = 2.0
+    rows.append(neg0)
+    x = F8.bf16_round(np.stack(rows + [rng.standard_normal(K) for _ in range(54)]))
+    R = x.shape[0]
+    q = torch.empty(R, K, dtype=torch.uint8, device="cuda")
+    e8 = torch.empty(R, dtype=torch.uint8, device="cuda")
+    B.moe_quantize_fp8_rows(R, K, bf16_dev(x), q, e8)
+    # the sorted-order scatter: rows r -> positions perm[r * k + j]
+    k = 3
+    perm = rng.permutation(R * k).astype(np.int32)
+    e8s = torch.empty(R * k, dtype=torch.uint8, device="cuda")
+    q2 = torch.empty_like(q)
+    B.moe_quantize_fp8_rows(R, K, bf16_dev(x), q2, e8s, torch.from_numpy(perm).to("cuda"), k)
+    torch.cuda.synchronize()
+    rq, re8 = F8.quantize_rows(x)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(e8.cpu().numpy(), re8)
+    assert np.array_equal(q2.cpu().numpy(), rq)
+    want = np.empty(R * k, dtype=np.uint8)
+    want[perm] = np.repeat(re8, k)
+    assert np.array_equal(e8s.cpu().numpy(), want)
+
+
+def fp8_forward(d: U.DevInputs):
+    from mixture_experts_expert_amd import binding as B
+    c = d.cfg
+    T, M = d.t["x"].shape[0], c.T * c.k
+    s = B.shape(T, c.H, c.E, c.k, c.I, torch.bfloat16)
+    dev = "cuda"
+    i32, u8 = torch.int32, torch.uint8
+    w = B.FP8Weights(d.t["w_gate"], d.t["w_up"], d.t["w_down"])
+    out = dict(
+        logits=torch.empty(T, c.E, device=dev), topk_idx=torch.empty(T, c.k, dtype=i32, device=dev),
+        topk_w=torch.empty(T, c.k, device=dev), counts=torch.empty(c.E, dtype=i32, device=dev),
+        offsets=torch.empty(c.E + 1, dtype=i32, device=dev), sorted_to_flat=torch.empty(M, dtype=i32, device=dev),
+        flat_to_sorted=torch.empty(M, dtype=i32, device=dev), row_token=torch.empty(M, dtype=i32, device=dev),
+        row_weight=torch.empty(M, device=dev), xq=torch.empty(T, c.H, dtype=u8, device=dev),
+        x_e8=torch.empty(M, dtype=u8, device=dev), a=torch.empty(M, c.I, dtype=torch.bfloat16, device=dev),
+        aq=torch.empty(M, c.I, dtype=u8, device=dev), a_e8=torch.empty(M, dtype=u8, device=dev),
+        o_perm=torch.empty(M, c.H, dtype=torch.bfloat16, device=dev),
+        y=torch.empty(T, c.H, dtype=torch.bfloat16, device=dev))
+    ws = torch.empty(B.moe_workspace_bytes(s), dtype=u8, device=dev)
+    o = out
+    B.moe_forward_fused_fp8(s, d.t["x"], d.t["w_router"], d.bias, w.gate[0], w.gate[1], w.up[0], w.up[1], w.down[0],
+                            w.down[1], o["logits"], o["topk_idx"], o["topk_w"], o["counts"], o["offsets"],
+                            o["sorted_to_flat"], o["flat_to_sorted"], o["row_token"], o["row_weight"], o["xq"],
+                            o["x_e8"], o["a"], o["aq"], o["a_e8"], o["o_perm"], o["y"], ws)
+    torch.cuda.synchronize()
+    return w, out
+
+
+def check_fp8(inp, w, out, check_weights=True):
+    c = inp.cfg
+    ref_r = U.oracle_route(inp)
+    for n in ["topk_idx", "counts", "offsets", "sorted_to_flat", "flat_to_sorted"]:
+        assert np.array_equal(U.to_np(out[n]), ref_r[n]), n
+    assert U.same_bits(U.to_np(out["logits"]), ref_r["logits"]), "logits differ"
+    x = inp.f32("x").astype(np.float64)
+    wg, wu, wd = (F8.quantize_weights(inp.f32(n).astype(np.float64)) for n in ["w_gate", "w_up", "w_down"])
+    if check_weights:
+        for (q, e8), ref in zip((w.gate, w.up, w.down), (wg, wu, wd)):
+            assert np.array_equal(q.cpu().numpy(), ref[0]) and np.array_equal(e8.cpu().numpy(), ref[1])
+    s2f = ref_r["sorted_to_flat"].astype(np.int64)
+    row_token = (s2f // c.k).astype(np.int32)
+    row_weight = ref_r["topk_w"].reshape(-1)[s2f].astype(np.float64)
+    ref = F8.experts_fp8(x, row_token, row_weight, ref_r["offsets"], wg, wu, wd)
+    assert np.array_equal(out["xq"].cpu().numpy(), ref["xq"])
+    assert np.array_equal(out["x_e8"].cpu().numpy(), ref["xe"][row_token])
+    U.check_close("a", U.to_np(out["a"]), ref["a"], U.BF16_TOL)
+    # a's codes: where a differs by a rounding step, a code (or, if the
+    # row's largest element moves across a power of two, the row's scale)
+    # can differ; both must be rare.
+    aq, ae = out["aq"].cpu().numpy(), out["a_e8"].cpu().numpy()
+    same_scale = ae == ref["ae"]
+    U.say(f"  a scales differ on {np.mean(~same_scale):.4f} of rows, "
+          f"codes on {np.mean(aq[same_scale] != ref['aq'][same_scale]):.5f} of the rest")
+    assert np.mean(~same_scale) <= 0.02
+    assert np.mean(aq[same_scale] != ref["aq"][same_scale]) <= 0.01
+    # Downstream of those flips the comparison is at E4M3's own precision.
+    U.check_close("o_perm", U.to_np(out["o_perm"]), ref["o_perm"], FP8_TOL)
+    y = F8.combine_sum(ref["o_perm"], ref_r["flat_to_sorted"], c.T, c.k)
+    U.check_close("y", U.to_np(out["y"]), y, FP8_TOL)
+
+
+@pytest.mark.parametrize("cfg", FP8_SMALL, ids=lambda c: c.name)
+def test_fp8_forward_small(cfg):
+    U.say(f"[fp8 forward] {cfg}")
+    inp = synth.make_inputs(cfg, seed=5, with_dy=False)
+    d = U.DevInputs(inp)
+    w, out = fp8_forward(d)
+    check_fp8(inp, w, out)
+
+
+def test_fp8_forward_qwen3_30b_a3b_full():
+    """T=4096, H=2048, E=128, k=8, I=768: every output element of the fp8 forward."""
+    cfg = synth.CONFIGS["qwen3_30b_a3b_fwd"]
+    U.say(f"[fp8 forward] {cfg}")
+    inp = synth.make_inputs(cfg, seed=0)
+    d = U.DevInputs(inp)
+    w, out = fp8_forward(d)
+    check_fp8(inp, w, out)
