@@ -7,8 +7,9 @@ in HBM, on one stream: route -> expert indexing + gather -> gate/up GEMM
 (SwiGLU epilogue) -> down GEMM -> combine, then combine backward -> down
 dgrad (SwiGLU backward epilogue) -> down wgrad -> gate/up dgrad -> gate/up
 wgrad -> unpermute-sum -> router backward, every step a call of the C ABI
-(the six GEMMs through their one-kernel entry points, which is what
-moe_grouped_gemm_fwd/bwd chain).
+(the six GEMMs through their single-GEMM entry points: moe_grouped_gemm_fwd
+chains the first two, moe_grouped_gemm_bwd runs the other four as two
+paired launches, timed separately below).
 
 Prints one JSON line. `value` is tokens/s of the whole stage; TFLOP/s counts
 the expert GEMMs (18*T*k*H*I per step). Around every call the timed steps

@@ -129,8 +129,9 @@ moe_status moe_grouped_gemm_fwd(moe_shape s, const void* x_perm, const int32_t* 
                                 const void* w_up, const void* w_down, void* g, void* u, void* a, void* o_perm,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* The six grouped GEMMs one at a time (moe_grouped_gemm_fwd and
- * moe_grouped_gemm_bwd chain them). Same operands, layouts and arithmetic as
+/* The six grouped GEMMs one at a time (moe_grouped_gemm_fwd chains the
+ * first two; moe_grouped_gemm_bwd runs the other four as the two paired
+ * launches below, with the same results). Same operands, layouts and arithmetic as
  * described there; dgu is [T*k, 2I] in dtype holding dG in columns [0, I)
  * and dU in columns [I, 2I). Callers that train adapters on frozen experts
  * can run the data gradients without the weight gradients.
