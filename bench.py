@@ -24,8 +24,9 @@ taken from the committed summary under profiles/ and reported only while the
 GEMM source still hashes to the value recorded there. `cpu_baseline` times
 the CPU oracle on a bounded token sample of the same workload.
 
-After the timed steps (and outside them): `two_stream_ms_per_step` times the
-same step with the backward's weight-gradient GEMMs on a second stream,
+After the timed steps (and outside them): `graph_ms_per_step` times the same
+step captured once into a HIP graph and replayed; `two_stream_ms_per_step`
+the step with the backward's weight-gradient GEMMs on a second stream,
 concurrently with the data-gradient GEMMs; `gather_fused_ms` the step
 without x_perm (gate/up and its weight gradient read x through the sorted
 rows' tokens) and its three changed calls; and `inference_forward_ms` the
@@ -283,6 +284,19 @@ def main() -> int:
     if two_stream_ms is not None:
         log(f"two-stream backward: {two_stream_ms:.3f} ms/step")
 
+    # The same step captured once into a HIP graph and replayed (no launch
+    # gaps between the calls).
+    graph_ms = None
+    if not args.timed_only:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            step()
+        torch.cuda.synchronize()
+        graph_ms = round(time_fn(graph.replay), 4)
+        log(f"graph replay: {graph_ms:.3f} ms/step")
+
     # The same step without x_perm: the sort also writes each sorted row's
     # token, and gate/up and its weight gradient read x rows through it.
     rt = dict(row_token=torch.empty(cfg.M, dtype=torch.int32, device="cuda"),
@@ -431,6 +445,7 @@ def main() -> int:
         "hbm_frac": hbm_frac,
         "roofline": roof,
         "two_stream_ms_per_step": two_stream_ms,
+        "graph_ms_per_step": graph_ms,
         "gather_fused_ms": gather_fused_ms,
         "paired_ms": paired_ms,
         "inference_forward_ms": infer,
