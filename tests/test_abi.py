@@ -113,6 +113,21 @@ def test_fused_forward_validation(B):
     assert B.lib.moe_gemm_gate_up_bwd(s, F, None, None, F, F, F, F, F, F, 0, F, need, None) == 1
     assert B.lib.moe_gemm_gate_up_bwd(s, F, F, None, F, F, F, F, F, F, 0, F, need - 1, None) == 3
     assert B.lib.moe_gemm_gate_up_bwd(big, F, F, F, F, F, F, F, F, F, 0, F, B.moe_workspace_bytes(big), None) == 2
+    # fp8: quantiser arguments, shapes (bf16 only, H and I multiples of 64), pointers, workspace
+    Q = B.lib.moe_quantize_fp8_rows
+    assert Q(4, 12, F, F, F, None, 0, None) == 1          # K % 8 != 0
+    assert Q(-1, 64, F, F, F, None, 0, None) == 1
+    assert Q(4, 64, F, None, F, None, 0, None) == 1
+    assert Q(4, 64, F, F, F, F, 0, None) == 1             # scatter needs k >= 1
+    f32s = B.shape(64, 128, 8, 2, 64, "f32")
+    odd = B.shape(64, 96, 8, 2, 64, "bf16")
+    G8 = B.lib.moe_gemm_gate_up_fp8
+    assert G8(f32s, *[F] * 9, None) == 2 and G8(odd, *[F] * 9, None) == 2
+    assert G8(s, F, None, F, F, F, F, F, F, F, None) == 1
+    D8 = B.lib.moe_gemm_down_fp8
+    assert D8(odd, *[F] * 7, None) == 2 and D8(s, F, F, F, F, F, None, F, None) == 1
+    assert B.lib.moe_forward_fused_fp8(s, *[F] * 26, need - 1, None) == 3
+    assert B.lib.moe_forward_fused_fp8(odd, *[F] * 26, need, None) == 2
     W = B.lib.moe_gemm_gate_up_wgrad_gathered
     assert W(s, F, F, None, F, F, F, 0, F, need, None) == 1
     assert W(s, F, F, F, F, F, F, 2, F, need, None) == 1
