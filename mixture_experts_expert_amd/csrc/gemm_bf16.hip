@@ -1258,6 +1258,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
     const int fe = e, frow0 = row0, fmvalid = mvalid, fm0 = m0, fn0 = n0, fp = pidx;
     const int Lnext = L + nslots;
     constexpr std::false_type no{};
+    constexpr bool EPI_PER_VARIANT = MODE == GATEUP && !F8;
     auto kst = [&](auto nbc, auto first, const bf16_t* Ac, const bf16_t* An, int sn, bf16_t* Ln, bool last)
                    __attribute__((always_inline)) {
       if constexpr (F8) kstep8(nbc, first, Ac, An, sn, Ln, last);
@@ -1276,6 +1277,10 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
       kst(nbc, no, lds1, lds2, 0, lds0, false);
       kst(nbc, no, lds2, lds3, 1, lds1, false);
       kst(nbc, no, lds3, lds0, 2, lds2, true);
+      // The bf16 gate/up epilogue inside each variant: blocks without valid
+      // rows are dead there, which leaves it without register spills (shared
+      // behind the switch it spills; the other modes do best shared).
+      if constexpr (EPI_PER_VARIANT) epilogue(fe, frow0, fmvalid, fm0, fn0, decltype(nbc)::value, fp);
     };
     switch (nbm) {
       case 4: kloop(std::integral_constant<int, 4>{}); break;
@@ -1284,7 +1289,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
       case 1: kloop(std::integral_constant<int, 1>{}); break;
       default: kloop(std::integral_constant<int, 0>{}); break;
     }
-    epilogue(fe, frow0, fmvalid, fm0, fn0, nbm, fp);
+    if constexpr (!EPI_PER_VARIANT) epilogue(fe, frow0, fmvalid, fm0, fn0, nbm, fp);
     // The next tile's first steps have landed (everything this wavefront
     // issued has: loads and the epilogue's stores, which the counter does
     // not order against each other) in every wavefront, and all are done
