@@ -31,7 +31,9 @@ concurrently with the data-gradient GEMMs; `gather_fused_ms` the step
 without x_perm (gate/up and its weight gradient read x through the sorted
 rows' tokens) and its three changed calls; and `inference_forward_ms` the
 forward alone, unfused and fused (no x_perm, routing weights in the down
-GEMM's epilogue). `--timed-only` skips these and the CPU baseline, so that
+GEMM's epilogue); `lora_ms` the training step with rank-64 adapters on frozen
+experts (merges, forward on the merged weights, data and adapter gradients)
+and its two adapter calls. `--timed-only` skips these and the CPU baseline, so that
 under a profiler the last K launches of every kernel are the timed steps.
 """
 from __future__ import annotations
@@ -395,6 +397,30 @@ def main() -> int:
         infer["fp8_down"] = round(time_fn(down8, reps=5), 4)
         log(f"inference forward: {infer}")
 
+    # Adapter training step at the same shape (rank 64, scale 2; outside the
+    # timed steps): the three merges W' = W + s B A, the forward on W', the
+    # data gradients and the adapter gradients; no frozen-weight gradient.
+    lora = None
+    if not args.timed_only:
+        r = 64
+        ad = {n: torch.from_numpy(v.view(np.int16)).to("cuda").view(torch.bfloat16)
+              for n, v in synth.make_adapters(cfg, r, args.seed).items()}
+        ls = B.LoRAStage(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, r, 2.0)
+        lb = ls.buf
+
+        def lora_step():
+            ls.forward(x, wr, wg, wu, wd, ad, bias)
+            ls.backward(dy)
+
+        lora = {"rank": r, "step": round(time_fn(lora_step), 4)}
+        lora["moe_lora_merge_x3"] = round(time_fn(lambda: ls.merge(wg, wu, wd, ad), reps=5), 4)
+        lora["moe_lora_grads"] = round(time_fn(lambda: B.moe_lora_grads(
+            ls.s, r, 2.0, lb["x_perm"], lb["a"], lb["dgu"], lb["do_perm"], lb["offsets"],
+            *(ad[n] for n in B.LORA_NAMES), *(lb["d" + n] for n in B.LORA_NAMES), ls.lora_ws), reps=5), 4)
+        log(f"adapter step: {lora}")
+        del ls, lb, ad
+        torch.cuda.empty_cache()
+
     flops = gemm_flops(cfg)
     nbytes = alg_bytes(cfg)
     step_flops = sum(flops.values())
@@ -449,6 +475,7 @@ def main() -> int:
         "gather_fused_ms": gather_fused_ms,
         "paired_ms": paired_ms,
         "inference_forward_ms": infer,
+        "lora_ms": lora,
     }
     if not (args.no_cpu_baseline or args.timed_only):
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")

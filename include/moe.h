@@ -16,6 +16,10 @@
  *             moe_gemm_down -> moe_combine; moe_combine_bwd -> moe_gemm_down_dgrad,
  *             moe_gemm_down_wgrad, moe_gemm_gate_up_dgrad,
  *             moe_gemm_gate_up_wgrad_gathered -> moe_unpermute_sum -> moe_route_bwd
+ *   adapters on frozen experts: moe_lora_merge -> the forward on the merged
+ *             weights; moe_combine_bwd -> moe_gemm_down_dgrad ->
+ *             moe_gemm_gate_up_dgrad -> moe_unpermute_sum -> moe_route_bwd,
+ *             moe_lora_grads
  *
  * It replaces the per-expert for-loop of the Hugging Face MoE block (axolotl
  * issue #3155, "Feature description") with router softmax/top-k, a sort of the
@@ -334,6 +338,49 @@ moe_status moe_forward_fused_fp8(moe_shape s, const void* x, const void* w_route
                                  int32_t* sorted_to_flat, int32_t* flat_to_sorted, int32_t* row_token,
                                  float* row_weight, uint8_t* xq, uint8_t* x_e8, void* a, uint8_t* aq, uint8_t* a_e8,
                                  void* o_perm, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Low-rank adapters on the frozen experts (unsloth PR #3812, the LoRA path of
+ * the grouped GEMM; axolotl issue #3155, fine-tuning Qwen3 MoE). Per expert e
+ * and projection P in {gate, up, down} with frozen W_P [E,N,K] (w_gate, w_up
+ * [E,I,H]; w_down [E,H,I]), adapters A_P [E,r,K] and B_P [E,N,r] (bf16) and
+ * scale s, the stage is the plain one on W'_P = W_P + s B_P A_P. Training:
+ *   moe_lora_merge (three times) -> the forward chain on W' ->
+ *   moe_combine_bwd -> moe_gemm_down_dgrad -> moe_gemm_gate_up_dgrad ->
+ *   moe_unpermute_sum -> moe_route_bwd, and moe_lora_grads for the adapters
+ * (the frozen weights take no gradient). Rank r: a multiple of 8, at most
+ * 128 (MOE_EUNSUPPORTED otherwise; r <= 0 is MOE_EINVAL). */
+
+/* W'[e] = bf16(W[e] + s * B[e] A[e]) for w [E,N,K], a [E,r,K], b [E,N,r],
+ * w_out [E,N,K], all bf16: the product summed in fp32 from exact bf16
+ * products, scaled and added in fp32, rounded once. w_out may be w (in
+ * place); otherwise the two must not overlap. K % 8 == 0 and E <= 65535
+ * (MOE_EUNSUPPORTED otherwise). */
+moe_status moe_lora_merge(int32_t E, int32_t N, int32_t K, int32_t r, float scale, const void* w, const void* a,
+                          const void* b, void* w_out, hipStream_t stream);
+
+/* Bytes of device workspace for moe_lora_grads at this shape and rank on
+ * the current device (0 if either is rejected): the scaled adapters, the
+ * rank-wide row projections and the split-K partial tiles. */
+size_t moe_lora_workspace_bytes(moe_shape s, int32_t r);
+
+/* Adapter gradients of the stage on the merged weights (chain rule through
+ * W' = W + s B A: dA = s B^T dW', dB = s dW' A^T, with dW' the plain weight
+ * gradient, formed here without dW'): over each expert's sorted rows,
+ *   dB_gate = s dG^T (x_perm A_gate^T)   dA_gate = s (dG B_gate)^T x_perm
+ *   dB_up   = s dU^T (x_perm A_up^T)     dA_up   = s (dU B_up)^T x_perm
+ *   dB_down = s do_perm^T (a A_down^T)   dA_down = s (do_perm B_down)^T a
+ * Inputs (bf16, from the forward and backward on W'): x_perm [T*k,H], a (the
+ * activations) [T*k,I], dgu = [dG | dU] [T*k,2I] (moe_gemm_down_dgrad),
+ * do_perm [T*k,H], offsets [E+1], the adapters. Outputs: fp32 da_* [E,r,K]
+ * and db_* [E,N,r], overwritten; an expert with no rows gets zeros. The
+ * scaled adapters and the projections x_perm (sA)^T, dY (sB) are rounded to
+ * bf16 once; every sum is fp32. Requires shape.dtype MOE_BF16; ws of
+ * ws_bytes >= moe_lora_workspace_bytes(s, r), else MOE_EWORKSPACE. */
+moe_status moe_lora_grads(moe_shape s, int32_t r, float scale, const void* x_perm, const void* act, const void* dgu,
+                          const void* do_perm, const int32_t* offsets, const void* a_gate, const void* b_gate,
+                          const void* a_up, const void* b_up, const void* a_down, const void* b_down, float* da_gate,
+                          float* db_gate, float* da_up, float* db_up, float* da_down, float* db_down, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
 
 /* A static, human-readable name for a status code. */
 const char* moe_status_string(moe_status status);

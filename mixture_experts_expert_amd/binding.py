@@ -72,6 +72,10 @@ _SIGS = {
     "moe_gemm_gate_up_wgrad_gathered": ([moe_shape, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_size_t, _P],
                                         ctypes.c_int),
     "moe_forward_fused": ([moe_shape] + [_P] * 19 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_lora_workspace_bytes": ([moe_shape, ctypes.c_int32], ctypes.c_size_t),
+    "moe_lora_merge": ([ctypes.c_int32] * 4 + [ctypes.c_float] + [_P] * 5, ctypes.c_int),
+    "moe_lora_grads": ([moe_shape, ctypes.c_int32, ctypes.c_float] + [_P] * 18 + [ctypes.c_size_t, _P],
+                       ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -294,6 +298,24 @@ def moe_forward_fused(s, x, w_router, logit_bias, w_gate, w_up, w_down, logits, 
         _ptr(row_token), _ptr(row_weight), _ptr(a), _ptr(o_perm), _ptr(y), _ptr(ws), nb, _stream(stream)))
 
 
+def moe_lora_workspace_bytes(s: moe_shape, r: int) -> int:
+    return int(lib.moe_lora_workspace_bytes(s, r))
+
+
+def moe_lora_merge(E, N, K, r, scale, w, a, b, w_out, stream=None):
+    _check("moe_lora_merge", lib.moe_lora_merge(E, N, K, r, float(scale), _ptr(w), _ptr(a), _ptr(b), _ptr(w_out),
+                                                _stream(stream)))
+
+
+def moe_lora_grads(s, r, scale, x_perm, act, dgu, do_perm, offsets, a_gate, b_gate, a_up, b_up, a_down, b_down,
+                   da_gate, db_gate, da_up, db_up, da_down, db_down, ws, ws_bytes=None, stream=None):
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_lora_grads", lib.moe_lora_grads(
+        s, r, float(scale), _ptr(x_perm), _ptr(act), _ptr(dgu), _ptr(do_perm), _ptr(offsets), _ptr(a_gate),
+        _ptr(b_gate), _ptr(a_up), _ptr(b_up), _ptr(a_down), _ptr(b_down), _ptr(da_gate), _ptr(db_gate), _ptr(da_up),
+        _ptr(db_up), _ptr(da_down), _ptr(db_down), _ptr(ws), nb, _stream(stream)))
+
+
 class MoEStage:
     """Buffers and call order of one MoE layer's expert stage on one GPU.
 
@@ -312,6 +334,7 @@ class MoEStage:
                  gather_fused: bool = False):
         self.T, self.H, self.E, self.k, self.I, self.dtype = T, H, E, k, I, dtype
         self.gather_fused = gather_fused
+        self.weight_grads = True  # dw_* buffers (the adapter stage trains no frozen weight)
         self.s = shape(T, H, E, k, I, dtype)
         M = T * k
         dev = torch.device(device)
@@ -343,9 +366,14 @@ class MoEStage:
         self.buf.update({
             "do_perm": torch.empty(M, H, dtype=dt, device=dev), "d_topk_w": torch.empty(T, k, dtype=f32, device=dev),
             "dx_perm": torch.empty(M, H, dtype=dt, device=dev), "dx": torch.empty(T, H, dtype=dt, device=dev),
-            "dw_gate": torch.empty(E, I, H, dtype=f32, device=dev), "dw_up": torch.empty(E, I, H, dtype=f32, device=dev),
-            "dw_down": torch.empty(E, H, I, dtype=f32, device=dev), "d_logits": torch.empty(T, E, dtype=f32, device=dev),
+            "d_logits": torch.empty(T, E, dtype=f32, device=dev),
         })
+        if self.weight_grads:
+            self.buf.update({
+                "dw_gate": torch.empty(E, I, H, dtype=f32, device=dev),
+                "dw_up": torch.empty(E, I, H, dtype=f32, device=dev),
+                "dw_down": torch.empty(E, H, I, dtype=f32, device=dev),
+            })
         self._bwd_ready = True
 
     def forward(self, x, w_router, w_gate, w_up, w_down, logit_bias=None, stream=None):
@@ -412,6 +440,71 @@ class MoEStage:
             joined = torch.cuda.Event()
             joined.record(aux_stream)
             main.wait_event(joined)
+        moe_unpermute_sum(s, b["dx_perm"], b["flat_to_sorted"], b["dx"], stream)
+        moe_route_bwd(s, b["d_topk_w"], b["topk_w"], b["topk_idx"], b["d_logits"], stream)
+        return b["dx"]
+
+
+LORA_NAMES = ("a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")
+
+
+class LoRAStage(MoEStage):
+    """The stage with low-rank adapters on frozen experts.
+
+    ``forward(x, w_router, w_gate, w_up, w_down, adapters)`` merges each
+    projection (moe_lora_merge into held W' buffers) and runs the plain
+    forward on W'; ``backward(dy)`` runs the data gradients on W' and
+    moe_lora_grads, and returns dx. The adapter gradients (float32) are in
+    ``buf["d" + name]``; the frozen weights get none. ``adapters``: a_P
+    [E,r,K], b_P [E,N,r] bf16 for P in gate, up, down.
+    """
+
+    def __init__(self, T: int, H: int, E: int, k: int, I: int, rank: int, scale: float, device="cuda"):
+        super().__init__(T, H, E, k, I, torch.bfloat16, device=device)
+        self.weight_grads = False
+        self.rank, self.scale = rank, scale
+        nb = moe_lora_workspace_bytes(self.s, rank)
+        if nb == 0:
+            raise MoEError("moe_lora_workspace_bytes", 2, "shape or rank rejected")
+        dev = self.ws.device
+        self.lora_ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        bf = torch.bfloat16
+        self.merged = (torch.empty(E, I, H, dtype=bf, device=dev), torch.empty(E, I, H, dtype=bf, device=dev),
+                       torch.empty(E, H, I, dtype=bf, device=dev))
+        f32 = torch.float32
+        self.buf.update({
+            "da_gate": torch.empty(E, rank, H, dtype=f32, device=dev), "db_gate": torch.empty(E, I, rank, dtype=f32,
+                                                                                            device=dev),
+            "da_up": torch.empty(E, rank, H, dtype=f32, device=dev), "db_up": torch.empty(E, I, rank, dtype=f32,
+                                                                                        device=dev),
+            "da_down": torch.empty(E, rank, I, dtype=f32, device=dev), "db_down": torch.empty(E, H, rank, dtype=f32,
+                                                                                            device=dev),
+            "dgu": torch.empty(T * k, 2 * I, dtype=bf, device=dev),
+        })
+
+    def merge(self, w_gate, w_up, w_down, adapters, stream=None):
+        E, H, I, r = self.E, self.H, self.I, self.rank
+        wg, wu, wd = self.merged
+        moe_lora_merge(E, I, H, r, self.scale, w_gate, adapters["a_gate"], adapters["b_gate"], wg, stream)
+        moe_lora_merge(E, I, H, r, self.scale, w_up, adapters["a_up"], adapters["b_up"], wu, stream)
+        moe_lora_merge(E, H, I, r, self.scale, w_down, adapters["a_down"], adapters["b_down"], wd, stream)
+        return self.merged
+
+    def forward(self, x, w_router, w_gate, w_up, w_down, adapters, logit_bias=None, stream=None):
+        self.adapters = adapters
+        wg, wu, wd = self.merge(w_gate, w_up, w_down, adapters, stream)
+        return super().forward(x, w_router, wg, wu, wd, logit_bias, stream)
+
+    def backward(self, dy, stream=None):
+        self._alloc_bwd()
+        b, s = self.buf, self.s
+        wg, wu, wd = self.merged
+        ad = self.adapters
+        moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["do_perm"], b["d_topk_w"], stream)
+        moe_gemm_down_dgrad(s, b["do_perm"], b["offsets"], wd, b["g"], b["u"], b["dgu"], stream)
+        moe_gemm_gate_up_dgrad(s, b["dgu"], b["offsets"], wg, wu, b["dx_perm"], stream)
+        moe_lora_grads(s, self.rank, self.scale, b["x_perm"], b["a"], b["dgu"], b["do_perm"], b["offsets"],
+                       *(ad[n] for n in LORA_NAMES), *(b["d" + n] for n in LORA_NAMES), self.lora_ws, stream=stream)
         moe_unpermute_sum(s, b["dx_perm"], b["flat_to_sorted"], b["dx"], stream)
         moe_route_bwd(s, b["d_topk_w"], b["topk_w"], b["topk_idx"], b["d_logits"], stream)
         return b["dx"]

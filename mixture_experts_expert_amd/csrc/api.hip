@@ -467,4 +467,67 @@ moe_status moe_route_bwd(moe_shape s, const float* d_topk_w, const float* topk_w
   return from_hip(moe::launch_route_bwd(s, d_topk_w, topk_w, topk_idx, d_logits, stream));
 }
 
+namespace {
+// Adapter rank: a multiple of 8 (16-byte rows of B) up to 128 (the merge's
+// LDS tile); every GEMM shape of the adapter-gradient path must pass the
+// shape checks.
+moe_status check_lora(const moe_shape& s, int32_t r) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (r <= 0) return MOE_EINVAL;
+  if (s.dtype != MOE_BF16 || r > 128 || r % 8 != 0) return MOE_EUNSUPPORTED;
+  const int rp = moe::lora_padded_rank(r);
+  const int hi[8][2] = {{2 * rp, s.H}, {rp, s.I}, {2 * rp, 2 * s.I}, {rp, s.H},
+                        {2 * s.I, 2 * rp}, {2 * rp, s.H}, {s.H, rp}, {rp, s.I}};
+  for (const auto& d : hi)
+    if ((st = check_shape(moe::lora_gemm_shape(s, d[0], d[1]))) != MOE_OK) return st;
+  return MOE_OK;
+}
+}  // namespace
+
+size_t moe_lora_workspace_bytes(moe_shape s, int32_t r) {
+  if (check_lora(s, r) != MOE_OK) return 0;
+  return moe::lora_layout(s, r).total;
+}
+
+moe_status moe_lora_merge(int32_t E, int32_t N, int32_t K, int32_t r, float scale, const void* w, const void* a,
+                          const void* b, void* w_out, hipStream_t stream) {
+  if (E <= 0 || N <= 0 || K <= 0 || r <= 0) return MOE_EINVAL;
+  if (any_null(w, a, b, w_out)) return MOE_EINVAL;
+  if (r > 128 || r % 8 != 0 || K % 8 != 0 || E > 65535 || (N + 127) / 128 > 65535) return MOE_EUNSUPPORTED;
+  return from_hip(moe::launch_lora_merge(E, N, K, r, scale, w, a, b, w_out, stream));
+}
+
+moe_status moe_lora_grads(moe_shape s, int32_t r, float scale, const void* x_perm, const void* act, const void* dgu,
+                          const void* do_perm, const int32_t* offsets, const void* a_gate, const void* b_gate,
+                          const void* a_up, const void* b_up, const void* a_down, const void* b_down, float* da_gate,
+                          float* db_gate, float* da_up, float* db_up, float* da_down, float* db_down, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_lora(s, r);
+  if (st != MOE_OK) return st;
+  if (any_null(x_perm, act, dgu, do_perm, offsets, a_gate, b_gate, a_up, b_up, a_down, b_down, da_gate, db_gate,
+               da_up, db_up, da_down, db_down, ws))
+    return MOE_EINVAL;
+  if (ws_bytes < moe::lora_layout(s, r).total) return MOE_EWORKSPACE;
+  moe::LoraArgs g{};
+  g.offsets = offsets;
+  g.x_perm = x_perm;
+  g.act = act;
+  g.dgu = dgu;
+  g.do_perm = do_perm;
+  g.a_gate = a_gate;
+  g.b_gate = b_gate;
+  g.a_up = a_up;
+  g.b_up = b_up;
+  g.a_down = a_down;
+  g.b_down = b_down;
+  g.da_gate = da_gate;
+  g.db_gate = db_gate;
+  g.da_up = da_up;
+  g.db_up = db_up;
+  g.da_down = da_down;
+  g.db_down = db_down;
+  return from_hip(moe::launch_lora_grads(s, r, scale, g, ws, stream));
+}
+
 }  // extern "C"

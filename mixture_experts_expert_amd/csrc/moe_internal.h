@@ -165,4 +165,34 @@ inline hipError_t launch_gemm_pair(GemmMode ma, GemmMode mb, const moe_shape& s,
   return err != hipSuccess ? err : launch_gemm_f32(mb, s, gb, st);
 }
 
+
+// Low-rank adapters (lora.hip). The gradient path pads the rank to rp, a
+// multiple of 64, so that every reinterpreted GEMM shape meets the kernels'
+// H % 64 == 0 and I % 64 == 0.
+int lora_padded_rank(int r);
+moe_shape lora_gemm_shape(const moe_shape& s, int H, int I);  // s with H and I replaced
+
+struct LoraLayout {  // byte offsets in the adapter-gradient workspace
+  size_t sa_gu, sa_d, sbt_gu, sbt_d;  // bf16 scaled adapter stacks
+  size_t z_gu, z_d, y_gu, y_d;        // bf16 row projections [T*k][2rp | rp]
+  size_t da_gu, db_gu, da_d, db_d;    // fp32 padded gradients
+  size_t part;                        // fp32 split-K partial tiles
+  size_t total;
+};
+LoraLayout lora_layout(const moe_shape& s, int r);
+
+struct LoraArgs {
+  const int32_t* offsets;
+  const void* x_perm;   // [T*k][H]
+  const void* act;      // [T*k][I]
+  const void* dgu;      // [T*k][2I]
+  const void* do_perm;  // [T*k][H]
+  const void *a_gate, *b_gate, *a_up, *b_up, *a_down, *b_down;
+  float *da_gate, *db_gate, *da_up, *db_up, *da_down, *db_down;
+};
+
+hipError_t launch_lora_merge(int E, int N, int K, int r, float s, const void* w, const void* a, const void* b,
+                             void* w_out, hipStream_t st);
+hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraArgs& g, void* ws, hipStream_t st);
+
 }  // namespace moe

@@ -157,6 +157,23 @@ def make_inputs(cfg: MoEConfig, seed: int = 0, *, T: Optional[int] = None,
     return Inputs(cfg, seed, t, bias)
 
 
+ADAPTER_NAMES = ("a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")
+
+
+def make_adapters(cfg: MoEConfig, r: int, seed: int = 0) -> Dict[str, np.ndarray]:
+    """Low-rank adapters of rank r for every expert projection, as bf16 bit
+    patterns (uint16). Drawn from ``default_rng(seed + 2)`` in the order
+    a_gate [E, r, H], b_gate [E, I, r], a_up [E, r, H], b_up [E, I, r],
+    a_down [E, r, I], b_down [E, H, r], each 0.02 * standard normal float32
+    rounded to bf16 (trained adapters: B is no longer zero)."""
+    rng = np.random.default_rng(seed + 2)
+    E, H, I = cfg.E, cfg.H, cfg.I
+    shapes = {"a_gate": (E, r, H), "b_gate": (E, I, r), "a_up": (E, r, H), "b_up": (E, I, r),
+              "a_down": (E, r, I), "b_down": (E, H, r)}
+    return {n: bf16_round(np.float32(0.02) * rng.standard_normal(shapes[n], dtype=np.float32))
+            for n in ADAPTER_NAMES}
+
+
 def random_small_config(rng: np.random.Generator, dtype: str = "f32", backward: bool = True,
                         max_T: int = 24) -> MoEConfig:
     """A random tiny shape for brute-force checks (any H, I; k <= E)."""

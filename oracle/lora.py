@@ -28,8 +28,7 @@ import numpy as np
 
 def merge(w: np.ndarray, a: np.ndarray, b: np.ndarray, s: float) -> np.ndarray:
     """W' = W + s B A for stacked [E, N, K] weights, a [E, r, K], b [E, N, r]."""
-    return np.asarray(w, np.float64) + s * np.einsum("enr,erk->enk", np.asarray(b, np.float64),
-                                                     np.asarray(a, np.float64))
+    return np.asarray(w, np.float64) + s * np.matmul(np.asarray(b, np.float64), np.asarray(a, np.float64))
 
 
 def forward_backward(x, dy, topk_idx, topk_w, w_gate, w_up, w_down, ad: Dict[str, np.ndarray], s: float):

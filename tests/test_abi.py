@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(B):
     names = declared_functions()
-    assert len(names) == 27, names
+    assert len(names) == 30, names
     for n in names:
         assert hasattr(B.lib, n), n
 
@@ -133,6 +133,31 @@ def test_fused_forward_validation(B):
     assert W(s, F, F, F, F, F, F, 2, F, need, None) == 1
     assert W(s, F, F, F, F, F, F, 0, F, need - 1, None) == 3
     assert W(big, F, F, F, F, F, F, 0, F, B.moe_workspace_bytes(big), None) == 2
+
+
+def test_lora_validation(B):
+    F = FAKE
+    s = B.shape(64, 128, 8, 2, 64, "bf16")
+    need = B.moe_lora_workspace_bytes(s, 16)
+    # workspace: the padded rank's stacks, projections and partial tiles
+    assert need >= 64 * 2 * 2 * 64 * 2
+    assert B.moe_lora_workspace_bytes(s, 12) == 0             # r % 8
+    assert B.moe_lora_workspace_bytes(s, 136) == 0            # r > 128
+    assert B.moe_lora_workspace_bytes(B.shape(64, 128, 8, 2, 64, "f32"), 16) == 0
+    M = B.lib.moe_lora_merge
+    assert M(0, 64, 128, 16, 1.0, F, F, F, F, None) == 1
+    assert M(8, 64, 128, 0, 1.0, F, F, F, F, None) == 1
+    assert M(8, 64, 128, 16, 1.0, F, None, F, F, None) == 1
+    assert M(8, 64, 124, 16, 1.0, F, F, F, F, None) == 2      # K % 8
+    assert M(8, 64, 128, 20, 1.0, F, F, F, F, None) == 2      # r % 8
+    assert M(8, 64, 128, 256, 1.0, F, F, F, F, None) == 2     # r > 128
+    G = B.lib.moe_lora_grads
+    P = [F] * 18
+    assert G(s, 16, 1.0, *P, need - 1, None) == 3
+    assert G(s, 0, 1.0, *P, need, None) == 1
+    assert G(s, 20, 1.0, *P, need, None) == 2
+    assert G(B.shape(64, 96, 8, 2, 64, "bf16"), 16, 1.0, *P, need, None) == 2
+    assert G(s, 16, 1.0, *P[:5], None, *P[6:], need, None) == 1
 
 
 def test_binding_raises_on_error(B):
