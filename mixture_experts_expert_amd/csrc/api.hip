@@ -477,8 +477,8 @@ moe_status check_lora(const moe_shape& s, int32_t r) {
   if (r <= 0) return MOE_EINVAL;
   if (s.dtype != MOE_BF16 || r > 128 || r % 8 != 0) return MOE_EUNSUPPORTED;
   const int rp = moe::lora_padded_rank(r);
-  const int hi[8][2] = {{2 * rp, s.H}, {rp, s.I}, {2 * rp, 2 * s.I}, {rp, s.H},
-                        {2 * s.I, 2 * rp}, {2 * rp, s.H}, {s.H, rp}, {rp, s.I}};
+  const int hi[7][2] = {{2 * rp, s.H}, {rp, s.I}, {2 * rp, 2 * s.I}, {rp, s.H},
+                        {2 * s.I, 2 * rp}, {s.H, rp}, {rp, s.I}};
   for (const auto& d : hi)
     if ((st = check_shape(moe::lora_gemm_shape(s, d[0], d[1]))) != MOE_OK) return st;
   return MOE_OK;
@@ -495,6 +495,8 @@ moe_status moe_lora_merge(int32_t E, int32_t N, int32_t K, int32_t r, float scal
   if (E <= 0 || N <= 0 || K <= 0 || r <= 0) return MOE_EINVAL;
   if (any_null(w, a, b, w_out)) return MOE_EINVAL;
   if (r > 128 || r % 8 != 0 || K % 8 != 0 || E > 65535 || (N + 127) / 128 > 65535) return MOE_EUNSUPPORTED;
+  // One expert's weights are addressed with 32-bit byte offsets.
+  if (static_cast<int64_t>(N + 128) * K >= (static_cast<int64_t>(1) << 30)) return MOE_EUNSUPPORTED;
   return from_hip(moe::launch_lora_merge(E, N, K, r, scale, w, a, b, w_out, stream));
 }
 

@@ -18,56 +18,79 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer loads: a wavefront-uniform base and byte range; a lane whose
+// offset falls outside the range reads zeros (no branch, so the compiler
+// can count the loads in flight exactly).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 load16(rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 constexpr int kThreads = 256;
 constexpr int kMT = 128;          // merge tile: 128 weight rows x 128 weight columns of one expert
+constexpr int kMergeRowTiles = 4; // row tiles per merge block
 constexpr int kMaxRank = 128;
 constexpr int kLdsRow = kMaxRank + 8;  // A^T row in LDS (bf16); +8 keeps rows 16-byte aligned and off one bank
+constexpr int kStageRow = kMT + 4;     // fp32 stage row: 16-byte aligned, rows 4 banks apart
+static_assert(kMT * kLdsRow * 2 <= kMT * kStageRow * 4, "A^T fits in the stage region");
+
+// Workgroup barrier for LDS hand-offs: waits for this wavefront's LDS
+// traffic only (s_waitcnt lgkmcnt(0), vmcnt and expcnt unconstrained: gfx9
+// encoding 0xC07F), so global loads issued ahead stay in flight; a
+// __syncthreads() would wait for them too. The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ float bf16f(bf16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
 
 // W'[e][n][c] = bf16(W[e][n][c] + s * sum_j B[e][n][j] A[e][j][c]): the sum
 // on the matrix cores (v_mfma_f32_32x32x16_bf16, exact bf16 products, fp32
-// accumulation), the scale and the add in fp32, one rounding.
+// accumulation in j order), the scale and the add in fp32, one rounding.
 //
-// Block: 128 columns x 128 rows of expert blockIdx.z, 4 wavefronts of
-// 64 x 64 (2 x 2 MFMA blocks of 32 x 32). MFMA rows are weight columns
-// (operand: A^T, staged transposed in LDS), MFMA columns weight rows
-// (operand: B's rows, 16 contiguous bytes per lane straight from memory).
-// Lane l then holds, per block and i < 4, four consecutive weight columns
-// 8i + 4(l/32) .. + 3 of weight row l%32; a half-wave exchange pairs them
-// into eight (16 bytes) so W is read and W' written in 16-byte pieces. The
-// W loads are issued before the reduction so that they are in flight during it.
-// w_out may be w: every element is read and written by the same lane.
-__global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, float s, const bf16_t* __restrict__ w,
+// Block: 128 columns of expert blockIdx.z and up to kMergeRowTiles tiles of
+// 128 rows; 4 wavefronts, each 64 columns x 64 rows of a tile (2 x 2 MFMA
+// blocks of 32 x 32). MFMA rows are weight columns: the operand is A^T,
+// staged transposed in LDS once per block and then held in registers for
+// every row tile. MFMA columns are weight rows: the operand is B's rows, 16
+// contiguous bytes per lane straight from memory. The sums go through LDS
+// (fp32, the region A^T used) so that W is read and W' written in row runs:
+// 16 lanes cover a row's 256 bytes, each lane 16 bytes (the MFMA layout
+// itself gives each lane 8-byte pieces of 32 different rows, which streams
+// at about half the rate). A row tile's loads (B fragments and W) are
+// issued during the previous tile's epilogue. NS = ceil(r / 16) reduction
+// steps. w_out may be w: every element is read and written by the same
+// thread.
+template <int NS>
+__global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, float s, const bf16_t* w,
                                                          const bf16_t* __restrict__ a, const bf16_t* __restrict__ b,
                                                          bf16_t* w_out) {
-  __shared__ __attribute__((aligned(16))) bf16_t at[kMT * kLdsRow];
+  __shared__ __attribute__((aligned(16))) float lds[kMT * kStageRow];
+  bf16_t* at = reinterpret_cast<bf16_t*>(lds);  // A^T [128][kLdsRow], then the fp32 stage [128][kStageRow]
   const int e = blockIdx.z;
-  const int c0 = blockIdx.x * kMT, n0 = blockIdx.y * kMT;
+  const int c0 = blockIdx.x * kMT, nbeg = blockIdx.y * kMT * kMergeRowTiles;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wc = wave & 1, wn = wave >> 1;
   const int h = lane >> 5, l32 = lane & 31;
-  const int r16 = (r + 15) & ~15;
   const int64_t wbase = static_cast<int64_t>(e) * N * K;
-
-  // This lane's W pieces: block (tc, tn), pair p -> row n, columns col .. col + 7.
-  uint4 wv[2][2][2];
-#pragma unroll
-  for (int tc = 0; tc < 2; ++tc)
-#pragma unroll
-    for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int n = n0 + wn * 64 + tn * 32 + l32;
-        const int col = c0 + wc * 64 + tc * 32 + 16 * p + 8 * h;
-        wv[tc][tn][p] = n < N && col < K ? *reinterpret_cast<const uint4*>(w + wbase + static_cast<int64_t>(n) * K + col)
-                                         : make_uint4(0, 0, 0, 0);
-      }
+  // Row runs of the epilogue: pass q covers tile rows 16q + tid/16, columns
+  // 8 (tid%16) .. + 7.
+  const int rrow = tid >> 4, rcol = (tid & 15) * 8;
 
   // A[e][j][c0 .. c0 + 127] -> at[c][j] (zeros past r and past K).
   const bf16_t* ae = a + static_cast<int64_t>(e) * r * K;
-  for (int q = tid; q < r16 * (kMT / 8); q += kThreads) {
+  for (int q = tid; q < NS * 16 * (kMT / 8); q += kThreads) {
     const int j = q / (kMT / 8), ch = q % (kMT / 8);
     const int col = c0 + ch * 8;
     uint4 v = make_uint4(0, 0, 0, 0);
@@ -77,120 +100,156 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
     for (int t = 0; t < 8; ++t) at[(ch * 8 + t) * kLdsRow + j] = static_cast<bf16_t>(u[t >> 1] >> (16 * (t & 1)));
   }
   __syncthreads();
-
-  f32x16 acc[2][2];
+  bf16x8 fa[2][NS];
 #pragma unroll
   for (int tc = 0; tc < 2; ++tc)
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn) acc[tc][tn] = f32x16{};
+    for (int q = 0; q < NS; ++q)
+      fa[tc][q] = *reinterpret_cast<const bf16x8*>(&at[(wc * 64 + tc * 32 + l32) * kLdsRow + 16 * q + 8 * h]);
+
   const bf16_t* be = b + static_cast<int64_t>(e) * N * r;
-  for (int j0 = 0; j0 < r16; j0 += 16) {
-    const int j = j0 + 8 * h;  // this lane's 8 reduction indices
-    bf16x8 fa[2], fb[2];
-#pragma unroll
-    for (int tc = 0; tc < 2; ++tc)
-      fa[tc] = *reinterpret_cast<const bf16x8*>(&at[(wc * 64 + tc * 32 + l32) * kLdsRow + j]);
+  const bool cok = c0 + rcol < K;
+  bf16x8 fb[2][NS];
+  uint4 wv[2][kMT / 16];  // W row runs of the current and the next row tile
+  const rsrc_t rw = make_rsrc(w + wbase, 2 * N * K), rb = make_rsrc(be, 2 * N * r);
+  auto load_tile = [&](int nt, uint4 (&wt)[kMT / 16]) __attribute__((always_inline)) {
 #pragma unroll
     for (int tn = 0; tn < 2; ++tn) {
-      const int n = n0 + wn * 64 + tn * 32 + l32;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n < N && j < r) v = *reinterpret_cast<const uint4*>(be + static_cast<int64_t>(n) * r + j);
-      fb[tn] = __builtin_bit_cast(bf16x8, v);
+      const int n = nt + wn * 64 + tn * 32 + l32;  // rows past N read zeros
+#pragma unroll
+      for (int q = 0; q < NS; ++q) {
+        const int j = 16 * q + 8 * h;
+        fb[tn][q] = __builtin_bit_cast(bf16x8, load16(rb, j < r ? 2u * static_cast<uint32_t>(n * r + j) : kOutOfRange));
+      }
     }
+#pragma unroll
+    for (int q = 0; q < kMT / 16; ++q) {
+      const int n = nt + 16 * q + rrow;
+      wt[q] = load16(rw, cok ? 2u * static_cast<uint32_t>(n * K + c0 + rcol) : kOutOfRange);
+    }
+  };
+  load_tile(nbeg, wv[0]);
+#pragma unroll
+  for (int t = 0; t < kMergeRowTiles; ++t) {
+    const int nt = nbeg + t * kMT;
+    if (nt >= N) break;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int tc = 0; tc < 2; ++tc)
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn) {
+        acc[tc][tn] = f32x16{};
+#pragma unroll
+        for (int q = 0; q < NS; ++q)
+          acc[tc][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tc][q], fb[tn][q], acc[tc][tn], 0, 0, 0);
+      }
+    // The next tile's loads fly during this tile's epilogue.
+    if (t + 1 < kMergeRowTiles && nt + kMT < N) load_tile(nt + kMT, wv[(t + 1) & 1]);
+    lds_barrier();  // A^T (first tile) or the previous tile's stage has been read
+    // Lane l holds, per block and i < 4, columns 8i + 4(l/32) .. + 3 of row l%32.
 #pragma unroll
     for (int tc = 0; tc < 2; ++tc)
 #pragma unroll
       for (int tn = 0; tn < 2; ++tn)
-        acc[tc][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tc], fb[tn], acc[tc][tn], 0, 0, 0);
-  }
-
 #pragma unroll
-  for (int tc = 0; tc < 2; ++tc)
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<float4*>(&lds[(wn * 64 + tn * 32 + l32) * kStageRow + wc * 64 + tc * 32 + 8 * i + 4 * h]) =
+              make_float4(acc[tc][tn][4 * i], acc[tc][tn][4 * i + 1], acc[tc][tn][4 * i + 2], acc[tc][tn][4 * i + 3]);
+    lds_barrier();
+    const uint4 (&wc_t)[kMT / 16] = wv[t & 1];
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn)
+    for (int q = 0; q < kMT / 16; ++q) {
+      const int n = nt + 16 * q + rrow;
+      if (n >= N || !cok) continue;
+      const float* sp = &lds[(16 * q + rrow) * kStageRow + rcol];
+      const float4 v0 = *reinterpret_cast<const float4*>(sp), v1 = *reinterpret_cast<const float4*>(sp + 4);
+      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      const uint32_t win[4] = {wc_t[q].x, wc_t[q].y, wc_t[q].z, wc_t[q].w};
+      uint32_t o[4];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        // Columns 16p .. 16p + 15 of the block: lane half 0 keeps 16p + 0..3
-        // and takes 16p + 4..7 from its partner; half 1 takes 16p + 8..11 and
-        // keeps 16p + 12..15.
-        float v[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float mine0 = acc[tc][tn][4 * (2 * p) + q], mine1 = acc[tc][tn][4 * (2 * p + 1) + q];
-          const float other = __shfl_xor(h ? mine0 : mine1, 32, 64);
-          v[q] = h ? other : mine0;
-          v[4 + q] = h ? mine1 : other;
-        }
-        const int n = n0 + wn * 64 + tn * 32 + l32;
-        const int col = c0 + wc * 64 + tc * 32 + 16 * p + 8 * h;
-        if (n >= N || col >= K) continue;
-        const uint4 wi = wv[tc][tn][p];
-        const uint32_t win[4] = {wi.x, wi.y, wi.z, wi.w};
-        uint32_t o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float lo = __uint_as_float(win[q] << 16) + s * v[2 * q];
-          const float hi = __uint_as_float(win[q] & 0xffff0000u) + s * v[2 * q + 1];
-          o[q] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
-        }
-        *reinterpret_cast<uint4*>(w_out + wbase + static_cast<int64_t>(n) * K + col) = make_uint4(o[0], o[1], o[2], o[3]);
+      for (int p = 0; p < 4; ++p) {
+        const float lo = __uint_as_float(win[p] << 16) + s * v[2 * p];
+        const float hi = __uint_as_float(win[p] & 0xffff0000u) + s * v[2 * p + 1];
+        o[p] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
       }
+      *reinterpret_cast<uint4*>(w_out + wbase + static_cast<int64_t>(n) * K + c0 + rcol) =
+          make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t scale_pair(uint32_t v, float s) {
+  const float lo = s * __uint_as_float(v << 16), hi = s * __uint_as_float(v & 0xffff0000u);
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
 // Stacked, scaled adapter rows, each block padded to rp rows:
 //   out[e][blk rp + j][c] = bf16(s in_blk[e][j][c]) for j < r, else 0,
 // blk < 2 when in1 is given (gate then up), else blk = 0; in_blk [E][r][K].
-__global__ __launch_bounds__(kThreads) void stack_a_kernel(int E, int r, int rp, int K, float s,
+// Block x = output row, threads over its 16-byte chunks.
+__global__ __launch_bounds__(kThreads) void stack_a_kernel(int r, int rp, int K, float s,
                                                            const bf16_t* __restrict__ in0,
                                                            const bf16_t* __restrict__ in1, bf16_t* __restrict__ out) {
+  const int row = blockIdx.x;
+  const int c = (blockIdx.y * kThreads + threadIdx.x) * 8;
+  if (c >= K) return;
   const int nb = in1 ? 2 : 1;
-  const int64_t q = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t per = static_cast<int64_t>(nb) * rp * K;
-  if (q >= per * E) return;
-  const int e = static_cast<int>(q / per);
-  const int64_t rem = q - e * per;
-  const int row = static_cast<int>(rem / K), c = static_cast<int>(rem - static_cast<int64_t>(row) * K);
-  const int blk = row / rp, j = row - blk * rp;
-  float v = 0.0f;
-  if (j < r) v = s * bf16f((blk ? in1 : in0)[(static_cast<int64_t>(e) * r + j) * K + c]);
-  out[q] = f32_to_bf16(v);
+  const int e = row / (nb * rp), rem = row - e * nb * rp, blk = rem / rp, j = rem - blk * rp;
+  uint4 o = make_uint4(0, 0, 0, 0);
+  if (j < r) {
+    const uint4 v = *reinterpret_cast<const uint4*>((blk ? in1 : in0) + (static_cast<int64_t>(e) * r + j) * K + c);
+    o = make_uint4(scale_pair(v.x, s), scale_pair(v.y, s), scale_pair(v.z, s), scale_pair(v.w, s));
+  }
+  *reinterpret_cast<uint4*>(out + static_cast<int64_t>(row) * K + c) = o;
 }
 
 // Block-diagonal transposed stack: out[e][J][c], J < nb rp, c < nb C, with
 // J = bj rp + j, c = bc C + cc: bf16(s in_bj[e][cc][j]) where bj == bc and
-// j < r, else 0; in_b [E][C][r], nb = 2 when in1 is given.
-__global__ __launch_bounds__(kThreads) void blockdiag_t_kernel(int E, int C, int r, int rp, float s,
+// j < r, else 0; in_b [E][C][r], nb = 2 when in1 is given, C % 64 == 0.
+// Block (x, e): output columns 64x .. 64x + 63, all of one block column bc;
+// their 64 rows of in_bc are read whole into LDS and written out transposed.
+__global__ __launch_bounds__(kThreads) void blockdiag_t_kernel(int C, int r, int rp, float s,
                                                                const bf16_t* __restrict__ in0,
                                                                const bf16_t* __restrict__ in1,
                                                                bf16_t* __restrict__ out) {
+  __shared__ float tile[64][kMaxRank + 1];
   const int nb = in1 ? 2 : 1;
-  const int64_t q = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t per = static_cast<int64_t>(nb) * rp * nb * C;
-  if (q >= per * E) return;
-  const int e = static_cast<int>(q / per);
-  const int64_t rem = q - e * per;
-  const int J = static_cast<int>(rem / (nb * C)), c = static_cast<int>(rem - static_cast<int64_t>(J) * nb * C);
-  const int bj = J / rp, j = J - bj * rp, bc = c / C, cc = c - bc * C;
-  float v = 0.0f;
-  if (bj == bc && j < r) v = s * bf16f((bj ? in1 : in0)[(static_cast<int64_t>(e) * C + cc) * r + j]);
-  out[q] = f32_to_bf16(v);
+  const int e = blockIdx.y, c0 = blockIdx.x * 64, bc = c0 / C, cc0 = c0 - bc * C;
+  const int tid = threadIdx.x;
+  const bf16_t* src = (bc ? in1 : in0) + (static_cast<int64_t>(e) * C + cc0) * r;
+  for (int q = tid; q < 64 * r; q += kThreads) tile[q / r][q % r] = s * bf16f(src[q]);
+  __syncthreads();
+  // Thread: output columns 8 (tid%8) .. + 7 of rows J = tid/8, tid/8 + 32, ...
+  const int cq = (tid & 7) * 8;
+  bf16_t* dst = out + static_cast<int64_t>(e) * nb * rp * nb * C + c0 + cq;
+  for (int J = tid >> 3; J < nb * rp; J += kThreads / 8) {
+    const int bj = J / rp, j = J - bj * rp;
+    const bool live = bj == bc && j < r;
+    uint32_t o[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float lo = live ? tile[cq + 2 * p][j] : 0.0f, hi = live ? tile[cq + 2 * p + 1][j] : 0.0f;
+      o[p] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    }
+    *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(J) * nb * C) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
 }
 
-// dst[e][i][j] = src[e][row0 + i][col0 + j] for i < rows, j < cols; src has
-// src_rows rows of src_cols floats per expert.
-__global__ __launch_bounds__(kThreads) void extract_kernel(int E, int rows, int cols, const float* __restrict__ src,
+// dst[e][i][j] = src[e][row0 + i][col0 + j] for i < rows, j < cols (cols,
+// col0 and src_cols multiples of 4); src has src_rows rows of src_cols
+// floats per expert. One thread per 16 bytes.
+__global__ __launch_bounds__(kThreads) void extract_kernel(int64_t total4, int rows, int cols, const float* __restrict__ src,
                                                            int src_rows, int src_cols, int row0, int col0,
                                                            float* __restrict__ dst) {
   const int64_t q = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t per = static_cast<int64_t>(rows) * cols;
-  if (q >= per * E) return;
-  const int e = static_cast<int>(q / per);
-  const int64_t rem = q - e * per;
-  const int i = static_cast<int>(rem / cols), j = static_cast<int>(rem - static_cast<int64_t>(i) * cols);
-  dst[q] = src[(static_cast<int64_t>(e) * src_rows + row0 + i) * src_cols + col0 + j];
+  if (q >= total4) return;
+  const int c4 = cols / 4;
+  const int64_t row = q / c4;  // e * rows + i
+  const int j = static_cast<int>(q - row * c4) * 4;
+  const int64_t e = row / rows, i = row - e * rows;
+  *reinterpret_cast<float4*>(dst + q * 4) =
+      *reinterpret_cast<const float4*>(src + (e * src_rows + row0 + i) * src_cols + col0 + j);
 }
-
-inline unsigned blocks_for(int64_t n) { return static_cast<unsigned>(ceil_div64(n, kThreads)); }
 
 // out [M, N] = rows [M, K] x W[e]^T over each expert's rows, W [E, N, K]: the
 // "down" GEMM with H = N, I = K.
@@ -247,7 +306,8 @@ LoraLayout lora_layout(const moe_shape& s, int r) {
   l.z_d = take(M * rp * 2);
   l.y_gu = take(M * 2 * rp * 2);
   l.y_d = take(M * rp * 2);
-  l.da_gu = take(E * 2 * rp * H * 4);
+  l.da_g = take(E * rp * H * 4);
+  l.da_u = take(E * rp * H * 4);
   l.db_gu = take(E * 2 * I * 2 * rp * 4);
   l.da_d = take(E * rp * I * 4);
   l.db_d = take(E * H * rp * 4);
@@ -258,10 +318,23 @@ LoraLayout lora_layout(const moe_shape& s, int r) {
 
 hipError_t launch_lora_merge(int E, int N, int K, int r, float s, const void* w, const void* a, const void* b,
                              void* w_out, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(ceil_div(K, kMT)), static_cast<unsigned>(ceil_div(N, kMT)),
+  const dim3 grid(static_cast<unsigned>(ceil_div(K, kMT)), static_cast<unsigned>(ceil_div(N, kMT * kMergeRowTiles)),
                   static_cast<unsigned>(E));
-  merge_kernel<<<grid, kThreads, 0, st>>>(N, K, r, s, static_cast<const bf16_t*>(w), static_cast<const bf16_t*>(a),
-                                          static_cast<const bf16_t*>(b), static_cast<bf16_t*>(w_out));
+  const bf16_t* wp = static_cast<const bf16_t*>(w);
+  const bf16_t* ap = static_cast<const bf16_t*>(a);
+  const bf16_t* bp = static_cast<const bf16_t*>(b);
+  bf16_t* op = static_cast<bf16_t*>(w_out);
+  switch ((r + 15) / 16) {
+    case 1: merge_kernel<1><<<grid, kThreads, 0, st>>>(N, K, r, s, wp, ap, bp, op); break;
+    case 2: merge_kernel<2><<<grid, kThreads, 0, st>>>(N, K, r, s, wp, ap, bp, op); break;
+    case 3: merge_kernel<3><<<grid, kThreads, 0, st>>>(N, K, r, s, wp, ap, bp, op); break;
+    case 4: merge_kernel<4><<<grid, kThreads, 0, st>>>(N, K, r, s, wp, ap, bp, op); break;
+    case 5: merge_kernel<5><<<grid, kThreads, 0, st>>>(N, K, r, s, wp, ap, bp, op); break;
+    case 6: merge_kernel<6><<<grid, kThreads, 0, st>>>(N, K, r, s, wp, ap, bp, op); break;
+    case 7: merge_kernel<7><<<grid, kThreads, 0, st>>>(N, K, r, s, wp, ap, bp, op); break;
+    case 8: merge_kernel<8><<<grid, kThreads, 0, st>>>(N, K, r, s, wp, ap, bp, op); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -276,13 +349,15 @@ hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraA
   void* z_d = base + l.z_d;
   void* y_gu = base + l.y_gu;
   void* y_d = base + l.y_d;
-  float* da_gu = reinterpret_cast<float*>(base + l.da_gu);
   float* db_gu = reinterpret_cast<float*>(base + l.db_gu);
   float* part = reinterpret_cast<float*>(base + l.part);
   const int E = s.E, H = s.H, I = s.I, rp = lora_padded_rank(r);
-  // With rp == r the down-projection gradients land in place.
-  float* da_d = rp == r ? g.da_down : reinterpret_cast<float*>(base + l.da_d);
-  float* db_d = rp == r ? g.db_down : reinterpret_cast<float*>(base + l.db_d);
+  // With rp == r the dA and dB_down gradients land in place.
+  const bool padded = rp != r;
+  float* da_g = padded ? reinterpret_cast<float*>(base + l.da_g) : g.da_gate;
+  float* da_u = padded ? reinterpret_cast<float*>(base + l.da_u) : g.da_up;
+  float* da_d = padded ? reinterpret_cast<float*>(base + l.da_d) : g.da_down;
+  float* db_d = padded ? reinterpret_cast<float*>(base + l.db_d) : g.db_down;
   const bf16_t* a_gate = static_cast<const bf16_t*>(g.a_gate);
   const bf16_t* a_up = static_cast<const bf16_t*>(g.a_up);
   const bf16_t* a_down = static_cast<const bf16_t*>(g.a_down);
@@ -294,42 +369,52 @@ hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraA
   if ((err = (x)) != hipSuccess) return err
   // Scaled, stacked adapters (bf16, rounded once): sA_gu = [sA_gate; sA_up],
   // sA_d, the transposed block diagonal of sB_gate and sB_up, sB_down^T.
-  stack_a_kernel<<<blocks_for(int64_t{E} * 2 * rp * H), kThreads, 0, st>>>(E, r, rp, H, scale, a_gate, a_up, sa_gu);
+  stack_a_kernel<<<dim3(E * 2 * rp, ceil_div(H / 8, kThreads)), kThreads, 0, st>>>(r, rp, H, scale, a_gate, a_up,
+                                                                                     sa_gu);
   MOE_TRY(hipGetLastError());
-  stack_a_kernel<<<blocks_for(int64_t{E} * rp * I), kThreads, 0, st>>>(E, r, rp, I, scale, a_down, nullptr, sa_d);
+  stack_a_kernel<<<dim3(E * rp, ceil_div(I / 8, kThreads)), kThreads, 0, st>>>(r, rp, I, scale, a_down, nullptr,
+                                                                                 sa_d);
   MOE_TRY(hipGetLastError());
-  blockdiag_t_kernel<<<blocks_for(int64_t{E} * 4 * rp * I), kThreads, 0, st>>>(E, I, r, rp, scale, b_gate, b_up,
-                                                                               sbt_gu);
+  blockdiag_t_kernel<<<dim3(2 * I / 64, E), kThreads, 0, st>>>(I, r, rp, scale, b_gate, b_up, sbt_gu);
   MOE_TRY(hipGetLastError());
-  blockdiag_t_kernel<<<blocks_for(int64_t{E} * rp * H), kThreads, 0, st>>>(E, H, r, rp, scale, b_down, nullptr,
-                                                                           sbt_d);
+  blockdiag_t_kernel<<<dim3(H / 64, E), kThreads, 0, st>>>(H, r, rp, scale, b_down, nullptr, sbt_d);
   MOE_TRY(hipGetLastError());
   // Row projections Z = X (sA)^T, Y = dY (sB).
   MOE_TRY(row_projection(s, 2 * rp, H, g.offsets, g.x_perm, sa_gu, z_gu, st));    // [Z_gate | Z_up]
   MOE_TRY(row_projection(s, rp, I, g.offsets, g.act, sa_d, z_d, st));             // Z_down
   MOE_TRY(row_projection(s, 2 * rp, 2 * I, g.offsets, g.dgu, sbt_gu, y_gu, st));  // [dG sB_gate | dU sB_up]
   MOE_TRY(row_projection(s, rp, H, g.offsets, g.do_perm, sbt_d, y_d, st));        // dO sB_down
-  // Outer products over each expert's rows.
+  // Outer products over each expert's rows. [Y_gate | Y_up]^T X has the
+  // layout of the gate/up weight gradient with I = rp: its two halves go to
+  // dA_gate and dA_up directly.
+  {
+    GemmArgs ga{};
+    ga.offsets = g.offsets;
+    ga.a = y_gu;
+    ga.b0 = g.x_perm;
+    ga.dw0 = da_g;
+    ga.dw1 = da_u;
+    ga.part = part;
+    MOE_TRY(launch_gemm(GEMM_WGRAD_GATEUP, lora_gemm_shape(s, H, rp), ga, st));
+  }
   MOE_TRY(outer_product(s, 2 * I, 2 * rp, g.offsets, g.dgu, z_gu, db_gu, part, st));  // [dG | dU]^T [Z_gate | Z_up]
-  MOE_TRY(outer_product(s, 2 * rp, H, g.offsets, y_gu, g.x_perm, da_gu, part, st));   // [Y_gate | Y_up]^T X
   MOE_TRY(outer_product(s, H, rp, g.offsets, g.do_perm, z_d, db_d, part, st));       // dO^T Z_down
   MOE_TRY(outer_product(s, rp, I, g.offsets, y_d, g.act, da_d, part, st));           // Y_down^T Act
   // The adapters' own blocks.
-  extract_kernel<<<blocks_for(int64_t{E} * r * H), kThreads, 0, st>>>(E, r, H, da_gu, 2 * rp, H, 0, 0, g.da_gate);
-  MOE_TRY(hipGetLastError());
-  extract_kernel<<<blocks_for(int64_t{E} * r * H), kThreads, 0, st>>>(E, r, H, da_gu, 2 * rp, H, rp, 0, g.da_up);
-  MOE_TRY(hipGetLastError());
-  extract_kernel<<<blocks_for(int64_t{E} * I * r), kThreads, 0, st>>>(E, I, r, db_gu, 2 * I, 2 * rp, 0, 0,
-                                                                      g.db_gate);
-  MOE_TRY(hipGetLastError());
-  extract_kernel<<<blocks_for(int64_t{E} * I * r), kThreads, 0, st>>>(E, I, r, db_gu, 2 * I, 2 * rp, I, rp,
-                                                                      g.db_up);
-  MOE_TRY(hipGetLastError());
-  if (rp != r) {
-    extract_kernel<<<blocks_for(int64_t{E} * r * I), kThreads, 0, st>>>(E, r, I, da_d, rp, I, 0, 0, g.da_down);
-    MOE_TRY(hipGetLastError());
-    extract_kernel<<<blocks_for(int64_t{E} * H * r), kThreads, 0, st>>>(E, H, r, db_d, H, rp, 0, 0, g.db_down);
-    MOE_TRY(hipGetLastError());
+  auto extract = [&](int rows, int cols, const float* src, int src_rows, int src_cols, int row0, int col0,
+                     float* dst) {
+    const int64_t total4 = static_cast<int64_t>(E) * rows * cols / 4;
+    extract_kernel<<<static_cast<unsigned>(ceil_div64(total4, kThreads)), kThreads, 0, st>>>(
+        total4, rows, cols, src, src_rows, src_cols, row0, col0, dst);
+    return hipGetLastError();
+  };
+  MOE_TRY(extract(I, r, db_gu, 2 * I, 2 * rp, 0, 0, g.db_gate));
+  MOE_TRY(extract(I, r, db_gu, 2 * I, 2 * rp, I, rp, g.db_up));
+  if (padded) {
+    MOE_TRY(extract(r, H, da_g, rp, H, 0, 0, g.da_gate));
+    MOE_TRY(extract(r, H, da_u, rp, H, 0, 0, g.da_up));
+    MOE_TRY(extract(r, I, da_d, rp, I, 0, 0, g.da_down));
+    MOE_TRY(extract(H, r, db_d, H, rp, 0, 0, g.db_down));
   }
 #undef MOE_TRY
   return hipSuccess;

@@ -175,7 +175,7 @@ moe_shape lora_gemm_shape(const moe_shape& s, int H, int I);  // s with H and I 
 struct LoraLayout {  // byte offsets in the adapter-gradient workspace
   size_t sa_gu, sa_d, sbt_gu, sbt_d;  // bf16 scaled adapter stacks
   size_t z_gu, z_d, y_gu, y_d;        // bf16 row projections [T*k][2rp | rp]
-  size_t da_gu, db_gu, da_d, db_d;    // fp32 padded gradients
+  size_t da_g, da_u, db_gu, da_d, db_d;  // fp32 padded gradients
   size_t part;                        // fp32 split-K partial tiles
   size_t total;
 };
