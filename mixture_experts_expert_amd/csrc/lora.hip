@@ -1,5 +1,6 @@
-// Low-rank adapters on the frozen experts (unsloth PR #3812, the LoRA path
-// of the grouped GEMM; axolotl issue #3155, fine-tuning Qwen3 MoE).
+// Low-rank adapters on the frozen, stacked experts (sourcepulse summary,
+// "Highlighted Details": LoRA and QLoRA on the fused experts, in the fused
+// adapter format; torchtune PR #2820: LoRA support for the Qwen3 MoE port).
 //
 // Forward and data gradients run the plain stage on merged weights
 // W' = W + s B A (one pass over each projection, merge_kernel below). The
@@ -251,16 +252,207 @@ __global__ __launch_bounds__(kThreads) void extract_kernel(int64_t total4, int r
       *reinterpret_cast<const float4*>(src + (e * src_rows + row0 + i) * src_cols + col0 + j);
 }
 
-// out [M, N] = rows [M, K] x W[e]^T over each expert's rows, W [E, N, K]: the
-// "down" GEMM with H = N, I = K.
-hipError_t row_projection(const moe_shape& s, int N, int K, const int32_t* offsets, const void* rows, const void* w,
-                          void* out, hipStream_t st) {
-  GemmArgs g{};
-  g.offsets = offsets;
-  g.a = rows;
-  g.b0 = w;
-  g.out0 = out;
-  return launch_gemm(GEMM_DOWN, lora_gemm_shape(s, N, K), g, st);
+// Rank-wide projections: out[p][n] = sum_k rows[p][k] W[e][n][k] over each
+// expert e's sorted rows p, W [E][N][K], N a multiple of 64 up to 32 NB,
+// K % 64 == 0; bf16 in and out, fp32 sums. One launch runs up to four such
+// jobs over the same experts (the four projections of the adapter
+// gradients), so that their tiles fill the chip together instead of each
+// leaving a tail.
+//
+// Tile: 128 rows of one expert x 32 NB columns (columns past the job's N
+// read zero weights and are not stored), 4 wavefronts of 32 rows. k-chunks
+// of 64 go global -> registers -> LDS (double-buffered; the loads of the
+// next two chunks are in flight during a chunk's MFMAs), each load
+// instruction covering 8 rows x 128 bytes. MFMA rows are output columns
+// (operand: W's rows), MFMA columns output rows (operand: the tile's rows),
+// so a lane holds four consecutive output columns of one row; a half-wave
+// exchange makes them eight for 16-byte stores. The tile list is built on
+// the device from the offsets (a block-wide scan of the experts' tile
+// counts), the jobs interleaved tile by tile, and cut into 8 contiguous
+// ranges, one per XCD, so an expert's tiles share its W in one L2.
+constexpr int kPR = 128;        // rows per projection tile
+constexpr int kPK = 64;         // k-chunk
+constexpr int kPLds = kPK + 8;  // LDS row (bf16): 144 bytes, rows 4 banks apart
+
+struct ProjJob {
+  const bf16_t* rows;  // [T*k][K]
+  const bf16_t* w;     // [E][N][K]
+  bf16_t* out;         // [T*k][N]
+  int K, N;
+};
+struct ProjJobs {
+  ProjJob job[4];
+  int n;
+};
+
+template <int NB>
+__global__ __launch_bounds__(kThreads) void proj_kernel(int E, const int32_t* __restrict__ offsets, ProjJobs jobs) {
+  constexpr int NMAX = 32 * NB;
+  __shared__ __attribute__((aligned(16))) bf16_t xs[2][kPR * kPLds];
+  __shared__ __attribute__((aligned(16))) bf16_t wl[2][NMAX * kPLds];
+  __shared__ int wsum[kThreads / 64];
+  __shared__ int found[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+
+  // Tile counts of experts 4 tid .. 4 tid + 3 and their exclusive prefix.
+  int cnt[4], sum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid * 4 + j;
+    cnt[j] = e < E ? (offsets[e + 1] - offsets[e] + kPR - 1) / kPR : 0;
+    sum += cnt[j];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int start = incl - sum, per_job = 0;
+#pragma unroll
+  for (int v = 0; v < kThreads / 64; ++v) {
+    start += v < wave ? wsum[v] : 0;
+    per_job += wsum[v];
+  }
+  const int total = per_job * jobs.n;
+  const int per_xcd = (total + 7) / 8;
+  const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (static_cast<int>(blockIdx.x / 8) >= per_xcd || t >= total) return;  // uniform over the block
+  const int jb = t % jobs.n, tt = t / jobs.n;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (tt >= start && tt < start + cnt[j]) {
+      found[0] = tid * 4 + j;
+      found[1] = tt - start;
+    }
+    start += cnt[j];
+  }
+  __syncthreads();
+  const int e = found[0];
+  const int r0 = offsets[e] + found[1] * kPR;
+  const int valid = min(kPR, offsets[e + 1] - r0);
+  const ProjJob& J = jobs.job[jb];
+  const int K = J.K, N = J.N;
+  const bf16_t* rows = J.rows;
+  const bf16_t* w = J.w;
+  bf16_t* out = J.out;
+
+  // Buffer ranges start at the chunk's first column: rows past the tile's
+  // valid ones fall outside and read zeros. The per-lane offsets stay fixed.
+  const bf16_t* abase = rows + static_cast<int64_t>(r0) * K;
+  const bf16_t* wbase = w + static_cast<int64_t>(e) * N * K;
+  // 16-byte pieces of a chunk: piece q is row q / 8, bytes 16 (q % 8) of its 128.
+  constexpr int PA = kPR * 8 / kThreads, PB = NMAX * 8 / kThreads;
+  uint32_t oa[PA], ob[PB];
+#pragma unroll
+  for (int i = 0; i < PA; ++i) {
+    const int q = tid + kThreads * i;
+    oa[i] = 2u * static_cast<uint32_t>((q >> 3) * K) + 16u * (q & 7);
+  }
+#pragma unroll
+  for (int i = 0; i < PB; ++i) {
+    const int q = tid + kThreads * i;
+    ob[i] = 2u * static_cast<uint32_t>((q >> 3) * K) + 16u * (q & 7);
+  }
+  uint4 pa[2][PA], pb[2][PB];  // two chunks in flight
+  auto load_chunk = [&](int k0, uint4 (&qa)[PA], uint4 (&qb)[PB]) __attribute__((always_inline)) {
+    // Past the last chunk the ranges are empty: the loads read zeros and
+    // touch no memory, so the loop needs no branch around them.
+    const bool live = k0 < K;
+    const rsrc_t ra = make_rsrc(abase + (live ? k0 : 0), live ? 2 * (valid * K - k0) : 0);
+    const rsrc_t rw = make_rsrc(wbase + (live ? k0 : 0), live ? 2 * (N * K - k0) : 0);
+#pragma unroll
+    for (int i = 0; i < PA; ++i) qa[i] = load16(ra, oa[i]);
+#pragma unroll
+    for (int i = 0; i < PB; ++i) qb[i] = load16(rw, ob[i]);
+  };
+  auto store_chunk = [&](int buf, const uint4 (&qa)[PA], const uint4 (&qb)[PB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PA; ++i) {
+      const int q = tid + kThreads * i;
+      *reinterpret_cast<uint4*>(&xs[buf][(q >> 3) * kPLds + (q & 7) * 8]) = qa[i];
+    }
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int q = tid + kThreads * i;
+      *reinterpret_cast<uint4*>(&wl[buf][(q >> 3) * kPLds + (q & 7) * 8]) = qb[i];
+    }
+  };
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
+  // LDS holds chunk c; register set (c + 1) % 2 holds chunk c + 1 and set
+  // c % 2 takes chunk c + 2 (issued during chunk c). The chunk count is
+  // rounded up to even: a chunk past the end is all zeros and adds nothing,
+  // so no step, load or store needs a branch (a branch would make the
+  // compiler wait for every load in flight at the join).
+  const int nch = (K / kPK + 1) & ~1;
+  load_chunk(0, pa[0], pb[0]);
+  load_chunk(kPK, pa[1], pb[1]);
+  store_chunk(0, pa[0], pb[0]);
+  lds_barrier();
+  auto step = [&](int c, uint4 (&na)[PA], uint4 (&nb_)[PB], uint4 (&ca)[PA], uint4 (&cb)[PB])
+      __attribute__((always_inline)) {
+    // na/nb_: the register set that held chunk c (free), now chunk c + 2;
+    // ca/cb: chunk c + 1, stored to LDS after this chunk's MFMAs.
+    const int buf = c & 1;
+    load_chunk((c + 2) * kPK, na, nb_);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this chunk's MFMAs
+#pragma unroll
+    for (int sl = 0; sl < kPK / 16; ++sl) {
+      const bf16x8 fx = *reinterpret_cast<const bf16x8*>(&xs[buf][(wave * 32 + l32) * kPLds + 16 * sl + 8 * h]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const bf16x8 fw = *reinterpret_cast<const bf16x8*>(&wl[buf][(nb * 32 + l32) * kPLds + 16 * sl + 8 * h]);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw, fx, acc[nb], 0, 0, 0);
+      }
+    }
+    store_chunk(buf ^ 1, ca, cb);
+    lds_barrier();  // chunk c + 1 is in LDS; nobody reads buffer buf any more
+  };
+  for (int c = 0; c < nch; c += 2) {
+    step(c, pa[0], pb[0], pa[1], pb[1]);
+    step(c + 1, pa[1], pb[1], pa[0], pb[0]);
+  }
+
+  // Lane l: output row wave * 32 + l%32, columns 8i + 4(l/32) .. + 3 of each 32-column block.
+  const int row = wave * 32 + l32;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float mine0 = acc[nb][4 * (2 * p) + q], mine1 = acc[nb][4 * (2 * p + 1) + q];
+        const float other = __shfl_xor(h ? mine0 : mine1, 32, 64);
+        v[q] = h ? other : mine0;
+        v[4 + q] = h ? mine1 : other;
+      }
+      if (row >= valid || nb * 32 >= N) continue;
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = static_cast<uint32_t>(f32_to_bf16(v[2 * q])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * q + 1])) << 16);
+      *reinterpret_cast<uint4*>(out + static_cast<int64_t>(r0 + row) * N + nb * 32 + 16 * p + 8 * h) =
+          make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+// The four rank-wide projections in one launch; nmax = the widest N.
+hipError_t projections(const moe_shape& s, int nmax, const int32_t* offsets, const ProjJobs& jobs, hipStream_t st) {
+  const int64_t M = static_cast<int64_t>(s.T) * s.k;
+  // >= the tile count (each job: at most M / 128 + E tiles), a multiple of 8.
+  const unsigned grid = static_cast<unsigned>(8 * ((jobs.n * (M / kPR + s.E) + 8) / 8));
+  switch (nmax / 32) {
+    case 4: proj_kernel<4><<<grid, kThreads, 0, st>>>(s.E, offsets, jobs); break;
+    case 8: proj_kernel<8><<<grid, kThreads, 0, st>>>(s.E, offsets, jobs); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // dW [E, Mo, No] = L_e^T R_e over each expert's rows, L [M, Mo], R [M, No]:
@@ -379,11 +571,18 @@ hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraA
   MOE_TRY(hipGetLastError());
   blockdiag_t_kernel<<<dim3(H / 64, E), kThreads, 0, st>>>(H, r, rp, scale, b_down, nullptr, sbt_d);
   MOE_TRY(hipGetLastError());
-  // Row projections Z = X (sA)^T, Y = dY (sB).
-  MOE_TRY(row_projection(s, 2 * rp, H, g.offsets, g.x_perm, sa_gu, z_gu, st));    // [Z_gate | Z_up]
-  MOE_TRY(row_projection(s, rp, I, g.offsets, g.act, sa_d, z_d, st));             // Z_down
-  MOE_TRY(row_projection(s, 2 * rp, 2 * I, g.offsets, g.dgu, sbt_gu, y_gu, st));  // [dG sB_gate | dU sB_up]
-  MOE_TRY(row_projection(s, rp, H, g.offsets, g.do_perm, sbt_d, y_d, st));        // dO sB_down
+  // Row projections Z = X (sA)^T, Y = dY (sB): [Z_gate | Z_up], [dG sB_gate |
+  // dU sB_up], Z_down, dO sB_down.
+  {
+    ProjJobs pj{};
+    const bf16_t* xp = static_cast<const bf16_t*>(g.x_perm);
+    pj.job[0] = {xp, sa_gu, static_cast<bf16_t*>(z_gu), H, 2 * rp};
+    pj.job[1] = {static_cast<const bf16_t*>(g.dgu), sbt_gu, static_cast<bf16_t*>(y_gu), 2 * I, 2 * rp};
+    pj.job[2] = {static_cast<const bf16_t*>(g.act), sa_d, static_cast<bf16_t*>(z_d), I, rp};
+    pj.job[3] = {static_cast<const bf16_t*>(g.do_perm), sbt_d, static_cast<bf16_t*>(y_d), H, rp};
+    pj.n = 4;
+    MOE_TRY(projections(s, 2 * rp, g.offsets, pj, st));
+  }
   // Outer products over each expert's rows. [Y_gate | Y_up]^T X has the
   // layout of the gate/up weight gradient with I = rp: its two halves go to
   // dA_gate and dA_up directly.
