@@ -36,7 +36,7 @@ __device__ __forceinline__ uint4 load16(rsrc_t r, uint32_t off) {
 
 constexpr int kThreads = 256;
 constexpr int kMT = 128;          // merge tile: 128 weight rows x 128 weight columns of one expert
-constexpr int kMergeRowTiles = 4; // row tiles per merge block
+constexpr int kMergeRowTiles = 2; // row tiles per merge block
 constexpr int kMaxRank = 128;
 constexpr int kLdsRow = kMaxRank + 8;  // A^T row in LDS (bf16); +8 keeps rows 16-byte aligned and off one bank
 constexpr int kStageRow = kMT + 4;     // fp32 stage row: 16-byte aligned, rows 4 banks apart
@@ -133,7 +133,6 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
 #pragma unroll
   for (int t = 0; t < kMergeRowTiles; ++t) {
     const int nt = nbeg + t * kMT;
-    if (nt >= N) break;
     f32x16 acc[2][2];
 #pragma unroll
     for (int tc = 0; tc < 2; ++tc)
@@ -145,7 +144,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
           acc[tc][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tc][q], fb[tn][q], acc[tc][tn], 0, 0, 0);
       }
     // The next tile's loads fly during this tile's epilogue.
-    if (t + 1 < kMergeRowTiles && nt + kMT < N) load_tile(nt + kMT, wv[(t + 1) & 1]);
+    // Rows past N read zeros and are not stored: no branch, so the
+    // compiler keeps these loads in flight across the epilogue's waits.
+    if (t + 1 < kMergeRowTiles) load_tile(nt + kMT, wv[(t + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
     lds_barrier();  // A^T (first tile) or the previous tile's stage has been read
     // Lane l holds, per block and i < 4, columns 8i + 4(l/32) .. + 3 of row l%32.
 #pragma unroll
