@@ -155,6 +155,52 @@ def cpu_baseline(cfg, seed: int, tokens: int) -> dict:
             "sample": f"{tokens} of {cfg.T} tokens (same H, E, k, I), fwd+bwd, {dt:.1f} s"}
 
 
+def time_calls(fn, stream, reps=10) -> float:
+    """Average ms of fn() over reps calls between two HIP events on stream (two untimed calls first)."""
+    import torch
+    for _ in range(2):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def lora_timing(cfg, seed: int, tensors, bias, stream, r: int = 64, scale: float = 2.0) -> dict:
+    """The training step with rank-r adapters on the frozen experts at the
+    same shape: the three merges W' = W + s B A, the forward on W', the data
+    gradients and the adapter gradients (no frozen-weight gradient); then
+    the merges and the adapter-gradient call on their own."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_expert_amd import binding as B
+    from mixture_experts_expert_amd import synth
+    x, wr, wg, wu, wd, dy = tensors
+    ad = {n: torch.from_numpy(v.view(np.int16)).to("cuda").view(torch.bfloat16)
+          for n, v in synth.make_adapters(cfg, r, seed).items()}
+    ls = B.LoRAStage(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, r, scale)
+    lb = ls.buf
+
+    def lora_step():
+        ls.forward(x, wr, wg, wu, wd, ad, bias)
+        ls.backward(dy)
+
+    out = {"rank": r, "scale": scale, "step": round(time_calls(lora_step, stream), 4)}
+    out["moe_lora_merge_x3"] = round(time_calls(lambda: ls.merge(wg, wu, wd, ad), stream, reps=5), 4)
+    out["moe_lora_grads"] = round(time_calls(lambda: B.moe_lora_grads(
+        ls.s, r, scale, lb["x_perm"], lb["a"], lb["dgu"], lb["do_perm"], lb["offsets"],
+        *(ad[n] for n in B.LORA_NAMES), *(lb["d" + n] for n in B.LORA_NAMES), ls.lora_ws), stream, reps=5), 4)
+    log(f"adapter step: {out}")
+    del ls, lb, ad
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +212,8 @@ def main() -> int:
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--timed-only", action="store_true",
                     help="launch nothing after the timed steps (for profiling): no sequential, inference or CPU pass")
+    ap.add_argument("--lora-only", action="store_true",
+                    help="only time the adapter (LoRA) step and its calls; prints {\"lora_ms\": ...}")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (PMC counter calibration)")
     args = ap.parse_args()
@@ -191,6 +239,12 @@ def main() -> int:
     dev = {n: torch.from_numpy(inp.bits[n].view(np.int16)).to("cuda").view(torch.bfloat16) for n in inp.names()}
     bias = None if inp.logit_bias is None else torch.from_numpy(inp.logit_bias).to("cuda")
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    if args.lora_only:
+        tensors = tuple(dev[n] for n in ["x", "w_router", "w_gate", "w_up", "w_down", "dy"])
+        print(json.dumps({"lora_ms": lora_timing(cfg, args.seed, tensors, bias, torch.cuda.current_stream()),
+                          "config": {"workload": cfg.name}}), flush=True)
+        return 0
 
     st = B.MoEStage(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, torch.bfloat16)
     st._alloc_bwd()
@@ -271,16 +325,7 @@ def main() -> int:
     log(f"timed {args.steps} steps: {ms:.3f} ms/step; " + ", ".join(f"{n}={v:.3f}" for n, v in per_call.items()))
 
     def time_fn(fn, reps=10):
-        for _ in range(2):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        return time_calls(fn, stream, reps)
 
     two_stream_ms = None if args.timed_only else round(time_fn(step_two_streams), 4)
     if two_stream_ms is not None:
@@ -397,29 +442,7 @@ def main() -> int:
         infer["fp8_down"] = round(time_fn(down8, reps=5), 4)
         log(f"inference forward: {infer}")
 
-    # Adapter training step at the same shape (rank 64, scale 2; outside the
-    # timed steps): the three merges W' = W + s B A, the forward on W', the
-    # data gradients and the adapter gradients; no frozen-weight gradient.
-    lora = None
-    if not args.timed_only:
-        r = 64
-        ad = {n: torch.from_numpy(v.view(np.int16)).to("cuda").view(torch.bfloat16)
-              for n, v in synth.make_adapters(cfg, r, args.seed).items()}
-        ls = B.LoRAStage(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, r, 2.0)
-        lb = ls.buf
-
-        def lora_step():
-            ls.forward(x, wr, wg, wu, wd, ad, bias)
-            ls.backward(dy)
-
-        lora = {"rank": r, "step": round(time_fn(lora_step), 4)}
-        lora["moe_lora_merge_x3"] = round(time_fn(lambda: ls.merge(wg, wu, wd, ad), reps=5), 4)
-        lora["moe_lora_grads"] = round(time_fn(lambda: B.moe_lora_grads(
-            ls.s, r, 2.0, lb["x_perm"], lb["a"], lb["dgu"], lb["do_perm"], lb["offsets"],
-            *(ad[n] for n in B.LORA_NAMES), *(lb["d" + n] for n in B.LORA_NAMES), ls.lora_ws), reps=5), 4)
-        log(f"adapter step: {lora}")
-        del ls, lb, ad
-        torch.cuda.empty_cache()
+    lora = None if args.timed_only else lora_timing(cfg, args.seed, (x, wr, wg, wu, wd, dy), bias, stream)
 
     flops = gemm_flops(cfg)
     nbytes = alg_bytes(cfg)

@@ -339,8 +339,10 @@ moe_status moe_forward_fused_fp8(moe_shape s, const void* x, const void* w_route
                                  float* row_weight, uint8_t* xq, uint8_t* x_e8, void* a, uint8_t* aq, uint8_t* a_e8,
                                  void* o_perm, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Low-rank adapters on the frozen experts (unsloth PR #3812, the LoRA path of
- * the grouped GEMM; axolotl issue #3155, fine-tuning Qwen3 MoE). Per expert e
+/* Low-rank adapters on the frozen experts (sourcepulse summary, "Highlighted
+ * Details": LoRA and QLoRA on the fused experts; torchtune PR #2820: LoRA
+ * support for the Qwen3 MoE port). Adapters come in the fused format, one
+ * stacked tensor per projection over all experts. Per expert e
  * and projection P in {gate, up, down} with frozen W_P [E,N,K] (w_gate, w_up
  * [E,I,H]; w_down [E,H,I]), adapters A_P [E,r,K] and B_P [E,N,r] (bf16) and
  * scale s, the stage is the plain one on W'_P = W_P + s B_P A_P. Training:

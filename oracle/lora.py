@@ -3,9 +3,12 @@
 TEST INFRASTRUCTURE ONLY: the test suite uses it; the product path never
 does. Plain numpy in float64.
 
-The pages fine-tune MoE models with LoRA adapters on the expert projections
-(unsloth PR #3812, the LoRA path of the grouped GEMM; axolotl issue #3155,
-fine-tuning Qwen3 MoE). For expert e and projection P in {gate, up, down}
+The pages fine-tune MoE models with LoRA adapters on the fused (stacked)
+expert projections (sourcepulse summary, "Highlighted Details": LoRA and
+QLoRA on the fused experts, fused and unfused adapter formats; torchtune PR
+#2820 lists LoRA support for the Qwen3 MoE port as still to do). The
+adapter itself is the usual low-rank update of a frozen weight; the pages
+print no formula for it. For expert e and projection P in {gate, up, down}
 with frozen W_P[e] [N, K], adapters A_P[e] [r, K] and B_P[e] [N, r], and
 scale s:
     W'_P[e] = W_P[e] + s * B_P[e] @ A_P[e]
