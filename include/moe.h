@@ -356,7 +356,7 @@ moe_status moe_forward_fused_fp8(moe_shape s, const void* x, const void* w_route
  * w_out [E,N,K], all bf16: the product summed in fp32 from exact bf16
  * products, scaled and added in fp32, rounded once. w_out may be w (in
  * place); otherwise the two must not overlap. K % 8 == 0, E <= 65535 and
- * (N + 128) K < 2^30 (MOE_EUNSUPPORTED otherwise). */
+ * (N + 256) K < 2^30 (MOE_EUNSUPPORTED otherwise). */
 moe_status moe_lora_merge(int32_t E, int32_t N, int32_t K, int32_t r, float scale, const void* w, const void* a,
                           const void* b, void* w_out, hipStream_t stream);
 

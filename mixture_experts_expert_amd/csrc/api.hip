@@ -495,7 +495,9 @@ moe_status moe_lora_merge(int32_t E, int32_t N, int32_t K, int32_t r, float scal
   if (any_null(w, a, b, w_out)) return MOE_EINVAL;
   if (r > 128 || r % 8 != 0 || K % 8 != 0 || E > 65535 || (N + 127) / 128 > 65535) return MOE_EUNSUPPORTED;
   // One expert's weights are addressed with 32-bit byte offsets.
-  if (static_cast<int64_t>(N + 128) * K >= (static_cast<int64_t>(1) << 30)) return MOE_EUNSUPPORTED;
+  // (Row tiles of a block reach up to 255 rows past the last; their loads
+  // are range-checked and their results never stored.)
+  if ((static_cast<int64_t>(N) + 256) * K >= (static_cast<int64_t>(1) << 30)) return MOE_EUNSUPPORTED;
   return from_hip(moe::launch_lora_merge(E, N, K, r, scale, w, a, b, w_out, stream));
 }
 
