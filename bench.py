@@ -3,34 +3,37 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--timed-only]
 
 One step is the whole stage on one batch of synthetic input already resident
-in HBM, on one stream: route -> expert indexing + gather -> gate/up GEMM
+in HBM, on one stream, as the library chains it (MoEStage; moe_grouped_gemm_fwd
+and moe_grouped_gemm_bwd): route -> expert indexing + gather -> gate/up GEMM
 (SwiGLU epilogue) -> down GEMM -> combine, then combine backward -> down
-dgrad (SwiGLU backward epilogue) -> down wgrad -> gate/up dgrad -> gate/up
-wgrad -> unpermute-sum -> router backward, every step a call of the C ABI
-(the six GEMMs through their single-GEMM entry points: moe_grouped_gemm_fwd
-chains the first two, moe_grouped_gemm_bwd runs the other four as two
-paired launches, timed separately below).
+backward (data gradient with the SwiGLU backward epilogue, then the weight
+gradient, in one persistent launch) -> gate/up backward (likewise) ->
+unpermute-sum -> router backward, every step a call of the C ABI.
 
 Prints one JSON line. `value` is tokens/s of the whole stage; TFLOP/s counts
-the expert GEMMs (18*T*k*H*I per step). Around every call the timed steps
-also record HIP events on the stream, which give `call_ms`, `gemm_tflops`,
-`hbm_frac` and `roofline`. `roofline` covers the dominant kernel (the call
-with the largest average time): its algorithmic flops or bytes per launch
-(whichever of the MFMA and HBM minimum times is larger decides the bound)
-over its average launch time. `traffic` is the HBM bytes per launch that
+the expert GEMMs (18*T*k*H*I per step). Around every GEMM call the timed
+steps also record HIP events on the stream, which give `call_ms`,
+`gemm_tflops` and `roofline`; the calls without matrix work are timed each
+on its own afterwards (`other_call_ms`, `hbm_frac`). `roofline` covers the
+dominant kernel (the GEMM call with the largest average time): its
+algorithmic flops or bytes per launch (whichever of the MFMA and HBM minimum
+times is larger decides the bound) over its average launch time. `traffic` is the HBM bytes per launch that
 rocprofv3's FETCH_SIZE and WRITE_SIZE counters gave for that kernel, scaled by
 what they read for a plain device copy of known size (--calibrate-copy); it is
 taken from the committed summary under profiles/ and reported only while the
 GEMM source still hashes to the value recorded there. `cpu_baseline` times
 the CPU oracle on a bounded token sample of the same workload.
 
-After the timed steps (and outside them): `graph_ms_per_step` times the same
+After the timed steps (and outside them): `ms_per_step_without_call_events`
+times the same step without the per-call events; `graph_ms_per_step` the same
 step captured once into a HIP graph and replayed; `two_stream_ms_per_step`
-the step with the backward's weight-gradient GEMMs on a second stream,
-concurrently with the data-gradient GEMMs; `gather_fused_ms` the step
-without x_perm (gate/up and its weight gradient read x through the sorted
-rows' tokens) and its three changed calls; and `inference_forward_ms` the
-forward alone, unfused and fused (no x_perm, routing weights in the down
+the step with one launch per GEMM and the weight-gradient GEMMs on a second
+stream, concurrently with the data-gradient GEMMs; `gather_fused_ms` the step
+without x_perm (gate/up and the gate/up backward read x through the sorted
+rows' tokens) and its three changed calls; `single_launch_ms` the step with
+one launch per GEMM (the six single-GEMM entry points) and the four backward
+GEMMs on their own (whose TFLOP/s join `gemm_tflops`); `inference_forward_ms`
+the forward alone, unfused and fused (no x_perm, routing weights in the down
 GEMM's epilogue); `lora_ms` the training step with rank-64 adapters on frozen
 experts (merges, forward on the merged weights, data and adapter gradients)
 and its two adapter calls. `--timed-only` skips these and the CPU baseline, so that
@@ -80,6 +83,11 @@ def alg_bytes(c) -> dict:
         "moe_gemm_gate_up_wgrad": 2 * M * I * b16 + M * H * b16 + 2 * E * I * H * f32,
         "moe_unpermute_sum": M * H * b16 + M * i32 + T * H * b16,
         "moe_route_bwd": 3 * M * i32 + T * E * f32,
+        # The paired backward launches: both GEMMs' tensors, the shared input once.
+        "moe_gemm_down_bwd": (M * H * b16 + E * H * I * b16 + 2 * M * I * b16 + 2 * M * I * b16
+                              + M * I * b16 + E * H * I * f32),
+        "moe_gemm_gate_up_bwd": (2 * M * I * b16 + 2 * E * I * H * b16 + M * H * b16
+                                 + M * H * b16 + 2 * E * I * H * f32),
     }
 
 
@@ -133,6 +141,8 @@ def gemm_flops(c) -> dict:
         "moe_gemm_down_wgrad": 2.0 * m * h * i,
         "moe_gemm_gate_up_dgrad": 4.0 * m * h * i,
         "moe_gemm_gate_up_wgrad": 4.0 * m * h * i,
+        "moe_gemm_down_bwd": 4.0 * m * h * i,
+        "moe_gemm_gate_up_bwd": 8.0 * m * h * i,
     }
 
 
@@ -252,9 +262,14 @@ def main() -> int:
     dgu = torch.empty(cfg.M, 2 * cfg.I, dtype=torch.bfloat16, device="cuda")  # [dG | dU]
     x, wr, wg, wu, wd, dy = (dev[n] for n in ["x", "w_router", "w_gate", "w_up", "w_down", "dy"])
     stream = torch.cuda.current_stream()
+    # The 12 C-ABI calls with one launch per GEMM; the timed step runs the
+    # library's own chain (what MoEStage and moe_grouped_gemm_bwd do): the
+    # backward's GEMMs as the two paired launches.
+    single_names = ["moe_route", "moe_permute", "moe_gemm_gate_up", "moe_gemm_down", "moe_combine",
+                    "moe_combine_bwd", "moe_gemm_down_dgrad", "moe_gemm_down_wgrad", "moe_gemm_gate_up_dgrad",
+                    "moe_gemm_gate_up_wgrad", "moe_unpermute_sum", "moe_route_bwd"]
     names = ["moe_route", "moe_permute", "moe_gemm_gate_up", "moe_gemm_down", "moe_combine", "moe_combine_bwd",
-             "moe_gemm_down_dgrad", "moe_gemm_down_wgrad", "moe_gemm_gate_up_dgrad", "moe_gemm_gate_up_wgrad",
-             "moe_unpermute_sum", "moe_route_bwd"]
+             "moe_gemm_down_bwd", "moe_gemm_gate_up_bwd", "moe_unpermute_sum", "moe_route_bwd"]
     calls = [
         lambda: B.moe_route(s, x, wr, bias, b["logits"], b["topk_idx"], b["topk_w"]),
         lambda: B.moe_permute(s, b["topk_idx"], x, b["counts"], b["offsets"], b["sorted_to_flat"],
@@ -271,17 +286,35 @@ def main() -> int:
         lambda: B.moe_unpermute_sum(s, b["dx_perm"], b["flat_to_sorted"], b["dx"]),
         lambda: B.moe_route_bwd(s, b["d_topk_w"], b["topk_w"], b["topk_idx"], b["d_logits"]),
     ]
-    by_name = dict(zip(names, calls))
-    ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+    by_name = dict(zip(single_names, calls))
+    by_name["moe_gemm_down_bwd"] = lambda: B.moe_gemm_down_bwd(s, b["do_perm"], b["a"], b["offsets"], wd, b["g"],
+                                                               b["u"], dgu, b["dw_down"], 0, st.ws)
+    by_name["moe_gemm_gate_up_bwd"] = lambda: B.moe_gemm_gate_up_bwd(s, dgu, b["x_perm"], None, b["offsets"], wg,
+                                                                     wu, b["dx_perm"], b["dw_gate"], b["dw_up"], 0,
+                                                                     st.ws)
+    # HIP events in the timed steps bracket the GEMM calls only (an event
+    # between two calls costs about 5 us; bracketing all ten calls added
+    # 0.1 ms to a 3 ms step): one event before the first GEMM of each run of
+    # consecutive GEMM calls and one after every GEMM call. The other calls
+    # are timed on their own after the timed steps.
+    gemm_names = [n for n in names if n.startswith("moe_gemm")]
+    # The event each GEMM call's time starts at: the previous call's end when
+    # that was a GEMM, else an event of its own recorded just before it.
+    start_of = {}
+    for i, n in enumerate(names):
+        if n in gemm_names:
+            start_of[n] = names[i - 1] if i > 0 and names[i - 1] in gemm_names else "start_" + n
+    ev = [{e: torch.cuda.Event(enable_timing=True) for e in gemm_names + list(start_of.values())}
           for _ in range(args.steps)]
 
     def step(events=None):
         for n in names:
-            if events is not None:
-                events[n][0].record(stream)
+            timed = events is not None and n in gemm_names
+            if timed and start_of[n].startswith("start_"):
+                events[start_of[n]].record(stream)
             by_name[n]()
-            if events is not None:
-                events[n][1].record(stream)
+            if timed:
+                events[n].record(stream)
 
     # The same step with the weight-gradient GEMMs on a second stream
     # (default priority), each overlapping a data-gradient GEMM; they run one
@@ -320,13 +353,18 @@ def main() -> int:
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps
-    per_call = {n: sum(ev[k][n][0].elapsed_time(ev[k][n][1]) for k in range(args.steps)) / args.steps
-                for n in names}
+    per_call = {n: sum(ev[k][start_of[n]].elapsed_time(ev[k][n]) for k in range(args.steps)) / args.steps
+                for n in gemm_names}
     log(f"timed {args.steps} steps: {ms:.3f} ms/step; " + ", ".join(f"{n}={v:.3f}" for n, v in per_call.items()))
 
     def time_fn(fn, reps=10):
         return time_calls(fn, stream, reps)
 
+    # The calls without matrix work, each on its own (outside the timed steps).
+    other_ms = None if args.timed_only else {n: round(time_fn(by_name[n]), 4) for n in names if n not in gemm_names}
+
+    # The same step without the per-call events (what the events themselves cost).
+    plain_ms = None if args.timed_only else round(time_fn(step), 4)
     two_stream_ms = None if args.timed_only else round(time_fn(step_two_streams), 4)
     if two_stream_ms is not None:
         log(f"two-stream backward: {two_stream_ms:.3f} ms/step")
@@ -345,7 +383,8 @@ def main() -> int:
         log(f"graph replay: {graph_ms:.3f} ms/step")
 
     # The same step without x_perm: the sort also writes each sorted row's
-    # token, and gate/up and its weight gradient read x rows through it.
+    # token, and gate/up and the gate/up backward pair (its weight gradient)
+    # read x rows through it.
     rt = dict(row_token=torch.empty(cfg.M, dtype=torch.int32, device="cuda"),
               row_weight=torch.empty(cfg.M, device="cuda"))
     gf_calls = dict(by_name)
@@ -354,8 +393,8 @@ def main() -> int:
         rt["row_token"], rt["row_weight"], st.ws)
     gf_calls["moe_gemm_gate_up"] = lambda: B.moe_gemm_gate_up_gathered(
         s, x, rt["row_token"], b["offsets"], wg, wu, b["g"], b["u"], b["a"])
-    gf_calls["moe_gemm_gate_up_wgrad"] = lambda: B.moe_gemm_gate_up_wgrad_gathered(
-        s, dgu, x, rt["row_token"], b["offsets"], b["dw_gate"], b["dw_up"], 0, st.ws)
+    gf_calls["moe_gemm_gate_up_bwd"] = lambda: B.moe_gemm_gate_up_bwd(
+        s, dgu, x, rt["row_token"], b["offsets"], wg, wu, b["dx_perm"], b["dw_gate"], b["dw_up"], 0, st.ws)
 
     def step_gather_fused():
         for n in names:
@@ -364,42 +403,18 @@ def main() -> int:
     gather_fused_ms = None
     if not args.timed_only:
         gather_fused_ms = {"step": round(time_fn(step_gather_fused), 4)}
-        for n in ["moe_permute", "moe_gemm_gate_up", "moe_gemm_gate_up_wgrad"]:
+        for n in ["moe_permute", "moe_gemm_gate_up", "moe_gemm_gate_up_bwd"]:
             gather_fused_ms[n] = round(time_fn(gf_calls[n], reps=5), 4)
         log(f"step without x_perm: {gather_fused_ms}")
 
-    # The backward's GEMMs in two launches, each a data gradient and a weight
-    # gradient side by side (moe_gemm_down_bwd, moe_gemm_gate_up_bwd).
-    pair_calls = {
-        "moe_gemm_down_bwd": lambda: B.moe_gemm_down_bwd(s, b["do_perm"], b["a"], b["offsets"], wd, b["g"], b["u"],
-                                                         dgu, b["dw_down"], 0, st.ws),
-        "moe_gemm_gate_up_bwd": lambda: B.moe_gemm_gate_up_bwd(s, dgu, b["x_perm"], None, b["offsets"], wg, wu,
-                                                               b["dx_perm"], b["dw_gate"], b["dw_up"], 0, st.ws),
-    }
-    paired = ["moe_gemm_down_dgrad", "moe_gemm_down_wgrad", "moe_gemm_gate_up_dgrad", "moe_gemm_gate_up_wgrad"]
-
-    def step_paired(calls):
-        for n in names:
-            if n == "moe_gemm_down_dgrad":
-                pair_calls["moe_gemm_down_bwd"]()
-            elif n == "moe_gemm_gate_up_dgrad":
-                calls["moe_gemm_gate_up_bwd"]()
-            elif n not in paired:
-                calls[n]()
-
-    paired_ms = None
+    # The same step with one launch per GEMM (the six single-GEMM entry
+    # points), and each backward GEMM on its own.
+    single_ms = None
     if not args.timed_only:
-        gf_pair = dict(gf_calls)
-        gf_pair["moe_gemm_gate_up_bwd"] = lambda: B.moe_gemm_gate_up_bwd(
-            s, dgu, x, rt["row_token"], b["offsets"], wg, wu, b["dx_perm"], b["dw_gate"], b["dw_up"], 0, st.ws)
-        xp_pair = dict(by_name)
-        xp_pair["moe_gemm_gate_up_bwd"] = pair_calls["moe_gemm_gate_up_bwd"]
-        paired_ms = {"step": round(time_fn(lambda: step_paired(xp_pair)), 4),
-                     "step_without_x_perm": round(time_fn(lambda: step_paired(gf_pair)), 4)}
-        for n, c in pair_calls.items():
-            paired_ms[n] = round(time_fn(c, reps=5), 4)
-        paired_ms["moe_gemm_gate_up_bwd_gathered"] = round(time_fn(gf_pair["moe_gemm_gate_up_bwd"], reps=5), 4)
-        log(f"paired backward GEMMs: {paired_ms}")
+        single_ms = {"step": round(time_fn(lambda: [by_name[n]() for n in single_names]), 4)}
+        for n in ["moe_gemm_down_dgrad", "moe_gemm_down_wgrad", "moe_gemm_gate_up_dgrad", "moe_gemm_gate_up_wgrad"]:
+            single_ms[n] = round(time_fn(by_name[n], reps=5), 4)
+        log(f"one launch per GEMM: {single_ms}")
 
     # Inference forward at the same shape (outside the timed training steps):
     # the unfused chain (route, permute with the gather, the two GEMMs, the
@@ -446,11 +461,11 @@ def main() -> int:
 
     flops = gemm_flops(cfg)
     nbytes = alg_bytes(cfg)
-    step_flops = sum(flops.values())
+    step_flops = sum(flops[n] for n in names if n in flops)
     tflops = step_flops / (ms * 1e-3) / 1e12
 
     def roofline(times):
-        dominant = max(names, key=lambda n: times[n])
+        dominant = max(times, key=times.get)
         t_mfma = flops.get(dominant, 0.0) / (PEAK_BF16_TFLOPS * 1e12)
         t_hbm = nbytes[dominant] / (PEAK_HBM_GBS * 1e9)
         secs = times[dominant] * 1e-3
@@ -468,10 +483,13 @@ def main() -> int:
         return roof
 
     roof = roofline(per_call)
-    gemm_tflops = {n: round(flops[n] / (per_call[n] * 1e-3) / 1e12, 1) for n in flops}
+    gemm_tflops = {n: round(flops[n] / (per_call[n] * 1e-3) / 1e12, 1) for n in names if n in flops}
+    if single_ms is not None:
+        for n in ["moe_gemm_down_dgrad", "moe_gemm_down_wgrad", "moe_gemm_gate_up_dgrad", "moe_gemm_gate_up_wgrad"]:
+            gemm_tflops[n] = round(flops[n] / (single_ms[n] * 1e-3) / 1e12, 1)
     # HBM fraction of the calls without matrix work (algorithmic bytes).
-    hbm_frac = {n: round(nbytes[n] / (per_call[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)
-                for n in names if n not in flops}
+    hbm_frac = None if other_ms is None else {
+        n: round(nbytes[n] / (other_ms[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 3) for n in other_ms}
     out = {
         "metric": METRIC,
         "value": round(cfg.T / (ms * 1e-3), 1),
@@ -491,12 +509,14 @@ def main() -> int:
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "gemm_tflops": gemm_tflops,
         "call_ms": {n: round(v, 4) for n, v in per_call.items()},
+        "other_call_ms": other_ms,
         "hbm_frac": hbm_frac,
         "roofline": roof,
+        "ms_per_step_without_call_events": plain_ms,
         "two_stream_ms_per_step": two_stream_ms,
         "graph_ms_per_step": graph_ms,
         "gather_fused_ms": gather_fused_ms,
-        "paired_ms": paired_ms,
+        "single_launch_ms": single_ms,
         "inference_forward_ms": infer,
         "lora_ms": lora,
     }
