@@ -7,11 +7,11 @@
 // adapter gradients
 //   dB = s dY^T (X A^T),   dA = s (dY B)^T X
 // (dY, X per projection: dG or dU with the sorted hidden states, dO with the
-// expert activations) are low-rank grouped GEMMs, run on the grouped-GEMM
-// kernels with their shapes read differently: the row projections X (sA)^T
-// and dY (sB) as "down" GEMMs (reduction over the row length, output width
-// the padded rank), and the outer products as "down weight gradients" over
-// each expert's rows. The frozen weights get no gradient.
+// expert activations) are low-rank grouped GEMMs: the four rank-wide row
+// projections X (sA)^T and dY (sB) in one launch of proj_kernel below, and
+// the outer products over each expert's rows on the grouped weight-gradient
+// kernels, with their shapes read differently. The frozen weights get no
+// gradient.
 #include "moe_internal.h"
 
 namespace moe {
