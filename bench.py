@@ -201,6 +201,14 @@ def lora_timing(cfg, seed: int, tensors, bias, stream, r: int = 64, scale: float
         ls.backward(dy)
 
     out = {"rank": r, "scale": scale, "step": round(time_calls(lora_step, stream), 4)}
+    aux = torch.cuda.Stream()
+
+    def lora_step_two_streams():
+        ls.forward(x, wr, wg, wu, wd, ad, bias, aux_stream=aux)
+        ls.backward(dy)
+
+    # The merges on a second stream, concurrent with the routing and the sort.
+    out["step_merges_on_second_stream"] = round(time_calls(lora_step_two_streams, stream), 4)
     out["moe_lora_merge_x3"] = round(time_calls(lambda: ls.merge(wg, wu, wd, ad), stream, reps=5), 4)
     out["moe_lora_grads"] = round(time_calls(lambda: B.moe_lora_grads(
         ls.s, r, scale, lb["x_perm"], lb["a"], lb["dgu"], lb["do_perm"], lb["offsets"],

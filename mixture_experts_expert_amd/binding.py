@@ -490,10 +490,40 @@ class LoRAStage(MoEStage):
         moe_lora_merge(E, H, I, r, self.scale, w_down, adapters["a_down"], adapters["b_down"], wd, stream)
         return self.merged
 
-    def forward(self, x, w_router, w_gate, w_up, w_down, adapters, logit_bias=None, stream=None):
+    def forward(self, x, w_router, w_gate, w_up, w_down, adapters, logit_bias=None, stream=None, aux_stream=None):
+        """With ``aux_stream`` (a second stream, default priority) the three
+        merges run there, concurrently with the routing and the sort on
+        ``stream``; gate/up waits for its two merges and down for its own.
+        The results are the same bits either way."""
         self.adapters = adapters
-        wg, wu, wd = self.merge(w_gate, w_up, w_down, adapters, stream)
-        return super().forward(x, w_router, wg, wu, wd, logit_bias, stream)
+        if aux_stream is None:
+            wg, wu, wd = self.merge(w_gate, w_up, w_down, adapters, stream)
+            return super().forward(x, w_router, wg, wu, wd, logit_bias, stream)
+        E, H, I, r = self.E, self.H, self.I, self.rank
+        wg, wu, wd = self.merged
+        main = torch.cuda.current_stream() if stream is None else stream
+        forked = torch.cuda.Event()
+        forked.record(main)
+        aux_stream.wait_event(forked)
+        moe_lora_merge(E, I, H, r, self.scale, w_gate, adapters["a_gate"], adapters["b_gate"], wg, aux_stream)
+        moe_lora_merge(E, I, H, r, self.scale, w_up, adapters["a_up"], adapters["b_up"], wu, aux_stream)
+        gu_ready = torch.cuda.Event()
+        gu_ready.record(aux_stream)
+        moe_lora_merge(E, H, I, r, self.scale, w_down, adapters["a_down"], adapters["b_down"], wd, aux_stream)
+        d_ready = torch.cuda.Event()
+        d_ready.record(aux_stream)
+        b, s = self.buf, self.s
+        self.w = (wg, wu, wd)
+        self.x = x
+        moe_route(s, x, w_router, logit_bias, b["logits"], b["topk_idx"], b["topk_w"], main)
+        moe_permute(s, b["topk_idx"], x, b["counts"], b["offsets"], b["sorted_to_flat"], b["flat_to_sorted"],
+                    b["x_perm"], self.ws, stream=main)
+        main.wait_event(gu_ready)
+        moe_gemm_gate_up(s, b["x_perm"], b["offsets"], wg, wu, b["g"], b["u"], b["a"], main)
+        main.wait_event(d_ready)
+        moe_gemm_down(s, b["a"], b["offsets"], wd, b["o_perm"], main)
+        moe_combine(s, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["y"], main)
+        return b["y"]
 
     def backward(self, dy, stream=None):
         self._alloc_bwd()

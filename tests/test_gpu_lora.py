@@ -142,3 +142,37 @@ def test_lora_stage_qwen3_30b_a3b_full():
     ref = oracle_lora(inp, adapters, s, idx, ref_r["topk_w"])
     for n in NAMES:
         U.check_close("d" + n, U.to_np(st.buf["d" + n][experts]), ref["d" + n][experts], U.BF16_TOL)
+
+
+def test_lora_merges_on_a_second_stream_same_bits():
+    """LoRAStage.forward(aux_stream=...) runs the merges concurrently with the
+    routing and the sort: every output equals the one-stream step bit for bit,
+    over two steps (the second merge overwrites weights the first backward read)."""
+    from mixture_experts_expert_amd import binding as B
+    cfg, r, s = SPLIT_K, 64, 2.0
+    U.say(f"[lora two streams] {cfg} r={r}")
+    inp = synth.make_inputs(cfg, seed=9, with_dy=True)
+    adapters = synth.make_adapters(cfg, r, seed=9)
+    d = U.DevInputs(inp)
+    ad = {n: U.to_dev(adapters[n]) for n in NAMES}
+    T = d.t["x"].shape[0]
+    outs = ["y", "dx", "d_logits", "topk_idx", "offsets"] + ["d" + n for n in NAMES]
+
+    def run(aux):
+        st = B.LoRAStage(T, cfg.H, cfg.E, cfg.k, cfg.I, r, s)
+        for _ in range(2):
+            st.forward(d.t["x"], d.t["w_router"], d.t["w_gate"], d.t["w_up"], d.t["w_down"], ad, d.bias,
+                       aux_stream=aux)
+            st.backward(d.t["dy"])
+        torch.cuda.synchronize()
+        return {n: st.buf[n].clone() for n in outs}, [w.clone() for w in st.merged]
+
+    ref, ref_w = run(None)
+    got, got_w = run(torch.cuda.Stream())
+    for n in outs:
+        a, b_ = ref[n], got[n]
+        if a.dtype == torch.bfloat16:
+            a, b_ = a.view(torch.int16), b_.view(torch.int16)
+        assert torch.equal(a, b_), n
+    for a, b_ in zip(ref_w, got_w):
+        assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
