@@ -145,16 +145,24 @@ __global__ __launch_bounds__(kThreads) void rank_scatter_kernel(int n, int E, in
   }
 }
 
-// x_perm[p, :] = x[s2f[p] / k, :] with 16-byte copies; one wavefront per row.
-__global__ __launch_bounds__(kThreads) void gather_kernel(int64_t rows, int k, int chunks_per_row,
-                                                          const int32_t* __restrict__ s2f,
+// x_perm[f2s[t k + j], :] = x[t, :] for j < k: one wavefront per token t.
+// Each 16-byte chunk of the token's row is read once and written to the
+// token's k sorted rows (a wavefront per sorted row would read every x row k
+// times, in an order that misses the L2). The token index and its k
+// destinations are wavefront-uniform.
+__global__ __launch_bounds__(kThreads) void gather_kernel(int tokens, int k, int chunks_per_row,
+                                                          const int32_t* __restrict__ f2s,
                                                           const uint4* __restrict__ x, uint4* __restrict__ x_perm) {
   const int lane = threadIdx.x % kWave;
-  const int64_t p = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
-  if (p >= rows) return;
-  const int64_t src = static_cast<int64_t>(s2f[p] / k) * chunks_per_row;
-  const int64_t dst = p * chunks_per_row;
-  for (int c = lane; c < chunks_per_row; c += kWave) x_perm[dst + c] = x[src + c];
+  const int t = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWavesPerBlock +
+                                               static_cast<int>(threadIdx.x) / kWave);
+  if (t >= tokens) return;
+  const int64_t src = static_cast<int64_t>(t) * chunks_per_row;
+  const int32_t* dst_rows = f2s + static_cast<int64_t>(t) * k;
+  for (int c = lane; c < chunks_per_row; c += kWave) {
+    const uint4 v = x[src + c];
+    for (int j = 0; j < k; ++j) x_perm[static_cast<int64_t>(dst_rows[j]) * chunks_per_row + c] = v;
+  }
 }
 
 }  // namespace
@@ -202,12 +210,11 @@ hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const void* x,
                           hipStream_t st) {
   hipError_t err = launch_sort(s, idx, counts, offsets, s2f, f2s, nullptr, nullptr, nullptr, ws, st);
   if (err != hipSuccess) return err;
-  const int n = s.T * s.k;
   const int esz = s.dtype == MOE_BF16 ? 2 : 4;
   const int chunks = s.H * esz / 16;
-  gather_kernel<<<ceil_div(n, kWavesPerBlock), kThreads, 0, st>>>(n, s.k, chunks, s2f,
-                                                                  static_cast<const uint4*>(x),
-                                                                  static_cast<uint4*>(x_perm));
+  gather_kernel<<<ceil_div(s.T, kWavesPerBlock), kThreads, 0, st>>>(s.T, s.k, chunks, f2s,
+                                                                    static_cast<const uint4*>(x),
+                                                                    static_cast<uint4*>(x_perm));
   return hipGetLastError();
 }
 
