@@ -220,7 +220,17 @@ __global__ __launch_bounds__(kThreads) void blockdiag_t_kernel(int C, int r, int
   const int e = blockIdx.y, c0 = blockIdx.x * 64, bc = c0 / C, cc0 = c0 - bc * C;
   const int tid = threadIdx.x;
   const bf16_t* src = (bc ? in1 : in0) + (static_cast<int64_t>(e) * C + cc0) * r;
-  for (int q = tid; q < 64 * r; q += kThreads) tile[q / r][q % r] = s * bf16f(src[q]);
+  const int c8 = r / 8;  // 16-byte pieces per row of in_bc (r % 8 == 0)
+  for (int q = tid; q < 64 * c8; q += kThreads) {
+    const int row = q / c8, j0 = (q - row * c8) * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + row * r + j0);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      tile[row][j0 + 2 * t] = s * __uint_as_float(u[t] << 16);
+      tile[row][j0 + 2 * t + 1] = s * __uint_as_float(u[t] & 0xffff0000u);
+    }
+  }
   __syncthreads();
   // Thread: output columns 8 (tid%8) .. + 7 of rows J = tid/8, tid/8 + 32, ...
   const int cq = (tid & 7) * 8;
