@@ -360,9 +360,9 @@ moe_status moe_forward_fused_fp8(moe_shape s, const void* x, const void* w_route
 moe_status moe_lora_merge(int32_t E, int32_t N, int32_t K, int32_t r, float scale, const void* w, const void* a,
                           const void* b, void* w_out, hipStream_t stream);
 
-/* Bytes of device workspace for moe_lora_grads at this shape and rank on
- * the current device (0 if either is rejected): the scaled adapters, the
- * rank-wide row projections and the split-K partial tiles. */
+/* Bytes of device workspace for moe_lora_grads at this shape and rank (0 if
+ * either is rejected): the scaled adapters and the rank-wide row
+ * projections. */
 size_t moe_lora_workspace_bytes(moe_shape s, int32_t r);
 
 /* Adapter gradients of the stage on the merged weights (chain rule through

@@ -469,17 +469,12 @@ moe_status moe_route_bwd(moe_shape s, const float* d_topk_w, const float* topk_w
 
 namespace {
 // Adapter rank: a multiple of 8 (16-byte rows of B) up to 128 (the merge's
-// LDS tile); the outer products of the adapter gradients run on the grouped
-// weight-gradient kernels, whose shapes must pass the shape checks.
+// LDS tile and the gradient kernels' register tiles).
 moe_status check_lora(const moe_shape& s, int32_t r) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if (r <= 0) return MOE_EINVAL;
   if (s.dtype != MOE_BF16 || r > 128 || r % 8 != 0) return MOE_EUNSUPPORTED;
-  const int rp = moe::lora_padded_rank(r);
-  const int hi[3][2] = {{2 * s.I, 2 * rp}, {s.H, rp}, {rp, s.I}};  // the outer products' (H, I)
-  for (const auto& d : hi)
-    if ((st = check_shape(moe::lora_gemm_shape(s, d[0], d[1]))) != MOE_OK) return st;
   return MOE_OK;
 }
 }  // namespace

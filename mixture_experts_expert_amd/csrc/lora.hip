@@ -8,9 +8,9 @@
 //   dB = s dY^T (X A^T),   dA = s (dY B)^T X
 // (dY, X per projection: dG or dU with the sorted hidden states, dO with the
 // expert activations) are low-rank grouped GEMMs: the four rank-wide row
-// projections X (sA)^T and dY (sB) in one launch of proj_kernel below, and
-// the outer products over each expert's rows on the grouped weight-gradient
-// kernels, with their shapes read differently. The frozen weights get no
+// projections X (sA)^T and dY (sB) in one launch of proj_kernel, and the
+// outer products over each expert's rows in two launches of outer_kernel,
+// which write the adapter gradients in place. The frozen weights get no
 // gradient.
 #include "moe_internal.h"
 
@@ -248,22 +248,6 @@ __global__ __launch_bounds__(kThreads) void blockdiag_t_kernel(int C, int r, int
   }
 }
 
-// dst[e][i][j] = src[e][row0 + i][col0 + j] for i < rows, j < cols (cols,
-// col0 and src_cols multiples of 4); src has src_rows rows of src_cols
-// floats per expert. One thread per 16 bytes.
-__global__ __launch_bounds__(kThreads) void extract_kernel(int64_t total4, int rows, int cols, const float* __restrict__ src,
-                                                           int src_rows, int src_cols, int row0, int col0,
-                                                           float* __restrict__ dst) {
-  const int64_t q = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (q >= total4) return;
-  const int c4 = cols / 4;
-  const int64_t row = q / c4;  // e * rows + i
-  const int j = static_cast<int>(q - row * c4) * 4;
-  const int64_t e = row / rows, i = row - e * rows;
-  *reinterpret_cast<float4*>(dst + q * 4) =
-      *reinterpret_cast<const float4*>(src + (e * src_rows + row0 + i) * src_cols + col0 + j);
-}
-
 // Rank-wide projections: out[p][n] = sum_k rows[p][k] W[e][n][k] over each
 // expert e's sorted rows p, W [E][N][K], N a multiple of 64 up to 32 NB,
 // K % 64 == 0; bf16 in and out, fp32 sums. One launch runs up to four such
@@ -467,30 +451,203 @@ hipError_t projections(const moe_shape& s, int nmax, const int32_t* offsets, con
   return hipGetLastError();
 }
 
-// dW [E, Mo, No] = L_e^T R_e over each expert's rows, L [M, Mo], R [M, No]:
-// the "down weight gradient" GEMM with H = Mo, I = No.
-hipError_t outer_product(const moe_shape& s, int Mo, int No, const int32_t* offsets, const void* L, const void* R,
-                         float* dw, float* part, hipStream_t st) {
-  GemmArgs g{};
-  g.offsets = offsets;
-  g.a = L;
-  g.b0 = R;
-  g.dw0 = dw;
-  g.part = part;
-  g.accumulate = 0;
-  return launch_gemm(GEMM_WGRAD_DOWN, lora_gemm_shape(s, Mo, No), g, st);
+// Adapter-gradient outer products: for each expert e, over its sorted rows p,
+//   D[i][j] = sum_p L[p][l0 + i] S[p][s0 + j],  i < nl (the long side: I or
+//   H columns), j < ns (the rank side, ns <= 32 NB),
+// written as out[e][i][j] (dB: [nl][ns]) or, with TRANS, as out[e][j][i]
+// (dA: [ns][nl]); with out1, rows j >= ns1 of a TRANS job go to out1 instead
+// (row j - ns1), so that [dA_gate; dA_up] come out of one pass over x_perm.
+// Only the blocks the adapters need are computed (no padded or off-diagonal
+// outputs) and the results land in place, fp32 from fp32 sums.
+//
+// Tile: 128 long-side columns of one expert x the whole rank side, 4
+// wavefronts of 32 long-side columns. The reduction runs over the expert's
+// rows in chunks of 64: each thread loads 16-byte pieces (8 consecutive
+// columns of one row) and writes them to LDS as they are ([row][column]);
+// the matrix-core fragments (8 consecutive rows of one column) come out of
+// transposed LDS reads (frag_tr); two chunks are in flight. MFMA rows are chosen so that a
+// lane ends with four consecutive output elements of one output row (the
+// rank side for dB, the long side for dA): 16-byte stores. The tile list is
+// static (every expert, rows or not, gets its tiles: an expert without rows
+// writes zeros).
+constexpr int kOC = 64;         // rows per reduction chunk
+// LDS rows of a chunk ([row][column], as loaded): 128 long-side columns, or
+// 32 NB rank-side columns, padded so that a row's stride is 16 or 48 dwords
+// mod 64: the four rows of a transposed read group then fall on disjoint banks.
+constexpr int kOLw = 128 + 32;  // bf16 per long-side row (80 dwords)
+__host__ __device__ constexpr int orow_s(int nb) { return 32 * nb + (nb % 2 == 1 ? 0 : 32); }
+typedef short v4i16o __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16o lds_v4i16o;
+
+// MFMA fragment (8 consecutive rows k of one column) of a [row][column] LDS
+// tile through two ds_read_b64_tr_b16: lane l addresses row 8 (l/32) +
+// (l%16)/4 and columns 4 (l%4) .. + 3 of the 16-column half (l/16)%2 of the
+// 32-column block at col0; within each 16 lanes the read hands lane i
+// element i%4 of the pieces that lanes 4j + i/4 address, so lane l ends with
+// rows 8 (l/32) .. + 3 of column col0 + l%32, and the second read (4 rows
+// on) with the next four.
+__device__ __forceinline__ bf16x8 frag_tr(const bf16_t* tile, int row_elems, int row0, int col0, int lane) {
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int k = row0 + 8 * (g16 >> 1) + (i16 >> 2);
+  const int col = col0 + 16 * (g16 & 1) + 4 * (i16 & 3);
+  const bf16_t* p = tile + k * row_elems + col;
+  const v4i16o lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16o*)(p));
+  const v4i16o hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16o*)(p + 4 * row_elems));
+  const v4i16o both[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+struct OuterJob {
+  const bf16_t* L;  // [T*k][ldl], columns l0 .. l0 + nl
+  const bf16_t* S;  // [T*k][lds], columns s0 .. s0 + ns
+  float* out;       // per expert nl * ns floats (out1: the rows j >= ns1 of a TRANS job)
+  float* out1;
+  int ldl, l0, nl, lds, s0, ns, ns1, rows1;  // rows1: rows of out / out1 per expert (TRANS)
+};
+struct OuterJobs {
+  OuterJob job[3];
+  int n;
+};
+
+template <int NB, bool TRANS>
+__global__ __launch_bounds__(kThreads) void outer_kernel(int E, const int32_t* __restrict__ offsets, OuterJobs jobs) {
+  constexpr int kOS = orow_s(NB);
+  __shared__ __attribute__((aligned(16))) bf16_t lt[2][kOC * kOLw];
+  __shared__ __attribute__((aligned(16))) bf16_t st[2][kOC * kOS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  // Static tile list: job-major, then expert, then 128-column block.
+  int t = blockIdx.x, jb = 0;
+  for (; jb < jobs.n; ++jb) {
+    const int nt = E * ((jobs.job[jb].nl + 127) / 128);
+    if (t < nt) break;
+    t -= nt;
+  }
+  if (jb >= jobs.n) return;  // uniform over the block
+  const OuterJob& J = jobs.job[jb];
+  const int tpe = (J.nl + 127) / 128;
+  const int e = t / tpe, i0 = (t - e * tpe) * 128;
+  const int r0 = offsets[e], rows = offsets[e + 1] - r0;
+
+  // Pieces of a chunk: L: row q / 16, columns i0 + 8 (q % 16) .. + 7; S: row
+  // q / (4 NB), columns 8 (q % (4 NB)) .. + 7. Columns past the window read
+  // zeros (out of range); rows past the expert's fall outside the buffer range.
+  constexpr int PL = kOC * 16 / kThreads, PS = kOC * 4 * NB / kThreads;
+  uint32_t ol[PL], os[PS];
+#pragma unroll
+  for (int u = 0; u < PL; ++u) {
+    const int q = tid + kThreads * u, c = i0 + 8 * (q & 15);
+    ol[u] = c < J.nl ? 2u * static_cast<uint32_t>((q >> 4) * J.ldl + J.l0 + c) : kOutOfRange;
+  }
+#pragma unroll
+  for (int u = 0; u < PS; ++u) {
+    const int q = tid + kThreads * u, c = 8 * (q % (4 * NB));
+    os[u] = c < J.ns ? 2u * static_cast<uint32_t>((q / (4 * NB)) * J.lds + J.s0 + c) : kOutOfRange;
+  }
+  const bf16_t* lbase = J.L + static_cast<int64_t>(r0) * J.ldl;
+  const bf16_t* sbase = J.S + static_cast<int64_t>(r0) * J.lds;
+  uint4 pl[2][PL], ps[2][PS];
+  auto load_chunk = [&](int c, uint4 (&ql)[PL], uint4 (&qs)[PS]) __attribute__((always_inline)) {
+    const int p0 = c * kOC;
+    const bool live = p0 < rows;
+    const int left = live ? min(rows - p0, kOC) : 0;  // the rows this chunk can address
+    const rsrc_t rl = make_rsrc(lbase + (live ? static_cast<int64_t>(p0) * J.ldl : 0), 2 * left * J.ldl);
+    const rsrc_t rs = make_rsrc(sbase + (live ? static_cast<int64_t>(p0) * J.lds : 0), 2 * left * J.lds);
+#pragma unroll
+    for (int u = 0; u < PL; ++u) ql[u] = load16(rl, ol[u]);
+#pragma unroll
+    for (int u = 0; u < PS; ++u) qs[u] = load16(rs, os[u]);
+  };
+  auto store_chunk = [&](int buf, const uint4 (&ql)[PL], const uint4 (&qs)[PS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < PL; ++u) {
+      const int q = tid + kThreads * u;
+      *reinterpret_cast<uint4*>(&lt[buf][(q >> 4) * kOLw + 8 * (q & 15)]) = ql[u];
+    }
+#pragma unroll
+    for (int u = 0; u < PS; ++u) {
+      const int q = tid + kThreads * u;
+      *reinterpret_cast<uint4*>(&st[buf][(q / (4 * NB)) * kOS + 8 * (q % (4 * NB))]) = qs[u];
+    }
+  };
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
+  // Same pipeline as proj_kernel: LDS holds chunk c, one register set chunk
+  // c + 1, the other takes chunk c + 2; the chunk count is rounded up to even
+  // (a chunk past the rows is all zeros).
+  const int nch = ((rows + kOC - 1) / kOC + 1) & ~1;
+  load_chunk(0, pl[0], ps[0]);
+  load_chunk(1, pl[1], ps[1]);
+  store_chunk(0, pl[0], ps[0]);
+  lds_barrier();
+  auto step = [&](int c, uint4 (&nl_)[PL], uint4 (&ns_)[PS], uint4 (&cl)[PL], uint4 (&cs)[PS])
+      __attribute__((always_inline)) {
+    const int buf = c & 1;
+    load_chunk(c + 2, nl_, ns_);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int sl = 0; sl < kOC / 16; ++sl) {
+      const bf16x8 fl = frag_tr(lt[buf], kOLw, 16 * sl, wave * 32, lane);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const bf16x8 fs = frag_tr(st[buf], kOS, 16 * sl, nb * 32, lane);
+        if constexpr (TRANS) acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl, fs, acc[nb], 0, 0, 0);
+        else acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fs, fl, acc[nb], 0, 0, 0);
+      }
+    }
+    store_chunk(buf ^ 1, cl, cs);
+    lds_barrier();
+  };
+  for (int c = 0; c < nch; c += 2) {
+    step(c, pl[0], ps[0], pl[1], ps[1]);
+    step(c + 1, pl[1], ps[1], pl[0], ps[0]);
+  }
+
+  // Lane l holds D[8q + 4(l/32) + u][l%32], u < 4, of each 32 x 32 block nb.
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = make_float4(acc[nb][4 * q], acc[nb][4 * q + 1], acc[nb][4 * q + 2], acc[nb][4 * q + 3]);
+      const int a = 8 * q + 4 * h;  // first of four consecutive MFMA rows
+      if constexpr (TRANS) {
+        // MFMA rows: long side i; columns: rank side j.
+        const int i = i0 + wave * 32 + a, j = nb * 32 + l32;
+        if (i >= J.nl || j >= J.ns) continue;
+        const bool second = j >= J.ns1;
+        const int jr = second ? j - J.ns1 : j;  // row of out or out1
+        if (jr >= J.rows1) continue;
+        float* dst = (second ? J.out1 : J.out) + (static_cast<int64_t>(e) * J.rows1 + jr) * J.nl;
+        *reinterpret_cast<float4*>(dst + i) = v;
+      } else {
+        // MFMA rows: rank side j; columns: long side i.
+        const int j = nb * 32 + a, i = i0 + wave * 32 + l32;
+        if (i >= J.nl || j >= J.ns) continue;
+        *reinterpret_cast<float4*>(J.out + (static_cast<int64_t>(e) * J.nl + i) * J.ns + j) = v;
+      }
+    }
+}
+
+template <bool TRANS>
+hipError_t outer_products(int E, int nb, const int32_t* offsets, const OuterJobs& jobs, hipStream_t st) {
+  int tiles = 0;
+  for (int j = 0; j < jobs.n; ++j) tiles += E * ((jobs.job[j].nl + 127) / 128);
+  if (tiles == 0) return hipSuccess;
+  switch (nb) {
+    case 1: outer_kernel<1, TRANS><<<tiles, kThreads, 0, st>>>(E, offsets, jobs); break;
+    case 2: outer_kernel<2, TRANS><<<tiles, kThreads, 0, st>>>(E, offsets, jobs); break;
+    case 3: outer_kernel<3, TRANS><<<tiles, kThreads, 0, st>>>(E, offsets, jobs); break;
+    case 4: outer_kernel<4, TRANS><<<tiles, kThreads, 0, st>>>(E, offsets, jobs); break;
+    case 8: outer_kernel<8, TRANS><<<tiles, kThreads, 0, st>>>(E, offsets, jobs); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 int lora_padded_rank(int r) { return (r + 63) & ~63; }
-
-moe_shape lora_gemm_shape(const moe_shape& s, int H, int I) {
-  moe_shape g = s;
-  g.H = H;
-  g.I = I;
-  return g;
-}
 
 LoraLayout lora_layout(const moe_shape& s, int r) {
   LoraLayout l{};
@@ -510,12 +667,6 @@ LoraLayout lora_layout(const moe_shape& s, int r) {
   l.z_d = take(M * rp * 2);
   l.y_gu = take(M * 2 * rp * 2);
   l.y_d = take(M * rp * 2);
-  l.da_g = take(E * rp * H * 4);
-  l.da_u = take(E * rp * H * 4);
-  l.db_gu = take(E * 2 * I * 2 * rp * 4);
-  l.da_d = take(E * rp * I * 4);
-  l.db_d = take(E * H * rp * 4);
-  l.part = take(static_cast<int64_t>(2 * gemm_grid()) * 256 * 256 * 4);
   l.total = off;
   return l;
 }
@@ -553,15 +704,7 @@ hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraA
   void* z_d = base + l.z_d;
   void* y_gu = base + l.y_gu;
   void* y_d = base + l.y_d;
-  float* db_gu = reinterpret_cast<float*>(base + l.db_gu);
-  float* part = reinterpret_cast<float*>(base + l.part);
   const int E = s.E, H = s.H, I = s.I, rp = lora_padded_rank(r);
-  // With rp == r the dA and dB_down gradients land in place.
-  const bool padded = rp != r;
-  float* da_g = padded ? reinterpret_cast<float*>(base + l.da_g) : g.da_gate;
-  float* da_u = padded ? reinterpret_cast<float*>(base + l.da_u) : g.da_up;
-  float* da_d = padded ? reinterpret_cast<float*>(base + l.da_d) : g.da_down;
-  float* db_d = padded ? reinterpret_cast<float*>(base + l.db_d) : g.db_down;
   const bf16_t* a_gate = static_cast<const bf16_t*>(g.a_gate);
   const bf16_t* a_up = static_cast<const bf16_t*>(g.a_up);
   const bf16_t* a_down = static_cast<const bf16_t*>(g.a_down);
@@ -595,37 +738,26 @@ hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraA
     pj.n = 4;
     MOE_TRY(projections(s, 2 * rp, g.offsets, pj, st));
   }
-  // Outer products over each expert's rows. [Y_gate | Y_up]^T X has the
-  // layout of the gate/up weight gradient with I = rp: its two halves go to
-  // dA_gate and dA_up directly.
+  // Outer products over each expert's rows, straight into the adapter
+  // gradients: dB_gate = dG^T Z_gate, dB_up = dU^T Z_up, dB_down = dO^T
+  // Z_down; then [dA_gate; dA_up] = [Y_gate | Y_up]^T X (one pass over
+  // x_perm) and dA_down = Y_down^T Act.
   {
-    GemmArgs ga{};
-    ga.offsets = g.offsets;
-    ga.a = y_gu;
-    ga.b0 = g.x_perm;
-    ga.dw0 = da_g;
-    ga.dw1 = da_u;
-    ga.part = part;
-    MOE_TRY(launch_gemm(GEMM_WGRAD_GATEUP, lora_gemm_shape(s, H, rp), ga, st));
-  }
-  MOE_TRY(outer_product(s, 2 * I, 2 * rp, g.offsets, g.dgu, z_gu, db_gu, part, st));  // [dG | dU]^T [Z_gate | Z_up]
-  MOE_TRY(outer_product(s, H, rp, g.offsets, g.do_perm, z_d, db_d, part, st));       // dO^T Z_down
-  MOE_TRY(outer_product(s, rp, I, g.offsets, y_d, g.act, da_d, part, st));           // Y_down^T Act
-  // The adapters' own blocks.
-  auto extract = [&](int rows, int cols, const float* src, int src_rows, int src_cols, int row0, int col0,
-                     float* dst) {
-    const int64_t total4 = static_cast<int64_t>(E) * rows * cols / 4;
-    extract_kernel<<<static_cast<unsigned>(ceil_div64(total4, kThreads)), kThreads, 0, st>>>(
-        total4, rows, cols, src, src_rows, src_cols, row0, col0, dst);
-    return hipGetLastError();
-  };
-  MOE_TRY(extract(I, r, db_gu, 2 * I, 2 * rp, 0, 0, g.db_gate));
-  MOE_TRY(extract(I, r, db_gu, 2 * I, 2 * rp, I, rp, g.db_up));
-  if (padded) {
-    MOE_TRY(extract(r, H, da_g, rp, H, 0, 0, g.da_gate));
-    MOE_TRY(extract(r, H, da_u, rp, H, 0, 0, g.da_up));
-    MOE_TRY(extract(r, I, da_d, rp, I, 0, 0, g.da_down));
-    MOE_TRY(extract(H, r, db_d, H, rp, 0, 0, g.db_down));
+    const bf16_t* dgu = static_cast<const bf16_t*>(g.dgu);
+    OuterJobs ob{};
+    ob.job[0] = {dgu, static_cast<const bf16_t*>(z_gu), g.db_gate, nullptr, 2 * I, 0, I, 2 * rp, 0, r, r, r};
+    ob.job[1] = {dgu, static_cast<const bf16_t*>(z_gu), g.db_up, nullptr, 2 * I, I, I, 2 * rp, rp, r, r, r};
+    ob.job[2] = {static_cast<const bf16_t*>(g.do_perm), static_cast<const bf16_t*>(z_d), g.db_down, nullptr, H, 0,
+                 H, rp, 0, r, r, r};
+    ob.n = 3;
+    MOE_TRY(outer_products<false>(E, (r + 31) / 32, g.offsets, ob, st));
+    OuterJobs oa{};
+    oa.job[0] = {static_cast<const bf16_t*>(g.x_perm), static_cast<const bf16_t*>(y_gu), g.da_gate, g.da_up, H, 0,
+                 H, 2 * rp, 0, 2 * rp, rp, r};
+    oa.job[1] = {static_cast<const bf16_t*>(g.act), static_cast<const bf16_t*>(y_d), g.da_down, nullptr, I, 0, I, rp,
+                 0, r, r, r};
+    oa.n = 2;
+    MOE_TRY(outer_products<true>(E, 2 * rp / 32, g.offsets, oa, st));
   }
 #undef MOE_TRY
   return hipSuccess;

@@ -166,17 +166,13 @@ inline hipError_t launch_gemm_pair(GemmMode ma, GemmMode mb, const moe_shape& s,
 }
 
 
-// Low-rank adapters (lora.hip). The gradient path pads the rank to rp, a
-// multiple of 64, so that every reinterpreted GEMM shape meets the kernels'
-// H % 64 == 0 and I % 64 == 0.
+// Low-rank adapters (lora.hip). The projections pad the rank to rp, a
+// multiple of 64 (the padding rows of the scaled adapters are zeros).
 int lora_padded_rank(int r);
-moe_shape lora_gemm_shape(const moe_shape& s, int H, int I);  // s with H and I replaced
 
 struct LoraLayout {  // byte offsets in the adapter-gradient workspace
   size_t sa_gu, sa_d, sbt_gu, sbt_d;  // bf16 scaled adapter stacks
   size_t z_gu, z_d, y_gu, y_d;        // bf16 row projections [T*k][2rp | rp]
-  size_t da_g, da_u, db_gu, da_d, db_d;  // fp32 padded gradients
-  size_t part;                        // fp32 split-K partial tiles
   size_t total;
 };
 LoraLayout lora_layout(const moe_shape& s, int r);
