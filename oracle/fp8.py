@@ -4,9 +4,11 @@ TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg use it; the product path never does. Plain numpy in float64.
 
 The pages' memory-saving path stores expert weights in fewer bits and
-dequantises them inside the grouped GEMM (unsloth PR #3812, the quantised
-weight path of the grouped GEMM; sourcepulse summary, "Highlighted Details",
-4-bit loading). On this chip the matrix cores multiply 8-bit floats
+dequantises them inside the fused MoE linear layers (sourcepulse summary:
+bitsandbytes 4-bit compatibility, "Quick Start & Requirements"; QLoRA and
+training over quantised GGUF models, "Highlighted Details"; the fused 4-bit
+dequantisation, "Limitations & Caveats"; torchtune PR #2820, the question on
+fp8 checkpoints). On this chip the matrix cores multiply 8-bit floats
 directly, so both GEMM operands are 8-bit here:
 
 - Element format: OCP 8-bit float E4M3 (1 sign, 4 exponent bits with bias 7,

@@ -118,13 +118,18 @@ int route(int T, int H, int E, int k, const R* x, const R* wr, const R* bias,
       l[e] = acc;
     }
     // Selection on the logits (softmax is monotone in them): the largest
-    // first; among equal logits the lower expert index first.
+    // first; among equal logits the lower expert index first. A NaN logit
+    // ranks below every number, -inf included (among NaNs, the lower index).
+    auto above = [](R a, R b) {
+      if (std::isnan(b)) return !std::isnan(a);
+      return !std::isnan(a) && a > b;
+    };
     std::vector<char> taken(E, 0);
     for (int j = 0; j < k; ++j) {
       int best = -1;
       for (int e = 0; e < E; ++e) {
         if (taken[e]) continue;
-        if (best < 0 || l[e] > l[best]) best = e;
+        if (best < 0 || above(l[e], l[best])) best = e;
       }
       taken[best] = 1;
       idx[t * k + j] = best;

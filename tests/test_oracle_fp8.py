@@ -10,7 +10,12 @@
   the normal range come back within 2^-4 relative error, zero rows are zero;
 * the expert GEMMs against element-by-element Python loops on tiny inputs,
   and, on inputs that quantise without loss, against the plain float32
-  oracle's G and U.
+  oracle along the whole chain: G and U equal its G and U; A is its A
+  rounded once to bf16; O_perm equals its gate GEMM run on the dequantised
+  codes of A and of the down weights (the oracle's G = X W^T with X := A
+  and W := W_down), weighted and rounded once to bf16;
+* the per-token sum against an element loop over slots in ascending order
+  at k > 1 (a slot-order or reshape mistake changes the float32 sum).
 """
 import math
 
@@ -144,7 +149,9 @@ def test_experts_fp8_against_loops():
 
 def test_experts_fp8_lossless_inputs_match_plain_oracle():
     """Inputs whose rows are E4M3 codes times a power of two quantise without
-    loss, so G and U equal the float32 oracle's on the same values."""
+    loss, so G and U equal the float32 oracle's on the same values; A is the
+    oracle's A rounded to bf16; O_perm is the oracle's GEMM on the
+    dequantised A and W_down, weighted and rounded to bf16."""
     from oracle import oracle as O
     rng = np.random.default_rng(3)
     T, H, I, E, k = 6, 64, 32, 2, 1
@@ -160,11 +167,53 @@ def test_experts_fp8_lossless_inputs_match_plain_oracle():
     wr = np.zeros((E, H), dtype=np.float32)
     f = O.forward(x.astype(np.float32), wr, wg.astype(np.float32), wu.astype(np.float32), wd.astype(np.float32), k)
     offsets, s2f = f["offsets"], f["sorted_to_flat"]
-    out = F8.experts_fp8(x, (s2f // k).astype(np.int32), np.ones(T * k), offsets, F8.quantize_weights(wg),
+    row_weight = rng.uniform(0.25, 1.0, T * k)
+    out = F8.experts_fp8(x, (s2f // k).astype(np.int32), row_weight, offsets, F8.quantize_weights(wg),
                          F8.quantize_weights(wu), F8.quantize_weights(wd))
     for n in ["g", "u"]:
         ref = f[n].astype(np.float64)
         assert np.max(np.abs(out[n] - ref)) <= 1e-6 * np.max(np.abs(ref)), n
+    # A: the oracle's fp32 A, rounded once to bf16 (within a rounding step of
+    # it; the float32 and float64 silu may straddle a bf16 midpoint)
+    a32 = f["a"].astype(np.float64)
+    assert np.all(np.abs(out["a"] - a32) <= 2.0 ** -8 * np.abs(a32) + 1e-30)
+    assert np.mean(out["a"] == F8.bf16_round(a32)) >= 0.99
+    # O_perm: the oracle's own GEMM (its G = X W^T) on X = deq(aq), W = deq(W_down)
+    ad = F8.dequantize_rows(out["aq"], out["ae"])
+    wq, we = F8.quantize_weights(wd)
+    wdd = F8.dequantize_rows(wq.reshape(E * H, I), we.reshape(E * H)).reshape(E, H, I)
+    g2 = O.experts_fwd(ad.astype(np.float32), offsets, wdd.astype(np.float32), np.zeros((E, H, I), np.float32),
+                       np.zeros((E, I, H), np.float32))[0].astype(np.float64)
+    want = F8.bf16_round(g2 * row_weight[:, None])
+    assert np.all(np.abs(out["o_perm"] - want) <= 2.0 ** -8 * np.abs(want) + 1e-30)
+    assert np.mean(out["o_perm"] == want) >= 0.99
+
+
+def test_combine_sum_slots_in_order():
+    """k = 3: each token's sum, element by element, adds its slots' rows in
+    ascending slot order in float32, then rounds once to bf16."""
+    rng = np.random.default_rng(5)
+    T, k, H = 5, 3, 8
+    o = F8.bf16_round(rng.standard_normal((T * k, H)) * 2.0 ** rng.integers(-20, 20, (T * k, 1)))
+    f2s = rng.permutation(T * k).astype(np.int32)
+    # in the first four columns a token's slots hold 1, 2^30 and -2^30: in
+    # slot order the 1 is absorbed (sum 0), in reverse order it survives
+    slots = f2s.reshape(T, k)
+    o[slots[:, 0], :4] = 1.0
+    o[slots[:, 1], :4] = 2.0 ** 30
+    o[slots[:, 2], :4] = -(2.0 ** 30)
+    got = F8.combine_sum(o, f2s, T, k)
+    for t in range(T):
+        for h in range(H):
+            acc = np.float32(0.0)
+            for j in range(k):
+                acc = np.float32(acc + np.float32(o[f2s[t * k + j], h]))
+            assert got[t, h] == F8.bf16_round(np.array([acc]))[0], (t, h)
+    # a slot-order mistake shows: the reversed order gives a different sum somewhere
+    rev = np.zeros((T, H), np.float32)
+    for j in reversed(range(k)):
+        rev = rev + o[f2s.reshape(T, k)[:, j]].astype(np.float32)
+    assert not np.array_equal(F8.bf16_round(rev), got)
 
 
 def test_combine_sum_one_slot_is_the_row():

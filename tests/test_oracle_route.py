@@ -138,3 +138,30 @@ def test_zipf_bias_skews_routing(oracle):
     counts = np.bincount(idx.ravel(), minlength=cfg.E)
     assert (counts == 0).sum() >= 1
     assert counts.max() > 0.10 * idx.size
+
+
+def test_selection_ranks_nan_below_every_number(oracle):
+    """A NaN logit ranks below every number, -inf included; equal logits and
+    NaNs keep the lower expert index first (so every token selects k valid
+    experts whatever its logits)."""
+    nan, inf = float("nan"), float("inf")
+    bias = np.array([-inf, nan, 1.0, nan, -inf, 0.0], dtype=np.float32)
+    x = np.zeros((2, 16), np.float32)  # logits = 0 + bias
+    wr = np.zeros((6, 16), np.float32)
+    _, idx, _ = oracle.route(x, wr, 6, bias)
+    assert idx.tolist() == [[2, 5, 0, 4, 1, 3]] * 2
+    # A token whose hidden state holds a NaN: every logit is NaN, the
+    # selection is experts 0 .. k-1 and the weights are NaN.
+    rng = np.random.default_rng(0)
+    x = _rand(rng, (4, 32))
+    x[2, 7] = nan
+    wr = _rand(rng, (8, 32), 0.5)
+    logits, idx, w = oracle.route(x, wr, 3)
+    assert np.all(np.isnan(logits[2])) and idx[2].tolist() == [0, 1, 2] and np.all(np.isnan(w[2]))
+    for t in (0, 1, 3):
+        assert idx[t].tolist() == list(np.argsort(-logits[t], kind="stable")[:3]) and np.all(np.isfinite(w[t]))
+    # A NaN router row: that expert's logit is NaN on every token, so no
+    # token selects it while k leaves enough other experts.
+    wr[5, 0] = nan
+    _, idx, _ = oracle.route(np.nan_to_num(x), wr, 3)
+    assert not np.any(idx == 5)
