@@ -16,12 +16,15 @@ directly, so both GEMM operands are 8-bit here:
   largest finite value 448; subnormals m * 2^-9).
 - Scales: one power of two per row (a token's row of x or of the expert
   activations, an output channel's row of a weight), stored as its biased
-  8-bit exponent (the E8M0 encoding: code c means 2^(c - 127)). Following
-  the shared-exponent rule of the OCP microscaling formats, a row with
-  largest magnitude amax gets exponent X = floor(log2(amax)) - 8 (8 being
-  E4M3's largest exponent), clamped to [-127, 127]; an all-zero row gets
-  -127. Elements are x / 2^X (exact: a power of two), clamped to +-448 and
-  rounded to the nearest E4M3 value, ties to the even code.
+  8-bit exponent (the E8M0 encoding: code c means 2^(c - 127)). A row with
+  largest magnitude amax gets the smallest exponent X with amax / 2^X <= 448
+  (E4M3's largest finite value), clamped to [-127, 127]; an all-zero row
+  gets -127. The row's largest element then lands in (224, 448], so no
+  element is clipped (the shared-exponent rule of the OCP microscaling
+  formats, floor(log2(amax)) - 8, puts it in [256, 512) and clips the part
+  above 448, up to an eighth of the element). Elements are x / 2^X (exact: a
+  power of two), clamped to +-448 and rounded to the nearest E4M3 value, ties
+  to the even code.
 - A dequantised element is decode(code) * 2^X, exact in float64.
 
 Readings taken where the pages are silent (listed with the others in the
@@ -79,8 +82,10 @@ def quantize_rows(x: np.ndarray):
     """Rows of x [R, K] -> (codes [R, K] uint8, e8 [R] uint8)."""
     x = np.asarray(x, dtype=np.float64)
     amax = np.max(np.abs(x), axis=1)
-    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
-    X = np.where(amax > 0, (ex - 1) - 8, -E8M0_BIAS)  # floor(log2(amax)) - 8
+    # amax = f 2^ex with f in [0.5, 1) and 448 = 0.875 2^9: amax / 2^(ex - 9)
+    # = 512 f is at most 448 exactly when f <= 0.875, else one more power of two.
+    f, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    X = np.where(amax > 0, ex - 9 + (f > 0.875), -E8M0_BIAS)
     X = np.clip(X, -E8M0_BIAS, E8M0_BIAS)
     codes = e4m3_encode(np.ldexp(x, -X[:, None]))
     return codes, (X + E8M0_BIAS).astype(np.uint8)

@@ -5,9 +5,11 @@
 * encoding inverts decoding on every finite code, rounds to the nearest
   value with ties to the even code (checked against torch's conversion on
   random values and on every midpoint), and saturates at +-448;
-* row quantisation: the scale exponent is floor(log2(amax)) - 8 (from
-  math.frexp per row), the largest element lands in [256, 448], elements in
-  the normal range come back within 2^-4 relative error, zero rows are zero;
+* row quantisation: the scale exponent is the smallest X with
+  amax / 2^X <= 448 (found by a search over integers with math.ldexp per
+  row), the largest element lands in (224, 448] and no element is clipped,
+  elements in the normal range come back within 2^-4 relative error, zero
+  rows are zero;
 * the expert GEMMs against element-by-element Python loops on tiny inputs,
   and, on inputs that quantise without loss, against the plain float32
   oracle along the whole chain: G and U equal its G and U; A is its A
@@ -85,23 +87,30 @@ def test_quantize_rows_scale_and_error():
     rows = [rng.standard_normal(96) * 2.0 ** s for s in (-20, -3, 0, 5, 30)]
     rows.append(np.zeros(96))
     rows.append(np.r_[np.zeros(95), -3.0])
+    # largest magnitudes on both sides of 448 * 2^k and of 224 * 2^k
+    for top in (448.0, 448.0 * (1 + 2.0 ** -7), 449.0 / 2 ** 3, 224.0, 224.0 * (1 + 2.0 ** -7), 7.99, 8.0):
+        rows.append(np.r_[rng.uniform(-1, 1, 95), top])
     x = np.stack(rows).astype(np.float32).astype(np.float64)
     q, e8 = F8.quantize_rows(x)
-    for r in range(len(rows)):
+    for r in range(len(x)):
         amax = np.max(np.abs(x[r]))
         if amax == 0:
             assert e8[r] == 0 and not q[r].any()
             continue
-        m, ex = math.frexp(amax)
-        X = ex - 1 - 8
+        X = -200
+        while math.ldexp(amax, -X) > 448.0:  # the smallest X with amax / 2^X <= 448
+            X += 1
         assert int(e8[r]) - 127 == X
         deq = F8.dequantize_rows(q[r:r + 1], e8[r:r + 1])[0]
         top = np.max(np.abs(F8.e4m3_decode(q[r])))
-        assert 256.0 <= top <= 448.0
+        assert 224.0 <= top <= 448.0
         normal = np.abs(x[r]) >= 2.0 ** (X - 6)
         assert np.all(np.abs(deq - x[r])[normal] <= 2.0 ** -4 * np.abs(x[r])[normal])
         # below the normal range the error is at most half a subnormal step
         assert np.all(np.abs(deq - x[r])[~normal] <= 2.0 ** (X - 10))
+        # nothing clipped: the largest element is within half an E4M3 step
+        i = int(np.argmax(np.abs(x[r])))
+        assert abs(deq[i] - x[r, i]) <= 2.0 ** -4 * abs(x[r, i])
 
 
 def test_bf16_round():
