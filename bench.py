@@ -1,6 +1,7 @@
 """Throughput of one MoE layer's expert stage (forward + backward) on one GPU.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--timed-only]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--seeds 0,1,2]
+                    [--no-cpu-baseline] [--timed-only]
 
 One step is the whole stage on one batch of synthetic input already resident
 in HBM, on one stream, as the library chains it (MoEStage; moe_grouped_gemm_fwd
@@ -10,7 +11,9 @@ backward (data gradient with the SwiGLU backward epilogue, then the weight
 gradient, in one persistent launch) -> gate/up backward (likewise) ->
 unpermute-sum -> router backward, every step a call of the C ABI.
 
-Prints one JSON line. `value` is tokens/s of the whole stage; TFLOP/s counts
+Each input seed (default 0, 1 and 2) gets W untimed warmup steps and K timed
+steps; the line reports the seed with the median time (`ms_per_step_by_seed`
+lists all three). Prints one JSON line. `value` is tokens/s of the whole stage; TFLOP/s counts
 the expert GEMMs (18*T*k*H*I per step). Around every GEMM call the timed
 steps also record HIP events on the stream, which give `call_ms`,
 `gemm_tflops` and `roofline`; the calls without matrix work are timed each
@@ -22,7 +25,9 @@ rocprofv3's FETCH_SIZE and WRITE_SIZE counters gave for that kernel, scaled by
 what they read for a plain device copy of known size (--calibrate-copy); it is
 taken from the committed summary under profiles/ and reported only while the
 GEMM source still hashes to the value recorded there. `cpu_baseline` times
-the CPU oracle on a bounded token sample of the same workload.
+the CPU oracle on every token of the same workload (first seed), on every
+host thread this job may use (the CPUs it may run on, capped by
+OMP_NUM_THREADS), with the host's CPU count and model.
 
 After the timed steps (and outside them): `ms_per_step_without_call_events`
 times the same step without the per-call events; `graph_ms_per_step` the same
@@ -146,23 +151,51 @@ def gemm_flops(c) -> dict:
     }
 
 
+def host_threads() -> dict:
+    """The host's CPU count, the CPUs this process may run on, and the share
+    the oracle uses: all of those, capped by OMP_NUM_THREADS when it is set
+    (a machine that shares its host between jobs sets it to the job's share)."""
+    nproc = os.cpu_count() or 1
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:
+        allowed = nproc
+    share = allowed
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        share = min(share, int(cap))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": nproc, "affinity": allowed, "threads": share, "cpu_model": model}
+
+
 def cpu_baseline(cfg, seed: int, tokens: int) -> dict:
-    """The oracle, as it stands, on the first `tokens` tokens of the workload."""
+    """The oracle, as it stands, on the first `tokens` tokens of the workload
+    (all of them by default), on every host thread this job may use."""
     import numpy as np  # noqa: F401
 
     from mixture_experts_expert_amd import synth
     from oracle import oracle as O
 
-    threads = min(16, os.cpu_count() or 1)
-    O.set_threads(threads)
+    host = host_threads()
+    O.set_threads(host["threads"])
     inp = synth.make_inputs(cfg, seed, T=tokens)
     f = {n: inp.f32(n) for n in inp.names()}
     t0 = time.perf_counter()
     fwd = O.forward(f["x"], f["w_router"], f["w_gate"], f["w_up"], f["w_down"], cfg.k, logit_bias=inp.logit_bias)
     O.backward(fwd, f["dy"], f["w_gate"], f["w_up"], f["w_down"])
     dt = time.perf_counter() - t0
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{tokens} of {cfg.T} tokens (same H, E, k, I), fwd+bwd, {dt:.1f} s"}
+    what = "all" if tokens == cfg.T else f"{tokens} of {cfg.T}"
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": host["threads"], "kind": "oracle",
+            "sample": f"{what} tokens of the workload (seed {seed}), fwd+bwd, {dt:.1f} s",
+            "host": host}
 
 
 def time_calls(fn, stream, reps=10) -> float:
@@ -225,9 +258,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_30b_a3b_train")
-    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--seeds", default="0,1,2",
+                    help="input seeds; each runs W warmup and K timed steps, the line reports the median")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample (default: every token of the workload)")
     ap.add_argument("--timed-only", action="store_true",
                     help="launch nothing after the timed steps (for profiling): no sequential, inference or CPU pass")
     ap.add_argument("--lora-only", action="store_true",
@@ -250,17 +284,29 @@ def main() -> int:
 
     cfg = synth.CONFIGS[args.workload]
     assert cfg.backward and cfg.dtype == "bf16", "the benchmark runs bf16 training-step workloads"
+    seeds = [int(v) for v in args.seeds.split(",")]
     torch.cuda.set_device(0)
-    log(f"workload {cfg}")
-    t0 = time.perf_counter()
-    inp = synth.make_inputs(cfg, args.seed)
-    dev = {n: torch.from_numpy(inp.bits[n].view(np.int16)).to("cuda").view(torch.bfloat16) for n in inp.names()}
-    bias = None if inp.logit_bias is None else torch.from_numpy(inp.logit_bias).to("cuda")
-    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    log(f"workload {cfg}, seeds {seeds}")
+
+    # The step's input tensors; the call lambdas below read them from here,
+    # so that switching seeds swaps the tensors they see.
+    cur = {}
+
+    def load(seed):
+        t0 = time.perf_counter()
+        cur.clear()
+        torch.cuda.empty_cache()
+        inp = synth.make_inputs(cfg, seed)
+        for n in inp.names():
+            cur[n] = torch.from_numpy(inp.bits[n].view(np.int16)).to("cuda").view(torch.bfloat16)
+        cur["bias"] = None if inp.logit_bias is None else torch.from_numpy(inp.logit_bias).to("cuda")
+        torch.cuda.synchronize()
+        log(f"seed {seed}: inputs ready in {time.perf_counter() - t0:.1f} s")
 
     if args.lora_only:
-        tensors = tuple(dev[n] for n in ["x", "w_router", "w_gate", "w_up", "w_down", "dy"])
-        print(json.dumps({"lora_ms": lora_timing(cfg, args.seed, tensors, bias, torch.cuda.current_stream()),
+        load(seeds[0])
+        tensors = tuple(cur[n] for n in ["x", "w_router", "w_gate", "w_up", "w_down", "dy"])
+        print(json.dumps({"lora_ms": lora_timing(cfg, seeds[0], tensors, cur["bias"], torch.cuda.current_stream()),
                           "config": {"workload": cfg.name}}), flush=True)
         return 0
 
@@ -268,8 +314,10 @@ def main() -> int:
     st._alloc_bwd()
     b, s = st.buf, st.s
     dgu = torch.empty(cfg.M, 2 * cfg.I, dtype=torch.bfloat16, device="cuda")  # [dG | dU]
-    x, wr, wg, wu, wd, dy = (dev[n] for n in ["x", "w_router", "w_gate", "w_up", "w_down", "dy"])
     stream = torch.cuda.current_stream()
+    # The calls below read these names when they run (closures bind late), so
+    # loading another seed's inputs and rebinding them switches every call.
+    x = wr = wg = wu = wd = dy = bias = None
     # The 12 C-ABI calls with one launch per GEMM; the timed step runs the
     # library's own chain (what MoEStage and moe_grouped_gemm_bwd do): the
     # backward's GEMMs as the two paired launches.
@@ -348,22 +396,28 @@ def main() -> int:
         e.record(aux)
         stream.wait_event(e)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done")
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for k in range(args.steps):
-        step(ev[k])
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms = total_ms / args.steps
-    per_call = {n: sum(ev[k][start_of[n]].elapsed_time(ev[k][n]) for k in range(args.steps)) / args.steps
-                for n in gemm_names}
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step; " + ", ".join(f"{n}={v:.3f}" for n, v in per_call.items()))
+    # W warmup and K timed steps per seed; the line reports the median seed.
+    runs = []
+    for seed in seeds[1:] + seeds[:1]:  # the first seed last: the later measurements use its inputs
+        load(seed)
+        x, wr, wg, wu, wd, dy, bias = (cur[n] for n in ["x", "w_router", "w_gate", "w_up", "w_down", "dy", "bias"])
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for k in range(args.steps):
+            step(ev[k])
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_seed = start.elapsed_time(end) / args.steps
+        per_call_seed = {n: sum(ev[k][start_of[n]].elapsed_time(ev[k][n]) for k in range(args.steps)) / args.steps
+                         for n in gemm_names}
+        runs.append((ms_seed, seed, per_call_seed))
+        log(f"seed {seed}: {args.warmup} warmup, {args.steps} timed steps: {ms_seed:.3f} ms/step; "
+            + ", ".join(f"{n}={v:.3f}" for n, v in per_call_seed.items()))
+    ms, median_seed, per_call = sorted(runs)[len(runs) // 2]
+    ms_by_seed = {str(sd): round(m, 4) for m, sd, _ in sorted(runs, key=lambda r: r[1])}
 
     def time_fn(fn, reps=10):
         return time_calls(fn, stream, reps)
@@ -465,7 +519,7 @@ def main() -> int:
         infer["fp8_down"] = round(time_fn(down8, reps=5), 4)
         log(f"inference forward: {infer}")
 
-    lora = None if args.timed_only else lora_timing(cfg, args.seed, (x, wr, wg, wu, wd, dy), bias, stream)
+    lora = None if args.timed_only else lora_timing(cfg, seeds[0], (x, wr, wg, wu, wd, dy), bias, stream)
 
     flops = gemm_flops(cfg)
     nbytes = alg_bytes(cfg)
@@ -512,7 +566,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded normal inputs, random-init weights of the Qwen3-30B-A3B MoE layer shape)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
-                   "seed": args.seed, "pass": "fwd+bwd"},
+                   "seeds": seeds, "pass": "fwd+bwd"},
+        "ms_per_step_by_seed": ms_by_seed,
         "tflops": round(tflops, 1),
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "gemm_tflops": gemm_tflops,
@@ -529,8 +584,9 @@ def main() -> int:
         "lora_ms": lora,
     }
     if not (args.no_cpu_baseline or args.timed_only):
-        log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
-        out["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_tokens)
+        tokens = args.cpu_tokens or cfg.T
+        log(f"cpu baseline: oracle on {tokens} tokens")
+        out["cpu_baseline"] = cpu_baseline(cfg, seeds[0], tokens)
     print(json.dumps(out), flush=True)
     return 0
 

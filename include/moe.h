@@ -96,8 +96,10 @@ size_t moe_workspace_bytes(moe_shape s);
  *   or NULL.
  *   logits[t,e] = fp32 fma chain over h ascending from +0, then + bias[e];
  *   topk_idx[t,:] = the k largest logits, largest first, ties to the lower
- *   expert index; topk_w[t,j] = p[idx] / (sum_j p[idx] + 1e-20) with
- *   p = softmax(logits[t,:]) in fp32.
+ *   expert index; a NaN logit ranks below every number, -inf included (so
+ *   every index is a valid expert whatever the logits); topk_w[t,j] =
+ *   p[idx] / (sum_j p[idx] + 1e-20) with p = softmax(logits[t,:]) in fp32 (NaN
+ *   for a token with a NaN logit).
  * Outputs: logits [T,E] f32, topk_idx [T,k] int32, topk_w [T,k] f32. */
 moe_status moe_route(moe_shape s, const void* x, const void* w_router, const float* logit_bias,
                      float* logits, int32_t* topk_idx, float* topk_w, hipStream_t stream);
@@ -223,7 +225,8 @@ moe_status moe_unpermute_sum(moe_shape s, const void* dx_perm, const int32_t* fl
  *   d_logits[t,e] = w_j (g_j - sum_i w_i g_i) if e = topk_idx[t,j], else 0,
  *   with w = topk_w and g = d_topk_w. (The exact derivative also carries terms
  *   of relative size 1e-20 from the renormalisation constant; they are
- *   dropped.) Output: d_logits [T,E] f32. */
+ *   dropped.) An index outside [0, E) contributes nothing (its slot still
+ *   counts in the sum). Output: d_logits [T,E] f32. */
 moe_status moe_route_bwd(moe_shape s, const float* d_topk_w, const float* topk_w, const int32_t* topk_idx,
                          float* d_logits, hipStream_t stream);
 
@@ -286,19 +289,22 @@ moe_status moe_forward_fused(moe_shape s, const void* x, const void* w_router, c
                              int32_t* sorted_to_flat, int32_t* flat_to_sorted, int32_t* row_token, float* row_weight,
                              void* a, void* o_perm, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* ---- fp8 inference forward (the quantised-weight path of unsloth PR #3812,
- * "[MoE] Improve moe kernels for unsloth fine tuning", and the 4-bit loading
- * of the sourcepulse summary, "Highlighted Details", taken to the 8-bit
- * floats gfx950's matrix cores multiply natively). Both GEMM operands are
+/* ---- fp8 inference forward (the quantised expert weights of the sourcepulse
+ * summary: bitsandbytes 4-bit compatibility, "Quick Start & Requirements";
+ * QLoRA and training over quantised GGUF models, "Highlighted Details"; the
+ * fused 4-bit dequantisation, "Limitations & Caveats"; and the question on
+ * fp8 checkpoints in torchtune PR #2820; taken to the 8-bit floats gfx950's
+ * matrix cores multiply natively). Both GEMM operands are
  * OCP E4M3 codes (bias 7, largest finite 448, 0x7F/0xFF NaN); every row of
  * an operand carries one power-of-two scale as an E8M0 byte c (2^(c-127)).
  * The GEMMs multiply codes and apply both scales inside the matrix core, so
  * a product is exactly dequant(a) * dequant(w), summed in fp32. */
 
 /* Rows [rows, K] of bf16 -> E4M3 codes q [rows, K] and one scale per row.
- * Scale 2^X with X = floor(log2(max |row|)) - 8, clamped to [-127, 127]
- * (-127 for an all-zero row); q = E4M3(clamp(x / 2^X, -448, 448)), rounded
- * to nearest, ties to even. e8 layout: [rows] when flat_to_sorted is NULL;
+ * Scale 2^X with X the smallest integer for which max |row| / 2^X <= 448,
+ * clamped to [-127, 127] (-127 for an all-zero row), so that no element is
+ * clipped; q = E4M3(clamp(x / 2^X, -448, 448)), rounded to nearest, ties to
+ * even. e8 layout: [rows] when flat_to_sorted is NULL;
  * otherwise [rows * k] in sorted order, row r's scale written at
  * flat_to_sorted[r * k + j] for every j < k (x's scales for the gathered
  * gate/up GEMM). K % 8 == 0 (MOE_EINVAL otherwise). Weights are quantised

@@ -30,6 +30,11 @@ bool any_null(P... p) {
 
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+// x read through row tokens is addressed with 32-bit byte offsets.
+bool gathered_x_fits(const moe_shape& s) {
+  return static_cast<int64_t>(s.T) * s.H * (s.dtype == MOE_BF16 ? 2 : 4) < (static_cast<int64_t>(1) << 31);
+}
+
 }  // namespace
 
 extern "C" {
@@ -261,6 +266,7 @@ moe_status moe_forward_fused(moe_shape s, const void* x, const void* w_router, c
   if (any_null(x, w_router, w_gate, w_up, w_down, logits, topk_idx, topk_w, counts, offsets, sorted_to_flat,
                flat_to_sorted, row_token, row_weight, a, o_perm, y, ws))
     return MOE_EINVAL;
+  if (!gathered_x_fits(s)) return MOE_EUNSUPPORTED;
   if (ws_bytes < moe::ws_layout(s).total) return MOE_EWORKSPACE;
   if ((st = moe_route(s, x, w_router, logit_bias, logits, topk_idx, topk_w, stream)) != MOE_OK) return st;
   if ((st = moe_permute_fused(s, topk_idx, topk_w, counts, offsets, sorted_to_flat, flat_to_sorted, row_token,

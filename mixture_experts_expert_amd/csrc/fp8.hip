@@ -1,16 +1,17 @@
 // Rows of a bf16 matrix -> 8-bit floats (OCP E4M3) with one power-of-two
 // scale per row, for the fp8 expert GEMMs.
 //
-// The pages' memory-saving path keeps expert weights in fewer bits (unsloth
-// PR #3812, quantised weights in the grouped GEMM; sourcepulse summary,
-// "Highlighted Details"). Here both GEMM operands are E4M3 and each row
-// carries its scale as a biased exponent byte (E8M0, 2^(c - 127)), chosen by
-// the shared-exponent rule of the OCP microscaling formats: X =
-// floor(log2(max |x|)) - 8, so the row's largest element lands in [256, 512)
-// before the clamp to E4M3's 448. Dividing by 2^X is exact, so the only
-// rounding is the conversion to E4M3 (nearest, ties to even), which the
-// hardware does; values past 448 are clamped first because the conversion
-// turns them into NaN instead of saturating.
+// The pages' memory-saving path keeps expert weights in fewer bits
+// (sourcepulse summary: bitsandbytes 4-bit weights, "Quick Start &
+// Requirements"; QLoRA and quantised GGUF models, "Highlighted Details").
+// Here both GEMM operands are E4M3 and each row carries its scale as a
+// biased exponent byte (E8M0, 2^(c - 127)): the smallest X with
+// max |x| / 2^X <= 448, so the row's largest element lands in (224, 448] and
+// nothing is clipped. Dividing by 2^X is exact, so the only rounding is the
+// conversion to E4M3 (nearest, ties to even), which the hardware does; the
+// clamp to +-448 before it (a no-op unless X hit its limit of 127) is there
+// because the conversion turns values past 448 into NaN instead of
+// saturating.
 //
 // One wavefront per row; lanes take 16-byte chunks (8 elements) of it.
 #include "moe_internal.h"
@@ -49,9 +50,11 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(int rows, int K
   for (int o = kWave / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
   int X = -127;
   if (amax > 0.0f) {
+    // amax = f 2^ex, f in [0.5, 1); 448 = 0.875 2^9, so amax / 2^(ex - 9) =
+    // 512 f is at most 448 exactly when f <= 0.875, else one power more.
     int ex;
-    frexpf(amax, &ex);  // amax = f 2^ex, f in [0.5, 1): floor(log2(amax)) = ex - 1
-    X = min(127, max(-127, ex - 1 - 8));
+    const float f = frexpf(amax, &ex);
+    X = min(127, max(-127, ex - 9 + (f > 0.875f ? 1 : 0)));
   }
   uint2* dst = q + static_cast<int64_t>(row) * chunks;
   for (int c = lane; c < chunks; c += kWave) {

@@ -184,13 +184,13 @@ WsLayout ws_layout(const moe_shape& s) {
 
 namespace {
 
-// The stable counting sort shared by both permute entry points.
+// The stable counting sort shared by the permute entry points; hist holds
+// ceil(T*k / kPermBlock) * E int32 (every element is written before it is read).
 hipError_t launch_sort(const moe_shape& s, const int32_t* idx, int32_t* counts, int32_t* offsets, int32_t* s2f,
-                       int32_t* f2s, const float* w, int32_t* row_token, float* row_weight, void* ws,
+                       int32_t* f2s, const float* w, int32_t* row_token, float* row_weight, int32_t* hist,
                        hipStream_t st) {
   const int n = s.T * s.k;
   const int nb = ceil_div(n, kPermBlock);
-  int32_t* hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ws_layout(s).hist_off);
   int nbits = 0;
   while ((1 << nbits) < s.E) ++nbits;
   block_hist_kernel<<<nb, kThreads, 0, st>>>(n, s.E, idx, hist);
@@ -203,12 +203,16 @@ hipError_t launch_sort(const moe_shape& s, const int32_t* idx, int32_t* counts, 
   return hipGetLastError();
 }
 
+int32_t* ws_hist(const moe_shape& s, void* ws) {
+  return reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ws_layout(s).hist_off);
+}
+
 }  // namespace
 
 hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const void* x, int32_t* counts,
                           int32_t* offsets, int32_t* s2f, int32_t* f2s, void* x_perm, void* ws,
                           hipStream_t st) {
-  hipError_t err = launch_sort(s, idx, counts, offsets, s2f, f2s, nullptr, nullptr, nullptr, ws, st);
+  hipError_t err = launch_sort(s, idx, counts, offsets, s2f, f2s, nullptr, nullptr, nullptr, ws_hist(s, ws), st);
   if (err != hipSuccess) return err;
   const int esz = s.dtype == MOE_BF16 ? 2 : 4;
   const int chunks = s.H * esz / 16;
@@ -221,7 +225,7 @@ hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const void* x,
 hipError_t launch_permute_fused(const moe_shape& s, const int32_t* idx, const float* w, int32_t* counts,
                                 int32_t* offsets, int32_t* s2f, int32_t* f2s, int32_t* row_token, float* row_weight,
                                 void* ws, hipStream_t st) {
-  return launch_sort(s, idx, counts, offsets, s2f, f2s, w, row_token, row_weight, ws, st);
+  return launch_sort(s, idx, counts, offsets, s2f, f2s, w, row_token, row_weight, ws_hist(s, ws), st);
 }
 
 }  // namespace moe

@@ -138,9 +138,13 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(int Tn, in
 constexpr int kMaxPerLane = 1024 / kWave;  // E <= 1024
 constexpr int kTokPerBlock = 4;            // one wave per token
 
-// (value, index) order of the selection: larger value first, then lower index.
+// (value, index) order of the selection: larger value first, then lower
+// index. A NaN ranks below every number, -inf included (two NaNs: the lower
+// index first), so every token selects k valid experts whatever its logits.
 __device__ __forceinline__ bool before(float v, int i, float ov, int oi) {
-  return v > ov || (v == ov && i < oi);
+  const bool vn = v != v, on = ov != ov;
+  if (vn != on) return on;
+  return v > ov || (!(v < ov) && i < oi);
 }
 
 __global__ __launch_bounds__(kWave* kTokPerBlock) void router_topk_kernel(int Tn, int E, int k,
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(kWave* kTokPerBlock) void router_topk_kernel(int Tn
 
   float vmax = 0.0f;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
+    float bv = __builtin_nanf("");  // below every candidate, NaN logits included
     int bi = 0x7fffffff;
 #pragma unroll
     for (int c = 0; c < kMaxPerLane; ++c) {
@@ -226,7 +230,10 @@ __global__ __launch_bounds__(kWave* kTokPerBlock) void router_bwd_kernel(int Tn,
   gs = wave_sum(gs);
   __syncthreads();
   if (active)
-    for (int j = lane; j < k; j += kWave) row[wv][idx[tk + j]] = w[tk + j] * (gw[tk + j] - gs);
+    for (int j = lane; j < k; j += kWave) {
+      const int e = idx[tk + j];
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) row[wv][e] = w[tk + j] * (gw[tk + j] - gs);
+    }
   __syncthreads();
   if (active)
     for (int e = lane; e < E; e += kWave) d_logits[static_cast<int64_t>(t) * E + e] = row[wv][e];

@@ -19,6 +19,15 @@ def oracle():
     return O
 
 
+@pytest.fixture(autouse=True)
+def _parity_log_section():
+    """Checks log under the workload their own test names (gpu_util.begin)."""
+    yield
+    gu = sys.modules.get("gpu_util")
+    if gu is not None:
+        gu._current["workload"] = None
+
+
 def _ensure_built():
     lib = os.path.join(ROOT, "mixture_experts_expert_amd", "libmoe.so")
     if not os.path.exists(lib):

@@ -3,9 +3,29 @@ inputs, one pass of the stage through the C ABI, oracle references on the
 same bytes, and the error metrics.
 
 Tolerances: integers (routing indices, counts, offsets, permutations) and the
-router logits must match bit for bit; float outputs must satisfy
-max|gpu - oracle| / max|oracle| <= 2e-2 for bf16 workloads (fp32
-accumulation, bf16 storage of intermediates) and <= 1e-4 for fp32 ones.
+router logits must match bit for bit. Float outputs are held to a normwise
+relative error max|gpu - oracle| / max|oracle| <= 2e-2 for bf16 workloads
+(fp32 accumulation, bf16 storage of intermediates) and <= 1e-4 for fp32
+ones, taken per row: per token for y, dx, d_topk_w and d_logits, per sorted
+row for g, u, a, o_perm, do_perm and dx_perm, per expert for the weight
+gradients. A small row or expert is then held to its own scale, not to the
+largest one's. Two outputs are sums that can cancel: g = d_topk_w[t,j] =
+<dY[t], O_perm[p]> (a token whose k dot products are all near zero has
+its error, from O_perm's rounding to bf16, measured against a tiny
+denominator), and d_logits = w_j (g_j - sum_i w_i g_i) (also cancelling
+when a token's g_j are nearly equal). Their per-token denominators are
+max_j |g_j|, floored at the root mean square of g over the whole tensor,
+times max_j w_j for d_logits (the oracle's topk_w and d_topk_w): a token
+is held to its own scale unless that scale is below the tensor's typical
+one. Every check also reports the median elementwise relative error
+|gpu - oracle| / |oracle| over a fixed-stride sample of at most 2^22
+elements (for d_logits, over the top-k entries only: off them the oracle
+holds rounding residues of its chain rule, of order 1e-8, where the GPU
+writes zeros).
+
+When MOE_PARITY_DIR is set, every check appends a line (output, metric,
+largest error, median elementwise error, rows) to
+$MOE_PARITY_DIR/parity.<workload>.txt.
 """
 from __future__ import annotations
 
@@ -114,54 +134,126 @@ def oracle_route(inp: synth.Inputs) -> Dict[str, np.ndarray]:
                 flat_to_sorted=f2s)
 
 
+PARITY_DIR = os.environ.get("MOE_PARITY_DIR")
+MEDIAN_SAMPLE = 1 << 22
+_current = {"workload": None}
+
+
+def begin(name: str, header: str = "") -> None:
+    """Names the workload that the following checks log under (and starts its
+    section of the parity log)."""
+    _current["workload"] = name
+    _log(f"# {header or name}")
+
+
+def _log(line: str) -> None:
+    name = _current["workload"]
+    if PARITY_DIR and name:
+        os.makedirs(PARITY_DIR, exist_ok=True)
+        with open(os.path.join(PARITY_DIR, f"parity.{name}.txt"), "a") as f:
+            f.write(line + "\n")
+
+
+def g_scale(d_topk_w: np.ndarray) -> np.ndarray:
+    """Per token: max_j |g_j|, floored at the tensor's root mean square of g
+    (oracle values)."""
+    g = np.asarray(d_topk_w, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(g * g))) if g.size else 0.0
+    return np.maximum(np.abs(g).max(axis=1), rms)
+
+
+def d_logits_scale(topk_w: np.ndarray, d_topk_w: np.ndarray) -> np.ndarray:
+    """Per token: max_j |w_j| * g_scale, the scale of the terms whose
+    difference d_logits is (oracle values)."""
+    return np.abs(topk_w).max(axis=1).astype(np.float64) * g_scale(d_topk_w)
+
+
+def topk_mask(topk_idx: np.ndarray, E: int) -> np.ndarray:
+    m = np.zeros((topk_idx.shape[0], E), dtype=bool)
+    np.put_along_axis(m, topk_idx.astype(np.int64), True, axis=1)
+    return m
+
+
 def check_routing(st, ref: Dict[str, np.ndarray]) -> None:
     b = st.buf
     assert same_bits(to_np(b["logits"]), ref["logits"]), "logits differ"
     for n in ["topk_idx", "counts", "offsets", "sorted_to_flat", "flat_to_sorted"]:
         assert np.array_equal(to_np(b[n]), ref[n]), n
-    err = normwise(to_np(b["topk_w"]), ref["topk_w"])
-    assert err <= 1e-5, ("topk_w", err)
+    _log("logits topk_idx counts offsets sorted_to_flat flat_to_sorted: bit-exact")
+    check_close("topk_w", to_np(b["topk_w"]), ref["topk_w"], 1e-5)
 
 
-def check_close(name: str, gpu: np.ndarray, ref: np.ndarray, tolerance: float) -> float:
-    err = normwise(gpu, ref)
-    say(f"  {name:10s} normwise err {err:.3e}")
-    assert err <= tolerance, (name, err, tolerance)
+def rowwise(gpu: np.ndarray, ref: np.ndarray, chunk: int = 4096, scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """Normwise relative error of every row (axis 0): max|gpu - ref| over the
+    row / max|ref| over the row (or / scale[row] when given); a row whose
+    denominator is zero gets max|gpu - ref| (so it passes only when the GPU
+    wrote the oracle's zeros)."""
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    R = gpu.shape[0]
+    if R == 0:
+        return np.zeros(0)
+    g2 = gpu.reshape(R, -1)
+    r2 = ref.reshape(R, -1)
+    out = np.empty(R)
+    for lo in range(0, R, chunk):
+        g = np.asarray(g2[lo:lo + chunk], dtype=np.float64)
+        r = np.asarray(r2[lo:lo + chunk], dtype=np.float64)
+        den = np.abs(r).max(axis=1) if r.shape[1] else np.zeros(len(r))
+        if scale is not None:
+            den = np.asarray(scale[lo:lo + chunk], dtype=np.float64)
+        num = np.abs(g - r).max(axis=1) if r.shape[1] else np.zeros(len(r))
+        out[lo:lo + chunk] = np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+    return out
+
+
+def median_rel(gpu: np.ndarray, ref: np.ndarray, mask: Optional[np.ndarray] = None) -> float:
+    """Median of |gpu - ref| / |ref| over the nonzero oracle elements (and
+    where mask is true) of a fixed-stride sample (at most MEDIAN_SAMPLE)."""
+    g = np.asarray(gpu).reshape(-1)
+    r = np.asarray(ref).reshape(-1)
+    stride = max(1, r.size // MEDIAN_SAMPLE)
+    g = g[::stride].astype(np.float64)
+    r = r[::stride].astype(np.float64)
+    nz = r != 0
+    if mask is not None:
+        nz &= np.asarray(mask).reshape(-1)[::stride]
+    if not nz.any():
+        return 0.0
+    return float(np.median(np.abs(g[nz] - r[nz]) / np.abs(r[nz])))
+
+
+def check_close(name: str, gpu: np.ndarray, ref: np.ndarray, tolerance: float, per: str = "row",
+                scale: Optional[np.ndarray] = None, mask: Optional[np.ndarray] = None) -> float:
+    """Per-row (token, sorted row or expert: axis 0) normwise error <= tolerance
+    for every row; per = "tensor" takes the whole tensor as one row; scale
+    replaces each row's own largest oracle element as its denominator."""
+    gpu = np.asarray(gpu)
+    ref = np.asarray(ref)
+    if per == "tensor":
+        errs = np.array([normwise(gpu, ref)])
+    else:
+        errs = rowwise(gpu, ref, scale=scale)
+        if scale is not None:
+            per = "scale"
+    err = float(errs.max()) if errs.size else 0.0
+    med = median_rel(gpu, ref, mask)
+    worst = int(errs.argmax()) if errs.size else -1
+    line = (f"{name:12s} per {per:6s} max {err:.3e} (row {worst}) median elementwise {med:.3e} "
+            f"rows {errs.size} tol {tolerance:.1e}")
+    say("  " + line)
+    _log(line)
+    assert err <= tolerance, (name, err, worst, tolerance)
     return err
 
 
-def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:
-    rng = np.random.default_rng(seed)
-    picks = set(rng.choice(T, size=min(n - 2, T), replace=False).tolist()) | {0, T - 1}
-    return np.array(sorted(picks), dtype=np.int64)
+def check_output(name: str, gpu: np.ndarray, ref: Dict[str, np.ndarray], tolerance: float) -> float:
+    """check_close of one stage output against ref[name], with d_logits
+    measured against the scale of its terms (ref's topk_w and d_topk_w)."""
+    scale, mask = None, None
+    if name == "d_logits":
+        scale = d_logits_scale(ref["topk_w"], ref["d_topk_w"])
+        mask = topk_mask(ref["topk_idx"], ref["d_logits"].shape[1])
+    elif name == "d_topk_w":
+        scale = g_scale(ref["d_topk_w"])
+    return check_close(name, gpu, ref[name], tolerance, scale=scale, mask=mask)
 
-
-def check_sampled(d: DevInputs, st, experts: Sequence[int], n_tokens: int = 48, backward: bool = True) -> None:
-    """Full-size workload: token rows and whole experts checked against the oracle one by one."""
-    inp, c = d.inp, d.cfg
-    b = st.buf
-    tolerance = tol(c)
-    rows = sample_tokens(c.T, n_tokens)
-    say(f"  oracle on {len(rows)} sampled tokens")
-    ref = oracle_full(inp, backward, rows=rows)
-    check_close("y", to_np(b["y"][torch.from_numpy(rows).cuda()]), ref["y"], tolerance)
-    check_close("topk_w", to_np(b["topk_w"][torch.from_numpy(rows).cuda()]), ref["topk_w"], 1e-5)
-    if backward:
-        idx = torch.from_numpy(rows).cuda()
-        check_close("dx", to_np(b["dx"][idx]), ref["dx"], tolerance)
-        check_close("d_topk_w", to_np(b["d_topk_w"][idx]), ref["d_topk_w"], tolerance)
-        check_close("d_logits", to_np(b["d_logits"][idx]), ref["d_logits"], tolerance)
-        # Whole experts: the tokens routed to them, in order, give the same rows.
-        topk = to_np(b["topk_idx"])
-        for e in experts:
-            toks = np.nonzero((topk == e).any(axis=1))[0]
-            mask = np.zeros(c.E, np.uint8)
-            mask[e] = 1
-            say(f"  oracle on expert {e} ({len(toks)} tokens)")
-            if len(toks) == 0:
-                for n in ["dw_gate", "dw_up", "dw_down"]:
-                    assert not b[n][e].any().item(), (n, e)
-                continue
-            r = oracle_full(inp, True, rows=toks, expert_mask=mask)
-            for n in ["dw_gate", "dw_up", "dw_down"]:
-                check_close(f"{n}[{e}]", to_np(b[n][e]), r[n][e], tolerance)

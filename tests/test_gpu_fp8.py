@@ -10,8 +10,16 @@ through the C ABI.
   applies both power-of-two scales) with fp32 sums: a is within the bf16
   tolerance of the oracle, which runs the same definition in float64. a's
   E4M3 codes and scales equal the oracle's except on rare elements and rows
-  where a sits on a rounding boundary; o_perm and y, downstream of those,
-  are within one E4M3 rounding step (2^-4) normwise.
+  where a sits on a rounding boundary (both must be rare). Per row: where
+  a's codes and scale equal the oracle's the result is unique, and those
+  rows of o_perm (and the tokens of y whose k rows all match) are held to
+  2e-2 like every other output; where they differ, two quantisations of
+  nearly equal values are both valid and one product of the row can move by
+  one E4M3 step (an eighth of it), so those rows are held to 2^-4. Over the
+  whole tensor o_perm and y are held to 2e-2 when I >= 512: a flip on the
+  row's largest product moves an output by about 3 / (8 sqrt(I)) of the
+  tensor's largest one (1.4e-2 at I = 512; 3e-2 at I = 128, where only the
+  per-row bounds apply).
 """
 import numpy as np
 import pytest
@@ -26,10 +34,11 @@ from test_gpu_parity import SMALL
 pytestmark = pytest.mark.gpu
 
 FP8_SMALL = [c for c in SMALL if c.dtype == "bf16" and c.H % 64 == 0 and c.I % 64 == 0]
-# One E4M3 rounding step (3 mantissa bits): the normwise bound for outputs
-# downstream of the quantisation of a, whose codes can flip where a itself
-# differs from the oracle's by a bf16 rounding step.
-FP8_TOL = 2.0 ** -4
+# Outputs downstream of the quantisation of a: the bound of every other
+# output over the tensor and on rows whose codes and scale equal the
+# oracle's; one E4M3 step on the others.
+FP8_TOL = 2e-2
+FP8_ROW_TOL = 2.0 ** -4
 
 
 def bf16_dev(a: np.ndarray) -> torch.Tensor:
@@ -47,7 +56,8 @@ def test_quantize_rows_bit_exact():
     z = np.zeros(K)
     z[5] = -3.0e-3
     rows.append(z)
-    rows.append(np.r_[rng.uniform(-1, 1, K - 1), 7.99])  # largest element just under 8: scaled to 511.4 -> 448
+    rows.append(np.r_[rng.uniform(-1, 1, K - 1), 7.99])  # largest element just under 8: scale 2^-5, 255.7
+    rows.append(np.r_[rng.uniform(-1, 1, K - 1), 7.0])  # 448 * 2^-6 exactly: scale 2^-6, no clipping
     rows.append(np.r_[rng.uniform(-1e-6, 1e-6, K - 1), 1.0])  # most elements subnormal or zero in E4M3
     neg0 = np.zeros(K)
     neg0[::2] = -0.0
@@ -125,19 +135,35 @@ def check_fp8(inp, w, out, check_weights=True):
     # can differ; both must be rare.
     aq, ae = out["aq"].cpu().numpy(), out["a_e8"].cpu().numpy()
     same_scale = ae == ref["ae"]
-    U.say(f"  a scales differ on {np.mean(~same_scale):.4f} of rows, "
-          f"codes on {np.mean(aq[same_scale] != ref['aq'][same_scale]):.5f} of the rest")
+    line = (f"a scales differ on {np.mean(~same_scale):.4f} of rows, "
+            f"codes on {np.mean(aq[same_scale] != ref['aq'][same_scale]):.5f} of the rest")
+    U.say("  " + line)
+    U._log(line)
     assert np.mean(~same_scale) <= 0.02
     assert np.mean(aq[same_scale] != ref["aq"][same_scale]) <= 0.01
     # Downstream of those flips the comparison is at E4M3's own precision.
-    U.check_close("o_perm", U.to_np(out["o_perm"]), ref["o_perm"], FP8_TOL)
-    y = F8.combine_sum(ref["o_perm"], ref_r["flat_to_sorted"], c.T, c.k)
-    U.check_close("y", U.to_np(out["y"]), y, FP8_TOL)
+    same_row = same_scale & np.all(aq == ref["aq"], axis=1)
+    f2s = ref_r["flat_to_sorted"].reshape(c.T, c.k)
+    same_tok = np.all(same_row[f2s], axis=1)
+    line = (f"rows whose codes and scale all match: o_perm {same_row.sum()} of {same_row.size}, "
+            f"y {same_tok.sum()} of {same_tok.size}")
+    U.say("  " + line)
+    U._log(line)
+    o, y = U.to_np(out["o_perm"]), U.to_np(out["y"])
+    y_ref = F8.combine_sum(ref["o_perm"], ref_r["flat_to_sorted"], c.T, c.k)
+    for n, got, want, same in (("o_perm", o, ref["o_perm"], same_row), ("y", y, y_ref, same_tok)):
+        if c.I >= 512:
+            U.check_close(n, got, want, FP8_TOL, per="tensor")
+        if same.any():
+            U.check_close(n + " same", got[same], want[same], FP8_TOL)
+        if (~same).any():
+            U.check_close(n + " other", got[~same], want[~same], FP8_ROW_TOL)
 
 
 @pytest.mark.parametrize("cfg", FP8_SMALL, ids=lambda c: c.name)
 def test_fp8_forward_small(cfg):
     U.say(f"[fp8 forward] {cfg}")
+    U.begin(f"fp8.{cfg.name}", f"{cfg} seed 5, fp8 forward")
     inp = synth.make_inputs(cfg, seed=5, with_dy=False)
     d = U.DevInputs(inp)
     w, out = fp8_forward(d)
@@ -148,6 +174,7 @@ def test_fp8_forward_qwen3_30b_a3b_full():
     """T=4096, H=2048, E=128, k=8, I=768: every output element of the fp8 forward."""
     cfg = synth.CONFIGS["qwen3_30b_a3b_fwd"]
     U.say(f"[fp8 forward] {cfg}")
+    U.begin(f"fp8.{cfg.name}", f"{cfg} seed 0, fp8 forward")
     inp = synth.make_inputs(cfg, seed=0)
     d = U.DevInputs(inp)
     w, out = fp8_forward(d)

@@ -63,6 +63,7 @@ def check_fused_indices(out, k: int) -> None:
 def test_fused_forward_small(cfg):
     from mixture_experts_expert_amd import binding as B
     U.say(f"[fused] {cfg}")
+    U.begin("fused_forward." + cfg.name, f"{cfg}, fused inference forward")
     inp = synth.make_inputs(cfg, seed=1, with_dy=False)
     d = U.DevInputs(inp)
     s, out = fused_forward(d)
@@ -100,6 +101,7 @@ def test_fused_forward_qwen3_30b_a3b_full():
     """T=4096, H=2048, E=128, k=8, I=768, the fused inference forward: every output element."""
     cfg = synth.CONFIGS["qwen3_30b_a3b_fwd"]
     U.say(f"[fused] {cfg}")
+    U.begin("fused_forward." + cfg.name, f"{cfg} seed 0, fused inference forward")
     inp = synth.make_inputs(cfg, seed=0)
     d = U.DevInputs(inp)
     s, out = fused_forward(d)
@@ -137,6 +139,7 @@ def test_gather_fused_training_small(cfg):
     path (overwrite and accumulate, one and two streams), and within the
     tolerance of the oracle."""
     U.say(f"[gather-fused training] {cfg}")
+    U.begin("gather_fused." + cfg.name, f"{cfg} seed 2, training without x_perm")
     inp = synth.make_inputs(cfg, seed=2, with_dy=True)
     d = U.DevInputs(inp)
     plain = U.run_stage(d, True)
@@ -148,7 +151,7 @@ def test_gather_fused_training_small(cfg):
     ref = U.oracle_full(inp, True)
     tolerance = U.tol(cfg)
     for n in ["y", "dx", "dw_gate", "dw_up", "dw_down", "d_logits"]:
-        U.check_close(n, U.to_np(st.buf[n]), ref[n], tolerance)
+        U.check_output(n, U.to_np(st.buf[n]), ref, tolerance)
     # accumulate_dw on both, then the two-stream backward (overwrite).
     U.run_stage(d, True, accumulate=True, stage=plain)
     U.run_stage(d, True, accumulate=True, stage=st)
@@ -163,12 +166,15 @@ def test_gather_fused_training_small(cfg):
         assert same_tensor(st.buf[n], plain.buf[n]), (n, "two streams")
 
 
+@pytest.mark.timeout(600)
 def test_gather_fused_training_qwen3_30b_a3b_full():
     """T=8192, H=2048, E=128, k=8, I=768: the training step without x_perm
-    equals the x_perm path bit for bit on every output (the x_perm path is
-    checked against the oracle at this size on sampled rows and experts)."""
+    equals the x_perm path bit for bit on every output, and every element of
+    y, dx, the weight gradients and d_logits is within tolerance of the
+    oracle."""
     cfg = synth.CONFIGS["qwen3_30b_a3b_train"]
     U.say(f"[gather-fused training] {cfg}")
+    U.begin("gather_fused." + cfg.name, f"{cfg} seed 0, training without x_perm")
     inp = synth.make_inputs(cfg, seed=0)
     d = U.DevInputs(inp)
     plain = U.run_stage(d, True)
@@ -176,3 +182,7 @@ def test_gather_fused_training_qwen3_30b_a3b_full():
     check_fused_indices(st.buf, cfg.k)
     for n in STAGE_OUT:
         assert same_tensor(st.buf[n], plain.buf[n]), n
+    U.say("  oracle on all tokens")
+    ref = U.oracle_full(inp, True)
+    for n in ["y", "dx", "dw_gate", "dw_up", "dw_down", "d_logits"]:
+        U.check_output(n, U.to_np(st.buf[n]), ref, U.BF16_TOL)

@@ -8,10 +8,9 @@ the C ABI.
   gradients, moe_lora_grads): routing bit-exact; y, dx, d_topk_w, d_logits
   and the six adapter gradients within the bf16 tolerance of the float64
   oracle. Small shapes cover a padded rank (16 -> 64) and an unpadded one,
-  experts with no rows (zero gradients), many experts and a split-K
-  reduction; the full 30B-A3B training shape is checked on sampled tokens
-  (y, dx and the routing gradients are per token) and on whole sampled
-  experts (an expert's adapter gradients depend on its own rows only).
+  experts with no rows (zero gradients), many experts, a split-K reduction
+  and the ranks 72 and 96; the full 30B-A3B training shape is checked on
+  every element (per token, per expert).
 """
 import numpy as np
 import pytest
@@ -34,7 +33,7 @@ def widen(bits: np.ndarray) -> np.ndarray:
 
 
 @pytest.mark.parametrize("E,N,K,r", [(3, 200, 264, 8), (2, 128, 128, 16), (4, 257, 520, 40), (2, 70, 2048, 128),
-                                     (1, 1, 8, 64)])
+                                     (1, 1, 8, 64), (3, 300, 200, 96), (2, 129, 136, 72)])
 @pytest.mark.parametrize("in_place", [False, True], ids=["out", "in_place"])
 def test_merge(E, N, K, r, in_place):
     from mixture_experts_expert_amd import binding as B
@@ -87,9 +86,12 @@ def check_tokens(st, ref_r, ref, rows=None):
     idx = ref_r["topk_idx"] if rows is None else ref_r["topk_idx"][rows]
     U.check_close("y", U.to_np(sel(b["y"])), ref["y"], U.BF16_TOL)
     U.check_close("dx", U.to_np(sel(b["dx"])), ref["dx"], U.BF16_TOL)
-    U.check_close("d_topk_w", U.to_np(sel(b["d_topk_w"])), ref["d_topk_w"], U.BF16_TOL)
+    U.check_close("d_topk_w", U.to_np(sel(b["d_topk_w"])), ref["d_topk_w"], U.BF16_TOL,
+                  scale=U.g_scale(ref["d_topk_w"]))
     d_logits = O.route_bwd(logits, idx, ref["d_topk_w"].astype(np.float32))
-    U.check_close("d_logits", U.to_np(sel(b["d_logits"])), d_logits, U.BF16_TOL)
+    w = ref_r["topk_w"] if rows is None else ref_r["topk_w"][rows]
+    U.check_close("d_logits", U.to_np(sel(b["d_logits"])), d_logits, U.BF16_TOL,
+                  scale=U.d_logits_scale(w, ref["d_topk_w"]), mask=U.topk_mask(idx, d_logits.shape[1]))
 
 
 SMALL_LORA = [
@@ -99,12 +101,19 @@ SMALL_LORA = [
     (synth.MoEConfig("bf16_one_token", T=1, H=64, E=16, k=8, I=64, dtype="bf16", backward=True), 8),
     (synth.MoEConfig("bf16_skew", T=900, H=256, E=32, k=4, I=128, dtype="bf16", backward=True, zipf_s=2.5), 128),
     (SPLIT_K, 64),
+    # Ranks that are not a multiple of the 32-wide blocks of the adapter
+    # kernels: the odd block count of the outer products (r = 72 -> 3 blocks
+    # of 32 on the rank side, an unpadded LDS row) and the padded rank
+    # (r < 128 = the padded width) whose padding must be skipped.
+    (synth.MoEConfig("bf16_many_experts", T=333, H=256, E=40, k=5, I=128, dtype="bf16", backward=True), 72),
+    (synth.MoEConfig("bf16_tiles", T=700, H=512, E=6, k=2, I=320, dtype="bf16", backward=True), 96),
 ]
 
 
 @pytest.mark.parametrize("cfg,r", SMALL_LORA, ids=[f"{c.name}-r{r}" for c, r in SMALL_LORA])
 def test_lora_stage_small(cfg, r):
     U.say(f"[lora stage] {cfg} r={r}")
+    U.begin(f"lora_r{r}.{cfg.name}", f"{cfg} seed 8, adapters rank {r}")
     s = 2.0 if r == 64 else 0.75
     inp = synth.make_inputs(cfg, seed=8, with_dy=True)
     adapters = synth.make_adapters(cfg, r, seed=8)
@@ -121,27 +130,28 @@ def test_lora_stage_small(cfg, r):
         assert not np.any(got[counts == 0]), ("experts without rows", n)
 
 
+@pytest.mark.timeout(900)
 def test_lora_stage_qwen3_30b_a3b_full():
-    """T=8192, H=2048, E=128, k=8, I=768, r=64, s=2: sampled tokens and experts."""
+    """T=8192, H=2048, E=128, k=8, I=768, r=64, s=2: every element of y, dx,
+    d_topk_w, d_logits and of all six adapter gradients."""
     cfg = synth.CONFIGS["qwen3_30b_a3b_train"]
     r, s = 64, 2.0
     U.say(f"[lora stage] {cfg} r={r}")
+    U.begin("lora_r64." + cfg.name, f"{cfg} seed 0, adapters rank {r}, scale {s}")
     inp = synth.make_inputs(cfg, seed=0)
     adapters = synth.make_adapters(cfg, r, seed=0)
     d = U.DevInputs(inp)
     st = lora_run(d, r, s, adapters)
     ref_r = U.oracle_route(inp)
     U.check_routing(st, ref_r)
-    rows = U.sample_tokens(cfg.T, 48)
-    U.say(f"  oracle on {len(rows)} sampled tokens")
-    check_tokens(st, ref_r, oracle_lora(inp, adapters, s, ref_r["topk_idx"], ref_r["topk_w"], rows=rows), rows)
+    U.say("  adapter oracle on all tokens")
+    ref = oracle_lora(inp, adapters, s, ref_r["topk_idx"], ref_r["topk_w"])
+    check_tokens(st, ref_r, ref)
     counts = ref_r["counts"]
-    experts = sorted({0, int(np.argmax(counts)), int(np.argmin(counts)), cfg.E - 1})
-    idx = np.where(np.isin(ref_r["topk_idx"], experts), ref_r["topk_idx"], -1).astype(np.int32)
-    U.say(f"  oracle on experts {experts} ({[int(counts[e]) for e in experts]} rows)")
-    ref = oracle_lora(inp, adapters, s, idx, ref_r["topk_w"])
     for n in NAMES:
-        U.check_close("d" + n, U.to_np(st.buf["d" + n][experts]), ref["d" + n][experts], U.BF16_TOL)
+        got = U.to_np(st.buf["d" + n])
+        U.check_close("d" + n, got, ref["d" + n], U.BF16_TOL)
+        assert not np.any(got[counts == 0]), ("experts without rows", n)
 
 
 def test_lora_merges_on_a_second_stream_same_bits():
