@@ -289,6 +289,22 @@ moe_status moe_forward_fused(moe_shape s, const void* x, const void* w_router, c
                              int32_t* sorted_to_flat, int32_t* flat_to_sorted, int32_t* row_token, float* row_weight,
                              void* a, void* o_perm, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_forward_fused for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * calls and results, bit for bit, with no workspace argument. The sort's
+ * per-block histograms (ceil(T*k / 1024) * E int32) live instead in a static
+ * device array of the library, 4 MiB per device, held by each device the
+ * library runs on until the process ends; a larger shape returns
+ * MOE_EWORKSPACE with nothing enqueued. The function allocates nothing. Every
+ * call on a device shares that device's array, so calls that overlap in time
+ * on one device (concurrent streams, other host threads) race and must be
+ * ordered by the caller. */
+moe_status moe_forward_fused_noalloc(moe_shape s, const void* x, const void* w_router, const float* logit_bias,
+                                     const void* w_gate, const void* w_up, const void* w_down, float* logits,
+                                     int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                                     int32_t* sorted_to_flat, int32_t* flat_to_sorted, int32_t* row_token,
+                                     float* row_weight, void* a, void* o_perm, void* y, hipStream_t stream);
+
 /* ---- fp8 inference forward (the quantised expert weights of the sourcepulse
  * summary: bitsandbytes 4-bit compatibility, "Quick Start & Requirements";
  * QLoRA and training over quantised GGUF models, "Highlighted Details"; the

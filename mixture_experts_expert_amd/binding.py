@@ -72,6 +72,7 @@ _SIGS = {
     "moe_gemm_gate_up_wgrad_gathered": ([moe_shape, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_size_t, _P],
                                         ctypes.c_int),
     "moe_forward_fused": ([moe_shape] + [_P] * 19 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_forward_fused_noalloc": ([moe_shape] + [_P] * 18 + [_P], ctypes.c_int),
     "moe_lora_workspace_bytes": ([moe_shape, ctypes.c_int32], ctypes.c_size_t),
     "moe_lora_merge": ([ctypes.c_int32] * 4 + [ctypes.c_float] + [_P] * 5, ctypes.c_int),
     "moe_lora_grads": ([moe_shape, ctypes.c_int32, ctypes.c_float] + [_P] * 18 + [ctypes.c_size_t, _P],
@@ -296,6 +297,15 @@ def moe_forward_fused(s, x, w_router, logit_bias, w_gate, w_up, w_down, logits, 
         s, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(logits),
         _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(sorted_to_flat), _ptr(flat_to_sorted),
         _ptr(row_token), _ptr(row_weight), _ptr(a), _ptr(o_perm), _ptr(y), _ptr(ws), nb, _stream(stream)))
+
+
+def moe_forward_fused_noalloc(s, x, w_router, logit_bias, w_gate, w_up, w_down, logits, topk_idx, topk_w, counts,
+                              offsets, sorted_to_flat, flat_to_sorted, row_token, row_weight, a, o_perm, y,
+                              stream=None):
+    _check("moe_forward_fused_noalloc", lib.moe_forward_fused_noalloc(
+        s, _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(logits),
+        _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(sorted_to_flat), _ptr(flat_to_sorted),
+        _ptr(row_token), _ptr(row_weight), _ptr(a), _ptr(o_perm), _ptr(y), _stream(stream)))
 
 
 def moe_lora_workspace_bytes(s: moe_shape, r: int) -> int:

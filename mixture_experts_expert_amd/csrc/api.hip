@@ -278,6 +278,28 @@ moe_status moe_forward_fused(moe_shape s, const void* x, const void* w_router, c
   return moe_unpermute_sum(s, o_perm, flat_to_sorted, y, stream);
 }
 
+moe_status moe_forward_fused_noalloc(moe_shape s, const void* x, const void* w_router, const float* logit_bias,
+                                     const void* w_gate, const void* w_up, const void* w_down, float* logits,
+                                     int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                                     int32_t* sorted_to_flat, int32_t* flat_to_sorted, int32_t* row_token,
+                                     float* row_weight, void* a, void* o_perm, void* y, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(x, w_router, w_gate, w_up, w_down, logits, topk_idx, topk_w, counts, offsets, sorted_to_flat,
+               flat_to_sorted, row_token, row_weight, a, o_perm, y))
+    return MOE_EINVAL;
+  if (!gathered_x_fits(s)) return MOE_EUNSUPPORTED;
+  if (moe::sort_hist_bytes(s) > moe::kScratchBytes) return MOE_EWORKSPACE;
+  if ((st = moe_route(s, x, w_router, logit_bias, logits, topk_idx, topk_w, stream)) != MOE_OK) return st;
+  if ((st = from_hip(moe::launch_permute_fused_noalloc(s, topk_idx, topk_w, counts, offsets, sorted_to_flat,
+                                                       flat_to_sorted, row_token, row_weight, stream))) != MOE_OK)
+    return st;
+  if ((st = moe_gemm_gate_up_gathered(s, x, row_token, offsets, w_gate, w_up, nullptr, nullptr, a, stream)) != MOE_OK)
+    return st;
+  if ((st = moe_gemm_down_weighted(s, a, offsets, w_down, row_weight, o_perm, stream)) != MOE_OK) return st;
+  return moe_unpermute_sum(s, o_perm, flat_to_sorted, y, stream);
+}
+
 moe_status moe_quantize_fp8_rows(int32_t rows, int32_t K, const void* in, uint8_t* q, uint8_t* e8,
                                  const int32_t* flat_to_sorted, int32_t k, hipStream_t stream) {
   if (rows < 0 || K <= 0 || K % 8 != 0) return MOE_EINVAL;

@@ -96,6 +96,14 @@ hipError_t launch_combine_bwd(const moe_shape& s, const void* dy, const void* o_
 hipError_t launch_permute_fused(const moe_shape& s, const int32_t* idx, const float* w, int32_t* counts,
                                 int32_t* offsets, int32_t* s2f, int32_t* f2s, int32_t* row_token, float* row_weight,
                                 void* ws, hipStream_t st);
+// The allocation-free sort: the per-block histograms in the library's static
+// scratch (kScratchBytes per device) instead of a workspace; the caller checks
+// sort_hist_bytes(s) <= kScratchBytes first.
+constexpr size_t kScratchBytes = 4u << 20;
+size_t sort_hist_bytes(const moe_shape& s);
+hipError_t launch_permute_fused_noalloc(const moe_shape& s, const int32_t* idx, const float* w, int32_t* counts,
+                                        int32_t* offsets, int32_t* s2f, int32_t* f2s, int32_t* row_token,
+                                        float* row_weight, hipStream_t st);
 hipError_t launch_unpermute_sum(const moe_shape& s, const void* dx_perm, const int32_t* f2s, void* dx,
                                 hipStream_t st);
 

@@ -13,7 +13,15 @@
 //      chunks are ordered through per-expert counters in LDS.
 // The position of pair f is offsets[e] + (pairs of expert e in earlier
 // blocks) + (rank inside its block): the definition of the stable order.
+#include <mutex>
+
 #include "moe_internal.h"
+
+// Device memory of the allocation-free sort (moe_forward_fused_noalloc): the
+// per-block histograms live in this array instead of a caller's workspace.
+// Each device holds its own copy for the life of the process; host code
+// reaches it only through the per-device address from hipGetSymbolAddress.
+static __device__ __align__(256) int32_t scratch[moe::kScratchBytes / sizeof(int32_t)];
 
 namespace moe {
 namespace {
@@ -226,6 +234,38 @@ hipError_t launch_permute_fused(const moe_shape& s, const int32_t* idx, const fl
                                 int32_t* offsets, int32_t* s2f, int32_t* f2s, int32_t* row_token, float* row_weight,
                                 void* ws, hipStream_t st) {
   return launch_sort(s, idx, counts, offsets, s2f, f2s, w, row_token, row_weight, ws_hist(s, ws), st);
+}
+
+size_t sort_hist_bytes(const moe_shape& s) { return ws_layout(s).hist_bytes; }
+
+// The scratch array's address on the current device, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept.
+hipError_t scratch_address(int32_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    addr[dev] = p;
+  }
+  *out = static_cast<int32_t*>(addr[dev]);
+  return hipSuccess;
+}
+
+hipError_t launch_permute_fused_noalloc(const moe_shape& s, const int32_t* idx, const float* w, int32_t* counts,
+                                        int32_t* offsets, int32_t* s2f, int32_t* f2s, int32_t* row_token,
+                                        float* row_weight, hipStream_t st) {
+  int32_t* hist = nullptr;
+  const hipError_t err = scratch_address(&hist);
+  if (err != hipSuccess) return err;
+  return launch_sort(s, idx, counts, offsets, s2f, f2s, w, row_token, row_weight, hist, st);
 }
 
 }  // namespace moe

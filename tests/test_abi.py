@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(B):
     names = declared_functions()
-    assert len(names) == 30, names
+    assert len(names) == 31, names
     for n in names:
         assert hasattr(B.lib, n), n
 
@@ -168,3 +168,18 @@ def test_binding_raises_on_error(B):
         B.lib  # noqa: B018
         B._check("moe_route", _route(B, s))
     assert ei.value.status == 1
+
+
+def test_noalloc_forward_rejects_on_the_host(B):
+    """moe_forward_fused_noalloc: a shape whose sort histograms exceed the
+    static 4 MiB scratch (ceil(T*k / 1024) * E int32) is MOE_EWORKSPACE, a
+    null pointer MOE_EINVAL, both before any HIP call."""
+    fn = B.lib.moe_forward_fused_noalloc
+    big = B.shape(131073, 64, 1024, 8, 64, "bf16")  # 1025 blocks x 1024 experts x 4 bytes > 4 MiB
+    assert fn(big, *([FAKE] * 18), None) == 3
+    ok = B.shape(1024, 64, 1024, 8, 64, "bf16")
+    args = [FAKE] * 18
+    args[2] = None  # logit_bias may be NULL: not the rejected argument
+    args[0] = None  # x
+    assert fn(ok, *args, None) == 1
+
