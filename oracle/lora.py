@@ -34,6 +34,21 @@ def merge(w: np.ndarray, a: np.ndarray, b: np.ndarray, s: float) -> np.ndarray:
     return np.asarray(w, np.float64) + s * np.matmul(np.asarray(b, np.float64), np.asarray(a, np.float64))
 
 
+def dequantize_weights(wq: np.ndarray, e8: np.ndarray) -> np.ndarray:
+    """Frozen expert weights kept in 8 bits (the QLoRA-style base of the
+    sourcepulse summary, "Highlighted Details" and "Quick Start &
+    Requirements"; taken to E4M3 here): codes wq [E, N, K] with one E8M0
+    scale per row e8 [E, N] -> float64 values decode(code) * 2^(e8 - 127)."""
+    from oracle import fp8 as F8
+    E, N, K = wq.shape
+    return F8.dequantize_rows(np.asarray(wq).reshape(E * N, K), np.asarray(e8).reshape(E * N)).reshape(E, N, K)
+
+
+def merge_fp8(wq: np.ndarray, e8: np.ndarray, a: np.ndarray, b: np.ndarray, s: float) -> np.ndarray:
+    """W' = deq(Wq) + s B A: the adapters over the dequantised frozen weights."""
+    return merge(dequantize_weights(wq, e8), a, b, s)
+
+
 def forward_backward(x, dy, topk_idx, topk_w, w_gate, w_up, w_down, ad: Dict[str, np.ndarray], s: float):
     """The stage with adapters, forward and backward, in float64.
 

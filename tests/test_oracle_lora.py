@@ -5,7 +5,11 @@
 * B = 0: the stage equals the plain one and every dA is exactly zero;
 * every adapter gradient against central finite differences of
   L = <dY, Y> in float64 along random directions (the routing does not depend
-  on the adapters, so no draw changes the selection).
+  on the adapters, so no draw changes the selection);
+* 8-bit frozen weights: weights that E4M3 holds exactly (codes times a power
+  of two) give the plain merge bit for bit, and any weights come back within
+  E4M3's half step (2^-4 relative in its normal range) plus the subnormal
+  step below it, checked element by element against the decoded codes.
 """
 import numpy as np
 import pytest
@@ -82,3 +86,30 @@ def test_adapter_gradients_finite_differences(name):
         fd = (loss(up) - loss(dn)) / (2 * h)
         an = float(np.sum(out["d" + name] * v))
         assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_fp8_base_merge_lossless_and_bounded():
+    from oracle import fp8 as F8
+    rng = np.random.default_rng(11)
+    E, N, K, r = 3, 5, 16, 4
+    a, b = rng.standard_normal((E, r, K)) * 0.1, rng.standard_normal((E, N, r)) * 0.1
+    # codes times 2^-12 with every row's largest element at 448 * 2^-12:
+    # quantised without loss, so the fp8 merge is the plain merge
+    codes = rng.integers(0, 0x7E, size=(E, N, K)).astype(np.uint8) | (rng.integers(0, 2, (E, N, K)) << 7).astype(np.uint8)
+    w = F8.e4m3_decode(codes) * 2.0 ** -12
+    w[:, :, 0] = 448.0 * 2.0 ** -12
+    wq, e8 = F8.quantize_weights(w)
+    assert np.array_equal(LO.merge_fp8(wq, e8, a, b, 0.5), LO.merge(w, a, b, 0.5))
+    # generic weights: each dequantised element within half an E4M3 step
+    w = rng.standard_normal((E, N, K)) * 0.02
+    wq, e8 = F8.quantize_weights(w)
+    deq = LO.dequantize_weights(wq, e8)
+    for e in range(E):
+        for n in range(N):
+            X = int(e8[e, n]) - 127
+            for c in range(K):
+                err = abs(deq[e, n, c] - w[e, n, c])
+                bound = 2.0 ** -4 * abs(w[e, n, c]) if abs(w[e, n, c]) >= 2.0 ** (X - 6) else 2.0 ** (X - 10)
+                assert err <= bound, (e, n, c)
+    assert np.allclose(LO.merge_fp8(wq, e8, a, b, 0.5) - deq, 0.5 * np.matmul(b, a), rtol=0, atol=1e-15)
+
