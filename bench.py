@@ -243,6 +243,16 @@ def lora_timing(cfg, seed: int, tensors, bias, stream, r: int = 64, scale: float
     # The merges on a second stream, concurrent with the routing and the sort.
     out["step_merges_on_second_stream"] = round(time_calls(lora_step_two_streams, stream), 4)
     out["moe_lora_merge_x3"] = round(time_calls(lambda: ls.merge(wg, wu, wd, ad), stream, reps=5), 4)
+    # The same step over E4M3 frozen experts (QLoRA-style; quantised once,
+    # outside the timing): the merges dequantise.
+    w8 = B.FP8Weights(wg, wu, wd)
+
+    def lora_step_fp8():
+        ls.forward(x, wr, w8.gate, w8.up, w8.down, ad, bias)
+        ls.backward(dy)
+
+    out["step_fp8_base"] = round(time_calls(lora_step_fp8, stream), 4)
+    out["moe_lora_merge_fp8_x3"] = round(time_calls(lambda: ls.merge(w8.gate, w8.up, w8.down, ad), stream, reps=5), 4)
     out["moe_lora_grads"] = round(time_calls(lambda: B.moe_lora_grads(
         ls.s, r, scale, lb["x_perm"], lb["a"], lb["dgu"], lb["do_perm"], lb["offsets"],
         *(ad[n] for n in B.LORA_NAMES), *(lb["d" + n] for n in B.LORA_NAMES), ls.lora_ws), stream, reps=5), 4)
@@ -469,6 +479,32 @@ def main() -> int:
             gather_fused_ms[n] = round(time_fn(gf_calls[n], reps=5), 4)
         log(f"step without x_perm: {gather_fused_ms}")
 
+    # The same step without do_perm: the gate/up GEMM also writes the weighted
+    # activations, the combine backward writes d_topk_w only, and the down
+    # backward reads dy through the sorted rows' tokens.
+    a_w = torch.empty(cfg.M, cfg.I, dtype=torch.bfloat16, device="cuda")
+    dy_calls = dict(by_name)
+    dy_calls["moe_permute"] = lambda: B.moe_permute_rows(
+        s, b["topk_idx"], b["topk_w"], x, b["counts"], b["offsets"], b["sorted_to_flat"], b["flat_to_sorted"],
+        rt["row_token"], rt["row_weight"], b["x_perm"], st.ws)
+    dy_calls["moe_gemm_gate_up"] = lambda: B.moe_gemm_gate_up_aw(
+        s, b["x_perm"], None, rt["row_weight"], b["offsets"], wg, wu, b["g"], b["u"], b["a"], a_w)
+    dy_calls["moe_combine_bwd"] = lambda: B.moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"],
+                                                            None, b["d_topk_w"])
+    dy_calls["moe_gemm_down_bwd"] = lambda: B.moe_gemm_down_bwd_dy(
+        s, dy, rt["row_token"], rt["row_weight"], a_w, b["offsets"], wd, b["g"], b["u"], dgu, b["dw_down"], 0, st.ws)
+
+    def step_dy_fused():
+        for n in names:
+            dy_calls[n]()
+
+    dy_fused_ms = None
+    if not args.timed_only:
+        dy_fused_ms = {"step": round(time_fn(step_dy_fused), 4)}
+        for n in ["moe_permute", "moe_gemm_gate_up", "moe_combine_bwd", "moe_gemm_down_bwd"]:
+            dy_fused_ms[n] = round(time_fn(dy_calls[n], reps=5), 4)
+        log(f"step without do_perm: {dy_fused_ms}")
+
     # The same step with one launch per GEMM (the six single-GEMM entry
     # points), and each backward GEMM on its own.
     single_ms = None
@@ -579,6 +615,7 @@ def main() -> int:
         "two_stream_ms_per_step": two_stream_ms,
         "graph_ms_per_step": graph_ms,
         "gather_fused_ms": gather_fused_ms,
+        "dy_fused_ms": dy_fused_ms,
         "single_launch_ms": single_ms,
         "inference_forward_ms": infer,
         "lora_ms": lora,

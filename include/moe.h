@@ -11,6 +11,10 @@
  *   fp8 inference: moe_forward_fused_fp8 = moe_route -> moe_permute_fused ->
  *             moe_quantize_fp8_rows (x) -> moe_gemm_gate_up_fp8 ->
  *             moe_quantize_fp8_rows (a) -> moe_gemm_down_fp8 -> moe_unpermute_sum
+ *   training without do_perm: moe_route -> moe_permute_rows ->
+ *             moe_gemm_gate_up_aw -> moe_gemm_down -> moe_combine;
+ *             moe_combine_bwd (do_perm NULL) -> moe_gemm_down_bwd_dy ->
+ *             moe_gemm_gate_up_bwd -> moe_unpermute_sum -> moe_route_bwd
  *   training without x_perm (the gather fused into both GEMMs that read x):
  *             moe_route -> moe_permute_fused -> moe_gemm_gate_up_gathered ->
  *             moe_gemm_down -> moe_combine; moe_combine_bwd -> moe_gemm_down_dgrad,
@@ -175,7 +179,8 @@ moe_status moe_combine(moe_shape s, const void* o_perm, const float* topk_w, con
 /* Backward of moe_combine (chain rule of the combine above).
  *   do_perm[p,:] = topk_w[t,j] * dy[t,:], d_topk_w[t,j] = <dy[t,:], o_perm[p,:]>
  *   with p = flat_to_sorted[t*k+j]. Outputs: do_perm [T*k,H] (dtype),
- *   d_topk_w [T,k] f32. */
+ *   d_topk_w [T,k] f32. do_perm may be NULL: only d_topk_w is written (the
+ *   backward of moe_gemm_down_bwd_dy reads dy itself). */
 moe_status moe_combine_bwd(moe_shape s, const void* dy, const void* o_perm, const float* topk_w,
                            const int32_t* flat_to_sorted, void* do_perm, float* d_topk_w, hipStream_t stream);
 
@@ -214,6 +219,53 @@ moe_status moe_gemm_gate_up_bwd(moe_shape s, const void* dgu, const void* x_rows
                                 const int32_t* offsets, const void* w_gate, const void* w_up, void* dx_perm,
                                 float* dw_gate, float* dw_up, int accumulate_dw, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
+
+/* ---- Training step without do_perm (unsloth PR #3812, "[MoE] Improve moe
+ * kernels for unsloth fine tuning", Codex review of the grouped GEMM's
+ * fused routing-weight multiply; modelopt.torch.utils.moe, a2a_moe: each
+ * token's expert outputs weighted by its routing weights). The backward of
+ * the weighted combine no longer materialises do_perm = w * dy per sorted
+ * row: the down data gradient reads dy rows through the rows' tokens and
+ * applies the routing weight to dA in fp32, and the down weight gradient
+ * reads the same dy rows against the weighted activations a_w = w * a that
+ * the forward's gate/up GEMM writes. Chain (bf16 only): moe_route ->
+ * moe_permute_rows -> moe_gemm_gate_up_aw -> moe_gemm_down -> moe_combine;
+ * moe_combine_bwd (do_perm NULL) -> moe_gemm_down_bwd_dy ->
+ * moe_gemm_gate_up_bwd -> moe_unpermute_sum -> moe_route_bwd. */
+
+/* moe_permute with, for each sorted row p, row_token[p] = sorted_to_flat[p] / k
+ * (int32 [T*k]) and row_weight[p] = topk_w[sorted_to_flat[p]] (f32 [T*k]) as
+ * in moe_permute_fused; every other output (counts, offsets, both
+ * permutations, x_perm) exactly as moe_permute. */
+moe_status moe_permute_rows(moe_shape s, const int32_t* topk_idx, const float* topk_w, const void* x,
+                            int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted,
+                            int32_t* row_token, float* row_weight, void* x_perm, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* moe_gemm_gate_up that also writes the weighted activations
+ *   a_w[p,:] = bf16(row_weight[p] * a[p,:])  (a in fp32 before its rounding)
+ * for moe_gemm_down_bwd_dy. x_rows is x_perm [T*k,H] when row_token is NULL,
+ * else x [T,H] with sorted row p read as row row_token[p] (then
+ * T*H*2 < 2^31, MOE_EUNSUPPORTED otherwise). g, u, a, a_w [T*k,I] bf16;
+ * shape.dtype MOE_BF16 (MOE_EUNSUPPORTED otherwise). */
+moe_status moe_gemm_gate_up_aw(moe_shape s, const void* x_rows, const int32_t* row_token, const float* row_weight,
+                               const int32_t* offsets, const void* w_gate, const void* w_up, void* g, void* u,
+                               void* a, void* a_w, hipStream_t stream);
+
+/* The down backward pair (moe_gemm_down_bwd) reading dy [T,H] through the
+ * rows' tokens instead of do_perm. For each expert e and sorted row p of it,
+ * t = row_token[p], w = row_weight[p]:
+ *   dA[p] = w * (dy[t] W_down[e])   (fp32; then dU, dG into dgu as in moe_gemm_down_bwd)
+ *   dW_down[e] = sum over p of dy[t]^T a_w[p]   (a_w from moe_gemm_gate_up_aw)
+ * which is the chain rule through do_perm[p] = w dy[t] with the weight moved
+ * to the other factor (rounded once to bf16 with a, instead of with dy).
+ * dgu [T*k,2I] bf16, dw_down [E,H,I] f32 (+= if accumulate_dw); workspace as
+ * moe_gemm_down_bwd. bf16 only; T*H*2 < 2^31 and 4*(T*k + 256) < 2^31
+ * (MOE_EUNSUPPORTED otherwise). */
+moe_status moe_gemm_down_bwd_dy(moe_shape s, const void* dy, const int32_t* row_token, const float* row_weight,
+                                const void* a_w, const int32_t* offsets, const void* w_down, const void* g,
+                                const void* u, void* dgu, float* dw_down, int accumulate_dw, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
 
 /* Backward of the gather in moe_permute: dx[t,:] = sum over j ascending of
  * dx_perm[flat_to_sorted[t*k+j],:] in fp32, rounded once. Output: dx [T,H]. */
@@ -381,6 +433,20 @@ moe_status moe_forward_fused_fp8(moe_shape s, const void* x, const void* w_route
  * (N + 256) K < 2^30 (MOE_EUNSUPPORTED otherwise). */
 moe_status moe_lora_merge(int32_t E, int32_t N, int32_t K, int32_t r, float scale, const void* w, const void* a,
                           const void* b, void* w_out, hipStream_t stream);
+
+/* QLoRA-style adapters over 8-bit frozen experts (sourcepulse summary,
+ * "Highlighted Details": QLoRA, LoRA training over quantised GGUF models;
+ * "Quick Start & Requirements": bitsandbytes 4-bit weights; torchtune PR
+ * #2820: fp8 checkpoints). The frozen weights stay in E4M3 with one E8M0
+ * scale per output row (moe_quantize_fp8_rows), half the bytes of bf16; the
+ * merge dequantises them (exactly) and adds the adapters' product:
+ *   W'[e] = bf16(deq(wq[e]) + s * B[e] A[e]),  deq(wq)[n,c] = E4M3(wq[n,c]) * 2^(w_e8[n] - 127)
+ * wq [E,N,K] codes, w_e8 [E,N] (one byte per row of every expert), a, b,
+ * w_out as in moe_lora_merge (w_out bf16 [E,N,K], not overlapping wq). The
+ * rest of the adapter step runs on W' exactly as with bf16 frozen weights.
+ * Same limits and errors as moe_lora_merge. */
+moe_status moe_lora_merge_fp8(int32_t E, int32_t N, int32_t K, int32_t r, float scale, const uint8_t* wq,
+                              const uint8_t* w_e8, const void* a, const void* b, void* w_out, hipStream_t stream);
 
 /* Bytes of device workspace for moe_lora_grads at this shape and rank (0 if
  * either is rejected): the scaled adapters and the rank-wide row

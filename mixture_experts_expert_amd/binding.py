@@ -73,8 +73,12 @@ _SIGS = {
                                         ctypes.c_int),
     "moe_forward_fused": ([moe_shape] + [_P] * 19 + [ctypes.c_size_t, _P], ctypes.c_int),
     "moe_forward_fused_noalloc": ([moe_shape] + [_P] * 18 + [_P], ctypes.c_int),
+    "moe_permute_rows": ([moe_shape] + [_P] * 11 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_gemm_gate_up_aw": ([moe_shape] + [_P] * 10 + [_P], ctypes.c_int),
+    "moe_gemm_down_bwd_dy": ([moe_shape] + [_P] * 10 + [ctypes.c_int, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "moe_lora_workspace_bytes": ([moe_shape, ctypes.c_int32], ctypes.c_size_t),
     "moe_lora_merge": ([ctypes.c_int32] * 4 + [ctypes.c_float] + [_P] * 5, ctypes.c_int),
+    "moe_lora_merge_fp8": ([ctypes.c_int32] * 4 + [ctypes.c_float] + [_P] * 6, ctypes.c_int),
     "moe_lora_grads": ([moe_shape, ctypes.c_int32, ctypes.c_float] + [_P] * 18 + [ctypes.c_size_t, _P],
                        ctypes.c_int),
 }
@@ -299,6 +303,28 @@ def moe_forward_fused(s, x, w_router, logit_bias, w_gate, w_up, w_down, logits, 
         _ptr(row_token), _ptr(row_weight), _ptr(a), _ptr(o_perm), _ptr(y), _ptr(ws), nb, _stream(stream)))
 
 
+def moe_permute_rows(s, topk_idx, topk_w, x, counts, offsets, sorted_to_flat, flat_to_sorted, row_token, row_weight,
+                     x_perm, ws, ws_bytes=None, stream=None):
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_permute_rows", lib.moe_permute_rows(
+        s, _ptr(topk_idx), _ptr(topk_w), _ptr(x), _ptr(counts), _ptr(offsets), _ptr(sorted_to_flat),
+        _ptr(flat_to_sorted), _ptr(row_token), _ptr(row_weight), _ptr(x_perm), _ptr(ws), nb, _stream(stream)))
+
+
+def moe_gemm_gate_up_aw(s, x_rows, row_token, row_weight, offsets, w_gate, w_up, g, u, a, a_w, stream=None):
+    _check("moe_gemm_gate_up_aw", lib.moe_gemm_gate_up_aw(
+        s, _ptr(x_rows), _ptr(row_token), _ptr(row_weight), _ptr(offsets), _ptr(w_gate), _ptr(w_up), _ptr(g), _ptr(u),
+        _ptr(a), _ptr(a_w), _stream(stream)))
+
+
+def moe_gemm_down_bwd_dy(s, dy, row_token, row_weight, a_w, offsets, w_down, g, u, dgu, dw_down, accumulate_dw, ws,
+                         ws_bytes=None, stream=None):
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_gemm_down_bwd_dy", lib.moe_gemm_down_bwd_dy(
+        s, _ptr(dy), _ptr(row_token), _ptr(row_weight), _ptr(a_w), _ptr(offsets), _ptr(w_down), _ptr(g), _ptr(u),
+        _ptr(dgu), _ptr(dw_down), int(accumulate_dw), _ptr(ws), nb, _stream(stream)))
+
+
 def moe_forward_fused_noalloc(s, x, w_router, logit_bias, w_gate, w_up, w_down, logits, topk_idx, topk_w, counts,
                               offsets, sorted_to_flat, flat_to_sorted, row_token, row_weight, a, o_perm, y,
                               stream=None):
@@ -315,6 +341,20 @@ def moe_lora_workspace_bytes(s: moe_shape, r: int) -> int:
 def moe_lora_merge(E, N, K, r, scale, w, a, b, w_out, stream=None):
     _check("moe_lora_merge", lib.moe_lora_merge(E, N, K, r, float(scale), _ptr(w), _ptr(a), _ptr(b), _ptr(w_out),
                                                 _stream(stream)))
+
+
+def moe_lora_merge_fp8(E, N, K, r, scale, wq, w_e8, a, b, w_out, stream=None):
+    _check("moe_lora_merge_fp8", lib.moe_lora_merge_fp8(E, N, K, r, ctypes.c_float(scale), _ptr(wq), _ptr(w_e8), _ptr(a),
+                                                        _ptr(b), _ptr(w_out), _stream(stream)))
+
+
+def _merge_any(E, N, K, r, scale, w, a, b, w_out, stream=None):
+    """moe_lora_merge for a bf16 frozen weight, moe_lora_merge_fp8 for an
+    (E4M3 codes, E8M0 row scales) pair (FP8Weights.gate / .up / .down)."""
+    if isinstance(w, tuple):
+        moe_lora_merge_fp8(E, N, K, r, scale, w[0], w[1], a, b, w_out, stream)
+    else:
+        moe_lora_merge(E, N, K, r, scale, w, a, b, w_out, stream)
 
 
 def moe_lora_grads(s, r, scale, x_perm, act, dgu, do_perm, offsets, a_gate, b_gate, a_up, b_up, a_down, b_down,
@@ -338,12 +378,22 @@ class MoEStage:
     ``gather_fused``: no x_perm. The sort also gives each sorted row's token
     (moe_permute_fused), and the two GEMMs that read x rows (gate/up and its
     weight gradient) read them from x through it. Same results, bit for bit.
+
+    ``dy_fused`` (bf16): no do_perm. The forward's gate/up GEMM also writes
+    the weighted activations a_w (moe_gemm_gate_up_aw), the combine backward
+    writes d_topk_w only, and the down backward reads dy through the sorted
+    rows' tokens (moe_gemm_down_bwd_dy). The same mathematics with the
+    routing weight applied at another point: within tolerance of the oracle,
+    not bit-identical to the do_perm path. Not combined with aux_stream.
     """
 
     def __init__(self, T: int, H: int, E: int, k: int, I: int, dtype: torch.dtype, device="cuda",
-                 gather_fused: bool = False):
+                 gather_fused: bool = False, dy_fused: bool = False):
         self.T, self.H, self.E, self.k, self.I, self.dtype = T, H, E, k, I, dtype
         self.gather_fused = gather_fused
+        self.dy_fused = dy_fused
+        if dy_fused and dtype != torch.bfloat16:
+            raise ValueError("dy_fused needs bf16")
         self.weight_grads = True  # dw_* buffers (the adapter stage trains no frozen weight)
         self.s = shape(T, H, E, k, I, dtype)
         M = T * k
@@ -356,10 +406,12 @@ class MoEStage:
             "flat_to_sorted": e(M, dt=i32), "g": e(M, I), "u": e(M, I), "a": e(M, I),
             "o_perm": e(M, H), "y": e(T, H),
         }
-        if gather_fused:
+        if gather_fused or dy_fused:
             self.buf.update({"row_token": e(M, dt=i32), "row_weight": e(M, dt=f32)})
-        else:
+        if not gather_fused:
             self.buf["x_perm"] = e(M, H)
+        if dy_fused:
+            self.buf["a_w"] = e(M, I)
         ws_bytes = moe_workspace_bytes(self.s)
         if ws_bytes == 0:
             raise MoEError("moe_workspace_bytes", 1, "shape rejected")
@@ -373,8 +425,10 @@ class MoEStage:
         dev = self.ws.device
         M = T * k
         f32 = torch.float32
+        if not self.dy_fused:
+            self.buf["do_perm"] = torch.empty(M, H, dtype=dt, device=dev)
         self.buf.update({
-            "do_perm": torch.empty(M, H, dtype=dt, device=dev), "d_topk_w": torch.empty(T, k, dtype=f32, device=dev),
+            "d_topk_w": torch.empty(T, k, dtype=f32, device=dev),
             "dx_perm": torch.empty(M, H, dtype=dt, device=dev), "dx": torch.empty(T, H, dtype=dt, device=dev),
             "d_logits": torch.empty(T, E, dtype=f32, device=dev),
         })
@@ -391,7 +445,20 @@ class MoEStage:
         self.w = (w_gate, w_up, w_down)
         self.x = x
         moe_route(s, x, w_router, logit_bias, b["logits"], b["topk_idx"], b["topk_w"], stream)
-        if self.gather_fused:
+        if self.dy_fused:
+            if self.gather_fused:
+                moe_permute_fused(s, b["topk_idx"], b["topk_w"], b["counts"], b["offsets"], b["sorted_to_flat"],
+                                  b["flat_to_sorted"], b["row_token"], b["row_weight"], self.ws, stream=stream)
+                moe_gemm_gate_up_aw(s, x, b["row_token"], b["row_weight"], b["offsets"], w_gate, w_up, b["g"],
+                                    b["u"], b["a"], b["a_w"], stream)
+            else:
+                moe_permute_rows(s, b["topk_idx"], b["topk_w"], x, b["counts"], b["offsets"], b["sorted_to_flat"],
+                                 b["flat_to_sorted"], b["row_token"], b["row_weight"], b["x_perm"], self.ws,
+                                 stream=stream)
+                moe_gemm_gate_up_aw(s, b["x_perm"], None, b["row_weight"], b["offsets"], w_gate, w_up, b["g"],
+                                    b["u"], b["a"], b["a_w"], stream)
+            moe_gemm_down(s, b["a"], b["offsets"], w_down, b["o_perm"], stream)
+        elif self.gather_fused:
             moe_permute_fused(s, b["topk_idx"], b["topk_w"], b["counts"], b["offsets"], b["sorted_to_flat"],
                               b["flat_to_sorted"], b["row_token"], b["row_weight"], self.ws, stream=stream)
             moe_gemm_gate_up_gathered(s, x, b["row_token"], b["offsets"], w_gate, w_up, b["g"], b["u"], b["a"],
@@ -415,9 +482,23 @@ class MoEStage:
         self._alloc_bwd()
         b, s = self.buf, self.s
         w_gate, w_up, w_down = self.w
-        moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["do_perm"], b["d_topk_w"], stream)
+        moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b.get("do_perm"), b["d_topk_w"],
+                        stream)
         acc = int(accumulate_dw)
-        if aux_stream is None and not self.gather_fused:
+        if self.dy_fused:
+            if aux_stream is not None:
+                raise ValueError("dy_fused runs the backward on one stream")
+            if "dgu" not in b:
+                b["dgu"] = torch.empty(self.T * self.k, 2 * self.I, dtype=self.dtype, device=self.ws.device)
+            moe_gemm_down_bwd_dy(s, dy, b["row_token"], b["row_weight"], b["a_w"], b["offsets"], w_down, b["g"],
+                                 b["u"], b["dgu"], b["dw_down"], acc, self.ws, stream=stream)
+            if self.gather_fused:
+                moe_gemm_gate_up_bwd(s, b["dgu"], self.x, b["row_token"], b["offsets"], w_gate, w_up, b["dx_perm"],
+                                     b["dw_gate"], b["dw_up"], acc, self.ws, stream=stream)
+            else:
+                moe_gemm_gate_up_bwd(s, b["dgu"], b["x_perm"], None, b["offsets"], w_gate, w_up, b["dx_perm"],
+                                     b["dw_gate"], b["dw_up"], acc, self.ws, stream=stream)
+        elif aux_stream is None and not self.gather_fused:
             moe_grouped_gemm_bwd(s, b["do_perm"], b["x_perm"], b["g"], b["u"], b["a"], b["offsets"], w_gate, w_up,
                                  w_down, b["dx_perm"], b["dw_gate"], b["dw_up"], b["dw_down"], acc, self.ws,
                                  stream=stream)
@@ -466,7 +547,9 @@ class LoRAStage(MoEStage):
     forward on W'; ``backward(dy)`` runs the data gradients on W' and
     moe_lora_grads, and returns dx. The adapter gradients (float32) are in
     ``buf["d" + name]``; the frozen weights get none. ``adapters``: a_P
-    [E,r,K], b_P [E,N,r] bf16 for P in gate, up, down.
+    [E,r,K], b_P [E,N,r] bf16 for P in gate, up, down. Each frozen weight is
+    a bf16 tensor or, kept in 8 bits (QLoRA-style), the (E4M3 codes, E8M0
+    row scales) pair of FP8Weights (moe_lora_merge_fp8 dequantises it).
     """
 
     def __init__(self, T: int, H: int, E: int, k: int, I: int, rank: int, scale: float, device="cuda"):
@@ -495,9 +578,9 @@ class LoRAStage(MoEStage):
     def merge(self, w_gate, w_up, w_down, adapters, stream=None):
         E, H, I, r = self.E, self.H, self.I, self.rank
         wg, wu, wd = self.merged
-        moe_lora_merge(E, I, H, r, self.scale, w_gate, adapters["a_gate"], adapters["b_gate"], wg, stream)
-        moe_lora_merge(E, I, H, r, self.scale, w_up, adapters["a_up"], adapters["b_up"], wu, stream)
-        moe_lora_merge(E, H, I, r, self.scale, w_down, adapters["a_down"], adapters["b_down"], wd, stream)
+        _merge_any(E, I, H, r, self.scale, w_gate, adapters["a_gate"], adapters["b_gate"], wg, stream)
+        _merge_any(E, I, H, r, self.scale, w_up, adapters["a_up"], adapters["b_up"], wu, stream)
+        _merge_any(E, H, I, r, self.scale, w_down, adapters["a_down"], adapters["b_down"], wd, stream)
         return self.merged
 
     def forward(self, x, w_router, w_gate, w_up, w_down, adapters, logit_bias=None, stream=None, aux_stream=None):
@@ -515,11 +598,11 @@ class LoRAStage(MoEStage):
         forked = torch.cuda.Event()
         forked.record(main)
         aux_stream.wait_event(forked)
-        moe_lora_merge(E, I, H, r, self.scale, w_gate, adapters["a_gate"], adapters["b_gate"], wg, aux_stream)
-        moe_lora_merge(E, I, H, r, self.scale, w_up, adapters["a_up"], adapters["b_up"], wu, aux_stream)
+        _merge_any(E, I, H, r, self.scale, w_gate, adapters["a_gate"], adapters["b_gate"], wg, aux_stream)
+        _merge_any(E, I, H, r, self.scale, w_up, adapters["a_up"], adapters["b_up"], wu, aux_stream)
         gu_ready = torch.cuda.Event()
         gu_ready.record(aux_stream)
-        moe_lora_merge(E, H, I, r, self.scale, w_down, adapters["a_down"], adapters["b_down"], wd, aux_stream)
+        _merge_any(E, H, I, r, self.scale, w_down, adapters["a_down"], adapters["b_down"], wd, aux_stream)
         d_ready = torch.cuda.Event()
         d_ready.record(aux_stream)
         b, s = self.buf, self.s

@@ -397,8 +397,79 @@ moe_status moe_combine_bwd(moe_shape s, const void* dy, const void* o_perm, cons
                            const int32_t* flat_to_sorted, void* do_perm, float* d_topk_w, hipStream_t stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
-  if (any_null(dy, o_perm, topk_w, flat_to_sorted, do_perm, d_topk_w)) return MOE_EINVAL;
+  if (any_null(dy, o_perm, topk_w, flat_to_sorted, d_topk_w)) return MOE_EINVAL;  // do_perm may be NULL
   return from_hip(moe::launch_combine_bwd(s, dy, o_perm, topk_w, flat_to_sorted, do_perm, d_topk_w, stream));
+}
+
+moe_status moe_permute_rows(moe_shape s, const int32_t* topk_idx, const float* topk_w, const void* x,
+                            int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted,
+                            int32_t* row_token, float* row_weight, void* x_perm, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(topk_idx, topk_w, x, counts, offsets, sorted_to_flat, flat_to_sorted, row_token, row_weight, x_perm,
+               ws))
+    return MOE_EINVAL;
+  if (ws_bytes < moe::ws_layout(s).total) return MOE_EWORKSPACE;
+  return from_hip(moe::launch_permute_rows(s, topk_idx, topk_w, x, counts, offsets, sorted_to_flat, flat_to_sorted,
+                                           row_token, row_weight, x_perm, ws, stream));
+}
+
+moe_status moe_gemm_gate_up_aw(moe_shape s, const void* x_rows, const int32_t* row_token, const float* row_weight,
+                               const int32_t* offsets, const void* w_gate, const void* w_up, void* g, void* u,
+                               void* a, void* a_w, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(x_rows, row_weight, offsets, w_gate, w_up, g, u, a, a_w)) return MOE_EINVAL;
+  if (s.dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (row_token != nullptr && !gathered_x_fits(s)) return MOE_EUNSUPPORTED;
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = x_rows;
+  ga.row_token = row_token;
+  ga.row_weight = row_weight;
+  ga.b0 = w_gate;
+  ga.b1 = w_up;
+  ga.out0 = g;
+  ga.out1 = u;
+  ga.out2 = a;
+  ga.out3 = a_w;
+  return from_hip(moe::launch_gemm(moe::GEMM_GATEUP, s, ga, stream));
+}
+
+moe_status moe_gemm_down_bwd_dy(moe_shape s, const void* dy, const int32_t* row_token, const float* row_weight,
+                                const void* a_w, const int32_t* offsets, const void* w_down, const void* g,
+                                const void* u, void* dgu, float* dw_down, int accumulate_dw, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(dy, row_token, row_weight, a_w, offsets, w_down, g, u, dgu, dw_down, ws)) return MOE_EINVAL;
+  if (accumulate_dw != 0 && accumulate_dw != 1) return MOE_EINVAL;
+  if (s.dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  // dy rows are addressed with 32-bit byte offsets; the row tokens of the
+  // weight gradient's k-rows are read up to two steps past the last row.
+  if (!gathered_x_fits(s) || 4 * (static_cast<int64_t>(s.T) * s.k + 256) >= (static_cast<int64_t>(1) << 31))
+    return MOE_EUNSUPPORTED;
+  const WsLayout l = moe::ws_layout(s);
+  if (ws_bytes < l.total) return MOE_EWORKSPACE;
+  moe::GemmArgs gd{};
+  gd.offsets = offsets;
+  gd.a = dy;
+  gd.row_token = row_token;
+  gd.row_weight = row_weight;
+  gd.b0 = w_down;
+  gd.g_in = g;
+  gd.u_in = u;
+  gd.out0 = dgu;
+  moe::GemmArgs gw{};
+  gw.part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.part_off);
+  gw.offsets = offsets;
+  gw.a = dy;
+  gw.row_token = row_token;
+  gw.b0 = a_w;
+  gw.dw0 = dw_down;
+  gw.accumulate = accumulate_dw;
+  return from_hip(moe::launch_gemm_pair(moe::GEMM_DGRAD_DOWN, moe::GEMM_WGRAD_DOWN, s, gd, gw, stream));
 }
 
 moe_status moe_grouped_gemm_bwd(moe_shape s, const void* do_perm, const void* x_perm, const void* g, const void* u,
@@ -522,6 +593,15 @@ moe_status moe_lora_merge(int32_t E, int32_t N, int32_t K, int32_t r, float scal
   // are range-checked and their results never stored.)
   if ((static_cast<int64_t>(N) + 256) * K >= (static_cast<int64_t>(1) << 30)) return MOE_EUNSUPPORTED;
   return from_hip(moe::launch_lora_merge(E, N, K, r, scale, w, a, b, w_out, stream));
+}
+
+moe_status moe_lora_merge_fp8(int32_t E, int32_t N, int32_t K, int32_t r, float scale, const uint8_t* wq,
+                              const uint8_t* w_e8, const void* a, const void* b, void* w_out, hipStream_t stream) {
+  if (E <= 0 || N <= 0 || K <= 0 || r <= 0) return MOE_EINVAL;
+  if (any_null(wq, w_e8, a, b, w_out)) return MOE_EINVAL;
+  if (r > 128 || r % 8 != 0 || K % 8 != 0 || E > 65535 || (N + 127) / 128 > 65535) return MOE_EUNSUPPORTED;
+  if ((static_cast<int64_t>(N) + 256) * K >= (static_cast<int64_t>(1) << 30)) return MOE_EUNSUPPORTED;
+  return from_hip(moe::launch_lora_merge_fp8(E, N, K, r, scale, wq, w_e8, a, b, w_out, stream));
 }
 
 moe_status moe_lora_grads(moe_shape s, int32_t r, float scale, const void* x_perm, const void* act, const void* dgu,

@@ -106,10 +106,11 @@ __global__ __launch_bounds__(kThreads) void gather_sum_kernel(int Tn, int k, int
 }
 
 // do_perm[p] = w[t,j] * dy[t];  gw[t,j] = <dy[t], o_perm[p]>,  p = f2s[t*k+j]
-// Slots go in batches of kBwdBatch; for each batch the row is walked in
-// bands of kWave chunks with the batch's o_perm chunks in flight together.
-constexpr int kBwdBatch = 4;
-template <class T>
+// Slots go in batches of BATCH; for each batch the row is walked in bands of
+// kWave chunks with the batch's o_perm chunks in flight together. Without
+// do_perm (WRITE_DO false: the backward that reads dy through the rows'
+// tokens) only gw is written, eight slots at a time.
+template <class T, bool WRITE_DO, int BATCH>
 __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(int Tn, int k, int chunks,
                                                                const uint4* __restrict__ dy,
                                                                const uint4* __restrict__ o_perm,
@@ -122,6 +123,7 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(int Tn, int k, in
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + static_cast<int>(threadIdx.x) / kWave);
   if (t >= Tn) return;  // wave-uniform: no block barrier in this kernel
   const int64_t tk = static_cast<int64_t>(t) * k;
+  constexpr int kBwdBatch = BATCH;
   for (int j0 = 0; j0 < k; j0 += kBwdBatch) {
     int idx;
     float wt;
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(int Tn, int k, in
           dot[jj] += d[i] * o[i];
         }
         // Slots past k repeat the last row: the same values again, harmless.
-        do_perm[p[jj] * chunks + c] = Vec<T>::pack(g);
+        if constexpr (WRITE_DO) do_perm[p[jj] * chunks + c] = Vec<T>::pack(g);
       }
     }
 #pragma unroll
@@ -189,14 +191,18 @@ hipError_t launch_unpermute_sum(const moe_shape& s, const void* dx_perm, const i
 hipError_t launch_combine_bwd(const moe_shape& s, const void* dy, const void* o_perm, const float* w,
                               const int32_t* f2s, void* do_perm, float* gw, hipStream_t st) {
   const dim3 grid(ceil_div(s.T, kWavesPerBlock));
-  if (s.dtype == MOE_BF16)
-    combine_bwd_kernel<bf16_t><<<grid, kThreads, 0, st>>>(
-        s.T, s.k, s.H / Vec<bf16_t>::N, static_cast<const uint4*>(dy), static_cast<const uint4*>(o_perm), w, f2s,
-        static_cast<uint4*>(do_perm), gw);
-  else
-    combine_bwd_kernel<float><<<grid, kThreads, 0, st>>>(
-        s.T, s.k, s.H / Vec<float>::N, static_cast<const uint4*>(dy), static_cast<const uint4*>(o_perm), w, f2s,
-        static_cast<uint4*>(do_perm), gw);
+  const uint4* d = static_cast<const uint4*>(dy);
+  const uint4* o = static_cast<const uint4*>(o_perm);
+  uint4* dp = static_cast<uint4*>(do_perm);
+  if (s.dtype == MOE_BF16) {
+    const int ch = s.H / Vec<bf16_t>::N;
+    if (do_perm) combine_bwd_kernel<bf16_t, true, 4><<<grid, kThreads, 0, st>>>(s.T, s.k, ch, d, o, w, f2s, dp, gw);
+    else combine_bwd_kernel<bf16_t, false, 8><<<grid, kThreads, 0, st>>>(s.T, s.k, ch, d, o, w, f2s, dp, gw);
+  } else {
+    const int ch = s.H / Vec<float>::N;
+    if (do_perm) combine_bwd_kernel<float, true, 4><<<grid, kThreads, 0, st>>>(s.T, s.k, ch, d, o, w, f2s, dp, gw);
+    else combine_bwd_kernel<float, false, 8><<<grid, kThreads, 0, st>>>(s.T, s.k, ch, d, o, w, f2s, dp, gw);
+  }
   return hipGetLastError();
 }
 

@@ -98,6 +98,7 @@ struct Params {
   bf16_t* out0;        // g | o_perm | dgu | dx_perm
   bf16_t* out1;        // u (GATEUP)
   bf16_t* out2;        // a (GATEUP)
+  bf16_t* out3;        // GATEUP with AW: a_w[p] = bf16(row_weight[p] a[p])
   float* dw0;          // dw_down | dw_gate
   float* dw1;          // dw_up
   int accumulate;
@@ -105,7 +106,10 @@ struct Params {
   // Fused gather and routing weights (both optional): GATEUP reads row p of A
   // as row row_token[p] of x [T][H] (no x_perm), WGRAD_GATEUP reads k-row p of
   // B likewise; DOWN scales output row p by row_weight[p] before rounding.
-  // GATEUP with out0 == nullptr stores A only.
+  // GATEUP with out0 == nullptr stores A only. In the backward without
+  // do_perm, DGRAD_DOWN reads row p of A as row row_token[p] of dy [T][H] and
+  // scales dA row p by row_weight[p] in fp32 before the SwiGLU backward, and
+  // WGRAD_DOWN reads k-row p of A likewise (its B is then a_w).
   const int32_t* row_token;
   const float* row_weight;
   // fp8 (E4M3) GATEUP/DOWN of the inference forward: a, b0, b1 hold 8-bit
@@ -367,9 +371,10 @@ struct Smem {
 // Every tile of one GEMM that workgroup `bid` of `nblk` (a multiple of 8)
 // owns, start to finish: on return every load and store this workgroup
 // issued has completed and its waves are past a barrier.
-template <int MODE, bool FUSED, bool F8 = false>
+template <int MODE, bool FUSED, bool F8 = false, bool AW = false>
 __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const int nblk, const Smem& sm) {
   static_assert(!F8 || (FUSED && (MODE == GATEUP || MODE == DOWN)), "fp8: the inference forward's two GEMMs");
+  static_assert(!AW || (MODE == GATEUP && !F8), "a_w: the gate/up GEMM of the training step");
   // Element size in bytes, elements per k-step (64 bytes of a k-major row
   // either way) and per 16-byte chunk.
   constexpr int ESZ = F8 ? 1 : 2;
@@ -487,9 +492,15 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
 
   constexpr bool A_KMAJOR = !grouped_k(MODE);
   constexpr bool B_KMAJOR = b_kcontig(MODE);
-  // Gate/up weight gradient with x read through row_token: the k-rows of B
-  // are gathered, so B's load offsets change with every k-step.
+  // Rows of a k-major A read through row_token (x for gate/up, dy for the
+  // down data gradient): per-lane offsets set at each tile start.
+  constexpr bool GATHER_A_ROWS = (MODE == GATEUP || MODE == DGRAD_DOWN) && FUSED;
+  // Weight gradients with an operand read through row_token: the k-rows of
+  // B (x, gate/up) or of A (dy, down) are gathered, so that operand's load
+  // offsets change with every k-step.
   constexpr bool GATHER_B = MODE == WGRAD_GATEUP && FUSED;
+  constexpr bool GATHER_A = MODE == WGRAD_DOWN && FUSED;
+  constexpr bool GATHER_K = GATHER_A || GATHER_B;
 
   // ---- tile state ------------------------------------------------------------
   // Everything the operand loads of a tile depend on. A tile's last k-step
@@ -506,9 +517,9 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
 
   int e = 0, row0 = 0, mvalid = 0, m0 = 0, n0 = 0, kbeg = 0, kend = 0, ksteps = 0;
   int pidx = -1;  // grouped-K: partial tile of a later chunk, -1 for chunk 0
-  int nkbeg = 0;  // GATHER_B: first k-row of this workgroup's next tile
+  int nkbeg = 0;  // GATHER_K: first k-row of this workgroup's next tile
   uint32_t aoff[LOADS / 2], boff[LOADS / 2];
-  uint32_t bcol[LOADS / 2];  // GATHER_B: column byte offsets of the B loads
+  uint32_t gcol[LOADS / 2];  // GATHER_K: column byte offsets of the gathered operand's loads
   const char* abase_m = reinterpret_cast<const char*>(P.a);  // grouped-M: the tile's first row of A
 
   // Grouped-K: the first k-row of tile Lx's chunk.
@@ -570,7 +581,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
     kend = __builtin_amdgcn_readfirstlane(tkend);
     pidx = __builtin_amdgcn_readfirstlane(tpidx);
     ksteps = grouped_k(MODE) ? (kend - kbeg + BK - 1) / BK : kfixed;
-    if constexpr (GATHER_B)  // the row tokens run two steps ahead, into the next tile
+    if constexpr (GATHER_K)  // the row tokens run two steps ahead, into the next tile
       nkbeg = __builtin_amdgcn_readfirstlane(L + nslots < hi ? kbeg_of(L + nslots) : 0);
   };
   // Per-lane load offsets of the current tile (vector registers; recomputed
@@ -595,7 +606,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
       if constexpr (A_KMAJOR) {
         const int r = blk * 16 + (lane >> 2);
         const int c = (lane & 3) ^ swk(r);
-        if (MODE == GATEUP && FUSED)  // row of x; rows >= mvalid read zeros
+        if (GATHER_A_ROWS)  // row of x or dy; rows >= mvalid read zeros
           aoff[t] = r < mvalid ? ESZ * (static_cast<uint32_t>(P.row_token[row0 + r]) * H + c * CK) : kNoWrite;
         else
           aoff[t] = ESZ * (r * lda + c * CK);  // rows >= mvalid: outside the range, read as zeros
@@ -603,7 +614,8 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
         const int k = blk * 2 + (lane >> 5);
         const int c = (lane & 31) ^ swt(k);
         const int mrows = MODE == WGRAD_DOWN ? H : 2 * I;
-        aoff[t] = 2u * (k * lda + min(m0 + c * 8, mrows - 8));
+        if constexpr (GATHER_A) gcol[t] = 2u * min(m0 + c * 8, mrows - 8);  // row part: gather_off
+        else aoff[t] = 2u * (k * lda + min(m0 + c * 8, mrows - 8));
       }
       if constexpr (MODE == GATEUP) {
         // LDS row r: wavefront column half r / 128 and 32-column block
@@ -622,7 +634,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
         const int k = blk * 2 + (lane >> 5);
         const int c = (lane & 31) ^ swt(k);
         const int ncols = (MODE == DGRAD_DOWN || MODE == WGRAD_DOWN) ? I : H;
-        if constexpr (GATHER_B) bcol[t] = 2u * min(n0 + c * 8, ncols - 8);  // row part: gather_boff
+        if constexpr (GATHER_B) gcol[t] = 2u * min(n0 + c * 8, ncols - 8);  // row part: gather_off
         else boff[t] = 2u * (k * ldb + min(n0 + c * 8, ncols - 8));
       }
     }
@@ -643,11 +655,12 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   auto rsrc_a = [&](int s) -> rsrc_t {
     const int k0 = s * KS;
     if constexpr (A_KMAJOR) {
-      if (MODE == GATEUP && FUSED)
+      if (GATHER_A_ROWS)
         return make_rsrc(reinterpret_cast<const char*>(P.a) + k0 * ESZ, s < ksteps ? ESZ * (P.T * H - k0) : 0);
       return make_rsrc(abase_m + k0 * ESZ, s < ksteps ? ESZ * (mvalid * lda - k0) : 0);
     } else {
       const int left = kend - kbeg - k0;
+      if constexpr (GATHER_A) return make_rsrc(P.a, left > 0 ? 2 * P.T * H : 0);
       return make_rsrc(P.a + static_cast<int64_t>(kbeg + k0) * lda, left > 0 ? 2 * left * lda : 0);
     }
   };
@@ -675,14 +688,14 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
     }
   };
 
-  // GATHER_B: the row tokens of B's k-rows. Instruction t of a wavefront's B
-  // loads covers k-rows 8 wave + 2t (lanes 0-31) and 8 wave + 2t + 1 (lanes
-  // 32-63) of its step; lane l fetches the token of k-row
+  // GATHER_K: the row tokens of the gathered operand's k-rows. Instruction t
+  // of a wavefront's A or B loads covers k-rows 8 wave + 2t (lanes 0-31) and
+  // 8 wave + 2t + 1 (lanes 32-63) of its step; lane l fetches the token of k-row
   // 8 wave + 2 (l % 4) + l / 32, so that lanes t and 32 + t hold the two rows
   // of instruction t. Step q of the current tile, or (q past the tile's
   // padded step count) step q - that count of the next one. Reads past the
   // end of row_token return 0; such rows are never used.
-  const rsrc_t rtok = make_rsrc(P.row_token, GATHER_B ? 4 * P.M : 0);
+  const rsrc_t rtok = make_rsrc(P.row_token, GATHER_K ? 4 * P.M : 0);
   auto load_tok = [&](int q) -> uint32_t {
     const int nst = max(NSTAGE, (ksteps + NSTAGE - 1) / NSTAGE * NSTAGE);
     const bool nxt = q >= nst;
@@ -691,10 +704,11 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
     const int row = (nxt ? nkbeg : kbeg) + (nxt ? q - nst : q) * BK + wave * 8 + 2 * (lane & 3) + (lane >> 5);
     return __builtin_amdgcn_raw_buffer_load_b32(rtok, 4u * static_cast<uint32_t>(row), 0, 0);
   };
-  // B's byte offsets for step sn of the current tile from its tokens: row
-  // token * 2H plus the column part; k-rows past the chunk's end get an
-  // offset outside the range (zeros).
-  auto gather_boff = [&](uint32_t tok, int sn) __attribute__((always_inline)) {
+  // The gathered operand's byte offsets for step sn of the current tile
+  // from its tokens: row token * 2H (x and dy rows are H long) plus the
+  // column part; k-rows past the chunk's end get an offset outside the range
+  // (zeros).
+  auto gather_off = [&](uint32_t tok, int sn) __attribute__((always_inline)) {
     const int left = kend - kbeg - sn * BK - wave * 8;
     const bool hi32 = lane_id >= 32;
 #pragma unroll
@@ -703,7 +717,9 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
       const uint32_t t1 = __builtin_amdgcn_readlane(tok, 32 + t);
       const uint32_t o0 = 2 * t < left ? t0 * (2u * H) : kNoWrite;
       const uint32_t o1 = 2 * t + 1 < left ? t1 * (2u * H) : kNoWrite;
-      boff[t] = (hi32 ? o1 : o0) + bcol[t];
+      const uint32_t o = (hi32 ? o1 : o0) + gcol[t];
+      if constexpr (GATHER_A) aoff[t] = o;
+      else boff[t] = o;
     }
   };
   // Tokens of steps sn and sn + 1 at the start of the k-step that loads sn.
@@ -830,11 +846,11 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   // the next tile's first steps comes after the epilogue.
   auto kstep = [&](auto nbc, auto first, const bf16_t* Ac, const bf16_t* An, int sn, bf16_t* Ln, bool last)
                    __attribute__((always_inline)) {
-    if constexpr (GATHER_B) {
+    if constexpr (GATHER_K) {
       // Step sn's B offsets from tokens loaded two k-steps ago (their wait
       // covers only loads the pipeline has already waited for), then the
       // tokens of step sn + 2, ahead of this step's operand loads.
-      gather_boff(tkA, sn);
+      gather_off(tkA, sn);
       const uint32_t tn = load_tok(sn + 2);
       tkA = tkB;
       tkB = tn;
@@ -848,8 +864,8 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
     __builtin_amdgcn_sched_barrier(0);
     mfma_slice(nbc, first, fa0, fb0, 0, ra, rb, Ln);
     if (!last) {
-      // GATHER_B: two token loads more among the newest.
-      __builtin_amdgcn_s_waitcnt(GATHER_B ? kWaitVm14 : kWaitVm12);
+      // GATHER_K: two token loads more among the newest.
+      __builtin_amdgcn_s_waitcnt(GATHER_K ? kWaitVm14 : kWaitVm12);
       step_barrier();
       read_slice(nbc, An, 0, fa0, fb0);
     }
@@ -1005,14 +1021,26 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
       // of the wavefront's 64.
       const int hrow = 4 * (lane >> 5) + prow;
       const int idx = tn0 + wn * 64 + ((lane >> 2) & 1) * 32 + ((lane & 31) >> 3) * 8;
+      // AW: a_w = bf16(row_weight[p] a) as well, from the fp32 a (transposed
+      // first, so that each lane holds one row and takes that row's weight).
+      const rsrc_t rwr = make_rsrc(P.row_weight + (AW ? trow0 : 0), AW ? 4 * tmvalid : 0);
+      const rsrc_t raw = make_rsrc(AW ? P.out3 + base : P.out2, AW ? bytes : 0);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
+        float rwi[4];
+        if constexpr (AW) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            rwi[b] = i < nbm ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                   rwr, 4u * static_cast<uint32_t>(wm * WTM + i * 32 + 8 * b + hrow), 0, 0))
+                             : 0.0f;
+        }
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           if (i >= nbm) continue;  // no valid rows in this block
           const int r = wm * WTM + i * 32 + 8 * b + hrow;
           const uint32_t off = idx < I ? 2u * static_cast<uint32_t>(r * I + idx) : kNoWrite;
-          u32x2 gp[2], up[2], ap[2];
+          u32x2 gp[2], up[2], ap[2], wp[2];
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             float g[4], u[4], a[4];
@@ -1024,14 +1052,24 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
             }
             gp[j] = quad_transpose_bf16(g, lane);
             up[j] = quad_transpose_bf16(u, lane);
-            ap[j] = quad_transpose_bf16(a, lane);
+            if constexpr (AW) {
+              quad_transpose(a, lane);  // row 8b + hrow, four columns
+              ap[j] = pack_bf16x4v(a);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) a[q] *= rwi[b];
+              wp[j] = pack_bf16x4v(a);
+            } else {
+              ap[j] = quad_transpose_bf16(a, lane);
+            }
           }
           if (store_gu) {
             store_b128(pair_cols8(gp[0], gp[1], lane), rg, off);
             store_b128(pair_cols8(up[0], up[1], lane), ru, off);
           }
           store_b128(pair_cols8(ap[0], ap[1], lane), rs, off);
+          if constexpr (AW) store_b128(pair_cols8(wp[0], wp[1], lane), raw, off);
         }
+      }
     } else if constexpr (MODE == DOWN || MODE == DGRAD_GATEUP) {
       // 16-byte stores: lane l writes row 8b + 4(l/32) + l%4, columns
       // jp*64 + 32*((l/4)%2) + 8*((l%32)/8) .. + 7 (pair_cols8).
@@ -1092,8 +1130,18 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
       // the previous block's arithmetic and stores.
       const int hrow = 4 * (lane >> 5) + prow;
       const int ncol8 = ((lane >> 2) & 1) * 32 + ((lane & 31) >> 3) * 8;
+      // FUSED (dy read through row_token): dA row p is scaled by
+      // row_weight[p] in fp32 first; the weights travel with G and U.
+      const rsrc_t rwr = make_rsrc(P.row_weight + (FUSED ? trow0 : 0), FUSED ? 4 * tmvalid : 0);
       typedef u32x4 GU[FN / 2][4];
+      float rwb[2][4];
       auto load_gu = [&](int i, GU& gb, GU& ub) __attribute__((always_inline)) {
+        if constexpr (FUSED) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            rwb[i & 1][b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rwr, 4u * static_cast<uint32_t>(wm * WTM + i * 32 + 8 * b + hrow), 0, 0));
+        }
 #pragma unroll
         for (int jp = 0; jp < FN / 2; ++jp)
 #pragma unroll
@@ -1127,6 +1175,10 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
               quad_transpose(da[j], lane);
             }
             pair_cols8(da[0], da[1], lane, d8);
+            if constexpr (FUSED) {
+#pragma unroll
+              for (int q = 0; q < 8; ++q) d8[q] *= rwb[i & 1][b];
+            }
             const u32x4 gw = gc[jp][b], uw = uc[jp][b];
             const uint32_t gwv[4] = {gw.x, gw.y, gw.z, gw.w}, uwv[4] = {uw.x, uw.y, uw.z, uw.w};
             uint32_t dgp[4], dup[4];
@@ -1221,15 +1273,15 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   int L = lo + slot;
   if (L < hi) {
     set_tile_and_offsets(L);
-    if constexpr (GATHER_B) {
+    if constexpr (GATHER_K) {
       const uint32_t tk0 = load_tok(0), tk1 = load_tok(1), tk2 = load_tok(2);
       tkA = load_tok(3);
       tkB = load_tok(4);
-      gather_boff(tk0, 0);
+      gather_off(tk0, 0);
       issue(0, lds0);
-      gather_boff(tk1, 1);
+      gather_off(tk1, 1);
       issue(1, lds1);
-      gather_boff(tk2, 2);
+      gather_off(tk2, 2);
       issue(2, lds2);
     } else {
       issue(0, lds0);
@@ -1302,11 +1354,11 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   }
 }
 
-template <int MODE, bool FUSED, bool F8>
+template <int MODE, bool FUSED, bool F8, bool AW>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(
     Params P) {
   MOE_GEMM_SMEM
-  gemm_tiles<MODE, FUSED, F8>(P, blockIdx.x, gridDim.x, sm);
+  gemm_tiles<MODE, FUSED, F8, AW>(P, blockIdx.x, gridDim.x, sm);
 }
 
 // Two independent GEMMs of the backward in one persistent launch: a data
@@ -1316,11 +1368,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
 // so only the launch's end has a tail. (Half the workgroups starting on B
 // was measured too and was slower: each XCD then works on tiles twice as
 // far apart, whose operands share its L2 less.)
-template <int MA, int MB, bool FB>
+template <int MA, int MB, bool FA, bool FB>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void
 grouped_gemm_pair_kernel(Params PA, Params PB) {
   MOE_GEMM_SMEM
-  gemm_tiles<MA, false>(PA, blockIdx.x, gridDim.x, sm);
+  gemm_tiles<MA, FA>(PA, blockIdx.x, gridDim.x, sm);
   __syncthreads();  // the tables and stages are B's now
   gemm_tiles<MB, FB>(PB, blockIdx.x, gridDim.x, sm);
 }
@@ -1413,10 +1465,10 @@ int persistent_grid() {
   return cached;
 }
 
-template <int MODE, bool FUSED = false, bool F8 = false>
+template <int MODE, bool FUSED = false, bool F8 = false, bool AW = false>
 hipError_t run(const Params& p, hipStream_t st) {
   const int grid = persistent_grid();
-  grouped_gemm_kernel<MODE, FUSED, F8><<<grid, NT, 0, st>>>(p);
+  grouped_gemm_kernel<MODE, FUSED, F8, AW><<<grid, NT, 0, st>>>(p);
   hipError_t err = hipGetLastError();
   if constexpr (grouped_k(MODE)) {
     if (err != hipSuccess) return err;
@@ -1425,10 +1477,10 @@ hipError_t run(const Params& p, hipStream_t st) {
   return err;
 }
 
-template <int MA, int MB, bool FB = false>
+template <int MA, int MB, bool FA = false, bool FB = false>
 hipError_t run_pair(const Params& pa, const Params& pb, hipStream_t st) {
   const int grid = persistent_grid();
-  grouped_gemm_pair_kernel<MA, MB, FB><<<grid, NT, 0, st>>>(pa, pb);
+  grouped_gemm_pair_kernel<MA, MB, FA, FB><<<grid, NT, 0, st>>>(pa, pb);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_wgrad_reduce<MB>(pb, grid, st);
@@ -1450,6 +1502,7 @@ Params make_params(const moe_shape& s, const GemmArgs& g) {
   p.out0 = static_cast<bf16_t*>(g.out0);
   p.out1 = static_cast<bf16_t*>(g.out1);
   p.out2 = static_cast<bf16_t*>(g.out2);
+  p.out3 = static_cast<bf16_t*>(g.out3);
   p.dw0 = g.dw0;
   p.dw1 = g.dw1;
   p.accumulate = g.accumulate;
@@ -1478,13 +1531,15 @@ hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g
   switch (mode) {
     case GEMM_GATEUP:
       if (g.a_scale) return g.row_token ? run<GATEUP, true, true>(p, st) : hipErrorInvalidValue;
+      if (g.out3)  // a_w (needs row_weight)
+        return g.row_token ? run<GATEUP, true, false, true>(p, st) : run<GATEUP, false, false, true>(p, st);
       return g.row_token ? run<GATEUP, true>(p, st) : run<GATEUP>(p, st);
     case GEMM_DOWN:
       if (g.a_scale) return g.row_weight ? run<DOWN, true, true>(p, st) : hipErrorInvalidValue;
       return g.row_weight ? run<DOWN, true>(p, st) : run<DOWN>(p, st);
-    case GEMM_DGRAD_DOWN: return run<DGRAD_DOWN>(p, st);
+    case GEMM_DGRAD_DOWN: return g.row_token ? run<DGRAD_DOWN, true>(p, st) : run<DGRAD_DOWN>(p, st);
     case GEMM_DGRAD_GATEUP: return run<DGRAD_GATEUP>(p, st);
-    case GEMM_WGRAD_DOWN: return run<WGRAD_DOWN>(p, st);
+    case GEMM_WGRAD_DOWN: return g.row_token ? run<WGRAD_DOWN, true>(p, st) : run<WGRAD_DOWN>(p, st);
     case GEMM_WGRAD_GATEUP: return g.row_token ? run<WGRAD_GATEUP, true>(p, st) : run<WGRAD_GATEUP>(p, st);
   }
   return hipErrorInvalidValue;
@@ -1493,9 +1548,13 @@ hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g
 hipError_t launch_gemm_pair_bf16(GemmMode ma, GemmMode mb, const moe_shape& s, const GemmArgs& ga, const GemmArgs& gb,
                                  hipStream_t st) {
   const Params pa = make_params(s, ga), pb = make_params(s, gb);
-  if (ma == GEMM_DGRAD_DOWN && mb == GEMM_WGRAD_DOWN) return run_pair<DGRAD_DOWN, WGRAD_DOWN>(pa, pb, st);
+  if (ma == GEMM_DGRAD_DOWN && mb == GEMM_WGRAD_DOWN) {
+    if ((ga.row_token == nullptr) != (gb.row_token == nullptr)) return hipErrorInvalidValue;
+    return ga.row_token ? run_pair<DGRAD_DOWN, WGRAD_DOWN, true, true>(pa, pb, st)
+                        : run_pair<DGRAD_DOWN, WGRAD_DOWN>(pa, pb, st);
+  }
   if (ma == GEMM_DGRAD_GATEUP && mb == GEMM_WGRAD_GATEUP)
-    return gb.row_token ? run_pair<DGRAD_GATEUP, WGRAD_GATEUP, true>(pa, pb, st)
+    return gb.row_token ? run_pair<DGRAD_GATEUP, WGRAD_GATEUP, false, true>(pa, pb, st)
                         : run_pair<DGRAD_GATEUP, WGRAD_GATEUP>(pa, pb, st);
   return hipErrorInvalidValue;
 }

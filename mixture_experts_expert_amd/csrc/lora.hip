@@ -20,6 +20,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Raw buffer loads: a wavefront-uniform base and byte range; a lane whose
@@ -73,10 +75,18 @@ __device__ __forceinline__ float bf16f(bf16_t v) { return __uint_as_float(static
 // issued during the previous tile's epilogue. NS = ceil(r / 16) reduction
 // steps. w_out may be w: every element is read and written by the same
 // thread.
-template <int NS>
-__global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, float s, const bf16_t* w,
+//
+// FP8W: the frozen W arrives as E4M3 codes [E][N][K] with one E8M0 scale
+// per row (w8 [E][N], 2^(c - 127)): each element is decoded to fp32 (the
+// hardware conversion, exact) and multiplied by its row's power of two
+// (exact) before the add, so W' = bf16(deq(W) + s B A) with the same single
+// rounding as the bf16 form.
+template <int NS, bool FP8W>
+__global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, float s, const void* wv_in,
+                                                         const uint8_t* __restrict__ w8,
                                                          const bf16_t* __restrict__ a, const bf16_t* __restrict__ b,
                                                          bf16_t* w_out) {
+  const bf16_t* w = static_cast<const bf16_t*>(wv_in);
   __shared__ __attribute__((aligned(16))) float lds[kMT * kStageRow];
   bf16_t* at = reinterpret_cast<bf16_t*>(lds);  // A^T [128][kLdsRow], then the fp32 stage [128][kStageRow]
   const int e = blockIdx.z;
@@ -111,9 +121,15 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
   const bf16_t* be = b + static_cast<int64_t>(e) * N * r;
   const bool cok = c0 + rcol < K;
   bf16x8 fb[2][NS];
-  uint4 wv[2][kMT / 16];  // W row runs of the current and the next row tile
-  const rsrc_t rw = make_rsrc(w + wbase, 2 * N * K), rb = make_rsrc(be, 2 * N * r);
-  auto load_tile = [&](int nt, uint4 (&wt)[kMT / 16]) __attribute__((always_inline)) {
+  // W row runs of the current and the next row tile: 8 bf16 (16 bytes) or
+  // 8 E4M3 codes (8 bytes) per thread and pass, and (FP8W) the row's scale.
+  typedef std::conditional_t<FP8W, uint2, uint4> WRun;
+  WRun wv[2][kMT / 16];
+  int wsc[2][kMT / 16];
+  const rsrc_t rw = FP8W ? make_rsrc(static_cast<const uint8_t*>(wv_in) + wbase, N * K) : make_rsrc(w + wbase, 2 * N * K);
+  const rsrc_t rsc = make_rsrc(w8 + (FP8W ? static_cast<int64_t>(e) * N : 0), FP8W ? N : 0);
+  const rsrc_t rb = make_rsrc(be, 2 * N * r);
+  auto load_tile = [&](int nt, WRun (&wt)[kMT / 16], int (&sc)[kMT / 16]) __attribute__((always_inline)) {
 #pragma unroll
     for (int tn = 0; tn < 2; ++tn) {
       const int n = nt + wn * 64 + tn * 32 + l32;  // rows past N read zeros
@@ -126,10 +142,18 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
 #pragma unroll
     for (int q = 0; q < kMT / 16; ++q) {
       const int n = nt + 16 * q + rrow;
-      wt[q] = load16(rw, cok ? 2u * static_cast<uint32_t>(n * K + c0 + rcol) : kOutOfRange);
+      if constexpr (FP8W) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rw, cok ? static_cast<uint32_t>(n * K + c0 + rcol)
+                                                                     : kOutOfRange, 0, 0);
+        wt[q] = make_uint2(v.x, v.y);
+        sc[q] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b8(rsc, static_cast<uint32_t>(n), 0, 0));
+      } else {
+        wt[q] = load16(rw, cok ? 2u * static_cast<uint32_t>(n * K + c0 + rcol) : kOutOfRange);
+        sc[q] = 0;
+      }
     }
   };
-  load_tile(nbeg, wv[0]);
+  load_tile(nbeg, wv[0], wsc[0]);
 #pragma unroll
   for (int t = 0; t < kMergeRowTiles; ++t) {
     const int nt = nbeg + t * kMT;
@@ -146,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
     // The next tile's loads fly during this tile's epilogue.
     // Rows past N read zeros and are not stored: no branch, so the
     // compiler keeps these loads in flight across the epilogue's waits.
-    if (t + 1 < kMergeRowTiles) load_tile(nt + kMT, wv[(t + 1) & 1]);
+    if (t + 1 < kMergeRowTiles) load_tile(nt + kMT, wv[(t + 1) & 1], wsc[(t + 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();  // A^T (first tile) or the previous tile's stage has been read
     // Lane l holds, per block and i < 4, columns 8i + 4(l/32) .. + 3 of row l%32.
@@ -159,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
           *reinterpret_cast<float4*>(&lds[(wn * 64 + tn * 32 + l32) * kStageRow + wc * 64 + tc * 32 + 8 * i + 4 * h]) =
               make_float4(acc[tc][tn][4 * i], acc[tc][tn][4 * i + 1], acc[tc][tn][4 * i + 2], acc[tc][tn][4 * i + 3]);
     lds_barrier();
-    const uint4 (&wc_t)[kMT / 16] = wv[t & 1];
+    const WRun (&wc_t)[kMT / 16] = wv[t & 1];
 #pragma unroll
     for (int q = 0; q < kMT / 16; ++q) {
       const int n = nt + 16 * q + rrow;
@@ -167,12 +191,32 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
       const float* sp = &lds[(16 * q + rrow) * kStageRow + rcol];
       const float4 v0 = *reinterpret_cast<const float4*>(sp), v1 = *reinterpret_cast<const float4*>(sp + 4);
       const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      const uint32_t win[4] = {wc_t[q].x, wc_t[q].y, wc_t[q].z, wc_t[q].w};
+      float wf[8];
+      if constexpr (FP8W) {
+        const int X = (wsc[t & 1][q] & 0xff) - 127;  // the row's E8M0 scale
+        const uint32_t c2[2] = {wc_t[q].x, wc_t[q].y};
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c2[p]), false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c2[p]), true);
+          wf[4 * p] = ldexpf(lo.x, X);
+          wf[4 * p + 1] = ldexpf(lo.y, X);
+          wf[4 * p + 2] = ldexpf(hi.x, X);
+          wf[4 * p + 3] = ldexpf(hi.y, X);
+        }
+      } else {
+        const uint32_t win[4] = {wc_t[q].x, wc_t[q].y, wc_t[q].z, wc_t[q].w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          wf[2 * p] = __uint_as_float(win[p] << 16);
+          wf[2 * p + 1] = __uint_as_float(win[p] & 0xffff0000u);
+        }
+      }
       uint32_t o[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const float lo = __uint_as_float(win[p] << 16) + s * v[2 * p];
-        const float hi = __uint_as_float(win[p] & 0xffff0000u) + s * v[2 * p + 1];
+        const float lo = wf[2 * p] + s * v[2 * p];
+        const float hi = wf[2 * p + 1] + s * v[2 * p + 1];
         o[p] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
       }
       *reinterpret_cast<uint4*>(w_out + wbase + static_cast<int64_t>(n) * K + c0 + rcol) =
@@ -671,26 +715,38 @@ LoraLayout lora_layout(const moe_shape& s, int r) {
   return l;
 }
 
-hipError_t launch_lora_merge(int E, int N, int K, int r, float s, const void* w, const void* a, const void* b,
-                             void* w_out, hipStream_t st) {
+namespace {
+template <bool FP8W>
+hipError_t merge_launch(int E, int N, int K, int r, float s, const void* w, const uint8_t* w8, const void* a,
+                        const void* b, void* w_out, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(ceil_div(K, kMT)), static_cast<unsigned>(ceil_div(N, kMT * kMergeRowTiles)),
                   static_cast<unsigned>(E));
-  const bf16_t* wp = static_cast<const bf16_t*>(w);
   const bf16_t* ap = static_cast<const bf16_t*>(a);
   const bf16_t* bp = static_cast<const bf16_t*>(b);
   bf16_t* op = static_cast<bf16_t*>(w_out);
   switch ((r + 15) / 16) {
-    case 1: merge_kernel<1><<<grid, kThreads, 0, st>>>(N, K, r, s, wp, ap, bp, op); break;
-    case 2: merge_kernel<2><<<grid, kThreads, 0, st>>>(N, K, r, s, wp, ap, bp, op); break;
-    case 3: merge_kernel<3><<<grid, kThreads, 0, st>>>(N, K, r, s, wp, ap, bp, op); break;
-    case 4: merge_kernel<4><<<grid, kThreads, 0, st>>>(N, K, r, s, wp, ap, bp, op); break;
-    case 5: merge_kernel<5><<<grid, kThreads, 0, st>>>(N, K, r, s, wp, ap, bp, op); break;
-    case 6: merge_kernel<6><<<grid, kThreads, 0, st>>>(N, K, r, s, wp, ap, bp, op); break;
-    case 7: merge_kernel<7><<<grid, kThreads, 0, st>>>(N, K, r, s, wp, ap, bp, op); break;
-    case 8: merge_kernel<8><<<grid, kThreads, 0, st>>>(N, K, r, s, wp, ap, bp, op); break;
+    case 1: merge_kernel<1, FP8W><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
+    case 2: merge_kernel<2, FP8W><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
+    case 3: merge_kernel<3, FP8W><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
+    case 4: merge_kernel<4, FP8W><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
+    case 5: merge_kernel<5, FP8W><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
+    case 6: merge_kernel<6, FP8W><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
+    case 7: merge_kernel<7, FP8W><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
+    case 8: merge_kernel<8, FP8W><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_lora_merge(int E, int N, int K, int r, float s, const void* w, const void* a, const void* b,
+                             void* w_out, hipStream_t st) {
+  return merge_launch<false>(E, N, K, r, s, w, nullptr, a, b, w_out, st);
+}
+
+hipError_t launch_lora_merge_fp8(int E, int N, int K, int r, float s, const uint8_t* wq, const uint8_t* w8,
+                                 const void* a, const void* b, void* w_out, hipStream_t st) {
+  return merge_launch<true>(E, N, K, r, s, wq, w8, a, b, w_out, st);
 }
 
 hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraArgs& g, void* ws, hipStream_t st) {

@@ -93,6 +93,9 @@ hipError_t launch_combine(const moe_shape& s, const void* o_perm, const float* w
                           hipStream_t st);
 hipError_t launch_combine_bwd(const moe_shape& s, const void* dy, const void* o_perm, const float* w,
                               const int32_t* f2s, void* do_perm, float* gw, hipStream_t st);
+hipError_t launch_permute_rows(const moe_shape& s, const int32_t* idx, const float* w, const void* x,
+                               int32_t* counts, int32_t* offsets, int32_t* s2f, int32_t* f2s, int32_t* row_token,
+                               float* row_weight, void* x_perm, void* ws, hipStream_t st);
 hipError_t launch_permute_fused(const moe_shape& s, const int32_t* idx, const float* w, int32_t* counts,
                                 int32_t* offsets, int32_t* s2f, int32_t* f2s, int32_t* row_token, float* row_weight,
                                 void* ws, hipStream_t st);
@@ -136,11 +139,14 @@ struct GemmArgs {
   void* out0;
   void* out1;
   void* out2;
+  void* out3;   // GATEUP: a_w = bf16(row_weight[p] a[p]) (with row_weight)
   float* dw0;
   float* dw1;
   int accumulate;
-  const int32_t* row_token;  // GATEUP: row p of A, WGRAD_GATEUP: k-row p of B is row row_token[p] of x [T][H]
-  const float* row_weight;   // fused forward, DOWN: output row p scaled by row_weight[p]
+  const int32_t* row_token;  // GATEUP: row p of A, WGRAD_GATEUP: k-row p of B is row row_token[p] of x [T][H];
+                             // DGRAD_DOWN: row p of A, WGRAD_DOWN: k-row p of A is row row_token[p] of dy [T][H]
+  const float* row_weight;   // DOWN: output row p scaled by row_weight[p]; DGRAD_DOWN with row_token: dA row p
+                             // scaled by it; GATEUP with out3: a_w row p
   // fp8 GATEUP (with row_token) and DOWN (with row_weight): a and b* hold
   // E4M3 codes; E8M0 scales per sorted row of a and per weight row.
   const uint8_t* a_scale;
@@ -197,6 +203,10 @@ struct LoraArgs {
 
 hipError_t launch_lora_merge(int E, int N, int K, int r, float s, const void* w, const void* a, const void* b,
                              void* w_out, hipStream_t st);
+// The same with the frozen W as E4M3 codes wq [E][N][K] and E8M0 row scales
+// w8 [E][N]: W' = bf16(deq(wq) + s B A).
+hipError_t launch_lora_merge_fp8(int E, int N, int K, int r, float s, const uint8_t* wq, const uint8_t* w8,
+                                 const void* a, const void* b, void* w_out, hipStream_t st);
 hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraArgs& g, void* ws, hipStream_t st);
 
 }  // namespace moe

@@ -230,6 +230,19 @@ hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const void* x,
   return hipGetLastError();
 }
 
+hipError_t launch_permute_rows(const moe_shape& s, const int32_t* idx, const float* w, const void* x,
+                               int32_t* counts, int32_t* offsets, int32_t* s2f, int32_t* f2s, int32_t* row_token,
+                               float* row_weight, void* x_perm, void* ws, hipStream_t st) {
+  hipError_t err = launch_sort(s, idx, counts, offsets, s2f, f2s, w, row_token, row_weight, ws_hist(s, ws), st);
+  if (err != hipSuccess) return err;
+  const int esz = s.dtype == MOE_BF16 ? 2 : 4;
+  const int chunks = s.H * esz / 16;
+  gather_kernel<<<ceil_div(s.T, kWavesPerBlock), kThreads, 0, st>>>(s.T, s.k, chunks, f2s,
+                                                                    static_cast<const uint4*>(x),
+                                                                    static_cast<uint4*>(x_perm));
+  return hipGetLastError();
+}
+
 hipError_t launch_permute_fused(const moe_shape& s, const int32_t* idx, const float* w, int32_t* counts,
                                 int32_t* offsets, int32_t* s2f, int32_t* f2s, int32_t* row_token, float* row_weight,
                                 void* ws, hipStream_t st) {

@@ -5,25 +5,28 @@
 // they are computed in a fixed order that a CPU can reproduce bit for bit: one
 // fp32 fma chain per (token, expert) over h ascending from +0, then + bias.
 // The chain runs on the vector ALUs; a matrix-core accumulation order is not
-// specified and could not be matched. Each thread keeps 4 tokens x 4 experts
-// = 16 independent chains in flight: per h it reads one float4 of tokens and
-// one of experts from LDS for 16 FMAs (2 bytes per FMA, what LDS returns at
-// the full fp32 FMA rate), and 16 chains per lane is also the most that still
-// gives every SIMD a wavefront at T = 8192, E = 128.
+// specified and could not be matched. Each thread keeps 4 tokens x 2 experts
+// = 8 independent chains in flight: per h it reads one float4 of tokens and
+// one float2 of experts from LDS for 8 FMAs (3 bytes per FMA). A block covers
+// 64 tokens x 32 experts, so that at T = 8192, E = 128 the grid gives every
+// SIMD two wavefronts: with one, LDS returns at most about 120 bytes per clock
+// and compute unit (the reads of one wavefront stay latency-bound), which
+// caps the FMA rate at half the VALU's; with two it returns about 240, the
+// 192 that the full FMA rate needs at 3 bytes per FMA.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 constexpr int kRT = 4;              // tokens per thread
-constexpr int kRE = 4;              // experts per thread
+constexpr int kRE = 2;              // experts per thread
 constexpr int kTy = 16, kTx = 16;   // thread grid of a block
 constexpr int kTileT = kTy * kRT;   // 64 tokens per block
-constexpr int kTileE = kTx * kRE;   // 64 experts per block
+constexpr int kTileE = kTx * kRE;   // 32 experts per block
 constexpr int kHC = 64;             // h values staged per step
 constexpr int kLogitThreads = kTy * kTx;  // 256
 constexpr int kXS = kTileT + 4;     // LDS row strides (floats), 16-byte aligned
-constexpr int kWS = kTileE + 4;
+constexpr int kWS = kTileE + 2;
 
 // Staging of one kHC-wide h slice of `rows` rows into LDS as fp32 [h][row]:
 // 16-byte global loads along h (coalesced), one thread per chunk.
@@ -101,9 +104,9 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(int Tn, in
 #pragma unroll 16
     for (int hh = 0; hh < kHC; ++hh) {
       const float4 xv = *reinterpret_cast<const float4*>(xb + hh * kXS + ty * kRT);
-      const float4 wv = *reinterpret_cast<const float4*>(wb + hh * kWS + tx * kRE);
+      const float2 wv = *reinterpret_cast<const float2*>(wb + hh * kWS + tx * kRE);
       const float xa[kRT] = {xv.x, xv.y, xv.z, xv.w};
-      const float wa[kRE] = {wv.x, wv.y, wv.z, wv.w};
+      const float wa[kRE] = {wv.x, wv.y};
 #pragma unroll
       for (int i = 0; i < kRT; ++i)
 #pragma unroll
@@ -125,8 +128,8 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(int Tn, in
 #pragma unroll
     for (int j = 0; j < kRE; ++j) v[j] = (bias && e + j < E) ? acc[i][j] + bias[e + j] : acc[i][j];
     float* dst = logits + static_cast<int64_t>(t) * E + e;
-    if (e + kRE <= E && (E % 4) == 0) {
-      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+    if (e + kRE <= E && (E % 2) == 0) {
+      *reinterpret_cast<float2*>(dst) = make_float2(v[0], v[1]);
     } else {
 #pragma unroll
       for (int j = 0; j < kRE; ++j)
@@ -135,8 +138,7 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(int Tn, in
   }
 }
 
-constexpr int kMaxPerLane = 1024 / kWave;  // E <= 1024
-constexpr int kTokPerBlock = 4;            // one wave per token
+constexpr int kTokPerBlock = 4;  // one wave per token
 
 // (value, index) order of the selection: larger value first, then lower
 // index. A NaN ranks below every number, -inf included (two NaNs: the lower
@@ -147,10 +149,14 @@ __device__ __forceinline__ bool before(float v, int i, float ov, int oi) {
   return v > ov || (!(v < ov) && i < oi);
 }
 
+// NC logits per lane (E <= 64 NC): compiled per power of two up to 16, so
+// that the selection loops run over the lane's own logits only.
+template <int NC>
 __global__ __launch_bounds__(kWave* kTokPerBlock) void router_topk_kernel(int Tn, int E, int k,
                                                                           const float* __restrict__ logits,
                                                                           int32_t* __restrict__ idx,
                                                                           float* __restrict__ w) {
+  constexpr int kMaxPerLane = NC;
   __shared__ float sval[kTokPerBlock][1024];
   const int lane = threadIdx.x % kWave;
   const int wv = threadIdx.x / kWave;
@@ -252,7 +258,13 @@ hipError_t launch_route(const moe_shape& s, const void* x, const void* wr, const
         s.T, s.H, s.E, static_cast<const float*>(x), static_cast<const float*>(wr), bias, logits);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  router_topk_kernel<<<ceil_div(s.T, kTokPerBlock), kWave * kTokPerBlock, 0, st>>>(s.T, s.E, s.k, logits, idx, w);
+  const dim3 g(ceil_div(s.T, kTokPerBlock)), b(kWave * kTokPerBlock);
+  const int nc = ceil_div(s.E, kWave);
+  if (nc <= 1) router_topk_kernel<1><<<g, b, 0, st>>>(s.T, s.E, s.k, logits, idx, w);
+  else if (nc <= 2) router_topk_kernel<2><<<g, b, 0, st>>>(s.T, s.E, s.k, logits, idx, w);
+  else if (nc <= 4) router_topk_kernel<4><<<g, b, 0, st>>>(s.T, s.E, s.k, logits, idx, w);
+  else if (nc <= 8) router_topk_kernel<8><<<g, b, 0, st>>>(s.T, s.E, s.k, logits, idx, w);
+  else router_topk_kernel<16><<<g, b, 0, st>>>(s.T, s.E, s.k, logits, idx, w);
   return hipGetLastError();
 }
 

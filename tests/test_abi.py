@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(B):
     names = declared_functions()
-    assert len(names) == 31, names
+    assert len(names) == 35, names
     for n in names:
         assert hasattr(B.lib, n), n
 
@@ -72,7 +72,7 @@ def test_null_pointers_rejected(B):
     P = [FAKE] * 8
     assert B.lib.moe_permute(s, None, *P[:6], FAKE, 1 << 30, None) == 1
     assert B.lib.moe_combine(s, FAKE, FAKE, None, FAKE, None) == 1
-    assert B.lib.moe_combine_bwd(s, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == 1
+    assert B.lib.moe_combine_bwd(s, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1  # d_topk_w (do_perm may be NULL)
     assert B.lib.moe_unpermute_sum(s, FAKE, FAKE, None, None) == 1
     assert B.lib.moe_route_bwd(s, FAKE, None, FAKE, FAKE, None) == 1
     assert B.lib.moe_grouped_gemm_fwd(s, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 1
@@ -182,4 +182,24 @@ def test_noalloc_forward_rejects_on_the_host(B):
     args[2] = None  # logit_bias may be NULL: not the rejected argument
     args[0] = None  # x
     assert fn(ok, *args, None) == 1
+
+
+def test_training_without_do_perm_rejects_on_the_host(B):
+    """moe_gemm_gate_up_aw and moe_gemm_down_bwd_dy are bf16 only
+    (MOE_EUNSUPPORTED for fp32), need every operand (MOE_EINVAL) and the
+    workspace (MOE_EWORKSPACE); moe_permute_rows needs all its outputs."""
+    bf, f32 = B.shape(64, 128, 8, 2, 64, "bf16"), B.shape(64, 128, 8, 2, 64, "f32")
+    gu = B.lib.moe_gemm_gate_up_aw
+    assert gu(f32, *([FAKE] * 10), None) == 2
+    args = [FAKE] * 10
+    args[1] = None  # row_token may be NULL (x_perm rows)
+    assert gu(bf, *args[:2], None, *args[3:], None) == 1  # row_weight NULL
+    dn = B.lib.moe_gemm_down_bwd_dy
+    assert dn(f32, *([FAKE] * 10), 0, FAKE, 1 << 40, None) == 2
+    assert dn(bf, *([FAKE] * 10), 0, FAKE, 16, None) == 3  # workspace too small
+    assert dn(bf, *([FAKE] * 10), 2, FAKE, 1 << 40, None) == 1  # accumulate_dw not 0/1
+    assert dn(bf, FAKE, None, *([FAKE] * 8), 0, FAKE, 1 << 40, None) == 1  # row_token NULL
+    pr = B.lib.moe_permute_rows
+    assert pr(bf, *([FAKE] * 9), None, FAKE, 1 << 40, None) == 1  # x_perm NULL
+    assert pr(bf, *([FAKE] * 11), 16, None) == 3
 

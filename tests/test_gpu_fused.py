@@ -186,3 +186,81 @@ def test_gather_fused_training_qwen3_30b_a3b_full():
     ref = U.oracle_full(inp, True)
     for n in ["y", "dx", "dw_gate", "dw_up", "dw_down", "d_logits"]:
         U.check_output(n, U.to_np(st.buf[n]), ref, U.BF16_TOL)
+
+
+# ---- training without do_perm (dy read through the sorted rows' tokens) ----
+
+DY_SMALL = [c for c in SMALL if c.backward and c.dtype == "bf16"] + [SPLIT_K]
+FWD_SAME = ["logits", "topk_idx", "topk_w", "counts", "offsets", "sorted_to_flat", "flat_to_sorted", "g", "u", "a",
+            "o_perm", "y", "d_topk_w", "d_logits"]
+
+
+def dy_fused_stage(d: U.DevInputs, gather_fused: bool):
+    from mixture_experts_expert_amd import binding as B
+    c = d.cfg
+    return B.MoEStage(d.t["x"].shape[0], c.H, c.E, c.k, c.I, torch.bfloat16, gather_fused=gather_fused,
+                      dy_fused=True)
+
+
+def check_dy_fused(d: U.DevInputs, st, plain, ref, tolerance):
+    """Forward, d_topk_w and d_logits bit-identical to the do_perm path (same
+    kernels and sums); a_w, dx_perm, dx and the weight gradients within
+    tolerance of the oracle."""
+    c = d.cfg
+    for n in FWD_SAME:
+        assert same_tensor(st.buf[n], plain.buf[n]), n
+    check_fused_indices(st.buf, c.k)
+    assert "do_perm" not in st.buf
+    # a_w = bf16(w a): the oracle's fp32 a times the sorted row's routing weight
+    s2f = ref["sorted_to_flat"].astype(np.int64)
+    a_w = ref["a"].astype(np.float64) * ref["topk_w"].reshape(-1)[s2f][:, None]
+    U.check_close("a_w", U.to_np(st.buf["a_w"]), a_w, tolerance)
+    for n in ["dx_perm", "dx", "dw_gate", "dw_up", "dw_down"]:
+        U.check_output(n, U.to_np(st.buf[n]), ref, tolerance)
+    empty = np.nonzero(ref["counts"] == 0)[0]
+    if len(empty):
+        idx = torch.from_numpy(empty).cuda()
+        for n in ["dw_gate", "dw_up", "dw_down"]:
+            assert not st.buf[n][idx].any().item(), n
+
+
+@pytest.mark.parametrize("gather", [False, True], ids=["x_perm", "gathered_x"])
+@pytest.mark.parametrize("cfg", DY_SMALL, ids=lambda c: c.name)
+def test_dy_fused_training_small(cfg, gather):
+    """Training step without do_perm (moe_permute_rows or moe_permute_fused,
+    moe_gemm_gate_up_aw, moe_combine_bwd without do_perm,
+    moe_gemm_down_bwd_dy): against the do_perm path and the oracle, then
+    accumulate_dw adding a second pass onto the first."""
+    U.say(f"[dy-fused training] {cfg} gathered x={gather}")
+    U.begin(f"dy_fused{'_gathered' if gather else ''}.{cfg.name}", f"{cfg} seed 2, training without do_perm")
+    inp = synth.make_inputs(cfg, seed=2, with_dy=True)
+    d = U.DevInputs(inp)
+    plain = U.run_stage(d, True)
+    st = U.run_stage(d, True, stage=dy_fused_stage(d, gather))
+    ref = U.oracle_full(inp, True)
+    check_dy_fused(d, st, plain, ref, U.BF16_TOL)
+    first = {n: st.buf[n].clone() for n in ["dw_gate", "dw_up", "dw_down", "dx"]}
+    U.run_stage(d, True, stage=st)  # a rerun: the same bits
+    for n, v in first.items():
+        assert same_tensor(st.buf[n], v), (n, "rerun")
+    st.backward(d.t["dy"], accumulate_dw=True)
+    torch.cuda.synchronize()
+    for n in ["dw_gate", "dw_up", "dw_down"]:
+        U.check_close(n + " x2", U.to_np(st.buf[n]), 2.0 * U.to_np(first[n]), 1e-6)
+
+
+@pytest.mark.timeout(600)
+def test_dy_fused_training_qwen3_30b_a3b_full():
+    """T=8192, H=2048, E=128, k=8, I=768, training without do_perm: every
+    element against the oracle, and bit-identical to the do_perm path where
+    the arithmetic is the same (forward, d_topk_w, d_logits)."""
+    cfg = synth.CONFIGS["qwen3_30b_a3b_train"]
+    U.say(f"[dy-fused training] {cfg}")
+    U.begin("dy_fused." + cfg.name, f"{cfg} seed 0, training without do_perm")
+    inp = synth.make_inputs(cfg, seed=0)
+    d = U.DevInputs(inp)
+    plain = U.run_stage(d, True)
+    st = U.run_stage(d, True, stage=dy_fused_stage(d, False))
+    U.say("  oracle on all tokens")
+    ref = U.oracle_full(inp, True)
+    check_dy_fused(d, st, plain, ref, U.BF16_TOL)

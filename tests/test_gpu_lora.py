@@ -186,3 +186,108 @@ def test_lora_merges_on_a_second_stream_same_bits():
         assert torch.equal(a, b_), n
     for a, b_ in zip(ref_w, got_w):
         assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
+
+
+# ---- adapters over 8-bit frozen experts (QLoRA-style) ----
+
+def test_merge_fp8_decodes_every_code():
+    """B = 0: W' = bf16(deq(wq)) must be the decoded code times the row's
+    power of two, exactly (every finite E4M3 code, scales from 2^-20 to 2^10)."""
+    from mixture_experts_expert_amd import binding as B
+    from oracle import fp8 as F8
+    U.say("[lora merge fp8] every code")
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    E, N, K, r = 2, 16, codes.size + 2, 8  # K % 8 == 0
+    rng = np.random.default_rng(3)
+    wq = np.stack([np.stack([np.roll(np.r_[codes, codes[:2]], n) for n in range(N)]) for _ in range(E)])
+    e8 = (127 + rng.integers(-20, 11, size=(E, N))).astype(np.uint8)
+    a = np.zeros((E, r, K), np.uint16)
+    b = np.zeros((E, N, r), np.uint16)
+    out = torch.empty(E, N, K, dtype=torch.bfloat16, device="cuda")
+    B.moe_lora_merge_fp8(E, N, K, r, 1.0, torch.from_numpy(wq).cuda(), torch.from_numpy(e8).cuda(), U.to_dev(a),
+                         U.to_dev(b), out)
+    torch.cuda.synchronize()
+    want = F8.dequantize_rows(wq.reshape(E * N, K), e8.reshape(E * N)).reshape(E, N, K)
+    assert np.array_equal(U.to_np(out).astype(np.float64), want)
+
+
+@pytest.mark.parametrize("E,N,K,r", [(3, 200, 264, 8), (2, 129, 136, 72), (4, 257, 520, 40), (2, 70, 2048, 128)])
+def test_merge_fp8(E, N, K, r):
+    """W' = bf16(deq(wq) + s B A) against the float64 oracle on its own
+    quantisation of the same weights (the GPU quantiser's codes equal it)."""
+    from mixture_experts_expert_amd import binding as B
+    from oracle import fp8 as F8
+    U.say(f"[lora merge fp8] E={E} N={N} K={K} r={r}")
+    rng = np.random.default_rng(E * 131 + N + K + r)
+    w = synth.bf16_round(np.float32(0.02) * rng.standard_normal((E, N, K), dtype=np.float32))
+    a = synth.bf16_round(np.float32(0.02) * rng.standard_normal((E, r, K), dtype=np.float32))
+    b = synth.bf16_round(np.float32(0.02) * rng.standard_normal((E, N, r), dtype=np.float32))
+    s = 1.25
+    wq = torch.empty(E, N, K, dtype=torch.uint8, device="cuda")
+    e8 = torch.empty(E, N, dtype=torch.uint8, device="cuda")
+    B.moe_quantize_fp8_rows(E * N, K, U.to_dev(w), wq, e8)
+    out = torch.full((E, N, K), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.moe_lora_merge_fp8(E, N, K, r, s, wq, e8, U.to_dev(a), U.to_dev(b), out)
+    torch.cuda.synchronize()
+    rq, re8 = F8.quantize_weights(widen(w))
+    assert np.array_equal(wq.cpu().numpy(), rq) and np.array_equal(e8.cpu().numpy(), re8)
+    got = U.to_np(out).astype(np.float64)
+    deq = LO.dequantize_weights(rq, re8)
+    ref = LO.merge_fp8(rq, re8, widen(a), widen(b), s)
+    lowrank = np.abs(ref - deq)
+    bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -22 * (np.abs(deq) + lowrank)
+    assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) - bound))
+    frac = float(np.mean(got == widen(synth.bf16_round(ref.astype(np.float32)))))
+    U.say(f"  equal to the nearest bf16: {frac:.5f}")
+    assert frac >= 0.999
+
+
+def fp8_lora_check(cfg, r, s, seed, full=False):
+    from mixture_experts_expert_amd import binding as B
+    from oracle import fp8 as F8
+    inp = synth.make_inputs(cfg, seed=seed, with_dy=True)
+    adapters = synth.make_adapters(cfg, r, seed=seed)
+    d = U.DevInputs(inp)
+    w8 = B.FP8Weights(d.t["w_gate"], d.t["w_up"], d.t["w_down"])
+    ad = {n: U.to_dev(adapters[n]) for n in NAMES}
+    T = d.t["x"].shape[0]
+    st = B.LoRAStage(T, cfg.H, cfg.E, cfg.k, cfg.I, r, s)
+    st.forward(d.t["x"], d.t["w_router"], w8.gate, w8.up, w8.down, ad, d.bias)
+    st.backward(d.t["dy"])
+    torch.cuda.synchronize()
+    ref_r = U.oracle_route(inp)
+    U.check_routing(st, ref_r)
+    wdeq = [LO.dequantize_weights(*F8.quantize_weights(inp.f32(n).astype(np.float64)))
+            for n in ["w_gate", "w_up", "w_down"]]
+    x, dy = inp.f32("x").astype(np.float64), inp.f32("dy").astype(np.float64)
+    if full:
+        U.say("  adapter oracle on all tokens")
+    ref = LO.forward_backward(x, dy, ref_r["topk_idx"], ref_r["topk_w"].astype(np.float64), *wdeq,
+                              {n: widen(adapters[n]) for n in NAMES}, s)
+    check_tokens(st, ref_r, ref)
+    counts = ref_r["counts"]
+    for n in NAMES:
+        got = U.to_np(st.buf["d" + n])
+        U.check_close("d" + n, got, ref["d" + n], U.BF16_TOL)
+        assert not np.any(got[counts == 0]), ("experts without rows", n)
+
+
+@pytest.mark.parametrize("cfg,r", [SMALL_LORA[1], SMALL_LORA[2], SMALL_LORA[4]],
+                         ids=[f"{c.name}-r{r}" for c, r in [SMALL_LORA[1], SMALL_LORA[2], SMALL_LORA[4]]])
+def test_lora_fp8_base_small(cfg, r):
+    """The adapter step over E4M3 frozen experts against the float64 oracle
+    on the dequantised weights: routing bit-exact, y, dx, d_topk_w, d_logits
+    and the six adapter gradients within 2e-2."""
+    U.say(f"[lora fp8 base] {cfg} r={r}")
+    U.begin(f"lora_fp8_r{r}.{cfg.name}", f"{cfg} seed 8, adapters rank {r} over E4M3 frozen weights")
+    fp8_lora_check(cfg, r, 2.0 if r == 64 else 0.75, 8)
+
+
+@pytest.mark.timeout(900)
+def test_lora_fp8_base_qwen3_30b_a3b_full():
+    """T=8192, H=2048, E=128, k=8, I=768, r=64, s=2 over E4M3 frozen experts:
+    every element."""
+    cfg = synth.CONFIGS["qwen3_30b_a3b_train"]
+    U.say(f"[lora fp8 base] {cfg} r=64")
+    U.begin("lora_fp8_r64." + cfg.name, f"{cfg} seed 0, adapters rank 64, scale 2, over E4M3 frozen weights")
+    fp8_lora_check(cfg, 64, 2.0, 0, full=True)
