@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void blockdiag_t_kernel(int C, int r, int
 }
 
 // Rank-wide projections: out[p][n] = sum_k rows[p][k] W[e][n][k] over each
-// expert e's sorted rows p, W [E][N][K], N a multiple of 64 up to 32 NB,
+// expert e's sorted rows p, W [E][N][K], N a multiple of 32 up to 32 NB,
 // K % 64 == 0; bf16 in and out, fp32 sums. One launch runs up to four such
 // jobs over the same experts (the four projections of the adapter
 // gradients), so that their tiles fill the chip together instead of each
@@ -488,6 +488,7 @@ hipError_t projections(const moe_shape& s, int nmax, const int32_t* offsets, con
   // >= the tile count (each job: at most M / 128 + E tiles), a multiple of 8.
   const unsigned grid = static_cast<unsigned>(8 * ((jobs.n * (M / kPR + s.E) + 8) / 8));
   switch (nmax / 32) {
+    case 2: proj_kernel<2><<<grid, kThreads, 0, st>>>(s.E, offsets, jobs); break;
     case 4: proj_kernel<4><<<grid, kThreads, 0, st>>>(s.E, offsets, jobs); break;
     case 8: proj_kernel<8><<<grid, kThreads, 0, st>>>(s.E, offsets, jobs); break;
     default: return hipErrorInvalidValue;
@@ -511,9 +512,18 @@ hipError_t projections(const moe_shape& s, int nmax, const int32_t* offsets, con
 // the matrix-core fragments (8 consecutive rows of one column) come out of
 // transposed LDS reads (frag_tr); two chunks are in flight. MFMA rows are chosen so that a
 // lane ends with four consecutive output elements of one output row (the
-// rank side for dB, the long side for dA): 16-byte stores. The tile list is
-// static (every expert, rows or not, gets its tiles: an expert without rows
-// writes zeros).
+// rank side for dB, the long side for dA): 16-byte stores. Every expert,
+// rows or not, gets its tiles (an expert without rows writes zeros).
+//
+// Long experts are split: the launch is persistent (one block per CU), and
+// an expert whose row chunks exceed cap = max(kOuterMinChunks, W / (2 grid))
+// (W the launch's total work in chunk-tiles) has its rows cut into
+// ceil(chunks / cap) pieces of about equal length, each a tile of its own.
+// Piece 0 writes the gradient; later pieces write fp32 partial tiles to the
+// workspace, which outer_reduce_kernel adds in piece order afterwards (no
+// atomics: the result does not depend on timing). Under skewed routing the
+// few experts holding a large share of the rows then no longer leave their
+// tiles running long after the others.
 constexpr int kOC = 64;         // rows per reduction chunk
 // LDS rows of a chunk ([row][column], as loaded): 128 long-side columns, or
 // 32 NB rank-side columns, padded so that a row's stride is 16 or 48 dwords
@@ -553,25 +563,162 @@ struct OuterJobs {
   int n;
 };
 
+constexpr int kOuterMinChunks = 16;     // a piece of a split expert: at least 16 chunks of 64 rows
+
+// Persistent grid of the outer products: one block per compute unit.
+int outer_grid() {
+  static int cached = 0;
+  if (cached == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    cached = cus;
+  }
+  return cached;
+}
+constexpr int kOuterPartFloats = 128 * 256;  // one partial tile (128 long-side x up to 256 rank-side)
+
+// The split plan, made once per launch by outer_plan_kernel (one block) into
+// the workspace. Expert e has chunks(e) = ceil(rows / kOC) row chunks and
+// pieces(e) = ceil(chunks / cap) when chunks > cap (else 1), each piece of
+// ceil(chunks / pieces) chunks; a tile is (expert, piece, job, 128-column
+// block). The experts are taken longest first (so the split ones come first
+// and the hardware starts the longest tiles earliest); tile t of the launch
+// is piece g = t / tpe of that order, column index t % tpe over the jobs'
+// column blocks (tpe of them). A later piece of a split expert writes a
+// partial tile (slot) and each (split expert, job, column block) is a unit
+// of the reduction, which adds its pieces' slots in piece order.
+struct OuterDesc {
+  int job, e, piece, pieces, cb, slot;
+};
+struct OuterUnit {
+  int job, e, cb, slot1, pieces;  // piece p >= 1 in slot slot1 + (p - 1) tpe
+};
+__device__ __forceinline__ int outer_pieces(int steps, int cap) { return steps > cap ? (steps + cap - 1) / cap : 1; }
+
+constexpr int kPlanThreads = 1024;  // one expert per thread (E <= 1024)
+
+// Block-wide exclusive scan of v (thread q) into out[0 .. n] (out[n] the
+// total): a wavefront scan through shuffles, then the wavefronts' totals.
+__device__ __forceinline__ void plan_scan(int v, int* out, int* wtot, int n, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += x;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanThreads / 64; ++w) {
+    before += w < wave ? wtot[w] : 0;
+    total += wtot[w];
+  }
+  if (tid < n) out[tid] = before + incl - v;
+  if (tid == 0) out[n] = total;
+  __syncthreads();  // out complete; wtot free for the next scan
+}
+
+// Largest q < n with a[q] <= v (a non-decreasing, a[0] <= v).
+__device__ __forceinline__ int plan_find(const int* a, int n, int v) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a[mid] <= v) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Job and column block of column index c (< tpe) over the jobs.
+__device__ __forceinline__ void plan_column(const OuterJobs& jobs, int c, int& job, int& cb) {
+  job = 0;
+  for (; job < jobs.n - 1; ++job) {
+    const int n = (jobs.job[job].nl + 127) / 128;
+    if (c < n) break;
+    c -= n;
+  }
+  cb = c;
+}
+
+// hdr[0] = tiles, hdr[1] = reduction units; desc [tiles], units [units].
+__global__ __launch_bounds__(kPlanThreads) void outer_plan_kernel(int E, const int32_t* __restrict__ offsets,
+                                                                  OuterJobs jobs, int grid, int* __restrict__ hdr,
+                                                                  OuterDesc* __restrict__ desc,
+                                                                  OuterUnit* __restrict__ units) {
+  __shared__ int key[kPlanThreads], order[kPlanThreads], wtot[kPlanThreads / 64];
+  __shared__ int pst[kPlanThreads + 1], qst[kPlanThreads + 1], sst[kPlanThreads + 1];
+  const int tid = threadIdx.x;
+  const int chunks = tid < E ? (offsets[tid + 1] - offsets[tid] + kOC - 1) / kOC : 0;
+  // Experts by chunk count, descending, ties to the lower index: expert e's
+  // position is the number of keys above its own.
+  const int mykey = chunks * 2048 + (2047 - tid);
+  key[tid] = mykey;
+  plan_scan(chunks, pst, wtot, E, tid);  // (its barriers publish key too)
+  int tpe = 0;
+  for (int j = 0; j < jobs.n; ++j) tpe += (jobs.job[j].nl + 127) / 128;
+  // cap >= work / (2 grid): fewer than 2 grid partial tiles at any shape
+  const int64_t work = static_cast<int64_t>(tpe) * max(pst[E], E);
+  const int cap = max(kOuterMinChunks, static_cast<int>((work + 2 * grid - 1) / (2 * grid)));
+  if (tid < E) {
+    int pos = 0;
+    for (int q = 0; q < E; ++q) pos += key[q] > mykey ? 1 : 0;
+    order[pos] = tid;
+  }
+  __syncthreads();
+  // From here on, thread q stands for the expert at position q.
+  const int eq = tid < E ? order[tid] : 0;
+  const int cq = tid < E ? (offsets[eq + 1] - offsets[eq] + kOC - 1) / kOC : 0;
+  const int pieces = tid < E ? outer_pieces(cq, cap) : 0;
+  plan_scan(pieces, pst, wtot, E, tid);
+  plan_scan(tid < E ? pieces - 1 : 0, qst, wtot, E, tid);
+  plan_scan(pieces > 1 ? 1 : 0, sst, wtot, E, tid);  // the split experts: the first sst[E] positions
+  const int tiles = pst[E] * tpe, nunits = sst[E] * tpe;
+  for (int t = tid; t < tiles; t += kPlanThreads) {
+    const int g = t / tpe, c = t - g * tpe;
+    const int q = plan_find(pst, E, g);
+    const int np = pst[q + 1] - pst[q], p = g - pst[q];
+    int job, cb;
+    plan_column(jobs, c, job, cb);
+    desc[t] = OuterDesc{job, order[q], p, np, cb, p > 0 ? (qst[q] + p - 1) * tpe + c : -1};
+  }
+  for (int u = tid; u < nunits; u += kPlanThreads) {
+    const int q = u / tpe, c = u - q * tpe;
+    int job, cb;
+    plan_column(jobs, c, job, cb);
+    units[u] = OuterUnit{job, order[q], cb, qst[q] * tpe + c, pst[q + 1] - pst[q]};
+  }
+  if (tid == 0) {
+    hdr[0] = tiles;
+    hdr[1] = nunits;
+  }
+}
+
 template <int NB, bool TRANS>
-__global__ __launch_bounds__(kThreads) void outer_kernel(int E, const int32_t* __restrict__ offsets, OuterJobs jobs) {
+__global__ __launch_bounds__(kThreads) void outer_kernel(int E, const int32_t* __restrict__ offsets, OuterJobs jobs,
+                                                         const int* __restrict__ hdr,
+                                                         const OuterDesc* __restrict__ descs,
+                                                         float* __restrict__ part) {
   constexpr int kOS = orow_s(NB);
   __shared__ __attribute__((aligned(16))) bf16_t lt[2][kOC * kOLw];
   __shared__ __attribute__((aligned(16))) bf16_t st[2][kOC * kOS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  // Static tile list: job-major, then expert, then 128-column block.
-  int t = blockIdx.x, jb = 0;
-  for (; jb < jobs.n; ++jb) {
-    const int nt = E * ((jobs.job[jb].nl + 127) / 128);
-    if (t < nt) break;
-    t -= nt;
-  }
-  if (jb >= jobs.n) return;  // uniform over the block
-  const OuterJob& J = jobs.job[jb];
-  const int tpe = (J.nl + 127) / 128;
-  const int e = t / tpe, i0 = (t - e * tpe) * 128;
-  const int r0 = offsets[e], rows = offsets[e + 1] - r0;
-
+  if (static_cast<int>(blockIdx.x) >= hdr[0]) return;  // uniform over the block
+  const OuterDesc d = descs[blockIdx.x];
+  const OuterJob& J = jobs.job[d.job];
+  const int e = d.e, i0 = d.cb * 128;
+  (void)E;
+  // The piece's rows: pieces of ceil(chunks / pieces) chunks each (the last
+  // one may be shorter, or empty: it then writes zeros).
+  const int eb = offsets[e], erows = offsets[e + 1] - eb;
+  const int per = ((erows + kOC - 1) / kOC + d.pieces - 1) / d.pieces;
+  const int first = d.piece * per * kOC;
+  const int r0 = eb + min(first, erows);
+  const int rows = max(0, min(erows, first + per * kOC) - first);
+  float* const pdst = d.slot >= 0 ? part + static_cast<int64_t>(d.slot) * kOuterPartFloats : nullptr;
   // Pieces of a chunk: L: row q / 16, columns i0 + 8 (q % 16) .. + 7; S: row
   // q / (4 NB), columns 8 (q % (4 NB)) .. + 7. Columns past the window read
   // zeros (out of range); rows past the expert's fall outside the buffer range.
@@ -649,6 +796,8 @@ __global__ __launch_bounds__(kThreads) void outer_kernel(int E, const int32_t* _
   }
 
   // Lane l holds D[8q + 4(l/32) + u][l%32], u < 4, of each 32 x 32 block nb.
+  // A later piece of a split expert writes its partial tile instead, in the
+  // same orientation: [i - i0][j] (row 256) or, TRANS, [j][i - i0] (row 128).
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -659,6 +808,10 @@ __global__ __launch_bounds__(kThreads) void outer_kernel(int E, const int32_t* _
         // MFMA rows: long side i; columns: rank side j.
         const int i = i0 + wave * 32 + a, j = nb * 32 + l32;
         if (i >= J.nl || j >= J.ns) continue;
+        if (pdst) {
+          *reinterpret_cast<float4*>(pdst + j * 128 + (i - i0)) = v;
+          continue;
+        }
         const bool second = j >= J.ns1;
         const int jr = second ? j - J.ns1 : j;  // row of out or out1
         if (jr >= J.rows1) continue;
@@ -668,30 +821,121 @@ __global__ __launch_bounds__(kThreads) void outer_kernel(int E, const int32_t* _
         // MFMA rows: rank side j; columns: long side i.
         const int j = nb * 32 + a, i = i0 + wave * 32 + l32;
         if (i >= J.nl || j >= J.ns) continue;
+        if (pdst) {
+          *reinterpret_cast<float4*>(pdst + (i - i0) * 256 + j) = v;
+          continue;
+        }
         *reinterpret_cast<float4*>(J.out + (static_cast<int64_t>(e) * J.nl + i) * J.ns + j) = v;
       }
     }
 }
 
+// Adds the partial tiles of a split expert into its adapter gradient, in
+// piece order (piece 0 is already there): one block per reduction unit
+// (job, split expert, column block) of the plan.
 template <bool TRANS>
-hipError_t outer_products(int E, int nb, const int32_t* offsets, const OuterJobs& jobs, hipStream_t st) {
-  int tiles = 0;
-  for (int j = 0; j < jobs.n; ++j) tiles += E * ((jobs.job[j].nl + 127) / 128);
-  if (tiles == 0) return hipSuccess;
+__global__ __launch_bounds__(kThreads) void outer_reduce_kernel(OuterJobs jobs, int tpe, const int* __restrict__ hdr,
+                                                                const OuterUnit* __restrict__ units,
+                                                                const float* __restrict__ part) {
+  if (static_cast<int>(blockIdx.x) >= hdr[1]) return;  // uniform over the block
+  const OuterUnit U = units[blockIdx.x];
+  const OuterJob& J = jobs.job[U.job];
+  const int e = U.e, i0 = U.cb * 128;
+  // Four consecutive elements per thread along the contiguous side (i for
+  // TRANS, j otherwise; nl and ns are multiples of 8).
+  constexpr int kU = 4;  // groups per thread and pass, their loads in flight together
+  const int groups = 32 * J.ns;  // 128 x ns elements
+  for (int g0 = threadIdx.x; g0 < groups; g0 += kU * kThreads) {
+    float* dst[kU];
+    int local[kU];
+    float4 sum[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int g = g0 + u * kThreads;
+      dst[u] = nullptr;
+      if (g >= groups) continue;
+      int i, j;
+      if constexpr (TRANS) {
+        j = g / 32;
+        i = i0 + 4 * (g - j * 32);
+      } else {
+        const int per = J.ns / 4;
+        i = i0 + g / per;
+        j = 4 * (g - (g / per) * per);
+      }
+      if (i >= J.nl) continue;
+      if constexpr (TRANS) {
+        const bool second = j >= J.ns1;
+        const int jr = second ? j - J.ns1 : j;
+        if (jr >= J.rows1) continue;
+        dst[u] = (second ? J.out1 : J.out) + (static_cast<int64_t>(e) * J.rows1 + jr) * J.nl + i;
+      } else {
+        dst[u] = J.out + (static_cast<int64_t>(e) * J.nl + i) * J.ns + j;
+      }
+      local[u] = TRANS ? j * 128 + (i - i0) : (i - i0) * 256 + j;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (dst[u]) sum[u] = *reinterpret_cast<const float4*>(dst[u]);
+    for (int p = 1; p < U.pieces; ++p) {
+      const float* src = part + static_cast<int64_t>(U.slot1 + (p - 1) * tpe) * kOuterPartFloats;
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (dst[u]) {
+          const float4 v = *reinterpret_cast<const float4*>(src + local[u]);
+          sum[u].x += v.x;
+          sum[u].y += v.y;
+          sum[u].z += v.z;
+          sum[u].w += v.w;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (dst[u]) *reinterpret_cast<float4*>(dst[u]) = sum[u];
+  }
+}
+
+// Workspace of one outer-product launch: the plan (header, tile
+// descriptors, reduction units) and the partial tiles.
+struct OuterSpace {
+  int* hdr;
+  OuterDesc* desc;
+  OuterUnit* units;
+  float* part;
+};
+
+template <bool TRANS>
+hipError_t outer_products(int E, int nb, const int32_t* offsets, const OuterJobs& jobs, const OuterSpace& w,
+                          hipStream_t st) {
+  const int grid = outer_grid();
+  int tiles_per_expert = 0;
+  for (int j = 0; j < jobs.n; ++j) tiles_per_expert += (jobs.job[j].nl + 127) / 128;
+  // At most one tile per (job, expert, column block) plus fewer than 2 grid
+  // partial tiles; blocks past the plan's count return at once.
+  const unsigned tiles = static_cast<unsigned>(tiles_per_expert * E + 2 * grid);
+  outer_plan_kernel<<<1, kPlanThreads, 0, st>>>(E, offsets, jobs, grid, w.hdr, w.desc, w.units);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
   switch (nb) {
-    case 1: outer_kernel<1, TRANS><<<tiles, kThreads, 0, st>>>(E, offsets, jobs); break;
-    case 2: outer_kernel<2, TRANS><<<tiles, kThreads, 0, st>>>(E, offsets, jobs); break;
-    case 3: outer_kernel<3, TRANS><<<tiles, kThreads, 0, st>>>(E, offsets, jobs); break;
-    case 4: outer_kernel<4, TRANS><<<tiles, kThreads, 0, st>>>(E, offsets, jobs); break;
-    case 8: outer_kernel<8, TRANS><<<tiles, kThreads, 0, st>>>(E, offsets, jobs); break;
+    case 1: outer_kernel<1, TRANS><<<tiles, kThreads, 0, st>>>(E, offsets, jobs, w.hdr, w.desc, w.part); break;
+    case 2: outer_kernel<2, TRANS><<<tiles, kThreads, 0, st>>>(E, offsets, jobs, w.hdr, w.desc, w.part); break;
+    case 3: outer_kernel<3, TRANS><<<tiles, kThreads, 0, st>>>(E, offsets, jobs, w.hdr, w.desc, w.part); break;
+    case 4: outer_kernel<4, TRANS><<<tiles, kThreads, 0, st>>>(E, offsets, jobs, w.hdr, w.desc, w.part); break;
+    case 8: outer_kernel<8, TRANS><<<tiles, kThreads, 0, st>>>(E, offsets, jobs, w.hdr, w.desc, w.part); break;
     default: return hipErrorInvalidValue;
   }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  outer_reduce_kernel<TRANS><<<static_cast<unsigned>(2 * grid), kThreads, 0, st>>>(jobs, tiles_per_expert, w.hdr,
+                                                                                      w.units, w.part);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int lora_padded_rank(int r) { return (r + 63) & ~63; }
+// The projections' output width: the rank rounded up to 32, 64 or 128 (whole
+// 32-column blocks of the projection tile; a rank of 8 does 4x, not 8x, its
+// own work).
+int lora_padded_rank(int r) { return r <= 32 ? 32 : (r <= 64 ? 64 : 128); }
 
 LoraLayout lora_layout(const moe_shape& s, int r) {
   LoraLayout l{};
@@ -711,6 +955,13 @@ LoraLayout lora_layout(const moe_shape& s, int r) {
   l.z_d = take(M * rp * 2);
   l.y_gu = take(M * 2 * rp * 2);
   l.y_d = take(M * rp * 2);
+  // Split plan and partial tiles of the outer products: at most 2 ceil(I /
+  // 128) + ceil(H / 128) tiles per expert plus fewer than 2 grid partial
+  // tiles (cap >= total work / (2 grid)), and fewer reduction units.
+  const int64_t grid = outer_grid();
+  const int64_t max_tiles = (2 * ceil_div(I, 128) + ceil_div(H, 128)) * E + 2 * grid;
+  l.plan = take(256 + max_tiles * static_cast<int64_t>(sizeof(OuterDesc)) + 2 * grid * sizeof(OuterUnit));
+  l.part = take(2 * grid * kOuterPartFloats * 4);
   l.total = off;
   return l;
 }
@@ -806,14 +1057,20 @@ hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraA
     ob.job[2] = {static_cast<const bf16_t*>(g.do_perm), static_cast<const bf16_t*>(z_d), g.db_down, nullptr, H, 0,
                  H, rp, 0, r, r, r};
     ob.n = 3;
-    MOE_TRY(outer_products<false>(E, (r + 31) / 32, g.offsets, ob, st));
+    const int64_t max_tiles = (2 * ceil_div(I, 128) + ceil_div(H, 128)) * static_cast<int64_t>(E) + 2 * outer_grid();
+    OuterSpace os{};
+    os.hdr = reinterpret_cast<int*>(base + l.plan);
+    os.desc = reinterpret_cast<OuterDesc*>(base + l.plan + 256);
+    os.units = reinterpret_cast<OuterUnit*>(base + l.plan + 256 + max_tiles * sizeof(OuterDesc));
+    os.part = reinterpret_cast<float*>(base + l.part);
+    MOE_TRY(outer_products<false>(E, (r + 31) / 32, g.offsets, ob, os, st));
     OuterJobs oa{};
     oa.job[0] = {static_cast<const bf16_t*>(g.x_perm), static_cast<const bf16_t*>(y_gu), g.da_gate, g.da_up, H, 0,
                  H, 2 * rp, 0, 2 * rp, rp, r};
     oa.job[1] = {static_cast<const bf16_t*>(g.act), static_cast<const bf16_t*>(y_d), g.da_down, nullptr, I, 0, I, rp,
                  0, r, r, r};
     oa.n = 2;
-    MOE_TRY(outer_products<true>(E, 2 * rp / 32, g.offsets, oa, st));
+    MOE_TRY(outer_products<true>(E, 2 * rp / 32, g.offsets, oa, os, st));
   }
 #undef MOE_TRY
   return hipSuccess;

@@ -180,13 +180,15 @@ inline hipError_t launch_gemm_pair(GemmMode ma, GemmMode mb, const moe_shape& s,
 }
 
 
-// Low-rank adapters (lora.hip). The projections pad the rank to rp, a
-// multiple of 64 (the padding rows of the scaled adapters are zeros).
+// Low-rank adapters (lora.hip). The projections pad the rank to rp = 32, 64
+// or 128 (the padding rows of the scaled adapters are zeros).
 int lora_padded_rank(int r);
 
 struct LoraLayout {  // byte offsets in the adapter-gradient workspace
   size_t sa_gu, sa_d, sbt_gu, sbt_d;  // bf16 scaled adapter stacks
   size_t z_gu, z_d, y_gu, y_d;        // bf16 row projections [T*k][2rp | rp]
+  size_t plan;                        // split plan of the outer products (descriptors)
+  size_t part;                        // fp32 partial tiles of split outer products
   size_t total;
 };
 LoraLayout lora_layout(const moe_shape& s, int r);
