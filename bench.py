@@ -24,7 +24,10 @@ times is larger decides the bound) over its average launch time. `traffic` is th
 rocprofv3's FETCH_SIZE and WRITE_SIZE counters gave for that kernel, scaled by
 what they read for a plain device copy of known size (--calibrate-copy); it is
 taken from the committed summary under profiles/ and reported only while the
-GEMM source still hashes to the value recorded there. `cpu_baseline` times
+GEMM source still hashes to the value recorded there, as are
+`mfma_busy_counter` (SQ_VALU_MFMA_BUSY_CYCLES over the SIMD-cycles of the
+dispatch, GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) and `clock_ghz_counter`
+(the shader clock the kernel ran at). `cpu_baseline` times
 the CPU oracle on every token of the same workload (first seed), on every
 host thread this job may use (the CPUs it may run on, capped by
 OMP_NUM_THREADS), with the host's CPU count and model.
@@ -101,12 +104,13 @@ def source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def profiled_traffic(kernel: str, workload: str):
-    """HBM bytes per launch of `kernel` from profiles/<kernel>.<workload>.traffic.txt,
-    or None when there is no such summary or the GEMM source changed since."""
+def profiled_counters(kernel: str, workload: str) -> dict:
+    """The committed counter summary profiles/<kernel>.<workload>.traffic.txt
+    (HBM bytes per launch, MFMA busy fraction, clock), or {} when there is
+    none or the GEMM source changed since it was taken."""
     path = os.path.join(PROFILES, f"{kernel}.{workload}.traffic.txt")
     if not os.path.exists(path):
-        return None
+        return {}
     rec = {}
     with open(path) as f:
         for line in f:
@@ -114,11 +118,14 @@ def profiled_traffic(kernel: str, workload: str):
                 key, val = line.split(":", 1)
                 rec[key.strip()] = val.strip()
     if rec.get("gemm_source_sha256_16") != source_hash():
-        return None
-    try:
-        return int(rec["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        return {}
+    out = {}
+    for key, conv in [("hbm_bytes_per_launch", int), ("mfma_busy_frac", float), ("clock_ghz", float)]:
+        try:
+            out[key] = conv(rec[key])
+        except (KeyError, ValueError):
+            pass
+    return out
 
 
 def calibrate_copy(nbytes: int, reps: int) -> int:
@@ -574,10 +581,15 @@ def main() -> int:
             roof = {"kernel": dominant, "bound": "hbm", "achieved": round(nbytes[dominant] / secs / 1e9, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s"}
         roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-        roof["traffic"] = profiled_traffic(dominant, cfg.name)
+        ctr = profiled_counters(dominant, cfg.name)
+        roof["traffic"] = ctr.get("hbm_bytes_per_launch")
         roof["alg_bytes"] = nbytes[dominant]
         if dominant in flops:
             roof["mfma_frac"] = round(flops[dominant] / secs / 1e12 / PEAK_BF16_TFLOPS, 4)
+            # From rocprofv3 counters (same source): SIMD-cycles with the matrix
+            # core busy, and the clock the kernel ran at.
+            roof["mfma_busy_counter"] = ctr.get("mfma_busy_frac")
+            roof["clock_ghz_counter"] = ctr.get("clock_ghz")
         return roof
 
     roof = roofline(per_call)
