@@ -4,12 +4,19 @@
                     [--no-cpu-baseline] [--timed-only]
 
 One step is the whole stage on one batch of synthetic input already resident
-in HBM, on one stream, as the library chains it (MoEStage; moe_grouped_gemm_fwd
-and moe_grouped_gemm_bwd): route -> expert indexing + gather -> gate/up GEMM
-(SwiGLU epilogue) -> down GEMM -> combine, then combine backward -> down
-backward (data gradient with the SwiGLU backward epilogue, then the weight
-gradient, in one persistent launch) -> gate/up backward (likewise) ->
-unpermute-sum -> router backward, every step a call of the C ABI.
+in HBM, on one stream, every step a call of the C ABI, as the library chains
+it (MoEStage; moe_grouped_gemm_fwd and moe_grouped_gemm_bwd): route -> expert
+indexing + gather (x_perm) -> gate/up GEMM (SwiGLU epilogue) -> down GEMM ->
+combine, then combine backward (do_perm, d_topk_w) -> down backward (data
+gradient with the SwiGLU backward epilogue, then the weight gradient, in one
+persistent launch) -> gate/up backward (likewise) -> unpermute-sum -> router
+backward. --chain fused times the chain that materialises neither x_perm nor
+do_perm (MoEStage with gather_fused and dy_fused): the sort writes each
+sorted row's token and routing weight, gate/up reads x through the tokens and
+also writes the weighted activations a_w, the combine backward writes
+d_topk_w only, the down backward reads dy through the tokens and takes the
+routing weight in its epilogue, the gate/up backward reads x through the
+tokens. The line also reports the other chain's time.
 
 Each input seed (default 0, 1 and 2) gets W untimed warmup steps and K timed
 steps; the line reports the seed with the median time (`ms_per_step_by_seed`
@@ -36,9 +43,13 @@ After the timed steps (and outside them): `ms_per_step_without_call_events`
 times the same step without the per-call events; `graph_ms_per_step` the same
 step captured once into a HIP graph and replayed; `two_stream_ms_per_step`
 the step with one launch per GEMM and the weight-gradient GEMMs on a second
-stream, concurrently with the data-gradient GEMMs; `gather_fused_ms` the step
-without x_perm (gate/up and the gate/up backward read x through the sorted
-rows' tokens) and its three changed calls; `single_launch_ms` the step with
+stream, concurrently with the data-gradient GEMMs (x_perm chain);
+`xperm_chain_ms_per_step` (or `fused_chain_ms_per_step`) the chain not timed
+above; `gather_fused_ms` the x_perm chain without x_perm only (gate/up and
+the gate/up backward read x through the sorted rows' tokens),
+`dy_fused_ms` the x_perm chain without do_perm only, and
+`gather_dy_fused_ms` without both (the default chain), each with its changed
+calls on their own; `single_launch_ms` the step with
 one launch per GEMM (the six single-GEMM entry points) and the four backward
 GEMMs on their own (whose TFLOP/s join `gemm_tflops`); `inference_forward_ms`
 the forward alone, unfused and fused (no x_perm, routing weights in the down
@@ -99,15 +110,36 @@ def alg_bytes(c) -> dict:
     }
 
 
+def alg_bytes_fused(c) -> dict:
+    """alg_bytes of the calls that differ in the chain without x_perm and
+    do_perm: x and dy are read through the sorted rows' tokens (each tensor
+    once: T rows), the sort writes row_token and row_weight, gate/up also
+    writes a_w, the combine backward writes d_topk_w only."""
+    T, H, E, k, I = c.T, c.H, c.E, c.k, c.I
+    M = T * k
+    b16, f32, i32 = 2, 4, 4
+    out = dict(alg_bytes(c))
+    out.update({
+        "moe_permute": M * i32 + M * f32 + 3 * M * i32 + M * f32,
+        "moe_gemm_gate_up": T * H * b16 + 2 * M * i32 + 2 * E * I * H * b16 + 4 * M * I * b16,
+        "moe_combine_bwd": T * H * b16 + M * H * b16 + 2 * M * i32 + M * f32,
+        "moe_gemm_down_bwd": (T * H * b16 + M * i32 + M * f32 + E * H * I * b16 + 2 * M * I * b16
+                              + 2 * M * I * b16 + M * I * b16 + E * H * I * f32),
+        "moe_gemm_gate_up_bwd": (2 * M * I * b16 + 2 * E * I * H * b16 + T * H * b16 + M * i32
+                                 + M * H * b16 + 2 * E * I * H * f32),
+    })
+    return out
+
+
 def source_hash() -> str:
     with open(GEMM_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def profiled_counters(kernel: str, workload: str) -> dict:
+def profiled_counters(kernel: str, workload: str, chain: str) -> dict:
     """The committed counter summary profiles/<kernel>.<workload>.traffic.txt
     (HBM bytes per launch, MFMA busy fraction, clock), or {} when there is
-    none or the GEMM source changed since it was taken."""
+    none, it was taken on the other chain or the GEMM source changed since."""
     path = os.path.join(PROFILES, f"{kernel}.{workload}.traffic.txt")
     if not os.path.exists(path):
         return {}
@@ -117,7 +149,7 @@ def profiled_counters(kernel: str, workload: str) -> dict:
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 rec[key.strip()] = val.strip()
-    if rec.get("gemm_source_sha256_16") != source_hash():
+    if rec.get("gemm_source_sha256_16") != source_hash() or rec.get("chain", "xperm") != chain:
         return {}
     out = {}
     for key, conv in [("hbm_bytes_per_launch", int), ("mfma_busy_frac", float), ("clock_ghz", float)]:
@@ -279,6 +311,8 @@ def main() -> int:
                     help="input seeds; each runs W warmup and K timed steps, the line reports the median")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample (default: every token of the workload)")
+    ap.add_argument("--chain", choices=["xperm", "fused"], default="xperm",
+                    help="the timed chain: materialising x_perm and do_perm (default), or without both")
     ap.add_argument("--timed-only", action="store_true",
                     help="launch nothing after the timed steps (for profiling): no sequential, inference or CPU pass")
     ap.add_argument("--lora-only", action="store_true",
@@ -365,6 +399,50 @@ def main() -> int:
     by_name["moe_gemm_gate_up_bwd"] = lambda: B.moe_gemm_gate_up_bwd(s, dgu, b["x_perm"], None, b["offsets"], wg,
                                                                      wu, b["dx_perm"], b["dw_gate"], b["dw_up"], 0,
                                                                      st.ws)
+    # The same step without x_perm: the sort also writes each sorted row's
+    # token, and gate/up and the gate/up backward pair (its weight gradient)
+    # read x rows through it.
+    rt = dict(row_token=torch.empty(cfg.M, dtype=torch.int32, device="cuda"),
+              row_weight=torch.empty(cfg.M, device="cuda"))
+    gf_calls = dict(by_name)
+    gf_calls["moe_permute"] = lambda: B.moe_permute_fused(
+        s, b["topk_idx"], b["topk_w"], b["counts"], b["offsets"], b["sorted_to_flat"], b["flat_to_sorted"],
+        rt["row_token"], rt["row_weight"], st.ws)
+    gf_calls["moe_gemm_gate_up"] = lambda: B.moe_gemm_gate_up_gathered(
+        s, x, rt["row_token"], b["offsets"], wg, wu, b["g"], b["u"], b["a"])
+    gf_calls["moe_gemm_gate_up_bwd"] = lambda: B.moe_gemm_gate_up_bwd(
+        s, dgu, x, rt["row_token"], b["offsets"], wg, wu, b["dx_perm"], b["dw_gate"], b["dw_up"], 0, st.ws)
+
+    # The same step without do_perm: the gate/up GEMM also writes the weighted
+    # activations, the combine backward writes d_topk_w only, and the down
+    # backward reads dy through the sorted rows' tokens.
+    a_w = torch.empty(cfg.M, cfg.I, dtype=torch.bfloat16, device="cuda")
+    dy_calls = dict(by_name)
+    dy_calls["moe_permute"] = lambda: B.moe_permute_rows(
+        s, b["topk_idx"], b["topk_w"], x, b["counts"], b["offsets"], b["sorted_to_flat"], b["flat_to_sorted"],
+        rt["row_token"], rt["row_weight"], b["x_perm"], st.ws)
+    dy_calls["moe_gemm_gate_up"] = lambda: B.moe_gemm_gate_up_aw(
+        s, b["x_perm"], None, rt["row_weight"], b["offsets"], wg, wu, b["g"], b["u"], b["a"], a_w)
+    dy_calls["moe_combine_bwd"] = lambda: B.moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"],
+                                                            None, b["d_topk_w"])
+    dy_calls["moe_gemm_down_bwd"] = lambda: B.moe_gemm_down_bwd_dy(
+        s, dy, rt["row_token"], rt["row_weight"], a_w, b["offsets"], wd, b["g"], b["u"], dgu, b["dw_down"], 0, st.ws)
+
+    # The step with neither x_perm nor do_perm: the sort writes each sorted
+    # row's token and weight, gate/up reads x through the token and also
+    # writes the weighted activations, the down backward reads dy through the
+    # token, the gate/up backward reads x through it.
+    both_calls = dict(dy_calls)
+    both_calls["moe_permute"] = gf_calls["moe_permute"]
+    both_calls["moe_gemm_gate_up"] = lambda: B.moe_gemm_gate_up_aw(
+        s, x, rt["row_token"], rt["row_weight"], b["offsets"], wg, wu, b["g"], b["u"], b["a"], a_w)
+    both_calls["moe_gemm_gate_up_bwd"] = gf_calls["moe_gemm_gate_up_bwd"]
+
+    # The timed chain: by default the one that materialises x_perm and
+    # do_perm (by_name); --chain fused times the one without both
+    # (both_calls).
+    chain = both_calls if args.chain == "fused" else by_name
+
     # HIP events in the timed steps bracket the GEMM calls only (an event
     # between two calls costs about 5 us; bracketing all ten calls added
     # 0.1 ms to a 3 ms step): one event before the first GEMM of each run of
@@ -385,7 +463,7 @@ def main() -> int:
             timed = events is not None and n in gemm_names
             if timed and start_of[n].startswith("start_"):
                 events[start_of[n]].record(stream)
-            by_name[n]()
+            chain[n]()
             if timed:
                 events[n].record(stream)
 
@@ -440,10 +518,13 @@ def main() -> int:
         return time_calls(fn, stream, reps)
 
     # The calls without matrix work, each on its own (outside the timed steps).
-    other_ms = None if args.timed_only else {n: round(time_fn(by_name[n]), 4) for n in names if n not in gemm_names}
+    other_ms = None if args.timed_only else {n: round(time_fn(chain[n]), 4) for n in names if n not in gemm_names}
 
     # The same step without the per-call events (what the events themselves cost).
     plain_ms = None if args.timed_only else round(time_fn(step), 4)
+    # The other chain, for comparison.
+    other_chain = by_name if args.chain == "fused" else both_calls
+    other_chain_ms = None if args.timed_only else round(time_fn(lambda: [other_chain[n]() for n in names]), 4)
     two_stream_ms = None if args.timed_only else round(time_fn(step_two_streams), 4)
     if two_stream_ms is not None:
         log(f"two-stream backward: {two_stream_ms:.3f} ms/step")
@@ -461,20 +542,6 @@ def main() -> int:
         graph_ms = round(time_fn(graph.replay), 4)
         log(f"graph replay: {graph_ms:.3f} ms/step")
 
-    # The same step without x_perm: the sort also writes each sorted row's
-    # token, and gate/up and the gate/up backward pair (its weight gradient)
-    # read x rows through it.
-    rt = dict(row_token=torch.empty(cfg.M, dtype=torch.int32, device="cuda"),
-              row_weight=torch.empty(cfg.M, device="cuda"))
-    gf_calls = dict(by_name)
-    gf_calls["moe_permute"] = lambda: B.moe_permute_fused(
-        s, b["topk_idx"], b["topk_w"], b["counts"], b["offsets"], b["sorted_to_flat"], b["flat_to_sorted"],
-        rt["row_token"], rt["row_weight"], st.ws)
-    gf_calls["moe_gemm_gate_up"] = lambda: B.moe_gemm_gate_up_gathered(
-        s, x, rt["row_token"], b["offsets"], wg, wu, b["g"], b["u"], b["a"])
-    gf_calls["moe_gemm_gate_up_bwd"] = lambda: B.moe_gemm_gate_up_bwd(
-        s, dgu, x, rt["row_token"], b["offsets"], wg, wu, b["dx_perm"], b["dw_gate"], b["dw_up"], 0, st.ws)
-
     def step_gather_fused():
         for n in names:
             gf_calls[n]()
@@ -486,21 +553,6 @@ def main() -> int:
             gather_fused_ms[n] = round(time_fn(gf_calls[n], reps=5), 4)
         log(f"step without x_perm: {gather_fused_ms}")
 
-    # The same step without do_perm: the gate/up GEMM also writes the weighted
-    # activations, the combine backward writes d_topk_w only, and the down
-    # backward reads dy through the sorted rows' tokens.
-    a_w = torch.empty(cfg.M, cfg.I, dtype=torch.bfloat16, device="cuda")
-    dy_calls = dict(by_name)
-    dy_calls["moe_permute"] = lambda: B.moe_permute_rows(
-        s, b["topk_idx"], b["topk_w"], x, b["counts"], b["offsets"], b["sorted_to_flat"], b["flat_to_sorted"],
-        rt["row_token"], rt["row_weight"], b["x_perm"], st.ws)
-    dy_calls["moe_gemm_gate_up"] = lambda: B.moe_gemm_gate_up_aw(
-        s, b["x_perm"], None, rt["row_weight"], b["offsets"], wg, wu, b["g"], b["u"], b["a"], a_w)
-    dy_calls["moe_combine_bwd"] = lambda: B.moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"],
-                                                            None, b["d_topk_w"])
-    dy_calls["moe_gemm_down_bwd"] = lambda: B.moe_gemm_down_bwd_dy(
-        s, dy, rt["row_token"], rt["row_weight"], a_w, b["offsets"], wd, b["g"], b["u"], dgu, b["dw_down"], 0, st.ws)
-
     def step_dy_fused():
         for n in names:
             dy_calls[n]()
@@ -511,6 +563,17 @@ def main() -> int:
         for n in ["moe_permute", "moe_gemm_gate_up", "moe_combine_bwd", "moe_gemm_down_bwd"]:
             dy_fused_ms[n] = round(time_fn(dy_calls[n], reps=5), 4)
         log(f"step without do_perm: {dy_fused_ms}")
+
+    def step_both_fused():
+        for n in names:
+            both_calls[n]()
+
+    both_fused_ms = None
+    if not args.timed_only:
+        both_fused_ms = {"step": round(time_fn(step_both_fused), 4)}
+        for n in ["moe_permute", "moe_gemm_gate_up", "moe_combine_bwd", "moe_gemm_down_bwd", "moe_gemm_gate_up_bwd"]:
+            both_fused_ms[n] = round(time_fn(both_calls[n], reps=5), 4)
+        log(f"step without x_perm and do_perm: {both_fused_ms}")
 
     # The same step with one launch per GEMM (the six single-GEMM entry
     # points), and each backward GEMM on its own.
@@ -565,7 +628,7 @@ def main() -> int:
     lora = None if args.timed_only else lora_timing(cfg, seeds[0], (x, wr, wg, wu, wd, dy), bias, stream)
 
     flops = gemm_flops(cfg)
-    nbytes = alg_bytes(cfg)
+    nbytes = alg_bytes_fused(cfg) if args.chain == "fused" else alg_bytes(cfg)
     step_flops = sum(flops[n] for n in names if n in flops)
     tflops = step_flops / (ms * 1e-3) / 1e12
 
@@ -581,7 +644,7 @@ def main() -> int:
             roof = {"kernel": dominant, "bound": "hbm", "achieved": round(nbytes[dominant] / secs / 1e9, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s"}
         roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-        ctr = profiled_counters(dominant, cfg.name)
+        ctr = profiled_counters(dominant, cfg.name, args.chain)
         roof["traffic"] = ctr.get("hbm_bytes_per_launch")
         roof["alg_bytes"] = nbytes[dominant]
         if dominant in flops:
@@ -614,7 +677,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded normal inputs, random-init weights of the Qwen3-30B-A3B MoE layer shape)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
-                   "seeds": seeds, "pass": "fwd+bwd"},
+                   "seeds": seeds, "pass": "fwd+bwd", "chain": args.chain},
         "ms_per_step_by_seed": ms_by_seed,
         "tflops": round(tflops, 1),
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -624,10 +687,12 @@ def main() -> int:
         "hbm_frac": hbm_frac,
         "roofline": roof,
         "ms_per_step_without_call_events": plain_ms,
+        ("xperm_chain_ms_per_step" if args.chain == "fused" else "fused_chain_ms_per_step"): other_chain_ms,
         "two_stream_ms_per_step": two_stream_ms,
         "graph_ms_per_step": graph_ms,
         "gather_fused_ms": gather_fused_ms,
         "dy_fused_ms": dy_fused_ms,
+        "gather_dy_fused_ms": both_fused_ms,
         "single_launch_ms": single_ms,
         "inference_forward_ms": infer,
         "lora_ms": lora,
