@@ -47,7 +47,7 @@
 // place: gate and up of one element share a lane; a DPP quad transpose and a
 // half-wave swap turn the MFMA layout into four-row x 128-byte store runs,
 // written non-temporally), so those loads land while the results go out.
-// Row blocks of a ragged last tile that hold no rows skip their MFMAs.
+// Row blocks of a short tile that hold no rows skip their MFMAs.
 //
 // Scheduling: one workgroup per CU, persistent. Tile i of the list belongs
 // to XCD-local workgroups: the list is cut into 8 contiguous ranges, one per
@@ -546,8 +546,13 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
       const int mte = tstart[te + 1] - tstart[te];
       const int nt = rem / mte;
       const int mt = rem - nt * mte;
-      trow0 = eoff[te] + mt * BM;
-      tmvalid = min(BM, eoff[te + 1] - trow0);
+      // The expert's rows split evenly over its mte tiles (at most BM each):
+      // no short last tile that would race ahead of its siblings, fetching
+      // the weight slice they share on its own.
+      const int64_t cnt = eoff[te + 1] - eoff[te];
+      const int r0 = static_cast<int>((mt * cnt) / mte);
+      trow0 = eoff[te] + r0;
+      tmvalid = static_cast<int>(((mt + 1) * cnt) / mte) - r0;
       tn0 = nt * (MODE == GATEUP ? GU_COLS : BN);
     } else {
       int l2 = 0, h2 = E - 1;
