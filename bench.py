@@ -55,7 +55,9 @@ GEMMs on their own (whose TFLOP/s join `gemm_tflops`); `inference_forward_ms`
 the forward alone, unfused and fused (no x_perm, routing weights in the down
 GEMM's epilogue); `lora_ms` the training step with rank-64 adapters on frozen
 experts (merges, forward on the merged weights, data and adapter gradients)
-and its two adapter calls. `--timed-only` skips these and the CPU baseline, so that
+and its two adapter calls, over bf16 and over E4M3 frozen weights, and the
+step without x_perm and do_perm (`step_gathered`, with
+`moe_lora_grads_gathered`). `--timed-only` skips these and the CPU baseline, so that
 under a profiler the last K launches of every kernel are the timed steps.
 """
 from __future__ import annotations
@@ -295,8 +297,23 @@ def lora_timing(cfg, seed: int, tensors, bias, stream, r: int = 64, scale: float
     out["moe_lora_grads"] = round(time_calls(lambda: B.moe_lora_grads(
         ls.s, r, scale, lb["x_perm"], lb["a"], lb["dgu"], lb["do_perm"], lb["offsets"],
         *(ad[n] for n in B.LORA_NAMES), *(lb["d" + n] for n in B.LORA_NAMES), ls.lora_ws), stream, reps=5), 4)
+    del ls, lb
+    torch.cuda.empty_cache()
+    # The step without x_perm and do_perm: x and dy read through the sorted
+    # rows' tokens in the GEMMs and in the adapter gradients.
+    gs = B.LoRAStage(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, r, scale, gathered=True)
+    gb = gs.buf
+
+    def lora_step_gathered():
+        gs.forward(x, wr, wg, wu, wd, ad, bias)
+        gs.backward(dy)
+
+    out["step_gathered"] = round(time_calls(lora_step_gathered, stream), 4)
+    out["moe_lora_grads_gathered"] = round(time_calls(lambda: B.moe_lora_grads_gathered(
+        gs.s, r, scale, x, gb["row_token"], gb["row_weight"], gb["a"], gb["dgu"], dy, gb["offsets"],
+        *(ad[n] for n in B.LORA_NAMES), *(gb["d" + n] for n in B.LORA_NAMES), gs.lora_ws), stream, reps=5), 4)
     log(f"adapter step: {out}")
-    del ls, lb, ad
+    del gs, gb, ad
     torch.cuda.empty_cache()
     return out
 

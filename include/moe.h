@@ -465,12 +465,45 @@ size_t moe_lora_workspace_bytes(moe_shape s, int32_t r);
  * and db_* [E,N,r], overwritten; an expert with no rows gets zeros. The
  * scaled adapters and the projections x_perm (sA)^T, dY (sB) are rounded to
  * bf16 once; every sum is fp32. Requires shape.dtype MOE_BF16; ws of
- * ws_bytes >= moe_lora_workspace_bytes(s, r), else MOE_EWORKSPACE. */
+ * ws_bytes >= moe_lora_workspace_bytes(s, r), else MOE_EWORKSPACE;
+ * T k max(H, 2I) < 2^30 (32-bit byte offsets of the sorted rows), else
+ * MOE_EUNSUPPORTED. */
 moe_status moe_lora_grads(moe_shape s, int32_t r, float scale, const void* x_perm, const void* act, const void* dgu,
                           const void* do_perm, const int32_t* offsets, const void* a_gate, const void* b_gate,
                           const void* a_up, const void* b_up, const void* a_down, const void* b_down, float* da_gate,
                           float* db_gate, float* da_up, float* db_up, float* da_down, float* db_down, void* ws,
                           size_t ws_bytes, hipStream_t stream);
+
+/* The same adapter gradients without x_perm and do_perm (unsloth PR #3812:
+ * the grouped GEMMs read rows through the gather indices; the routing weight
+ * applied inside the expert computation): row p of x_perm is row
+ * row_token[p] of x [T,H], and row p of do_perm is row_weight[p] *
+ * dy[row_token[p]] (dy [T,H] bf16, the stage's upstream gradient;
+ * row_token, row_weight [T*k] from moe_permute_fused). The weight is applied
+ * in fp32 to the two rank-wide projections that carry dO (a A_down^T for
+ * dB_down, dy B_down for dA_down) before their rounding to bf16, so results
+ * are within rounding of moe_lora_grads, not bit-identical. Training chain
+ * without x_perm and do_perm: moe_permute_fused -> moe_gemm_gate_up_gathered
+ * -> moe_gemm_down -> moe_combine; moe_combine_bwd (do_perm NULL) ->
+ * moe_gemm_down_dgrad_dy -> moe_gemm_gate_up_dgrad -> this ->
+ * moe_unpermute_sum -> moe_route_bwd. Same limits and errors as
+ * moe_lora_grads; every pointer non-NULL (MOE_EINVAL). */
+moe_status moe_lora_grads_gathered(moe_shape s, int32_t r, float scale, const void* x, const int32_t* row_token,
+                                   const float* row_weight, const void* act, const void* dgu, const void* dy,
+                                   const int32_t* offsets, const void* a_gate, const void* b_gate, const void* a_up,
+                                   const void* b_up, const void* a_down, const void* b_down, float* da_gate,
+                                   float* db_gate, float* da_up, float* db_up, float* da_down, float* db_down,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Down data gradient without do_perm (the data-gradient half of
+ * moe_gemm_down_bwd_dy, for callers that train no frozen W_down, such as
+ * the adapter step): dA[p] = row_weight[p] (dy[row_token[p]] W_down[e]) in
+ * fp32, then the SwiGLU backward with the saved g, u into dgu = [dG | dU]
+ * [T*k, 2I] (bf16). bf16 only and T*H*2 < 2^31 (MOE_EUNSUPPORTED otherwise);
+ * every pointer non-NULL (MOE_EINVAL). */
+moe_status moe_gemm_down_dgrad_dy(moe_shape s, const void* dy, const int32_t* row_token, const float* row_weight,
+                                  const int32_t* offsets, const void* w_down, const void* g, const void* u, void* dgu,
+                                  hipStream_t stream);
 
 /* A static, human-readable name for a status code. */
 const char* moe_status_string(moe_status status);

@@ -81,6 +81,9 @@ _SIGS = {
     "moe_lora_merge_fp8": ([ctypes.c_int32] * 4 + [ctypes.c_float] + [_P] * 6, ctypes.c_int),
     "moe_lora_grads": ([moe_shape, ctypes.c_int32, ctypes.c_float] + [_P] * 18 + [ctypes.c_size_t, _P],
                        ctypes.c_int),
+    "moe_lora_grads_gathered": ([moe_shape, ctypes.c_int32, ctypes.c_float] + [_P] * 20 + [ctypes.c_size_t, _P],
+                                ctypes.c_int),
+    "moe_gemm_down_dgrad_dy": ([moe_shape] + [_P] * 9, ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -366,6 +369,22 @@ def moe_lora_grads(s, r, scale, x_perm, act, dgu, do_perm, offsets, a_gate, b_ga
         _ptr(db_up), _ptr(da_down), _ptr(db_down), _ptr(ws), nb, _stream(stream)))
 
 
+def moe_lora_grads_gathered(s, r, scale, x, row_token, row_weight, act, dgu, dy, offsets, a_gate, b_gate, a_up,
+                            b_up, a_down, b_down, da_gate, db_gate, da_up, db_up, da_down, db_down, ws, ws_bytes=None,
+                            stream=None):
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_lora_grads_gathered", lib.moe_lora_grads_gathered(
+        s, r, float(scale), _ptr(x), _ptr(row_token), _ptr(row_weight), _ptr(act), _ptr(dgu), _ptr(dy), _ptr(offsets),
+        _ptr(a_gate), _ptr(b_gate), _ptr(a_up), _ptr(b_up), _ptr(a_down), _ptr(b_down), _ptr(da_gate), _ptr(db_gate),
+        _ptr(da_up), _ptr(db_up), _ptr(da_down), _ptr(db_down), _ptr(ws), nb, _stream(stream)))
+
+
+def moe_gemm_down_dgrad_dy(s, dy, row_token, row_weight, offsets, w_down, g, u, dgu, stream=None):
+    _check("moe_gemm_down_dgrad_dy", lib.moe_gemm_down_dgrad_dy(
+        s, _ptr(dy), _ptr(row_token), _ptr(row_weight), _ptr(offsets), _ptr(w_down), _ptr(g), _ptr(u), _ptr(dgu),
+        _stream(stream)))
+
+
 class MoEStage:
     """Buffers and call order of one MoE layer's expert stage on one GPU.
 
@@ -425,7 +444,7 @@ class MoEStage:
         dev = self.ws.device
         M = T * k
         f32 = torch.float32
-        if not self.dy_fused:
+        if not self.dy_fused and not getattr(self, "gathered", False):
             self.buf["do_perm"] = torch.empty(M, H, dtype=dt, device=dev)
         self.buf.update({
             "d_topk_w": torch.empty(T, k, dtype=f32, device=dev),
@@ -550,10 +569,19 @@ class LoRAStage(MoEStage):
     [E,r,K], b_P [E,N,r] bf16 for P in gate, up, down. Each frozen weight is
     a bf16 tensor or, kept in 8 bits (QLoRA-style), the (E4M3 codes, E8M0
     row scales) pair of FP8Weights (moe_lora_merge_fp8 dequantises it).
+
+    ``gathered``: neither x_perm nor do_perm. The forward reads x through the
+    sorted rows' tokens (moe_permute_fused, moe_gemm_gate_up_gathered); the
+    backward's down data gradient reads dy through them and applies the
+    routing weight (moe_gemm_down_dgrad_dy), and the adapter gradients read x
+    and dy through them (moe_lora_grads_gathered). Within rounding of the
+    default chain. Not combined with the forward's aux_stream.
     """
 
-    def __init__(self, T: int, H: int, E: int, k: int, I: int, rank: int, scale: float, device="cuda"):
-        super().__init__(T, H, E, k, I, torch.bfloat16, device=device)
+    def __init__(self, T: int, H: int, E: int, k: int, I: int, rank: int, scale: float, device="cuda",
+                 gathered: bool = False):
+        super().__init__(T, H, E, k, I, torch.bfloat16, device=device, gather_fused=gathered)
+        self.gathered = gathered
         self.weight_grads = False
         self.rank, self.scale = rank, scale
         nb = moe_lora_workspace_bytes(self.s, rank)
@@ -592,6 +620,8 @@ class LoRAStage(MoEStage):
         if aux_stream is None:
             wg, wu, wd = self.merge(w_gate, w_up, w_down, adapters, stream)
             return super().forward(x, w_router, wg, wu, wd, logit_bias, stream)
+        if self.gathered:
+            raise ValueError("the gathered adapter step runs its merges on the forward's stream")
         E, H, I, r = self.E, self.H, self.I, self.rank
         wg, wu, wd = self.merged
         main = torch.cuda.current_stream() if stream is None else stream
@@ -623,11 +653,22 @@ class LoRAStage(MoEStage):
         b, s = self.buf, self.s
         wg, wu, wd = self.merged
         ad = self.adapters
-        moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["do_perm"], b["d_topk_w"], stream)
-        moe_gemm_down_dgrad(s, b["do_perm"], b["offsets"], wd, b["g"], b["u"], b["dgu"], stream)
-        moe_gemm_gate_up_dgrad(s, b["dgu"], b["offsets"], wg, wu, b["dx_perm"], stream)
-        moe_lora_grads(s, self.rank, self.scale, b["x_perm"], b["a"], b["dgu"], b["do_perm"], b["offsets"],
-                       *(ad[n] for n in LORA_NAMES), *(b["d" + n] for n in LORA_NAMES), self.lora_ws, stream=stream)
+        if self.gathered:
+            moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"], None, b["d_topk_w"], stream)
+            moe_gemm_down_dgrad_dy(s, dy, b["row_token"], b["row_weight"], b["offsets"], wd, b["g"], b["u"], b["dgu"],
+                                   stream)
+            moe_gemm_gate_up_dgrad(s, b["dgu"], b["offsets"], wg, wu, b["dx_perm"], stream)
+            moe_lora_grads_gathered(s, self.rank, self.scale, self.x, b["row_token"], b["row_weight"], b["a"],
+                                    b["dgu"], dy, b["offsets"], *(ad[n] for n in LORA_NAMES),
+                                    *(b["d" + n] for n in LORA_NAMES), self.lora_ws, stream=stream)
+        else:
+            moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["do_perm"], b["d_topk_w"],
+                            stream)
+            moe_gemm_down_dgrad(s, b["do_perm"], b["offsets"], wd, b["g"], b["u"], b["dgu"], stream)
+            moe_gemm_gate_up_dgrad(s, b["dgu"], b["offsets"], wg, wu, b["dx_perm"], stream)
+            moe_lora_grads(s, self.rank, self.scale, b["x_perm"], b["a"], b["dgu"], b["do_perm"], b["offsets"],
+                           *(ad[n] for n in LORA_NAMES), *(b["d" + n] for n in LORA_NAMES), self.lora_ws,
+                           stream=stream)
         moe_unpermute_sum(s, b["dx_perm"], b["flat_to_sorted"], b["dx"], stream)
         moe_route_bwd(s, b["d_topk_w"], b["topk_w"], b["topk_idx"], b["d_logits"], stream)
         return b["dx"]

@@ -2,6 +2,8 @@
 // Every check runs before any HIP call, so a rejected call enqueues nothing.
 #include <limits.h>
 
+#include <algorithm>
+
 #include "moe_internal.h"
 
 using moe::WsLayout;
@@ -574,6 +576,9 @@ moe_status check_lora(const moe_shape& s, int32_t r) {
   if (st != MOE_OK) return st;
   if (r <= 0) return MOE_EINVAL;
   if (s.dtype != MOE_BF16 || r > 128 || r % 8 != 0) return MOE_EUNSUPPORTED;
+  // The outer products address the sorted rows with 32-bit byte offsets.
+  if (static_cast<int64_t>(s.T) * s.k * std::max(s.H, 2 * s.I) * 2 >= (static_cast<int64_t>(1) << 31))
+    return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 }  // namespace
@@ -634,6 +639,61 @@ moe_status moe_lora_grads(moe_shape s, int32_t r, float scale, const void* x_per
   g.da_down = da_down;
   g.db_down = db_down;
   return from_hip(moe::launch_lora_grads(s, r, scale, g, ws, stream));
+}
+
+moe_status moe_lora_grads_gathered(moe_shape s, int32_t r, float scale, const void* x, const int32_t* row_token,
+                                   const float* row_weight, const void* act, const void* dgu, const void* dy,
+                                   const int32_t* offsets, const void* a_gate, const void* b_gate, const void* a_up,
+                                   const void* b_up, const void* a_down, const void* b_down, float* da_gate,
+                                   float* db_gate, float* da_up, float* db_up, float* da_down, float* db_down,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_lora(s, r);
+  if (st != MOE_OK) return st;
+  if (any_null(x, row_token, row_weight, act, dgu, dy, offsets, a_gate, b_gate, a_up, b_up, a_down, b_down, da_gate,
+               db_gate, da_up, db_up, da_down, db_down, ws))
+    return MOE_EINVAL;
+  if (ws_bytes < moe::lora_layout(s, r).total) return MOE_EWORKSPACE;
+  moe::LoraArgs g{};
+  g.offsets = offsets;
+  g.x_perm = x;
+  g.act = act;
+  g.dgu = dgu;
+  g.do_perm = dy;
+  g.row_token = row_token;
+  g.row_weight = row_weight;
+  g.a_gate = a_gate;
+  g.b_gate = b_gate;
+  g.a_up = a_up;
+  g.b_up = b_up;
+  g.a_down = a_down;
+  g.b_down = b_down;
+  g.da_gate = da_gate;
+  g.db_gate = db_gate;
+  g.da_up = da_up;
+  g.db_up = db_up;
+  g.da_down = da_down;
+  g.db_down = db_down;
+  return from_hip(moe::launch_lora_grads(s, r, scale, g, ws, stream));
+}
+
+moe_status moe_gemm_down_dgrad_dy(moe_shape s, const void* dy, const int32_t* row_token, const float* row_weight,
+                                  const int32_t* offsets, const void* w_down, const void* g, const void* u, void* dgu,
+                                  hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(dy, row_token, row_weight, offsets, w_down, g, u, dgu)) return MOE_EINVAL;
+  if (s.dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (!gathered_x_fits(s)) return MOE_EUNSUPPORTED;  // dy rows: 32-bit byte offsets
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = dy;
+  ga.row_token = row_token;
+  ga.row_weight = row_weight;
+  ga.b0 = w_down;
+  ga.g_in = g;
+  ga.u_in = u;
+  ga.out0 = dgu;
+  return from_hip(moe::launch_gemm(moe::GEMM_DGRAD_DOWN, s, ga, stream));
 }
 
 }  // extern "C"

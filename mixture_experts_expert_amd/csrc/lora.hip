@@ -315,10 +315,13 @@ constexpr int kPK = 64;         // k-chunk
 constexpr int kPLds = kPK + 8;  // LDS row (bf16): 144 bytes, rows 4 banks apart
 
 struct ProjJob {
-  const bf16_t* rows;  // [T*k][K]
+  const bf16_t* rows;  // [T*k][K], or [nsrc][K] read through tok
   const bf16_t* w;     // [E][N][K]
   bf16_t* out;         // [T*k][N]
   int K, N;
+  const int32_t* tok;  // optional: sorted row p reads row tok[p] of rows
+  const float* rw;     // optional: output row p scaled by rw[p] (fp32, before rounding)
+  int nsrc;            // rows of `rows` when gathered
 };
 struct ProjJobs {
   ProjJob job[4];
@@ -381,15 +384,26 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(int E, const int32_t* __
 
   // Buffer ranges start at the chunk's first column: rows past the tile's
   // valid ones fall outside and read zeros. The per-lane offsets stay fixed.
-  const bf16_t* abase = rows + static_cast<int64_t>(r0) * K;
+  // Gathered rows: the range covers the whole source, and each lane's row
+  // offset comes from the row's token (rows past the valid ones get an
+  // offset outside the range).
+  const bool gathered = J.tok != nullptr;
+  const bf16_t* abase = gathered ? rows : rows + static_cast<int64_t>(r0) * K;
+  const int arows = gathered ? J.nsrc : valid;
   const bf16_t* wbase = w + static_cast<int64_t>(e) * N * K;
   // 16-byte pieces of a chunk: piece q is row q / 8, bytes 16 (q % 8) of its 128.
   constexpr int PA = kPR * 8 / kThreads, PB = NMAX * 8 / kThreads;
   uint32_t oa[PA], ob[PB];
 #pragma unroll
   for (int i = 0; i < PA; ++i) {
-    const int q = tid + kThreads * i;
-    oa[i] = 2u * static_cast<uint32_t>((q >> 3) * K) + 16u * (q & 7);
+    const int q = tid + kThreads * i, row = q >> 3;
+    if (gathered) {
+      const rsrc_t rt = make_rsrc(J.tok + r0, 4 * valid);
+      const int t = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(rt, 4u * row, 0, 0));
+      oa[i] = row < valid ? 2u * static_cast<uint32_t>(t * K) + 16u * (q & 7) : kOutOfRange;
+    } else {
+      oa[i] = 2u * static_cast<uint32_t>(row * K) + 16u * (q & 7);
+    }
   }
 #pragma unroll
   for (int i = 0; i < PB; ++i) {
@@ -401,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(int E, const int32_t* __
     // Past the last chunk the ranges are empty: the loads read zeros and
     // touch no memory, so the loop needs no branch around them.
     const bool live = k0 < K;
-    const rsrc_t ra = make_rsrc(abase + (live ? k0 : 0), live ? 2 * (valid * K - k0) : 0);
+    const rsrc_t ra = make_rsrc(abase + (live ? k0 : 0), live ? 2 * (arows * K - k0) : 0);
     const rsrc_t rw = make_rsrc(wbase + (live ? k0 : 0), live ? 2 * (N * K - k0) : 0);
 #pragma unroll
     for (int i = 0; i < PA; ++i) qa[i] = load16(ra, oa[i]);
@@ -460,6 +474,7 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(int E, const int32_t* __
 
   // Lane l: output row wave * 32 + l%32, columns 8i + 4(l/32) .. + 3 of each 32-column block.
   const int row = wave * 32 + l32;
+  const float rwt = J.rw != nullptr && row < valid ? J.rw[r0 + row] : 1.0f;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -473,6 +488,10 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(int E, const int32_t* __
         v[4 + q] = h ? mine1 : other;
       }
       if (row >= valid || nb * 32 >= N) continue;
+      if (J.rw != nullptr) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] *= rwt;
+      }
       uint32_t o[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -552,11 +571,13 @@ __device__ __forceinline__ bf16x8 frag_tr(const bf16_t* tile, int row_elems, int
 }
 
 struct OuterJob {
-  const bf16_t* L;  // [T*k][ldl], columns l0 .. l0 + nl
+  const bf16_t* L;  // [T*k][ldl], columns l0 .. l0 + nl (or [lsrc][ldl] read through ltok)
   const bf16_t* S;  // [T*k][lds], columns s0 .. s0 + ns
   float* out;       // per expert nl * ns floats (out1: the rows j >= ns1 of a TRANS job)
   float* out1;
   int ldl, l0, nl, lds, s0, ns, ns1, rows1;  // rows1: rows of out / out1 per expert (TRANS)
+  const int32_t* ltok;  // optional: sorted row p of L is row ltok[p] of L
+  int lsrc;             // rows of L
 };
 struct OuterJobs {
   OuterJob job[3];
@@ -721,32 +742,51 @@ __global__ __launch_bounds__(kThreads) void outer_kernel(int E, const int32_t* _
   float* const pdst = d.slot >= 0 ? part + static_cast<int64_t>(d.slot) * kOuterPartFloats : nullptr;
   // Pieces of a chunk: L: row q / 16, columns i0 + 8 (q % 16) .. + 7; S: row
   // q / (4 NB), columns 8 (q % (4 NB)) .. + 7. Columns past the window read
-  // zeros (out of range); rows past the expert's fall outside the buffer range.
+  // zeros (out of range); rows past the piece's fall outside the S buffer
+  // range and get an L offset outside L's range. L is addressed by source
+  // row: the sorted row itself, or its token (read two chunks ahead of the
+  // loads that use it, so that waiting for it waits for nothing newer).
   constexpr int PL = kOC * 16 / kThreads, PS = kOC * 4 * NB / kThreads;
-  uint32_t ol[PL], os[PS];
+  uint32_t lcol[PL], os[PS];
 #pragma unroll
   for (int u = 0; u < PL; ++u) {
     const int q = tid + kThreads * u, c = i0 + 8 * (q & 15);
-    ol[u] = c < J.nl ? 2u * static_cast<uint32_t>((q >> 4) * J.ldl + J.l0 + c) : kOutOfRange;
+    lcol[u] = c < J.nl ? 2u * static_cast<uint32_t>(J.l0 + c) : kOutOfRange;
   }
 #pragma unroll
   for (int u = 0; u < PS; ++u) {
     const int q = tid + kThreads * u, c = 8 * (q % (4 * NB));
     os[u] = c < J.ns ? 2u * static_cast<uint32_t>((q / (4 * NB)) * J.lds + J.s0 + c) : kOutOfRange;
   }
-  const bf16_t* lbase = J.L + static_cast<int64_t>(r0) * J.ldl;
+  const rsrc_t rl = make_rsrc(J.L, 2 * J.lsrc * J.ldl);
+  const rsrc_t rtok = make_rsrc(J.ltok != nullptr ? static_cast<const void*>(J.ltok + r0) : static_cast<const void*>(J.L),
+                                J.ltok != nullptr ? 4 * rows : 0);
+  const int tok_add = J.ltok != nullptr ? 0 : r0;  // identity rows: the token is the sorted row
   const bf16_t* sbase = J.S + static_cast<int64_t>(r0) * J.lds;
   uint4 pl[2][PL], ps[2][PS];
-  auto load_chunk = [&](int c, uint4 (&ql)[PL], uint4 (&qs)[PS]) __attribute__((always_inline)) {
+  int tk[2][PL];  // source rows of the chunks to load next (by chunk parity)
+  auto load_tok = [&](int c, int (&t)[PL]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < PL; ++u) {
+      const int row = c * kOC + ((tid + kThreads * u) >> 4);
+      t[u] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(rtok, 4u * static_cast<uint32_t>(row), 0, 0)) +
+             tok_add + (J.ltok != nullptr ? 0 : row);
+    }
+  };
+  auto load_chunk = [&](int c, uint4 (&ql)[PL], uint4 (&qs)[PS], int (&t)[PL]) __attribute__((always_inline)) {
     const int p0 = c * kOC;
     const bool live = p0 < rows;
     const int left = live ? min(rows - p0, kOC) : 0;  // the rows this chunk can address
-    const rsrc_t rl = make_rsrc(lbase + (live ? static_cast<int64_t>(p0) * J.ldl : 0), 2 * left * J.ldl);
     const rsrc_t rs = make_rsrc(sbase + (live ? static_cast<int64_t>(p0) * J.lds : 0), 2 * left * J.lds);
 #pragma unroll
-    for (int u = 0; u < PL; ++u) ql[u] = load16(rl, ol[u]);
+    for (int u = 0; u < PL; ++u) {
+      const int row = p0 + ((tid + kThreads * u) >> 4);
+      const uint32_t off = row < rows ? 2u * static_cast<uint32_t>(t[u] * J.ldl) + lcol[u] : kOutOfRange;
+      ql[u] = load16(rl, lcol[u] == kOutOfRange ? kOutOfRange : off);
+    }
 #pragma unroll
     for (int u = 0; u < PS; ++u) qs[u] = load16(rs, os[u]);
+    load_tok(c + 2, t);  // this register set's next chunk
   };
   auto store_chunk = [&](int buf, const uint4 (&ql)[PL], const uint4 (&qs)[PS]) __attribute__((always_inline)) {
 #pragma unroll
@@ -768,14 +808,16 @@ __global__ __launch_bounds__(kThreads) void outer_kernel(int E, const int32_t* _
   // c + 1, the other takes chunk c + 2; the chunk count is rounded up to even
   // (a chunk past the rows is all zeros).
   const int nch = ((rows + kOC - 1) / kOC + 1) & ~1;
-  load_chunk(0, pl[0], ps[0]);
-  load_chunk(1, pl[1], ps[1]);
+  load_tok(0, tk[0]);
+  load_tok(1, tk[1]);
+  load_chunk(0, pl[0], ps[0], tk[0]);
+  load_chunk(1, pl[1], ps[1], tk[1]);
   store_chunk(0, pl[0], ps[0]);
   lds_barrier();
-  auto step = [&](int c, uint4 (&nl_)[PL], uint4 (&ns_)[PS], uint4 (&cl)[PL], uint4 (&cs)[PS])
+  auto step = [&](int c, uint4 (&nl_)[PL], uint4 (&ns_)[PS], uint4 (&cl)[PL], uint4 (&cs)[PS], int (&tkn)[PL])
       __attribute__((always_inline)) {
     const int buf = c & 1;
-    load_chunk(c + 2, nl_, ns_);
+    load_chunk(c + 2, nl_, ns_, tkn);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int sl = 0; sl < kOC / 16; ++sl) {
@@ -791,8 +833,8 @@ __global__ __launch_bounds__(kThreads) void outer_kernel(int E, const int32_t* _
     lds_barrier();
   };
   for (int c = 0; c < nch; c += 2) {
-    step(c, pl[0], ps[0], pl[1], ps[1]);
-    step(c + 1, pl[1], ps[1], pl[0], ps[0]);
+    step(c, pl[0], ps[0], pl[1], ps[1], tk[0]);
+    step(c + 1, pl[1], ps[1], pl[0], ps[0], tk[1]);
   }
 
   // Lane l holds D[8q + 4(l/32) + u][l%32], u < 4, of each 32 x 32 block nb.
@@ -1035,13 +1077,21 @@ hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraA
   MOE_TRY(hipGetLastError());
   // Row projections Z = X (sA)^T, Y = dY (sB): [Z_gate | Z_up], [dG sB_gate |
   // dU sB_up], Z_down, dO sB_down.
+  // With row_token, x and dy are read through the sorted rows' tokens, and
+  // dO = w dy enters through the weight applied in fp32 to the two
+  // projections that carry it: Z_down' = w Z_down (for dB_down = dy^T Z_down')
+  // and Y_down = w (dy sB_down).
+  const int32_t* tok = g.row_token;
+  const float* rwt = tok != nullptr ? g.row_weight : nullptr;
+  const int M = s.T * s.k, nsrc = tok != nullptr ? s.T : M;
   {
     ProjJobs pj{};
     const bf16_t* xp = static_cast<const bf16_t*>(g.x_perm);
-    pj.job[0] = {xp, sa_gu, static_cast<bf16_t*>(z_gu), H, 2 * rp};
-    pj.job[1] = {static_cast<const bf16_t*>(g.dgu), sbt_gu, static_cast<bf16_t*>(y_gu), 2 * I, 2 * rp};
-    pj.job[2] = {static_cast<const bf16_t*>(g.act), sa_d, static_cast<bf16_t*>(z_d), I, rp};
-    pj.job[3] = {static_cast<const bf16_t*>(g.do_perm), sbt_d, static_cast<bf16_t*>(y_d), H, rp};
+    pj.job[0] = {xp, sa_gu, static_cast<bf16_t*>(z_gu), H, 2 * rp, tok, nullptr, nsrc};
+    pj.job[1] = {static_cast<const bf16_t*>(g.dgu), sbt_gu, static_cast<bf16_t*>(y_gu), 2 * I, 2 * rp, nullptr,
+                 nullptr, M};
+    pj.job[2] = {static_cast<const bf16_t*>(g.act), sa_d, static_cast<bf16_t*>(z_d), I, rp, nullptr, rwt, M};
+    pj.job[3] = {static_cast<const bf16_t*>(g.do_perm), sbt_d, static_cast<bf16_t*>(y_d), H, rp, tok, rwt, nsrc};
     pj.n = 4;
     MOE_TRY(projections(s, 2 * rp, g.offsets, pj, st));
   }
@@ -1052,10 +1102,12 @@ hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraA
   {
     const bf16_t* dgu = static_cast<const bf16_t*>(g.dgu);
     OuterJobs ob{};
-    ob.job[0] = {dgu, static_cast<const bf16_t*>(z_gu), g.db_gate, nullptr, 2 * I, 0, I, 2 * rp, 0, r, r, r};
-    ob.job[1] = {dgu, static_cast<const bf16_t*>(z_gu), g.db_up, nullptr, 2 * I, I, I, 2 * rp, rp, r, r, r};
+    ob.job[0] = {dgu, static_cast<const bf16_t*>(z_gu), g.db_gate, nullptr, 2 * I, 0, I, 2 * rp, 0, r, r, r,
+                 nullptr, M};
+    ob.job[1] = {dgu, static_cast<const bf16_t*>(z_gu), g.db_up, nullptr, 2 * I, I, I, 2 * rp, rp, r, r, r,
+                 nullptr, M};
     ob.job[2] = {static_cast<const bf16_t*>(g.do_perm), static_cast<const bf16_t*>(z_d), g.db_down, nullptr, H, 0,
-                 H, rp, 0, r, r, r};
+                 H, rp, 0, r, r, r, tok, nsrc};
     ob.n = 3;
     const int64_t max_tiles = (2 * ceil_div(I, 128) + ceil_div(H, 128)) * static_cast<int64_t>(E) + 2 * outer_grid();
     OuterSpace os{};
@@ -1066,9 +1118,9 @@ hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraA
     MOE_TRY(outer_products<false>(E, (r + 31) / 32, g.offsets, ob, os, st));
     OuterJobs oa{};
     oa.job[0] = {static_cast<const bf16_t*>(g.x_perm), static_cast<const bf16_t*>(y_gu), g.da_gate, g.da_up, H, 0,
-                 H, 2 * rp, 0, 2 * rp, rp, r};
+                 H, 2 * rp, 0, 2 * rp, rp, r, tok, nsrc};
     oa.job[1] = {static_cast<const bf16_t*>(g.act), static_cast<const bf16_t*>(y_d), g.da_down, nullptr, I, 0, I, rp,
-                 0, r, r, r};
+                 0, r, r, r, nullptr, M};
     oa.n = 2;
     MOE_TRY(outer_products<true>(E, 2 * rp / 32, g.offsets, oa, os, st));
   }

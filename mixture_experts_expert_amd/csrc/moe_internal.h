@@ -195,10 +195,12 @@ LoraLayout lora_layout(const moe_shape& s, int r);
 
 struct LoraArgs {
   const int32_t* offsets;
-  const void* x_perm;   // [T*k][H]
+  const void* x_perm;   // [T*k][H], or x [T][H] with row_token
   const void* act;      // [T*k][I]
   const void* dgu;      // [T*k][2I]
-  const void* do_perm;  // [T*k][H]
+  const void* do_perm;  // [T*k][H], or dy [T][H] with row_token (dO row p = row_weight[p] dy[row_token[p]])
+  const int32_t* row_token;  // optional: x_perm and do_perm are x and dy read through it
+  const float* row_weight;
   const void *a_gate, *b_gate, *a_up, *b_up, *a_down, *b_down;
   float *da_gate, *db_gate, *da_up, *db_up, *da_down, *db_down;
 };

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(B):
     names = declared_functions()
-    assert len(names) == 35, names
+    assert len(names) == 37, names
     for n in names:
         assert hasattr(B.lib, n), n
 
@@ -158,6 +158,20 @@ def test_lora_validation(B):
     assert G(s, 20, 1.0, *P, need, None) == 2
     assert G(B.shape(64, 96, 8, 2, 64, "bf16"), 16, 1.0, *P, need, None) == 2
     assert G(s, 16, 1.0, *P[:5], None, *P[6:], need, None) == 1
+    # sorted rows addressed with 32-bit byte offsets: T k max(H, 2I) < 2^30
+    big = B.shape(1 << 17, 2048, 8, 8, 64, "bf16")
+    assert G(big, 16, 1.0, *P, 1 << 40, None) == 2
+    # without x_perm and do_perm: every pointer, the same limits
+    GG = B.lib.moe_lora_grads_gathered
+    Q = [F] * 20
+    assert GG(s, 16, 1.0, *Q, need - 1, None) == 3
+    assert GG(s, 20, 1.0, *Q, need, None) == 2
+    assert GG(s, 16, 1.0, *Q[:1], None, *Q[2:], need, None) == 1   # row_token
+    assert GG(s, 16, 1.0, *Q[:2], None, *Q[3:], need, None) == 1   # row_weight
+    assert GG(big, 16, 1.0, *Q, 1 << 40, None) == 2
+    DD = B.lib.moe_gemm_down_dgrad_dy
+    assert DD(B.shape(64, 128, 8, 2, 64, "f32"), *([F] * 8), None) == 2
+    assert DD(s, F, None, *([F] * 6), None) == 1
 
 
 def test_binding_raises_on_error(B):

@@ -7,10 +7,12 @@ the C ABI.
 - The stage with adapters (LoRAStage: merge, the forward on W', the data
   gradients, moe_lora_grads): routing bit-exact; y, dx, d_topk_w, d_logits
   and the six adapter gradients within the bf16 tolerance of the float64
-  oracle. Small shapes cover a padded rank (16 -> 64) and an unpadded one,
+  oracle. Small shapes cover padded ranks (8, 16 -> 32) and unpadded ones,
   experts with no rows (zero gradients), many experts, a split-K reduction
   and the ranks 72 and 96; the full 30B-A3B training shape is checked on
-  every element (per token, per expert).
+  every element (per token, per expert). Each also without x_perm and
+  do_perm (LoRAStage(gathered=True): moe_gemm_down_dgrad_dy and
+  moe_lora_grads_gathered).
 """
 import numpy as np
 import pytest
@@ -58,12 +60,12 @@ def test_merge(E, N, K, r, in_place):
     assert frac >= 0.999
 
 
-def lora_run(d: U.DevInputs, r: int, s: float, adapters):
+def lora_run(d: U.DevInputs, r: int, s: float, adapters, gathered: bool = False):
     from mixture_experts_expert_amd import binding as B
     c = d.cfg
     T = d.t["x"].shape[0]
     ad = {n: U.to_dev(adapters[n]) for n in NAMES}
-    st = B.LoRAStage(T, c.H, c.E, c.k, c.I, r, s)
+    st = B.LoRAStage(T, c.H, c.E, c.k, c.I, r, s, gathered=gathered)
     st.forward(d.t["x"], d.t["w_router"], d.t["w_gate"], d.t["w_up"], d.t["w_down"], ad, d.bias)
     st.backward(d.t["dy"])
     torch.cuda.synchronize()
@@ -110,15 +112,18 @@ SMALL_LORA = [
 ]
 
 
+@pytest.mark.parametrize("gathered", [False, True], ids=["x_perm", "gathered"])
 @pytest.mark.parametrize("cfg,r", SMALL_LORA, ids=[f"{c.name}-r{r}" for c, r in SMALL_LORA])
-def test_lora_stage_small(cfg, r):
-    U.say(f"[lora stage] {cfg} r={r}")
-    U.begin(f"lora_r{r}.{cfg.name}", f"{cfg} seed 8, adapters rank {r}")
+def test_lora_stage_small(cfg, r, gathered):
+    """gathered: neither x_perm nor do_perm (x and dy read through the sorted
+    rows' tokens in the GEMMs and the adapter gradients)."""
+    U.say(f"[lora stage] {cfg} r={r} gathered={gathered}")
+    U.begin(f"lora_r{r}{'_gathered' if gathered else ''}.{cfg.name}", f"{cfg} seed 8, adapters rank {r}")
     s = 2.0 if r == 64 else 0.75
     inp = synth.make_inputs(cfg, seed=8, with_dy=True)
     adapters = synth.make_adapters(cfg, r, seed=8)
     d = U.DevInputs(inp)
-    st = lora_run(d, r, s, adapters)
+    st = lora_run(d, r, s, adapters, gathered)
     ref_r = U.oracle_route(inp)
     U.check_routing(st, ref_r)
     ref = oracle_lora(inp, adapters, s, ref_r["topk_idx"], ref_r["topk_w"])
@@ -131,17 +136,18 @@ def test_lora_stage_small(cfg, r):
 
 
 @pytest.mark.timeout(900)
-def test_lora_stage_qwen3_30b_a3b_full():
+@pytest.mark.parametrize("gathered", [False, True], ids=["x_perm", "gathered"])
+def test_lora_stage_qwen3_30b_a3b_full(gathered):
     """T=8192, H=2048, E=128, k=8, I=768, r=64, s=2: every element of y, dx,
     d_topk_w, d_logits and of all six adapter gradients."""
     cfg = synth.CONFIGS["qwen3_30b_a3b_train"]
     r, s = 64, 2.0
-    U.say(f"[lora stage] {cfg} r={r}")
-    U.begin("lora_r64." + cfg.name, f"{cfg} seed 0, adapters rank {r}, scale {s}")
+    U.say(f"[lora stage] {cfg} r={r} gathered={gathered}")
+    U.begin(f"lora_r64{'_gathered' if gathered else ''}." + cfg.name, f"{cfg} seed 0, adapters rank {r}, scale {s}")
     inp = synth.make_inputs(cfg, seed=0)
     adapters = synth.make_adapters(cfg, r, seed=0)
     d = U.DevInputs(inp)
-    st = lora_run(d, r, s, adapters)
+    st = lora_run(d, r, s, adapters, gathered)
     ref_r = U.oracle_route(inp)
     U.check_routing(st, ref_r)
     U.say("  adapter oracle on all tokens")
