@@ -49,6 +49,21 @@ def merge_fp8(wq: np.ndarray, e8: np.ndarray, a: np.ndarray, b: np.ndarray, s: f
     return merge(dequantize_weights(wq, e8), a, b, s)
 
 
+def dequantize_weights_mxfp4(wq: np.ndarray, e8: np.ndarray) -> np.ndarray:
+    """Frozen expert weights in 4 bits (the OCP microscaling FP4 format of
+    oracle/mxfp4.py): packed codes wq [E, N, K/2] with one E8M0 scale per 32
+    elements of a row, e8 [E, N, K/32] -> float64 [E, N, K]."""
+    from oracle import mxfp4 as MX
+    E, N, K2 = wq.shape
+    return MX.dequantize_blocks(np.asarray(wq).reshape(E * N, K2),
+                                np.asarray(e8).reshape(E * N, -1)).reshape(E, N, 2 * K2)
+
+
+def merge_mxfp4(wq: np.ndarray, e8: np.ndarray, a: np.ndarray, b: np.ndarray, s: float) -> np.ndarray:
+    """W' = deq(Wq) + s B A over a 4-bit frozen base."""
+    return merge(dequantize_weights_mxfp4(wq, e8), a, b, s)
+
+
 def forward_backward(x, dy, topk_idx, topk_w, w_gate, w_up, w_down, ad: Dict[str, np.ndarray], s: float):
     """The stage with adapters, forward and backward, in float64.
 
