@@ -55,7 +55,7 @@ GEMMs on their own (whose TFLOP/s join `gemm_tflops`); `inference_forward_ms`
 the forward alone, unfused and fused (no x_perm, routing weights in the down
 GEMM's epilogue); `lora_ms` the training step with rank-64 adapters on frozen
 experts (merges, forward on the merged weights, data and adapter gradients)
-and its two adapter calls, over bf16 and over E4M3 frozen weights, and the
+and its two adapter calls, over bf16, E4M3 and MXFP4 frozen weights, and the
 step without x_perm and do_perm (`step_gathered`, with
 `moe_lora_grads_gathered`). `--timed-only` skips these and the CPU baseline, so that
 under a profiler the last K launches of every kernel are the timed steps.
@@ -294,6 +294,18 @@ def lora_timing(cfg, seed: int, tensors, bias, stream, r: int = 64, scale: float
 
     out["step_fp8_base"] = round(time_calls(lora_step_fp8, stream), 4)
     out["moe_lora_merge_fp8_x3"] = round(time_calls(lambda: ls.merge(w8.gate, w8.up, w8.down, ad), stream, reps=5), 4)
+    del w8
+    # And over MXFP4 frozen experts (E2M1, a scale per 32 elements).
+    w4 = B.MXFP4Weights(wg, wu, wd)
+
+    def lora_step_mxfp4():
+        ls.forward(x, wr, w4.gate, w4.up, w4.down, ad, bias)
+        ls.backward(dy)
+
+    out["step_mxfp4_base"] = round(time_calls(lora_step_mxfp4, stream), 4)
+    out["moe_lora_merge_mxfp4_x3"] = round(time_calls(lambda: ls.merge(w4.gate, w4.up, w4.down, ad), stream,
+                                                      reps=5), 4)
+    del w4
     out["moe_lora_grads"] = round(time_calls(lambda: B.moe_lora_grads(
         ls.s, r, scale, lb["x_perm"], lb["a"], lb["dgu"], lb["do_perm"], lb["offsets"],
         *(ad[n] for n in B.LORA_NAMES), *(lb["d" + n] for n in B.LORA_NAMES), ls.lora_ws), stream, reps=5), 4)

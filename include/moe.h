@@ -448,6 +448,32 @@ moe_status moe_lora_merge(int32_t E, int32_t N, int32_t K, int32_t r, float scal
 moe_status moe_lora_merge_fp8(int32_t E, int32_t N, int32_t K, int32_t r, float scale, const uint8_t* wq,
                               const uint8_t* w_e8, const void* a, const void* b, void* w_out, hipStream_t stream);
 
+/* Adapters over 4-bit frozen experts (sourcepulse summary, "Highlighted
+ * Details": QLoRA over 4-bit bases; "Quick Start & Requirements":
+ * bitsandbytes 4-bit weights), in the 4-bit format native to gfx950: the
+ * OCP microscaling FP4 (MXFP4). Elements are E2M1 (sign, 2 exponent bits
+ * with bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two
+ * per byte with the even element in the low nibble; every 32 consecutive
+ * elements of a row share one E8M0 scale byte c (2^(c - 127)).
+ *
+ * moe_quantize_mxfp4_rows: rows [rows, K] of bf16 (K % 32 == 0, else
+ * MOE_EINVAL) -> codes q [rows, K/2] and scales e8 [rows, K/32]. A block's
+ * scale is 2^X with X the smallest integer for which max |block| / 2^X <= 6,
+ * clamped to [-127, 127] (-127 for an all-zero block), so nothing is
+ * clipped; each element is x / 2^X rounded to the nearest E2M1 magnitude,
+ * ties to the even mantissa, with x's sign (a negative value that rounds to
+ * zero is a negative zero). Inputs must be finite. */
+moe_status moe_quantize_mxfp4_rows(int32_t rows, int32_t K, const void* in, uint8_t* q, uint8_t* e8,
+                                   hipStream_t stream);
+
+/* W'[e] = bf16(deq(wq[e]) + s * B[e] A[e]) over MXFP4 frozen weights: wq
+ * [E,N,K/2] codes and w_e8 [E,N,K/32] scales as moe_quantize_mxfp4_rows
+ * writes them for the E*N rows of a stacked weight; deq exact in fp32. a, b,
+ * w_out as in moe_lora_merge. K % 32 == 0 and the limits of moe_lora_merge
+ * (MOE_EUNSUPPORTED otherwise). */
+moe_status moe_lora_merge_mxfp4(int32_t E, int32_t N, int32_t K, int32_t r, float scale, const uint8_t* wq,
+                                const uint8_t* w_e8, const void* a, const void* b, void* w_out, hipStream_t stream);
+
 /* Bytes of device workspace for moe_lora_grads at this shape and rank (0 if
  * either is rejected): the scaled adapters and the rank-wide row
  * projections. */

@@ -81,6 +81,8 @@ _SIGS = {
     "moe_lora_merge_fp8": ([ctypes.c_int32] * 4 + [ctypes.c_float] + [_P] * 6, ctypes.c_int),
     "moe_lora_grads": ([moe_shape, ctypes.c_int32, ctypes.c_float] + [_P] * 18 + [ctypes.c_size_t, _P],
                        ctypes.c_int),
+    "moe_quantize_mxfp4_rows": ([ctypes.c_int32, ctypes.c_int32] + [_P] * 4, ctypes.c_int),
+    "moe_lora_merge_mxfp4": ([ctypes.c_int32] * 4 + [ctypes.c_float] + [_P] * 6, ctypes.c_int),
     "moe_lora_grads_gathered": ([moe_shape, ctypes.c_int32, ctypes.c_float] + [_P] * 20 + [ctypes.c_size_t, _P],
                                 ctypes.c_int),
     "moe_gemm_down_dgrad_dy": ([moe_shape] + [_P] * 9, ctypes.c_int),
@@ -265,6 +267,42 @@ class FP8Weights:
         moe_quantize_fp8_rows(E * H, I, w_down, self.down[0], self.down[1], stream=stream)
 
 
+def moe_quantize_mxfp4_rows(rows, K, inp, q, e8, stream=None):
+    _check("moe_quantize_mxfp4_rows", lib.moe_quantize_mxfp4_rows(int(rows), int(K), _ptr(inp), _ptr(q), _ptr(e8),
+                                                                  _stream(stream)))
+
+
+def moe_lora_merge_mxfp4(E, N, K, r, scale, wq, w_e8, a, b, w_out, stream=None):
+    _check("moe_lora_merge_mxfp4", lib.moe_lora_merge_mxfp4(int(E), int(N), int(K), int(r), float(scale), _ptr(wq),
+                                                            _ptr(w_e8), _ptr(a), _ptr(b), _ptr(w_out),
+                                                            _stream(stream)))
+
+
+class MXFP4Tensor(tuple):
+    """(codes [E,N,K/2] uint8, E8M0 scales [E,N,K/32] uint8) of one stacked
+    weight in MXFP4 (moe_quantize_mxfp4_rows)."""
+
+
+class MXFP4Weights:
+    """Expert weights quantised once to MXFP4 (E2M1, one E8M0 scale per 32
+    elements along the reduction axis), for adapters over a 4-bit frozen
+    base: gate/up codes [E,I,H/2] and scales [E,I,H/32], down [E,H,I/2] and
+    [E,H,I/32]."""
+
+    def __init__(self, w_gate, w_up, w_down, stream=None):
+        E, I, H = w_gate.shape
+        dev = w_gate.device
+        u8 = torch.uint8
+
+        def quant(w, N, K):
+            t = MXFP4Tensor((torch.empty(E, N, K // 2, dtype=u8, device=dev),
+                             torch.empty(E, N, K // 32, dtype=u8, device=dev)))
+            moe_quantize_mxfp4_rows(E * N, K, w, t[0], t[1], stream=stream)
+            return t
+
+        self.gate, self.up, self.down = quant(w_gate, I, H), quant(w_up, I, H), quant(w_down, H, I)
+
+
 def moe_gemm_down_bwd(s, do_perm, a, offsets, w_down, g, u, dgu, dw_down, accumulate_dw, ws, ws_bytes=None,
                       stream=None):
     nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
@@ -352,9 +390,12 @@ def moe_lora_merge_fp8(E, N, K, r, scale, wq, w_e8, a, b, w_out, stream=None):
 
 
 def _merge_any(E, N, K, r, scale, w, a, b, w_out, stream=None):
-    """moe_lora_merge for a bf16 frozen weight, moe_lora_merge_fp8 for an
+    """moe_lora_merge for a bf16 frozen weight, moe_lora_merge_mxfp4 for an
+    MXFP4Tensor (MXFP4Weights.gate / .up / .down), moe_lora_merge_fp8 for an
     (E4M3 codes, E8M0 row scales) pair (FP8Weights.gate / .up / .down)."""
-    if isinstance(w, tuple):
+    if isinstance(w, MXFP4Tensor):
+        moe_lora_merge_mxfp4(E, N, K, r, scale, w[0], w[1], a, b, w_out, stream)
+    elif isinstance(w, tuple):
         moe_lora_merge_fp8(E, N, K, r, scale, w[0], w[1], a, b, w_out, stream)
     else:
         moe_lora_merge(E, N, K, r, scale, w, a, b, w_out, stream)
@@ -567,8 +608,9 @@ class LoRAStage(MoEStage):
     moe_lora_grads, and returns dx. The adapter gradients (float32) are in
     ``buf["d" + name]``; the frozen weights get none. ``adapters``: a_P
     [E,r,K], b_P [E,N,r] bf16 for P in gate, up, down. Each frozen weight is
-    a bf16 tensor or, kept in 8 bits (QLoRA-style), the (E4M3 codes, E8M0
-    row scales) pair of FP8Weights (moe_lora_merge_fp8 dequantises it).
+    a bf16 tensor or, kept in 8 or 4 bits (QLoRA-style), the (E4M3 codes,
+    E8M0 row scales) pair of FP8Weights or the MXFP4Tensor of MXFP4Weights
+    (moe_lora_merge_fp8 or moe_lora_merge_mxfp4 dequantises it).
 
     ``gathered``: neither x_perm nor do_perm. The forward reads x through the
     sorted rows' tokens (moe_permute_fused, moe_gemm_gate_up_gathered); the

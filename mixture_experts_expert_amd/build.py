@@ -20,7 +20,8 @@ ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 
-SOURCES = ["api.hip", "route.hip", "permute.hip", "combine.hip", "fp8.hip", "lora.hip", "gemm_f32.hip", "gemm_bf16.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "combine.hip", "fp8.hip", "mxfp4.hip", "lora.hip", "gemm_f32.hip",
+           "gemm_bf16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -609,6 +609,22 @@ moe_status moe_lora_merge_fp8(int32_t E, int32_t N, int32_t K, int32_t r, float 
   return from_hip(moe::launch_lora_merge_fp8(E, N, K, r, scale, wq, w_e8, a, b, w_out, stream));
 }
 
+moe_status moe_quantize_mxfp4_rows(int32_t rows, int32_t K, const void* in, uint8_t* q, uint8_t* e8,
+                                   hipStream_t stream) {
+  if (rows < 0 || K <= 0 || K % 32 != 0) return MOE_EINVAL;
+  if (any_null(in, q, e8)) return MOE_EINVAL;
+  return from_hip(moe::launch_quantize_mxfp4_rows(rows, K, in, q, e8, stream));
+}
+
+moe_status moe_lora_merge_mxfp4(int32_t E, int32_t N, int32_t K, int32_t r, float scale, const uint8_t* wq,
+                                const uint8_t* w_e8, const void* a, const void* b, void* w_out, hipStream_t stream) {
+  if (E <= 0 || N <= 0 || K <= 0 || r <= 0) return MOE_EINVAL;
+  if (any_null(wq, w_e8, a, b, w_out)) return MOE_EINVAL;
+  if (r > 128 || r % 8 != 0 || K % 32 != 0 || E > 65535 || (N + 127) / 128 > 65535) return MOE_EUNSUPPORTED;
+  if ((static_cast<int64_t>(N) + 256) * K >= (static_cast<int64_t>(1) << 30)) return MOE_EUNSUPPORTED;
+  return from_hip(moe::launch_lora_merge_mxfp4(E, N, K, r, scale, wq, w_e8, a, b, w_out, stream));
+}
+
 moe_status moe_lora_grads(moe_shape s, int32_t r, float scale, const void* x_perm, const void* act, const void* dgu,
                           const void* do_perm, const int32_t* offsets, const void* a_gate, const void* b_gate,
                           const void* a_up, const void* b_up, const void* a_down, const void* b_down, float* da_gate,

@@ -76,12 +76,24 @@ __device__ __forceinline__ float bf16f(bf16_t v) { return __uint_as_float(static
 // steps. w_out may be w: every element is read and written by the same
 // thread.
 //
-// FP8W: the frozen W arrives as E4M3 codes [E][N][K] with one E8M0 scale
-// per row (w8 [E][N], 2^(c - 127)): each element is decoded to fp32 (the
-// hardware conversion, exact) and multiplied by its row's power of two
-// (exact) before the add, so W' = bf16(deq(W) + s B A) with the same single
-// rounding as the bf16 form.
-template <int NS, bool FP8W>
+// WF (the frozen W's format): kBf16; kE4M3, codes [E][N][K] with one E8M0
+// scale per row (w8 [E][N], 2^(c - 127)); kMxfp4, E2M1 codes two per byte
+// [E][N][K/2] (even element in the low nibble) with one E8M0 scale per 32
+// elements of a row (w8 [E][N][K/32]). Each element is decoded to fp32
+// (exact) and multiplied by its scale (exact) before the add, so W' =
+// bf16(deq(W) + s B A) with the same single rounding as the bf16 form.
+enum WFormat : int { kBf16 = 0, kE4M3 = 1, kMxfp4 = 2 };
+
+// E2M1 code (4 bits) -> float: exponent field 0 is m / 2, otherwise
+// (1 + m / 2) 2^(e - 1); the sign bit kept (a negative zero too).
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const int e = static_cast<int>((c >> 1) & 3u);
+  const float m = static_cast<float>(c & 1u);
+  const float mag = e == 0 ? 0.5f * m : ldexpf(1.0f + 0.5f * m, e - 1);
+  return (c & 8u) ? -mag : mag;
+}
+
+template <int NS, int WF>
 __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, float s, const void* wv_in,
                                                          const uint8_t* __restrict__ w8,
                                                          const bf16_t* __restrict__ a, const bf16_t* __restrict__ b,
@@ -121,13 +133,18 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
   const bf16_t* be = b + static_cast<int64_t>(e) * N * r;
   const bool cok = c0 + rcol < K;
   bf16x8 fb[2][NS];
-  // W row runs of the current and the next row tile: 8 bf16 (16 bytes) or
-  // 8 E4M3 codes (8 bytes) per thread and pass, and (FP8W) the row's scale.
-  typedef std::conditional_t<FP8W, uint2, uint4> WRun;
+  // W row runs of the current and the next row tile: 8 bf16 (16 bytes), 8
+  // E4M3 codes (8 bytes) or 8 E2M1 codes (4 bytes) per thread and pass, and
+  // the scale of the row (E4M3) or of the row's 32-element block (E2M1).
+  typedef std::conditional_t<WF == kBf16, uint4, std::conditional_t<WF == kE4M3, uint2, uint32_t>> WRun;
   WRun wv[2][kMT / 16];
   int wsc[2][kMT / 16];
-  const rsrc_t rw = FP8W ? make_rsrc(static_cast<const uint8_t*>(wv_in) + wbase, N * K) : make_rsrc(w + wbase, 2 * N * K);
-  const rsrc_t rsc = make_rsrc(w8 + (FP8W ? static_cast<int64_t>(e) * N : 0), FP8W ? N : 0);
+  const uint8_t* w_codes = static_cast<const uint8_t*>(wv_in);
+  const rsrc_t rw = WF == kE4M3   ? make_rsrc(w_codes + wbase, N * K)
+                    : WF == kMxfp4 ? make_rsrc(w_codes + wbase / 2, N * (K / 2))
+                                   : make_rsrc(w + wbase, 2 * N * K);
+  const int nsc = WF == kE4M3 ? N : (WF == kMxfp4 ? N * (K / 32) : 0);  // scales of one expert
+  const rsrc_t rsc = make_rsrc(w8 + (WF == kBf16 ? 0 : static_cast<int64_t>(e) * nsc), nsc);
   const rsrc_t rb = make_rsrc(be, 2 * N * r);
   auto load_tile = [&](int nt, WRun (&wt)[kMT / 16], int (&sc)[kMT / 16]) __attribute__((always_inline)) {
 #pragma unroll
@@ -142,11 +159,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
 #pragma unroll
     for (int q = 0; q < kMT / 16; ++q) {
       const int n = nt + 16 * q + rrow;
-      if constexpr (FP8W) {
+      if constexpr (WF == kE4M3) {
         const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rw, cok ? static_cast<uint32_t>(n * K + c0 + rcol)
                                                                      : kOutOfRange, 0, 0);
         wt[q] = make_uint2(v.x, v.y);
         sc[q] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b8(rsc, static_cast<uint32_t>(n), 0, 0));
+      } else if constexpr (WF == kMxfp4) {
+        wt[q] = __builtin_amdgcn_raw_buffer_load_b32(rw, cok ? static_cast<uint32_t>(n * K + c0 + rcol) / 2
+                                                             : kOutOfRange, 0, 0);
+        sc[q] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b8(
+            rsc, cok ? static_cast<uint32_t>(n * (K / 32) + (c0 + rcol) / 32) : kOutOfRange, 0, 0));
       } else {
         wt[q] = load16(rw, cok ? 2u * static_cast<uint32_t>(n * K + c0 + rcol) : kOutOfRange);
         sc[q] = 0;
@@ -192,7 +214,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
       const float4 v0 = *reinterpret_cast<const float4*>(sp), v1 = *reinterpret_cast<const float4*>(sp + 4);
       const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       float wf[8];
-      if constexpr (FP8W) {
+      if constexpr (WF == kMxfp4) {
+        const int X = (wsc[t & 1][q] & 0xff) - 127;  // the block's E8M0 scale
+        const uint32_t c8 = wc_t[q];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) wf[p] = ldexpf(e2m1_value((c8 >> (4 * p)) & 15u), X);
+      } else if constexpr (WF == kE4M3) {
         const int X = (wsc[t & 1][q] & 0xff) - 127;  // the row's E8M0 scale
         const uint32_t c2[2] = {wc_t[q].x, wc_t[q].y};
 #pragma unroll
@@ -1009,7 +1036,7 @@ LoraLayout lora_layout(const moe_shape& s, int r) {
 }
 
 namespace {
-template <bool FP8W>
+template <int WF>
 hipError_t merge_launch(int E, int N, int K, int r, float s, const void* w, const uint8_t* w8, const void* a,
                         const void* b, void* w_out, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(ceil_div(K, kMT)), static_cast<unsigned>(ceil_div(N, kMT * kMergeRowTiles)),
@@ -1018,14 +1045,14 @@ hipError_t merge_launch(int E, int N, int K, int r, float s, const void* w, cons
   const bf16_t* bp = static_cast<const bf16_t*>(b);
   bf16_t* op = static_cast<bf16_t*>(w_out);
   switch ((r + 15) / 16) {
-    case 1: merge_kernel<1, FP8W><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
-    case 2: merge_kernel<2, FP8W><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
-    case 3: merge_kernel<3, FP8W><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
-    case 4: merge_kernel<4, FP8W><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
-    case 5: merge_kernel<5, FP8W><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
-    case 6: merge_kernel<6, FP8W><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
-    case 7: merge_kernel<7, FP8W><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
-    case 8: merge_kernel<8, FP8W><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
+    case 1: merge_kernel<1, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
+    case 2: merge_kernel<2, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
+    case 3: merge_kernel<3, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
+    case 4: merge_kernel<4, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
+    case 5: merge_kernel<5, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
+    case 6: merge_kernel<6, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
+    case 7: merge_kernel<7, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
+    case 8: merge_kernel<8, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1034,12 +1061,17 @@ hipError_t merge_launch(int E, int N, int K, int r, float s, const void* w, cons
 
 hipError_t launch_lora_merge(int E, int N, int K, int r, float s, const void* w, const void* a, const void* b,
                              void* w_out, hipStream_t st) {
-  return merge_launch<false>(E, N, K, r, s, w, nullptr, a, b, w_out, st);
+  return merge_launch<kBf16>(E, N, K, r, s, w, nullptr, a, b, w_out, st);
 }
 
 hipError_t launch_lora_merge_fp8(int E, int N, int K, int r, float s, const uint8_t* wq, const uint8_t* w8,
                                  const void* a, const void* b, void* w_out, hipStream_t st) {
-  return merge_launch<true>(E, N, K, r, s, wq, w8, a, b, w_out, st);
+  return merge_launch<kE4M3>(E, N, K, r, s, wq, w8, a, b, w_out, st);
+}
+
+hipError_t launch_lora_merge_mxfp4(int E, int N, int K, int r, float s, const uint8_t* wq, const uint8_t* w8,
+                                   const void* a, const void* b, void* w_out, hipStream_t st) {
+  return merge_launch<kMxfp4>(E, N, K, r, s, wq, w8, a, b, w_out, st);
 }
 
 hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraArgs& g, void* ws, hipStream_t st) {

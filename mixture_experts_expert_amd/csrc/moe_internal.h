@@ -164,6 +164,10 @@ inline hipError_t launch_gemm(GemmMode mode, const moe_shape& s, const GemmArgs&
 // (E8M0 byte). K % 8 == 0. e8 has one byte per row, or, with flat_to_sorted
 // (a [rows * k] map), one per sorted row: the scale of row r lands at
 // flat_to_sorted[r k + j] for every j < k.
+// Rows [rows][K] of bf16 (K % 32 == 0) -> MXFP4: codes q [rows][K/2] (two
+// per byte, the even element in the low nibble) and one E8M0 scale per 32
+// elements, e8 [rows][K/32] (mxfp4.hip).
+hipError_t launch_quantize_mxfp4_rows(int rows, int K, const void* in, uint8_t* q, uint8_t* e8, hipStream_t st);
 hipError_t launch_quantize_fp8_rows(int rows, int K, const void* in, uint8_t* q, uint8_t* e8,
                                     const int32_t* flat_to_sorted, int k, hipStream_t st);
 
@@ -211,6 +215,10 @@ hipError_t launch_lora_merge(int E, int N, int K, int r, float s, const void* w,
 // w8 [E][N]: W' = bf16(deq(wq) + s B A).
 hipError_t launch_lora_merge_fp8(int E, int N, int K, int r, float s, const uint8_t* wq, const uint8_t* w8,
                                  const void* a, const void* b, void* w_out, hipStream_t st);
+// The same over MXFP4 codes wq [E][N][K/2] with E8M0 scales w8 [E][N][K/32]:
+// W' = bf16(deq(wq) + s B A).
+hipError_t launch_lora_merge_mxfp4(int E, int N, int K, int r, float s, const uint8_t* wq, const uint8_t* w8,
+                                   const void* a, const void* b, void* w_out, hipStream_t st);
 hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraArgs& g, void* ws, hipStream_t st);
 
 }  // namespace moe

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(B):
     names = declared_functions()
-    assert len(names) == 37, names
+    assert len(names) == 39, names
     for n in names:
         assert hasattr(B.lib, n), n
 
@@ -169,6 +169,13 @@ def test_lora_validation(B):
     assert GG(s, 16, 1.0, *Q[:1], None, *Q[2:], need, None) == 1   # row_token
     assert GG(s, 16, 1.0, *Q[:2], None, *Q[3:], need, None) == 1   # row_weight
     assert GG(big, 16, 1.0, *Q, 1 << 40, None) == 2
+    QM = B.lib.moe_quantize_mxfp4_rows
+    assert QM(4, 48, F, F, F, None) == 1            # K % 32
+    assert QM(4, 64, F, None, F, None) == 1
+    MM = B.lib.moe_lora_merge_mxfp4
+    assert MM(8, 64, 48, 16, 1.0, F, F, F, F, F, None) == 2   # K % 32
+    assert MM(8, 64, 128, 12, 1.0, F, F, F, F, F, None) == 2  # r % 8
+    assert MM(8, 64, 128, 16, 1.0, F, None, F, F, F, None) == 1
     DD = B.lib.moe_gemm_down_dgrad_dy
     assert DD(B.shape(64, 128, 8, 2, 64, "f32"), *([F] * 8), None) == 2
     assert DD(s, F, None, *([F] * 6), None) == 1

@@ -248,13 +248,24 @@ def test_merge_fp8(E, N, K, r):
     assert frac >= 0.999
 
 
-def fp8_lora_check(cfg, r, s, seed, full=False):
+def oracle_mxfp4_weights(w: np.ndarray):
+    """[E,N,K] float64 -> the oracle's MXFP4 (codes [E,N,K/2], scales [E,N,K/32])."""
+    from oracle import mxfp4 as MX
+    E, N, K = w.shape
+    q, e8 = MX.quantize_blocks(w.reshape(E * N, K))
+    return q.reshape(E, N, K // 2), e8.reshape(E, N, K // 32)
+
+
+def fp8_lora_check(cfg, r, s, seed, full=False, fmt="fp8"):
     from mixture_experts_expert_amd import binding as B
     from oracle import fp8 as F8
     inp = synth.make_inputs(cfg, seed=seed, with_dy=True)
     adapters = synth.make_adapters(cfg, r, seed=seed)
     d = U.DevInputs(inp)
-    w8 = B.FP8Weights(d.t["w_gate"], d.t["w_up"], d.t["w_down"])
+    if fmt == "fp8":
+        w8 = B.FP8Weights(d.t["w_gate"], d.t["w_up"], d.t["w_down"])
+    else:
+        w8 = B.MXFP4Weights(d.t["w_gate"], d.t["w_up"], d.t["w_down"])
     ad = {n: U.to_dev(adapters[n]) for n in NAMES}
     T = d.t["x"].shape[0]
     st = B.LoRAStage(T, cfg.H, cfg.E, cfg.k, cfg.I, r, s)
@@ -263,8 +274,16 @@ def fp8_lora_check(cfg, r, s, seed, full=False):
     torch.cuda.synchronize()
     ref_r = U.oracle_route(inp)
     U.check_routing(st, ref_r)
-    wdeq = [LO.dequantize_weights(*F8.quantize_weights(inp.f32(n).astype(np.float64)))
-            for n in ["w_gate", "w_up", "w_down"]]
+    if fmt == "fp8":
+        wdeq = [LO.dequantize_weights(*F8.quantize_weights(inp.f32(n).astype(np.float64)))
+                for n in ["w_gate", "w_up", "w_down"]]
+    else:
+        wdeq = []
+        for n, mine in zip(["w_gate", "w_up", "w_down"], [w8.gate, w8.up, w8.down]):
+            rq, re8 = oracle_mxfp4_weights(inp.f32(n).astype(np.float64))
+            # the GPU quantiser's codes and scales are the oracle's, bit for bit
+            assert np.array_equal(mine[0].cpu().numpy(), rq) and np.array_equal(mine[1].cpu().numpy(), re8), n
+            wdeq.append(LO.dequantize_weights_mxfp4(rq, re8))
     x, dy = inp.f32("x").astype(np.float64), inp.f32("dy").astype(np.float64)
     if full:
         U.say("  adapter oracle on all tokens")
@@ -297,3 +316,111 @@ def test_lora_fp8_base_qwen3_30b_a3b_full():
     U.say(f"[lora fp8 base] {cfg} r=64")
     U.begin("lora_fp8_r64." + cfg.name, f"{cfg} seed 0, adapters rank 64, scale 2, over E4M3 frozen weights")
     fp8_lora_check(cfg, 64, 2.0, 0, full=True)
+
+
+def test_quantize_mxfp4_bit_exact():
+    """moe_quantize_mxfp4_rows against the oracle, codes and scales bit for
+    bit: normal weights, and hand-made blocks (all zeros, a lone element,
+    negative zeros, magnitudes from 2^-120 to 2^100, values on the E2M1 grid
+    and on every rounding midpoint at several scales)."""
+    from mixture_experts_expert_amd import binding as B
+    from oracle import mxfp4 as MX
+    U.say("[mxfp4] quantiser")
+    rng = np.random.default_rng(11)
+    rows, K = 64, 256
+    w = np.float32(0.02) * rng.standard_normal((rows, K), dtype=np.float32)
+    w[0] = 0.0
+    w[1] = 0.0
+    w[1, 37] = -3.0
+    w[2] = -0.0
+    w[3] = w[3] * np.float32(2.0 ** -120)
+    w[4] = w[4] * np.float32(2.0 ** 100)
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float32)
+    mids = (mags[:-1] + mags[1:]) / 2
+    for i, X in enumerate([-10, 0, 7]):
+        pattern = np.r_[mags, -mags, mids, -mids, 6.0, -6.0]  # 32 values: each block's largest is 6 2^X
+        grid = np.ldexp(np.tile(pattern, K // 32), X).astype(np.float32)
+        w[5 + i] = grid
+    bits = synth.bf16_round(w)
+    q = torch.empty(rows, K // 2, dtype=torch.uint8, device="cuda")
+    e8 = torch.empty(rows, K // 32, dtype=torch.uint8, device="cuda")
+    B.moe_quantize_mxfp4_rows(rows, K, U.to_dev(bits), q, e8)
+    torch.cuda.synchronize()
+    rq, re8 = MX.quantize_blocks(widen(bits))
+    gq, ge8 = q.cpu().numpy(), e8.cpu().numpy()
+    assert np.array_equal(ge8, re8), np.argwhere(ge8 != re8)[:5]
+    assert np.array_equal(gq, rq), np.argwhere(gq != rq)[:5]
+
+
+def test_merge_mxfp4_decodes_every_code():
+    """B = 0: W' = bf16(deq(wq)) must be the decoded E2M1 value times its
+    block's power of two, exactly (all 16 codes, scales from 2^-20 to 2^10)."""
+    from mixture_experts_expert_amd import binding as B
+    from oracle import mxfp4 as MX
+    U.say("[lora merge mxfp4] every code")
+    E, N, K, r = 2, 16, 256, 8
+    rng = np.random.default_rng(4)
+    codes = np.stack([np.stack([np.roll(np.tile(np.arange(16), K // 16), 3 * n + 7 * e) for n in range(N)])
+                      for e in range(E)]).astype(np.uint8)
+    wq = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    e8 = (127 + rng.integers(-20, 11, size=(E, N, K // 32))).astype(np.uint8)
+    a = np.zeros((E, r, K), np.uint16)
+    b = np.zeros((E, N, r), np.uint16)
+    out = torch.empty(E, N, K, dtype=torch.bfloat16, device="cuda")
+    B.moe_lora_merge_mxfp4(E, N, K, r, 1.0, torch.from_numpy(wq).cuda(), torch.from_numpy(e8).cuda(), U.to_dev(a),
+                           U.to_dev(b), out)
+    torch.cuda.synchronize()
+    want = MX.dequantize_blocks(wq.reshape(E * N, K // 2), e8.reshape(E * N, K // 32)).reshape(E, N, K)
+    got = U.to_np(out).astype(np.float64)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("E,N,K,r", [(3, 200, 256, 8), (2, 129, 160, 72), (4, 257, 544, 40), (2, 70, 2048, 128)])
+def test_merge_mxfp4(E, N, K, r):
+    """W' = bf16(deq(wq) + s B A) against the float64 oracle on its own
+    quantisation of the same weights (the GPU quantiser's codes equal it)."""
+    from mixture_experts_expert_amd import binding as B
+    U.say(f"[lora merge mxfp4] E={E} N={N} K={K} r={r}")
+    rng = np.random.default_rng(E * 137 + N + K + r)
+    w = synth.bf16_round(np.float32(0.02) * rng.standard_normal((E, N, K), dtype=np.float32))
+    a = synth.bf16_round(np.float32(0.02) * rng.standard_normal((E, r, K), dtype=np.float32))
+    b = synth.bf16_round(np.float32(0.02) * rng.standard_normal((E, N, r), dtype=np.float32))
+    s = 1.25
+    wq = torch.empty(E, N, K // 2, dtype=torch.uint8, device="cuda")
+    e8 = torch.empty(E, N, K // 32, dtype=torch.uint8, device="cuda")
+    B.moe_quantize_mxfp4_rows(E * N, K, U.to_dev(w), wq, e8)
+    out = torch.full((E, N, K), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.moe_lora_merge_mxfp4(E, N, K, r, s, wq, e8, U.to_dev(a), U.to_dev(b), out)
+    torch.cuda.synchronize()
+    rq, re8 = oracle_mxfp4_weights(widen(w))
+    assert np.array_equal(wq.cpu().numpy(), rq) and np.array_equal(e8.cpu().numpy(), re8)
+    got = U.to_np(out).astype(np.float64)
+    deq = LO.dequantize_weights_mxfp4(rq, re8)
+    ref = LO.merge_mxfp4(rq, re8, widen(a), widen(b), s)
+    lowrank = np.abs(ref - deq)
+    bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -22 * (np.abs(deq) + lowrank)
+    assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) - bound))
+    frac = float(np.mean(got == widen(synth.bf16_round(ref.astype(np.float32)))))
+    U.say(f"  equal to the nearest bf16: {frac:.5f}")
+    assert frac >= 0.999
+
+
+@pytest.mark.parametrize("cfg,r", [SMALL_LORA[1], SMALL_LORA[2], SMALL_LORA[4]],
+                         ids=[f"{c.name}-r{r}" for c, r in [SMALL_LORA[1], SMALL_LORA[2], SMALL_LORA[4]]])
+def test_lora_mxfp4_base_small(cfg, r):
+    """The adapter step over MXFP4 frozen experts against the float64 oracle
+    on the dequantised weights: routing bit-exact, y, dx, d_topk_w, d_logits
+    and the six adapter gradients within 2e-2."""
+    U.say(f"[lora mxfp4 base] {cfg} r={r}")
+    U.begin(f"lora_mxfp4_r{r}.{cfg.name}", f"{cfg} seed 8, adapters rank {r} over MXFP4 frozen weights")
+    fp8_lora_check(cfg, r, 2.0 if r == 64 else 0.75, 8, fmt="mxfp4")
+
+
+@pytest.mark.timeout(900)
+def test_lora_mxfp4_base_qwen3_30b_a3b_full():
+    """T=8192, H=2048, E=128, k=8, I=768, r=64, s=2 over MXFP4 frozen experts:
+    every element."""
+    cfg = synth.CONFIGS["qwen3_30b_a3b_train"]
+    U.say(f"[lora mxfp4 base] {cfg} r=64")
+    U.begin("lora_mxfp4_r64." + cfg.name, f"{cfg} seed 0, adapters rank 64, scale 2, over MXFP4 frozen weights")
+    fp8_lora_check(cfg, 64, 2.0, 0, full=True, fmt="mxfp4")
