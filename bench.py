@@ -652,6 +652,24 @@ def main() -> int:
                                             fb["row_weight"], b["o_perm"])
         infer["fp8_gate_up"] = round(time_fn(gate_up8, reps=5), 4)
         infer["fp8_down"] = round(time_fn(down8, reps=5), 4)
+        # MXFP4 weights (E2M1, one scale per 32 along K) against the same
+        # fp8 activations.
+        w4 = B.MXFP4GemmWeights(wg, wu, wd)
+
+        def infer_mxfp4():
+            B.moe_forward_fused_mxfp4(s, x, wr, bias, w4.gate[0], w4.gate[1], w4.up[0], w4.up[1], w4.down[0],
+                                      w4.down[1], b["logits"], b["topk_idx"], b["topk_w"], b["counts"], b["offsets"],
+                                      b["sorted_to_flat"], b["flat_to_sorted"], fb["row_token"], fb["row_weight"],
+                                      f8["xq"], f8["x_e8"], b["a"], f8["aq"], f8["a_e8"], b["o_perm"], b["y"], st.ws)
+
+        infer["mxfp4"] = round(time_fn(infer_mxfp4), 4)
+        gate_up4 = lambda: B.moe_gemm_gate_up_mxfp4(s, f8["xq"], f8["x_e8"], fb["row_token"], b["offsets"],  # noqa: E731
+                                                    w4.gate[0], w4.gate[1], w4.up[0], w4.up[1], b["a"])
+        down4 = lambda: B.moe_gemm_down_mxfp4(s, f8["aq"], f8["a_e8"], b["offsets"], w4.down[0], w4.down[1],  # noqa: E731
+                                              fb["row_weight"], b["o_perm"])
+        infer["mxfp4_gate_up"] = round(time_fn(gate_up4, reps=5), 4)
+        infer["mxfp4_down"] = round(time_fn(down4, reps=5), 4)
+        del w4
         log(f"inference forward: {infer}")
 
     lora = None if args.timed_only else lora_timing(cfg, seeds[0], (x, wr, wg, wu, wd, dy), bias, stream)

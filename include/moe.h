@@ -11,6 +11,7 @@
  *   fp8 inference: moe_forward_fused_fp8 = moe_route -> moe_permute_fused ->
  *             moe_quantize_fp8_rows (x) -> moe_gemm_gate_up_fp8 ->
  *             moe_quantize_fp8_rows (a) -> moe_gemm_down_fp8 -> moe_unpermute_sum
+ *             (moe_forward_fused_mxfp4: the same with MXFP4 weights)
  *   training without do_perm: moe_route -> moe_permute_rows ->
  *             moe_gemm_gate_up_aw -> moe_gemm_down -> moe_combine;
  *             moe_combine_bwd (do_perm NULL) -> moe_gemm_down_bwd_dy ->
@@ -473,6 +474,49 @@ moe_status moe_quantize_mxfp4_rows(int32_t rows, int32_t K, const void* in, uint
  * (MOE_EUNSUPPORTED otherwise). */
 moe_status moe_lora_merge_mxfp4(int32_t E, int32_t N, int32_t K, int32_t r, float scale, const uint8_t* wq,
                                 const uint8_t* w_e8, const void* a, const void* b, void* w_out, hipStream_t stream);
+
+/* fp8 activations x MXFP4 weights for the inference forward: the 4-bit
+ * expert weights of the sourcepulse summary ("Quick Start & Requirements":
+ * bitsandbytes 4-bit; "Limitations & Caveats": the fused 4-bit
+ * dequantisation), in the microscaling FP4 format gfx950's matrix cores
+ * multiply natively against E4M3 operands. Weight elements as in
+ * moe_quantize_mxfp4_rows (E2M1, one E8M0 scale per 32 along K); the
+ * activations stay E4M3 with one scale per row (moe_quantize_fp8_rows). The
+ * matrix core applies both scales, so each product is exactly
+ * dequant(a) * dequant(w), summed in fp32.
+ *
+ * moe_quantize_mxfp4_weights: a stacked weight w [E,N,K] bf16 (w_gate,
+ * w_up [E,I,H]; w_down [E,H,I]) -> codes q [E,N,K/2] and scales e8
+ * stored block-major per expert, [E,K/32,N] (the byte for expert e, block b
+ * of row n at (e * K/32 + b) * N + n), the layout the GEMMs below read.
+ * Codes and scales equal those of moe_quantize_mxfp4_rows on the E*N rows.
+ * K % 32 == 0 (MOE_EINVAL otherwise); E*N < 2^31 (MOE_EUNSUPPORTED). */
+moe_status moe_quantize_mxfp4_weights(int32_t E, int32_t N, int32_t K, const void* w, uint8_t* q, uint8_t* e8,
+                                      hipStream_t stream);
+
+/* moe_gemm_gate_up_fp8 with MXFP4 weights: wq_gate, wq_up [E,I,H/2] codes,
+ * w_gate_e8, w_up_e8 [E,H/32,I] scales (moe_quantize_mxfp4_weights); the
+ * rest (xq, x_e8, a, the SwiGLU epilogue) and the shape limits as there. */
+moe_status moe_gemm_gate_up_mxfp4(moe_shape s, const uint8_t* xq, const uint8_t* x_e8, const int32_t* row_token,
+                                  const int32_t* offsets, const uint8_t* wq_gate, const uint8_t* w_gate_e8,
+                                  const uint8_t* wq_up, const uint8_t* w_up_e8, void* a, hipStream_t stream);
+
+/* moe_gemm_down_fp8 with MXFP4 weights: wq_down [E,H,I/2] codes, w_down_e8
+ * [E,I/32,H] scales; the rest as there. */
+moe_status moe_gemm_down_mxfp4(moe_shape s, const uint8_t* aq, const uint8_t* a_e8, const int32_t* offsets,
+                               const uint8_t* wq_down, const uint8_t* w_down_e8, const float* row_weight,
+                               void* o_perm, hipStream_t stream);
+
+/* moe_forward_fused_fp8 with the two MXFP4 GEMMs above in place of the fp8
+ * ones: the same arguments, buffers, workspace and errors, the weights as
+ * moe_quantize_mxfp4_weights writes them. */
+moe_status moe_forward_fused_mxfp4(moe_shape s, const void* x, const void* w_router, const float* logit_bias,
+                                   const uint8_t* wq_gate, const uint8_t* w_gate_e8, const uint8_t* wq_up,
+                                   const uint8_t* w_up_e8, const uint8_t* wq_down, const uint8_t* w_down_e8,
+                                   float* logits, int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                                   int32_t* sorted_to_flat, int32_t* flat_to_sorted, int32_t* row_token,
+                                   float* row_weight, uint8_t* xq, uint8_t* x_e8, void* a, uint8_t* aq, uint8_t* a_e8,
+                                   void* o_perm, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Bytes of device workspace for moe_lora_grads at this shape and rank (0 if
  * either is rejected): the scaled adapters and the rank-wide row

@@ -67,6 +67,10 @@ _SIGS = {
     "moe_gemm_gate_up_fp8": ([moe_shape] + [_P] * 9 + [_P], ctypes.c_int),
     "moe_gemm_down_fp8": ([moe_shape] + [_P] * 7 + [_P], ctypes.c_int),
     "moe_forward_fused_fp8": ([moe_shape] + [_P] * 26 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_gemm_gate_up_mxfp4": ([moe_shape] + [_P] * 9 + [_P], ctypes.c_int),
+    "moe_gemm_down_mxfp4": ([moe_shape] + [_P] * 7 + [_P], ctypes.c_int),
+    "moe_forward_fused_mxfp4": ([moe_shape] + [_P] * 26 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_quantize_mxfp4_weights": ([ctypes.c_int32] * 3 + [_P] * 4, ctypes.c_int),
     "moe_gemm_down_bwd": ([moe_shape] + [_P] * 8 + [ctypes.c_int, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "moe_gemm_gate_up_bwd": ([moe_shape] + [_P] * 9 + [ctypes.c_int, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "moe_gemm_gate_up_wgrad_gathered": ([moe_shape, _P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_size_t, _P],
@@ -248,6 +252,52 @@ def moe_forward_fused_fp8(s, x, w_router, logit_bias, wq_gate, w_gate_e8, wq_up,
             topk_w, counts, offsets, sorted_to_flat, flat_to_sorted, row_token, row_weight, xq, x_e8, a, aq, a_e8,
             o_perm, y, ws]
     _check("moe_forward_fused_fp8", lib.moe_forward_fused_fp8(s, *[_ptr(t) for t in args], nb, _stream(stream)))
+
+
+def moe_gemm_gate_up_mxfp4(s, xq, x_e8, row_token, offsets, wq_gate, w_gate_e8, wq_up, w_up_e8, a, stream=None):
+    _check("moe_gemm_gate_up_mxfp4", lib.moe_gemm_gate_up_mxfp4(
+        s, _ptr(xq), _ptr(x_e8), _ptr(row_token), _ptr(offsets), _ptr(wq_gate), _ptr(w_gate_e8), _ptr(wq_up),
+        _ptr(w_up_e8), _ptr(a), _stream(stream)))
+
+
+def moe_gemm_down_mxfp4(s, aq, a_e8, offsets, wq_down, w_down_e8, row_weight, o_perm, stream=None):
+    _check("moe_gemm_down_mxfp4", lib.moe_gemm_down_mxfp4(s, _ptr(aq), _ptr(a_e8), _ptr(offsets), _ptr(wq_down),
+                                                          _ptr(w_down_e8), _ptr(row_weight), _ptr(o_perm),
+                                                          _stream(stream)))
+
+
+def moe_forward_fused_mxfp4(s, x, w_router, logit_bias, wq_gate, w_gate_e8, wq_up, w_up_e8, wq_down, w_down_e8,
+                            logits, topk_idx, topk_w, counts, offsets, sorted_to_flat, flat_to_sorted, row_token,
+                            row_weight, xq, x_e8, a, aq, a_e8, o_perm, y, ws, ws_bytes=None, stream=None):
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    args = [x, w_router, logit_bias, wq_gate, w_gate_e8, wq_up, w_up_e8, wq_down, w_down_e8, logits, topk_idx,
+            topk_w, counts, offsets, sorted_to_flat, flat_to_sorted, row_token, row_weight, xq, x_e8, a, aq, a_e8,
+            o_perm, y, ws]
+    _check("moe_forward_fused_mxfp4", lib.moe_forward_fused_mxfp4(s, *[_ptr(t) for t in args], nb, _stream(stream)))
+
+
+def moe_quantize_mxfp4_weights(E, N, K, w, q, e8, stream=None):
+    _check("moe_quantize_mxfp4_weights", lib.moe_quantize_mxfp4_weights(int(E), int(N), int(K), _ptr(w), _ptr(q),
+                                                                        _ptr(e8), _stream(stream)))
+
+
+class MXFP4GemmWeights:
+    """Expert weights quantised once to MXFP4 for the fp8 x MXFP4 GEMMs of
+    the inference forward (moe_quantize_mxfp4_weights): codes gate/up
+    [E,I,H/2], down [E,H,I/2] (two E2M1 per byte) and their E8M0 block
+    scales stored block-major, [E,H/32,I] and [E,I/32,H]."""
+
+    def __init__(self, w_gate, w_up, w_down, stream=None):
+        E, I, H = w_gate.shape
+        dev = w_gate.device
+        u8 = torch.uint8
+
+        def quant(w, N, K):
+            q, e8 = torch.empty(E, N, K // 2, dtype=u8, device=dev), torch.empty(E, K // 32, N, dtype=u8, device=dev)
+            moe_quantize_mxfp4_weights(E, N, K, w, q, e8, stream=stream)
+            return q, e8
+
+        self.gate, self.up, self.down = quant(w_gate, I, H), quant(w_up, I, H), quant(w_down, H, I)
 
 
 class FP8Weights:

@@ -387,6 +387,72 @@ moe_status moe_forward_fused_fp8(moe_shape s, const void* x, const void* w_route
   return moe_unpermute_sum(s, o_perm, flat_to_sorted, y, stream);
 }
 
+moe_status moe_gemm_gate_up_mxfp4(moe_shape s, const uint8_t* xq, const uint8_t* x_e8, const int32_t* row_token,
+                                  const int32_t* offsets, const uint8_t* wq_gate, const uint8_t* w_gate_e8,
+                                  const uint8_t* wq_up, const uint8_t* w_up_e8, void* a, hipStream_t stream) {
+  moe_status st = check_fp8_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(xq, x_e8, row_token, offsets, wq_gate, w_gate_e8, wq_up, w_up_e8, a)) return MOE_EINVAL;
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = xq;
+  ga.a_scale = x_e8;
+  ga.row_token = row_token;
+  ga.b0 = wq_gate;
+  ga.b0_scale = w_gate_e8;
+  ga.b1 = wq_up;
+  ga.b1_scale = w_up_e8;
+  ga.b_fp4 = 1;
+  ga.out2 = a;
+  return from_hip(moe::launch_gemm(moe::GEMM_GATEUP, s, ga, stream));
+}
+
+moe_status moe_gemm_down_mxfp4(moe_shape s, const uint8_t* aq, const uint8_t* a_e8, const int32_t* offsets,
+                               const uint8_t* wq_down, const uint8_t* w_down_e8, const float* row_weight,
+                               void* o_perm, hipStream_t stream) {
+  moe_status st = check_fp8_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(aq, a_e8, offsets, wq_down, w_down_e8, row_weight, o_perm)) return MOE_EINVAL;
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = aq;
+  ga.a_scale = a_e8;
+  ga.b0 = wq_down;
+  ga.b0_scale = w_down_e8;
+  ga.b_fp4 = 1;
+  ga.row_weight = row_weight;
+  ga.out0 = o_perm;
+  return from_hip(moe::launch_gemm(moe::GEMM_DOWN, s, ga, stream));
+}
+
+moe_status moe_forward_fused_mxfp4(moe_shape s, const void* x, const void* w_router, const float* logit_bias,
+                                   const uint8_t* wq_gate, const uint8_t* w_gate_e8, const uint8_t* wq_up,
+                                   const uint8_t* w_up_e8, const uint8_t* wq_down, const uint8_t* w_down_e8,
+                                   float* logits, int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                                   int32_t* sorted_to_flat, int32_t* flat_to_sorted, int32_t* row_token,
+                                   float* row_weight, uint8_t* xq, uint8_t* x_e8, void* a, uint8_t* aq, uint8_t* a_e8,
+                                   void* o_perm, void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_fp8_shape(s);
+  if (st != MOE_OK) return st;
+  if (any_null(x, w_router, wq_gate, w_gate_e8, wq_up, w_up_e8, wq_down, w_down_e8, logits, topk_idx, topk_w, counts,
+               offsets, sorted_to_flat, flat_to_sorted, row_token, row_weight, xq, x_e8, a, aq, a_e8, o_perm, y, ws))
+    return MOE_EINVAL;
+  if (ws_bytes < moe::ws_layout(s).total) return MOE_EWORKSPACE;
+  const int32_t M = s.T * s.k;
+  if ((st = moe_route(s, x, w_router, logit_bias, logits, topk_idx, topk_w, stream)) != MOE_OK) return st;
+  if ((st = moe_permute_fused(s, topk_idx, topk_w, counts, offsets, sorted_to_flat, flat_to_sorted, row_token,
+                              row_weight, ws, ws_bytes, stream)) != MOE_OK)
+    return st;
+  if ((st = moe_quantize_fp8_rows(s.T, s.H, x, xq, x_e8, flat_to_sorted, s.k, stream)) != MOE_OK) return st;
+  if ((st = moe_gemm_gate_up_mxfp4(s, xq, x_e8, row_token, offsets, wq_gate, w_gate_e8, wq_up, w_up_e8, a,
+                                   stream)) != MOE_OK)
+    return st;
+  if ((st = moe_quantize_fp8_rows(M, s.I, a, aq, a_e8, nullptr, 0, stream)) != MOE_OK) return st;
+  if ((st = moe_gemm_down_mxfp4(s, aq, a_e8, offsets, wq_down, w_down_e8, row_weight, o_perm, stream)) != MOE_OK)
+    return st;
+  return moe_unpermute_sum(s, o_perm, flat_to_sorted, y, stream);
+}
+
 moe_status moe_combine(moe_shape s, const void* o_perm, const float* topk_w, const int32_t* flat_to_sorted,
                        void* y, hipStream_t stream) {
   moe_status st = check_shape(s);
@@ -613,7 +679,15 @@ moe_status moe_quantize_mxfp4_rows(int32_t rows, int32_t K, const void* in, uint
                                    hipStream_t stream) {
   if (rows < 0 || K <= 0 || K % 32 != 0) return MOE_EINVAL;
   if (any_null(in, q, e8)) return MOE_EINVAL;
-  return from_hip(moe::launch_quantize_mxfp4_rows(rows, K, in, q, e8, stream));
+  return from_hip(moe::launch_quantize_mxfp4_rows(rows, K, in, q, e8, 0, stream));
+}
+
+moe_status moe_quantize_mxfp4_weights(int32_t E, int32_t N, int32_t K, const void* w, uint8_t* q, uint8_t* e8,
+                                      hipStream_t stream) {
+  if (E <= 0 || N <= 0 || K <= 0 || K % 32 != 0) return MOE_EINVAL;
+  if (any_null(w, q, e8)) return MOE_EINVAL;
+  if (static_cast<int64_t>(E) * N >= (static_cast<int64_t>(1) << 31)) return MOE_EUNSUPPORTED;
+  return from_hip(moe::launch_quantize_mxfp4_rows(E * N, K, w, q, e8, N, stream));
 }
 
 moe_status moe_lora_merge_mxfp4(int32_t E, int32_t N, int32_t K, int32_t r, float scale, const uint8_t* wq,

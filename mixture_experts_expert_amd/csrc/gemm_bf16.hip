@@ -371,9 +371,10 @@ struct Smem {
 // Every tile of one GEMM that workgroup `bid` of `nblk` (a multiple of 8)
 // owns, start to finish: on return every load and store this workgroup
 // issued has completed and its waves are past a barrier.
-template <int MODE, bool FUSED, bool F8 = false, bool AW = false>
+template <int MODE, bool FUSED, bool F8 = false, bool AW = false, bool F4 = false>
 __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const int nblk, const Smem& sm) {
   static_assert(!F8 || (FUSED && (MODE == GATEUP || MODE == DOWN)), "fp8: the inference forward's two GEMMs");
+  static_assert(!F4 || F8, "MXFP4 weights: with fp8 activations");
   static_assert(!AW || (MODE == GATEUP && !F8), "a_w: the gate/up GEMM of the training step");
   // Element size in bytes, elements per k-step (64 bytes of a k-major row
   // either way) and per 16-byte chunk.
@@ -622,7 +623,32 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
         if constexpr (GATHER_A) gcol[t] = 2u * min(m0 + c * 8, mrows - 8);  // row part: gather_off
         else aoff[t] = 2u * (k * lda + min(m0 + c * 8, mrows - 8));
       }
-      if constexpr (MODE == GATEUP) {
+      if constexpr (F4) {
+        // MXFP4 B: a k-step is 32 bytes of a weight row. Block slots 0-7 hold
+        // the data (32 rows each: lane l, row 32 blk + l/2, chunk l%2);
+        // slot 8 (and 9 for gate/up) the step's two block scales of the 256
+        // rows (see rsrc_b4); the other slots load nothing.
+        const int K2 = MODE == GATEUP ? H / 2 : I / 2;  // bytes per weight row
+        if (blk < 8) {
+          const int r = blk * 32 + (lane >> 1);
+          int idx;
+          if constexpr (MODE == GATEUP) {
+            const int q = r & 127;
+            idx = min(n0 + (r >> 7) * 64 + (q & 63), I - 1);
+          } else {
+            idx = min(n0 + r, H - 1);
+          }
+          boff[t] = static_cast<uint32_t>(idx * K2 + (lane & 1) * 16);
+        } else if (MODE == GATEUP ? blk < 10 : blk == 8) {
+          if constexpr (MODE == GATEUP)  // lanes 0-15: block lane/8, half (lane/4)%2, 16 rows 16 (lane%4) ..
+            boff[t] = lane < 16 ? static_cast<uint32_t>((lane >> 3) * I + n0 + ((lane >> 2) & 1) * 64 + 16 * (lane & 3))
+                                : kNoWrite;
+          else  // lanes 0-31: block lane/16, 16 rows 16 (lane%16) ..
+            boff[t] = lane < 32 ? static_cast<uint32_t>((lane >> 4) * H + n0 + 16 * (lane & 15)) : kNoWrite;
+        } else {
+          boff[t] = kNoWrite;
+        }
+      } else if constexpr (MODE == GATEUP) {
         // LDS row r: wavefront column half r / 128 and 32-column block
         // j = (r % 128) / 32 of it (j < 2: gate, j >= 2: up, same indices).
         // A wavefront's 64 rows are all gate (even waves) or all up (odd).
@@ -737,12 +763,48 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
     if ((v & 1) == 0) buf_to_lds16(ra, aoff[t], L + (wave * (LOADS / 2) + t) * 512);
     else buf_to_lds16(rb, boff[t], L + STAGE_A + (wave * (LOADS / 2) + t) * 512);
   };
+  // MXFP4 B (F4), k-step s: block slot blk < 8 reads the weight rows' 32
+  // bytes of the step (gate rows for slots 0, 1, 4, 5 and up rows for 2, 3,
+  // 6, 7 in gate/up: LDS rows 32 blk ..); slot 8 (gate or down) and 9 (up)
+  // the step's two E8M0 block scales of the rows, from scales stored
+  // [E][K/32][N] (a block's scales of consecutive rows are contiguous).
+  auto rsrc_b4 = [&](int s, int blk) -> rsrc_t {
+    const int k0 = s * KS;
+    const bool live = s < ksteps;
+    if (blk < 8) {
+      if constexpr (MODE == GATEUP) {
+        const char* w = reinterpret_cast<const char*>((blk & 2) ? P.b1 : P.b0) + (static_cast<int64_t>(e) * I * H + k0) / 2;
+        return make_rsrc(w, live ? (I * H - k0) / 2 : 0);
+      } else {
+        return make_rsrc(reinterpret_cast<const char*>(P.b0) + (static_cast<int64_t>(e) * H * I + k0) / 2,
+                         live ? (H * I - k0) / 2 : 0);
+      }
+    }
+    if constexpr (MODE == GATEUP) {
+      const uint8_t* sc = (blk == 9 ? P.sb1 : P.sb0) + (static_cast<int64_t>(e) * (H / 32) + 2 * s) * I;
+      return make_rsrc(sc, live && blk < 10 ? 2 * I : 0);
+    } else {
+      const uint8_t* sc = P.sb0 + (static_cast<int64_t>(e) * (I / 32) + 2 * s) * H;
+      return make_rsrc(sc, live && blk == 8 ? 2 * H : 0);
+    }
+  };
+  auto vmem4 = [&](int v, const rsrc_t& ra, int s, bf16_t* L) __attribute__((always_inline)) {
+    const int t = v >> 1;
+    const int blk = wave * (LOADS / 2) + t;
+    if ((v & 1) == 0) buf_to_lds16(ra, aoff[t], L + blk * 512);
+    else buf_to_lds16(rsrc_b4(s, blk), boff[t], L + STAGE_A + blk * 512);
+  };
   // All 8 at once (the first steps of a workgroup's first tile).
   auto issue = [&](int s, bf16_t* L) __attribute__((always_inline)) {
     const rsrc_t ra = rsrc_a(s);
-    const rsrc_t rb = rsrc_b(s);
+    if constexpr (F4) {
 #pragma unroll
-    for (int v = 0; v < LOADS; ++v) vmem(v, ra, rb, L);
+      for (int v = 0; v < LOADS; ++v) vmem4(v, ra, s, L);
+    } else {
+      const rsrc_t rb = rsrc_b(s);
+#pragma unroll
+      for (int v = 0; v < LOADS; ++v) vmem(v, ra, rb, L);
+    }
   };
 
   // Operand fragments of k-slice kk (16 k; two per step) for 32-row block
@@ -887,22 +949,39 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   // rows' and columns' E8M0 bytes, replicated in every byte and in both
   // halves, so that the instruction applies 2^(Xa + Xb) to every product
   // whichever byte and lane it reads them from.
+  //
+  // With MXFP4 B (F4) the pairing is by k: B lane l holds the 32 E2M1
+  // values (16 bytes, even k in the low nibble) of row l % 32 for k 32 (l /
+  // 32) .. + 31, i.e. one 32-element scale block, scaled by the lane's
+  // scale byte; an fp8 A lane holds k 16 (l / 32) .. + 15 in its first 16
+  // bytes and k 32 + 16 (l / 32) .. + 15 in the other 16 (stage chunks l/32
+  // and l/32 + 2). Both were read off in-bounds probes of the instruction.
   i32x8 fa8[FM], fb8[FN];
   int sca[FM], scb[FN];
-  int aof8[FM], bof8[FN];
+  int aof8[FM], bof8[FN], sof4[FN];
   auto set_frag_offsets8 = [&]() __attribute__((always_inline)) {
     int lane = lane_id;
     asm volatile("" : "+v"(lane));
-    const int h2 = 2 * (lane >> 5);
+    const int h = lane >> 5, h2 = 2 * h;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = wm * WTM + i * 32 + (lane & 31);
-      aof8[i] = r * 64 + ((swk(r) ^ h2) << 4);
+      aof8[i] = r * 64 + ((swk(r) ^ (F4 ? h : h2)) << 4);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int r = wn * WTN + j * 32 + (lane & 31);
-      bof8[j] = r * 64 + ((swk(r) ^ h2) << 4);
+      if constexpr (F4) {
+        bof8[j] = r * 32 + h * 16;
+        if constexpr (MODE == GATEUP) {
+          const int q = r & 127, hf = r >> 7;
+          sof4[j] = (q < 64 ? 8 * 1024 + q : 9 * 1024 + (q - 64)) + h * 128 + hf * 64;
+        } else {
+          sof4[j] = 8 * 1024 + h * 256 + r;
+        }
+      } else {
+        bof8[j] = r * 64 + ((swk(r) ^ h2) << 4);
+      }
     }
   };
   // This tile's scales: rows of A (sorted rows, valid or not: the codes of
@@ -918,6 +997,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
+      if constexpr (F4) continue;  // block scales: from each k-step's stage
       int v;
       if constexpr (MODE == GATEUP) {  // wavefront columns: 64 gate (j < 2), then 64 up, same indices
         const int idx = min(n0 + wn * 64 + (j & 1) * 32 + l32, I - 1);
@@ -932,9 +1012,22 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   auto frag8 = [&](const bf16_t* S, int off) -> i32x8 {
     const char* base = reinterpret_cast<const char*>(S);
     const u32x4 lo = *reinterpret_cast<const u32x4*>(base + off);
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + (off ^ 16));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + (off ^ (F4 ? 32 : 16)));
     return i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
                  static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+  };
+  // B fragment of column block j from stage S (F4: 16 bytes and the block
+  // scale; otherwise as A).
+  auto fragb = [&](const bf16_t* S, int j) __attribute__((always_inline)) {
+    if constexpr (F4) {
+      const char* base = reinterpret_cast<const char*>(S + STAGE_A);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(base + bof8[j]);
+      fb8[j] = i32x8{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w),
+                     0, 0, 0, 0};
+      scb[j] = static_cast<int>(*reinterpret_cast<const uint8_t*>(base + sof4[j]));
+    } else {
+      fb8[j] = frag8(S + STAGE_A, bof8[j]);
+    }
   };
   // A tile's first step: row block 0 and every B fragment (the others are
   // read at the start of each step).
@@ -943,13 +1036,15 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
     if (nbm > 0) fa8[0] = frag8(S, aof8[0]);
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      if (nbm > 0) fb8[j] = frag8(S + STAGE_A, bof8[j]);
+      if (nbm > 0) fragb(S, j);
   };
   auto mfma8 = [&](auto zc, int i, int j) __attribute__((always_inline)) {
     if constexpr (decltype(zc)::value)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa8[i], fb8[j], f32x16{}, 0, 0, 0, sca[i], 0, scb[j]);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa8[i], fb8[j], f32x16{}, 0, F4 ? 4 : 0, 0, sca[i],
+                                                                 0, scb[j]);
     else
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa8[i], fb8[j], acc[i][j], 0, 0, 0, sca[i], 0, scb[j]);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa8[i], fb8[j], acc[i][j], 0, F4 ? 4 : 0, 0, sca[i],
+                                                                 0, scb[j]);
   };
   // One k-step (64 k) on the stage at Ac, loads of step sn into Ln. At entry
   // fa8[0] and fb8[] hold this step's fragments. First the wait for the next
@@ -963,7 +1058,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
                     __attribute__((always_inline)) {
     constexpr int nbm = decltype(nbc)::value;
     const rsrc_t ra = rsrc_a(sn);
-    const rsrc_t rb = rsrc_b(sn);
+    const rsrc_t rb = F4 ? ra : rsrc_b(sn);
     if (!last) {
       __builtin_amdgcn_s_waitcnt(kWaitVm8);
       step_barrier();
@@ -978,15 +1073,20 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           mfma8(first, i, j);
-          if (i == nbm - 1 && !last) fb8[j] = frag8(An + STAGE_A, bof8[j]);
+          if (i == nbm - 1 && !last) fragb(An, j);
         }
       } else if constexpr (decltype(first)::value) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
       }
       __builtin_amdgcn_sched_barrier(0);
-      vmem(2 * i, ra, rb, Ln);
-      vmem(2 * i + 1, ra, rb, Ln);
+      if constexpr (F4) {
+        vmem4(2 * i, ra, sn, Ln);
+        vmem4(2 * i + 1, ra, sn, Ln);
+      } else {
+        vmem(2 * i, ra, rb, Ln);
+        vmem(2 * i + 1, ra, rb, Ln);
+      }
       if (i == 0 && nbm > 0 && !last) fa8[0] = frag8(An, aof8[0]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1359,11 +1459,11 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   }
 }
 
-template <int MODE, bool FUSED, bool F8, bool AW>
+template <int MODE, bool FUSED, bool F8, bool AW, bool F4>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(
     Params P) {
   MOE_GEMM_SMEM
-  gemm_tiles<MODE, FUSED, F8, AW>(P, blockIdx.x, gridDim.x, sm);
+  gemm_tiles<MODE, FUSED, F8, AW, F4>(P, blockIdx.x, gridDim.x, sm);
 }
 
 // Two independent GEMMs of the backward in one persistent launch: a data
@@ -1470,10 +1570,10 @@ int persistent_grid() {
   return cached;
 }
 
-template <int MODE, bool FUSED = false, bool F8 = false, bool AW = false>
+template <int MODE, bool FUSED = false, bool F8 = false, bool AW = false, bool F4 = false>
 hipError_t run(const Params& p, hipStream_t st) {
   const int grid = persistent_grid();
-  grouped_gemm_kernel<MODE, FUSED, F8, AW><<<grid, NT, 0, st>>>(p);
+  grouped_gemm_kernel<MODE, FUSED, F8, AW, F4><<<grid, NT, 0, st>>>(p);
   hipError_t err = hipGetLastError();
   if constexpr (grouped_k(MODE)) {
     if (err != hipSuccess) return err;
@@ -1535,11 +1635,13 @@ hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g
   const Params p = make_params(s, g);
   switch (mode) {
     case GEMM_GATEUP:
+      if (g.a_scale && g.b_fp4) return g.row_token ? run<GATEUP, true, true, false, true>(p, st) : hipErrorInvalidValue;
       if (g.a_scale) return g.row_token ? run<GATEUP, true, true>(p, st) : hipErrorInvalidValue;
       if (g.out3)  // a_w (needs row_weight)
         return g.row_token ? run<GATEUP, true, false, true>(p, st) : run<GATEUP, false, false, true>(p, st);
       return g.row_token ? run<GATEUP, true>(p, st) : run<GATEUP>(p, st);
     case GEMM_DOWN:
+      if (g.a_scale && g.b_fp4) return g.row_weight ? run<DOWN, true, true, false, true>(p, st) : hipErrorInvalidValue;
       if (g.a_scale) return g.row_weight ? run<DOWN, true, true>(p, st) : hipErrorInvalidValue;
       return g.row_weight ? run<DOWN, true>(p, st) : run<DOWN>(p, st);
     case GEMM_DGRAD_DOWN: return g.row_token ? run<DGRAD_DOWN, true>(p, st) : run<DGRAD_DOWN>(p, st);

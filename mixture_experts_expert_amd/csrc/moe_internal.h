@@ -152,6 +152,10 @@ struct GemmArgs {
   const uint8_t* a_scale;
   const uint8_t* b0_scale;
   const uint8_t* b1_scale;
+  // With a_scale: b0/b1 hold MXFP4 weights instead (E2M1 codes [E][N][K/2],
+  // even k in the low nibble) and b*_scale their E8M0 block scales stored
+  // block-major, [E][K/32][N].
+  int b_fp4;
 };
 
 hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& a, hipStream_t st);
@@ -160,14 +164,17 @@ hipError_t launch_gemm_f32(GemmMode mode, const moe_shape& s, const GemmArgs& a,
 inline hipError_t launch_gemm(GemmMode mode, const moe_shape& s, const GemmArgs& a, hipStream_t st) {
   return s.dtype == MOE_BF16 ? launch_gemm_bf16(mode, s, a, st) : launch_gemm_f32(mode, s, a, st);
 }
+// Rows [rows][K] of bf16 (K % 32 == 0) -> MXFP4: codes q [rows][K/2] (two
+// per byte, the even element in the low nibble) and one E8M0 scale per 32
+// elements, e8 [rows][K/32] (mxfp4.hip); with kmajor_rows = R > 0 the rows
+// come in groups of R (one expert's weight) and the scales of a group are
+// stored block-major, [K/32][R].
+hipError_t launch_quantize_mxfp4_rows(int rows, int K, const void* in, uint8_t* q, uint8_t* e8, int kmajor_rows,
+                                      hipStream_t st);
 // Rows [rows, K] of bf16 -> OCP E4M3 codes with a power-of-two scale per row
 // (E8M0 byte). K % 8 == 0. e8 has one byte per row, or, with flat_to_sorted
 // (a [rows * k] map), one per sorted row: the scale of row r lands at
 // flat_to_sorted[r k + j] for every j < k.
-// Rows [rows][K] of bf16 (K % 32 == 0) -> MXFP4: codes q [rows][K/2] (two
-// per byte, the even element in the low nibble) and one E8M0 scale per 32
-// elements, e8 [rows][K/32] (mxfp4.hip).
-hipError_t launch_quantize_mxfp4_rows(int rows, int K, const void* in, uint8_t* q, uint8_t* e8, hipStream_t st);
 hipError_t launch_quantize_fp8_rows(int rows, int K, const void* in, uint8_t* q, uint8_t* e8,
                                     const int32_t* flat_to_sorted, int k, hipStream_t st);
 

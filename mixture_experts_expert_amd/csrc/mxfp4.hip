@@ -14,6 +14,9 @@
 //
 // One thread per block of 32: four 16-byte loads, one 16-byte store of the
 // codes and one byte of scale; neighbouring threads take neighbouring blocks.
+// The scales are stored row-major ([rows][K/32], for the adapter merge) or,
+// for the MXFP4 GEMMs, block-major within each expert's rows ([E][K/32][N]),
+// so that one k-step's scales of consecutive weight rows are contiguous.
 #include "moe_internal.h"
 
 namespace moe {
@@ -30,7 +33,8 @@ __device__ __forceinline__ uint32_t e2m1_code(float a) {
          static_cast<uint32_t>(a > 5.0f);
 }
 
-__global__ __launch_bounds__(kThreads) void quantize_mxfp4_kernel(int64_t blocks, const uint4* __restrict__ in,
+__global__ __launch_bounds__(kThreads) void quantize_mxfp4_kernel(int64_t blocks, int kb, int kmajor_rows,
+                                                                  const uint4* __restrict__ in,
                                                                   uint4* __restrict__ q, uint8_t* __restrict__ e8) {
   const int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (b >= blocks) return;
@@ -68,17 +72,23 @@ __global__ __launch_bounds__(kThreads) void quantize_mxfp4_kernel(int64_t blocks
     packed[i >> 3] |= code << (4 * (i & 7));
   }
   q[b] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-  e8[b] = static_cast<uint8_t>(X + 127);
+  int64_t si = b;  // scale of block j of row `row`: [rows][kb], or [group][kb][R] with R = kmajor_rows
+  if (kmajor_rows > 0) {
+    const int64_t row = b / kb, j = b - row * kb;
+    si = (row / kmajor_rows) * kb * kmajor_rows + j * kmajor_rows + row % kmajor_rows;
+  }
+  e8[si] = static_cast<uint8_t>(X + 127);
 }
 
 }  // namespace
 
-hipError_t launch_quantize_mxfp4_rows(int rows, int K, const void* in, uint8_t* q, uint8_t* e8, hipStream_t st) {
+hipError_t launch_quantize_mxfp4_rows(int rows, int K, const void* in, uint8_t* q, uint8_t* e8, int kmajor_rows,
+                                      hipStream_t st) {
   const int64_t blocks = static_cast<int64_t>(rows) * (K / 32);
   if (blocks == 0) return hipSuccess;
   const unsigned grid = static_cast<unsigned>((blocks + kThreads - 1) / kThreads);
-  quantize_mxfp4_kernel<<<grid, kThreads, 0, st>>>(blocks, static_cast<const uint4*>(in), reinterpret_cast<uint4*>(q),
-                                                   e8);
+  quantize_mxfp4_kernel<<<grid, kThreads, 0, st>>>(blocks, K / 32, kmajor_rows, static_cast<const uint4*>(in),
+                                                   reinterpret_cast<uint4*>(q), e8);
   return hipGetLastError();
 }
 

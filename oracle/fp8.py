@@ -122,14 +122,24 @@ def experts_fp8(x: np.ndarray, row_token: np.ndarray, row_weight: np.ndarray, of
       A = bf16(silu(G) U),  aq = quantize_rows(A),
       O[p] = bf16(row_weight[p] * deq(aq[p]) deq(Wd[e])^T).
     """
+    def deq(w):
+        q, e8 = w
+        E, N, K = q.shape
+        return dequantize_rows(q.reshape(E * N, K), e8.reshape(E * N)).reshape(E, N, K)
+    return experts_quantized(x, row_token, row_weight, offsets, deq(gate), deq(up), deq(down))
+
+
+def experts_quantized(x: np.ndarray, row_token: np.ndarray, row_weight: np.ndarray, offsets: np.ndarray,
+                      wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> Dict[str, np.ndarray]:
+    """experts_fp8 with the expert weights given dequantised (float64 wg, wu
+    [E, I, H], wd [E, H, I]): the activations x and A are quantised to E4M3
+    per row as there, whatever format the weights came in."""
     xq, xe = quantize_rows(x)
     xd = dequantize_rows(xq, xe)
     E = len(offsets) - 1
-    gq, ge = gate
-    uq, ue = up
-    dq, de = down
     M = len(row_token)
-    I, H = gq.shape[1], gq.shape[2]
+    I = wg.shape[1]
+    H = wg.shape[2]
     G = np.zeros((M, I))
     U = np.zeros((M, I))
     for e in range(E):
@@ -137,8 +147,8 @@ def experts_fp8(x: np.ndarray, row_token: np.ndarray, row_weight: np.ndarray, of
         if hi == lo:
             continue
         rows = xd[row_token[lo:hi]]
-        G[lo:hi] = rows @ dequantize_rows(gq[e], ge[e]).T
-        U[lo:hi] = rows @ dequantize_rows(uq[e], ue[e]).T
+        G[lo:hi] = rows @ wg[e].T
+        U[lo:hi] = rows @ wu[e].T
     A = bf16_round(G / (1.0 + np.exp(-G)) * U)
     aq, ae = quantize_rows(A)
     ad = dequantize_rows(aq, ae)
@@ -147,7 +157,7 @@ def experts_fp8(x: np.ndarray, row_token: np.ndarray, row_weight: np.ndarray, of
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
             continue
-        O[lo:hi] = ad[lo:hi] @ dequantize_rows(dq[e], de[e]).T
+        O[lo:hi] = ad[lo:hi] @ wd[e].T
     O = bf16_round(O * np.asarray(row_weight, dtype=np.float64)[:, None])
     return {"xq": xq, "xe": xe, "g": G, "u": U, "a": A, "aq": aq, "ae": ae, "o_perm": O}
 

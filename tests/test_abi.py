@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(B):
     names = declared_functions()
-    assert len(names) == 39, names
+    assert len(names) == 43, names
     for n in names:
         assert hasattr(B.lib, n), n
 
@@ -176,6 +176,19 @@ def test_lora_validation(B):
     assert MM(8, 64, 48, 16, 1.0, F, F, F, F, F, None) == 2   # K % 32
     assert MM(8, 64, 128, 12, 1.0, F, F, F, F, F, None) == 2  # r % 8
     assert MM(8, 64, 128, 16, 1.0, F, None, F, F, F, None) == 1
+    QW = B.lib.moe_quantize_mxfp4_weights
+    assert QW(8, 64, 48, F, F, F, None) == 1          # K % 32
+    assert QW(8, 64, 64, F, None, F, None) == 1
+    assert QW(1 << 16, 1 << 15, 64, F, F, F, None) == 2   # E*N >= 2^31
+    f32 = B.shape(64, 128, 8, 2, 64, "f32")
+    s4 = B.shape(64, 128, 8, 2, 64, "bf16")
+    GU, DN = B.lib.moe_gemm_gate_up_mxfp4, B.lib.moe_gemm_down_mxfp4
+    assert GU(f32, *([F] * 9), None) == 2
+    assert GU(B.shape(64, 96, 8, 2, 64, "bf16"), *([F] * 9), None) == 2   # H % 64
+    assert GU(s4, F, F, F, F, None, *([F] * 4), None) == 1
+    assert DN(s4, *([F] * 6), None, None) == 1
+    FF = B.lib.moe_forward_fused_mxfp4
+    assert FF(s4, *([F] * 26), 0, None) == 3
     DD = B.lib.moe_gemm_down_dgrad_dy
     assert DD(B.shape(64, 128, 8, 2, 64, "f32"), *([F] * 8), None) == 2
     assert DD(s, F, None, *([F] * 6), None) == 1

@@ -84,14 +84,18 @@ def test_quantize_rows_bit_exact():
     assert np.array_equal(e8s.cpu().numpy(), want)
 
 
-def fp8_forward(d: U.DevInputs):
+def fp8_forward(d: U.DevInputs, fmt: str = "fp8"):
+    """fmt "fp8": E4M3 weights; "mxfp4": MXFP4 weights (E2M1, a scale per 32)."""
     from mixture_experts_expert_amd import binding as B
     c = d.cfg
     T, M = d.t["x"].shape[0], c.T * c.k
     s = B.shape(T, c.H, c.E, c.k, c.I, torch.bfloat16)
     dev = "cuda"
     i32, u8 = torch.int32, torch.uint8
-    w = B.FP8Weights(d.t["w_gate"], d.t["w_up"], d.t["w_down"])
+    if fmt == "fp8":
+        w = B.FP8Weights(d.t["w_gate"], d.t["w_up"], d.t["w_down"])
+    else:
+        w = B.MXFP4GemmWeights(d.t["w_gate"], d.t["w_up"], d.t["w_down"])
     out = dict(
         logits=torch.empty(T, c.E, device=dev), topk_idx=torch.empty(T, c.k, dtype=i32, device=dev),
         topk_w=torch.empty(T, c.k, device=dev), counts=torch.empty(c.E, dtype=i32, device=dev),
@@ -104,29 +108,51 @@ def fp8_forward(d: U.DevInputs):
         y=torch.empty(T, c.H, dtype=torch.bfloat16, device=dev))
     ws = torch.empty(B.moe_workspace_bytes(s), dtype=u8, device=dev)
     o = out
-    B.moe_forward_fused_fp8(s, d.t["x"], d.t["w_router"], d.bias, w.gate[0], w.gate[1], w.up[0], w.up[1], w.down[0],
-                            w.down[1], o["logits"], o["topk_idx"], o["topk_w"], o["counts"], o["offsets"],
-                            o["sorted_to_flat"], o["flat_to_sorted"], o["row_token"], o["row_weight"], o["xq"],
-                            o["x_e8"], o["a"], o["aq"], o["a_e8"], o["o_perm"], o["y"], ws)
+    fwd = B.moe_forward_fused_fp8 if fmt == "fp8" else B.moe_forward_fused_mxfp4
+    fwd(s, d.t["x"], d.t["w_router"], d.bias, w.gate[0], w.gate[1], w.up[0], w.up[1], w.down[0],
+        w.down[1], o["logits"], o["topk_idx"], o["topk_w"], o["counts"], o["offsets"],
+        o["sorted_to_flat"], o["flat_to_sorted"], o["row_token"], o["row_weight"], o["xq"],
+        o["x_e8"], o["a"], o["aq"], o["a_e8"], o["o_perm"], o["y"], ws)
     torch.cuda.synchronize()
     return w, out
 
 
-def check_fp8(inp, w, out, check_weights=True):
+def oracle_weights(inp, fmt: str):
+    """The oracle's quantisation of the three expert weights (codes and
+    scales as the GPU stores them) and their dequantised float64 values."""
+    from oracle import mxfp4 as MX
+    out, deq = [], []
+    for n in ["w_gate", "w_up", "w_down"]:
+        w = inp.f32(n).astype(np.float64)
+        E, N, K = w.shape
+        if fmt == "fp8":
+            q, e8 = F8.quantize_weights(w)
+            d = F8.dequantize_rows(q.reshape(E * N, K), e8.reshape(E * N)).reshape(E, N, K)
+            out.append((q, e8))
+        else:
+            q, e8 = MX.quantize_blocks(w.reshape(E * N, K))
+            d = MX.dequantize_blocks(q, e8).reshape(E, N, K)
+            # scales block-major per expert, as the GEMMs read them
+            out.append((q.reshape(E, N, K // 2), e8.reshape(E, N, K // 32).transpose(0, 2, 1)))
+        deq.append(d)
+    return out, deq
+
+
+def check_fp8(inp, w, out, check_weights=True, fmt="fp8"):
     c = inp.cfg
     ref_r = U.oracle_route(inp)
     for n in ["topk_idx", "counts", "offsets", "sorted_to_flat", "flat_to_sorted"]:
         assert np.array_equal(U.to_np(out[n]), ref_r[n]), n
     assert U.same_bits(U.to_np(out["logits"]), ref_r["logits"]), "logits differ"
     x = inp.f32("x").astype(np.float64)
-    wg, wu, wd = (F8.quantize_weights(inp.f32(n).astype(np.float64)) for n in ["w_gate", "w_up", "w_down"])
+    qw, (wg, wu, wd) = oracle_weights(inp, fmt)
     if check_weights:
-        for (q, e8), ref in zip((w.gate, w.up, w.down), (wg, wu, wd)):
+        for (q, e8), ref in zip((w.gate, w.up, w.down), qw):
             assert np.array_equal(q.cpu().numpy(), ref[0]) and np.array_equal(e8.cpu().numpy(), ref[1])
     s2f = ref_r["sorted_to_flat"].astype(np.int64)
     row_token = (s2f // c.k).astype(np.int32)
     row_weight = ref_r["topk_w"].reshape(-1)[s2f].astype(np.float64)
-    ref = F8.experts_fp8(x, row_token, row_weight, ref_r["offsets"], wg, wu, wd)
+    ref = F8.experts_quantized(x, row_token, row_weight, ref_r["offsets"], wg, wu, wd)
     assert np.array_equal(out["xq"].cpu().numpy(), ref["xq"])
     assert np.array_equal(out["x_e8"].cpu().numpy(), ref["xe"][row_token])
     U.check_close("a", U.to_np(out["a"]), ref["a"], U.BF16_TOL)
@@ -179,3 +205,26 @@ def test_fp8_forward_qwen3_30b_a3b_full():
     d = U.DevInputs(inp)
     w, out = fp8_forward(d)
     check_fp8(inp, w, out)
+
+
+# MXFP4 weights (E2M1, one E8M0 scale per 32 along K) with fp8 activations:
+# the same checks, the oracle on the MXFP4-dequantised weights.
+@pytest.mark.parametrize("cfg", FP8_SMALL, ids=lambda c: c.name)
+def test_mxfp4_forward_small(cfg):
+    U.say(f"[mxfp4 forward] {cfg}")
+    U.begin(f"mxfp4.{cfg.name}", f"{cfg} seed 5, fp8 x MXFP4 forward")
+    inp = synth.make_inputs(cfg, seed=5, with_dy=False)
+    d = U.DevInputs(inp)
+    w, out = fp8_forward(d, "mxfp4")
+    check_fp8(inp, w, out, fmt="mxfp4")
+
+
+def test_mxfp4_forward_qwen3_30b_a3b_full():
+    """T=4096, H=2048, E=128, k=8, I=768: every output element of the fp8 x MXFP4 forward."""
+    cfg = synth.CONFIGS["qwen3_30b_a3b_fwd"]
+    U.say(f"[mxfp4 forward] {cfg}")
+    U.begin(f"mxfp4.{cfg.name}", f"{cfg} seed 0, fp8 x MXFP4 forward")
+    inp = synth.make_inputs(cfg, seed=0)
+    d = U.DevInputs(inp)
+    w, out = fp8_forward(d, "mxfp4")
+    check_fp8(inp, w, out, fmt="mxfp4")
