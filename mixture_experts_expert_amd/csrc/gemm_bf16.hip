@@ -520,6 +520,18 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   int pidx = -1;  // grouped-K: partial tile of a later chunk, -1 for chunk 0
   int nkbeg = 0;  // GATHER_K: first k-row of this workgroup's next tile
   uint32_t aoff[LOADS / 2], boff[LOADS / 2];
+  // MXFP4 B stage: LDS block of this wavefront's load t. Data blocks 0-7
+  // (t < 2): gate/up rows 32 b .. are gate for b in {0, 1, 4, 5}, up for
+  // {2, 3, 6, 7}; scales in block 8 (gate or down) and 9 (up); the loads
+  // that fetch nothing get blocks 10-15 of their own.
+  auto f4_slot = [&](int t) -> int {
+    if (t < 2) return (wave & 1) * 4 + (wave >> 1) * 2 + t;
+    if (t == 2) return MODE == GATEUP ? 8 + (wave >> 1) + 2 * (wave & 1) : 8 + wave;
+    return 12 + wave;
+  };
+  // Chunk swizzle of the 32-byte MXFP4 rows: 8 lanes reading one chunk of
+  // 8 consecutive rows hit 32 distinct banks.
+  auto sw4 = [](int r) -> int { return (r >> 2) & 1; };
   uint32_t gcol[LOADS / 2];  // GATHER_K: column byte offsets of the gathered operand's loads
   const char* abase_m = reinterpret_cast<const char*>(P.a);  // grouped-M: the tile's first row of A
 
@@ -624,22 +636,22 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
         else aoff[t] = 2u * (k * lda + min(m0 + c * 8, mrows - 8));
       }
       if constexpr (F4) {
-        // MXFP4 B: a k-step is 32 bytes of a weight row. Block slots 0-7 hold
-        // the data (32 rows each: lane l, row 32 blk + l/2, chunk l%2);
-        // slot 8 (and 9 for gate/up) the step's two block scales of the 256
-        // rows (see rsrc_b4); the other slots load nothing.
+        // MXFP4 B: a k-step is 32 bytes of a weight row, two 16-byte chunks
+        // swapped on rows with bit 2 set (sw4). Instructions 0 and 1 of a
+        // wavefront fill data block f4_slot (32 rows each: lane l, row
+        // 32 slot + l/2); in gate/up, wavefronts 0 and 1 hold the gate rows,
+        // 2 and 3 the up rows, so that each reads one weight. Instruction 2
+        // of wavefront 0 (and 2 for up) loads the step's two block scales of
+        // the 256 rows; the rest load nothing (see rsrc_b4).
         const int K2 = MODE == GATEUP ? H / 2 : I / 2;  // bytes per weight row
-        if (blk < 8) {
-          const int r = blk * 32 + (lane >> 1);
+        if (t < 2) {
+          const int r = f4_slot(t) * 32 + (lane >> 1);
+          const int c = (lane & 1) ^ sw4(r);
           int idx;
-          if constexpr (MODE == GATEUP) {
-            const int q = r & 127;
-            idx = min(n0 + (r >> 7) * 64 + (q & 63), I - 1);
-          } else {
-            idx = min(n0 + r, H - 1);
-          }
-          boff[t] = static_cast<uint32_t>(idx * K2 + (lane & 1) * 16);
-        } else if (MODE == GATEUP ? blk < 10 : blk == 8) {
+          if constexpr (MODE == GATEUP) idx = min(n0 + (r >> 7) * 64 + (r & 63), I - 1);
+          else idx = min(n0 + r, H - 1);
+          boff[t] = static_cast<uint32_t>(idx * K2 + c * 16);
+        } else if (t == 2 && (MODE == GATEUP ? (wave & 1) == 0 : wave == 0)) {
           if constexpr (MODE == GATEUP)  // lanes 0-15: block lane/8, half (lane/4)%2, 16 rows 16 (lane%4) ..
             boff[t] = lane < 16 ? static_cast<uint32_t>((lane >> 3) * I + n0 + ((lane >> 2) & 1) * 64 + 16 * (lane & 3))
                                 : kNoWrite;
@@ -763,43 +775,43 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
     if ((v & 1) == 0) buf_to_lds16(ra, aoff[t], L + (wave * (LOADS / 2) + t) * 512);
     else buf_to_lds16(rb, boff[t], L + STAGE_A + (wave * (LOADS / 2) + t) * 512);
   };
-  // MXFP4 B (F4), k-step s: block slot blk < 8 reads the weight rows' 32
-  // bytes of the step (gate rows for slots 0, 1, 4, 5 and up rows for 2, 3,
-  // 6, 7 in gate/up: LDS rows 32 blk ..); slot 8 (gate or down) and 9 (up)
-  // the step's two E8M0 block scales of the rows, from scales stored
-  // [E][K/32][N] (a block's scales of consecutive rows are contiguous).
-  auto rsrc_b4 = [&](int s, int blk) -> rsrc_t {
+  // MXFP4 B (F4), k-step s: the wavefront's data resource (gate or down
+  // weight, or up for wavefronts 2 and 3 of gate/up) and scale resource
+  // (the step's two E8M0 blocks of every row, scales stored [E][K/32][N]:
+  // one block's scales of consecutive rows are contiguous).
+  auto rsrc_b4 = [&](int s) -> rsrc_t {
     const int k0 = s * KS;
     const bool live = s < ksteps;
-    if (blk < 8) {
-      if constexpr (MODE == GATEUP) {
-        const char* w = reinterpret_cast<const char*>((blk & 2) ? P.b1 : P.b0) + (static_cast<int64_t>(e) * I * H + k0) / 2;
-        return make_rsrc(w, live ? (I * H - k0) / 2 : 0);
-      } else {
-        return make_rsrc(reinterpret_cast<const char*>(P.b0) + (static_cast<int64_t>(e) * H * I + k0) / 2,
-                         live ? (H * I - k0) / 2 : 0);
-      }
-    }
     if constexpr (MODE == GATEUP) {
-      const uint8_t* sc = (blk == 9 ? P.sb1 : P.sb0) + (static_cast<int64_t>(e) * (H / 32) + 2 * s) * I;
-      return make_rsrc(sc, live && blk < 10 ? 2 * I : 0);
+      const char* w = reinterpret_cast<const char*>((wave >> 1) ? P.b1 : P.b0) + (static_cast<int64_t>(e) * I * H + k0) / 2;
+      return make_rsrc(w, live ? (I * H - k0) / 2 : 0);
     } else {
-      const uint8_t* sc = P.sb0 + (static_cast<int64_t>(e) * (I / 32) + 2 * s) * H;
-      return make_rsrc(sc, live && blk == 8 ? 2 * H : 0);
+      return make_rsrc(reinterpret_cast<const char*>(P.b0) + (static_cast<int64_t>(e) * H * I + k0) / 2,
+                       live ? (H * I - k0) / 2 : 0);
     }
   };
-  auto vmem4 = [&](int v, const rsrc_t& ra, int s, bf16_t* L) __attribute__((always_inline)) {
+  auto rsrc_s4 = [&](int s) -> rsrc_t {
+    const bool live = s < ksteps;
+    if constexpr (MODE == GATEUP) {
+      const uint8_t* sc = ((wave >> 1) ? P.sb1 : P.sb0) + (static_cast<int64_t>(e) * (H / 32) + 2 * s) * I;
+      return make_rsrc(sc, live ? 2 * I : 0);
+    } else {
+      return make_rsrc(P.sb0 + (static_cast<int64_t>(e) * (I / 32) + 2 * s) * H, live ? 2 * H : 0);
+    }
+  };
+  auto vmem4 = [&](int v, const rsrc_t& ra, const rsrc_t& rd, const rsrc_t& rs, bf16_t* L)
+                   __attribute__((always_inline)) {
     const int t = v >> 1;
-    const int blk = wave * (LOADS / 2) + t;
-    if ((v & 1) == 0) buf_to_lds16(ra, aoff[t], L + blk * 512);
-    else buf_to_lds16(rsrc_b4(s, blk), boff[t], L + STAGE_A + blk * 512);
+    if ((v & 1) == 0) buf_to_lds16(ra, aoff[t], L + (wave * (LOADS / 2) + t) * 512);
+    else buf_to_lds16(t < 2 ? rd : rs, boff[t], L + STAGE_A + f4_slot(t) * 512);
   };
   // All 8 at once (the first steps of a workgroup's first tile).
   auto issue = [&](int s, bf16_t* L) __attribute__((always_inline)) {
     const rsrc_t ra = rsrc_a(s);
     if constexpr (F4) {
+      const rsrc_t rd = rsrc_b4(s), rs = rsrc_s4(s);
 #pragma unroll
-      for (int v = 0; v < LOADS; ++v) vmem4(v, ra, s, L);
+      for (int v = 0; v < LOADS; ++v) vmem4(v, ra, rd, rs, L);
     } else {
       const rsrc_t rb = rsrc_b(s);
 #pragma unroll
@@ -972,7 +984,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
     for (int j = 0; j < FN; ++j) {
       const int r = wn * WTN + j * 32 + (lane & 31);
       if constexpr (F4) {
-        bof8[j] = r * 32 + h * 16;
+        bof8[j] = r * 32 + ((h ^ sw4(r)) << 4);
         if constexpr (MODE == GATEUP) {
           const int q = r & 127, hf = r >> 7;
           sof4[j] = (q < 64 ? 8 * 1024 + q : 9 * 1024 + (q - 64)) + h * 128 + hf * 64;
@@ -1058,7 +1070,8 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
                     __attribute__((always_inline)) {
     constexpr int nbm = decltype(nbc)::value;
     const rsrc_t ra = rsrc_a(sn);
-    const rsrc_t rb = F4 ? ra : rsrc_b(sn);
+    const rsrc_t rb = F4 ? rsrc_b4(sn) : rsrc_b(sn);
+    const rsrc_t rs = F4 ? rsrc_s4(sn) : ra;
     if (!last) {
       __builtin_amdgcn_s_waitcnt(kWaitVm8);
       step_barrier();
@@ -1081,8 +1094,8 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (F4) {
-        vmem4(2 * i, ra, sn, Ln);
-        vmem4(2 * i + 1, ra, sn, Ln);
+        vmem4(2 * i, ra, rb, rs, Ln);
+        vmem4(2 * i + 1, ra, rb, rs, Ln);
       } else {
         vmem(2 * i, ra, rb, Ln);
         vmem(2 * i + 1, ra, rb, Ln);
