@@ -39,7 +39,7 @@ template <> struct Vec<bf16_t> {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      w[i] = static_cast<uint32_t>(f32_to_bf16(o[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(o[2 * i + 1])) << 16);
+      w[i] = pack_bf16x2(o[2 * i], o[2 * i + 1]);
     return make_uint4(w[0], w[1], w[2], w[3]);
   }
 };

@@ -208,10 +208,6 @@ __device__ __forceinline__ void store_b128(u32x4 v, rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStoreNT);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const f32x2 v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
 __device__ __forceinline__ u32x2 pack_bf16x4v(const float (&v)[4]) {
   return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }

@@ -38,7 +38,7 @@ __device__ __forceinline__ uint4 load16(rsrc_t r, uint32_t off) {
 
 constexpr int kThreads = 256;
 constexpr int kMT = 128;          // merge tile: 128 weight rows x 128 weight columns of one expert
-constexpr int kMergeRowTiles = 2; // row tiles per merge block
+constexpr int kMergeRowTiles = 8; // most row tiles per merge block (an expert's tiles are split evenly over blocks)
 constexpr int kMaxRank = 128;
 constexpr int kLdsRow = kMaxRank + 8;  // A^T row in LDS (bf16); +8 keeps rows 16-byte aligned and off one bank
 constexpr int kStageRow = kMT + 4;     // fp32 stage row: 16-byte aligned, rows 4 banks apart
@@ -62,9 +62,11 @@ __device__ __forceinline__ float bf16f(bf16_t v) { return __uint_as_float(static
 // on the matrix cores (v_mfma_f32_32x32x16_bf16, exact bf16 products, fp32
 // accumulation in j order), the scale and the add in fp32, one rounding.
 //
-// Block: 128 columns of expert blockIdx.z and up to kMergeRowTiles tiles of
-// 128 rows; 4 wavefronts, each 64 columns x 64 rows of a tile (2 x 2 MFMA
-// blocks of 32 x 32). MFMA rows are weight columns: the operand is A^T,
+// Block: 128 columns of expert blockIdx.z and `per` consecutive tiles of
+// 128 rows (fewer in the last block), per = the expert's ceil(N / 128)
+// tiles spread evenly over ceil(tiles / kMergeRowTiles) blocks; 4
+// wavefronts, each 64 columns x 64 rows of a tile (2 x 2 MFMA blocks of
+// 32 x 32). MFMA rows are weight columns: the operand is A^T,
 // staged transposed in LDS once per block and then held in registers for
 // every row tile. MFMA columns are weight rows: the operand is B's rows, 16
 // contiguous bytes per lane straight from memory. The sums go through LDS
@@ -97,12 +99,13 @@ template <int NS, int WF>
 __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, float s, const void* wv_in,
                                                          const uint8_t* __restrict__ w8,
                                                          const bf16_t* __restrict__ a, const bf16_t* __restrict__ b,
-                                                         bf16_t* w_out) {
+                                                         bf16_t* w_out, int per) {
   const bf16_t* w = static_cast<const bf16_t*>(wv_in);
   __shared__ __attribute__((aligned(16))) float lds[kMT * kStageRow];
   bf16_t* at = reinterpret_cast<bf16_t*>(lds);  // A^T [128][kLdsRow], then the fp32 stage [128][kStageRow]
   const int e = blockIdx.z;
-  const int c0 = blockIdx.x * kMT, nbeg = blockIdx.y * kMT * kMergeRowTiles;
+  const int c0 = blockIdx.x * kMT, nbeg = blockIdx.y * kMT * per;
+  const int nend = min(N, nbeg + kMT * per);  // this block's rows
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wc = wave & 1, wn = wave >> 1;
   const int h = lane >> 5, l32 = lane & 31;
@@ -175,10 +178,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
       }
     }
   };
-  load_tile(nbeg, wv[0], wsc[0]);
-#pragma unroll
-  for (int t = 0; t < kMergeRowTiles; ++t) {
-    const int nt = nbeg + t * kMT;
+  // One row tile at nt with its W runs in (wc_t, sc_t); the next tile's
+  // loads go to (wn_t, sn_t). Past the block's rows they address rows >= N,
+  // which read zeros without touching memory: no branch, so the compiler
+  // keeps the loads in flight across the epilogue's waits.
+  auto row_tile = [&](int nt, const WRun (&wc_t)[kMT / 16], const int (&sc_t)[kMT / 16], WRun (&wn_t)[kMT / 16],
+                      int (&sn_t)[kMT / 16]) __attribute__((always_inline)) {
     f32x16 acc[2][2];
 #pragma unroll
     for (int tc = 0; tc < 2; ++tc)
@@ -190,9 +195,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
           acc[tc][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tc][q], fb[tn][q], acc[tc][tn], 0, 0, 0);
       }
     // The next tile's loads fly during this tile's epilogue.
-    // Rows past N read zeros and are not stored: no branch, so the
-    // compiler keeps these loads in flight across the epilogue's waits.
-    if (t + 1 < kMergeRowTiles) load_tile(nt + kMT, wv[(t + 1) & 1], wsc[(t + 1) & 1]);
+    load_tile(nt + kMT < nend ? nt + kMT : N, wn_t, sn_t);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();  // A^T (first tile) or the previous tile's stage has been read
     // Lane l holds, per block and i < 4, columns 8i + 4(l/32) .. + 3 of row l%32.
@@ -205,7 +208,6 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
           *reinterpret_cast<float4*>(&lds[(wn * 64 + tn * 32 + l32) * kStageRow + wc * 64 + tc * 32 + 8 * i + 4 * h]) =
               make_float4(acc[tc][tn][4 * i], acc[tc][tn][4 * i + 1], acc[tc][tn][4 * i + 2], acc[tc][tn][4 * i + 3]);
     lds_barrier();
-    const WRun (&wc_t)[kMT / 16] = wv[t & 1];
 #pragma unroll
     for (int q = 0; q < kMT / 16; ++q) {
       const int n = nt + 16 * q + rrow;
@@ -215,12 +217,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
       const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       float wf[8];
       if constexpr (WF == kMxfp4) {
-        const int X = (wsc[t & 1][q] & 0xff) - 127;  // the block's E8M0 scale
+        const int X = (sc_t[q] & 0xff) - 127;  // the block's E8M0 scale
         const uint32_t c8 = wc_t[q];
 #pragma unroll
         for (int p = 0; p < 8; ++p) wf[p] = ldexpf(e2m1_value((c8 >> (4 * p)) & 15u), X);
       } else if constexpr (WF == kE4M3) {
-        const int X = (wsc[t & 1][q] & 0xff) - 127;  // the row's E8M0 scale
+        const int X = (sc_t[q] & 0xff) - 127;  // the row's E8M0 scale
         const uint32_t c2[2] = {wc_t[q].x, wc_t[q].y};
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
@@ -244,17 +246,24 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
       for (int p = 0; p < 4; ++p) {
         const float lo = wf[2 * p] + s * v[2 * p];
         const float hi = wf[2 * p + 1] + s * v[2 * p + 1];
-        o[p] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+        o[p] = pack_bf16x2(lo, hi);
       }
       *reinterpret_cast<uint4*>(w_out + wbase + static_cast<int64_t>(n) * K + c0 + rcol) =
           make_uint4(o[0], o[1], o[2], o[3]);
     }
+  };
+  // Row tiles two at a time, so that the two register sets of W runs stay
+  // compile-time named.
+  load_tile(nbeg, wv[0], wsc[0]);
+  for (int nt = nbeg; nt < nend; nt += 2 * kMT) {
+    row_tile(nt, wv[0], wsc[0], wv[1], wsc[1]);
+    if (nt + kMT < nend) row_tile(nt + kMT, wv[1], wsc[1], wv[0], wsc[0]);
   }
 }
 
 __device__ __forceinline__ uint32_t scale_pair(uint32_t v, float s) {
   const float lo = s * __uint_as_float(v << 16), hi = s * __uint_as_float(v & 0xffff0000u);
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  return pack_bf16x2(lo, hi);
 }
 
 // Stacked, scaled adapter rows, each block padded to rp rows:
@@ -313,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void blockdiag_t_kernel(int C, int r, int
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const float lo = live ? tile[cq + 2 * p][j] : 0.0f, hi = live ? tile[cq + 2 * p + 1][j] : 0.0f;
-      o[p] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+      o[p] = pack_bf16x2(lo, hi);
     }
     *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(J) * nb * C) = make_uint4(o[0], o[1], o[2], o[3]);
   }
@@ -522,7 +531,7 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(int E, const int32_t* __
       uint32_t o[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        o[q] = static_cast<uint32_t>(f32_to_bf16(v[2 * q])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * q + 1])) << 16);
+        o[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
       *reinterpret_cast<uint4*>(out + static_cast<int64_t>(r0 + row) * N + nb * 32 + 16 * p + 8 * h) =
           make_uint4(o[0], o[1], o[2], o[3]);
     }
@@ -1039,20 +1048,21 @@ namespace {
 template <int WF>
 hipError_t merge_launch(int E, int N, int K, int r, float s, const void* w, const uint8_t* w8, const void* a,
                         const void* b, void* w_out, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(ceil_div(K, kMT)), static_cast<unsigned>(ceil_div(N, kMT * kMergeRowTiles)),
+  const int tiles = ceil_div(N, kMT), per = ceil_div(tiles, ceil_div(tiles, kMergeRowTiles));
+  const dim3 grid(static_cast<unsigned>(ceil_div(K, kMT)), static_cast<unsigned>(ceil_div(tiles, per)),
                   static_cast<unsigned>(E));
   const bf16_t* ap = static_cast<const bf16_t*>(a);
   const bf16_t* bp = static_cast<const bf16_t*>(b);
   bf16_t* op = static_cast<bf16_t*>(w_out);
   switch ((r + 15) / 16) {
-    case 1: merge_kernel<1, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
-    case 2: merge_kernel<2, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
-    case 3: merge_kernel<3, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
-    case 4: merge_kernel<4, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
-    case 5: merge_kernel<5, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
-    case 6: merge_kernel<6, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
-    case 7: merge_kernel<7, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
-    case 8: merge_kernel<8, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op); break;
+    case 1: merge_kernel<1, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op, per); break;
+    case 2: merge_kernel<2, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op, per); break;
+    case 3: merge_kernel<3, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op, per); break;
+    case 4: merge_kernel<4, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op, per); break;
+    case 5: merge_kernel<5, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op, per); break;
+    case 6: merge_kernel<6, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op, per); break;
+    case 7: merge_kernel<7, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op, per); break;
+    case 8: merge_kernel<8, WF><<<grid, kThreads, 0, st>>>(N, K, r, s, w, w8, ap, bp, op, per); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
