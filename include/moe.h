@@ -475,6 +475,75 @@ moe_status moe_quantize_mxfp4_rows(int32_t rows, int32_t K, const void* in, uint
 moe_status moe_lora_merge_mxfp4(int32_t E, int32_t N, int32_t K, int32_t r, float scale, const uint8_t* wq,
                                 const uint8_t* w_e8, const void* a, const void* b, void* w_out, hipStream_t stream);
 
+/* The adapter step without merged weights (sourcepulse summary, "Highlighted
+ * Details": LoRA on the fused experts; torchtune PR #2820: LoRA for the
+ * Qwen3 MoE port). The frozen W_P stay as they are and no W' is built: each
+ * GEMM runs over a reduction extended by the adapter's rank,
+ *   G = [X | X (sA_gate)^T] [W_gate | B_gate]^T    (U likewise, A = silu(G) U)
+ *   O = [A | A (sA_down)^T] [W_down | B_down]^T
+ *   dA = [dO | dO (sB_down)] [W_down; A_down]      (then the SwiGLU backward)
+ *   dX_perm = [dG | dU | dG (sB_gate) | dU (sB_up)] [W_gate; W_up; A_gate; A_up]
+ * which equals the stage on W' = W + s B A up to rounding: the rank-wide row
+ * projections are rounded to bf16 before the GEMM, where the merged path
+ * rounds W'. The projections stay in the workspace and give the adapter
+ * gradients without a second pass (moe_lora_grads_unmerged). The chain, all
+ * on one stream:
+ *   moe_lora_prepare (once per step: the adapters, scaled and stacked) ->
+ *   moe_route -> moe_permute -> moe_lora_gemm_gate_up -> moe_lora_gemm_down ->
+ *   moe_combine; moe_combine_bwd -> moe_lora_gemm_down_dgrad ->
+ *   moe_lora_gemm_gate_up_dgrad -> moe_unpermute_sum -> moe_route_bwd, and
+ *   moe_lora_grads_unmerged.
+ * Every call takes the rank r (as moe_lora_grads: a multiple of 8, at most
+ * 128), the workspace ws of ws_bytes >= moe_lora_unmerged_workspace_bytes
+ * (MOE_EWORKSPACE otherwise; it holds the stacks and the projections
+ * between the calls, so the calls of one step must not overlap another
+ * step's) and the shapes and buffers of the plain call it replaces. The
+ * projections' rows are addressed with 32-bit byte offsets: T*k*4*rp < 2^31,
+ * rp = r rounded up to 32, 64 or 128 (MOE_EUNSUPPORTED otherwise). */
+
+/* Bytes of workspace for the unmerged adapter step (0 if shape or rank are
+ * rejected): moe_lora_workspace_bytes' regions plus the GEMMs' extensions,
+ * [B_gate | 0] and [0 | B_up] [E,I,2rp], B_down [E,H,rp], [A_gate; A_up]
+ * [E,2rp,H] and A_down [E,rp,I] (bf16, padded with zeros). */
+size_t moe_lora_unmerged_workspace_bytes(moe_shape s, int32_t r);
+
+/* The adapters of this step (a_P [E,r,K], b_P [E,N,r] bf16, scale s) into
+ * ws: the scaled stacks of the row projections and the GEMMs' extensions.
+ * Run once per step, before the other calls. */
+moe_status moe_lora_prepare(moe_shape s, int32_t r, float scale, const void* a_gate, const void* b_gate,
+                            const void* a_up, const void* b_up, const void* a_down, const void* b_down, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* moe_gemm_gate_up with the adapters: Z = x_perm [sA_gate; sA_up]^T [T*k,2rp]
+ * into ws, then G, U, A over the extended reduction. */
+moe_status moe_lora_gemm_gate_up(moe_shape s, int32_t r, const void* x_perm, const int32_t* offsets,
+                                 const void* w_gate, const void* w_up, void* g, void* u, void* a, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/* moe_gemm_down with the adapters: Z_down = a (sA_down)^T into ws, then
+ * o_perm over the extended reduction. */
+moe_status moe_lora_gemm_down(moe_shape s, int32_t r, const void* a, const int32_t* offsets, const void* w_down,
+                              void* o_perm, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_gemm_down_dgrad with the adapters: Y_down = do_perm sB_down into ws,
+ * then dA over the extended reduction and the SwiGLU backward into dgu. */
+moe_status moe_lora_gemm_down_dgrad(moe_shape s, int32_t r, const void* do_perm, const int32_t* offsets,
+                                    const void* w_down, const void* g, const void* u, void* dgu, void* ws,
+                                    size_t ws_bytes, hipStream_t stream);
+
+/* moe_gemm_gate_up_dgrad with the adapters: Y_gu = [dG sB_gate | dU sB_up]
+ * into ws, then dx_perm over the extended reduction. */
+moe_status moe_lora_gemm_gate_up_dgrad(moe_shape s, int32_t r, const void* dgu, const int32_t* offsets,
+                                       const void* w_gate, const void* w_up, void* dx_perm, void* ws,
+                                       size_t ws_bytes, hipStream_t stream);
+
+/* The six adapter gradients (as moe_lora_grads) from the projections the
+ * four calls above left in ws: the outer products only. */
+moe_status moe_lora_grads_unmerged(moe_shape s, int32_t r, const void* x_perm, const void* act, const void* dgu,
+                                   const void* do_perm, const int32_t* offsets, float* da_gate, float* db_gate,
+                                   float* da_up, float* db_up, float* da_down, float* db_down, void* ws,
+                                   size_t ws_bytes, hipStream_t stream);
+
 /* fp8 activations x MXFP4 weights for the inference forward: the 4-bit
  * expert weights of the sourcepulse summary ("Quick Start & Requirements":
  * bitsandbytes 4-bit; "Limitations & Caveats": the fused 4-bit

@@ -90,6 +90,13 @@ _SIGS = {
     "moe_lora_grads_gathered": ([moe_shape, ctypes.c_int32, ctypes.c_float] + [_P] * 20 + [ctypes.c_size_t, _P],
                                 ctypes.c_int),
     "moe_gemm_down_dgrad_dy": ([moe_shape] + [_P] * 9, ctypes.c_int),
+    "moe_lora_unmerged_workspace_bytes": ([moe_shape, ctypes.c_int32], ctypes.c_size_t),
+    "moe_lora_prepare": ([moe_shape, ctypes.c_int32, ctypes.c_float] + [_P] * 7 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_lora_gemm_gate_up": ([moe_shape, ctypes.c_int32] + [_P] * 8 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_lora_gemm_down": ([moe_shape, ctypes.c_int32] + [_P] * 5 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_lora_gemm_down_dgrad": ([moe_shape, ctypes.c_int32] + [_P] * 7 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_lora_gemm_gate_up_dgrad": ([moe_shape, ctypes.c_int32] + [_P] * 6 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_lora_grads_unmerged": ([moe_shape, ctypes.c_int32] + [_P] * 12 + [ctypes.c_size_t, _P], ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -460,6 +467,48 @@ def moe_lora_grads(s, r, scale, x_perm, act, dgu, do_perm, offsets, a_gate, b_ga
         _ptr(db_up), _ptr(da_down), _ptr(db_down), _ptr(ws), nb, _stream(stream)))
 
 
+def _nbytes(ws, ws_bytes):
+    return ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+
+
+def moe_lora_unmerged_workspace_bytes(s: moe_shape, r: int) -> int:
+    return int(lib.moe_lora_unmerged_workspace_bytes(s, r))
+
+
+def moe_lora_prepare(s, r, scale, a_gate, b_gate, a_up, b_up, a_down, b_down, ws, ws_bytes=None, stream=None):
+    _check("moe_lora_prepare", lib.moe_lora_prepare(
+        s, r, ctypes.c_float(scale), *[_ptr(t) for t in (a_gate, b_gate, a_up, b_up, a_down, b_down, ws)],
+        _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def moe_lora_gemm_gate_up(s, r, x_perm, offsets, w_gate, w_up, g, u, a, ws, ws_bytes=None, stream=None):
+    _check("moe_lora_gemm_gate_up", lib.moe_lora_gemm_gate_up(
+        s, r, *[_ptr(t) for t in (x_perm, offsets, w_gate, w_up, g, u, a, ws)], _nbytes(ws, ws_bytes),
+        _stream(stream)))
+
+
+def moe_lora_gemm_down(s, r, a, offsets, w_down, o_perm, ws, ws_bytes=None, stream=None):
+    _check("moe_lora_gemm_down", lib.moe_lora_gemm_down(
+        s, r, *[_ptr(t) for t in (a, offsets, w_down, o_perm, ws)], _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def moe_lora_gemm_down_dgrad(s, r, do_perm, offsets, w_down, g, u, dgu, ws, ws_bytes=None, stream=None):
+    _check("moe_lora_gemm_down_dgrad", lib.moe_lora_gemm_down_dgrad(
+        s, r, *[_ptr(t) for t in (do_perm, offsets, w_down, g, u, dgu, ws)], _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def moe_lora_gemm_gate_up_dgrad(s, r, dgu, offsets, w_gate, w_up, dx_perm, ws, ws_bytes=None, stream=None):
+    _check("moe_lora_gemm_gate_up_dgrad", lib.moe_lora_gemm_gate_up_dgrad(
+        s, r, *[_ptr(t) for t in (dgu, offsets, w_gate, w_up, dx_perm, ws)], _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def moe_lora_grads_unmerged(s, r, x_perm, act, dgu, do_perm, offsets, da_gate, db_gate, da_up, db_up, da_down,
+                            db_down, ws, ws_bytes=None, stream=None):
+    _check("moe_lora_grads_unmerged", lib.moe_lora_grads_unmerged(
+        s, r, *[_ptr(t) for t in (x_perm, act, dgu, do_perm, offsets, da_gate, db_gate, da_up, db_up, da_down,
+                                  db_down, ws)], _nbytes(ws, ws_bytes), _stream(stream)))
+
+
 def moe_lora_grads_gathered(s, r, scale, x, row_token, row_weight, act, dgu, dy, offsets, a_gate, b_gate, a_up,
                             b_up, a_down, b_down, da_gate, db_gate, da_up, db_up, da_down, db_down, ws, ws_bytes=None,
                             stream=None):
@@ -668,22 +717,32 @@ class LoRAStage(MoEStage):
     routing weight (moe_gemm_down_dgrad_dy), and the adapter gradients read x
     and dy through them (moe_lora_grads_gathered). Within rounding of the
     default chain. Not combined with the forward's aux_stream.
+
+    ``unmerged``: no W' at all (bf16 frozen weights only). moe_lora_prepare
+    stacks the adapters; every GEMM runs over its reduction extended by the
+    rank (moe_lora_gemm_gate_up, moe_lora_gemm_down, moe_lora_gemm_down_dgrad,
+    moe_lora_gemm_gate_up_dgrad), and moe_lora_grads_unmerged takes the
+    adapter gradients from the row projections those calls kept. Within
+    rounding of the merged chain.
     """
 
     def __init__(self, T: int, H: int, E: int, k: int, I: int, rank: int, scale: float, device="cuda",
-                 gathered: bool = False):
+                 gathered: bool = False, unmerged: bool = False):
+        if gathered and unmerged:
+            raise ValueError("the unmerged adapter step reads x_perm and do_perm")
         super().__init__(T, H, E, k, I, torch.bfloat16, device=device, gather_fused=gathered)
-        self.gathered = gathered
+        self.gathered, self.unmerged = gathered, unmerged
         self.weight_grads = False
         self.rank, self.scale = rank, scale
-        nb = moe_lora_workspace_bytes(self.s, rank)
+        nb = (moe_lora_unmerged_workspace_bytes if unmerged else moe_lora_workspace_bytes)(self.s, rank)
         if nb == 0:
             raise MoEError("moe_lora_workspace_bytes", 2, "shape or rank rejected")
         dev = self.ws.device
         self.lora_ws = torch.empty(nb, dtype=torch.uint8, device=dev)
         bf = torch.bfloat16
-        self.merged = (torch.empty(E, I, H, dtype=bf, device=dev), torch.empty(E, I, H, dtype=bf, device=dev),
-                       torch.empty(E, H, I, dtype=bf, device=dev))
+        self.merged = None if unmerged else (
+            torch.empty(E, I, H, dtype=bf, device=dev), torch.empty(E, I, H, dtype=bf, device=dev),
+            torch.empty(E, H, I, dtype=bf, device=dev))
         f32 = torch.float32
         self.buf.update({
             "da_gate": torch.empty(E, rank, H, dtype=f32, device=dev), "db_gate": torch.empty(E, I, rank, dtype=f32,
@@ -709,6 +768,10 @@ class LoRAStage(MoEStage):
         ``stream``; gate/up waits for its two merges and down for its own.
         The results are the same bits either way."""
         self.adapters = adapters
+        if self.unmerged:
+            if aux_stream is not None:
+                raise ValueError("the unmerged adapter step has no merges to move to a second stream")
+            return self._forward_unmerged(x, w_router, w_gate, w_up, w_down, adapters, logit_bias, stream)
         if aux_stream is None:
             wg, wu, wd = self.merge(w_gate, w_up, w_down, adapters, stream)
             return super().forward(x, w_router, wg, wu, wd, logit_bias, stream)
@@ -740,9 +803,36 @@ class LoRAStage(MoEStage):
         moe_combine(s, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["y"], main)
         return b["y"]
 
+    def _forward_unmerged(self, x, w_router, w_gate, w_up, w_down, adapters, logit_bias, stream):
+        b, s, r, lw = self.buf, self.s, self.rank, self.lora_ws
+        if not all(isinstance(w, torch.Tensor) and w.dtype == torch.bfloat16 for w in (w_gate, w_up, w_down)):
+            raise TypeError("the unmerged adapter step takes bf16 frozen weights")
+        self.w = (w_gate, w_up, w_down)
+        self.x = x
+        moe_lora_prepare(s, r, self.scale, *(adapters[n] for n in LORA_NAMES), lw, stream=stream)
+        moe_route(s, x, w_router, logit_bias, b["logits"], b["topk_idx"], b["topk_w"], stream)
+        moe_permute(s, b["topk_idx"], x, b["counts"], b["offsets"], b["sorted_to_flat"], b["flat_to_sorted"],
+                    b["x_perm"], self.ws, stream=stream)
+        moe_lora_gemm_gate_up(s, r, b["x_perm"], b["offsets"], w_gate, w_up, b["g"], b["u"], b["a"], lw, stream=stream)
+        moe_lora_gemm_down(s, r, b["a"], b["offsets"], w_down, b["o_perm"], lw, stream=stream)
+        moe_combine(s, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["y"], stream)
+        return b["y"]
+
     def backward(self, dy, stream=None):
         self._alloc_bwd()
         b, s = self.buf, self.s
+        if self.unmerged:
+            wg, wu, wd = self.w
+            r, lw = self.rank, self.lora_ws
+            moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["do_perm"], b["d_topk_w"],
+                            stream)
+            moe_lora_gemm_down_dgrad(s, r, b["do_perm"], b["offsets"], wd, b["g"], b["u"], b["dgu"], lw, stream=stream)
+            moe_lora_gemm_gate_up_dgrad(s, r, b["dgu"], b["offsets"], wg, wu, b["dx_perm"], lw, stream=stream)
+            moe_lora_grads_unmerged(s, r, b["x_perm"], b["a"], b["dgu"], b["do_perm"], b["offsets"],
+                                    *(b["d" + n] for n in LORA_NAMES), lw, stream=stream)
+            moe_unpermute_sum(s, b["dx_perm"], b["flat_to_sorted"], b["dx"], stream)
+            moe_route_bwd(s, b["d_topk_w"], b["topk_w"], b["topk_idx"], b["d_logits"], stream)
+            return b["dx"]
         wg, wu, wd = self.merged
         ad = self.adapters
         if self.gathered:

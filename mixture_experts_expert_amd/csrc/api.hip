@@ -731,6 +731,151 @@ moe_status moe_lora_grads(moe_shape s, int32_t r, float scale, const void* x_per
   return from_hip(moe::launch_lora_grads(s, r, scale, g, ws, stream));
 }
 
+// ---- The adapter step without merged weights --------------------------------
+namespace {
+// check_lora, the K extensions' rows [T*k][2rp] addressed with 32-bit byte
+// offsets, and the workspace.
+moe_status check_lora_unmerged(const moe_shape& s, int32_t r, size_t ws_bytes) {
+  const moe_status st = check_lora(s, r);
+  if (st != MOE_OK) return st;
+  if (static_cast<int64_t>(s.T) * s.k * 4 * moe::lora_padded_rank(r) >= (static_cast<int64_t>(1) << 31))
+    return MOE_EUNSUPPORTED;
+  if (ws_bytes < moe::lora_layout(s, r, true).total) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+void* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+}  // namespace
+
+size_t moe_lora_unmerged_workspace_bytes(moe_shape s, int32_t r) {
+  if (check_lora_unmerged(s, r, ~static_cast<size_t>(0)) != MOE_OK) return 0;
+  return moe::lora_layout(s, r, true).total;
+}
+
+moe_status moe_lora_prepare(moe_shape s, int32_t r, float scale, const void* a_gate, const void* b_gate,
+                            const void* a_up, const void* b_up, const void* a_down, const void* b_down, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  const moe_status st = check_lora_unmerged(s, r, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (any_null(a_gate, b_gate, a_up, b_up, a_down, b_down, ws)) return MOE_EINVAL;
+  moe::LoraArgs g{};
+  g.a_gate = a_gate;
+  g.b_gate = b_gate;
+  g.a_up = a_up;
+  g.b_up = b_up;
+  g.a_down = a_down;
+  g.b_down = b_down;
+  return from_hip(moe::launch_lora_prepare(s, r, scale, g, ws, true, stream));
+}
+
+moe_status moe_lora_gemm_gate_up(moe_shape s, int32_t r, const void* x_perm, const int32_t* offsets,
+                                 const void* w_gate, const void* w_up, void* g, void* u, void* a, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  const moe_status st = check_lora_unmerged(s, r, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (any_null(x_perm, offsets, w_gate, w_up, g, u, a, ws)) return MOE_EINVAL;
+  const moe::LoraLayout l = moe::lora_layout(s, r, true);
+  hipError_t err = moe::launch_lora_project(s, r, 0, x_perm, offsets, ws, stream);  // Z_gu
+  if (err != hipSuccess) return from_hip(err);
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = x_perm;
+  ga.b0 = w_gate;
+  ga.b1 = w_up;
+  ga.out0 = g;
+  ga.out1 = u;
+  ga.out2 = a;
+  ga.ax = at(ws, l.z_gu);
+  ga.bx0 = at(ws, l.bx_g);
+  ga.bx1 = at(ws, l.bx_u);
+  ga.kx = 2 * moe::lora_padded_rank(r);
+  return from_hip(moe::launch_gemm(moe::GEMM_GATEUP, s, ga, stream));
+}
+
+moe_status moe_lora_gemm_down(moe_shape s, int32_t r, const void* a, const int32_t* offsets, const void* w_down,
+                              void* o_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const moe_status st = check_lora_unmerged(s, r, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (any_null(a, offsets, w_down, o_perm, ws)) return MOE_EINVAL;
+  const moe::LoraLayout l = moe::lora_layout(s, r, true);
+  hipError_t err = moe::launch_lora_project(s, r, 2, a, offsets, ws, stream);  // Z_d
+  if (err != hipSuccess) return from_hip(err);
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = a;
+  ga.b0 = w_down;
+  ga.out0 = o_perm;
+  ga.ax = at(ws, l.z_d);
+  ga.bx0 = at(ws, l.bx_d);
+  ga.kx = moe::lora_padded_rank(r);
+  return from_hip(moe::launch_gemm(moe::GEMM_DOWN, s, ga, stream));
+}
+
+moe_status moe_lora_gemm_down_dgrad(moe_shape s, int32_t r, const void* do_perm, const int32_t* offsets,
+                                    const void* w_down, const void* g, const void* u, void* dgu, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  const moe_status st = check_lora_unmerged(s, r, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (any_null(do_perm, offsets, w_down, g, u, dgu, ws)) return MOE_EINVAL;
+  const moe::LoraLayout l = moe::lora_layout(s, r, true);
+  hipError_t err = moe::launch_lora_project(s, r, 3, do_perm, offsets, ws, stream);  // Y_d
+  if (err != hipSuccess) return from_hip(err);
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = do_perm;
+  ga.b0 = w_down;
+  ga.g_in = g;
+  ga.u_in = u;
+  ga.out0 = dgu;
+  ga.ax = at(ws, l.y_d);
+  ga.bx0 = at(ws, l.ax_d);
+  ga.kx = moe::lora_padded_rank(r);
+  return from_hip(moe::launch_gemm(moe::GEMM_DGRAD_DOWN, s, ga, stream));
+}
+
+moe_status moe_lora_gemm_gate_up_dgrad(moe_shape s, int32_t r, const void* dgu, const int32_t* offsets,
+                                       const void* w_gate, const void* w_up, void* dx_perm, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+  const moe_status st = check_lora_unmerged(s, r, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (any_null(dgu, offsets, w_gate, w_up, dx_perm, ws)) return MOE_EINVAL;
+  const moe::LoraLayout l = moe::lora_layout(s, r, true);
+  hipError_t err = moe::launch_lora_project(s, r, 1, dgu, offsets, ws, stream);  // Y_gu
+  if (err != hipSuccess) return from_hip(err);
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = dgu;
+  ga.b0 = w_gate;
+  ga.b1 = w_up;
+  ga.out0 = dx_perm;
+  ga.ax = at(ws, l.y_gu);
+  ga.bx0 = at(ws, l.ax_gu);
+  ga.kx = 2 * moe::lora_padded_rank(r);
+  return from_hip(moe::launch_gemm(moe::GEMM_DGRAD_GATEUP, s, ga, stream));
+}
+
+moe_status moe_lora_grads_unmerged(moe_shape s, int32_t r, const void* x_perm, const void* act, const void* dgu,
+                                   const void* do_perm, const int32_t* offsets, float* da_gate, float* db_gate,
+                                   float* da_up, float* db_up, float* da_down, float* db_down, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  const moe_status st = check_lora_unmerged(s, r, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (any_null(x_perm, act, dgu, do_perm, offsets, da_gate, db_gate, da_up, db_up, da_down, db_down, ws))
+    return MOE_EINVAL;
+  moe::LoraArgs g{};
+  g.offsets = offsets;
+  g.x_perm = x_perm;
+  g.act = act;
+  g.dgu = dgu;
+  g.do_perm = do_perm;
+  g.da_gate = da_gate;
+  g.db_gate = db_gate;
+  g.da_up = da_up;
+  g.db_up = db_up;
+  g.da_down = da_down;
+  g.db_down = db_down;
+  return from_hip(moe::launch_lora_outer(s, r, g, ws, stream));
+}
+
 moe_status moe_lora_grads_gathered(moe_shape s, int32_t r, float scale, const void* x, const int32_t* row_token,
                                    const float* row_weight, const void* act, const void* dgu, const void* dy,
                                    const int32_t* offsets, const void* a_gate, const void* b_gate, const void* a_up,

@@ -118,6 +118,15 @@ struct Params {
   const uint8_t* sa;
   const uint8_t* sb0;
   const uint8_t* sb1;
+  // K extended by kx (a multiple of BK) past the main reduction (KX
+  // instances: GATEUP, DOWN, DGRAD_DOWN, DGRAD_GATEUP on sorted rows): A's
+  // rows continue in ax [M][kx] and B's in bx0 / bx1 (gate, up), laid out
+  // as the main B with kx in place of its K: [E][N][kx] for GATEUP and DOWN
+  // (k-major), [E][kx][N] for the data gradients (k-rows).
+  const bf16_t* ax;
+  const bf16_t* bx0;
+  const bf16_t* bx1;
+  int kx;
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -367,10 +376,11 @@ struct Smem {
 // Every tile of one GEMM that workgroup `bid` of `nblk` (a multiple of 8)
 // owns, start to finish: on return every load and store this workgroup
 // issued has completed and its waves are past a barrier.
-template <int MODE, bool FUSED, bool F8 = false, bool AW = false, bool F4 = false>
+template <int MODE, bool FUSED, bool F8 = false, bool AW = false, bool F4 = false, bool KX = false>
 __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const int nblk, const Smem& sm) {
   static_assert(!F8 || (FUSED && (MODE == GATEUP || MODE == DOWN)), "fp8: the inference forward's two GEMMs");
   static_assert(!F4 || F8, "MXFP4 weights: with fp8 activations");
+  static_assert(!KX || (!FUSED && !F8 && !AW && !grouped_k(MODE)), "extended K: bf16 GEMMs over sorted rows");
   static_assert(!AW || (MODE == GATEUP && !F8), "a_w: the gate/up GEMM of the training step");
   // Element size in bytes, elements per k-step (64 bytes of a k-major row
   // either way) and per 16-byte chunk.
@@ -511,6 +521,8 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   if constexpr (MODE == DGRAD_GATEUP) { lda = 2 * I; ldb = H; kfixed = 2 * I / BK; }
   if constexpr (MODE == WGRAD_DOWN) { lda = H; ldb = I; }
   if constexpr (MODE == WGRAD_GATEUP) { lda = 2 * I; ldb = H; }
+  const int kmain = kfixed;  // k-steps of the main operands; KX: then P.kx / BK more
+  if constexpr (KX) kfixed += P.kx / BK;
 
   int e = 0, row0 = 0, mvalid = 0, m0 = 0, n0 = 0, kbeg = 0, kend = 0, ksteps = 0;
   int pidx = -1;  // grouped-K: partial tile of a later chunk, -1 for chunk 0
@@ -600,7 +612,9 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   };
   // Per-lane load offsets of the current tile (vector registers; recomputed
   // rather than kept alive across an epilogue).
-  auto set_offsets = [&]() __attribute__((always_inline)) {
+  auto set_offsets = [&](auto ext) __attribute__((always_inline)) {
+    // ext (KX): the extension's offsets, rows of length P.kx.
+    constexpr bool EXT = decltype(ext)::value;
     // An opaque copy of the lane index keeps the lane-only parts of these
     // offsets from being hoisted out of the tile loop (and spilled).
     int lane = lane_id;
@@ -623,7 +637,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
         if (GATHER_A_ROWS)  // row of x or dy; rows >= mvalid read zeros
           aoff[t] = r < mvalid ? ESZ * (static_cast<uint32_t>(P.row_token[row0 + r]) * H + c * CK) : kNoWrite;
         else
-          aoff[t] = ESZ * (r * lda + c * CK);  // rows >= mvalid: outside the range, read as zeros
+          aoff[t] = ESZ * (r * (EXT ? P.kx : lda) + c * CK);  // rows >= mvalid: outside the range, read as zeros
       } else {
         const int k = blk * 2 + (lane >> 5);
         const int c = (lane & 31) ^ swt(k);
@@ -664,11 +678,11 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
         const int c = (lane & 3) ^ swk(r);
         const int j = (r & 127) >> 5;
         const int idx = min(n0 + (r >> 7) * 64 + (j & 1) * 32 + (r & 31), I - 1);
-        boff[t] = ESZ * (idx * H + c * CK);
+        boff[t] = ESZ * (idx * (EXT ? P.kx : H) + c * CK);
       } else if constexpr (MODE == DOWN) {
         const int r = blk * 16 + (lane >> 2);
         const int c = (lane & 3) ^ swk(r);
-        boff[t] = ESZ * (min(n0 + r, H - 1) * I + c * CK);
+        boff[t] = ESZ * (min(n0 + r, H - 1) * (EXT ? P.kx : I) + c * CK);
       } else {
         const int k = blk * 2 + (lane >> 5);
         const int c = (lane & 31) ^ swt(k);
@@ -677,7 +691,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
         else boff[t] = 2u * (k * ldb + min(n0 + c * 8, ncols - 8));
       }
     }
-    abase_m = reinterpret_cast<const char*>(P.a) + static_cast<int64_t>(row0) * lda * ESZ;
+    if constexpr (!EXT) abase_m = reinterpret_cast<const char*>(P.a) + static_cast<int64_t>(row0) * lda * ESZ;
   };
   // No next tile: every load of the chained step reads an empty range.
   auto clear_tile = [&]() {
@@ -686,12 +700,19 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   };
   auto set_tile_and_offsets = [&](int L) __attribute__((always_inline)) {
     set_tile(L);
-    set_offsets();
+    set_offsets(std::false_type{});
   };
 
 
   // Buffer resources of k-step s (num_records 0 past the last step).
   auto rsrc_a = [&](int s) -> rsrc_t {
+    if constexpr (KX) {
+      if (s >= kmain) {  // the extension: rows of length kx, from the tile's first row
+        const int k0x = (s - kmain) * BK;
+        return make_rsrc(reinterpret_cast<const char*>(P.ax) + (static_cast<int64_t>(row0) * P.kx + k0x) * ESZ,
+                         s < ksteps ? ESZ * (mvalid * P.kx - k0x) : 0);
+      }
+    }
     const int k0 = s * KS;
     if constexpr (A_KMAJOR) {
       if (GATHER_A_ROWS)
@@ -704,6 +725,22 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
     }
   };
   auto rsrc_b = [&](int s) -> rsrc_t {
+    if constexpr (KX) {
+      if (s >= kmain) {
+        const int k0x = (s - kmain) * BK;
+        const bool livex = s < ksteps;
+        const int64_t kx = P.kx;
+        if constexpr (MODE == GATEUP)
+          return make_rsrc(((wave & 1) ? P.bx1 : P.bx0) + (static_cast<int64_t>(e) * I * kx + k0x),
+                           livex ? ESZ * (I * P.kx - k0x) : 0);
+        else if constexpr (MODE == DOWN)
+          return make_rsrc(P.bx0 + (static_cast<int64_t>(e) * H * kx + k0x), livex ? ESZ * (H * P.kx - k0x) : 0);
+        else if constexpr (MODE == DGRAD_DOWN)
+          return make_rsrc(P.bx0 + (static_cast<int64_t>(e) * kx + k0x) * I, livex ? 2 * (P.kx - k0x) * I : 0);
+        else
+          return make_rsrc(P.bx0 + (static_cast<int64_t>(e) * kx + k0x) * H, livex ? 2 * (P.kx - k0x) * H : 0);
+      }
+    }
     const int k0 = s * KS;
     const bool live = s < ksteps;
     if constexpr (MODE == GATEUP) {
@@ -803,6 +840,9 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   };
   // All 8 at once (the first steps of a workgroup's first tile).
   auto issue = [&](int s, bf16_t* L) __attribute__((always_inline)) {
+    if constexpr (KX) {
+      if (s >= kmain) set_offsets(std::true_type{});
+    }
     const rsrc_t ra = rsrc_a(s);
     if constexpr (F4) {
       const rsrc_t rd = rsrc_b4(s), rs = rsrc_s4(s);
@@ -930,6 +970,9 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
       tkA = tkB;
       tkB = tn;
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (KX) {  // the extension's steps: its offsets (a tile's last steps, or the next tile's first)
+      if (sn >= kmain) set_offsets(std::true_type{});
     }
     const rsrc_t ra = rsrc_a(sn);
     const rsrc_t rb = rsrc_b(sn);
@@ -1464,15 +1507,15 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
     step_barrier();
     // The offsets again rather than kept alive through the epilogue (the
     // opaque lane index in set_offsets makes this a real recomputation).
-    set_offsets();
+    set_offsets(std::false_type{});
   }
 }
 
-template <int MODE, bool FUSED, bool F8, bool AW, bool F4>
+template <int MODE, bool FUSED, bool F8, bool AW, bool F4, bool KX>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(
     Params P) {
   MOE_GEMM_SMEM
-  gemm_tiles<MODE, FUSED, F8, AW, F4>(P, blockIdx.x, gridDim.x, sm);
+  gemm_tiles<MODE, FUSED, F8, AW, F4, KX>(P, blockIdx.x, gridDim.x, sm);
 }
 
 // Two independent GEMMs of the backward in one persistent launch: a data
@@ -1579,10 +1622,10 @@ int persistent_grid() {
   return cached;
 }
 
-template <int MODE, bool FUSED = false, bool F8 = false, bool AW = false, bool F4 = false>
+template <int MODE, bool FUSED = false, bool F8 = false, bool AW = false, bool F4 = false, bool KX = false>
 hipError_t run(const Params& p, hipStream_t st) {
   const int grid = persistent_grid();
-  grouped_gemm_kernel<MODE, FUSED, F8, AW, F4><<<grid, NT, 0, st>>>(p);
+  grouped_gemm_kernel<MODE, FUSED, F8, AW, F4, KX><<<grid, NT, 0, st>>>(p);
   hipError_t err = hipGetLastError();
   if constexpr (grouped_k(MODE)) {
     if (err != hipSuccess) return err;
@@ -1626,6 +1669,10 @@ Params make_params(const moe_shape& s, const GemmArgs& g) {
   p.sa = g.a_scale;
   p.sb0 = g.b0_scale;
   p.sb1 = g.b1_scale;
+  p.ax = static_cast<const bf16_t*>(g.ax);
+  p.bx0 = static_cast<const bf16_t*>(g.bx0);
+  p.bx1 = static_cast<const bf16_t*>(g.bx1);
+  p.kx = g.kx;
   return p;
 }
 
@@ -1644,17 +1691,25 @@ hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g
   const Params p = make_params(s, g);
   switch (mode) {
     case GEMM_GATEUP:
+      if (g.kx > 0)
+        return g.row_token || g.a_scale || g.out3 ? hipErrorInvalidValue : run<GATEUP, false, false, false, false, true>(p, st);
       if (g.a_scale && g.b_fp4) return g.row_token ? run<GATEUP, true, true, false, true>(p, st) : hipErrorInvalidValue;
       if (g.a_scale) return g.row_token ? run<GATEUP, true, true>(p, st) : hipErrorInvalidValue;
       if (g.out3)  // a_w (needs row_weight)
         return g.row_token ? run<GATEUP, true, false, true>(p, st) : run<GATEUP, false, false, true>(p, st);
       return g.row_token ? run<GATEUP, true>(p, st) : run<GATEUP>(p, st);
     case GEMM_DOWN:
+      if (g.kx > 0)
+        return g.row_weight || g.a_scale ? hipErrorInvalidValue : run<DOWN, false, false, false, false, true>(p, st);
       if (g.a_scale && g.b_fp4) return g.row_weight ? run<DOWN, true, true, false, true>(p, st) : hipErrorInvalidValue;
       if (g.a_scale) return g.row_weight ? run<DOWN, true, true>(p, st) : hipErrorInvalidValue;
       return g.row_weight ? run<DOWN, true>(p, st) : run<DOWN>(p, st);
-    case GEMM_DGRAD_DOWN: return g.row_token ? run<DGRAD_DOWN, true>(p, st) : run<DGRAD_DOWN>(p, st);
-    case GEMM_DGRAD_GATEUP: return run<DGRAD_GATEUP>(p, st);
+    case GEMM_DGRAD_DOWN:
+      if (g.kx > 0) return g.row_token ? hipErrorInvalidValue : run<DGRAD_DOWN, false, false, false, false, true>(p, st);
+      return g.row_token ? run<DGRAD_DOWN, true>(p, st) : run<DGRAD_DOWN>(p, st);
+    case GEMM_DGRAD_GATEUP:
+      if (g.kx > 0) return run<DGRAD_GATEUP, false, false, false, false, true>(p, st);
+      return run<DGRAD_GATEUP>(p, st);
     case GEMM_WGRAD_DOWN: return g.row_token ? run<WGRAD_DOWN, true>(p, st) : run<WGRAD_DOWN>(p, st);
     case GEMM_WGRAD_GATEUP: return g.row_token ? run<WGRAD_GATEUP, true>(p, st) : run<WGRAD_GATEUP>(p, st);
   }

@@ -286,6 +286,22 @@ __global__ __launch_bounds__(kThreads) void stack_a_kernel(int r, int rp, int K,
   *reinterpret_cast<uint4*>(out + static_cast<int64_t>(row) * K + c) = o;
 }
 
+// Rows of B [rows][r] placed at columns off .. off + r - 1 of zero rows
+// [rows][width] (bf16; r % 8 == 0, off and width multiples of 8): the K
+// extensions [B_gate | 0], [0 | B_up] and [B_down | 0] of the unmerged
+// forward GEMMs. One thread per 8 output columns.
+__global__ __launch_bounds__(kThreads) void pad_cols_kernel(int64_t rows, int r, int width, int off,
+                                                            const bf16_t* __restrict__ in, bf16_t* __restrict__ out) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int per = width / 8;
+  if (q >= rows * per) return;
+  const int64_t row = q / per;
+  const int c = static_cast<int>(q - row * per) * 8 - off;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (c >= 0 && c < r) v = *reinterpret_cast<const uint4*>(in + row * r + c);
+  *reinterpret_cast<uint4*>(out + row * width + (c + off)) = v;
+}
+
 // Block-diagonal transposed stack: out[e][J][c], J < nb rp, c < nb C, with
 // J = bj rp + j, c = bc C + cc: bf16(s in_bj[e][cc][j]) where bj == bc and
 // j < r, else 0; in_b [E][C][r], nb = 2 when in1 is given, C % 64 == 0.
@@ -1015,7 +1031,7 @@ hipError_t outer_products(int E, int nb, const int32_t* offsets, const OuterJobs
 // own work).
 int lora_padded_rank(int r) { return r <= 32 ? 32 : (r <= 64 ? 64 : 128); }
 
-LoraLayout lora_layout(const moe_shape& s, int r) {
+LoraLayout lora_layout(const moe_shape& s, int r, bool unmerged) {
   LoraLayout l{};
   const int64_t M = static_cast<int64_t>(s.T) * s.k;
   const int64_t E = s.E, H = s.H, I = s.I, rp = lora_padded_rank(r);
@@ -1040,6 +1056,13 @@ LoraLayout lora_layout(const moe_shape& s, int r) {
   const int64_t max_tiles = (2 * ceil_div(I, 128) + ceil_div(H, 128)) * E + 2 * grid;
   l.plan = take(256 + max_tiles * static_cast<int64_t>(sizeof(OuterDesc)) + 2 * grid * sizeof(OuterUnit));
   l.part = take(2 * grid * kOuterPartFloats * 4);
+  if (unmerged) {
+    l.bx_g = take(E * I * 2 * rp * 2);
+    l.bx_u = take(E * I * 2 * rp * 2);
+    l.bx_d = take(E * H * rp * 2);
+    l.ax_gu = take(E * 2 * rp * H * 2);
+    l.ax_d = take(E * rp * I * 2);
+  }
   l.total = off;
   return l;
 }
@@ -1084,17 +1107,47 @@ hipError_t launch_lora_merge_mxfp4(int E, int N, int K, int r, float s, const ui
   return merge_launch<kMxfp4>(E, N, K, r, s, wq, w8, a, b, w_out, st);
 }
 
-hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraArgs& g, void* ws, hipStream_t st) {
-  const LoraLayout l = lora_layout(s, r);
+namespace {
+// The workspace's named regions.
+struct LoraPtrs {
+  bf16_t *sa_gu, *sa_d, *sbt_gu, *sbt_d, *z_gu, *z_d, *y_gu, *y_d, *bx_g, *bx_u, *bx_d, *ax_gu, *ax_d;
+  OuterSpace os;
+};
+LoraPtrs lora_ptrs(const moe_shape& s, int r, void* ws, bool unmerged) {
+  const LoraLayout l = lora_layout(s, r, unmerged);
   char* base = static_cast<char*>(ws);
-  bf16_t* sa_gu = reinterpret_cast<bf16_t*>(base + l.sa_gu);
-  bf16_t* sa_d = reinterpret_cast<bf16_t*>(base + l.sa_d);
-  bf16_t* sbt_gu = reinterpret_cast<bf16_t*>(base + l.sbt_gu);
-  bf16_t* sbt_d = reinterpret_cast<bf16_t*>(base + l.sbt_d);
-  void* z_gu = base + l.z_gu;
-  void* z_d = base + l.z_d;
-  void* y_gu = base + l.y_gu;
-  void* y_d = base + l.y_d;
+  auto at = [&](size_t o) { return reinterpret_cast<bf16_t*>(base + o); };
+  LoraPtrs p{};
+  p.sa_gu = at(l.sa_gu);
+  p.sa_d = at(l.sa_d);
+  p.sbt_gu = at(l.sbt_gu);
+  p.sbt_d = at(l.sbt_d);
+  p.z_gu = at(l.z_gu);
+  p.z_d = at(l.z_d);
+  p.y_gu = at(l.y_gu);
+  p.y_d = at(l.y_d);
+  if (unmerged) {
+    p.bx_g = at(l.bx_g);
+    p.bx_u = at(l.bx_u);
+    p.bx_d = at(l.bx_d);
+    p.ax_gu = at(l.ax_gu);
+    p.ax_d = at(l.ax_d);
+  }
+  const int64_t max_tiles = (2 * ceil_div(s.I, 128) + ceil_div(s.H, 128)) * static_cast<int64_t>(s.E) + 2 * outer_grid();
+  p.os.hdr = reinterpret_cast<int*>(base + l.plan);
+  p.os.desc = reinterpret_cast<OuterDesc*>(base + l.plan + 256);
+  p.os.units = reinterpret_cast<OuterUnit*>(base + l.plan + 256 + max_tiles * sizeof(OuterDesc));
+  p.os.part = reinterpret_cast<float*>(base + l.part);
+  return p;
+}
+}  // namespace
+
+#define MOE_TRY(x) \
+  if ((err = (x)) != hipSuccess) return err
+
+hipError_t launch_lora_prepare(const moe_shape& s, int r, float scale, const LoraArgs& g, void* ws, bool unmerged,
+                               hipStream_t st) {
+  const LoraPtrs p = lora_ptrs(s, r, ws, unmerged);
   const int E = s.E, H = s.H, I = s.I, rp = lora_padded_rank(r);
   const bf16_t* a_gate = static_cast<const bf16_t*>(g.a_gate);
   const bf16_t* a_up = static_cast<const bf16_t*>(g.a_up);
@@ -1103,20 +1156,87 @@ hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraA
   const bf16_t* b_up = static_cast<const bf16_t*>(g.b_up);
   const bf16_t* b_down = static_cast<const bf16_t*>(g.b_down);
   hipError_t err;
-#define MOE_TRY(x) \
-  if ((err = (x)) != hipSuccess) return err
   // Scaled, stacked adapters (bf16, rounded once): sA_gu = [sA_gate; sA_up],
   // sA_d, the transposed block diagonal of sB_gate and sB_up, sB_down^T.
   stack_a_kernel<<<dim3(E * 2 * rp, ceil_div(H / 8, kThreads)), kThreads, 0, st>>>(r, rp, H, scale, a_gate, a_up,
-                                                                                     sa_gu);
+                                                                                     p.sa_gu);
   MOE_TRY(hipGetLastError());
   stack_a_kernel<<<dim3(E * rp, ceil_div(I / 8, kThreads)), kThreads, 0, st>>>(r, rp, I, scale, a_down, nullptr,
-                                                                                 sa_d);
+                                                                                 p.sa_d);
   MOE_TRY(hipGetLastError());
-  blockdiag_t_kernel<<<dim3(2 * I / 64, E), kThreads, 0, st>>>(I, r, rp, scale, b_gate, b_up, sbt_gu);
+  blockdiag_t_kernel<<<dim3(2 * I / 64, E), kThreads, 0, st>>>(I, r, rp, scale, b_gate, b_up, p.sbt_gu);
   MOE_TRY(hipGetLastError());
-  blockdiag_t_kernel<<<dim3(H / 64, E), kThreads, 0, st>>>(H, r, rp, scale, b_down, nullptr, sbt_d);
+  blockdiag_t_kernel<<<dim3(H / 64, E), kThreads, 0, st>>>(H, r, rp, scale, b_down, nullptr, p.sbt_d);
   MOE_TRY(hipGetLastError());
+  if (unmerged) {
+    // The GEMMs' K extensions: the forward multiplies Z = X (sA)^T by B, the
+    // data gradients Y = dY (sB) by A, so B and A enter unscaled.
+    const int64_t ri = static_cast<int64_t>(E) * I, rh = static_cast<int64_t>(E) * H;
+    auto pad = [&](int64_t rows, int width, int off, const bf16_t* in, bf16_t* out) {
+      const int64_t n = rows * (width / 8);
+      pad_cols_kernel<<<static_cast<unsigned>(ceil_div(n, static_cast<int64_t>(kThreads))), kThreads, 0, st>>>(
+          rows, r, width, off, in, out);
+      return hipGetLastError();
+    };
+    MOE_TRY(pad(ri, 2 * rp, 0, b_gate, p.bx_g));
+    MOE_TRY(pad(ri, 2 * rp, rp, b_up, p.bx_u));
+    MOE_TRY(pad(rh, rp, 0, b_down, p.bx_d));
+    stack_a_kernel<<<dim3(E * 2 * rp, ceil_div(H / 8, kThreads)), kThreads, 0, st>>>(r, rp, H, 1.0f, a_gate, a_up,
+                                                                                       p.ax_gu);
+    MOE_TRY(hipGetLastError());
+    stack_a_kernel<<<dim3(E * rp, ceil_div(I / 8, kThreads)), kThreads, 0, st>>>(r, rp, I, 1.0f, a_down, nullptr,
+                                                                                   p.ax_d);
+    MOE_TRY(hipGetLastError());
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_lora_project(const moe_shape& s, int r, int which, const void* in, const int32_t* offsets,
+                               void* ws, hipStream_t st) {
+  const LoraPtrs p = lora_ptrs(s, r, ws, true);
+  const int H = s.H, I = s.I, rp = lora_padded_rank(r), M = s.T * s.k;
+  const bf16_t* x = static_cast<const bf16_t*>(in);
+  ProjJobs pj{};
+  switch (which) {
+    case 0: pj.job[0] = {x, p.sa_gu, p.z_gu, H, 2 * rp, nullptr, nullptr, M}; break;
+    case 1: pj.job[0] = {x, p.sbt_gu, p.y_gu, 2 * I, 2 * rp, nullptr, nullptr, M}; break;
+    case 2: pj.job[0] = {x, p.sa_d, p.z_d, I, rp, nullptr, nullptr, M}; break;
+    default: pj.job[0] = {x, p.sbt_d, p.y_d, H, rp, nullptr, nullptr, M}; break;
+  }
+  pj.n = 1;
+  return projections(s, pj.job[0].N < 64 ? 64 : pj.job[0].N, offsets, pj, st);  // the kernel's widths: 64, 128, 256
+}
+
+hipError_t launch_lora_outer(const moe_shape& s, int r, const LoraArgs& g, void* ws, hipStream_t st) {
+  const LoraPtrs p = lora_ptrs(s, r, ws, false);
+  const int E = s.E, H = s.H, I = s.I, rp = lora_padded_rank(r);
+  const int32_t* tok = g.row_token;
+  const int M = s.T * s.k, nsrc = tok != nullptr ? s.T : M;
+  hipError_t err;
+  // Outer products over each expert's rows, straight into the adapter
+  // gradients: dB_gate = dG^T Z_gate, dB_up = dU^T Z_up, dB_down = dO^T
+  // Z_down; then [dA_gate; dA_up] = [Y_gate | Y_up]^T X (one pass over
+  // x_perm) and dA_down = Y_down^T Act.
+  const bf16_t* dgu = static_cast<const bf16_t*>(g.dgu);
+  OuterJobs ob{};
+  ob.job[0] = {dgu, p.z_gu, g.db_gate, nullptr, 2 * I, 0, I, 2 * rp, 0, r, r, r, nullptr, M};
+  ob.job[1] = {dgu, p.z_gu, g.db_up, nullptr, 2 * I, I, I, 2 * rp, rp, r, r, r, nullptr, M};
+  ob.job[2] = {static_cast<const bf16_t*>(g.do_perm), p.z_d, g.db_down, nullptr, H, 0, H, rp, 0, r, r, r, tok, nsrc};
+  ob.n = 3;
+  MOE_TRY(outer_products<false>(E, (r + 31) / 32, g.offsets, ob, p.os, st));
+  OuterJobs oa{};
+  oa.job[0] = {static_cast<const bf16_t*>(g.x_perm), p.y_gu, g.da_gate, g.da_up, H, 0, H, 2 * rp, 0, 2 * rp, rp, r,
+               tok, nsrc};
+  oa.job[1] = {static_cast<const bf16_t*>(g.act), p.y_d, g.da_down, nullptr, I, 0, I, rp, 0, r, r, r, nullptr, M};
+  oa.n = 2;
+  return outer_products<true>(E, 2 * rp / 32, g.offsets, oa, p.os, st);
+}
+
+hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraArgs& g, void* ws, hipStream_t st) {
+  const LoraPtrs p = lora_ptrs(s, r, ws, false);
+  const int H = s.H, I = s.I, rp = lora_padded_rank(r);
+  hipError_t err;
+  MOE_TRY(launch_lora_prepare(s, r, scale, g, ws, false, st));
   // Row projections Z = X (sA)^T, Y = dY (sB): [Z_gate | Z_up], [dG sB_gate |
   // dU sB_up], Z_down, dO sB_down.
   // With row_token, x and dy are read through the sorted rows' tokens, and
@@ -1126,48 +1246,16 @@ hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraA
   const int32_t* tok = g.row_token;
   const float* rwt = tok != nullptr ? g.row_weight : nullptr;
   const int M = s.T * s.k, nsrc = tok != nullptr ? s.T : M;
-  {
-    ProjJobs pj{};
-    const bf16_t* xp = static_cast<const bf16_t*>(g.x_perm);
-    pj.job[0] = {xp, sa_gu, static_cast<bf16_t*>(z_gu), H, 2 * rp, tok, nullptr, nsrc};
-    pj.job[1] = {static_cast<const bf16_t*>(g.dgu), sbt_gu, static_cast<bf16_t*>(y_gu), 2 * I, 2 * rp, nullptr,
-                 nullptr, M};
-    pj.job[2] = {static_cast<const bf16_t*>(g.act), sa_d, static_cast<bf16_t*>(z_d), I, rp, nullptr, rwt, M};
-    pj.job[3] = {static_cast<const bf16_t*>(g.do_perm), sbt_d, static_cast<bf16_t*>(y_d), H, rp, tok, rwt, nsrc};
-    pj.n = 4;
-    MOE_TRY(projections(s, 2 * rp, g.offsets, pj, st));
-  }
-  // Outer products over each expert's rows, straight into the adapter
-  // gradients: dB_gate = dG^T Z_gate, dB_up = dU^T Z_up, dB_down = dO^T
-  // Z_down; then [dA_gate; dA_up] = [Y_gate | Y_up]^T X (one pass over
-  // x_perm) and dA_down = Y_down^T Act.
-  {
-    const bf16_t* dgu = static_cast<const bf16_t*>(g.dgu);
-    OuterJobs ob{};
-    ob.job[0] = {dgu, static_cast<const bf16_t*>(z_gu), g.db_gate, nullptr, 2 * I, 0, I, 2 * rp, 0, r, r, r,
-                 nullptr, M};
-    ob.job[1] = {dgu, static_cast<const bf16_t*>(z_gu), g.db_up, nullptr, 2 * I, I, I, 2 * rp, rp, r, r, r,
-                 nullptr, M};
-    ob.job[2] = {static_cast<const bf16_t*>(g.do_perm), static_cast<const bf16_t*>(z_d), g.db_down, nullptr, H, 0,
-                 H, rp, 0, r, r, r, tok, nsrc};
-    ob.n = 3;
-    const int64_t max_tiles = (2 * ceil_div(I, 128) + ceil_div(H, 128)) * static_cast<int64_t>(E) + 2 * outer_grid();
-    OuterSpace os{};
-    os.hdr = reinterpret_cast<int*>(base + l.plan);
-    os.desc = reinterpret_cast<OuterDesc*>(base + l.plan + 256);
-    os.units = reinterpret_cast<OuterUnit*>(base + l.plan + 256 + max_tiles * sizeof(OuterDesc));
-    os.part = reinterpret_cast<float*>(base + l.part);
-    MOE_TRY(outer_products<false>(E, (r + 31) / 32, g.offsets, ob, os, st));
-    OuterJobs oa{};
-    oa.job[0] = {static_cast<const bf16_t*>(g.x_perm), static_cast<const bf16_t*>(y_gu), g.da_gate, g.da_up, H, 0,
-                 H, 2 * rp, 0, 2 * rp, rp, r, tok, nsrc};
-    oa.job[1] = {static_cast<const bf16_t*>(g.act), static_cast<const bf16_t*>(y_d), g.da_down, nullptr, I, 0, I, rp,
-                 0, r, r, r, nullptr, M};
-    oa.n = 2;
-    MOE_TRY(outer_products<true>(E, 2 * rp / 32, g.offsets, oa, os, st));
-  }
-#undef MOE_TRY
-  return hipSuccess;
+  ProjJobs pj{};
+  const bf16_t* xp = static_cast<const bf16_t*>(g.x_perm);
+  pj.job[0] = {xp, p.sa_gu, p.z_gu, H, 2 * rp, tok, nullptr, nsrc};
+  pj.job[1] = {static_cast<const bf16_t*>(g.dgu), p.sbt_gu, p.y_gu, 2 * I, 2 * rp, nullptr, nullptr, M};
+  pj.job[2] = {static_cast<const bf16_t*>(g.act), p.sa_d, p.z_d, I, rp, nullptr, rwt, M};
+  pj.job[3] = {static_cast<const bf16_t*>(g.do_perm), p.sbt_d, p.y_d, H, rp, tok, rwt, nsrc};
+  pj.n = 4;
+  MOE_TRY(projections(s, 2 * rp, g.offsets, pj, st));
+  return launch_lora_outer(s, r, g, ws, st);
 }
+#undef MOE_TRY
 
 }  // namespace moe

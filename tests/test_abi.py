@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(B):
     names = declared_functions()
-    assert len(names) == 43, names
+    assert len(names) == 50, names
     for n in names:
         assert hasattr(B.lib, n), n
 
@@ -176,6 +176,26 @@ def test_lora_validation(B):
     assert MM(8, 64, 48, 16, 1.0, F, F, F, F, F, None) == 2   # K % 32
     assert MM(8, 64, 128, 12, 1.0, F, F, F, F, F, None) == 2  # r % 8
     assert MM(8, 64, 128, 16, 1.0, F, None, F, F, F, None) == 1
+    # the adapter step without merged weights: its own workspace (the GEMMs'
+    # K extensions on top), every check before any HIP call
+    un = B.moe_lora_unmerged_workspace_bytes(s, 16)
+    assert un > need
+    assert B.moe_lora_unmerged_workspace_bytes(s, 12) == 0
+    assert B.moe_lora_unmerged_workspace_bytes(B.shape(64, 128, 8, 2, 64, "f32"), 16) == 0
+    assert B.moe_lora_unmerged_workspace_bytes(B.shape(1 << 20, 64, 8, 8, 64, "bf16"), 128) == 0  # T k 4 rp >= 2^31
+    PR = B.lib.moe_lora_prepare
+    assert PR(s, 16, 1.0, *([F] * 7), un - 1, None) == 3
+    assert PR(s, 16, 1.0, *([F] * 6), None, un, None) == 1
+    assert PR(s, 20, 1.0, *([F] * 7), un, None) == 2
+    LG = B.lib.moe_lora_gemm_gate_up
+    assert LG(s, 16, *([F] * 8), un - 1, None) == 3
+    assert LG(s, 16, F, None, *([F] * 6), un, None) == 1
+    assert B.lib.moe_lora_gemm_down(s, 16, *([F] * 3), None, F, un, None) == 1
+    assert B.lib.moe_lora_gemm_down_dgrad(s, 136, *([F] * 7), un, None) == 2
+    assert B.lib.moe_lora_gemm_gate_up_dgrad(s, 16, *([F] * 6), un - 1, None) == 3
+    GU = B.lib.moe_lora_grads_unmerged
+    assert GU(s, 16, *([F] * 12), un - 1, None) == 3
+    assert GU(s, 16, *([F] * 5), None, *([F] * 6), un, None) == 1
     QW = B.lib.moe_quantize_mxfp4_weights
     assert QW(8, 64, 48, F, F, F, None) == 1          # K % 32
     assert QW(8, 64, 64, F, None, F, None) == 1

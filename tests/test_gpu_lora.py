@@ -12,7 +12,9 @@ the C ABI.
   and the ranks 72 and 96; the full 30B-A3B training shape is checked on
   every element (per token, per expert). Each also without x_perm and
   do_perm (LoRAStage(gathered=True): moe_gemm_down_dgrad_dy and
-  moe_lora_grads_gathered).
+  moe_lora_grads_gathered), and without merged weights
+  (LoRAStage(unmerged=True): every GEMM over its reduction extended by the
+  rank, moe_lora_grads_unmerged), against the same oracle.
 """
 import numpy as np
 import pytest
@@ -60,12 +62,17 @@ def test_merge(E, N, K, r, in_place):
     assert frac >= 0.999
 
 
-def lora_run(d: U.DevInputs, r: int, s: float, adapters, gathered: bool = False):
+MODES = ["x_perm", "gathered", "unmerged"]
+
+
+def lora_run(d: U.DevInputs, r: int, s: float, adapters, mode: str = "x_perm"):
+    """mode: "x_perm" (merged weights), "gathered" (merged, no x_perm and
+    do_perm) or "unmerged" (no merged weights)."""
     from mixture_experts_expert_amd import binding as B
     c = d.cfg
     T = d.t["x"].shape[0]
     ad = {n: U.to_dev(adapters[n]) for n in NAMES}
-    st = B.LoRAStage(T, c.H, c.E, c.k, c.I, r, s, gathered=gathered)
+    st = B.LoRAStage(T, c.H, c.E, c.k, c.I, r, s, gathered=mode == "gathered", unmerged=mode == "unmerged")
     st.forward(d.t["x"], d.t["w_router"], d.t["w_gate"], d.t["w_up"], d.t["w_down"], ad, d.bias)
     st.backward(d.t["dy"])
     torch.cuda.synchronize()
@@ -112,18 +119,18 @@ SMALL_LORA = [
 ]
 
 
-@pytest.mark.parametrize("gathered", [False, True], ids=["x_perm", "gathered"])
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("cfg,r", SMALL_LORA, ids=[f"{c.name}-r{r}" for c, r in SMALL_LORA])
-def test_lora_stage_small(cfg, r, gathered):
+def test_lora_stage_small(cfg, r, mode):
     """gathered: neither x_perm nor do_perm (x and dy read through the sorted
-    rows' tokens in the GEMMs and the adapter gradients)."""
-    U.say(f"[lora stage] {cfg} r={r} gathered={gathered}")
-    U.begin(f"lora_r{r}{'_gathered' if gathered else ''}.{cfg.name}", f"{cfg} seed 8, adapters rank {r}")
+    rows' tokens in the GEMMs and the adapter gradients); unmerged: no W'."""
+    U.say(f"[lora stage] {cfg} r={r} {mode}")
+    U.begin(f"lora_r{r}{'' if mode == 'x_perm' else '_' + mode}.{cfg.name}", f"{cfg} seed 8, adapters rank {r}")
     s = 2.0 if r == 64 else 0.75
     inp = synth.make_inputs(cfg, seed=8, with_dy=True)
     adapters = synth.make_adapters(cfg, r, seed=8)
     d = U.DevInputs(inp)
-    st = lora_run(d, r, s, adapters, gathered)
+    st = lora_run(d, r, s, adapters, mode)
     ref_r = U.oracle_route(inp)
     U.check_routing(st, ref_r)
     ref = oracle_lora(inp, adapters, s, ref_r["topk_idx"], ref_r["topk_w"])
@@ -136,18 +143,18 @@ def test_lora_stage_small(cfg, r, gathered):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("gathered", [False, True], ids=["x_perm", "gathered"])
-def test_lora_stage_qwen3_30b_a3b_full(gathered):
+@pytest.mark.parametrize("mode", MODES)
+def test_lora_stage_qwen3_30b_a3b_full(mode):
     """T=8192, H=2048, E=128, k=8, I=768, r=64, s=2: every element of y, dx,
     d_topk_w, d_logits and of all six adapter gradients."""
     cfg = synth.CONFIGS["qwen3_30b_a3b_train"]
     r, s = 64, 2.0
-    U.say(f"[lora stage] {cfg} r={r} gathered={gathered}")
-    U.begin(f"lora_r64{'_gathered' if gathered else ''}." + cfg.name, f"{cfg} seed 0, adapters rank {r}, scale {s}")
+    U.say(f"[lora stage] {cfg} r={r} {mode}")
+    U.begin(f"lora_r64{'' if mode == 'x_perm' else '_' + mode}." + cfg.name, f"{cfg} seed 0, adapters rank {r}, scale {s}")
     inp = synth.make_inputs(cfg, seed=0)
     adapters = synth.make_adapters(cfg, r, seed=0)
     d = U.DevInputs(inp)
-    st = lora_run(d, r, s, adapters, gathered)
+    st = lora_run(d, r, s, adapters, mode)
     ref_r = U.oracle_route(inp)
     U.check_routing(st, ref_r)
     U.say("  adapter oracle on all tokens")
