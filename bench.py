@@ -55,9 +55,10 @@ GEMMs on their own (whose TFLOP/s join `gemm_tflops`); `inference_forward_ms`
 the forward alone, unfused and fused (no x_perm, routing weights in the down
 GEMM's epilogue); `lora_ms` the training step with rank-64 adapters on frozen
 experts (merges, forward on the merged weights, data and adapter gradients)
-and its two adapter calls, over bf16, E4M3 and MXFP4 frozen weights, and the
+and its two adapter calls, over bf16, E4M3 and MXFP4 frozen weights, the
 step without x_perm and do_perm (`step_gathered`, with
-`moe_lora_grads_gathered`). `--timed-only` skips these and the CPU baseline, so that
+`moe_lora_grads_gathered`) and the step without merged weights
+(`step_unmerged`, its calls in `unmerged_call_ms`). `--timed-only` skips these and the CPU baseline, so that
 under a profiler the last K launches of every kernel are the timed steps.
 """
 from __future__ import annotations
@@ -258,7 +259,9 @@ def lora_timing(cfg, seed: int, tensors, bias, stream, r: int = 64, scale: float
     """The training step with rank-r adapters on the frozen experts at the
     same shape: the three merges W' = W + s B A, the forward on W', the data
     gradients and the adapter gradients (no frozen-weight gradient); then
-    the merges and the adapter-gradient call on their own."""
+    the merges and the adapter-gradient call on their own; the same over 8-
+    and 4-bit frozen weights, without x_perm and do_perm, and without merged
+    weights (step_unmerged, with its calls on their own)."""
     import numpy as np
     import torch
 
@@ -324,8 +327,34 @@ def lora_timing(cfg, seed: int, tensors, bias, stream, r: int = 64, scale: float
     out["moe_lora_grads_gathered"] = round(time_calls(lambda: B.moe_lora_grads_gathered(
         gs.s, r, scale, x, gb["row_token"], gb["row_weight"], gb["a"], gb["dgu"], dy, gb["offsets"],
         *(ad[n] for n in B.LORA_NAMES), *(gb["d" + n] for n in B.LORA_NAMES), gs.lora_ws), stream, reps=5), 4)
+    del gs, gb
+    torch.cuda.empty_cache()
+    # The step without merged weights: every GEMM over its reduction extended
+    # by the rank; its calls on their own.
+    us = B.LoRAStage(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, r, scale, unmerged=True)
+    ub, uw = us.buf, us.lora_ws
+
+    def lora_step_unmerged():
+        us.forward(x, wr, wg, wu, wd, ad, bias)
+        us.backward(dy)
+
+    out["step_unmerged"] = round(time_calls(lora_step_unmerged, stream), 4)
+    un_calls = {
+        "moe_lora_prepare": lambda: B.moe_lora_prepare(us.s, r, scale, *(ad[n] for n in B.LORA_NAMES), uw),
+        "moe_lora_gemm_gate_up": lambda: B.moe_lora_gemm_gate_up(us.s, r, ub["x_perm"], ub["offsets"], wg, wu, ub["g"],
+                                                                 ub["u"], ub["a"], uw),
+        "moe_lora_gemm_down": lambda: B.moe_lora_gemm_down(us.s, r, ub["a"], ub["offsets"], wd, ub["o_perm"], uw),
+        "moe_lora_gemm_down_dgrad": lambda: B.moe_lora_gemm_down_dgrad(us.s, r, ub["do_perm"], ub["offsets"], wd,
+                                                                       ub["g"], ub["u"], ub["dgu"], uw),
+        "moe_lora_gemm_gate_up_dgrad": lambda: B.moe_lora_gemm_gate_up_dgrad(us.s, r, ub["dgu"], ub["offsets"], wg, wu,
+                                                                             ub["dx_perm"], uw),
+        "moe_lora_grads_unmerged": lambda: B.moe_lora_grads_unmerged(
+            us.s, r, ub["x_perm"], ub["a"], ub["dgu"], ub["do_perm"], ub["offsets"],
+            *(ub["d" + n] for n in B.LORA_NAMES), uw),
+    }
+    out["unmerged_call_ms"] = {n: round(time_calls(f, stream, reps=5), 4) for n, f in un_calls.items()}
     log(f"adapter step: {out}")
-    del gs, gb, ad
+    del us, ub, uw, ad
     torch.cuda.empty_cache()
     return out
 
