@@ -1431,13 +1431,24 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   if (L < hi) {
     set_tile_and_offsets(L);
     if constexpr (GATHER_K) {
+      // The tokens of step 4 go out between steps 1 and 2, as in the steady
+      // state (one token load between two steps' operand loads): the first
+      // k-step's wait for step 1 counts 14 newer loads (GATHER_K: kWaitVm14),
+      // and with all five token loads ahead of step 0 only 13 would follow
+      // step 1, so step 1's last block could still be in flight when its
+      // fragments are read.
+      // The scheduling barriers keep the compiler from moving the token
+      // loads, whose place the count relies on.
       const uint32_t tk0 = load_tok(0), tk1 = load_tok(1), tk2 = load_tok(2);
       tkA = load_tok(3);
-      tkB = load_tok(4);
+      __builtin_amdgcn_sched_barrier(0);
       gather_off(tk0, 0);
       issue(0, lds0);
       gather_off(tk1, 1);
       issue(1, lds1);
+      __builtin_amdgcn_sched_barrier(0);
+      tkB = load_tok(4);
+      __builtin_amdgcn_sched_barrier(0);
       gather_off(tk2, 2);
       issue(2, lds2);
     } else {

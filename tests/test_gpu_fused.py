@@ -188,6 +188,27 @@ def test_gather_fused_training_qwen3_30b_a3b_full():
         U.check_output(n, U.to_np(st.buf[n]), ref, U.BF16_TOL)
 
 
+
+@pytest.mark.timeout(600)
+def test_gather_fused_weight_grads_repeat_bitwise():
+    """T=8192, H=2048, E=128, k=8, I=768: the gathered gate/up backward (x
+    read through the tokens, token loads among the operand loads) gives the
+    x_perm path's weight gradients bit for bit in each of six runs. A wait
+    one load short in the first tile of a workgroup once let a run read a
+    stage before its last block landed (a whole 256 x 256 tile off)."""
+    cfg = synth.CONFIGS["qwen3_30b_a3b_train"]
+    U.say(f"[gather-fused weight gradients, repeated] {cfg}")
+    inp = synth.make_inputs(cfg, seed=0)
+    d = U.DevInputs(inp)
+    plain = U.run_stage(d, True)
+    ref = {n: plain.buf[n].clone() for n in ["dw_gate", "dw_up", "dw_down"]}
+    del plain
+    for rep in range(6):
+        st = U.run_stage(d, True, stage=gather_fused_stage(d))
+        for n, v in ref.items():
+            assert same_tensor(st.buf[n], v), (rep, n)
+        del st
+
 # ---- training without do_perm (dy read through the sorted rows' tokens) ----
 
 DY_SMALL = [c for c in SMALL if c.backward and c.dtype == "bf16"] + [SPLIT_K]
