@@ -86,13 +86,15 @@ __device__ __forceinline__ float bf16f(bf16_t v) { return __uint_as_float(static
 // bf16(deq(W) + s B A) with the same single rounding as the bf16 form.
 enum WFormat : int { kBf16 = 0, kE4M3 = 1, kMxfp4 = 2 };
 
-// E2M1 code (4 bits) -> float: exponent field 0 is m / 2, otherwise
-// (1 + m / 2) 2^(e - 1); the sign bit kept (a negative zero too).
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  const int e = static_cast<int>((c >> 1) & 3u);
-  const float m = static_cast<float>(c & 1u);
-  const float mag = e == 0 ? 0.5f * m : ldexpf(1.0f + 0.5f * m, e - 1);
-  return (c & 8u) ? -mag : mag;
+// E8M0 scale byte c -> 2^(c - 127) as a float for gfx950's scaled
+// conversions (v_cvt_scalef32_pk_f32_fp4 / _fp8: two elements per
+// instruction, multiplied by the scale exactly); c = 0 (2^-127, below the
+// normal range) gives 2^-126 and the caller halves the results. An in-bounds
+// GPU check against a CPU decode of every code at scales 2^-126 .. 2^127
+// found them exact, E4M3's NaN codes included.
+__device__ __forceinline__ float e8m0_scale(int c) {
+  const int b = c & 0xff;
+  return __uint_as_float(static_cast<uint32_t>(b == 0 ? 1 : b) << 23);
 }
 
 template <int NS, int WF>
@@ -217,21 +219,35 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int N, int K, int r, fl
       const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       float wf[8];
       if constexpr (WF == kMxfp4) {
-        const int X = (sc_t[q] & 0xff) - 127;  // the block's E8M0 scale
+        // The block's E8M0 scale applied by the conversion itself (exact:
+        // a power of two); the element at byte j's low nibble comes first.
+        const float sc = e8m0_scale(sc_t[q]);
         const uint32_t c8 = wc_t[q];
+        const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c8, sc, 0);
+        const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c8, sc, 1);
+        const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c8, sc, 2);
+        const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c8, sc, 3);
+        wf[0] = v0.x, wf[1] = v0.y, wf[2] = v1.x, wf[3] = v1.y;
+        wf[4] = v2.x, wf[5] = v2.y, wf[6] = v3.x, wf[7] = v3.y;
+        if ((sc_t[q] & 0xff) == 0) {  // 2^-127 is below the normal range: 2^-126, then halved (exact)
 #pragma unroll
-        for (int p = 0; p < 8; ++p) wf[p] = ldexpf(e2m1_value((c8 >> (4 * p)) & 15u), X);
+          for (int p = 0; p < 8; ++p) wf[p] *= 0.5f;
+        }
       } else if constexpr (WF == kE4M3) {
-        const int X = (sc_t[q] & 0xff) - 127;  // the row's E8M0 scale
+        const float sc = e8m0_scale(sc_t[q]);  // the row's E8M0 scale
         const uint32_t c2[2] = {wc_t[q].x, wc_t[q].y};
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c2[p]), false);
-          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c2[p]), true);
-          wf[4 * p] = ldexpf(lo.x, X);
-          wf[4 * p + 1] = ldexpf(lo.y, X);
-          wf[4 * p + 2] = ldexpf(hi.x, X);
-          wf[4 * p + 3] = ldexpf(hi.y, X);
+          const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c2[p], sc, false);
+          const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c2[p], sc, true);
+          wf[4 * p] = lo.x;
+          wf[4 * p + 1] = lo.y;
+          wf[4 * p + 2] = hi.x;
+          wf[4 * p + 3] = hi.y;
+        }
+        if ((sc_t[q] & 0xff) == 0) {
+#pragma unroll
+          for (int p = 0; p < 8; ++p) wf[p] *= 0.5f;
         }
       } else {
         const uint32_t win[4] = {wc_t[q].x, wc_t[q].y, wc_t[q].z, wc_t[q].w};

@@ -382,6 +382,45 @@ def test_merge_mxfp4_decodes_every_code():
     assert np.array_equal(got, want)
 
 
+def bf16_rne(x: np.ndarray) -> np.ndarray:
+    """float64 values exact in float32 -> nearest bf16 (ties to even), as float64."""
+    u = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def test_merge_quantized_base_smallest_scale():
+    """B = 0 with every scale byte 0 (2^-127, below the float32 normal range):
+    W' = bf16(code value * 2^-127) for every E4M3 and E2M1 code, the
+    subnormal results included (the decode scales by 2^-126, then halves)."""
+    from mixture_experts_expert_amd import binding as B
+    from oracle import fp8 as F8
+    from oracle import mxfp4 as MX
+    U.say("[lora merge] scale 2^-127")
+    E, N, r = 2, 16, 8
+    codes8 = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    K8 = codes8.size + 2
+    wq8 = np.stack([np.stack([np.roll(np.r_[codes8, codes8[:2]], n) for n in range(N)]) for _ in range(E)])
+    e8 = np.zeros((E, N), np.uint8)
+    out = torch.empty(E, N, K8, dtype=torch.bfloat16, device="cuda")
+    B.moe_lora_merge_fp8(E, N, K8, r, 1.0, torch.from_numpy(wq8).cuda(), torch.from_numpy(e8).cuda(),
+                         U.to_dev(np.zeros((E, r, K8), np.uint16)), U.to_dev(np.zeros((E, N, r), np.uint16)), out)
+    torch.cuda.synchronize()
+    want = F8.dequantize_rows(wq8.reshape(E * N, K8), e8.reshape(E * N)).reshape(E, N, K8)
+    assert np.array_equal(U.to_np(out).astype(np.float64), bf16_rne(want))
+    K4 = 256
+    codes4 = np.stack([np.stack([np.roll(np.tile(np.arange(16), K4 // 16), 3 * n + e) for n in range(N)])
+                       for e in range(E)]).astype(np.uint8)
+    wq4 = (codes4[..., 0::2] | (codes4[..., 1::2] << 4)).astype(np.uint8)
+    e84 = np.zeros((E, N, K4 // 32), np.uint8)
+    out4 = torch.empty(E, N, K4, dtype=torch.bfloat16, device="cuda")
+    B.moe_lora_merge_mxfp4(E, N, K4, r, 1.0, torch.from_numpy(wq4).cuda(), torch.from_numpy(e84).cuda(),
+                           U.to_dev(np.zeros((E, r, K4), np.uint16)), U.to_dev(np.zeros((E, N, r), np.uint16)), out4)
+    torch.cuda.synchronize()
+    want4 = MX.dequantize_blocks(wq4.reshape(E * N, K4 // 2), e84.reshape(E * N, K4 // 32)).reshape(E, N, K4)
+    assert np.array_equal(U.to_np(out4).astype(np.float64), bf16_rne(want4))
+
+
 @pytest.mark.parametrize("E,N,K,r", [(3, 200, 256, 8), (2, 129, 160, 72), (4, 257, 544, 40), (2, 70, 2048, 128)])
 def test_merge_mxfp4(E, N, K, r):
     """W' = bf16(deq(wq) + s B A) against the float64 oracle on its own
