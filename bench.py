@@ -341,13 +341,15 @@ def lora_timing(cfg, seed: int, tensors, bias, stream, r: int = 64, scale: float
     out["step_unmerged"] = round(time_calls(lora_step_unmerged, stream), 4)
     un_calls = {
         "moe_lora_prepare": lambda: B.moe_lora_prepare(us.s, r, scale, *(ad[n] for n in B.LORA_NAMES), uw),
-        "moe_lora_gemm_gate_up": lambda: B.moe_lora_gemm_gate_up(us.s, r, ub["x_perm"], ub["offsets"], wg, wu, ub["g"],
-                                                                 ub["u"], ub["a"], uw),
-        "moe_lora_gemm_down": lambda: B.moe_lora_gemm_down(us.s, r, ub["a"], ub["offsets"], wd, ub["o_perm"], uw),
+        "moe_lora_gemm_gate_up": lambda: B.moe_lora_gemm_gate_up(us.s, r, ub["x_perm"], ub["offsets"], wg, wu,
+                                                                 ad["b_gate"], ad["b_up"], ub["g"], ub["u"], ub["a"], uw),
+        "moe_lora_gemm_down": lambda: B.moe_lora_gemm_down(us.s, r, ub["a"], ub["offsets"], wd, ad["b_down"],
+                                                           ub["o_perm"], uw),
         "moe_lora_gemm_down_dgrad": lambda: B.moe_lora_gemm_down_dgrad(us.s, r, ub["do_perm"], ub["offsets"], wd,
-                                                                       ub["g"], ub["u"], ub["dgu"], uw),
+                                                                       ad["a_down"], ub["g"], ub["u"], ub["dgu"], uw),
         "moe_lora_gemm_gate_up_dgrad": lambda: B.moe_lora_gemm_gate_up_dgrad(us.s, r, ub["dgu"], ub["offsets"], wg, wu,
-                                                                             ub["dx_perm"], uw),
+                                                                             ad["a_gate"], ad["a_up"], ub["dx_perm"],
+                                                                             uw),
         "moe_lora_grads_unmerged": lambda: B.moe_lora_grads_unmerged(
             us.s, r, ub["x_perm"], ub["a"], ub["dgu"], ub["do_perm"], ub["offsets"],
             *(ub["d" + n] for n in B.LORA_NAMES), uw),

@@ -502,40 +502,45 @@ moe_status moe_lora_merge_mxfp4(int32_t E, int32_t N, int32_t K, int32_t r, floa
  * rp = r rounded up to 32, 64 or 128 (MOE_EUNSUPPORTED otherwise). */
 
 /* Bytes of workspace for the unmerged adapter step (0 if shape or rank are
- * rejected): moe_lora_workspace_bytes' regions plus the GEMMs' extensions,
- * [B_gate | 0] and [0 | B_up] [E,I,2rp], B_down [E,H,rp], [A_gate; A_up]
- * [E,2rp,H] and A_down [E,rp,I] (bf16, padded with zeros). */
+ * rejected): the regions of moe_lora_workspace_bytes (the scaled stacks,
+ * the projections, the outer products' plan and partial tiles). The GEMMs'
+ * extensions read the adapters themselves, padded with zeros to rp inside
+ * the kernel. */
 size_t moe_lora_unmerged_workspace_bytes(moe_shape s, int32_t r);
 
 /* The adapters of this step (a_P [E,r,K], b_P [E,N,r] bf16, scale s) into
- * ws: the scaled stacks of the row projections and the GEMMs' extensions.
- * Run once per step, before the other calls. */
+ * ws: the scaled stacks of the row projections. Run once per step, before
+ * the other calls; the GEMM calls below also take the adapters they extend
+ * the reduction with (the same tensors, unchanged in between). */
 moe_status moe_lora_prepare(moe_shape s, int32_t r, float scale, const void* a_gate, const void* b_gate,
                             const void* a_up, const void* b_up, const void* a_down, const void* b_down, void* ws,
                             size_t ws_bytes, hipStream_t stream);
 
 /* moe_gemm_gate_up with the adapters: Z = x_perm [sA_gate; sA_up]^T [T*k,2rp]
- * into ws, then G, U, A over the extended reduction. */
+ * into ws, then G, U, A over the extended reduction, whose B side is
+ * b_gate [E,I,r] for the gate columns and b_up for the up columns. */
 moe_status moe_lora_gemm_gate_up(moe_shape s, int32_t r, const void* x_perm, const int32_t* offsets,
-                                 const void* w_gate, const void* w_up, void* g, void* u, void* a, void* ws,
-                                 size_t ws_bytes, hipStream_t stream);
+                                 const void* w_gate, const void* w_up, const void* b_gate, const void* b_up, void* g,
+                                 void* u, void* a, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* moe_gemm_down with the adapters: Z_down = a (sA_down)^T into ws, then
- * o_perm over the extended reduction. */
+ * o_perm over the extended reduction (B side b_down [E,H,r]). */
 moe_status moe_lora_gemm_down(moe_shape s, int32_t r, const void* a, const int32_t* offsets, const void* w_down,
-                              void* o_perm, void* ws, size_t ws_bytes, hipStream_t stream);
+                              const void* b_down, void* o_perm, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* moe_gemm_down_dgrad with the adapters: Y_down = do_perm sB_down into ws,
- * then dA over the extended reduction and the SwiGLU backward into dgu. */
+ * then dA over the extended reduction (its k-rows: a_down [E,r,I]) and the
+ * SwiGLU backward into dgu. */
 moe_status moe_lora_gemm_down_dgrad(moe_shape s, int32_t r, const void* do_perm, const int32_t* offsets,
-                                    const void* w_down, const void* g, const void* u, void* dgu, void* ws,
-                                    size_t ws_bytes, hipStream_t stream);
+                                    const void* w_down, const void* a_down, const void* g, const void* u, void* dgu,
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* moe_gemm_gate_up_dgrad with the adapters: Y_gu = [dG sB_gate | dU sB_up]
- * into ws, then dx_perm over the extended reduction. */
+ * into ws, then dx_perm over the extended reduction (its k-rows: a_gate,
+ * then a_up, [E,r,H]). */
 moe_status moe_lora_gemm_gate_up_dgrad(moe_shape s, int32_t r, const void* dgu, const int32_t* offsets,
-                                       const void* w_gate, const void* w_up, void* dx_perm, void* ws,
-                                       size_t ws_bytes, hipStream_t stream);
+                                       const void* w_gate, const void* w_up, const void* a_gate, const void* a_up,
+                                       void* dx_perm, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* The six adapter gradients (as moe_lora_grads) from the projections the
  * four calls above left in ws: the outer products only. */

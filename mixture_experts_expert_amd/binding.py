@@ -92,10 +92,10 @@ _SIGS = {
     "moe_gemm_down_dgrad_dy": ([moe_shape] + [_P] * 9, ctypes.c_int),
     "moe_lora_unmerged_workspace_bytes": ([moe_shape, ctypes.c_int32], ctypes.c_size_t),
     "moe_lora_prepare": ([moe_shape, ctypes.c_int32, ctypes.c_float] + [_P] * 7 + [ctypes.c_size_t, _P], ctypes.c_int),
-    "moe_lora_gemm_gate_up": ([moe_shape, ctypes.c_int32] + [_P] * 8 + [ctypes.c_size_t, _P], ctypes.c_int),
-    "moe_lora_gemm_down": ([moe_shape, ctypes.c_int32] + [_P] * 5 + [ctypes.c_size_t, _P], ctypes.c_int),
-    "moe_lora_gemm_down_dgrad": ([moe_shape, ctypes.c_int32] + [_P] * 7 + [ctypes.c_size_t, _P], ctypes.c_int),
-    "moe_lora_gemm_gate_up_dgrad": ([moe_shape, ctypes.c_int32] + [_P] * 6 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_lora_gemm_gate_up": ([moe_shape, ctypes.c_int32] + [_P] * 10 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_lora_gemm_down": ([moe_shape, ctypes.c_int32] + [_P] * 6 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_lora_gemm_down_dgrad": ([moe_shape, ctypes.c_int32] + [_P] * 8 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_lora_gemm_gate_up_dgrad": ([moe_shape, ctypes.c_int32] + [_P] * 8 + [ctypes.c_size_t, _P], ctypes.c_int),
     "moe_lora_grads_unmerged": ([moe_shape, ctypes.c_int32] + [_P] * 12 + [ctypes.c_size_t, _P], ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
@@ -481,25 +481,29 @@ def moe_lora_prepare(s, r, scale, a_gate, b_gate, a_up, b_up, a_down, b_down, ws
         _nbytes(ws, ws_bytes), _stream(stream)))
 
 
-def moe_lora_gemm_gate_up(s, r, x_perm, offsets, w_gate, w_up, g, u, a, ws, ws_bytes=None, stream=None):
+def moe_lora_gemm_gate_up(s, r, x_perm, offsets, w_gate, w_up, b_gate, b_up, g, u, a, ws, ws_bytes=None,
+                          stream=None):
     _check("moe_lora_gemm_gate_up", lib.moe_lora_gemm_gate_up(
-        s, r, *[_ptr(t) for t in (x_perm, offsets, w_gate, w_up, g, u, a, ws)], _nbytes(ws, ws_bytes),
+        s, r, *[_ptr(t) for t in (x_perm, offsets, w_gate, w_up, b_gate, b_up, g, u, a, ws)],
+        _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def moe_lora_gemm_down(s, r, a, offsets, w_down, b_down, o_perm, ws, ws_bytes=None, stream=None):
+    _check("moe_lora_gemm_down", lib.moe_lora_gemm_down(
+        s, r, *[_ptr(t) for t in (a, offsets, w_down, b_down, o_perm, ws)], _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def moe_lora_gemm_down_dgrad(s, r, do_perm, offsets, w_down, a_down, g, u, dgu, ws, ws_bytes=None, stream=None):
+    _check("moe_lora_gemm_down_dgrad", lib.moe_lora_gemm_down_dgrad(
+        s, r, *[_ptr(t) for t in (do_perm, offsets, w_down, a_down, g, u, dgu, ws)], _nbytes(ws, ws_bytes),
         _stream(stream)))
 
 
-def moe_lora_gemm_down(s, r, a, offsets, w_down, o_perm, ws, ws_bytes=None, stream=None):
-    _check("moe_lora_gemm_down", lib.moe_lora_gemm_down(
-        s, r, *[_ptr(t) for t in (a, offsets, w_down, o_perm, ws)], _nbytes(ws, ws_bytes), _stream(stream)))
-
-
-def moe_lora_gemm_down_dgrad(s, r, do_perm, offsets, w_down, g, u, dgu, ws, ws_bytes=None, stream=None):
-    _check("moe_lora_gemm_down_dgrad", lib.moe_lora_gemm_down_dgrad(
-        s, r, *[_ptr(t) for t in (do_perm, offsets, w_down, g, u, dgu, ws)], _nbytes(ws, ws_bytes), _stream(stream)))
-
-
-def moe_lora_gemm_gate_up_dgrad(s, r, dgu, offsets, w_gate, w_up, dx_perm, ws, ws_bytes=None, stream=None):
+def moe_lora_gemm_gate_up_dgrad(s, r, dgu, offsets, w_gate, w_up, a_gate, a_up, dx_perm, ws, ws_bytes=None,
+                                stream=None):
     _check("moe_lora_gemm_gate_up_dgrad", lib.moe_lora_gemm_gate_up_dgrad(
-        s, r, *[_ptr(t) for t in (dgu, offsets, w_gate, w_up, dx_perm, ws)], _nbytes(ws, ws_bytes), _stream(stream)))
+        s, r, *[_ptr(t) for t in (dgu, offsets, w_gate, w_up, a_gate, a_up, dx_perm, ws)], _nbytes(ws, ws_bytes),
+        _stream(stream)))
 
 
 def moe_lora_grads_unmerged(s, r, x_perm, act, dgu, do_perm, offsets, da_gate, db_gate, da_up, db_up, da_down,
@@ -813,8 +817,9 @@ class LoRAStage(MoEStage):
         moe_route(s, x, w_router, logit_bias, b["logits"], b["topk_idx"], b["topk_w"], stream)
         moe_permute(s, b["topk_idx"], x, b["counts"], b["offsets"], b["sorted_to_flat"], b["flat_to_sorted"],
                     b["x_perm"], self.ws, stream=stream)
-        moe_lora_gemm_gate_up(s, r, b["x_perm"], b["offsets"], w_gate, w_up, b["g"], b["u"], b["a"], lw, stream=stream)
-        moe_lora_gemm_down(s, r, b["a"], b["offsets"], w_down, b["o_perm"], lw, stream=stream)
+        moe_lora_gemm_gate_up(s, r, b["x_perm"], b["offsets"], w_gate, w_up, adapters["b_gate"], adapters["b_up"],
+                              b["g"], b["u"], b["a"], lw, stream=stream)
+        moe_lora_gemm_down(s, r, b["a"], b["offsets"], w_down, adapters["b_down"], b["o_perm"], lw, stream=stream)
         moe_combine(s, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["y"], stream)
         return b["y"]
 
@@ -826,8 +831,11 @@ class LoRAStage(MoEStage):
             r, lw = self.rank, self.lora_ws
             moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["do_perm"], b["d_topk_w"],
                             stream)
-            moe_lora_gemm_down_dgrad(s, r, b["do_perm"], b["offsets"], wd, b["g"], b["u"], b["dgu"], lw, stream=stream)
-            moe_lora_gemm_gate_up_dgrad(s, r, b["dgu"], b["offsets"], wg, wu, b["dx_perm"], lw, stream=stream)
+            ad = self.adapters
+            moe_lora_gemm_down_dgrad(s, r, b["do_perm"], b["offsets"], wd, ad["a_down"], b["g"], b["u"], b["dgu"], lw,
+                                     stream=stream)
+            moe_lora_gemm_gate_up_dgrad(s, r, b["dgu"], b["offsets"], wg, wu, ad["a_gate"], ad["a_up"], b["dx_perm"],
+                                        lw, stream=stream)
             moe_lora_grads_unmerged(s, r, b["x_perm"], b["a"], b["dgu"], b["do_perm"], b["offsets"],
                                     *(b["d" + n] for n in LORA_NAMES), lw, stream=stream)
             moe_unpermute_sum(s, b["dx_perm"], b["flat_to_sorted"], b["dx"], stream)

@@ -740,7 +740,7 @@ moe_status check_lora_unmerged(const moe_shape& s, int32_t r, size_t ws_bytes) {
   if (st != MOE_OK) return st;
   if (static_cast<int64_t>(s.T) * s.k * 4 * moe::lora_padded_rank(r) >= (static_cast<int64_t>(1) << 31))
     return MOE_EUNSUPPORTED;
-  if (ws_bytes < moe::lora_layout(s, r, true).total) return MOE_EWORKSPACE;
+  if (ws_bytes < moe::lora_layout(s, r).total) return MOE_EWORKSPACE;
   return MOE_OK;
 }
 void* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
@@ -748,7 +748,7 @@ void* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 size_t moe_lora_unmerged_workspace_bytes(moe_shape s, int32_t r) {
   if (check_lora_unmerged(s, r, ~static_cast<size_t>(0)) != MOE_OK) return 0;
-  return moe::lora_layout(s, r, true).total;
+  return moe::lora_layout(s, r).total;
 }
 
 moe_status moe_lora_prepare(moe_shape s, int32_t r, float scale, const void* a_gate, const void* b_gate,
@@ -764,16 +764,16 @@ moe_status moe_lora_prepare(moe_shape s, int32_t r, float scale, const void* a_g
   g.b_up = b_up;
   g.a_down = a_down;
   g.b_down = b_down;
-  return from_hip(moe::launch_lora_prepare(s, r, scale, g, ws, true, stream));
+  return from_hip(moe::launch_lora_prepare(s, r, scale, g, ws, stream));
 }
 
 moe_status moe_lora_gemm_gate_up(moe_shape s, int32_t r, const void* x_perm, const int32_t* offsets,
-                                 const void* w_gate, const void* w_up, void* g, void* u, void* a, void* ws,
-                                 size_t ws_bytes, hipStream_t stream) {
+                                 const void* w_gate, const void* w_up, const void* b_gate, const void* b_up, void* g,
+                                 void* u, void* a, void* ws, size_t ws_bytes, hipStream_t stream) {
   const moe_status st = check_lora_unmerged(s, r, ws_bytes);
   if (st != MOE_OK) return st;
-  if (any_null(x_perm, offsets, w_gate, w_up, g, u, a, ws)) return MOE_EINVAL;
-  const moe::LoraLayout l = moe::lora_layout(s, r, true);
+  if (any_null(x_perm, offsets, w_gate, w_up, b_gate, b_up, g, u, a, ws)) return MOE_EINVAL;
+  const moe::LoraLayout l = moe::lora_layout(s, r);
   hipError_t err = moe::launch_lora_project(s, r, 0, x_perm, offsets, ws, stream);  // Z_gu
   if (err != hipSuccess) return from_hip(err);
   moe::GemmArgs ga{};
@@ -785,18 +785,20 @@ moe_status moe_lora_gemm_gate_up(moe_shape s, int32_t r, const void* x_perm, con
   ga.out1 = u;
   ga.out2 = a;
   ga.ax = at(ws, l.z_gu);
-  ga.bx0 = at(ws, l.bx_g);
-  ga.bx1 = at(ws, l.bx_u);
-  ga.kx = 2 * moe::lora_padded_rank(r);
+  ga.bx0 = b_gate;
+  ga.bx1 = b_up;
+  ga.kxr = r;
+  ga.kxp = moe::lora_padded_rank(r);
+  ga.kx = 2 * ga.kxp;
   return from_hip(moe::launch_gemm(moe::GEMM_GATEUP, s, ga, stream));
 }
 
 moe_status moe_lora_gemm_down(moe_shape s, int32_t r, const void* a, const int32_t* offsets, const void* w_down,
-                              void* o_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+                              const void* b_down, void* o_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
   const moe_status st = check_lora_unmerged(s, r, ws_bytes);
   if (st != MOE_OK) return st;
-  if (any_null(a, offsets, w_down, o_perm, ws)) return MOE_EINVAL;
-  const moe::LoraLayout l = moe::lora_layout(s, r, true);
+  if (any_null(a, offsets, w_down, b_down, o_perm, ws)) return MOE_EINVAL;
+  const moe::LoraLayout l = moe::lora_layout(s, r);
   hipError_t err = moe::launch_lora_project(s, r, 2, a, offsets, ws, stream);  // Z_d
   if (err != hipSuccess) return from_hip(err);
   moe::GemmArgs ga{};
@@ -805,18 +807,19 @@ moe_status moe_lora_gemm_down(moe_shape s, int32_t r, const void* a, const int32
   ga.b0 = w_down;
   ga.out0 = o_perm;
   ga.ax = at(ws, l.z_d);
-  ga.bx0 = at(ws, l.bx_d);
-  ga.kx = moe::lora_padded_rank(r);
+  ga.bx0 = b_down;
+  ga.kxr = r;
+  ga.kxp = ga.kx = moe::lora_padded_rank(r);
   return from_hip(moe::launch_gemm(moe::GEMM_DOWN, s, ga, stream));
 }
 
 moe_status moe_lora_gemm_down_dgrad(moe_shape s, int32_t r, const void* do_perm, const int32_t* offsets,
-                                    const void* w_down, const void* g, const void* u, void* dgu, void* ws,
-                                    size_t ws_bytes, hipStream_t stream) {
+                                    const void* w_down, const void* a_down, const void* g, const void* u, void* dgu,
+                                    void* ws, size_t ws_bytes, hipStream_t stream) {
   const moe_status st = check_lora_unmerged(s, r, ws_bytes);
   if (st != MOE_OK) return st;
-  if (any_null(do_perm, offsets, w_down, g, u, dgu, ws)) return MOE_EINVAL;
-  const moe::LoraLayout l = moe::lora_layout(s, r, true);
+  if (any_null(do_perm, offsets, w_down, a_down, g, u, dgu, ws)) return MOE_EINVAL;
+  const moe::LoraLayout l = moe::lora_layout(s, r);
   hipError_t err = moe::launch_lora_project(s, r, 3, do_perm, offsets, ws, stream);  // Y_d
   if (err != hipSuccess) return from_hip(err);
   moe::GemmArgs ga{};
@@ -827,18 +830,19 @@ moe_status moe_lora_gemm_down_dgrad(moe_shape s, int32_t r, const void* do_perm,
   ga.u_in = u;
   ga.out0 = dgu;
   ga.ax = at(ws, l.y_d);
-  ga.bx0 = at(ws, l.ax_d);
-  ga.kx = moe::lora_padded_rank(r);
+  ga.bx0 = a_down;
+  ga.kxr = r;
+  ga.kxp = ga.kx = moe::lora_padded_rank(r);
   return from_hip(moe::launch_gemm(moe::GEMM_DGRAD_DOWN, s, ga, stream));
 }
 
 moe_status moe_lora_gemm_gate_up_dgrad(moe_shape s, int32_t r, const void* dgu, const int32_t* offsets,
-                                       const void* w_gate, const void* w_up, void* dx_perm, void* ws,
-                                       size_t ws_bytes, hipStream_t stream) {
+                                       const void* w_gate, const void* w_up, const void* a_gate, const void* a_up,
+                                       void* dx_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
   const moe_status st = check_lora_unmerged(s, r, ws_bytes);
   if (st != MOE_OK) return st;
-  if (any_null(dgu, offsets, w_gate, w_up, dx_perm, ws)) return MOE_EINVAL;
-  const moe::LoraLayout l = moe::lora_layout(s, r, true);
+  if (any_null(dgu, offsets, w_gate, w_up, a_gate, a_up, dx_perm, ws)) return MOE_EINVAL;
+  const moe::LoraLayout l = moe::lora_layout(s, r);
   hipError_t err = moe::launch_lora_project(s, r, 1, dgu, offsets, ws, stream);  // Y_gu
   if (err != hipSuccess) return from_hip(err);
   moe::GemmArgs ga{};
@@ -848,8 +852,11 @@ moe_status moe_lora_gemm_gate_up_dgrad(moe_shape s, int32_t r, const void* dgu, 
   ga.b1 = w_up;
   ga.out0 = dx_perm;
   ga.ax = at(ws, l.y_gu);
-  ga.bx0 = at(ws, l.ax_gu);
-  ga.kx = 2 * moe::lora_padded_rank(r);
+  ga.bx0 = a_gate;
+  ga.bx1 = a_up;
+  ga.kxr = r;
+  ga.kxp = moe::lora_padded_rank(r);
+  ga.kx = 2 * ga.kxp;
   return from_hip(moe::launch_gemm(moe::GEMM_DGRAD_GATEUP, s, ga, stream));
 }
 

@@ -120,13 +120,16 @@ struct Params {
   const uint8_t* sb1;
   // K extended by kx (a multiple of BK) past the main reduction (KX
   // instances: GATEUP, DOWN, DGRAD_DOWN, DGRAD_GATEUP on sorted rows): A's
-  // rows continue in ax [M][kx] and B's in bx0 / bx1 (gate, up), laid out
-  // as the main B with kx in place of its K: [E][N][kx] for GATEUP and DOWN
-  // (k-major), [E][kx][N] for the data gradients (k-rows).
+  // rows continue in ax [M][kx]. B's come straight from rank-kxr adapters,
+  // each padded with zeros to kxp (a multiple of BK) inside the extension:
+  // GATEUP, k-major, gate columns [bx0 | 0] and up columns [0 | bx1] with
+  // bx0, bx1 [E][N][kxr] (kx = 2 kxp); DOWN [bx0 | 0] (kx = kxp); the data
+  // gradients' k-rows bx0 [E][kxr][N] (DGRAD_DOWN, kx = kxp) or bx0 then
+  // bx1 (DGRAD_GATEUP, kx = 2 kxp).
   const bf16_t* ax;
   const bf16_t* bx0;
   const bf16_t* bx1;
-  int kx;
+  int kx, kxr, kxp;
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -523,6 +526,11 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   if constexpr (MODE == WGRAD_GATEUP) { lda = 2 * I; ldb = H; }
   const int kmain = kfixed;  // k-steps of the main operands; KX: then P.kx / BK more
   if constexpr (KX) kfixed += P.kx / BK;
+  // KX: the adapter column of extension step s (gate/up: within its half).
+  auto ext_col = [&](int s) -> int {
+    const int k0x = (s - kmain) * BK;
+    return MODE == GATEUP && k0x >= P.kxp ? k0x - P.kxp : k0x;
+  };
 
   int e = 0, row0 = 0, mvalid = 0, m0 = 0, n0 = 0, kbeg = 0, kend = 0, ksteps = 0;
   int pidx = -1;  // grouped-K: partial tile of a later chunk, -1 for chunk 0
@@ -612,8 +620,10 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   };
   // Per-lane load offsets of the current tile (vector registers; recomputed
   // rather than kept alive across an epilogue).
-  auto set_offsets = [&](auto ext) __attribute__((always_inline)) {
-    // ext (KX): the extension's offsets, rows of length P.kx.
+  auto set_offsets = [&](auto ext, int kk = 0) __attribute__((always_inline)) {
+    // ext (KX): the extension's offsets: A's rows of length P.kx; k-major
+    // B's rows are the adapters' (length P.kxr), at their column kk of this
+    // step, and a lane whose 8 columns lie past the rank loads nothing.
     constexpr bool EXT = decltype(ext)::value;
     // An opaque copy of the lane index keeps the lane-only parts of these
     // offsets from being hoisted out of the tile loop (and spilled).
@@ -678,11 +688,13 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
         const int c = (lane & 3) ^ swk(r);
         const int j = (r & 127) >> 5;
         const int idx = min(n0 + (r >> 7) * 64 + (j & 1) * 32 + (r & 31), I - 1);
-        boff[t] = ESZ * (idx * (EXT ? P.kx : H) + c * CK);
+        if constexpr (EXT) boff[t] = c * CK + kk < P.kxr ? ESZ * (idx * P.kxr + c * CK) : kNoWrite;
+        else boff[t] = ESZ * (idx * H + c * CK);
       } else if constexpr (MODE == DOWN) {
         const int r = blk * 16 + (lane >> 2);
         const int c = (lane & 3) ^ swk(r);
-        boff[t] = ESZ * (min(n0 + r, H - 1) * (EXT ? P.kx : I) + c * CK);
+        if constexpr (EXT) boff[t] = c * CK + kk < P.kxr ? ESZ * (min(n0 + r, H - 1) * P.kxr + c * CK) : kNoWrite;
+        else boff[t] = ESZ * (min(n0 + r, H - 1) * I + c * CK);
       } else {
         const int k = blk * 2 + (lane >> 5);
         const int c = (lane & 31) ^ swt(k);
@@ -727,18 +739,26 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   auto rsrc_b = [&](int s) -> rsrc_t {
     if constexpr (KX) {
       if (s >= kmain) {
+        // Step s's rank columns (or k-rows) kk of one adapter: gate/up's
+        // first kxp steps are the gate adapter's, the next kxp the up one's
+        // (in the forward, a wavefront of the other half reads nothing).
         const int k0x = (s - kmain) * BK;
-        const bool livex = s < ksteps;
-        const int64_t kx = P.kx;
-        if constexpr (MODE == GATEUP)
-          return make_rsrc(((wave & 1) ? P.bx1 : P.bx0) + (static_cast<int64_t>(e) * I * kx + k0x),
-                           livex ? ESZ * (I * P.kx - k0x) : 0);
-        else if constexpr (MODE == DOWN)
-          return make_rsrc(P.bx0 + (static_cast<int64_t>(e) * H * kx + k0x), livex ? ESZ * (H * P.kx - k0x) : 0);
-        else if constexpr (MODE == DGRAD_DOWN)
-          return make_rsrc(P.bx0 + (static_cast<int64_t>(e) * kx + k0x) * I, livex ? 2 * (P.kx - k0x) * I : 0);
-        else
-          return make_rsrc(P.bx0 + (static_cast<int64_t>(e) * kx + k0x) * H, livex ? 2 * (P.kx - k0x) * H : 0);
+        const bool second = (MODE == GATEUP || MODE == DGRAD_GATEUP) && k0x >= P.kxp;
+        const int kk = second ? k0x - P.kxp : k0x;
+        const bool live = s < ksteps && kk < P.kxr;
+        const int64_t r = P.kxr;
+        if constexpr (MODE == GATEUP) {
+          const bool mine = ((wave & 1) != 0) == second;  // odd wavefronts: the up columns
+          return make_rsrc((second ? P.bx1 : P.bx0) + (static_cast<int64_t>(e) * I * r + kk),
+                           live && mine ? ESZ * (I * P.kxr - kk) : 0);
+        } else if constexpr (MODE == DOWN) {
+          return make_rsrc(P.bx0 + (static_cast<int64_t>(e) * H * r + kk), live ? ESZ * (H * P.kxr - kk) : 0);
+        } else if constexpr (MODE == DGRAD_DOWN) {  // k-rows past the rank: outside the range, zeros
+          return make_rsrc(P.bx0 + (static_cast<int64_t>(e) * r + kk) * I, live ? 2 * (P.kxr - kk) * I : 0);
+        } else {
+          return make_rsrc((second ? P.bx1 : P.bx0) + (static_cast<int64_t>(e) * r + kk) * H,
+                           live ? 2 * (P.kxr - kk) * H : 0);
+        }
       }
     }
     const int k0 = s * KS;
@@ -841,7 +861,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
   // All 8 at once (the first steps of a workgroup's first tile).
   auto issue = [&](int s, bf16_t* L) __attribute__((always_inline)) {
     if constexpr (KX) {
-      if (s >= kmain) set_offsets(std::true_type{});
+      if (s >= kmain) set_offsets(std::true_type{}, ext_col(s));
     }
     const rsrc_t ra = rsrc_a(s);
     if constexpr (F4) {
@@ -972,7 +992,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (KX) {  // the extension's steps: its offsets (a tile's last steps, or the next tile's first)
-      if (sn >= kmain) set_offsets(std::true_type{});
+      if (sn >= kmain) set_offsets(std::true_type{}, ext_col(sn));
     }
     const rsrc_t ra = rsrc_a(sn);
     const rsrc_t rb = rsrc_b(sn);
@@ -1684,6 +1704,8 @@ Params make_params(const moe_shape& s, const GemmArgs& g) {
   p.bx0 = static_cast<const bf16_t*>(g.bx0);
   p.bx1 = static_cast<const bf16_t*>(g.bx1);
   p.kx = g.kx;
+  p.kxr = g.kxr;
+  p.kxp = g.kxp;
   return p;
 }
 

@@ -302,22 +302,6 @@ __global__ __launch_bounds__(kThreads) void stack_a_kernel(int r, int rp, int K,
   *reinterpret_cast<uint4*>(out + static_cast<int64_t>(row) * K + c) = o;
 }
 
-// Rows of B [rows][r] placed at columns off .. off + r - 1 of zero rows
-// [rows][width] (bf16; r % 8 == 0, off and width multiples of 8): the K
-// extensions [B_gate | 0], [0 | B_up] and [B_down | 0] of the unmerged
-// forward GEMMs. One thread per 8 output columns.
-__global__ __launch_bounds__(kThreads) void pad_cols_kernel(int64_t rows, int r, int width, int off,
-                                                            const bf16_t* __restrict__ in, bf16_t* __restrict__ out) {
-  const int64_t q = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int per = width / 8;
-  if (q >= rows * per) return;
-  const int64_t row = q / per;
-  const int c = static_cast<int>(q - row * per) * 8 - off;
-  uint4 v = make_uint4(0, 0, 0, 0);
-  if (c >= 0 && c < r) v = *reinterpret_cast<const uint4*>(in + row * r + c);
-  *reinterpret_cast<uint4*>(out + row * width + (c + off)) = v;
-}
-
 // Block-diagonal transposed stack: out[e][J][c], J < nb rp, c < nb C, with
 // J = bj rp + j, c = bc C + cc: bf16(s in_bj[e][cc][j]) where bj == bc and
 // j < r, else 0; in_b [E][C][r], nb = 2 when in1 is given, C % 64 == 0.
@@ -1047,7 +1031,7 @@ hipError_t outer_products(int E, int nb, const int32_t* offsets, const OuterJobs
 // own work).
 int lora_padded_rank(int r) { return r <= 32 ? 32 : (r <= 64 ? 64 : 128); }
 
-LoraLayout lora_layout(const moe_shape& s, int r, bool unmerged) {
+LoraLayout lora_layout(const moe_shape& s, int r) {
   LoraLayout l{};
   const int64_t M = static_cast<int64_t>(s.T) * s.k;
   const int64_t E = s.E, H = s.H, I = s.I, rp = lora_padded_rank(r);
@@ -1072,13 +1056,6 @@ LoraLayout lora_layout(const moe_shape& s, int r, bool unmerged) {
   const int64_t max_tiles = (2 * ceil_div(I, 128) + ceil_div(H, 128)) * E + 2 * grid;
   l.plan = take(256 + max_tiles * static_cast<int64_t>(sizeof(OuterDesc)) + 2 * grid * sizeof(OuterUnit));
   l.part = take(2 * grid * kOuterPartFloats * 4);
-  if (unmerged) {
-    l.bx_g = take(E * I * 2 * rp * 2);
-    l.bx_u = take(E * I * 2 * rp * 2);
-    l.bx_d = take(E * H * rp * 2);
-    l.ax_gu = take(E * 2 * rp * H * 2);
-    l.ax_d = take(E * rp * I * 2);
-  }
   l.total = off;
   return l;
 }
@@ -1126,11 +1103,11 @@ hipError_t launch_lora_merge_mxfp4(int E, int N, int K, int r, float s, const ui
 namespace {
 // The workspace's named regions.
 struct LoraPtrs {
-  bf16_t *sa_gu, *sa_d, *sbt_gu, *sbt_d, *z_gu, *z_d, *y_gu, *y_d, *bx_g, *bx_u, *bx_d, *ax_gu, *ax_d;
+  bf16_t *sa_gu, *sa_d, *sbt_gu, *sbt_d, *z_gu, *z_d, *y_gu, *y_d;
   OuterSpace os;
 };
-LoraPtrs lora_ptrs(const moe_shape& s, int r, void* ws, bool unmerged) {
-  const LoraLayout l = lora_layout(s, r, unmerged);
+LoraPtrs lora_ptrs(const moe_shape& s, int r, void* ws) {
+  const LoraLayout l = lora_layout(s, r);
   char* base = static_cast<char*>(ws);
   auto at = [&](size_t o) { return reinterpret_cast<bf16_t*>(base + o); };
   LoraPtrs p{};
@@ -1142,13 +1119,6 @@ LoraPtrs lora_ptrs(const moe_shape& s, int r, void* ws, bool unmerged) {
   p.z_d = at(l.z_d);
   p.y_gu = at(l.y_gu);
   p.y_d = at(l.y_d);
-  if (unmerged) {
-    p.bx_g = at(l.bx_g);
-    p.bx_u = at(l.bx_u);
-    p.bx_d = at(l.bx_d);
-    p.ax_gu = at(l.ax_gu);
-    p.ax_d = at(l.ax_d);
-  }
   const int64_t max_tiles = (2 * ceil_div(s.I, 128) + ceil_div(s.H, 128)) * static_cast<int64_t>(s.E) + 2 * outer_grid();
   p.os.hdr = reinterpret_cast<int*>(base + l.plan);
   p.os.desc = reinterpret_cast<OuterDesc*>(base + l.plan + 256);
@@ -1161,9 +1131,8 @@ LoraPtrs lora_ptrs(const moe_shape& s, int r, void* ws, bool unmerged) {
 #define MOE_TRY(x) \
   if ((err = (x)) != hipSuccess) return err
 
-hipError_t launch_lora_prepare(const moe_shape& s, int r, float scale, const LoraArgs& g, void* ws, bool unmerged,
-                               hipStream_t st) {
-  const LoraPtrs p = lora_ptrs(s, r, ws, unmerged);
+hipError_t launch_lora_prepare(const moe_shape& s, int r, float scale, const LoraArgs& g, void* ws, hipStream_t st) {
+  const LoraPtrs p = lora_ptrs(s, r, ws);
   const int E = s.E, H = s.H, I = s.I, rp = lora_padded_rank(r);
   const bf16_t* a_gate = static_cast<const bf16_t*>(g.a_gate);
   const bf16_t* a_up = static_cast<const bf16_t*>(g.a_up);
@@ -1184,32 +1153,12 @@ hipError_t launch_lora_prepare(const moe_shape& s, int r, float scale, const Lor
   MOE_TRY(hipGetLastError());
   blockdiag_t_kernel<<<dim3(H / 64, E), kThreads, 0, st>>>(H, r, rp, scale, b_down, nullptr, p.sbt_d);
   MOE_TRY(hipGetLastError());
-  if (unmerged) {
-    // The GEMMs' K extensions: the forward multiplies Z = X (sA)^T by B, the
-    // data gradients Y = dY (sB) by A, so B and A enter unscaled.
-    const int64_t ri = static_cast<int64_t>(E) * I, rh = static_cast<int64_t>(E) * H;
-    auto pad = [&](int64_t rows, int width, int off, const bf16_t* in, bf16_t* out) {
-      const int64_t n = rows * (width / 8);
-      pad_cols_kernel<<<static_cast<unsigned>(ceil_div(n, static_cast<int64_t>(kThreads))), kThreads, 0, st>>>(
-          rows, r, width, off, in, out);
-      return hipGetLastError();
-    };
-    MOE_TRY(pad(ri, 2 * rp, 0, b_gate, p.bx_g));
-    MOE_TRY(pad(ri, 2 * rp, rp, b_up, p.bx_u));
-    MOE_TRY(pad(rh, rp, 0, b_down, p.bx_d));
-    stack_a_kernel<<<dim3(E * 2 * rp, ceil_div(H / 8, kThreads)), kThreads, 0, st>>>(r, rp, H, 1.0f, a_gate, a_up,
-                                                                                       p.ax_gu);
-    MOE_TRY(hipGetLastError());
-    stack_a_kernel<<<dim3(E * rp, ceil_div(I / 8, kThreads)), kThreads, 0, st>>>(r, rp, I, 1.0f, a_down, nullptr,
-                                                                                   p.ax_d);
-    MOE_TRY(hipGetLastError());
-  }
   return hipSuccess;
 }
 
 hipError_t launch_lora_project(const moe_shape& s, int r, int which, const void* in, const int32_t* offsets,
                                void* ws, hipStream_t st) {
-  const LoraPtrs p = lora_ptrs(s, r, ws, true);
+  const LoraPtrs p = lora_ptrs(s, r, ws);
   const int H = s.H, I = s.I, rp = lora_padded_rank(r), M = s.T * s.k;
   const bf16_t* x = static_cast<const bf16_t*>(in);
   ProjJobs pj{};
@@ -1224,7 +1173,7 @@ hipError_t launch_lora_project(const moe_shape& s, int r, int which, const void*
 }
 
 hipError_t launch_lora_outer(const moe_shape& s, int r, const LoraArgs& g, void* ws, hipStream_t st) {
-  const LoraPtrs p = lora_ptrs(s, r, ws, false);
+  const LoraPtrs p = lora_ptrs(s, r, ws);
   const int E = s.E, H = s.H, I = s.I, rp = lora_padded_rank(r);
   const int32_t* tok = g.row_token;
   const int M = s.T * s.k, nsrc = tok != nullptr ? s.T : M;
@@ -1249,10 +1198,10 @@ hipError_t launch_lora_outer(const moe_shape& s, int r, const LoraArgs& g, void*
 }
 
 hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraArgs& g, void* ws, hipStream_t st) {
-  const LoraPtrs p = lora_ptrs(s, r, ws, false);
+  const LoraPtrs p = lora_ptrs(s, r, ws);
   const int H = s.H, I = s.I, rp = lora_padded_rank(r);
   hipError_t err;
-  MOE_TRY(launch_lora_prepare(s, r, scale, g, ws, false, st));
+  MOE_TRY(launch_lora_prepare(s, r, scale, g, ws, st));
   // Row projections Z = X (sA)^T, Y = dY (sB): [Z_gate | Z_up], [dG sB_gate |
   // dU sB_up], Z_down, dO sB_down.
   // With row_token, x and dy are read through the sorted rows' tokens, and

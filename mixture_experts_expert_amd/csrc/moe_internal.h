@@ -160,12 +160,14 @@ struct GemmArgs {
   int b_fp4;
   // Extended reduction (bf16 GATEUP, DOWN, DGRAD_DOWN, DGRAD_GATEUP over
   // sorted rows): kx > 0 (a multiple of 32) more k past the main K, A's
-  // from ax [T*k][kx], B's from bx0 (and bx1, the up half of gate/up): [E][N][kx]
-  // for GATEUP and DOWN, [E][kx][N] for the data gradients.
+  // from ax [T*k][kx], B's from rank-kxr adapters padded with zeros to kxp
+  // (kx = kxp, or 2 kxp for gate/up: the gate half, then the up half):
+  // bx0 (gate or down) and bx1 (up), [E][N][kxr] for GATEUP and DOWN,
+  // [E][kxr][N] for the data gradients.
   const void* ax;
   const void* bx0;
   const void* bx1;
-  int kx;
+  int kx, kxr, kxp;
 };
 
 hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& a, hipStream_t st);
@@ -210,13 +212,9 @@ struct LoraLayout {  // byte offsets in the adapter-gradient workspace
   size_t z_gu, z_d, y_gu, y_d;        // bf16 row projections [T*k][2rp | rp]
   size_t plan;                        // split plan of the outer products (descriptors)
   size_t part;                        // fp32 partial tiles of split outer products
-  // Unmerged step only: the GEMMs' K extensions (bf16), [B_gate | 0] and
-  // [0 | B_up] [E][I][2rp], B_down [E][H][rp] (forward), [A_gate; A_up]
-  // [E][2rp][H] and A_down [E][rp][I] (data gradients), rank padded with zeros.
-  size_t bx_g, bx_u, bx_d, ax_gu, ax_d;
   size_t total;
 };
-LoraLayout lora_layout(const moe_shape& s, int r, bool unmerged = false);
+LoraLayout lora_layout(const moe_shape& s, int r);
 
 struct LoraArgs {
   const int32_t* offsets;
@@ -241,13 +239,13 @@ hipError_t launch_lora_merge_fp8(int E, int N, int K, int r, float s, const uint
 hipError_t launch_lora_merge_mxfp4(int E, int N, int K, int r, float s, const uint8_t* wq, const uint8_t* w8,
                                    const void* a, const void* b, void* w_out, hipStream_t st);
 hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraArgs& g, void* ws, hipStream_t st);
-// The unmerged adapter step (lora.hip): the scaled stacks and the GEMMs' K
-// extensions from the adapters in g (launch_lora_prepare, once per step);
-// one row projection (launch_lora_project: 0 Z_gu = x_perm sA_gu^T, 1 Y_gu =
-// dgu sB_gu, 2 Z_d = act sA_d^T, 3 Y_d = do_perm sB_d) into the workspace;
-// the adapter gradients from the projections held there (launch_lora_outer).
-hipError_t launch_lora_prepare(const moe_shape& s, int r, float scale, const LoraArgs& g, void* ws, bool unmerged,
-                               hipStream_t st);
+// The unmerged adapter step (lora.hip): the scaled stacks of the row
+// projections from the adapters in g (launch_lora_prepare, once per step;
+// the GEMMs' K extensions read the adapters themselves); one row projection
+// (launch_lora_project: 0 Z_gu = x_perm sA_gu^T, 1 Y_gu = dgu sB_gu, 2 Z_d =
+// act sA_d^T, 3 Y_d = do_perm sB_d) into the workspace; the adapter
+// gradients from the projections held there (launch_lora_outer).
+hipError_t launch_lora_prepare(const moe_shape& s, int r, float scale, const LoraArgs& g, void* ws, hipStream_t st);
 hipError_t launch_lora_project(const moe_shape& s, int r, int which, const void* in, const int32_t* offsets,
                                void* ws, hipStream_t st);
 hipError_t launch_lora_outer(const moe_shape& s, int r, const LoraArgs& g, void* ws, hipStream_t st);

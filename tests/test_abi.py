@@ -179,7 +179,7 @@ def test_lora_validation(B):
     # the adapter step without merged weights: its own workspace (the GEMMs'
     # K extensions on top), every check before any HIP call
     un = B.moe_lora_unmerged_workspace_bytes(s, 16)
-    assert un > need
+    assert un == need
     assert B.moe_lora_unmerged_workspace_bytes(s, 12) == 0
     assert B.moe_lora_unmerged_workspace_bytes(B.shape(64, 128, 8, 2, 64, "f32"), 16) == 0
     assert B.moe_lora_unmerged_workspace_bytes(B.shape(1 << 20, 64, 8, 8, 64, "bf16"), 128) == 0  # T k 4 rp >= 2^31
@@ -188,11 +188,13 @@ def test_lora_validation(B):
     assert PR(s, 16, 1.0, *([F] * 6), None, un, None) == 1
     assert PR(s, 20, 1.0, *([F] * 7), un, None) == 2
     LG = B.lib.moe_lora_gemm_gate_up
-    assert LG(s, 16, *([F] * 8), un - 1, None) == 3
-    assert LG(s, 16, F, None, *([F] * 6), un, None) == 1
-    assert B.lib.moe_lora_gemm_down(s, 16, *([F] * 3), None, F, un, None) == 1
-    assert B.lib.moe_lora_gemm_down_dgrad(s, 136, *([F] * 7), un, None) == 2
-    assert B.lib.moe_lora_gemm_gate_up_dgrad(s, 16, *([F] * 6), un - 1, None) == 3
+    assert LG(s, 16, *([F] * 10), un - 1, None) == 3
+    assert LG(s, 16, F, None, *([F] * 8), un, None) == 1
+    assert LG(s, 16, *([F] * 4), None, *([F] * 5), un, None) == 1   # b_gate
+    assert B.lib.moe_lora_gemm_down(s, 16, *([F] * 3), None, F, F, un, None) == 1   # b_down
+    assert B.lib.moe_lora_gemm_down_dgrad(s, 136, *([F] * 8), un, None) == 2
+    assert B.lib.moe_lora_gemm_down_dgrad(s, 16, *([F] * 3), None, *([F] * 4), un, None) == 1   # a_down
+    assert B.lib.moe_lora_gemm_gate_up_dgrad(s, 16, *([F] * 8), un - 1, None) == 3
     GU = B.lib.moe_lora_grads_unmerged
     assert GU(s, 16, *([F] * 12), un - 1, None) == 3
     assert GU(s, 16, *([F] * 5), None, *([F] * 6), un, None) == 1
