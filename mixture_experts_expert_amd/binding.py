@@ -759,6 +759,8 @@ class LoRAStage(MoEStage):
         })
 
     def merge(self, w_gate, w_up, w_down, adapters, stream=None):
+        if self.unmerged:
+            raise ValueError("LoRAStage(unmerged=True) holds no merged weights")
         E, H, I, r = self.E, self.H, self.I, self.rank
         wg, wu, wd = self.merged
         _merge_any(E, I, H, r, self.scale, w_gate, adapters["a_gate"], adapters["b_gate"], wg, stream)
