@@ -58,7 +58,8 @@ experts (merges, forward on the merged weights, data and adapter gradients)
 and its two adapter calls, over bf16, E4M3 and MXFP4 frozen weights, the
 step without x_perm and do_perm (`step_gathered`, with
 `moe_lora_grads_gathered`) and the step without merged weights
-(`step_unmerged`, its calls in `unmerged_call_ms`). `--timed-only` skips these and the CPU baseline, so that
+(`step_unmerged`, its calls in `unmerged_call_ms`), and the step without
+either (`step_gathered_unmerged`). `--timed-only` skips these and the CPU baseline, so that
 under a profiler the last K launches of every kernel are the timed steps.
 """
 from __future__ import annotations
@@ -260,8 +261,8 @@ def lora_timing(cfg, seed: int, tensors, bias, stream, r: int = 64, scale: float
     same shape: the three merges W' = W + s B A, the forward on W', the data
     gradients and the adapter gradients (no frozen-weight gradient); then
     the merges and the adapter-gradient call on their own; the same over 8-
-    and 4-bit frozen weights, without x_perm and do_perm, and without merged
-    weights (step_unmerged, with its calls on their own)."""
+    and 4-bit frozen weights, without x_perm and do_perm, without merged
+    weights (step_unmerged, with its calls on their own), and without both."""
     import numpy as np
     import torch
 
@@ -355,8 +356,18 @@ def lora_timing(cfg, seed: int, tensors, bias, stream, r: int = 64, scale: float
             *(ub["d" + n] for n in B.LORA_NAMES), uw),
     }
     out["unmerged_call_ms"] = {n: round(time_calls(f, stream, reps=5), 4) for n, f in un_calls.items()}
+    del us, ub, uw
+    torch.cuda.empty_cache()
+    # Neither merged weights nor x_perm and do_perm.
+    gu = B.LoRAStage(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, r, scale, gathered=True, unmerged=True)
+
+    def lora_step_gathered_unmerged():
+        gu.forward(x, wr, wg, wu, wd, ad, bias)
+        gu.backward(dy)
+
+    out["step_gathered_unmerged"] = round(time_calls(lora_step_gathered_unmerged, stream), 4)
     log(f"adapter step: {out}")
-    del us, ub, uw, ad
+    del gu, ad
     torch.cuda.empty_cache()
     return out
 

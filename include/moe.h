@@ -542,6 +542,32 @@ moe_status moe_lora_gemm_gate_up_dgrad(moe_shape s, int32_t r, const void* dgu, 
                                        const void* w_gate, const void* w_up, const void* a_gate, const void* a_up,
                                        void* dx_perm, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Without x_perm and do_perm (the gathered chain: moe_permute_fused, then
+ * moe_combine_bwd with do_perm NULL): moe_lora_gemm_gate_up reading x [T,H]
+ * through row_token (Z from x's rows likewise), and moe_lora_gemm_down_dgrad
+ * reading dy [T,H] through row_token with the routing weight row_weight[p]
+ * applied in fp32 to the whole sum (the extension included) before the
+ * SwiGLU backward, as moe_gemm_down_dgrad_dy. moe_lora_gemm_down and
+ * moe_lora_gemm_gate_up_dgrad are the same calls in both chains. */
+moe_status moe_lora_gemm_gate_up_gathered(moe_shape s, int32_t r, const void* x, const int32_t* row_token,
+                                          const int32_t* offsets, const void* w_gate, const void* w_up,
+                                          const void* b_gate, const void* b_up, void* g, void* u, void* a, void* ws,
+                                          size_t ws_bytes, hipStream_t stream);
+moe_status moe_lora_gemm_down_dgrad_dy(moe_shape s, int32_t r, const void* dy, const int32_t* row_token,
+                                       const float* row_weight, const int32_t* offsets, const void* w_down,
+                                       const void* a_down, const void* g, const void* u, void* dgu, void* ws,
+                                       size_t ws_bytes, hipStream_t stream);
+
+/* The adapter gradients of the gathered unmerged chain, as
+ * moe_lora_grads_gathered: the two projections that carry dO = w dy again
+ * with the weight, then the outer products reading x and dy through
+ * row_token. */
+moe_status moe_lora_grads_unmerged_gathered(moe_shape s, int32_t r, const void* x, const int32_t* row_token,
+                                            const float* row_weight, const void* act, const void* dgu, const void* dy,
+                                            const int32_t* offsets, float* da_gate, float* db_gate, float* da_up,
+                                            float* db_up, float* da_down, float* db_down, void* ws, size_t ws_bytes,
+                                            hipStream_t stream);
+
 /* The six adapter gradients (as moe_lora_grads) from the projections the
  * four calls above left in ws: the outer products only. */
 moe_status moe_lora_grads_unmerged(moe_shape s, int32_t r, const void* x_perm, const void* act, const void* dgu,

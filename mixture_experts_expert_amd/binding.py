@@ -97,6 +97,10 @@ _SIGS = {
     "moe_lora_gemm_down_dgrad": ([moe_shape, ctypes.c_int32] + [_P] * 8 + [ctypes.c_size_t, _P], ctypes.c_int),
     "moe_lora_gemm_gate_up_dgrad": ([moe_shape, ctypes.c_int32] + [_P] * 8 + [ctypes.c_size_t, _P], ctypes.c_int),
     "moe_lora_grads_unmerged": ([moe_shape, ctypes.c_int32] + [_P] * 12 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_lora_gemm_gate_up_gathered": ([moe_shape, ctypes.c_int32] + [_P] * 11 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_lora_gemm_down_dgrad_dy": ([moe_shape, ctypes.c_int32] + [_P] * 10 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_lora_grads_unmerged_gathered": ([moe_shape, ctypes.c_int32] + [_P] * 14 + [ctypes.c_size_t, _P],
+                                         ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -513,6 +517,27 @@ def moe_lora_grads_unmerged(s, r, x_perm, act, dgu, do_perm, offsets, da_gate, d
                                   db_down, ws)], _nbytes(ws, ws_bytes), _stream(stream)))
 
 
+def moe_lora_gemm_gate_up_gathered(s, r, x, row_token, offsets, w_gate, w_up, b_gate, b_up, g, u, a, ws,
+                                   ws_bytes=None, stream=None):
+    _check("moe_lora_gemm_gate_up_gathered", lib.moe_lora_gemm_gate_up_gathered(
+        s, r, *[_ptr(t) for t in (x, row_token, offsets, w_gate, w_up, b_gate, b_up, g, u, a, ws)],
+        _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def moe_lora_gemm_down_dgrad_dy(s, r, dy, row_token, row_weight, offsets, w_down, a_down, g, u, dgu, ws,
+                                ws_bytes=None, stream=None):
+    _check("moe_lora_gemm_down_dgrad_dy", lib.moe_lora_gemm_down_dgrad_dy(
+        s, r, *[_ptr(t) for t in (dy, row_token, row_weight, offsets, w_down, a_down, g, u, dgu, ws)],
+        _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def moe_lora_grads_unmerged_gathered(s, r, x, row_token, row_weight, act, dgu, dy, offsets, da_gate, db_gate, da_up,
+                                     db_up, da_down, db_down, ws, ws_bytes=None, stream=None):
+    _check("moe_lora_grads_unmerged_gathered", lib.moe_lora_grads_unmerged_gathered(
+        s, r, *[_ptr(t) for t in (x, row_token, row_weight, act, dgu, dy, offsets, da_gate, db_gate, da_up, db_up,
+                                  da_down, db_down, ws)], _nbytes(ws, ws_bytes), _stream(stream)))
+
+
 def moe_lora_grads_gathered(s, r, scale, x, row_token, row_weight, act, dgu, dy, offsets, a_gate, b_gate, a_up,
                             b_up, a_down, b_down, da_gate, db_gate, da_up, db_up, da_down, db_down, ws, ws_bytes=None,
                             stream=None):
@@ -727,13 +752,13 @@ class LoRAStage(MoEStage):
     rank (moe_lora_gemm_gate_up, moe_lora_gemm_down, moe_lora_gemm_down_dgrad,
     moe_lora_gemm_gate_up_dgrad), and moe_lora_grads_unmerged takes the
     adapter gradients from the row projections those calls kept. Within
-    rounding of the merged chain.
+    rounding of the merged chain. With ``gathered`` as well, the gathered
+    calls (moe_lora_gemm_gate_up_gathered, moe_lora_gemm_down_dgrad_dy,
+    moe_lora_grads_unmerged_gathered) build neither x_perm nor do_perm.
     """
 
     def __init__(self, T: int, H: int, E: int, k: int, I: int, rank: int, scale: float, device="cuda",
                  gathered: bool = False, unmerged: bool = False):
-        if gathered and unmerged:
-            raise ValueError("the unmerged adapter step reads x_perm and do_perm")
         super().__init__(T, H, E, k, I, torch.bfloat16, device=device, gather_fused=gathered)
         self.gathered, self.unmerged = gathered, unmerged
         self.weight_grads = False
@@ -817,10 +842,16 @@ class LoRAStage(MoEStage):
         self.x = x
         moe_lora_prepare(s, r, self.scale, *(adapters[n] for n in LORA_NAMES), lw, stream=stream)
         moe_route(s, x, w_router, logit_bias, b["logits"], b["topk_idx"], b["topk_w"], stream)
-        moe_permute(s, b["topk_idx"], x, b["counts"], b["offsets"], b["sorted_to_flat"], b["flat_to_sorted"],
-                    b["x_perm"], self.ws, stream=stream)
-        moe_lora_gemm_gate_up(s, r, b["x_perm"], b["offsets"], w_gate, w_up, adapters["b_gate"], adapters["b_up"],
-                              b["g"], b["u"], b["a"], lw, stream=stream)
+        if self.gathered:
+            moe_permute_fused(s, b["topk_idx"], b["topk_w"], b["counts"], b["offsets"], b["sorted_to_flat"],
+                              b["flat_to_sorted"], b["row_token"], b["row_weight"], self.ws, stream=stream)
+            moe_lora_gemm_gate_up_gathered(s, r, x, b["row_token"], b["offsets"], w_gate, w_up, adapters["b_gate"],
+                                           adapters["b_up"], b["g"], b["u"], b["a"], lw, stream=stream)
+        else:
+            moe_permute(s, b["topk_idx"], x, b["counts"], b["offsets"], b["sorted_to_flat"], b["flat_to_sorted"],
+                        b["x_perm"], self.ws, stream=stream)
+            moe_lora_gemm_gate_up(s, r, b["x_perm"], b["offsets"], w_gate, w_up, adapters["b_gate"],
+                                  adapters["b_up"], b["g"], b["u"], b["a"], lw, stream=stream)
         moe_lora_gemm_down(s, r, b["a"], b["offsets"], w_down, adapters["b_down"], b["o_perm"], lw, stream=stream)
         moe_combine(s, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["y"], stream)
         return b["y"]
@@ -831,15 +862,24 @@ class LoRAStage(MoEStage):
         if self.unmerged:
             wg, wu, wd = self.w
             r, lw = self.rank, self.lora_ws
-            moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["do_perm"], b["d_topk_w"],
-                            stream)
             ad = self.adapters
-            moe_lora_gemm_down_dgrad(s, r, b["do_perm"], b["offsets"], wd, ad["a_down"], b["g"], b["u"], b["dgu"], lw,
-                                     stream=stream)
+            if self.gathered:
+                moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"], None, b["d_topk_w"], stream)
+                moe_lora_gemm_down_dgrad_dy(s, r, dy, b["row_token"], b["row_weight"], b["offsets"], wd, ad["a_down"],
+                                            b["g"], b["u"], b["dgu"], lw, stream=stream)
+            else:
+                moe_combine_bwd(s, dy, b["o_perm"], b["topk_w"], b["flat_to_sorted"], b["do_perm"], b["d_topk_w"],
+                                stream)
+                moe_lora_gemm_down_dgrad(s, r, b["do_perm"], b["offsets"], wd, ad["a_down"], b["g"], b["u"], b["dgu"],
+                                         lw, stream=stream)
             moe_lora_gemm_gate_up_dgrad(s, r, b["dgu"], b["offsets"], wg, wu, ad["a_gate"], ad["a_up"], b["dx_perm"],
                                         lw, stream=stream)
-            moe_lora_grads_unmerged(s, r, b["x_perm"], b["a"], b["dgu"], b["do_perm"], b["offsets"],
-                                    *(b["d" + n] for n in LORA_NAMES), lw, stream=stream)
+            if self.gathered:
+                moe_lora_grads_unmerged_gathered(s, r, self.x, b["row_token"], b["row_weight"], b["a"], b["dgu"], dy,
+                                                 b["offsets"], *(b["d" + n] for n in LORA_NAMES), lw, stream=stream)
+            else:
+                moe_lora_grads_unmerged(s, r, b["x_perm"], b["a"], b["dgu"], b["do_perm"], b["offsets"],
+                                        *(b["d" + n] for n in LORA_NAMES), lw, stream=stream)
             moe_unpermute_sum(s, b["dx_perm"], b["flat_to_sorted"], b["dx"], stream)
             moe_route_bwd(s, b["d_topk_w"], b["topk_w"], b["topk_idx"], b["d_logits"], stream)
             return b["dx"]

@@ -860,6 +860,93 @@ moe_status moe_lora_gemm_gate_up_dgrad(moe_shape s, int32_t r, const void* dgu, 
   return from_hip(moe::launch_gemm(moe::GEMM_DGRAD_GATEUP, s, ga, stream));
 }
 
+moe_status moe_lora_gemm_gate_up_gathered(moe_shape s, int32_t r, const void* x, const int32_t* row_token,
+                                          const int32_t* offsets, const void* w_gate, const void* w_up,
+                                          const void* b_gate, const void* b_up, void* g, void* u, void* a, void* ws,
+                                          size_t ws_bytes, hipStream_t stream) {
+  const moe_status st = check_lora_unmerged(s, r, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (any_null(x, row_token, offsets, w_gate, w_up, b_gate, b_up, g, u, a, ws)) return MOE_EINVAL;
+  const moe::LoraLayout l = moe::lora_layout(s, r);
+  hipError_t err = moe::launch_lora_project(s, r, 0, x, offsets, ws, stream, row_token);  // Z_gu from x's rows
+  if (err != hipSuccess) return from_hip(err);
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = x;
+  ga.row_token = row_token;
+  ga.b0 = w_gate;
+  ga.b1 = w_up;
+  ga.out0 = g;
+  ga.out1 = u;
+  ga.out2 = a;
+  ga.ax = at(ws, l.z_gu);
+  ga.bx0 = b_gate;
+  ga.bx1 = b_up;
+  ga.kxr = r;
+  ga.kxp = moe::lora_padded_rank(r);
+  ga.kx = 2 * ga.kxp;
+  return from_hip(moe::launch_gemm(moe::GEMM_GATEUP, s, ga, stream));
+}
+
+moe_status moe_lora_gemm_down_dgrad_dy(moe_shape s, int32_t r, const void* dy, const int32_t* row_token,
+                                       const float* row_weight, const int32_t* offsets, const void* w_down,
+                                       const void* a_down, const void* g, const void* u, void* dgu, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+  const moe_status st = check_lora_unmerged(s, r, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (any_null(dy, row_token, row_weight, offsets, w_down, a_down, g, u, dgu, ws)) return MOE_EINVAL;
+  const moe::LoraLayout l = moe::lora_layout(s, r);
+  // dy's rows through the tokens, unweighted: the kernel applies the
+  // routing weight to the whole sum, extension included.
+  hipError_t err = moe::launch_lora_project(s, r, 3, dy, offsets, ws, stream, row_token);
+  if (err != hipSuccess) return from_hip(err);
+  moe::GemmArgs ga{};
+  ga.offsets = offsets;
+  ga.a = dy;
+  ga.row_token = row_token;
+  ga.row_weight = row_weight;
+  ga.b0 = w_down;
+  ga.g_in = g;
+  ga.u_in = u;
+  ga.out0 = dgu;
+  ga.ax = at(ws, l.y_d);
+  ga.bx0 = a_down;
+  ga.kxr = r;
+  ga.kxp = ga.kx = moe::lora_padded_rank(r);
+  return from_hip(moe::launch_gemm(moe::GEMM_DGRAD_DOWN, s, ga, stream));
+}
+
+moe_status moe_lora_grads_unmerged_gathered(moe_shape s, int32_t r, const void* x, const int32_t* row_token,
+                                            const float* row_weight, const void* act, const void* dgu, const void* dy,
+                                            const int32_t* offsets, float* da_gate, float* db_gate, float* da_up,
+                                            float* db_up, float* da_down, float* db_down, void* ws, size_t ws_bytes,
+                                            hipStream_t stream) {
+  const moe_status st = check_lora_unmerged(s, r, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (any_null(x, row_token, row_weight, act, dgu, dy, offsets, da_gate, db_gate, da_up, db_up, da_down, db_down, ws))
+    return MOE_EINVAL;
+  // The two projections that carry dO = w dy, again with the weight: Z_down'
+  // = w Z_down (for dB_down = dy^T Z_down') and Y_down = w (dy sB_down).
+  hipError_t err = moe::launch_lora_project(s, r, 2, act, offsets, ws, stream, nullptr, row_weight);
+  if (err == hipSuccess) err = moe::launch_lora_project(s, r, 3, dy, offsets, ws, stream, row_token, row_weight);
+  if (err != hipSuccess) return from_hip(err);
+  moe::LoraArgs g{};
+  g.offsets = offsets;
+  g.x_perm = x;
+  g.act = act;
+  g.dgu = dgu;
+  g.do_perm = dy;
+  g.row_token = row_token;
+  g.row_weight = row_weight;
+  g.da_gate = da_gate;
+  g.db_gate = db_gate;
+  g.da_up = da_up;
+  g.db_up = db_up;
+  g.da_down = da_down;
+  g.db_down = db_down;
+  return from_hip(moe::launch_lora_outer(s, r, g, ws, stream));
+}
+
 moe_status moe_lora_grads_unmerged(moe_shape s, int32_t r, const void* x_perm, const void* act, const void* dgu,
                                    const void* do_perm, const int32_t* offsets, float* da_gate, float* db_gate,
                                    float* da_up, float* db_up, float* da_down, float* db_down, void* ws,

@@ -383,7 +383,8 @@ template <int MODE, bool FUSED, bool F8 = false, bool AW = false, bool F4 = fals
 __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const int nblk, const Smem& sm) {
   static_assert(!F8 || (FUSED && (MODE == GATEUP || MODE == DOWN)), "fp8: the inference forward's two GEMMs");
   static_assert(!F4 || F8, "MXFP4 weights: with fp8 activations");
-  static_assert(!KX || (!FUSED && !F8 && !AW && !grouped_k(MODE)), "extended K: bf16 GEMMs over sorted rows");
+  static_assert(!KX || (!F8 && !AW && !grouped_k(MODE) && (!FUSED || MODE == GATEUP || MODE == DGRAD_DOWN)),
+                "extended K: the bf16 forward and data-gradient GEMMs (gate/up and down dgrad also with gathered rows)");
   static_assert(!AW || (MODE == GATEUP && !F8), "a_w: the gate/up GEMM of the training step");
   // Element size in bytes, elements per k-step (64 bytes of a k-major row
   // either way) and per 16-byte chunk.
@@ -644,7 +645,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& P, const int bid, const
       if constexpr (A_KMAJOR) {
         const int r = blk * 16 + (lane >> 2);
         const int c = (lane & 3) ^ swk(r);
-        if (GATHER_A_ROWS)  // row of x or dy; rows >= mvalid read zeros
+        if (GATHER_A_ROWS && !EXT)  // row of x or dy; rows >= mvalid read zeros (the extension's rows are sorted)
           aoff[t] = r < mvalid ? ESZ * (static_cast<uint32_t>(P.row_token[row0 + r]) * H + c * CK) : kNoWrite;
         else
           aoff[t] = ESZ * (r * (EXT ? P.kx : lda) + c * CK);  // rows >= mvalid: outside the range, read as zeros
@@ -1724,8 +1725,11 @@ hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g
   const Params p = make_params(s, g);
   switch (mode) {
     case GEMM_GATEUP:
-      if (g.kx > 0)
-        return g.row_token || g.a_scale || g.out3 ? hipErrorInvalidValue : run<GATEUP, false, false, false, false, true>(p, st);
+      if (g.kx > 0) {
+        if (g.a_scale || g.out3) return hipErrorInvalidValue;
+        return g.row_token ? run<GATEUP, true, false, false, false, true>(p, st)
+                           : run<GATEUP, false, false, false, false, true>(p, st);
+      }
       if (g.a_scale && g.b_fp4) return g.row_token ? run<GATEUP, true, true, false, true>(p, st) : hipErrorInvalidValue;
       if (g.a_scale) return g.row_token ? run<GATEUP, true, true>(p, st) : hipErrorInvalidValue;
       if (g.out3)  // a_w (needs row_weight)
@@ -1738,7 +1742,9 @@ hipError_t launch_gemm_bf16(GemmMode mode, const moe_shape& s, const GemmArgs& g
       if (g.a_scale) return g.row_weight ? run<DOWN, true, true>(p, st) : hipErrorInvalidValue;
       return g.row_weight ? run<DOWN, true>(p, st) : run<DOWN>(p, st);
     case GEMM_DGRAD_DOWN:
-      if (g.kx > 0) return g.row_token ? hipErrorInvalidValue : run<DGRAD_DOWN, false, false, false, false, true>(p, st);
+      if (g.kx > 0)
+        return g.row_token ? run<DGRAD_DOWN, true, false, false, false, true>(p, st)
+                           : run<DGRAD_DOWN, false, false, false, false, true>(p, st);
       return g.row_token ? run<DGRAD_DOWN, true>(p, st) : run<DGRAD_DOWN>(p, st);
     case GEMM_DGRAD_GATEUP:
       if (g.kx > 0) return run<DGRAD_GATEUP, false, false, false, false, true>(p, st);

@@ -1157,16 +1157,17 @@ hipError_t launch_lora_prepare(const moe_shape& s, int r, float scale, const Lor
 }
 
 hipError_t launch_lora_project(const moe_shape& s, int r, int which, const void* in, const int32_t* offsets,
-                               void* ws, hipStream_t st) {
+                               void* ws, hipStream_t st, const int32_t* tok, const float* rw) {
   const LoraPtrs p = lora_ptrs(s, r, ws);
   const int H = s.H, I = s.I, rp = lora_padded_rank(r), M = s.T * s.k;
+  const int nsrc = tok != nullptr ? s.T : M;
   const bf16_t* x = static_cast<const bf16_t*>(in);
   ProjJobs pj{};
   switch (which) {
-    case 0: pj.job[0] = {x, p.sa_gu, p.z_gu, H, 2 * rp, nullptr, nullptr, M}; break;
-    case 1: pj.job[0] = {x, p.sbt_gu, p.y_gu, 2 * I, 2 * rp, nullptr, nullptr, M}; break;
-    case 2: pj.job[0] = {x, p.sa_d, p.z_d, I, rp, nullptr, nullptr, M}; break;
-    default: pj.job[0] = {x, p.sbt_d, p.y_d, H, rp, nullptr, nullptr, M}; break;
+    case 0: pj.job[0] = {x, p.sa_gu, p.z_gu, H, 2 * rp, tok, rw, nsrc}; break;
+    case 1: pj.job[0] = {x, p.sbt_gu, p.y_gu, 2 * I, 2 * rp, tok, rw, nsrc}; break;
+    case 2: pj.job[0] = {x, p.sa_d, p.z_d, I, rp, tok, rw, nsrc}; break;
+    default: pj.job[0] = {x, p.sbt_d, p.y_d, H, rp, tok, rw, nsrc}; break;
   }
   pj.n = 1;
   return projections(s, pj.job[0].N < 64 ? 64 : pj.job[0].N, offsets, pj, st);  // the kernel's widths: 64, 128, 256

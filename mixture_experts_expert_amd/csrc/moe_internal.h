@@ -243,11 +243,13 @@ hipError_t launch_lora_grads(const moe_shape& s, int r, float scale, const LoraA
 // projections from the adapters in g (launch_lora_prepare, once per step;
 // the GEMMs' K extensions read the adapters themselves); one row projection
 // (launch_lora_project: 0 Z_gu = x_perm sA_gu^T, 1 Y_gu = dgu sB_gu, 2 Z_d =
-// act sA_d^T, 3 Y_d = do_perm sB_d) into the workspace; the adapter
-// gradients from the projections held there (launch_lora_outer).
+// act sA_d^T, 3 Y_d = do_perm sB_d; with tok, the rows are those of x or dy
+// [T][K] read through it, and with rw, output row p is scaled by rw[p] in
+// fp32) into the workspace; the adapter gradients from the projections held
+// there (launch_lora_outer).
 hipError_t launch_lora_prepare(const moe_shape& s, int r, float scale, const LoraArgs& g, void* ws, hipStream_t st);
 hipError_t launch_lora_project(const moe_shape& s, int r, int which, const void* in, const int32_t* offsets,
-                               void* ws, hipStream_t st);
+                               void* ws, hipStream_t st, const int32_t* tok = nullptr, const float* rw = nullptr);
 hipError_t launch_lora_outer(const moe_shape& s, int r, const LoraArgs& g, void* ws, hipStream_t st);
 
 }  // namespace moe

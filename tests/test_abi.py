@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(B):
     names = declared_functions()
-    assert len(names) == 50, names
+    assert len(names) == 53, names
     for n in names:
         assert hasattr(B.lib, n), n
 
@@ -198,6 +198,18 @@ def test_lora_validation(B):
     GU = B.lib.moe_lora_grads_unmerged
     assert GU(s, 16, *([F] * 12), un - 1, None) == 3
     assert GU(s, 16, *([F] * 5), None, *([F] * 6), un, None) == 1
+    # the same without x_perm and do_perm: x and dy read through the tokens
+    GG = B.lib.moe_lora_gemm_gate_up_gathered
+    assert GG(s, 16, *([F] * 11), un - 1, None) == 3
+    assert GG(s, 16, F, None, *([F] * 9), un, None) == 1            # row_token
+    assert GG(s, 20, *([F] * 11), un, None) == 2
+    DY = B.lib.moe_lora_gemm_down_dgrad_dy
+    assert DY(s, 16, *([F] * 10), un - 1, None) == 3
+    assert DY(s, 16, F, F, None, *([F] * 7), un, None) == 1         # row_weight
+    assert DY(B.shape(64, 128, 8, 2, 64, "f32"), 16, *([F] * 10), un, None) == 2
+    GUG = B.lib.moe_lora_grads_unmerged_gathered
+    assert GUG(s, 16, *([F] * 14), un - 1, None) == 3
+    assert GUG(s, 16, F, F, None, *([F] * 11), un, None) == 1       # row_weight
     QW = B.lib.moe_quantize_mxfp4_weights
     assert QW(8, 64, 48, F, F, F, None) == 1          # K % 32
     assert QW(8, 64, 64, F, None, F, None) == 1

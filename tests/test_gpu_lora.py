@@ -14,7 +14,8 @@ the C ABI.
   do_perm (LoRAStage(gathered=True): moe_gemm_down_dgrad_dy and
   moe_lora_grads_gathered), and without merged weights
   (LoRAStage(unmerged=True): every GEMM over its reduction extended by the
-  rank, moe_lora_grads_unmerged), against the same oracle.
+  rank, moe_lora_grads_unmerged), and with neither (the gathered calls with
+  the extended reductions), against the same oracle.
 """
 import numpy as np
 import pytest
@@ -62,17 +63,18 @@ def test_merge(E, N, K, r, in_place):
     assert frac >= 0.999
 
 
-MODES = ["x_perm", "gathered", "unmerged"]
+MODES = ["x_perm", "gathered", "unmerged", "gathered_unmerged"]
 
 
 def lora_run(d: U.DevInputs, r: int, s: float, adapters, mode: str = "x_perm"):
     """mode: "x_perm" (merged weights), "gathered" (merged, no x_perm and
-    do_perm) or "unmerged" (no merged weights)."""
+    do_perm), "unmerged" (no merged weights) or "gathered_unmerged" (neither)."""
     from mixture_experts_expert_amd import binding as B
     c = d.cfg
     T = d.t["x"].shape[0]
     ad = {n: U.to_dev(adapters[n]) for n in NAMES}
-    st = B.LoRAStage(T, c.H, c.E, c.k, c.I, r, s, gathered=mode == "gathered", unmerged=mode == "unmerged")
+    st = B.LoRAStage(T, c.H, c.E, c.k, c.I, r, s, gathered="gathered" in mode,
+                     unmerged="unmerged" in mode)
     st.forward(d.t["x"], d.t["w_router"], d.t["w_gate"], d.t["w_up"], d.t["w_down"], ad, d.bias)
     st.backward(d.t["dy"])
     torch.cuda.synchronize()
