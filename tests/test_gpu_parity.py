@@ -192,8 +192,8 @@ def test_paired_backward_gemms_same_bits(cfg):
 
 def test_routing_with_nan_logits():
     """NaN logits (a hidden state holding a NaN; NaN and -inf biases) select
-    exactly the oracle's experts: a NaN ranks below every number, ties to the
-    lower index. The sort then places every row; route backward skips
+    exactly the oracle's experts: a NaN ranks below every number, equal
+    logits (NaN or not) go to the lower index. The sort then places every row; route backward skips
     caller indices outside [0, E)."""
     from mixture_experts_expert_amd import binding as B
     from oracle import oracle as O
@@ -204,9 +204,11 @@ def test_routing_with_nan_logits():
     inp = synth.make_inputs(cfg, seed=6, with_dy=True)
     x = inp.bits["x"].copy()
     x[3, 11] = 0x7FC0  # a bf16 NaN in token 3
+    x[5] = 0  # token 5's logits are the bias itself: equal logits tie on the index
     bias = np.zeros(E, np.float32)
     bias[[1, 9]] = nan
     bias[[4, 12]] = -inf
+    bias[[2, 7]] = 3.0
     s = B.shape(T, H, E, k, I, torch.bfloat16)
     dev = "cuda"
     logits = torch.empty(T, E, device=dev)
@@ -235,6 +237,7 @@ def test_routing_with_nan_logits():
     assert np.array_equal(gl[fin].view(np.uint32), rl[fin].view(np.uint32))
     assert np.array_equal(U.to_np(idx), ri)
     assert U.to_np(idx)[3].tolist() == [0, 1, 2, 3]  # every logit of token 3 is NaN
+    assert U.to_np(idx)[5].tolist() == [2, 7, 0, 3]  # 3, 3, then the lowest-index zeros
     others = np.arange(T) != 3
     assert not np.isin(U.to_np(idx)[others], [1, 9]).any()  # NaN biases are never picked over numbers
     c, o, a, b = O.permute_index(ri, E)
