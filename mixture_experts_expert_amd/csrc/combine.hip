@@ -77,6 +77,51 @@ __global__ __launch_bounds__(kThreads) void gather_sum_kernel(int Tn, int k, int
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + static_cast<int>(threadIdx.x) / kWave);
   if (t >= Tn) return;
   const int64_t tk = static_cast<int64_t>(t) * k;
+  if (k <= kBatch) {
+    // One batch of slots: the row indices once, then two bands of 64 chunks
+    // (16 row chunks) in flight together. A second band past the row repeats
+    // the first band's chunk and stores the same bytes there again (no branch
+    // for the loads to sink into).
+    int idx;
+    float wt;
+    load_slots(f2s, WEIGHTED ? w : nullptr, tk, 0, k, lane, idx, wt);
+    int64_t row[kBatch];
+    float wj[kBatch];
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj) {
+      row[jj] = static_cast<int64_t>(slot_bcast(idx, jj)) * chunks;
+      wj[jj] = slot_bcast(wt, jj);
+    }
+    for (int c = lane; c < chunks; c += 2 * kWave) {
+      const bool second = c + kWave < chunks;
+      const int c2 = second ? c + kWave : c;
+      uint4 v[2][kBatch];
+#pragma unroll
+      for (int jj = 0; jj < kBatch; ++jj) {
+        v[0][jj] = src[row[jj] + c];
+        v[1][jj] = src[row[jj] + c2];
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        float acc[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc[i] = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < kBatch; ++jj) {
+          const bool live = jj < k;
+          float x[N];
+          Vec<T>::unpack(v[b][jj], x);
+#pragma unroll
+          for (int i = 0; i < N; ++i) {
+            const float sum = WEIGHTED ? acc[i] + wj[jj] * x[i] : acc[i] + x[i];
+            acc[i] = live ? sum : acc[i];
+          }
+        }
+        out[static_cast<int64_t>(t) * chunks + (b == 0 ? c : c2)] = Vec<T>::pack(acc);
+      }
+    }
+    return;
+  }
   for (int c = lane; c < chunks; c += kWave) {
     float acc[N];
 #pragma unroll

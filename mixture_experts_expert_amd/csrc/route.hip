@@ -121,6 +121,12 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(int Tn, in
   float acc[kEW];
 #pragma unroll
   for (int j = 0; j < kEW; ++j) acc[j] = 0.0f;
+  // This wavefront's experts and their biases, loaded now so that their
+  // latency hides behind the chains.
+  const int e = e0 + wave * kEW;
+  float bv[kEW];
+#pragma unroll
+  for (int j = 0; j < kEW; ++j) bv[j] = (bias && e + j < E) ? bias[e + j] : 0.0f;
 
   Stager<T, kTileT> sx;
   Stager<T, kTileE> sw;
@@ -142,27 +148,32 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(int Tn, in
     }
     const float* xb = xs[buf] + xoff;
     const float* wb = ws[buf] + woff;
-#pragma unroll
-    for (int hb = 0; hb < kHC; hb += kHB) {
-      float xv[kHB], wv[8];
+    // Batch b + 1's LDS reads are in flight while batch b's FMAs run.
+    float xv[2][kHB], wv[2][8];
+    auto read_batch = [&](int hb, float(&xr)[kHB], float(&wr8)[8]) {
 #pragma unroll
       for (int i = 0; i < kHB / 4; ++i) {
         const float4 q = *reinterpret_cast<const float4*>(xb + hb + 4 * i);
-        xv[4 * i] = q.x;
-        xv[4 * i + 1] = q.y;
-        xv[4 * i + 2] = q.z;
-        xv[4 * i + 3] = q.w;
+        xr[4 * i] = q.x;
+        xr[4 * i + 1] = q.y;
+        xr[4 * i + 2] = q.z;
+        xr[4 * i + 3] = q.w;
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const float4 q = *reinterpret_cast<const float4*>(wb + hb + 4 * i);
-        wv[4 * i] = q.x;
-        wv[4 * i + 1] = q.y;
-        wv[4 * i + 2] = q.z;
-        wv[4 * i + 3] = q.w;
+        wr8[4 * i] = q.x;
+        wr8[4 * i + 1] = q.y;
+        wr8[4 * i + 2] = q.z;
+        wr8[4 * i + 3] = q.w;
       }
-      fma_8h<0>(acc, wv, xv);
-      fma_8h<1>(acc, wv, xv + 8);
+    };
+    read_batch(0, xv[0], wv[0]);
+#pragma unroll
+    for (int b = 0; b < kHC / kHB; ++b) {
+      if (b + 1 < kHC / kHB) read_batch((b + 1) * kHB, xv[(b + 1) & 1], wv[(b + 1) & 1]);
+      fma_8h<0>(acc, wv[b & 1], xv[b & 1]);
+      fma_8h<1>(acc, wv[b & 1], xv[b & 1] + 8);
     }
     if (s + 1 < nsteps) {
       sx.store(xs[buf ^ 1], tid);
@@ -173,10 +184,9 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(int Tn, in
 
   const int t = t0 + lane;
   if (t >= Tn) return;
-  const int e = e0 + wave * kEW;
   float v[kEW];
 #pragma unroll
-  for (int j = 0; j < kEW; ++j) v[j] = (bias && e + j < E) ? acc[j] + bias[e + j] : acc[j];
+  for (int j = 0; j < kEW; ++j) v[j] = bias ? acc[j] + bv[j] : acc[j];
   float* dst = logits + static_cast<int64_t>(t) * E + e;
   if (e + kEW <= E && (E % 4) == 0) {
     reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
