@@ -867,6 +867,8 @@ moe_status moe_lora_gemm_gate_up_gathered(moe_shape s, int32_t r, const void* x,
   const moe_status st = check_lora_unmerged(s, r, ws_bytes);
   if (st != MOE_OK) return st;
   if (any_null(x, row_token, offsets, w_gate, w_up, b_gate, b_up, g, u, a, ws)) return MOE_EINVAL;
+  // x's rows (and dy's, in the calls below) are addressed with 32-bit byte
+  // offsets: check_lora's bound on the sorted rows (T k >= T of them) covers them.
   const moe::LoraLayout l = moe::lora_layout(s, r);
   hipError_t err = moe::launch_lora_project(s, r, 0, x, offsets, ws, stream, row_token);  // Z_gu from x's rows
   if (err != hipSuccess) return from_hip(err);
