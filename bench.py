@@ -37,7 +37,9 @@ dispatch, GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) and `clock_ghz_counter`
 (the shader clock the kernel ran at). `cpu_baseline` times
 the CPU oracle on every token of the same workload (first seed), on every
 host thread this job may use (the CPUs it may run on, capped by
-OMP_NUM_THREADS), with the host's CPU count and model.
+OMP_NUM_THREADS), with the host's CPU count and model. --library-gemms prints,
+for context only, the vendor library's dense bf16 GEMMs (through torch) with
+the flops of the stage's grouped GEMMs at the workload's shape.
 
 After the timed steps (and outside them): `ms_per_step_without_call_events`
 times the same step without the per-call events; `graph_ms_per_step` the same
@@ -372,6 +374,47 @@ def lora_timing(cfg, seed: int, tensors, bias, stream, r: int = 64, scale: float
     return out
 
 
+def library_gemms(cfg, reps: int = 20) -> dict:
+    """Context only, not the product path: dense bf16 GEMMs of the vendor
+    library (torch.matmul / torch.bmm -> hipBLASLt) with the flops of the
+    stage's grouped GEMMs at this shape: each projection as one GEMM over all
+    T*k sorted rows (one weight, bf16 output), and gate/up as a batched GEMM
+    over E equal groups of rows (its right operand made contiguous first)."""
+    import torch
+    M, H, I, E = cfg.M, cfg.H, cfg.I, cfg.E
+    g = torch.Generator(device="cuda").manual_seed(0)
+
+    def rnd(*shape):
+        return torch.randn(*shape, device="cuda", dtype=torch.bfloat16, generator=g)
+
+    x, a, dgu = rnd(M, H), rnd(M, I), rnd(M, 2 * I)
+    wgu, wd = rnd(2 * I, H), rnd(H, I)
+    runs = {
+        "gate_up_fwd": (lambda: x @ wgu.t(), 4 * M * H * I),
+        "down_fwd": (lambda: a @ wd.t(), 2 * M * H * I),
+        "gate_up_dgrad": (lambda: dgu @ wgu, 4 * M * H * I),
+        "gate_up_wgrad": (lambda: dgu.t() @ x, 4 * M * H * I),
+    }
+    if M % E == 0:
+        xe = x.view(E, M // E, H)
+        wge = rnd(E, H, 2 * I)  # [E, H, 2I]: contiguous
+        runs["gate_up_fwd_batched"] = (lambda: torch.bmm(xe, wge), 4 * M * H * I)
+    out = {}
+    for name, (f, flops) in runs.items():
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1)}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -388,6 +431,8 @@ def main() -> int:
                     help="launch nothing after the timed steps (for profiling): no sequential, inference or CPU pass")
     ap.add_argument("--lora-only", action="store_true",
                     help="only time the adapter (LoRA) step and its calls; prints {\"lora_ms\": ...}")
+    ap.add_argument("--library-gemms", action="store_true",
+                    help="only time dense vendor-library GEMMs of the same flops (context); prints {\"library_gemm_ms\": ...}")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (PMC counter calibration)")
     args = ap.parse_args()
@@ -425,6 +470,9 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"seed {seed}: inputs ready in {time.perf_counter() - t0:.1f} s")
 
+    if args.library_gemms:
+        print(json.dumps({"library_gemm_ms": library_gemms(cfg), "config": {"workload": cfg.name}}), flush=True)
+        return 0
     if args.lora_only:
         load(seeds[0])
         tensors = tuple(cur[n] for n in ["x", "w_router", "w_gate", "w_up", "w_down", "dy"])
