@@ -1,0 +1,91 @@
+"""GPU parity on seeded random small shapes: every output of the training step
+against the oracle, element by element, through the default chain (x_perm,
+do_perm) and, for bf16, the chain without both (gather_fused + dy_fused).
+
+The fixed cases pin chosen shapes; these draw the ones in between from a
+fixed seed: expert counts that are not multiples of the router's 32-expert
+blocks (1 to 299, so both top-k kernels run: 16-lane rows for E <= 256 and
+k <= 16, a wavefront per token above), k from 1 to min(E, 20), hidden and
+intermediate sizes at their 64-element granularity, and 1 to 399 tokens
+(ragged 64-token router tiles, 256-row GEMM tiles and experts without rows).
+The adapter step (rank a multiple of 8 up to 128, random scale) runs the same
+way in its four forms: merged weights with x_perm or without x_perm and
+do_perm, and without merged weights, with or without them.
+"""
+import numpy as np
+import pytest
+
+from mixture_experts_expert_amd import synth
+
+import gpu_util as U
+from test_gpu_fused import check_dy_fused, dy_fused_stage
+from test_gpu_lora import MODES, NAMES, check_tokens, lora_run, oracle_lora
+from test_gpu_parity import check_all
+
+pytestmark = pytest.mark.gpu
+
+
+def random_configs(n: int, seed: int, dtype: str):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(1, 300)) if i % 3 else int(rng.integers(1, 40))
+        k = int(rng.integers(1, min(E, 20) + 1))
+        T = int(rng.integers(1, 400))
+        H = 64 * int(rng.integers(1, 7))
+        I = 64 * int(rng.integers(1, 6))
+        out.append(synth.MoEConfig(f"rand_{dtype}_{i}_T{T}_H{H}_E{E}_k{k}_I{I}", T=T, H=H, E=E, k=k, I=I,
+                                   dtype=dtype, backward=True))
+    return out
+
+
+BF16 = random_configs(30, 2024, "bf16")
+F32 = random_configs(4, 7, "f32")
+
+
+@pytest.mark.parametrize("cfg", BF16 + F32, ids=lambda c: c.name)
+def test_random_shape_all_outputs(cfg):
+    U.say(f"[random shape] {cfg}")
+    U.begin(cfg.name, f"{cfg} seed 3")
+    inp = synth.make_inputs(cfg, seed=3, with_dy=True)
+    d = U.DevInputs(inp)
+    plain = U.run_stage(d, True)
+    ref = U.oracle_full(inp, True)
+    check_all(plain, ref, cfg, True)
+    if cfg.dtype == "bf16":
+        U.say("  without x_perm and do_perm")
+        st = U.run_stage(d, True, stage=dy_fused_stage(d, True))
+        check_dy_fused(d, st, plain, ref, U.tol(cfg))
+
+
+def random_lora_configs(n: int, seed: int):
+    rng = np.random.default_rng(seed)
+    out = []
+    for cfg in random_configs(n, seed, "bf16"):
+        r = 8 * int(rng.integers(1, 17))
+        s = float(rng.choice([0.5, 1.0, 2.0]))
+        out.append((cfg, r, s))
+    return out
+
+
+LORA = random_lora_configs(6, 31)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("cfg,r,s", LORA, ids=[f"{c.name}-r{r}" for c, r, _ in LORA])
+def test_random_shape_lora(cfg, r, s, mode):
+    U.say(f"[random shape, adapters] {cfg} r={r} scale {s} {mode}")
+    U.begin(f"lora_{mode}.{cfg.name}", f"{cfg} seed 4, adapters rank {r}, scale {s}")
+    inp = synth.make_inputs(cfg, seed=4, with_dy=True)
+    adapters = synth.make_adapters(cfg, r, seed=4)
+    d = U.DevInputs(inp)
+    st = lora_run(d, r, s, adapters, mode)
+    ref_r = U.oracle_route(inp)
+    U.check_routing(st, ref_r)
+    ref = oracle_lora(inp, adapters, s, ref_r["topk_idx"], ref_r["topk_w"])
+    check_tokens(st, ref_r, ref)
+    counts = ref_r["counts"]
+    for n in NAMES:
+        got = U.to_np(st.buf["d" + n])
+        U.check_close("d" + n, got, ref["d" + n], U.BF16_TOL)
+        assert not np.any(got[counts == 0]), ("experts without rows", n)
