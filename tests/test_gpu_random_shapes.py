@@ -10,7 +10,8 @@ intermediate sizes at their 64-element granularity, and 1 to 399 tokens
 (ragged 64-token router tiles, 256-row GEMM tiles and experts without rows).
 The adapter step (rank a multiple of 8 up to 128, random scale) runs the same
 way in its four forms: merged weights with x_perm or without x_perm and
-do_perm, and without merged weights, with or without them.
+do_perm, and without merged weights, with or without them. The inference
+forwards (fused bf16, E4M3 and fp8 x MXFP4 weights) run on random shapes too.
 """
 import numpy as np
 import pytest
@@ -18,7 +19,8 @@ import pytest
 from mixture_experts_expert_amd import synth
 
 import gpu_util as U
-from test_gpu_fused import check_dy_fused, dy_fused_stage
+from test_gpu_fp8 import check_fp8, fp8_forward
+from test_gpu_fused import check_dy_fused, check_fused_indices, dy_fused_stage, fused_forward
 from test_gpu_lora import MODES, NAMES, check_tokens, lora_run, oracle_lora
 from test_gpu_parity import check_all
 
@@ -89,3 +91,27 @@ def test_random_shape_lora(cfg, r, s, mode):
         got = U.to_np(st.buf["d" + n])
         U.check_close("d" + n, got, ref["d" + n], U.BF16_TOL)
         assert not np.any(got[counts == 0]), ("experts without rows", n)
+
+
+FWD = random_configs(8, 55, "bf16")
+
+
+@pytest.mark.parametrize("fmt", ["bf16_fused", "fp8", "mxfp4"])
+@pytest.mark.parametrize("cfg", FWD, ids=lambda c: c.name)
+def test_random_shape_inference_forward(cfg, fmt):
+    U.say(f"[random shape, inference forward] {cfg} {fmt}")
+    U.begin(f"{fmt}.{cfg.name}", f"{cfg} seed 6, {fmt} inference forward")
+    inp = synth.make_inputs(cfg, seed=6, with_dy=False)
+    d = U.DevInputs(inp)
+    if fmt == "bf16_fused":
+        _, out = fused_forward(d)
+        ref = U.oracle_full(inp, False)
+        assert U.same_bits(U.to_np(out["logits"]), ref["logits"]), "logits differ"
+        for n in ["topk_idx", "counts", "offsets", "sorted_to_flat", "flat_to_sorted"]:
+            assert np.array_equal(U.to_np(out[n]), ref[n]), n
+        check_fused_indices(out, cfg.k)
+        U.check_close("a", U.to_np(out["a"]), ref["a"], U.tol(cfg))
+        U.check_close("y", U.to_np(out["y"]), ref["y"], U.tol(cfg))
+    else:
+        w, out = fp8_forward(d, fmt)
+        check_fp8(inp, w, out, fmt=fmt)
