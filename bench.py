@@ -5,18 +5,18 @@
 
 One step is the whole stage on one batch of synthetic input already resident
 in HBM, on one stream, every step a call of the C ABI, as the library chains
-it (MoEStage; moe_grouped_gemm_fwd and moe_grouped_gemm_bwd): route -> expert
-indexing + gather (x_perm) -> gate/up GEMM (SwiGLU epilogue) -> down GEMM ->
-combine, then combine backward (do_perm, d_topk_w) -> down backward (data
-gradient with the SwiGLU backward epilogue, then the weight gradient, in one
-persistent launch) -> gate/up backward (likewise) -> unpermute-sum -> router
-backward. --chain fused times the chain that materialises neither x_perm nor
-do_perm (MoEStage with gather_fused and dy_fused): the sort writes each
-sorted row's token and routing weight, gate/up reads x through the tokens and
-also writes the weighted activations a_w, the combine backward writes
-d_topk_w only, the down backward reads dy through the tokens and takes the
-routing weight in its epilogue, the gate/up backward reads x through the
-tokens. The line also reports the other chain's time.
+it (MoEStage with gather_fused and dy_fused; moe_grouped_gemm_fwd and
+moe_grouped_gemm_bwd): route -> expert indexing (the sort also writes each
+sorted row's token and routing weight) -> gate/up GEMM reading x through the
+tokens (SwiGLU epilogue; it also writes the weighted activations a_w) -> down
+GEMM -> combine, then combine backward (d_topk_w) -> down backward (data
+gradient reading dy through the tokens, with the routing weight and the
+SwiGLU backward in its epilogue, then the weight gradient, in one persistent
+launch) -> gate/up backward (likewise, x read through the tokens) ->
+unpermute-sum -> router backward. Neither x_perm nor do_perm is written.
+--chain xperm times the chain that materialises both (the gather writes
+x_perm, the combine backward writes do_perm, and the GEMMs read them). The
+line also reports the other chain's time.
 
 Each input seed (default 0, 1 and 2) gets W untimed warmup steps and K timed
 steps; the line reports the seed with the median time (`ms_per_step_by_seed`
@@ -50,7 +50,7 @@ stream, concurrently with the data-gradient GEMMs (x_perm chain);
 above; `gather_fused_ms` the x_perm chain without x_perm only (gate/up and
 the gate/up backward read x through the sorted rows' tokens),
 `dy_fused_ms` the x_perm chain without do_perm only, and
-`gather_dy_fused_ms` without both (the default chain), each with its changed
+`gather_dy_fused_ms` without both, each with its changed
 calls on their own; `single_launch_ms` the step with
 one launch per GEMM (the six single-GEMM entry points) and the four backward
 GEMMs on their own (whose TFLOP/s join `gemm_tflops`); `inference_forward_ms`
@@ -143,10 +143,13 @@ def source_hash() -> str:
 
 
 def profiled_counters(kernel: str, workload: str, chain: str) -> dict:
-    """The committed counter summary profiles/<kernel>.<workload>.traffic.txt
-    (HBM bytes per launch, MFMA busy fraction, clock), or {} when there is
-    none, it was taken on the other chain or the GEMM source changed since."""
-    path = os.path.join(PROFILES, f"{kernel}.{workload}.traffic.txt")
+    """The committed counter summary of a GEMM call (HBM bytes per launch,
+    MFMA busy fraction, clock): profiles/<kernel>.<workload>.traffic.txt for
+    the x_perm chain, profiles/<kernel>.gathered.<workload>.traffic.txt for
+    the chain without x_perm and do_perm; {} when there is none, it was taken
+    on the other chain or the GEMM source changed since."""
+    name = f"{kernel}.{workload}" if chain == "xperm" else f"{kernel}.gathered.{workload}"
+    path = os.path.join(PROFILES, f"{name}.traffic.txt")
     if not os.path.exists(path):
         return {}
     rec = {}
@@ -425,8 +428,8 @@ def main() -> int:
                     help="input seeds; each runs W warmup and K timed steps, the line reports the median")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample (default: every token of the workload)")
-    ap.add_argument("--chain", choices=["xperm", "fused"], default="xperm",
-                    help="the timed chain: materialising x_perm and do_perm (default), or without both")
+    ap.add_argument("--chain", choices=["xperm", "fused"], default="fused",
+                    help="the timed chain: without x_perm and do_perm (default), or materialising both")
     ap.add_argument("--timed-only", action="store_true",
                     help="launch nothing after the timed steps (for profiling): no sequential, inference or CPU pass")
     ap.add_argument("--lora-only", action="store_true",
@@ -557,9 +560,9 @@ def main() -> int:
         s, x, rt["row_token"], rt["row_weight"], b["offsets"], wg, wu, b["g"], b["u"], b["a"], a_w)
     both_calls["moe_gemm_gate_up_bwd"] = gf_calls["moe_gemm_gate_up_bwd"]
 
-    # The timed chain: by default the one that materialises x_perm and
-    # do_perm (by_name); --chain fused times the one without both
-    # (both_calls).
+    # The timed chain: by default the one without x_perm and do_perm
+    # (both_calls); --chain xperm times the one that materialises both
+    # (by_name).
     chain = both_calls if args.chain == "fused" else by_name
 
     # HIP events in the timed steps bracket the GEMM calls only (an event
