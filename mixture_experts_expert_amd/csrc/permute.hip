@@ -6,7 +6,8 @@
 // over fixed blocks of kPermBlock pairs, with no atomics on positions:
 //   1. per-block expert histograms (LDS integer atomics; counts only),
 //   2. one block scans each expert's column of block counts (block bases and
-//      counts) and the counts themselves (offsets),
+//      counts) and the counts themselves (offsets); with at most 128 blocks
+//      every block of pass 3 does this for itself instead, so two launches,
 //   3. each block ranks its pairs in flat order: inside a wavefront the pairs
 //      with the same expert are found by one ballot per bit of the expert id,
 //      and a pair's rank is the number of such lanes below it; wavefronts and
@@ -29,6 +30,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kScanThreads = 1024;
 constexpr int kSlabInts = 8192;  // block counts staged in LDS per scan step
+// Up to this many indexing blocks (T*k <= 131072 pairs), the ranking blocks
+// scan the block counts themselves; past it the column scan has a launch of
+// its own (each block would read nb * E counts).
+constexpr int kScanInBlocks = 128;
 
 __device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
 
@@ -94,10 +99,19 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 // The fused inference forward also takes, per sorted row p, its token
 // row_token[p] = s2f[p] / k and its routing weight row_weight[p] = w[s2f[p]]
 // (both null otherwise).
+//
+// SCAN = false: hist holds the column-scanned block counts and offsets is
+// read (scan_kernel ran before). SCAN = true (few blocks): hist holds the raw
+// block counts, and every block does the scan's work for itself instead of a
+// launch of its own: the pairs of each expert in earlier blocks and in all
+// blocks (nb reads per expert), then the exclusive scan of the totals over
+// the experts; block 0 writes counts and offsets. Same integers either way.
+template <bool SCAN>
 __global__ __launch_bounds__(kThreads) void rank_scatter_kernel(int n, int E, int nbits,
                                                                 const int32_t* __restrict__ idx,
                                                                 const int32_t* __restrict__ hist_base,
-                                                                const int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ offsets,
                                                                 int32_t* __restrict__ s2f,
                                                                 int32_t* __restrict__ f2s, int k,
                                                                 const float* __restrict__ w,
@@ -108,10 +122,97 @@ __global__ __launch_bounds__(kThreads) void rank_scatter_kernel(int n, int E, in
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wv = tid / kWave;
-  for (int e = tid; e < E; e += kThreads) {
-    running[e] = offsets[e] + hist_base[static_cast<int64_t>(blockIdx.x) * E + e];
+  if constexpr (SCAN) {
+    __shared__ int32_t total[1024];
+    __shared__ int32_t part[kWavesPerBlock];
+    __shared__ int32_t pb[kThreads], pa[kThreads];
+    const int nb = static_cast<int>(gridDim.x);
+    const int blk = static_cast<int>(blockIdx.x);
+    // Column sums with the block's G = 256 / E thread groups (one when E >
+    // 256) each taking every G-th run of 32 blocks, 32 loads in flight.
+    constexpr int kRun = 32;
+    const int G = E <= kThreads ? kThreads / E : 1;
+    const int g = tid / E;
+    auto col = [&](int e, int32_t& before, int32_t& all) {
+      before = 0;
+      all = 0;
+      for (int b0 = g * kRun; b0 < nb; b0 += G * kRun) {
+        int32_t c[kRun];
 #pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) wcount[w][e] = 0;
+        for (int u = 0; u < kRun; ++u) c[u] = b0 + u < nb ? hist_base[static_cast<int64_t>(b0 + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < kRun; ++u) {
+          before += b0 + u < blk ? c[u] : 0;
+          all += c[u];
+        }
+      }
+    };
+    if (G > 1) {
+      int32_t before = 0, all = 0;
+      if (g < G) col(tid % E, before, all);
+      pb[tid] = before;
+      pa[tid] = all;
+      __syncthreads();
+      for (int e = tid; e < E; e += kThreads) {
+        int32_t sb = 0, sa = 0;
+        for (int q = 0; q < G; ++q) {
+          sb += pb[q * E + e];
+          sa += pa[q * E + e];
+        }
+        running[e] = sb;
+        total[e] = sa;
+      }
+    } else {
+      for (int e = tid; e < E; e += kThreads) col(e, running[e], total[e]);
+    }
+    for (int e = tid; e < E; e += kThreads) {
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) wcount[w][e] = 0;
+    }
+    __syncthreads();
+    // Exclusive scan of total[0..E): thread tid sums the run of `per`
+    // experts starting at tid * per, a scan over the threads orders the
+    // runs, and each run is then walked in expert order.
+    const int per = (E + kThreads - 1) / kThreads;
+    int32_t mine = 0;
+    for (int q = 0; q < per; ++q) {
+      const int e = tid * per + q;
+      if (e < E) mine += total[e];
+    }
+    // inclusive scan of `mine` inside the wavefront, then across the four
+    int32_t incl = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int32_t v = __shfl_up(incl, o);
+      incl += lane >= o ? v : 0;
+    }
+    if (lane == kWave - 1) part[wv] = incl;
+    __syncthreads();
+    int32_t all_runs = 0;
+#pragma unroll
+    for (int q = 0; q < kWavesPerBlock; ++q) {
+      incl += q < wv ? part[q] : 0;
+      all_runs += part[q];
+    }
+    int32_t off = incl - mine;
+    for (int q = 0; q < per; ++q) {
+      const int e = tid * per + q;
+      if (e < E) {
+        running[e] += off;
+        if (blk == 0) {
+          counts[e] = total[e];
+          offsets[e] = off;
+        }
+        off += total[e];
+      }
+    }
+    if (blk == 0 && tid == 0) offsets[E] = all_runs;
+  } else {
+    for (int e = tid; e < E; e += kThreads) {
+      running[e] = offsets[e] + hist_base[static_cast<int64_t>(blockIdx.x) * E + e];
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) wcount[w][e] = 0;
+    }
   }
   __syncthreads();
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -204,10 +305,15 @@ hipError_t launch_sort(const moe_shape& s, const int32_t* idx, int32_t* counts, 
   block_hist_kernel<<<nb, kThreads, 0, st>>>(n, s.E, idx, hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (nb <= kScanInBlocks) {  // each ranking block scans for itself: one launch fewer
+    rank_scatter_kernel<true><<<nb, kThreads, 0, st>>>(n, s.E, nbits, idx, hist, counts, offsets, s2f, f2s, s.k, w,
+                                                       row_token, row_weight);
+    return hipGetLastError();
+  }
   scan_kernel<<<1, kScanThreads, 0, st>>>(nb, s.E, hist, counts, offsets);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  rank_scatter_kernel<<<nb, kThreads, 0, st>>>(n, s.E, nbits, idx, hist, offsets, s2f, f2s, s.k, w, row_token,
-                                                row_weight);
+  rank_scatter_kernel<false><<<nb, kThreads, 0, st>>>(n, s.E, nbits, idx, hist, counts, offsets, s2f, f2s, s.k, w,
+                                                      row_token, row_weight);
   return hipGetLastError();
 }
 

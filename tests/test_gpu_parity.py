@@ -251,3 +251,50 @@ def test_routing_with_nan_logits():
             if 0 <= ii[t, j] < E:
                 want[ii[t, j]] = 0.25 * ((j + 1) - 2.5)  # w (g_j - sum_i w g_i), exact in fp32
         assert np.array_equal(dl[t], want), t
+
+
+SORT_CASES = [
+    # (T, E, k, skewed): T*k = 131072 is 128 indexing blocks, the most whose
+    # ranking blocks scan the block counts themselves; one pair more and the
+    # column scan runs as a launch of its own.
+    (16384, 128, 8, False),
+    (16385, 128, 8, False),
+    (30000, 1024, 4, True),
+    (40000, 1024, 4, False),
+    (5, 3, 2, False),
+]
+
+
+@pytest.mark.parametrize("T,E,k,skewed", SORT_CASES, ids=lambda v: str(v))
+def test_sort_both_scan_forms(T, E, k, skewed):
+    """The sort alone (moe_permute_fused) on either side of the block count
+    where the column scan moves into the ranking blocks: counts, offsets,
+    both permutations, and each sorted row's token and weight, bit for bit
+    against the oracle's stable sort."""
+    from mixture_experts_expert_amd import binding as B
+    from oracle import oracle as O
+    U.say(f"[sort] T={T} E={E} k={k} skewed={skewed}")
+    rng = np.random.default_rng(T + E + k)
+    p = None
+    if skewed:
+        p = 1.0 / np.arange(1, E + 1) ** 1.2
+        p /= p.sum()
+    idx = rng.choice(E, size=(T, k), p=p).astype(np.int32)
+    w = rng.random((T, k), dtype=np.float32)
+    s = B.shape(T, 64, E, k, 64, torch.bfloat16)
+    dev = "cuda"
+    i32 = dict(dtype=torch.int32, device=dev)
+    counts, offsets = torch.empty(E, **i32), torch.empty(E + 1, **i32)
+    s2f, f2s = torch.empty(T * k, **i32), torch.empty(T * k, **i32)
+    row_token = torch.empty(T * k, **i32)
+    row_weight = torch.empty(T * k, device=dev)
+    ws = torch.empty(B.moe_workspace_bytes(s), dtype=torch.uint8, device=dev)
+    B.moe_permute_fused(s, U.to_dev(idx), U.to_dev(w), counts, offsets, s2f, f2s, row_token, row_weight, ws)
+    torch.cuda.synchronize()
+    rc, ro, rs2f, rf2s = O.permute_index(idx, E)
+    assert np.array_equal(U.to_np(counts), rc)
+    assert np.array_equal(U.to_np(offsets), ro)
+    assert np.array_equal(U.to_np(s2f), rs2f)
+    assert np.array_equal(U.to_np(f2s), rf2s)
+    assert np.array_equal(U.to_np(row_token), rs2f // k)
+    assert np.array_equal(U.to_np(row_weight).view(np.uint32), w.reshape(-1)[rs2f].view(np.uint32))
